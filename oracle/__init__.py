@@ -1,0 +1,143 @@
+"""CPU oracle for formal-concept enumeration.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the GPU library imports, links or runs
+anything in this package; only the tests, the smoke check and the CPU-baseline
+leg of the benchmark do.  It shares no code with the GPU path.
+
+* :func:`cbo` runs the serial Close-by-One in ``cbo.c`` (built with gcc into
+  ``liboracle_cbo.so`` next to it) and returns sorted intents, extents and the
+  work counters.
+* :mod:`oracle.brute` holds two brute-force enumerations written straight from
+  the definition of a concept, plus the CbO generation tree derived from the
+  closed sets alone; they pin the C oracle on small contexts.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "cbo.c")
+_LIB = os.path.join(_HERE, "liboracle_cbo.so")
+
+
+class _Result(ctypes.Structure):
+    _fields_ = [
+        ("n_concepts", ctypes.c_int64),
+        ("tests", ctypes.c_int64),
+        ("pairs", ctypes.c_int64),
+        ("sum_nzw", ctypes.c_int64),
+        ("sum_c", ctypes.c_int64),
+        ("saturation_violations", ctypes.c_int64),
+        ("n_levels", ctypes.c_int32),
+        ("truncated", ctypes.c_int32),
+        ("level_concepts", ctypes.POINTER(ctypes.c_int64)),
+        ("level_tests", ctypes.POINTER(ctypes.c_int64)),
+        ("intents", ctypes.POINTER(ctypes.c_uint64)),
+        ("extents", ctypes.POINTER(ctypes.c_uint64)),
+        ("wn", ctypes.c_int64),
+        ("wm", ctypes.c_int64),
+        ("seconds_enum", ctypes.c_double),
+        ("seconds_sort", ctypes.c_double),
+    ]
+
+
+def build(force: bool = False) -> str:
+    """Compile ``cbo.c`` into ``liboracle_cbo.so`` (plain gcc, -O2, no SIMD flags)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
+        os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "oracle_cbo.h"))
+    ):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-D_POSIX_C_SOURCE=199309L", "-fPIC", "-shared",
+             "-Wall", "-Wextra", "-o", tmp, _SRC],
+            cwd=_HERE,
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        lib.oracle_cbo.argtypes = [
+            ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_int64, ctypes.POINTER(_Result),
+        ]
+        lib.oracle_cbo.restype = ctypes.c_int
+        lib.oracle_free.argtypes = [ctypes.POINTER(_Result)]
+        lib.oracle_free.restype = None
+        _lib = lib
+    return _lib
+
+
+@dataclass
+class OracleResult:
+    n_objects: int
+    n_attrs: int
+    n_concepts: int
+    tests: int
+    pairs: int
+    sum_nzw: int
+    sum_c: int
+    saturation_violations: int
+    n_levels: int
+    truncated: bool
+    level_concepts: np.ndarray  # int64 [n_levels]
+    level_tests: np.ndarray     # int64 [n_levels]
+    intents: np.ndarray         # uint64 [K, wm], sorted by word tuple
+    extents: np.ndarray | None  # uint64 [K, wn] in the same order
+    seconds_enum: float
+    seconds_sort: float
+
+    @property
+    def wn(self) -> int:
+        return (self.n_objects + 63) // 64
+
+    @property
+    def wm(self) -> int:
+        return (self.n_attrs + 63) // 64
+
+
+def cbo(rows: np.ndarray, n_attrs: int, keep_extents: bool = True, max_tests: int = -1) -> OracleResult:
+    """Run the serial CbO oracle on packed rows (uint64 [N, ceil(M/64)])."""
+    lib = _load()
+    rows = np.ascontiguousarray(rows, dtype=np.uint64)
+    if rows.ndim != 2:
+        raise ValueError("rows must be 2-D")
+    n = rows.shape[0]
+    res = _Result()
+    rc = lib.oracle_cbo(
+        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), n, int(n_attrs), rows.shape[1],
+        1 if keep_extents else 0, int(max_tests), ctypes.byref(res),
+    )
+    if rc != 0:
+        raise RuntimeError("oracle_cbo failed with %d" % rc)
+    try:
+        k, wn, wm = res.n_concepts, res.wn, res.wm
+        nl = res.n_levels
+        intents = np.ctypeslib.as_array(res.intents, shape=(k * wm,)).reshape(k, wm).copy()
+        extents = None
+        if keep_extents:
+            extents = np.ctypeslib.as_array(res.extents, shape=(k * wn,)).reshape(k, wn).copy()
+        lc = np.ctypeslib.as_array(res.level_concepts, shape=(nl,)).copy()
+        lt = np.ctypeslib.as_array(res.level_tests, shape=(nl,)).copy()
+        return OracleResult(
+            n_objects=n, n_attrs=int(n_attrs), n_concepts=k, tests=res.tests, pairs=res.pairs,
+            sum_nzw=res.sum_nzw, sum_c=res.sum_c,
+            saturation_violations=res.saturation_violations, n_levels=nl,
+            truncated=bool(res.truncated), level_concepts=lc, level_tests=lt,
+            intents=intents, extents=extents, seconds_enum=res.seconds_enum,
+            seconds_sort=res.seconds_sort,
+        )
+    finally:
+        lib.oracle_free(ctypes.byref(res))

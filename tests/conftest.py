@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs a HIP device (MI355X) and the built libfcbo.so")
+    config.addinivalue_line("markers", "slow: longer CPU test")
+
+
+def _flush_case(item):
+    # Name the case before any GPU step, so a lost box still tells which one ran.
+    print("\n[case] %s" % item.nodeid, flush=True)
+
+
+@pytest.hookimpl(tryfirst=True)
+def pytest_runtest_setup(item):
+    if item.get_closest_marker("gpu") is not None:
+        _flush_case(item)

@@ -1,0 +1,274 @@
+"""Pins of the CPU oracle (oracle/cbo.c) against what the mathematics fixes.
+
+Nothing here touches the GPU library.  Every check compares the serial CbO
+oracle with something other than itself:
+  * hand-derived worked examples (tests/golden/*.txt),
+  * two brute-force enumerations from the definition of a concept
+    (all 2^M attribute subsets closed; all intersections of object rows),
+  * the CbO generation tree reconstructed from the closed sets alone, which
+    pins the closure-test count, item pairs, per-level counts and byte sums,
+  * closed forms (empty, full, diagonal, contranominal, one bicluster),
+  * invariances (duality, permutations, full rows/columns) and closedness
+    checked with numpy on the 0/1 matrix.
+"""
+
+import itertools
+from math import comb
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import brute
+from tests.golden_io import read_fixture
+
+
+def run(cells, keep_extents=True):
+    cells = np.asarray(cells, dtype=bool)
+    return oracle.cbo(synth.pack_rows(cells), cells.shape[1], keep_extents=keep_extents)
+
+
+def as_sets(words):
+    """uint64 [K, W] -> list of Python-int sets (in the given order)."""
+    out = []
+    for row in np.asarray(words, dtype=np.uint64):
+        v = 0
+        for w, x in enumerate(row):
+            v |= int(x) << (64 * w)
+        out.append(v)
+    return out
+
+
+def check_against_brute(cells, tree=True, subsets=None):
+    ctx = brute.Context(cells)
+    fam = brute.closed_intents_by_row_meets(ctx)
+    if subsets is None:
+        subsets = ctx.m <= 10
+    if subsets:
+        assert brute.closed_intents_by_subsets(ctx) == fam
+    r = run(cells)
+    ti, te = brute.sorted_concepts(ctx, fam)
+    assert r.n_concepts == len(fam)
+    assert np.array_equal(r.intents, ti)
+    assert np.array_equal(r.extents, te)
+    assert r.saturation_violations == 0
+    assert not r.truncated
+    if tree:
+        st = brute.cbo_tree(ctx, fam)
+        assert r.tests == st.tests
+        assert r.pairs == st.pairs
+        assert list(r.level_concepts) == st.level_concepts
+        assert list(r.level_tests) == st.level_tests
+        assert r.sum_nzw == st.sum_nzw
+        assert r.sum_c == st.sum_c
+    return r
+
+
+# --- worked examples -----------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["staircase4.txt", "two_blocks4.txt"])
+def test_hand_derived_examples(name):
+    cells, concepts, info = read_fixture(name)
+    r = run(cells)
+    assert r.n_concepts == info["concepts"]
+    assert r.tests == info["tests"]
+    assert r.pairs == info["pairs"]
+    assert list(r.level_concepts) == info["level_concepts"]
+    assert list(r.level_tests) == info["level_tests"]
+    want_i = synth.pack_rows(np.array([c[0] for c in concepts]))
+    want_e = synth.pack_rows(np.array([c[1] for c in concepts]))
+    assert np.array_equal(r.intents, want_i)
+    assert np.array_equal(r.extents, want_e)
+
+
+# --- brute force -------------------------------------------------------------------
+
+def test_ctx64x16_against_all_subsets():
+    cells = synth.make_config("ctx64x16", packed=False)
+    r = check_against_brute(cells, tree=True, subsets=True)
+    assert r.n_concepts == 419
+
+
+def test_random_tiny_contexts_against_brute_force():
+    rng = np.random.default_rng(12345)
+    n_cases = 0
+    for case in range(520):
+        n = int(rng.integers(1, 71))
+        m = int(rng.integers(1, 15))
+        density = float(rng.uniform(0.05, 0.95))
+        cells = synth.random_context(1000 + case, n, m, density)
+        ctx = brute.Context(cells)
+        fam = brute.closed_intents_by_row_meets(ctx)
+        check_against_brute(cells, tree=len(fam) <= 1500, subsets=m <= 8)
+        n_cases += 1
+    assert n_cases >= 500
+
+
+def test_multiword_random_against_row_meets():
+    # shapes that cross 64-bit word boundaries in both directions
+    for seed, (n, m, d) in enumerate([(65, 66, 0.04), (130, 70, 0.03), (64, 129, 0.02), (127, 64, 0.05)]):
+        cells = synth.random_context(77 + seed, n, m, d)
+        check_against_brute(cells, tree=True, subsets=False)
+
+
+# --- closed forms --------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m", [(1, 1), (5, 3), (64, 64), (65, 130)])
+def test_all_zero_context_has_top_and_bottom(n, m):
+    r = run(synth.all_zero(n, m))
+    assert r.n_concepts == 2  # (G, {}) and ({}, M)
+    assert as_sets(r.intents) == [0, (1 << m) - 1]
+
+
+@pytest.mark.parametrize("n,m", [(1, 1), (7, 70), (130, 3)])
+def test_all_ones_context_has_one_concept(n, m):
+    r = run(synth.all_ones(n, m))
+    assert r.n_concepts == 1
+    assert r.tests == 0
+    assert as_sets(r.extents) == [(1 << n) - 1]
+
+
+@pytest.mark.parametrize("k", [2, 3, 10, 64, 65, 100])
+def test_diagonal_context(k):
+    r = run(synth.diagonal(k))
+    assert r.n_concepts == k + 2
+    want = sorted([0, (1 << k) - 1] + [1 << i for i in range(k)])
+    got = as_sets(r.intents)
+    assert sorted(got) == want
+
+
+@pytest.mark.parametrize("k", [1, 2, 5, 8, 11])
+def test_contranominal_every_subset_closed(k):
+    r = run(synth.contranominal(k))
+    assert r.n_concepts == 2 ** k
+    # every closure test passes, so tests = K - 1; level d holds C(k, d) sets
+    assert r.tests == 2 ** k - 1
+    assert list(r.level_concepts) == [comb(k, d) for d in range(k + 1)]
+
+
+def test_contranominal_padded_across_words():
+    k = 12
+    cells = synth.pad_with_full(synth.contranominal(k), extra_objects=118, extra_attrs=58)  # 130 x 70
+    r = run(cells)
+    assert r.n_concepts == 2 ** k
+    assert r.tests == 2 ** k - 1
+    pad = sum(1 << a for a in range(k, k + 58))
+    assert set(as_sets(r.intents)) == {s | pad for s in range(2 ** k)}
+
+
+def test_single_planted_bicluster():
+    cells = synth.planted_bicluster(50, 20, objs=[3, 7, 11, 40], atts=[2, 5, 19])
+    r = run(cells)
+    assert r.n_concepts == 3
+    assert as_sets(r.intents) == [0, (1 << 2) | (1 << 5) | (1 << 19), (1 << 20) - 1]
+
+
+def test_full_rows_and_columns_leave_concepts_unchanged():
+    cells = synth.random_context(5, 40, 12, 0.35)
+    base = run(cells)
+    padded = run(synth.pad_with_full(cells, extra_objects=3, extra_attrs=0))
+    assert padded.n_concepts == base.n_concepts
+    assert np.array_equal(padded.intents, base.intents)
+    more = run(synth.pad_with_full(cells, extra_objects=0, extra_attrs=2))
+    assert more.n_concepts == base.n_concepts
+
+
+# --- invariances -------------------------------------------------------------------------
+
+def test_duality_ctx64x16():
+    cells = synth.make_config("ctx64x16", packed=False)
+    r = run(cells)
+    rt = run(cells.T)
+    assert rt.n_concepts == r.n_concepts
+    assert set(as_sets(rt.intents)) == set(as_sets(r.extents))
+    assert set(as_sets(rt.extents)) == set(as_sets(r.intents))
+
+
+def test_duality_random():
+    for seed in range(20):
+        cells = synth.random_context(300 + seed, 30, 25, 0.3)
+        r, rt = run(cells), run(cells.T)
+        assert rt.n_concepts == r.n_concepts
+        assert set(as_sets(rt.intents)) == set(as_sets(r.extents))
+
+
+def test_object_permutation_keeps_intents():
+    cells = synth.make_config("ctx64x16", packed=False)
+    perm = np.random.default_rng(9).permutation(cells.shape[0])
+    r, rp = run(cells), run(cells[perm])
+    assert np.array_equal(r.intents, rp.intents)
+
+
+def test_attribute_permutation_permutes_intents():
+    cells = synth.make_config("ctx64x16", packed=False)
+    perm = np.random.default_rng(10).permutation(cells.shape[1])
+    r, rp = run(cells), run(cells[:, perm])
+    assert rp.n_concepts == r.n_concepts
+    # attribute perm[i] of the original is attribute i of the permuted context
+    mapped = set()
+    for b in as_sets(rp.intents):
+        mapped.add(sum(1 << int(perm[i]) for i in range(cells.shape[1]) if (b >> i) & 1))
+    assert mapped == set(as_sets(r.intents))
+
+
+# --- invariants on the larger seeded contexts ----------------------------------------
+
+def _check_invariants(cells, r, sample=2000, seed=0):
+    n, m = cells.shape
+    k = r.n_concepts
+    ints = r.intents
+    # strictly increasing word tuples: sorted and no duplicates
+    order = np.lexsort(ints.T[::-1])
+    assert np.array_equal(order, np.arange(k))
+    if k > 1:
+        diff = np.any(ints[1:] != ints[:-1], axis=1)
+        assert diff.all()
+    ib = synth.unpack_rows(ints, m)
+    top = cells.all(axis=0)
+    assert (ib == top).all(axis=1).any()
+    assert ib.all(axis=1).any()  # bottom intent M
+    assert int(r.level_concepts.sum()) == k and r.level_concepts[0] == 1
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(k, size=min(sample, k), replace=False)
+    for i in idx:
+        b = ib[i]
+        ext = cells[:, b].all(axis=1)  # B'
+        back = cells[ext].all(axis=0) if ext.any() else np.ones(m, dtype=bool)  # B''
+        assert np.array_equal(back, b)
+        if r.extents is not None:
+            assert np.array_equal(synth.unpack_rows(r.extents[i:i + 1], n)[0], ext)
+
+
+def test_invariants_ctx2000x64():
+    cells = synth.make_config("ctx2000x64", packed=False)
+    r = run(cells)
+    _check_invariants(cells, r)
+    # |A| summed over all concepts = |G| for the root + sum of |C| over children
+    total = int(np.unpackbits(r.extents.view(np.uint8)).sum())
+    assert total == cells.shape[0] + r.sum_c
+
+
+def test_invariants_ctx10000x128():
+    cells = synth.make_config("ctx10000x128", packed=False)
+    r = run(cells, keep_extents=False)
+    _check_invariants(cells, r, sample=1000)
+
+
+@pytest.mark.parametrize("name,attrs", [("ctx2000x64", [0, 17, 63]), ("ctx10000x128", [3, 64, 127])])
+def test_slices_match_subcontexts(name, attrs):
+    """Intents containing j are exactly the intents of the objects having j."""
+    cells = synth.make_config(name, packed=False)
+    r = run(cells, keep_extents=False)
+    ib = synth.unpack_rows(r.intents, cells.shape[1])
+    for j in attrs:
+        sub = cells[cells[:, j]]
+        rs = run(sub, keep_extents=False)
+        mine = r.intents[ib[:, j]]
+        assert np.array_equal(rs.intents, mine)
+
+
+def test_truncation_budget():
+    cells = synth.make_config("ctx2000x64", packed=False)
+    r = oracle.cbo(synth.pack_rows(cells), 64, keep_extents=False, max_tests=1000)
+    assert r.truncated and r.tests == 1000
