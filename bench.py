@@ -1,0 +1,162 @@
+"""Benchmark: concept enumeration throughput on one MI355X.
+
+One step = one full call of fcbo_enumerate on the seeded 50,000 x 400 context:
+root, every level of closure tests and child writes, the intent sort and the
+sorted intents plus extent bitmaps written to preallocated device buffers.
+Inputs (the context) are resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--workload ctx50000x400]
+
+Prints one JSON line.  `value` is concepts per second; closure tests per
+second, per-kernel times (HIP events on the library's stream), the roofline of
+the dominant kernel and the CPU oracle timed on a bounded sample are added.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def kernel_bytes(cls, st, wm, wn, n, k, extents):
+    """Algorithmic bytes one step moves in a kernel class."""
+    if cls == "test_local":
+        return (st["local_parents"] * (8 * wm + 4 + 16 + 8 * wm + 8)
+                + st["local_parent_objects"] * (4 + 8 * wm))
+    if cls == "test_big":
+        return st["big_tests"] * (8 * wm + 4 + 16 + 4) + st["big_scanned_objects"] * (4 + 8)
+    if cls == "output":
+        reads = k * (4 + 8 * wm + 16) + (n + st["sum_child_objects"]) * 4
+        writes = k * 8 * wm + (k * 8 * wn if extents else 0)
+        return reads + writes
+    if cls == "sort":
+        return st["sort_passes"] * k * (8 + 12 + 12) + wm * k * (4 + 8 + 8)
+    return None
+
+
+def cpu_baseline(rows, m, max_tests):
+    import oracle
+
+    t0 = time.perf_counter()
+    r = oracle.cbo(rows, m, keep_extents=False, max_tests=max_tests)
+    wall = time.perf_counter() - t0
+    secs = r.seconds_enum + r.seconds_sort
+    return {
+        "value": r.n_concepts / secs,
+        "unit": "concepts/s",
+        "closure_tests_per_s": r.tests / secs,
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "serial CbO oracle, depth-first prefix of the same workload stopped after %d closure tests "
+                  "(%d concepts, %.1f s enumerate+sort, %.1f s wall)" % (r.tests, r.n_concepts, secs, wall),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="ctx50000x400")
+    ap.add_argument("--no-extents", action="store_true")
+    ap.add_argument("--cpu-tests", type=int, default=8_000_000, help="closure-test budget of the CPU sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import closed_set_enumeration_amd as fca
+    import synth
+
+    if not torch.cuda.is_available():
+        print("no HIP device", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    fca.load_library()
+    n, m, _ = synth.CONFIGS[args.workload]
+    rows = synth.make_config(args.workload)
+    extents = not args.no_extents
+    wn, wm = (n + 63) // 64, (m + 63) // 64
+
+    ctx = fca.Context(rows, m)
+    k = ctx.count()
+    ints, exts = ctx.alloc_outputs(k, extents)
+    print("[bench] %s: K=%d, output buffers %.2f GB" % (args.workload, k, (ints.numel() + (exts.numel() if extents else 0)) * 8 / 1e9),
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        rc, kk, st = ctx.enumerate_into(ints, exts, fca.FCBO_PROFILE)
+        assert rc == fca.FCBO_OK and kk == k
+        print("[bench] warmup %d: %.3f ms" % (i, st["enumerate_ms"]), file=sys.stderr, flush=True)
+
+    per_step = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        rc, kk, st = ctx.enumerate_into(ints, exts, fca.FCBO_PROFILE)
+        assert rc == fca.FCBO_OK and kk == k
+        per_step.append(st)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    print("[bench] timed %d steps: %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
+
+    st0 = per_step[-1]
+    kernel_ms = {c: sum(s["kernel_ms"][c] for s in per_step) / args.steps for c in fca.KERNEL_CLASSES}
+    launches = {c: sum(s["kernel_launches"][c] for s in per_step) / args.steps for c in fca.KERNEL_CLASSES}
+    dominant = max(kernel_ms, key=kernel_ms.get)
+    roof = None
+    b = kernel_bytes(dominant, st0, wm, wn, n, k, extents)
+    if b is not None and launches[dominant] > 0:
+        per_launch_bytes = b / launches[dominant]
+        avg_ms = kernel_ms[dominant] / launches[dominant]
+        achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": int(per_launch_bytes), "avg_launch_ms": round(avg_ms, 4)}
+
+    tests = st0["closure_tests"]
+    out = {
+        "metric": "concepts/sec and closure tests/sec at 1 GPU; % of HBM roofline",
+        "value": round(k / (ms_per_step * 1e-3), 1),
+        "unit": "concepts/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u64",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "objects": n, "attributes": m, "extents_out": extents,
+                   "concepts": k, "closure_tests": tests, "levels": st0["n_levels"]},
+        "closure_tests_per_s": round(tests / (ms_per_step * 1e-3), 1),
+        "device_ms": {"enumerate": round(sum(s["enumerate_ms"] for s in per_step) / args.steps, 4),
+                      "levels": round(sum(s["levels_ms"] for s in per_step) / args.steps, 4),
+                      "sort": round(sum(s["sort_ms"] for s in per_step) / args.steps, 4),
+                      "output": round(sum(s["output_ms"] for s in per_step) / args.steps, 4)},
+        "kernel_ms": {c: round(v, 4) for c, v in kernel_ms.items()},
+        "kernel_launches": launches,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    ctx.close()
+    del ints, exts
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(rows, m, args.cpu_tests)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,275 @@
+"""Formal-concept enumeration on MI355X: Python binding of libfcbo.so.
+
+The functions named like the C ABI (``fcbo_context_create``, ``fcbo_enumerate``,
+``fcbo_level_counts``, ``fcbo_copy_columns``, ``fcbo_destroy``,
+``fcbo_error_string``) only marshal arguments; every step of the enumeration
+runs in the HIP kernels of the library.  :class:`Context` is a convenience
+wrapper that takes device buffers and the stream from PyTorch.
+
+There is no CPU fallback: if ``libfcbo.so`` has not been built, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfcbo.so")
+
+FCBO_OK = 0
+FCBO_ERR_INVALID_ARGUMENT = -1
+FCBO_ERR_OUT_OF_MEMORY = -2
+FCBO_ERR_DEVICE = -3
+FCBO_ERR_CAPACITY = -4
+
+FCBO_ROWS_ON_DEVICE = 1
+FCBO_TINY_BUFFERS = 2
+FCBO_REUSE_RESULT = 1
+FCBO_PROFILE = 2
+
+KERNEL_CLASSES = ("count", "test_local", "test_big", "scan", "write_local", "write_big", "sort", "output")
+
+EXPORTED = (
+    "fcbo_context_create",
+    "fcbo_enumerate",
+    "fcbo_level_counts",
+    "fcbo_copy_columns",
+    "fcbo_destroy",
+    "fcbo_error_string",
+)
+
+
+class FcboStats(ctypes.Structure):
+    _fields_ = [
+        ("n_concepts", ctypes.c_uint64),
+        ("closure_tests", ctypes.c_uint64),
+        ("item_pairs", ctypes.c_uint64),
+        ("n_levels", ctypes.c_uint64),
+        ("sum_child_objects", ctypes.c_uint64),
+        ("output_bytes", ctypes.c_uint64),
+        ("local_parents", ctypes.c_uint64),
+        ("local_parent_objects", ctypes.c_uint64),
+        ("big_parents", ctypes.c_uint64),
+        ("big_tests", ctypes.c_uint64),
+        ("big_scanned_objects", ctypes.c_uint64),
+        ("sort_passes", ctypes.c_uint64),
+        ("enumerate_ms", ctypes.c_double),
+        ("levels_ms", ctypes.c_double),
+        ("sort_ms", ctypes.c_double),
+        ("output_ms", ctypes.c_double),
+        ("kernel_ms", ctypes.c_double * len(KERNEL_CLASSES)),
+        ("kernel_launches", ctypes.c_uint64 * len(KERNEL_CLASSES)),
+    ]
+
+    def as_dict(self) -> dict:
+        d = {name: getattr(self, name) for name, _ in self._fields_ if name not in ("kernel_ms", "kernel_launches")}
+        d["kernel_ms"] = dict(zip(KERNEL_CLASSES, list(self.kernel_ms)))
+        d["kernel_launches"] = dict(zip(KERNEL_CLASSES, [int(x) for x in self.kernel_launches]))
+        return d
+
+
+class FcboError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__("%s failed: %s (%d)" % (what, fcbo_error_string(code), code))
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfcbo.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libfcbo.so not found at %s; build it with closed_set_enumeration_amd.build.build() "
+            "(the enumeration has no CPU fallback)" % path
+        )
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.fcbo_context_create.argtypes = [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p,
+        P(ctypes.c_void_p),
+    ]
+    lib.fcbo_context_create.restype = ctypes.c_int
+    lib.fcbo_enumerate.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, P(ctypes.c_uint64),
+        P(FcboStats),
+    ]
+    lib.fcbo_enumerate.restype = ctypes.c_int
+    lib.fcbo_level_counts.argtypes = [
+        ctypes.c_void_p, P(ctypes.c_uint64), P(ctypes.c_uint64), ctypes.c_uint64, P(ctypes.c_uint64),
+    ]
+    lib.fcbo_level_counts.restype = ctypes.c_int
+    lib.fcbo_copy_columns.argtypes = [ctypes.c_void_p, P(ctypes.c_uint64), ctypes.c_uint64]
+    lib.fcbo_copy_columns.restype = ctypes.c_int
+    lib.fcbo_destroy.argtypes = [ctypes.c_void_p]
+    lib.fcbo_destroy.restype = None
+    lib.fcbo_error_string.argtypes = [ctypes.c_int]
+    lib.fcbo_error_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# --- C-ABI-named wrappers ------------------------------------------------------
+
+def fcbo_error_string(code: int) -> str:
+    return load_library().fcbo_error_string(int(code)).decode()
+
+
+def fcbo_context_create(rows_ptr: int, n_objects: int, n_attrs: int, row_stride_words: int, flags: int = 0,
+                        hip_stream: int = 0) -> int:
+    """Returns the context handle; raises FcboError on failure."""
+    out = ctypes.c_void_p()
+    rc = load_library().fcbo_context_create(
+        ctypes.c_void_p(rows_ptr), n_objects, n_attrs, row_stride_words, flags, ctypes.c_void_p(hip_stream),
+        ctypes.byref(out),
+    )
+    if rc != FCBO_OK:
+        raise FcboError(rc, "fcbo_context_create")
+    return out.value
+
+
+def fcbo_enumerate(ctx: int, intents_out_ptr: int, extents_out_ptr: int, capacity: int, flags: int = 0):
+    """Returns (rc, n_concepts, FcboStats); FCBO_ERR_CAPACITY is returned, not raised."""
+    k = ctypes.c_uint64(0)
+    st = FcboStats()
+    rc = load_library().fcbo_enumerate(
+        ctypes.c_void_p(ctx), ctypes.c_void_p(intents_out_ptr or None), ctypes.c_void_p(extents_out_ptr or None),
+        capacity, flags, ctypes.byref(k), ctypes.byref(st),
+    )
+    if rc not in (FCBO_OK, FCBO_ERR_CAPACITY):
+        raise FcboError(rc, "fcbo_enumerate")
+    return rc, k.value, st
+
+
+def fcbo_level_counts(ctx: int):
+    """(concepts per level, tests per level) of the last enumeration, as numpy uint64."""
+    lib = load_library()
+    nl = ctypes.c_uint64(0)
+    rc = lib.fcbo_level_counts(ctypes.c_void_p(ctx), None, None, 0, ctypes.byref(nl))
+    if rc != FCBO_OK:
+        raise FcboError(rc, "fcbo_level_counts")
+    conc = np.zeros(nl.value, dtype=np.uint64)
+    tests = np.zeros(nl.value, dtype=np.uint64)
+    P = ctypes.POINTER(ctypes.c_uint64)
+    rc = lib.fcbo_level_counts(ctypes.c_void_p(ctx), conc.ctypes.data_as(P), tests.ctypes.data_as(P), nl.value,
+                               ctypes.byref(nl))
+    if rc != FCBO_OK:
+        raise FcboError(rc, "fcbo_level_counts")
+    return conc, tests
+
+
+def fcbo_copy_columns(ctx: int, n_objects: int, n_attrs: int) -> np.ndarray:
+    wn = (n_objects + 63) // 64
+    out = np.zeros((n_attrs, wn), dtype=np.uint64)
+    rc = load_library().fcbo_copy_columns(ctypes.c_void_p(ctx), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                          out.size)
+    if rc != FCBO_OK:
+        raise FcboError(rc, "fcbo_copy_columns")
+    return out
+
+
+def fcbo_destroy(ctx: int) -> None:
+    if ctx:
+        load_library().fcbo_destroy(ctypes.c_void_p(ctx))
+
+
+# --- convenience wrapper over torch device buffers ----------------------------
+
+@dataclass
+class Result:
+    n_concepts: int
+    intents: "object"        # torch int64 tensor (K, wm) on the device, bits as in the C ABI
+    extents: "object"        # torch int64 tensor (K, wn) or None
+    stats: dict
+
+
+class Context:
+    """A formal context on the current HIP device.
+
+    ``rows`` is a uint64 (N, ceil(M/64)) numpy array (copied from the host) or
+    an int64/uint64 torch tensor already on the device.
+    """
+
+    def __init__(self, rows, n_attrs: int, stream=None, flags: int = 0):
+        import torch
+
+        if not torch.cuda.is_available():
+            raise RuntimeError("no HIP device available")
+        self._torch = torch
+        self.n_attrs = int(n_attrs)
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        extra = int(flags) & ~FCBO_ROWS_ON_DEVICE
+        if isinstance(rows, np.ndarray):
+            rows = np.ascontiguousarray(rows, dtype=np.uint64)
+            if rows.ndim != 2:
+                raise ValueError("rows must be 2-D")
+            self.n_objects = rows.shape[0]
+            ptr, stride, flags = rows.ctypes.data, rows.shape[1], 0
+            keep = rows
+        else:
+            if rows.dim() != 2 or not rows.is_cuda:
+                raise ValueError("a torch rows tensor must be 2-D and on the device")
+            rows = rows.contiguous()
+            self.n_objects = rows.shape[0]
+            ptr, stride, flags = rows.data_ptr(), rows.shape[1], FCBO_ROWS_ON_DEVICE
+            keep = rows
+        self.wn = (self.n_objects + 63) // 64
+        self.wm = (self.n_attrs + 63) // 64
+        self.handle = fcbo_context_create(ptr, self.n_objects, self.n_attrs, stride, flags | extra,
+                                          self.stream.cuda_stream)
+        del keep
+
+    def close(self):
+        if getattr(self, "handle", None):
+            fcbo_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def count(self) -> int:
+        """Enumerate (keeping the result in the context) and return K."""
+        rc, k, _ = fcbo_enumerate(self.handle, 0, 0, 0, 0)
+        assert rc == FCBO_ERR_CAPACITY
+        return k
+
+    def alloc_outputs(self, capacity: int, extents: bool = True):
+        torch = self._torch
+        dev = torch.device("cuda", torch.cuda.current_device())
+        ints = torch.empty((max(capacity, 1), self.wm), dtype=torch.int64, device=dev)
+        exts = torch.empty((max(capacity, 1), self.wn), dtype=torch.int64, device=dev) if extents else None
+        return ints, exts
+
+    def enumerate_into(self, intents, extents, flags: int = 0):
+        """One full call into preallocated buffers; returns (rc, K, stats dict)."""
+        cap = intents.shape[0]
+        rc, k, st = fcbo_enumerate(
+            self.handle, intents.data_ptr(), extents.data_ptr() if extents is not None else 0, cap, flags
+        )
+        return rc, k, st.as_dict()
+
+    def enumerate(self, extents: bool = True, profile: bool = False) -> Result:
+        k = self.count()
+        ints, exts = self.alloc_outputs(k, extents)
+        flags = FCBO_REUSE_RESULT | (FCBO_PROFILE if profile else 0)
+        rc, k2, st = self.enumerate_into(ints, exts, flags)
+        if rc != FCBO_OK or k2 != k:
+            raise FcboError(rc, "fcbo_enumerate")
+        return Result(k, ints[:k], exts[:k] if exts is not None else None, st)
+
+    def level_counts(self):
+        return fcbo_level_counts(self.handle)
+
+    def columns(self) -> np.ndarray:
+        return fcbo_copy_columns(self.handle, self.n_objects, self.n_attrs)

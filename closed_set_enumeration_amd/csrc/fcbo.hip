@@ -1,0 +1,603 @@
+// libfcbo host runtime: context, concept store, level loop, sort, output.
+// The C ABI is declared in include/fcbo.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "fcbo.h"
+#include "fcbo_device.h"
+
+using namespace fcbo;
+
+namespace {
+
+// Error propagation inside the library: every HIP call goes through CK.
+struct HipError {
+    int code;
+};
+
+inline int map_error(hipError_t e)
+{
+    if (e == hipSuccess) return FCBO_OK;
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return FCBO_ERR_OUT_OF_MEMORY;
+    return FCBO_ERR_DEVICE;
+}
+
+#define CK(expr)                                                   \
+    do {                                                           \
+        hipError_t e_ = (expr);                                    \
+        if (e_ != hipSuccess) throw HipError{map_error(e_)};       \
+    } while (0)
+
+#define CK_LAUNCH() CK(hipGetLastError())
+
+inline uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+template <typename T>
+void dfree(T *&p)
+{
+    if (p) (void)hipFree((void *)p);
+    p = nullptr;
+}
+
+// Grow a device array to hold at least `need` elements, keeping the first
+// `keep` elements.  Capacity grows at least by half to amortise copies.
+template <typename T>
+void ensure(T *&p, uint64_t &cap, uint64_t need, uint64_t keep, hipStream_t s, uint64_t min_cap = 1024)
+{
+    if (need <= cap && p) return;
+    uint64_t ncap = std::max<uint64_t>(need, cap + cap / 2);
+    ncap = std::max<uint64_t>(ncap, min_cap);
+    T *q = nullptr;
+    CK(hipMalloc((void **)&q, ncap * sizeof(T)));
+    if (p && keep) {
+        hipError_t e = hipMemcpyAsync(q, p, keep * sizeof(T), hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) {
+            (void)hipFree(q);
+            throw HipError{map_error(e)};
+        }
+    }
+    dfree(p);
+    p = q;
+    cap = ncap;
+}
+
+constexpr int kGridCap = 4096;  // blocks for grid-stride wave kernels
+
+}  // namespace
+
+struct fcbo_context {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    int64_t n = 0, m = 0;
+    int wn = 0, wm = 0;
+    uint64_t tail_m = 0;
+    bool tiny = false;  // FCBO_TINY_BUFFERS: every buffer starts at its minimum size
+    uint64_t *rows = nullptr;  // n x wm (+1 padding row)
+    uint64_t *cols = nullptr;  // m x wn
+
+    // concept store
+    uint64_t cap_k = 0, cap_int = 0, cap_cur = 0, cap_loff = 0, cap_o = 0;
+    uint64_t *intents = nullptr;
+    int32_t *cursor = nullptr;
+    uint64_t *loff = nullptr;
+    uint32_t *objs = nullptr;
+
+    // level scratch
+    uint64_t cap_pass = 0, cap_nch = 0, cap_nob = 0, cap_cb = 0, cap_ob = 0, cap_bi = 0, cap_bn = 0, cap_bo = 0;
+    uint64_t *pass = nullptr, *cbase = nullptr, *obase = nullptr, *big_off = nullptr;
+    uint32_t *nchild = nullptr, *nobj = nullptr, *big_idx = nullptr, *big_n = nullptr;
+    uint64_t cap_bt = 0, cap_bts = 0;
+    uint32_t *bt_size = nullptr;
+    uint64_t *bt_sscan = nullptr;
+    uint64_t *scan_part = nullptr;  // 2 x kScanBlocks
+    uint64_t *counters = nullptr;   // CNT_N
+    uint64_t *h_counters = nullptr; // pinned, CNT_N
+
+    // sort scratch
+    uint64_t cap_ka = 0, cap_kb = 0, cap_ia = 0, cap_ib = 0, cap_h = 0, cap_ho = 0;
+    uint64_t *keys_a = nullptr, *keys_b = nullptr;
+    uint32_t *idx_a = nullptr, *idx_b = nullptr;
+    uint32_t *hist = nullptr;
+    uint64_t *hist_off = nullptr;
+    uint64_t *sort_red = nullptr;  // 2 words
+    uint32_t *perm = nullptr;      // points at idx_a or idx_b after the sort
+
+    // result of the last enumeration
+    bool have_result = false;
+    bool have_perm = false;
+    uint64_t K = 0, tests = 0, pairs = 0, sum_c = 0;
+    uint64_t local_parents = 0, local_objs = 0, big_parents = 0, big_tests = 0, big_scan = 0, sort_passes = 0;
+    std::vector<uint64_t> lev_concepts, lev_tests;
+
+    // profiling
+    bool profile = false;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_used = 0;
+    std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> marks;
+
+    hipEvent_t ev_get()
+    {
+        if (ev_used == ev_pool.size()) {
+            hipEvent_t e;
+            CK(hipEventCreate(&e));
+            ev_pool.push_back(e);
+        }
+        return ev_pool[ev_used++];
+    }
+    hipEvent_t prof_begin()
+    {
+        if (!profile) return nullptr;
+        hipEvent_t e = ev_get();
+        CK(hipEventRecord(e, stream));
+        return e;
+    }
+    void prof_end(int cls, hipEvent_t b)
+    {
+        if (!profile) return;
+        hipEvent_t e = ev_get();
+        CK(hipEventRecord(e, stream));
+        marks.push_back({cls, {b, e}});
+    }
+
+    void free_all()
+    {
+        dfree(rows); dfree(cols);
+        dfree(intents); dfree(cursor); dfree(loff); dfree(objs);
+        dfree(pass); dfree(cbase); dfree(obase); dfree(big_off);
+        dfree(nchild); dfree(nobj); dfree(big_idx); dfree(big_n);
+        dfree(bt_size); dfree(bt_sscan); dfree(scan_part); dfree(counters);
+        dfree(keys_a); dfree(keys_b); dfree(idx_a); dfree(idx_b); dfree(hist); dfree(hist_off);
+        dfree(sort_red);
+        if (h_counters) (void)hipHostFree(h_counters);
+        h_counters = nullptr;
+        for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+        ev_pool.clear();
+    }
+
+    LevelArgs level_args() const
+    {
+        LevelArgs A;
+        memset(&A, 0, sizeof(A));
+        A.rows = rows; A.cols = cols;
+        A.n = (int)n; A.m = (int)m; A.wn = wn; A.wm = wm; A.tail_m = tail_m;
+        A.intents = intents; A.cursor = cursor; A.loff = loff; A.objs = objs;
+        A.pass = pass; A.nchild = nchild; A.nobj = nobj; A.cbase = cbase; A.obase = obase;
+        A.big_idx = big_idx; A.big_n = big_n; A.big_off = big_off;
+        A.bt_size = bt_size; A.bt_sscan = bt_sscan; A.bt_cap = std::min(cap_bt, cap_bts);
+        A.counters = counters;
+        return A;
+    }
+
+    // exclusive scan (see k_scan_*): a (and b) -> out_a (and out_b), n from the
+    // device or the host.
+    void scan(const uint32_t *a, const uint32_t *b, const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
+              uint64_t *out_a, uint64_t *out_b, uint64_t *tot_a, uint64_t *tot_b)
+    {
+        int nb = kScanBlocks;
+        if (!n_dev) nb = (int)std::min<uint64_t>(kScanBlocks, std::max<uint64_t>(1, div_up(n_host, 4 * kBlock)));
+        hipLaunchKernelGGL(k_scan_up, dim3(nb), dim3(kBlock), 0, stream, a, b, n_dev, n_host, n_cap, scan_part);
+        CK_LAUNCH();
+        hipLaunchKernelGGL(k_scan_mid, dim3(1), dim3(kScanBlocks), 0, stream, scan_part, nb, n_dev, n_host, n_cap,
+                           out_a, out_b, tot_a, tot_b);
+        CK_LAUNCH();
+        hipLaunchKernelGGL(k_scan_down, dim3(nb), dim3(kBlock), 0, stream, a, b, n_dev, n_host, n_cap,
+                           (const uint64_t *)scan_part, out_a, out_b);
+        CK_LAUNCH();
+    }
+
+    void enumerate_levels();
+    void sort_intents();
+    void write_output(uint64_t *intents_out, uint64_t *extents_out);
+};
+
+namespace {
+
+template <int WMC>
+void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
+{
+    const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kWavesPerBlock)));
+    hipEvent_t b = c->prof_begin();
+    hipLaunchKernelGGL(k_local_test<WMC>, dim3(gl), dim3(kBlock), 0, c->stream, A);
+    CK_LAUNCH();
+    c->prof_end(FCBO_K_TEST_LOCAL, b);
+    b = c->prof_begin();
+    hipLaunchKernelGGL(k_big_test<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+    CK_LAUNCH();
+    c->prof_end(FCBO_K_TEST_BIG, b);
+}
+
+template <int WMC>
+void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P)
+{
+    const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kWavesPerBlock)));
+    hipEvent_t b = c->prof_begin();
+    hipLaunchKernelGGL(k_local_write<WMC>, dim3(gl), dim3(kBlock), 0, c->stream, A);
+    CK_LAUNCH();
+    c->prof_end(FCBO_K_WRITE_LOCAL, b);
+    b = c->prof_begin();
+    hipLaunchKernelGGL(k_big_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+    CK_LAUNCH();
+    c->prof_end(FCBO_K_WRITE_BIG, b);
+}
+
+typedef void (*level_fn)(fcbo_context *, const LevelArgs &, uint64_t);
+
+struct LevelFns {
+    level_fn tests, writes;
+};
+
+LevelFns pick_level_fns(int wm)
+{
+    switch (wm) {
+    case 1: return {launch_level_tests<1>, launch_level_writes<1>};
+    case 2: return {launch_level_tests<2>, launch_level_writes<2>};
+    case 3: return {launch_level_tests<3>, launch_level_writes<3>};
+    case 4: return {launch_level_tests<4>, launch_level_writes<4>};
+    case 5: return {launch_level_tests<5>, launch_level_writes<5>};
+    case 6: return {launch_level_tests<6>, launch_level_writes<6>};
+    case 7: return {launch_level_tests<7>, launch_level_writes<7>};
+    case 8: return {launch_level_tests<8>, launch_level_writes<8>};
+    default:
+        if (wm <= 16) return {launch_level_tests<16>, launch_level_writes<16>};
+        if (wm <= 32) return {launch_level_tests<32>, launch_level_writes<32>};
+        return {launch_level_tests<64>, launch_level_writes<64>};
+    }
+}
+
+}  // namespace
+
+void fcbo_context::enumerate_levels()
+{
+    const LevelFns fns = pick_level_fns(wm);
+    // root
+    ensure(intents, cap_int, (uint64_t)wm * 1024, 0, stream, tiny ? 1 : 1024);
+    ensure(cursor, cap_cur, 1024, 0, stream, tiny ? 1 : 1024);
+    ensure(loff, cap_loff, 1025, 0, stream, tiny ? 1 : 1024);
+    ensure(objs, cap_o, (uint64_t)n, 0, stream, tiny ? 1 : 1024);
+    cap_k = std::min(cap_int / wm, std::min(cap_cur, cap_loff - 1));
+    {
+        uint64_t t = std::max<uint64_t>((uint64_t)n, (uint64_t)wm);
+        hipLaunchKernelGGL(k_root_init, dim3((unsigned)div_up(t, kBlock)), dim3(kBlock), 0, stream, intents, cursor,
+                           loff, objs, (int)n, wm, tail_m);
+        CK_LAUNCH();
+        unsigned gx = (unsigned)std::min<uint64_t>(256, div_up((uint64_t)n, kBlock));
+        hipLaunchKernelGGL(k_root_and, dim3(gx, wm), dim3(kBlock), 0, stream, (const uint64_t *)rows, intents,
+                           (int)n, wm);
+        CK_LAUNCH();
+    }
+    lev_concepts.clear();
+    lev_tests.clear();
+    tests = pairs = sum_c = 0;
+    local_parents = local_objs = big_parents = big_tests = big_scan = 0;
+    uint64_t lo = 0, P = 1, obj_hi = (uint64_t)n;  // parents [lo, lo+P); objects used so far
+    while (P > 0) {
+        if (P >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
+        // every level adds an attribute to the intent, so there are at most M + 1
+        if (lev_concepts.size() > (size_t)m + 1) throw HipError{FCBO_ERR_DEVICE};
+        ensure(pass, cap_pass, P * (uint64_t)wm, 0, stream, tiny ? 1 : 1024);
+        ensure(nchild, cap_nch, P, 0, stream, tiny ? 1 : 1024);
+        ensure(nobj, cap_nob, P, 0, stream, tiny ? 1 : 1024);
+        ensure(cbase, cap_cb, P + 1, 0, stream, tiny ? 1 : 1024);
+        ensure(obase, cap_ob, P + 1, 0, stream, tiny ? 1 : 1024);
+        ensure(big_idx, cap_bi, P, 0, stream, tiny ? 1 : 1024);
+        ensure(big_n, cap_bn, P, 0, stream, tiny ? 1 : 1024);
+        ensure(big_off, cap_bo, P + 1, 0, stream, tiny ? 1 : 1024);
+        if (!bt_size) {
+            const uint64_t first = tiny ? 1 : (1u << 20);
+            ensure(bt_size, cap_bt, first, 0, stream, tiny ? 1 : 1024);
+            ensure(bt_sscan, cap_bts, first + 1, 0, stream, tiny ? 1 : 1024);
+        }
+        bool redo;
+        int redos = 0;
+        uint64_t n_children = 0, n_objs = 0;
+        do {
+            redo = false;
+            if (redos > 2) throw HipError{FCBO_ERR_DEVICE};  // a grown buffer always fits the redo
+            LevelArgs A = level_args();
+            A.lo = lo;
+            A.P = P;
+            A.child_lo = lo + P;
+            A.child_obj_lo = obj_hi;
+            A.bt_cap = std::min(cap_bt, cap_bts - 1);
+            CK(hipMemsetAsync(counters, 0, CNT_N * sizeof(uint64_t), stream));
+            hipEvent_t b = prof_begin();
+            hipLaunchKernelGGL(k_count, dim3((unsigned)div_up(P, kBlock)), dim3(kBlock), 0, stream, A);
+            CK_LAUNCH();
+            prof_end(FCBO_K_COUNT, b);
+            b = prof_begin();
+            // offsets of the big parents' tests; total -> counters[CNT_TBIG]
+            scan(big_n, nullptr, counters + CNT_BIG, 0, P, big_off, nullptr, counters + CNT_TBIG, nullptr);
+            prof_end(FCBO_K_SCAN, b);
+            fns.tests(this, A, P);
+            b = prof_begin();
+            scan(bt_size, nullptr, counters + CNT_TBIG, 0, A.bt_cap, bt_sscan, nullptr, nullptr, nullptr);
+            scan(nchild, nobj, nullptr, P, P, cbase, obase, counters + CNT_CHILDREN, counters + CNT_OBJS);
+            prof_end(FCBO_K_SCAN, b);
+            CK(hipMemcpyAsync(h_counters, counters, CNT_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+            CK(hipStreamSynchronize(stream));
+            if (h_counters[CNT_OVERFLOW]) {
+                uint64_t need = h_counters[CNT_TBIG];
+                ensure(bt_size, cap_bt, need, 0, stream, tiny ? 1 : 1024);
+                ensure(bt_sscan, cap_bts, need + 1, 0, stream, tiny ? 1 : 1024);
+                redo = true;
+                ++redos;
+                continue;
+            }
+            n_children = h_counters[CNT_CHILDREN];
+            n_objs = h_counters[CNT_OBJS];
+            lev_concepts.push_back(P);
+            lev_tests.push_back(h_counters[CNT_TESTS]);
+            tests += h_counters[CNT_TESTS];
+            pairs += h_counters[CNT_PAIRS];
+            sum_c += n_objs;
+            big_parents += h_counters[CNT_BIG];
+            local_parents += P - h_counters[CNT_BIG];
+            local_objs += h_counters[CNT_SMALL_OBJS];
+            big_tests += h_counters[CNT_TBIG];
+            big_scan += h_counters[CNT_BIG_SCAN];
+            // room for the children in the store
+            const uint64_t k_end = lo + P + n_children;
+            const uint64_t keep_k = lo + P;
+            ensure(intents, cap_int, k_end * wm, keep_k * wm, stream, tiny ? 1 : 1024);
+            ensure(cursor, cap_cur, k_end, keep_k, stream, tiny ? 1 : 1024);
+            ensure(loff, cap_loff, k_end + 1, keep_k + 1, stream, tiny ? 1 : 1024);
+            ensure(objs, cap_o, obj_hi + n_objs, obj_hi, stream, tiny ? 1 : 1024);
+            if (n_children) {
+                A = level_args();
+                A.lo = lo;
+                A.P = P;
+                A.child_lo = lo + P;
+                A.child_obj_lo = obj_hi;
+                A.bt_cap = std::min(cap_bt, cap_bts - 1);
+                fns.writes(this, A, P);
+            }
+        } while (redo);
+        lo += P;
+        P = n_children;
+        obj_hi += n_objs;
+    }
+    K = lo;
+    have_result = true;
+    have_perm = false;
+}
+
+void fcbo_context::sort_intents()
+{
+    const uint64_t n_keys = K;
+    if (n_keys >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
+    ensure(keys_a, cap_ka, n_keys, 0, stream, tiny ? 1 : 1024);
+    ensure(keys_b, cap_kb, n_keys, 0, stream, tiny ? 1 : 1024);
+    ensure(idx_a, cap_ia, n_keys, 0, stream, tiny ? 1 : 1024);
+    ensure(idx_b, cap_ib, n_keys, 0, stream, tiny ? 1 : 1024);
+    const uint64_t ntiles = div_up(n_keys, kSortTile);
+    ensure(hist, cap_h, 256 * ntiles, 0, stream, tiny ? 1 : 1024);
+    ensure(hist_off, cap_ho, 256 * ntiles + 1, 0, stream, tiny ? 1 : 1024);
+    hipEvent_t b = prof_begin();
+    hipLaunchKernelGGL(k_iota, dim3((unsigned)div_up(n_keys, kBlock)), dim3(kBlock), 0, stream, idx_a, n_keys);
+    CK_LAUNCH();
+    prof_end(FCBO_K_SORT, b);
+    sort_passes = 0;
+    uint64_t *ka = keys_a, *kb = keys_b;
+    uint32_t *ia = idx_a, *ib = idx_b;
+    const unsigned gk = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(2048, div_up(n_keys, kBlock)));
+    for (int u = wm - 1; u >= 0; --u) {
+        CK(hipMemsetAsync(sort_red, 0, sizeof(uint64_t), stream));          // OR of the keys
+        CK(hipMemsetAsync(sort_red + 1, 0xFF, sizeof(uint64_t), stream));   // AND of the keys
+        b = prof_begin();
+        hipLaunchKernelGGL(k_gather_key, dim3(gk), dim3(kBlock), 0, stream, (const uint64_t *)intents, wm, u,
+                           (const uint32_t *)ia, ka, n_keys, sort_red);
+        CK_LAUNCH();
+        prof_end(FCBO_K_SORT, b);
+        CK(hipMemcpyAsync(h_counters, sort_red, 2 * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+        CK(hipStreamSynchronize(stream));
+        const uint64_t varying = h_counters[0] ^ h_counters[1];
+        for (int d = 0; d < 8; ++d) {
+            const int shift = 8 * d;
+            if (((varying >> shift) & 0xFFu) == 0) continue;  // every key has the same digit
+            b = prof_begin();
+            hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)ntiles), dim3(kBlock), 0, stream, (const uint64_t *)ka,
+                               n_keys, shift, hist, ntiles);
+            CK_LAUNCH();
+            scan(hist, nullptr, nullptr, 256 * ntiles, 256 * ntiles, hist_off, nullptr, nullptr, nullptr);
+            hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)ntiles), dim3(kBlock), 0, stream, (const uint64_t *)ka,
+                               (const uint32_t *)ia, n_keys, shift, (const uint64_t *)hist_off, ntiles, kb, ib);
+            CK_LAUNCH();
+            prof_end(FCBO_K_SORT, b);
+            std::swap(ka, kb);
+            std::swap(ia, ib);
+            ++sort_passes;
+        }
+    }
+    perm = ia;
+    have_perm = true;
+}
+
+void fcbo_context::write_output(uint64_t *intents_out, uint64_t *extents_out)
+{
+    hipEvent_t b = prof_begin();
+    const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(8192, div_up(K, kWavesPerBlock)));
+    hipLaunchKernelGGL(k_output, dim3(g), dim3(kBlock), 0, stream, (const uint64_t *)intents, (const uint64_t *)loff,
+                       (const uint32_t *)objs, (const uint32_t *)perm, K, wm, wn, intents_out, extents_out);
+    CK_LAUNCH();
+    prof_end(FCBO_K_OUTPUT, b);
+}
+
+// ---------------------------------------------------------------------------
+// C ABI
+
+extern "C" {
+
+const char *fcbo_error_string(int code)
+{
+    switch (code) {
+    case FCBO_OK: return "ok";
+    case FCBO_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FCBO_ERR_OUT_OF_MEMORY: return "device out of memory";
+    case FCBO_ERR_DEVICE: return "HIP device error";
+    case FCBO_ERR_CAPACITY: return "output capacity too small";
+    default: return "unknown error";
+    }
+}
+
+int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, int64_t row_stride_words,
+                        uint32_t flags, void *hip_stream, fcbo_context **out)
+{
+    if (!out) return FCBO_ERR_INVALID_ARGUMENT;
+    *out = nullptr;
+    if (!rows || n_objects < 1 || n_objects > INT32_MAX || n_attrs < 1 || n_attrs > 4096 ||
+        row_stride_words < (n_attrs + 63) / 64 || (flags & ~(FCBO_ROWS_ON_DEVICE | FCBO_TINY_BUFFERS)))
+        return FCBO_ERR_INVALID_ARGUMENT;
+    fcbo_context *c = new (std::nothrow) fcbo_context();
+    if (!c) return FCBO_ERR_OUT_OF_MEMORY;
+    try {
+        CK(hipGetDevice(&c->device));
+        c->stream = (hipStream_t)hip_stream;
+        c->tiny = (flags & FCBO_TINY_BUFFERS) != 0;
+        c->n = n_objects;
+        c->m = n_attrs;
+        c->wn = (int)((n_objects + 63) / 64);
+        c->wm = (int)((n_attrs + 63) / 64);
+        c->tail_m = (n_attrs & 63) ? ((1ull << (n_attrs & 63)) - 1ull) : ~0ull;
+        CK(hipMalloc((void **)&c->rows, ((uint64_t)n_objects + 1) * c->wm * sizeof(uint64_t)));
+        CK(hipMalloc((void **)&c->cols, (uint64_t)n_attrs * c->wn * sizeof(uint64_t)));
+        CK(hipMalloc((void **)&c->scan_part, 2 * kScanBlocks * sizeof(uint64_t)));
+        CK(hipMalloc((void **)&c->counters, CNT_N * sizeof(uint64_t)));
+        CK(hipMalloc((void **)&c->sort_red, 2 * sizeof(uint64_t)));
+        CK(hipHostMalloc((void **)&c->h_counters, CNT_N * sizeof(uint64_t), hipHostMallocDefault));
+        CK(hipMemsetAsync(c->rows, 0, ((uint64_t)n_objects + 1) * c->wm * sizeof(uint64_t), c->stream));
+        const hipMemcpyKind kind = (flags & FCBO_ROWS_ON_DEVICE) ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+        CK(hipMemcpy2DAsync(c->rows, (size_t)c->wm * sizeof(uint64_t), rows, (size_t)row_stride_words * sizeof(uint64_t),
+                            (size_t)c->wm * sizeof(uint64_t), (size_t)n_objects, kind, c->stream));
+        hipLaunchKernelGGL(k_mask_rows, dim3((unsigned)div_up((uint64_t)n_objects, kBlock)), dim3(kBlock), 0,
+                           c->stream, c->rows, (int)n_objects, c->wm, c->tail_m);
+        CK_LAUNCH();
+        const uint64_t waves = (uint64_t)c->wn * c->wm;
+        hipLaunchKernelGGL(k_transpose, dim3((unsigned)div_up(waves, kWavesPerBlock)), dim3(kBlock), 0, c->stream,
+                           (const uint64_t *)c->rows, c->cols, (int)n_objects, (int)n_attrs, c->wn, c->wm);
+        CK_LAUNCH();
+        CK(hipStreamSynchronize(c->stream));
+    } catch (const HipError &e) {
+        c->free_all();
+        delete c;
+        return e.code;
+    } catch (const std::bad_alloc &) {
+        c->free_all();
+        delete c;
+        return FCBO_ERR_OUT_OF_MEMORY;
+    }
+    *out = c;
+    return FCBO_OK;
+}
+
+int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_out, uint64_t capacity,
+                   uint32_t flags, uint64_t *n_concepts_out, fcbo_stats *stats_out)
+{
+    if (!ctx || (flags & ~(FCBO_REUSE_RESULT | FCBO_PROFILE))) return FCBO_ERR_INVALID_ARGUMENT;
+    fcbo_stats st;
+    memset(&st, 0, sizeof(st));
+    hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr, e3 = nullptr;
+    int rc = FCBO_OK;
+    try {
+        CK(hipSetDevice(ctx->device));
+        ctx->profile = (flags & FCBO_PROFILE) != 0;
+        ctx->ev_used = 0;
+        ctx->marks.clear();
+        e0 = ctx->ev_get();
+        e1 = ctx->ev_get();
+        e2 = ctx->ev_get();
+        e3 = ctx->ev_get();
+        CK(hipEventRecord(e0, ctx->stream));
+        const bool reuse = (flags & FCBO_REUSE_RESULT) && ctx->have_result;
+        if (!reuse) ctx->enumerate_levels();
+        CK(hipEventRecord(e1, ctx->stream));
+        if (n_concepts_out) *n_concepts_out = ctx->K;
+        if (!intents_out || capacity < ctx->K) {
+            rc = FCBO_ERR_CAPACITY;
+            CK(hipStreamSynchronize(ctx->stream));
+        } else {
+            if (!(reuse && ctx->have_perm)) ctx->sort_intents();
+            CK(hipEventRecord(e2, ctx->stream));
+            ctx->write_output(intents_out, extents_out);
+            CK(hipEventRecord(e3, ctx->stream));
+            CK(hipStreamSynchronize(ctx->stream));
+            float ms = 0;
+            CK(hipEventElapsedTime(&ms, e0, e3));
+            st.enumerate_ms = ms;
+            CK(hipEventElapsedTime(&ms, e1, e2));
+            st.sort_ms = ms;
+            CK(hipEventElapsedTime(&ms, e2, e3));
+            st.output_ms = ms;
+        }
+        float ms = 0;
+        CK(hipEventElapsedTime(&ms, e0, e1));
+        st.levels_ms = ms;
+        for (auto &mk : ctx->marks) {
+            CK(hipEventElapsedTime(&ms, mk.second.first, mk.second.second));
+            st.kernel_ms[mk.first] += ms;
+            st.kernel_launches[mk.first] += 1;
+        }
+    } catch (const HipError &e) {
+        return e.code;
+    } catch (const std::bad_alloc &) {
+        return FCBO_ERR_OUT_OF_MEMORY;
+    }
+    st.n_concepts = ctx->K;
+    st.closure_tests = ctx->tests;
+    st.item_pairs = ctx->pairs;
+    st.n_levels = ctx->lev_concepts.size();
+    st.sum_child_objects = ctx->sum_c;
+    st.local_parents = ctx->local_parents;
+    st.local_parent_objects = ctx->local_objs;
+    st.big_parents = ctx->big_parents;
+    st.big_tests = ctx->big_tests;
+    st.big_scanned_objects = ctx->big_scan;
+    st.sort_passes = ctx->sort_passes;
+    if (rc == FCBO_OK)
+        st.output_bytes = ctx->K * (uint64_t)ctx->wm * 8 + (extents_out ? ctx->K * (uint64_t)ctx->wn * 8 : 0);
+    if (stats_out) *stats_out = st;
+    return rc;
+}
+
+int fcbo_level_counts(const fcbo_context *ctx, uint64_t *concepts_per_level, uint64_t *tests_per_level,
+                      uint64_t max_levels, uint64_t *n_levels_out)
+{
+    if (!ctx || !ctx->have_result) return FCBO_ERR_INVALID_ARGUMENT;
+    const uint64_t nl = ctx->lev_concepts.size();
+    if (n_levels_out) *n_levels_out = nl;
+    for (uint64_t i = 0; i < nl && i < max_levels; ++i) {
+        if (concepts_per_level) concepts_per_level[i] = ctx->lev_concepts[i];
+        if (tests_per_level) tests_per_level[i] = ctx->lev_tests[i];
+    }
+    return FCBO_OK;
+}
+
+int fcbo_copy_columns(const fcbo_context *ctx, uint64_t *host_cols, uint64_t capacity_words)
+{
+    if (!ctx || !host_cols) return FCBO_ERR_INVALID_ARGUMENT;
+    const uint64_t words = (uint64_t)ctx->m * ctx->wn;
+    if (capacity_words < words) return FCBO_ERR_CAPACITY;
+    hipError_t e = hipSetDevice(ctx->device);
+    if (e == hipSuccess) e = hipMemcpyAsync(host_cols, ctx->cols, words * sizeof(uint64_t), hipMemcpyDeviceToHost, ctx->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+    return map_error(e);
+}
+
+void fcbo_destroy(fcbo_context *ctx)
+{
+    if (!ctx) return;
+    (void)hipSetDevice(ctx->device);
+    if (ctx->stream) (void)hipStreamSynchronize(ctx->stream);
+    else (void)hipDeviceSynchronize();
+    ctx->free_all();
+    delete ctx;
+}
+
+}  // extern "C"

@@ -1,0 +1,983 @@
+// Device kernels of libfcbo: Close-by-One concept enumeration on gfx950.
+//
+// Sets are LSB-first 64-bit bitmaps (element e = bit e&63 of word e>>6); one
+// 64-bit word per wavefront lane.  The context lives on the device twice:
+// rows (object -> attributes, N x WM words) and cols (attribute -> objects,
+// M x WN words); page "hnwysp.cn/news/97538" section 3.1 and page
+// "hotelren.com/news/5603750" section 2.3 keep both layouts for the two
+// derivation directions.
+//
+// Enumeration is level-synchronous (page 4, section 2.1): the concepts of one
+// level are the parents of the next.  Unlike page 4 the full canonical test of
+// CbO (page 1, sections 2.1-2.2 and 4.3) is kept, so every concept is produced
+// once and no sort-unique pass is needed.  Frontier extents are stored as
+// sorted object lists (CSR), not bitmaps: deep in the tree an extent holds a
+// handful of objects, so a list is hundreds of times smaller than a bitmap of
+// N bits.
+//
+// Per level:
+//   k_count        candidates per parent, list of parents with > 64 objects
+//   k_local_test   one wavefront per parent with <= 64 objects: the parent's
+//                  rows are staged in LDS, one lane per candidate attribute
+//   k_big_test     one wavefront per (big parent, candidate attribute)
+//   scans          child and object offsets per parent (exact sizes, so no
+//                  overflow and no atomics on the output)
+//   k_*_write      children (C, D, j) written in parent order, then j order
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fcbo {
+
+constexpr int kWave = 64;
+constexpr int kSmallMax = 64;       // parents with at most this many objects use the local path
+constexpr int kBlock = 256;         // threads per block for wave-per-item kernels
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kScanBlocks = 1024;   // blocks of the multi-block exclusive scan
+constexpr int kSortTile = 2048;     // keys per block in a radix pass (256 threads x 8)
+constexpr int kOutTileWords = 1024; // extent words staged in LDS per output tile
+
+// Device counters shared by the kernels of one level.
+enum {
+    CNT_BIG = 0,       // number of parents with more than kSmallMax objects
+    CNT_TESTS = 1,     // closure tests of this level
+    CNT_PAIRS = 2,     // (parent, j > cursor) pairs of this level
+    CNT_OVERFLOW = 3,  // big-test buffers too small: the level is redone
+    CNT_CHILDREN = 4,  // children of this level
+    CNT_OBJS = 5,      // objects in the children's extents
+    CNT_TBIG = 6,      // closure tests of the big parents
+    CNT_SMALL_OBJS = 7, // objects in the extents of parents with <= kSmallMax objects
+    CNT_BIG_SCAN = 8,  // sum over big parents of tests x objects (list entries the big tests read)
+    CNT_N = 10
+};
+
+// The per-level arguments, passed by value.
+struct LevelArgs {
+    const uint64_t *rows;  // N x wm
+    const uint64_t *cols;  // M x wn
+    int n, m, wn, wm;
+    uint64_t tail_m;       // valid bits of the last intent word
+    // concept store
+    uint64_t *intents;     // K x wm
+    int32_t *cursor;       // K, the attribute that generated the concept (-1 for the root)
+    uint64_t *loff;        // K + 1 offsets into objs
+    uint32_t *objs;        // extent lists, ascending object ids
+    uint64_t lo, P;        // parents are concepts [lo, lo + P)
+    uint64_t child_lo;     // index of the first child (= lo + P)
+    uint64_t child_obj_lo; // offset in objs of the first child's list
+    // per-level scratch, indexed by parent p in [0, P)
+    uint64_t *pass;        // P x wm, passing attributes of each parent
+    uint32_t *nchild;      // children per parent
+    uint32_t *nobj;        // objects in the children's extents per parent
+    uint64_t *cbase;       // exclusive scan of nchild (P + 1)
+    uint64_t *obase;       // exclusive scan of nobj (P + 1)
+    uint32_t *big_idx;     // parents with > kSmallMax objects (order not fixed)
+    uint32_t *big_n;       // their candidate counts
+    uint64_t *big_off;     // exclusive scan of big_n
+    uint32_t *bt_size;     // per big test: |C| if it passed, else 0
+    uint64_t *bt_sscan;    // exclusive scan of bt_size
+    uint64_t bt_cap;       // capacity of bt_size / bt_sscan
+    uint64_t *counters;    // CNT_*
+};
+
+// ---------------------------------------------------------------------------
+// small helpers
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// Bits of word u whose attribute index is greater than y.
+__device__ __forceinline__ uint64_t above_mask(int y, int u)
+{
+    int lo = y - 64 * u;
+    if (lo < 0) return ~0ull;
+    if (lo >= 63) return 0ull;
+    return ~0ull << (lo + 1);
+}
+
+// Bits 0 .. b-1 of a word (b in [0, 63]).
+__device__ __forceinline__ uint64_t below_mask(int b) { return b ? ((1ull << b) - 1ull) : 0ull; }
+
+// Position of the k-th (0-based) set bit of x; k < popcount(x).
+__device__ __forceinline__ int select64(uint64_t x, int k)
+{
+    int pos = 0;
+    int c = __popc((uint32_t)x);
+    if (k >= c) { k -= c; x >>= 32; pos += 32; }
+    uint32_t v = (uint32_t)x;
+    c = __popc(v & 0xFFFFu);
+    if (k >= c) { k -= c; v >>= 16; pos += 16; }
+    c = __popc(v & 0xFFu);
+    if (k >= c) { k -= c; v >>= 8; pos += 8; }
+    c = __popc(v & 0xFu);
+    if (k >= c) { k -= c; v >>= 4; pos += 4; }
+    c = __popc(v & 0x3u);
+    if (k >= c) { k -= c; v >>= 2; pos += 2; }
+    if (k >= (int)(v & 1u)) pos += 1;
+    return pos;
+}
+
+__device__ __forceinline__ uint64_t wave_and(uint64_t v)
+{
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) v &= __shfl_xor(v, s);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v)
+{
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) v += __shfl_xor(v, s);
+    return v;
+}
+
+// Exclusive prefix sum over the lanes of a wavefront.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v)
+{
+    const int lane = lane_id();
+    uint32_t x = v;
+#pragma unroll
+    for (int s = 1; s < kWave; s <<= 1) {
+        uint32_t t = __shfl_up(x, s);
+        if (lane >= s) x += t;
+    }
+    return x - v;
+}
+
+// Exclusive prefix sum over a 256-thread block (u64); returns the block total.
+__device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t *s_wave, uint64_t &total)
+{
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    uint64_t x = v;
+#pragma unroll
+    for (int s = 1; s < kWave; s <<= 1) {
+        uint64_t t = __shfl_up(x, s);
+        if (lane >= s) x += t;
+    }
+    if (lane == kWave - 1) s_wave[wv] = x;
+    __syncthreads();
+    uint64_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        uint64_t sw = s_wave[w];
+        before += (w < wv) ? sw : 0ull;
+        all += sw;
+    }
+    __syncthreads();
+    total = all;
+    return before + x - v;
+}
+
+// Loop bound helper: compile-time word count when WMC <= 8, runtime otherwise.
+template <int WMC>
+__device__ __forceinline__ int words_of(int wm) { return WMC <= 8 ? WMC : wm; }
+
+// The k-th set bit, in attribute numbering, of a WMC-word set.
+template <int WMC>
+__device__ __forceinline__ int select_words(const uint64_t (&x)[WMC], int wm, int k)
+{
+    int j = 0;
+    bool found = false;
+#pragma unroll
+    for (int u = 0; u < WMC; ++u) {
+        if (u < words_of<WMC>(wm) && !found) {
+            int c = __popcll(x[u]);
+            if (k < c) {
+                j = 64 * u + select64(x[u], k);
+                found = true;
+            } else {
+                k -= c;
+            }
+        }
+    }
+    return j;
+}
+
+// ---------------------------------------------------------------------------
+// context construction
+
+// Clear the bits past the last attribute in every row.
+__global__ void k_mask_rows(uint64_t *rows, int n, int wm, uint64_t tail_m)
+{
+    uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g < (uint64_t)n) rows[g * wm + wm - 1] &= tail_m;
+}
+
+// cols[j][w] = objects 64w..64w+63 that have attribute j.  One wavefront per
+// (object word w, attribute word v): lane l reads row 64w+l, 64 ballots turn
+// the 64x64 bit block around, lane t keeps the ballot of bit t.  No atomics.
+__global__ void __launch_bounds__(kBlock) k_transpose(const uint64_t *__restrict__ rows, uint64_t *__restrict__ cols,
+                                                       int n, int m, int wn, int wm)
+{
+    const int lane = lane_id();
+    const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    if (wave >= (uint64_t)wn * wm) return;
+    const int w = (int)(wave % wn), v = (int)(wave / wn);
+    const int64_t g = (int64_t)w * 64 + lane;
+    const uint64_t x = g < n ? rows[g * wm + v] : 0ull;
+    uint64_t mine = 0;
+#pragma unroll 8
+    for (int t = 0; t < 64; ++t) {
+        uint64_t b = __ballot((x >> t) & 1ull);
+        if (lane == t) mine = b;
+    }
+    const int j = 64 * v + lane;
+    if (j < m) cols[(uint64_t)j * wn + w] = mine;
+}
+
+// Root concept: extent = every object, intent = AND of all rows (page 4,
+// section 1.2), cursor -1.  The intent is filled with all attributes here and
+// narrowed by k_root_and.
+__global__ void k_root_init(uint64_t *intents, int32_t *cursor, uint64_t *loff, uint32_t *objs,
+                            int n, int wm, uint64_t tail_m)
+{
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < (uint64_t)n) objs[i] = (uint32_t)i;
+    if (i < (uint64_t)wm) intents[i] = (i == (uint64_t)wm - 1) ? tail_m : ~0ull;
+    if (i == 0) {
+        cursor[0] = -1;
+        loff[0] = 0;
+        loff[1] = (uint64_t)n;
+    }
+}
+
+__global__ void __launch_bounds__(kBlock) k_root_and(const uint64_t *__restrict__ rows, uint64_t *intent0, int n, int wm)
+{
+    __shared__ uint64_t s_red[kWavesPerBlock];
+    const int u = blockIdx.y;
+    uint64_t acc = ~0ull;
+    for (uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; g < (uint64_t)n;
+         g += (uint64_t)gridDim.x * blockDim.x)
+        acc &= rows[g * wm + u];
+    acc = wave_and(acc);
+    if (lane_id() == 0) s_red[threadIdx.x / kWave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t r = ~0ull;
+        for (int w = 0; w < kWavesPerBlock; ++w) r &= s_red[w];
+        if (r != ~0ull) atomicAnd((unsigned long long *)&intent0[u], (unsigned long long)r);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// per-level kernels
+
+// One thread per parent: candidate count (tests), item pairs, big-parent list,
+// and zeroed outputs for the test kernels.
+__global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
+{
+    __shared__ uint64_t s_red[4][kWavesPerBlock];
+    const uint64_t p = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t tests = 0, pairs = 0;
+    uint64_t small_objs = 0, big_scan = 0;
+    if (p < A.P) {
+        const uint64_t c = A.lo + p;
+        const int y = A.cursor[c];
+        for (int u = 0; u < A.wm; ++u) {
+            uint64_t cand = ~A.intents[c * A.wm + u] & above_mask(y, u);
+            if (u == A.wm - 1) cand &= A.tail_m;
+            tests += __popcll(cand);
+            A.pass[p * A.wm + u] = 0;
+        }
+        pairs = (uint32_t)(A.m - 1 - y);
+        const uint64_t a = A.loff[c + 1] - A.loff[c];
+        if (a > (uint64_t)kSmallMax) {
+            uint64_t pos = atomicAdd((unsigned long long *)&A.counters[CNT_BIG], 1ull);
+            A.big_idx[pos] = (uint32_t)p;
+            A.big_n[pos] = tests;
+            big_scan = a * tests;
+        } else {
+            small_objs = a;
+        }
+        A.nchild[p] = 0;
+        A.nobj[p] = 0;
+    }
+    uint64_t v[4] = {tests, pairs, small_objs, big_scan};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int s = 32; s > 0; s >>= 1) v[i] += __shfl_xor(v[i], s);
+    if (lane_id() == 0)
+        for (int i = 0; i < 4; ++i) s_red[i][threadIdx.x / kWave] = v[i];
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        uint64_t sum = 0;
+        for (int w = 0; w < kWavesPerBlock; ++w) sum += s_red[threadIdx.x][w];
+        const int slot[4] = {CNT_TESTS, CNT_PAIRS, CNT_SMALL_OBJS, CNT_BIG_SCAN};
+        if (sum) atomicAdd((unsigned long long *)&A.counters[slot[threadIdx.x]], (unsigned long long)sum);
+    }
+}
+
+// Closure tests of one parent (A, B, y) with |A| <= 64, one wavefront.
+//
+// Lane i stages the row of the i-th object of A in LDS.  For a candidate j
+// (j > y, j not in B) let c_j be the objects of A having j, as a bitmask over
+// the staged rows: C = A AND col[j] restricted to A.  Then D = C' is the AND of
+// their rows and the canonical test asks that D adds no attribute below j to
+// B (page 1, section 4.3: bits 0..j-1 compared, bit j excluded).
+//
+// Candidates split in two kinds:
+//   * j carried by some object of A (the set U): c_j is non-empty and is
+//     tested in full, one lane per candidate;
+//   * j carried by no object of A: C is empty, D = M, so the test passes only
+//     when every attribute below j is in B, i.e. j is the first attribute not
+//     in B.  That single candidate (if above y) yields the bottom concept.
+// Attribute-saturation pruning (page 1, section 2.3) is the j-in-B skip: with
+// B closed, A inside col[j] holds exactly when j is in B.
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_local_test(LevelArgs A)
+{
+    __shared__ uint64_t s_rows[kWavesPerBlock][kSmallMax * WMC];
+    __shared__ uint64_t s_pm[kWavesPerBlock][WMC];
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    const int wm = words_of<WMC>(A.wm);
+    uint64_t *R = s_rows[wv];
+    uint64_t *PM = s_pm[wv];
+    for (uint64_t p = (uint64_t)blockIdx.x * kWavesPerBlock + wv; p < A.P;
+         p += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t c0 = A.lo + p;
+        const uint64_t o0 = A.loff[c0];
+        const uint64_t a64 = A.loff[c0 + 1] - o0;
+        if (a64 > (uint64_t)kSmallMax) continue;
+        const int a = (int)a64;
+        const int y = A.cursor[c0];
+        uint64_t Bx[WMC];  // B plus the padding bits past M
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            Bx[u] = ~0ull;
+            if (u < wm) {
+                Bx[u] = A.intents[c0 * A.wm + u];
+                if (u == wm - 1) Bx[u] |= ~A.tail_m;
+            }
+        }
+        if (lane < a) {
+            const uint64_t g = A.objs[o0 + lane];
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                if (u < wm) R[lane * WMC + u] = A.rows[g * A.wm + u];
+        }
+        if (lane < wm) PM[lane] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // U = attributes outside B carried by some object of A, above y.
+        uint64_t U[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) U[u] = 0;
+        for (int i = 0; i < a; ++i) {
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                if (u < wm) U[u] |= R[i * WMC + u];
+        }
+        int nU = 0;
+        int j0 = -1;  // first attribute not in B
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            if (u < wm) {
+                uint64_t nb = ~Bx[u];
+                if (j0 < 0 && nb) j0 = 64 * u + __ffsll((unsigned long long)nb) - 1;
+                U[u] &= nb & above_mask(y, u);
+                nU += __popcll(U[u]);
+            }
+        }
+        bool bottom = false;
+        if (j0 > y) {
+            bottom = true;
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                if (u == (j0 >> 6) && ((U[u] >> (j0 & 63)) & 1ull)) bottom = false;
+        }
+        uint32_t nch = bottom ? 1u : 0u, nob = 0;
+        if (bottom && lane == 0) PM[j0 >> 6] |= 1ull << (j0 & 63);
+
+        for (int r = 0; r < nU; r += kWave) {
+            const int k = r + lane;
+            const bool active = k < nU;
+            const int j = active ? select_words<WMC>(U, wm, k) : 0;
+            const int wj = j >> 6, bj = j & 63;
+            uint64_t cj = 0;
+            for (int i = 0; i < a; ++i) cj |= ((R[i * WMC + wj] >> bj) & 1ull) << i;
+            uint64_t Dn[WMC];  // attributes outside B shared by the objects of c_j
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) Dn[u] = ~Bx[u];
+            uint64_t cc = active ? cj : 0ull;
+            while (cc) {
+                const int i = __ffsll((unsigned long long)cc) - 1;
+                cc &= cc - 1ull;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm && u <= wj) Dn[u] &= R[i * WMC + u];
+            }
+            uint64_t bad = 0;
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) {
+                if (u < wj) bad |= Dn[u];
+                else if (u == wj) bad |= Dn[u] & below_mask(bj);
+            }
+            const bool pass = active && bad == 0;
+            const uint64_t bal = __ballot(pass);
+            nch += (uint32_t)__popcll(bal);
+            nob += wave_sum(pass ? (uint32_t)__popcll(cj) : 0u);
+            if (pass) atomicOr((unsigned long long *)&PM[wj], (unsigned long long)(1ull << bj));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < wm) A.pass[p * A.wm + lane] = PM[lane];
+        if (lane == 0) {
+            A.nchild[p] = nch;
+            A.nobj[p] = nob;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Map a big test index t to (big slot bi, parent p, candidate rank k).
+__device__ __forceinline__ bool big_locate(const LevelArgs &A, uint64_t t, uint64_t nbig, uint64_t &bi,
+                                           uint64_t &p, int &k)
+{
+    // largest bi with big_off[bi] <= t
+    uint64_t lo = 0, hi = nbig;  // big_off[nbig] = total > t
+    while (hi - lo > 1) {
+        uint64_t mid = (lo + hi) >> 1;
+        if (A.big_off[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    bi = lo;
+    p = A.big_idx[bi];
+    k = (int)(t - A.big_off[bi]);
+    return true;
+}
+
+// Closure tests of parents with more than 64 objects: one wavefront per
+// (parent, candidate j).  The extent list is read 64 objects at a time; an
+// object is in C when its bit in col[j] is set, and its row is ANDed into the
+// lane's partial D (page 1, section 4.2: set bits of the extent walked, rows
+// ANDed, then a wavefront AND-reduction).
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_big_test(LevelArgs A)
+{
+    const int lane = lane_id();
+    const int wm = words_of<WMC>(A.wm);
+    const uint64_t nbig = A.counters[CNT_BIG];
+    const uint64_t tbig = A.big_off[nbig];
+    if (tbig > A.bt_cap) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) A.counters[CNT_OVERFLOW] = 1;
+        return;
+    }
+    for (uint64_t t = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < tbig;
+         t += (uint64_t)gridDim.x * kWavesPerBlock) {
+        uint64_t bi, p;
+        int k;
+        big_locate(A, t, nbig, bi, p, k);
+        const uint64_t c0 = A.lo + p;
+        const int y = A.cursor[c0];
+        uint64_t Bx[WMC], cand[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            Bx[u] = ~0ull;
+            cand[u] = 0;
+            if (u < wm) {
+                Bx[u] = A.intents[c0 * A.wm + u];
+                if (u == wm - 1) Bx[u] |= ~A.tail_m;
+                cand[u] = ~Bx[u] & above_mask(y, u);
+            }
+        }
+        const int j = select_words<WMC>(cand, wm, k);
+        const int wj = j >> 6, bj = j & 63;
+        const uint64_t o0 = A.loff[c0], o1 = A.loff[c0 + 1];
+        const uint64_t *col = A.cols + (uint64_t)j * A.wn;
+        uint64_t D[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
+        uint32_t cnt = 0;
+        for (uint64_t o = o0; o < o1; o += kWave) {
+            bool in = false;
+            uint32_t g = 0;
+            if (o + lane < o1) {
+                g = A.objs[o + lane];
+                in = (col[g >> 6] >> (g & 63)) & 1ull;
+            }
+            cnt += (uint32_t)__popcll(__ballot(in));
+            if (in) {
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm) D[u] &= A.rows[(uint64_t)g * A.wm + u];
+            }
+        }
+        uint64_t bad = 0;
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            if (u < wm) {
+                uint64_t d = wave_and(D[u]);
+                uint64_t extra = d & ~Bx[u];
+                if (u < wj) bad |= extra;
+                else if (u == wj) bad |= extra & below_mask(bj);
+            }
+        }
+        const bool pass = bad == 0;
+        if (lane == 0) {
+            A.bt_size[t] = pass ? cnt : 0u;
+            if (pass) {
+                atomicOr((unsigned long long *)&A.pass[p * A.wm + wj], (unsigned long long)(1ull << bj));
+                atomicAdd(&A.nchild[p], 1u);
+                atomicAdd(&A.nobj[p], cnt);
+            }
+        }
+    }
+}
+
+// Children of parents with <= 64 objects, one wavefront per parent, one lane
+// per child: recompute c_j for the passing attributes, D = AND of their rows
+// (all of M when c_j is empty), write intent, cursor and extent list at the
+// offsets the scans gave.
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
+{
+    __shared__ uint64_t s_rows[kWavesPerBlock][kSmallMax * WMC];
+    __shared__ uint32_t s_obj[kWavesPerBlock][kSmallMax];
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    const int wm = words_of<WMC>(A.wm);
+    uint64_t *R = s_rows[wv];
+    uint32_t *G = s_obj[wv];
+    for (uint64_t p = (uint64_t)blockIdx.x * kWavesPerBlock + wv; p < A.P;
+         p += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint32_t nch = A.nchild[p];
+        if (nch == 0) continue;
+        const uint64_t c0 = A.lo + p;
+        const uint64_t o0 = A.loff[c0];
+        const uint64_t a64 = A.loff[c0 + 1] - o0;
+        if (a64 > (uint64_t)kSmallMax) continue;
+        const int a = (int)a64;
+        uint64_t pm[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) pm[u] = (u < wm) ? A.pass[p * A.wm + u] : 0ull;
+        if (lane < a) {
+            const uint32_t g = A.objs[o0 + lane];
+            G[lane] = g;
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                if (u < wm) R[lane * WMC + u] = A.rows[(uint64_t)g * A.wm + u];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint64_t cb = A.child_lo + A.cbase[p];
+        uint64_t run = A.child_obj_lo + A.obase[p];
+        for (uint32_t r = 0; r < nch; r += kWave) {
+            const uint32_t k = r + lane;
+            const bool active = k < nch;
+            const int j = active ? select_words<WMC>(pm, wm, (int)k) : 0;
+            const int wj = j >> 6, bj = j & 63;
+            uint64_t cj = 0;
+            if (active)
+                for (int i = 0; i < a; ++i) cj |= ((R[i * WMC + wj] >> bj) & 1ull) << i;
+            uint64_t D[WMC];
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) D[u] = (u == wm - 1) ? A.tail_m : ~0ull;
+            uint64_t cc = cj;
+            while (cc) {
+                const int i = __ffsll((unsigned long long)cc) - 1;
+                cc &= cc - 1ull;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm) D[u] &= R[i * WMC + u];
+            }
+            const uint32_t sz = active ? (uint32_t)__popcll(cj) : 0u;
+            const uint64_t o = run + wave_excl_scan(sz);
+            run += wave_sum(sz);
+            if (active) {
+                const uint64_t child = cb + k;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm) A.intents[child * A.wm + u] = D[u];
+                A.cursor[child] = j;
+                A.loff[child] = o;
+                A.loff[child + 1] = o + sz;
+                uint64_t q = o;
+                cc = cj;
+                while (cc) {
+                    const int i = __ffsll((unsigned long long)cc) - 1;
+                    cc &= cc - 1ull;
+                    A.objs[q++] = G[i];
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Children of parents with more than 64 objects: one wavefront per big test,
+// only the passing ones do work.  The child's rank among its siblings is the
+// number of passing attributes below j; its list offset comes from the scan
+// of the passing tests' |C|.
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_big_write(LevelArgs A)
+{
+    const int lane = lane_id();
+    const int wm = words_of<WMC>(A.wm);
+    const uint64_t nbig = A.counters[CNT_BIG];
+    const uint64_t tbig = A.big_off[nbig];
+    if (tbig > A.bt_cap) return;
+    for (uint64_t t = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < tbig;
+         t += (uint64_t)gridDim.x * kWavesPerBlock) {
+        uint64_t bi, p;
+        int k;
+        big_locate(A, t, nbig, bi, p, k);
+        const uint64_t c0 = A.lo + p;
+        const int y = A.cursor[c0];
+        uint64_t cand[WMC], pm[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            cand[u] = 0;
+            pm[u] = 0;
+            if (u < wm) {
+                uint64_t bx = A.intents[c0 * A.wm + u];
+                if (u == wm - 1) bx |= ~A.tail_m;
+                cand[u] = ~bx & above_mask(y, u);
+                pm[u] = A.pass[p * A.wm + u];
+            }
+        }
+        const int j = select_words<WMC>(cand, wm, k);
+        const int wj = j >> 6, bj = j & 63;
+        bool passed = false;
+        int rank = 0;
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            if (u < wj) rank += __popcll(pm[u]);
+            else if (u == wj) {
+                rank += __popcll(pm[u] & below_mask(bj));
+                passed = (pm[u] >> bj) & 1ull;
+            }
+        }
+        if (!passed) continue;
+        const uint64_t child = A.child_lo + A.cbase[p] + (uint64_t)rank;
+        const uint64_t obeg = A.child_obj_lo + A.obase[p] + (A.bt_sscan[t] - A.bt_sscan[A.big_off[bi]]);
+        const uint64_t o0 = A.loff[c0], o1 = A.loff[c0 + 1];
+        const uint64_t *col = A.cols + (uint64_t)j * A.wn;
+        uint64_t D[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
+        uint64_t q = obeg;
+        for (uint64_t o = o0; o < o1; o += kWave) {
+            bool in = false;
+            uint32_t g = 0;
+            if (o + lane < o1) {
+                g = A.objs[o + lane];
+                in = (col[g >> 6] >> (g & 63)) & 1ull;
+            }
+            const uint64_t bal = __ballot(in);
+            if (in) {
+                A.objs[q + __popcll(bal & below_mask(lane))] = g;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm) D[u] &= A.rows[(uint64_t)g * A.wm + u];
+            }
+            q += __popcll(bal);
+        }
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            if (u < wm) {
+                uint64_t d = wave_and(D[u]);
+                if (u == wm - 1) d &= A.tail_m;
+                if (lane == 0) A.intents[child * A.wm + u] = d;
+            }
+        }
+        if (lane == 0) {
+            A.cursor[child] = j;
+            A.loff[child] = obeg;
+            A.loff[child + 1] = q;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// exclusive scan of one or two u32 arrays into u64 offsets, n read from the
+// device (n_dev, clamped to n_cap) or given by the host (n_dev == nullptr).
+// out[n] receives the total; *tot (optional) too.
+
+__device__ __forceinline__ uint64_t scan_count(const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap)
+{
+    uint64_t n = n_dev ? *n_dev : n_host;
+    return n < n_cap ? n : n_cap;
+}
+
+__global__ void __launch_bounds__(kBlock) k_scan_up(const uint32_t *__restrict__ a, const uint32_t *__restrict__ b,
+                                                     const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
+                                                     uint64_t *part)
+{
+    __shared__ uint64_t s_red[2][kWavesPerBlock];
+    const uint64_t n = scan_count(n_dev, n_host, n_cap);
+    const uint64_t per = (n + gridDim.x - 1) / gridDim.x;
+    const uint64_t s = (uint64_t)blockIdx.x * per;
+    const uint64_t e = s + per < n ? s + per : n;
+    uint64_t sa = 0, sb = 0;
+    for (uint64_t i = s + threadIdx.x; i < e; i += blockDim.x) {
+        sa += a[i];
+        if (b) sb += b[i];
+    }
+#pragma unroll
+    for (int k = 32; k > 0; k >>= 1) {
+        sa += __shfl_xor(sa, k);
+        sb += __shfl_xor(sb, k);
+    }
+    if (lane_id() == 0) {
+        s_red[0][threadIdx.x / kWave] = sa;
+        s_red[1][threadIdx.x / kWave] = sb;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t ta = 0, tb = 0;
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+            ta += s_red[0][w];
+            tb += s_red[1][w];
+        }
+        part[blockIdx.x] = ta;
+        part[kScanBlocks + blockIdx.x] = tb;
+    }
+}
+
+// One block of kScanBlocks threads: exclusive scan of the block partials.
+__global__ void __launch_bounds__(kScanBlocks) k_scan_mid(uint64_t *part, int nblocks, const uint64_t *n_dev,
+                                                          uint64_t n_host, uint64_t n_cap, uint64_t *out_a,
+                                                          uint64_t *out_b, uint64_t *tot_a, uint64_t *tot_b)
+{
+    __shared__ uint64_t s_w[2][kScanBlocks / kWave];
+    const int t = threadIdx.x, lane = lane_id(), wv = t / kWave;
+    uint64_t va = t < nblocks ? part[t] : 0, vb = t < nblocks ? part[kScanBlocks + t] : 0;
+    uint64_t xa = va, xb = vb;
+#pragma unroll
+    for (int s = 1; s < kWave; s <<= 1) {
+        uint64_t ya = __shfl_up(xa, s), yb = __shfl_up(xb, s);
+        if (lane >= s) {
+            xa += ya;
+            xb += yb;
+        }
+    }
+    if (lane == kWave - 1) {
+        s_w[0][wv] = xa;
+        s_w[1][wv] = xb;
+    }
+    __syncthreads();
+    uint64_t ba = 0, bb = 0, ta = 0, tb = 0;
+    for (int w = 0; w < kScanBlocks / kWave; ++w) {
+        if (w < wv) {
+            ba += s_w[0][w];
+            bb += s_w[1][w];
+        }
+        ta += s_w[0][w];
+        tb += s_w[1][w];
+    }
+    if (t < nblocks) {
+        part[t] = ba + xa - va;
+        part[kScanBlocks + t] = bb + xb - vb;
+    }
+    if (t == 0) {
+        const uint64_t n = scan_count(n_dev, n_host, n_cap);
+        out_a[n] = ta;
+        if (out_b) out_b[n] = tb;
+        if (tot_a) *tot_a = ta;
+        if (tot_b) *tot_b = tb;
+    }
+}
+
+__global__ void __launch_bounds__(kBlock) k_scan_down(const uint32_t *__restrict__ a, const uint32_t *__restrict__ b,
+                                                       const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
+                                                       const uint64_t *part, uint64_t *out_a, uint64_t *out_b)
+{
+    __shared__ uint64_t s_wave[kWavesPerBlock];
+    const uint64_t n = scan_count(n_dev, n_host, n_cap);
+    const uint64_t per = (n + gridDim.x - 1) / gridDim.x;
+    const uint64_t s = (uint64_t)blockIdx.x * per;
+    const uint64_t e = s + per < n ? s + per : n;
+    uint64_t carry_a = part[blockIdx.x], carry_b = part[kScanBlocks + blockIdx.x];
+    for (uint64_t base = s; base < e; base += blockDim.x) {
+        const uint64_t i = base + threadIdx.x;
+        const bool ok = i < e;
+        uint64_t tot;
+        const uint64_t xa = block_excl_scan(ok ? (uint64_t)a[i] : 0ull, s_wave, tot);
+        if (ok) out_a[i] = carry_a + xa;
+        carry_a += tot;
+        if (b) {
+            const uint64_t xb = block_excl_scan(ok ? (uint64_t)b[i] : 0ull, s_wave, tot);
+            if (ok) out_b[i] = carry_b + xb;
+            carry_b += tot;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// intent sort: LSD radix sort of a permutation, one 64-bit intent word at a
+// time from the last word to word 0, 8-bit digits, stable passes.
+
+__global__ void k_iota(uint32_t *idx, uint64_t n)
+{
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) idx[i] = (uint32_t)i;
+}
+
+// keys[i] = word u of the intent idx[i]; OR and AND of all keys into red[0..1].
+__global__ void __launch_bounds__(kBlock) k_gather_key(const uint64_t *__restrict__ intents, int wm, int u,
+                                                        const uint32_t *__restrict__ idx, uint64_t *__restrict__ keys,
+                                                        uint64_t n, uint64_t *red)
+{
+    __shared__ uint64_t s_or[kWavesPerBlock], s_and[kWavesPerBlock];
+    uint64_t vor = 0, vand = ~0ull;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t k = intents[(uint64_t)idx[i] * wm + u];
+        keys[i] = k;
+        vor |= k;
+        vand &= k;
+    }
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) {
+        vor |= __shfl_xor(vor, s);
+        vand &= __shfl_xor(vand, s);
+    }
+    if (lane_id() == 0) {
+        s_or[threadIdx.x / kWave] = vor;
+        s_and[threadIdx.x / kWave] = vand;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kWavesPerBlock; ++w) {
+            vor |= s_or[w];
+            vand &= s_and[w];
+        }
+        vor |= s_or[0];
+        vand &= s_and[0];
+        atomicOr((unsigned long long *)&red[0], (unsigned long long)vor);
+        atomicAnd((unsigned long long *)&red[1], (unsigned long long)vand);
+    }
+}
+
+// Digit histogram of one tile: hist[d * ntiles + tile].
+__global__ void __launch_bounds__(kBlock) k_radix_hist(const uint64_t *__restrict__ keys, uint64_t n, int shift,
+                                                        uint32_t *__restrict__ hist, uint64_t ntiles)
+{
+    __shared__ uint32_t s_h[256];
+    s_h[threadIdx.x] = 0;
+    __syncthreads();
+    const uint64_t base = (uint64_t)blockIdx.x * kSortTile;
+    for (int it = 0; it < kSortTile / kBlock; ++it) {
+        const uint64_t i = base + (uint64_t)it * kBlock + threadIdx.x;
+        if (i < n) atomicAdd(&s_h[(keys[i] >> shift) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    hist[(uint64_t)threadIdx.x * ntiles + blockIdx.x] = s_h[threadIdx.x];
+}
+
+// Stable scatter of one tile.  Items are taken in order, 256 at a time; the
+// rank of an item among equal digits of its wavefront comes from eight
+// ballots (lanes whose digit matches on every bit), the wavefronts of the
+// block are ordered through LDS counters.
+__global__ void __launch_bounds__(kBlock) k_radix_scatter(const uint64_t *__restrict__ keys_in,
+                                                           const uint32_t *__restrict__ idx_in, uint64_t n, int shift,
+                                                           const uint64_t *__restrict__ hist_off, uint64_t ntiles,
+                                                           uint64_t *__restrict__ keys_out,
+                                                           uint32_t *__restrict__ idx_out)
+{
+    __shared__ uint32_t s_run[256];
+    __shared__ uint32_t s_wc[kWavesPerBlock][256];
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    s_run[threadIdx.x] = 0;
+    for (int w = 0; w < kWavesPerBlock; ++w) s_wc[w][threadIdx.x] = 0;
+    __syncthreads();
+    const uint64_t gbase = hist_off[(uint64_t)threadIdx.x * ntiles + blockIdx.x];
+    __shared__ uint64_t s_gbase[256];
+    s_gbase[threadIdx.x] = gbase;
+    __syncthreads();
+    const uint64_t base = (uint64_t)blockIdx.x * kSortTile;
+    for (int it = 0; it < kSortTile / kBlock; ++it) {
+        const uint64_t i = base + (uint64_t)it * kBlock + threadIdx.x;
+        const bool ok = i < n;
+        uint64_t key = 0;
+        uint32_t id = 0;
+        if (ok) {
+            key = keys_in[i];
+            id = idx_in[i];
+        }
+        const uint32_t d = (uint32_t)((key >> shift) & 0xFFu);
+        uint64_t peers = __ballot(ok);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const bool v = (d >> bit) & 1u;
+            const uint64_t bal = __ballot(v);
+            peers &= v ? bal : ~bal;
+        }
+        const uint32_t rank = (uint32_t)__popcll(peers & below_mask(lane));
+        const bool last = ok && ((peers >> lane) >> 1) == 0ull;  // highest lane of the group
+        if (last) s_wc[wv][d] = rank + 1;
+        __syncthreads();
+        if (ok) {
+            uint32_t before = s_run[d];
+            for (int w = 0; w < wv; ++w) before += s_wc[w][d];
+            const uint64_t pos = s_gbase[d] + before + rank;
+            keys_out[pos] = key;
+            idx_out[pos] = id;
+        }
+        __syncthreads();
+        {
+            uint32_t add = 0;
+            for (int w = 0; w < kWavesPerBlock; ++w) {
+                add += s_wc[w][threadIdx.x];
+                s_wc[w][threadIdx.x] = 0;
+            }
+            s_run[threadIdx.x] += add;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// output: sorted intents and extent bitmaps into the caller's buffers.  One
+// wavefront per output row; the extent is assembled in LDS tile by tile from
+// its sorted object list and streamed out with coalesced stores.
+
+__global__ void __launch_bounds__(kBlock) k_output(const uint64_t *__restrict__ intents,
+                                                    const uint64_t *__restrict__ loff,
+                                                    const uint32_t *__restrict__ objs,
+                                                    const uint32_t *__restrict__ perm, uint64_t K, int wm, int wn,
+                                                    uint64_t *__restrict__ intents_out,
+                                                    uint64_t *__restrict__ extents_out)
+{
+    __shared__ uint64_t s_tile[kWavesPerBlock][kOutTileWords];
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    uint64_t *T = s_tile[wv];
+    for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + wv; i < K; i += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t src = perm[i];
+        for (int u = lane; u < wm; u += kWave) intents_out[i * wm + u] = intents[src * wm + u];
+        if (!extents_out) continue;
+        uint64_t o = loff[src];
+        const uint64_t o1 = loff[src + 1];
+        uint64_t *row = extents_out + i * (uint64_t)wn;
+        for (int w0 = 0; w0 < wn; w0 += kOutTileWords) {
+            const int tw = (wn - w0) < kOutTileWords ? (wn - w0) : kOutTileWords;
+            for (int w = lane; w < tw; w += kWave) T[w] = 0;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const uint64_t gend = (uint64_t)(w0 + tw) * 64;
+            while (o < o1) {
+                bool in = false;
+                uint32_t g = 0;
+                if (o + lane < o1) {
+                    g = objs[o + lane];
+                    in = (uint64_t)g < gend;
+                }
+                if (in) atomicOr((unsigned long long *)&T[(g >> 6) - w0], (unsigned long long)(1ull << (g & 63)));
+                const uint64_t bal = __ballot(in);
+                o += __popcll(bal);
+                if (bal != ~0ull) break;  // the list is sorted: the rest lies past this tile
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int w = lane; w < tw; w += kWave) __builtin_nontemporal_store(T[w], &row[w0 + w]);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+}  // namespace fcbo

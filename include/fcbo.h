@@ -1,0 +1,157 @@
+/*
+ * fcbo.h - C ABI of the MI355X formal-concept enumeration library (libfcbo.so).
+ *
+ * The library lists every formal concept (extent, intent) of a 0/1 formal
+ * context with Close-by-One: starting from the root (all objects, the
+ * attributes they share) every concept (A, B) with cursor y tries each
+ * attribute j > y that is not in B, forms C = A AND col[j] and D = C', and keeps
+ * (C, D) with cursor j iff D and B agree on the attributes below j.
+ *   - concept, derivation and closure: page "hnwysp.cn/news/97538", sections
+ *     1.1-1.2, and page "hotelren.com/news/5603750", section 1.1;
+ *   - the CbO step, canonical test and attribute-saturation skip: page 1,
+ *     sections 2.1-2.3 and 4.3; page 4, sections 1.2 and 3.2;
+ *   - the two bitmap layouts kept on the device: page 1 section 3.1, page 4
+ *     section 2.3;
+ *   - the sorted, deterministic output: page 1 section 6.2.
+ *
+ * Bit layout everywhere: element e of a set is bit (e & 63) of 64-bit word
+ * (e >> 6), least significant bit first.  Bits past the last object or the
+ * last attribute are zero in everything the library writes.
+ *
+ * Output order: concepts are sorted ascending by their intent read as a tuple
+ * of unsigned 64-bit words, word 0 compared first.  Intents are pairwise
+ * distinct, so the order is total and the output is byte-for-byte unique.
+ *
+ * Errors are reported only by return code; no call aborts or throws.  A HIP
+ * failure maps to FCBO_ERR_DEVICE (FCBO_ERR_OUT_OF_MEMORY for allocation) and
+ * leaves the context safe to destroy.  A context must not be used from two
+ * host threads at once.
+ */
+#ifndef FCBO_H
+#define FCBO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fcbo_context fcbo_context; /* opaque, owned by the library */
+
+enum {
+    FCBO_OK = 0,
+    FCBO_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, bad flag */
+    FCBO_ERR_OUT_OF_MEMORY = -2,    /* a device allocation failed */
+    FCBO_ERR_DEVICE = -3,           /* any other HIP runtime failure */
+    FCBO_ERR_CAPACITY = -4          /* output buffers hold fewer rows than concepts */
+};
+
+/* fcbo_context_create flags */
+#define FCBO_ROWS_ON_DEVICE 1u /* rows is a device pointer (else host memory) */
+#define FCBO_TINY_BUFFERS 2u   /* start every device buffer at its minimum size, so growth
+                                  and the level redo run on any input (for tests) */
+
+/* fcbo_enumerate flags */
+#define FCBO_REUSE_RESULT 1u /* reuse the concepts of the previous call if any */
+#define FCBO_PROFILE 2u      /* time every kernel with HIP events (fills kernel_ms) */
+
+/* Kernel classes reported in fcbo_stats.kernel_ms / kernel_launches. */
+enum {
+    FCBO_K_COUNT = 0,       /* per-parent candidate count, big-parent list */
+    FCBO_K_TEST_LOCAL = 1,  /* closure tests of parents with <= 64 objects */
+    FCBO_K_TEST_BIG = 2,    /* closure tests of parents with > 64 objects */
+    FCBO_K_SCAN = 3,        /* exclusive scans (children, objects, big tests) */
+    FCBO_K_WRITE_LOCAL = 4, /* child write, small parents */
+    FCBO_K_WRITE_BIG = 5,   /* child write, big parents */
+    FCBO_K_SORT = 6,        /* intent radix sort */
+    FCBO_K_OUTPUT = 7,      /* sorted intents + extent bitmaps to the caller */
+    FCBO_K_NUM_CLASSES = 8
+};
+
+typedef struct {
+    uint64_t n_concepts;    /* K */
+    uint64_t closure_tests; /* (parent, j) with j > cursor and j not in B */
+    uint64_t item_pairs;    /* (parent, j) with j > cursor */
+    uint64_t n_levels;      /* levels of the CbO tree, root level included */
+    uint64_t sum_child_objects; /* sum of |C| over all concepts except the root */
+    uint64_t output_bytes;  /* bytes written to the caller's buffers */
+    uint64_t local_parents; /* parents with <= 64 objects (row-local test kernel) */
+    uint64_t local_parent_objects; /* objects in their extents (rows staged) */
+    uint64_t big_parents;   /* parents with > 64 objects */
+    uint64_t big_tests;     /* closure tests made by them */
+    uint64_t big_scanned_objects; /* extent-list entries read by those tests */
+    uint64_t sort_passes;   /* radix passes run by the last sort */
+    double enumerate_ms;    /* whole call on the device stream (HIP events) */
+    double levels_ms;       /* enumeration part (root to last level) */
+    double sort_ms;         /* intent sort */
+    double output_ms;       /* writing the caller's buffers */
+    double kernel_ms[FCBO_K_NUM_CLASSES];       /* with FCBO_PROFILE only */
+    uint64_t kernel_launches[FCBO_K_NUM_CLASSES];
+} fcbo_stats;
+
+/*
+ * Build a context from the 0/1 row bitmap.
+ *   rows              row g (the attributes of object g) starts at
+ *                     rows + g * row_stride_words; host memory, or device
+ *                     memory on the current HIP device with FCBO_ROWS_ON_DEVICE.
+ *                     The library copies it; the caller keeps ownership.  Bits
+ *                     past n_attrs in the last word are ignored.
+ *   n_objects         N, 1 <= N <= 2^31 - 1
+ *   n_attrs           M, 1 <= M <= 4096
+ *   row_stride_words  >= ceil(M / 64)
+ *   hip_stream        hipStream_t for all device work, or NULL for the null stream
+ *   out               receives the context
+ * The device holds the rows (N x ceil(M/64) words) and their transpose, the
+ * columns (M x ceil(N/64) words, column j = objects having attribute j).
+ * Returns FCBO_OK or an error code; *out is NULL on error.
+ */
+int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs,
+                        int64_t row_stride_words, uint32_t flags, void *hip_stream,
+                        fcbo_context **out);
+
+/*
+ * Enumerate all concepts and write them, sorted by intent, to caller-owned
+ * device buffers on the context's device.
+ *   intents_out   K x ceil(M/64) words, row i = intent of concept i
+ *   extents_out   K x ceil(N/64) words in the same order, or NULL to skip
+ *   capacity      rows available in the output buffers
+ *   flags         FCBO_REUSE_RESULT, FCBO_PROFILE
+ *   n_concepts_out receives K (also on FCBO_ERR_CAPACITY)
+ *   stats_out     optional statistics, or NULL
+ * If intents_out is NULL or capacity < K the call returns FCBO_ERR_CAPACITY,
+ * stores K and writes nothing; the concepts stay in the context, so a second
+ * call with FCBO_REUSE_RESULT and large enough buffers only sorts and writes.
+ * The call returns after the stream has finished the work.
+ */
+int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_out,
+                   uint64_t capacity, uint32_t flags, uint64_t *n_concepts_out,
+                   fcbo_stats *stats_out);
+
+/*
+ * Per-level counts of the last enumeration: concepts generated on level k
+ * (level 0 is the root) and closure tests made by the concepts of level k.
+ * Copies min(n_levels, max_levels) entries; *n_levels_out gets n_levels.
+ * Either array may be NULL.  FCBO_ERR_INVALID_ARGUMENT if nothing was
+ * enumerated yet.
+ */
+int fcbo_level_counts(const fcbo_context *ctx, uint64_t *concepts_per_level,
+                      uint64_t *tests_per_level, uint64_t max_levels, uint64_t *n_levels_out);
+
+/*
+ * Copy the device column bitmap (M x ceil(N/64) words, column j = objects
+ * having attribute j) into a host buffer of at least that many words.  It is
+ * the transpose built by fcbo_context_create.
+ */
+int fcbo_copy_columns(const fcbo_context *ctx, uint64_t *host_cols, uint64_t capacity_words);
+
+/* Free the context and everything it owns.  NULL is allowed. */
+void fcbo_destroy(fcbo_context *ctx);
+
+/* Static text for an error code. */
+const char *fcbo_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FCBO_H */

@@ -1,0 +1,279 @@
+"""GPU parity: libfcbo against the CPU oracle, bit for bit.
+
+Every test calls the HIP path through the C ABI (closed_set_enumeration_amd
+marshals arguments only) and compares with oracle/ on the same seeded input:
+the concept count, the sorted intent array byte for byte, the extents, the
+closure-test and item-pair counts and the per-level counts.  All of it is
+integer work, so the bar is exact equality.
+"""
+
+import ctypes
+import hashlib
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.golden_io import read_fixture
+
+torch = pytest.importorskip("torch")
+import closed_set_enumeration_amd as fca  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def gpu_run(rows, m, extents=True, flags=0):
+    ctx = fca.Context(rows, m, flags=flags)
+    try:
+        res = ctx.enumerate(extents=extents)
+        torch.cuda.synchronize()
+        ints = res.intents.cpu().numpy().view(np.uint64)
+        exts = res.extents.cpu().numpy().view(np.uint64) if extents else None
+        conc, tests = ctx.level_counts()
+        return res, ints, exts, conc, tests
+    finally:
+        ctx.close()
+
+
+def assert_parity(cells, extents=True, flags=0):
+    cells = np.asarray(cells, dtype=bool)
+    rows = synth.pack_rows(cells)
+    m = cells.shape[1]
+    want = oracle.cbo(rows, m, keep_extents=extents)
+    res, ints, exts, conc, tests = gpu_run(rows, m, extents=extents, flags=flags)
+    assert res.n_concepts == want.n_concepts
+    assert ints.shape == want.intents.shape
+    assert np.array_equal(ints, want.intents)
+    if extents:
+        assert np.array_equal(exts, want.extents)
+    assert res.stats["closure_tests"] == want.tests
+    assert res.stats["item_pairs"] == want.pairs
+    assert res.stats["sum_child_objects"] == want.sum_c
+    assert [int(x) for x in conc] == [int(x) for x in want.level_concepts]
+    assert [int(x) for x in tests] == [int(x) for x in want.level_tests]
+    return res
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    fca.load_library()
+    torch.cuda.set_device(0)
+
+
+# --- worked examples and the small seeded contexts ---------------------------------
+
+@pytest.mark.parametrize("name", ["staircase4.txt", "two_blocks4.txt"])
+def test_hand_derived_examples(name):
+    cells, concepts, info = read_fixture(name)
+    res = assert_parity(cells)
+    assert res.n_concepts == info["concepts"]
+
+
+@pytest.mark.parametrize("name", ["ctx64x16", "ctx2000x64", "ctx10000x128"])
+@pytest.mark.parametrize("flags", [0, fca.FCBO_TINY_BUFFERS])
+def test_seeded_contexts(name, flags):
+    assert_parity(synth.make_config(name, packed=False), flags=flags)
+
+
+# --- edge shapes: word boundaries on both axes, ragged tails ---------------------------
+
+EDGE = [1, 63, 64, 65, 127, 128, 129]
+
+
+@pytest.mark.parametrize("n", EDGE)
+@pytest.mark.parametrize("m", EDGE)
+def test_edge_shapes(n, m):
+    density = min(0.4, 6.0 / m)
+    cells = synth.random_context(10007 * n + m, n, m, density)
+    assert_parity(cells)
+
+
+@pytest.mark.parametrize("n,m,d", [(40, 600, 0.01), (70, 1100, 0.004), (20, 4096, 0.001), (130, 520, 0.012)])
+def test_wide_attribute_sets(n, m, d):
+    # more than 8 intent words: the generic word-count kernels
+    assert_parity(synth.random_context(n * m, n, m, d))
+
+
+@pytest.mark.parametrize("n,m", [(65, 130), (130, 5), (1, 1), (300, 64)])
+def test_all_zero(n, m):
+    # the bottom ({}, M) comes from a parent with more than 64 objects when n > 64
+    res = assert_parity(synth.all_zero(n, m))
+    assert res.n_concepts == 2
+
+
+@pytest.mark.parametrize("n,m", [(129, 3), (1, 200), (64, 64)])
+def test_all_ones(n, m):
+    res = assert_parity(synth.all_ones(n, m))
+    assert res.n_concepts == 1
+
+
+@pytest.mark.parametrize("k", [65, 130])
+def test_diagonal(k):
+    res = assert_parity(synth.diagonal(k))
+    assert res.n_concepts == k + 2
+
+
+def test_contranominal_padded_multiword():
+    cells = synth.pad_with_full(synth.contranominal(12), extra_objects=118, extra_attrs=58)
+    res = assert_parity(cells)
+    assert res.n_concepts == 4096
+
+
+def test_contranominal_large():
+    # 2^16 concepts, every closure test passes
+    cells = synth.pad_with_full(synth.contranominal(16), extra_objects=60, extra_attrs=120)
+    res = assert_parity(cells, extents=True)
+    assert res.n_concepts == 65536
+    assert res.stats["closure_tests"] == 65535
+
+
+def test_big_parents_mixed_density():
+    # dense columns keep many parents above 64 objects for several levels
+    rng = np.random.default_rng(4242)
+    p = rng.uniform(0.02, 0.6, size=90)
+    cells = rng.random((700, 90)) < p[None, :]
+    assert_parity(cells, flags=fca.FCBO_TINY_BUFFERS)
+
+
+# --- interface behaviour ---------------------------------------------------------------
+
+def test_columns_are_the_transpose():
+    cells = synth.random_context(77, 200, 130, 0.1)
+    ctx = fca.Context(synth.pack_rows(cells), 130)
+    try:
+        cols = ctx.columns()
+    finally:
+        ctx.close()
+    assert np.array_equal(cols, synth.pack_rows(cells.T))
+
+
+def test_device_rows_and_strided_dirty_rows():
+    cells = synth.random_context(78, 150, 70, 0.12)
+    rows = synth.pack_rows(cells)
+    want = oracle.cbo(rows, 70)
+    # stride 3 words, junk in the padding word and in the bits past M
+    dirty = np.full((150, 3), np.uint64(0xDEADBEEFDEADBEEF), dtype=np.uint64)
+    dirty[:, :2] = rows
+    dirty[:, 1] |= np.uint64(~((1 << 6) - 1) & ((1 << 64) - 1))
+    res, ints, exts, _, _ = gpu_run(dirty, 70)
+    assert np.array_equal(ints, want.intents) and np.array_equal(exts, want.extents)
+    dev = torch.from_numpy(dirty.view(np.int64)).cuda()
+    res, ints, exts, _, _ = gpu_run(dev, 70)
+    assert np.array_equal(ints, want.intents) and np.array_equal(exts, want.extents)
+
+
+def test_run_twice_is_byte_identical():
+    rows = synth.make_config("ctx2000x64")
+    ctx = fca.Context(rows, 64)
+    try:
+        a = ctx.enumerate()
+        ai, ae = a.intents.clone(), a.extents.clone()
+        b = ctx.enumerate()
+        assert torch.equal(ai, b.intents) and torch.equal(ae, b.extents)
+    finally:
+        ctx.close()
+
+
+def test_capacity_error_and_reuse():
+    cells = synth.make_config("ctx64x16", packed=False)
+    rows = synth.pack_rows(cells)
+    want = oracle.cbo(rows, 16)
+    k = want.n_concepts
+    ctx = fca.Context(rows, 16)
+    try:
+        ints, exts = ctx.alloc_outputs(k, True)
+        ints.fill_(-7)
+        exts.fill_(-7)
+        small_i, small_e = ints[: k - 1], exts[: k - 1]
+        rc, k_seen, _ = ctx.enumerate_into(small_i, small_e)
+        assert rc == fca.FCBO_ERR_CAPACITY and k_seen == k
+        torch.cuda.synchronize()
+        assert bool((ints == -7).all()) and bool((exts == -7).all())
+        rc, k_seen, st = ctx.enumerate_into(ints, exts, fca.FCBO_REUSE_RESULT)
+        assert rc == fca.FCBO_OK and k_seen == k
+        got = ints.cpu().numpy().view(np.uint64)
+        assert np.array_equal(got, want.intents)
+        assert np.array_equal(exts.cpu().numpy().view(np.uint64), want.extents)
+        # intents only
+        rc, _, _ = ctx.enumerate_into(ints, None)
+        assert rc == fca.FCBO_OK
+        assert np.array_equal(ints.cpu().numpy().view(np.uint64), want.intents)
+    finally:
+        ctx.close()
+
+
+def test_invalid_arguments():
+    rows = synth.make_config("ctx64x16")
+    ptr = rows.ctypes.data
+    for n, m, stride, flags in [(0, 16, 1, 0), (64, 0, 1, 0), (64, 4097, 65, 0), (64, 130, 2, 0), (64, 16, 1, 8)]:
+        with pytest.raises(fca.FcboError) as e:
+            fca.fcbo_context_create(ptr, n, m, stride, flags, 0)
+        assert e.value.code == fca.FCBO_ERR_INVALID_ARGUMENT
+    h = fca.fcbo_context_create(ptr, 64, 16, 1, 0, torch.cuda.current_stream().cuda_stream)
+    try:
+        with pytest.raises(fca.FcboError):
+            fca.fcbo_enumerate(h, 0, 0, 0, 64)  # unknown flag
+        with pytest.raises(fca.FcboError):
+            fca.fcbo_level_counts(h)  # nothing enumerated yet
+    finally:
+        fca.fcbo_destroy(h)
+
+
+# --- full-size seeded workloads ----------------------------------------------------------
+
+def _popcount_rows(t, chunk=1 << 16):
+    lut = torch.tensor([bin(i).count("1") for i in range(256)], dtype=torch.int64, device=t.device)
+    total = 0
+    for s in range(0, t.shape[0], chunk):
+        total += int(lut[t[s:s + chunk].contiguous().view(torch.uint8).long()].sum())
+    return total
+
+
+def _sample_extents_match(cells, ints, exts_t, sample, seed):
+    n, m = cells.shape
+    ib = synth.unpack_rows(ints, m)
+    k = ints.shape[0]
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([[0, k - 1], rng.choice(k, size=min(sample, k), replace=False)]))
+    got = exts_t[torch.from_numpy(idx).to(exts_t.device)].cpu().numpy().view(np.uint64)
+    for r, i in enumerate(idx):
+        b = ib[i]
+        ext = cells[:, b].all(axis=1)  # B'
+        back = cells[ext].all(axis=0) if ext.any() else np.ones(m, dtype=bool)  # B''
+        assert np.array_equal(back, b), i
+        assert np.array_equal(synth.unpack_rows(got[r:r + 1], n)[0], ext), i
+
+
+def test_full_ctx50000x400_against_stored_oracle():
+    path = os.path.join(GOLDEN, "ctx50000x400.json")
+    if not os.path.exists(path):
+        pytest.skip("stored oracle values not generated")
+    g = json.load(open(path))
+    cells = synth.make_config("ctx50000x400", packed=False)
+    rows = synth.pack_rows(cells)
+    assert synth.rows_sha256(rows) == g["rows_sha256"]
+    ctx = fca.Context(rows, 400)
+    try:
+        res = ctx.enumerate(extents=True)
+        torch.cuda.synchronize()
+        ints = res.intents.cpu().numpy().view(np.uint64)
+        conc, tests = ctx.level_counts()
+        assert res.n_concepts == g["n_concepts"]
+        assert hashlib.sha256(np.ascontiguousarray(ints, dtype="<u8").tobytes()).hexdigest() == g["intents_sha256"]
+        assert res.stats["closure_tests"] == g["closure_tests"]
+        assert res.stats["item_pairs"] == g["item_pairs"]
+        assert res.stats["sum_child_objects"] == g["sum_c"]
+        assert [int(x) for x in conc] == g["level_concepts"]
+        assert [int(x) for x in tests] == g["level_tests"]
+        # every extent bit accounted for: |G| for the root plus |C| of every child
+        assert _popcount_rows(res.extents) == 50000 + g["sum_c"]
+        _sample_extents_match(cells, ints, res.extents, 1500, 4)
+    finally:
+        ctx.close()
