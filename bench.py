@@ -27,10 +27,16 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 def kernel_bytes(cls, st, wm, wn, n, k, extents):
     """Algorithmic bytes one step moves in a kernel class."""
     if cls == "test_local":
+        # per parent: intent, cursor, two list offsets in; pass mask, child and object counts out;
+        # per object of the extent: its list entry and its row
         return (st["local_parents"] * (8 * wm + 4 + 16 + 8 * wm + 8)
                 + st["local_parent_objects"] * (4 + 8 * wm))
+    if cls == "test_medium":
+        return (st["medium_parents"] * (4 + 8 * wm + 4 + 16 + 8 * wm + 8)
+                + st["medium_parent_objects"] * (4 + 8 * wm))
     if cls == "test_big":
-        return st["big_tests"] * (8 * wm + 4 + 16 + 4) + st["big_scanned_objects"] * (4 + 8)
+        # per test: task, parent index, intent, list offsets, result; per list entry read: entry and column word
+        return st["big_tests"] * (8 + 4 + 8 * wm + 16 + 4) + st["big_scanned_objects"] * (4 + 8)
     if cls == "output":
         reads = k * (4 + 8 * wm + 16) + (n + st["sum_child_objects"]) * 4
         writes = k * 8 * wm + (k * 8 * wn if extents else 0)
@@ -67,6 +73,8 @@ def main():
     ap.add_argument("--no-extents", action="store_true")
     ap.add_argument("--cpu-tests", type=int, default=8_000_000, help="closure-test budget of the CPU sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="run one device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
@@ -84,6 +92,15 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     fca.load_library()
+    if args.copy_probe_gib > 0:
+        nel = int(args.copy_probe_gib * (1 << 30)) // 8
+        src = torch.ones(nel, dtype=torch.int64, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy probe: %d bytes read, %d bytes written" % (nel * 8, nel * 8), file=sys.stderr, flush=True)
+        del src, dst
     n, m, _ = synth.CONFIGS[args.workload]
     rows = synth.make_config(args.workload)
     extents = not args.no_extents

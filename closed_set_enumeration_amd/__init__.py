@@ -31,7 +31,8 @@ FCBO_TINY_BUFFERS = 2
 FCBO_REUSE_RESULT = 1
 FCBO_PROFILE = 2
 
-KERNEL_CLASSES = ("count", "test_local", "test_big", "scan", "write_local", "write_big", "sort", "output")
+KERNEL_CLASSES = ("count", "test_local", "test_medium", "test_big", "scan", "write_local", "write_medium",
+                  "write_big", "sort", "output")
 
 EXPORTED = (
     "fcbo_context_create",
@@ -53,6 +54,8 @@ class FcboStats(ctypes.Structure):
         ("output_bytes", ctypes.c_uint64),
         ("local_parents", ctypes.c_uint64),
         ("local_parent_objects", ctypes.c_uint64),
+        ("medium_parents", ctypes.c_uint64),
+        ("medium_parent_objects", ctypes.c_uint64),
         ("big_parents", ctypes.c_uint64),
         ("big_tests", ctypes.c_uint64),
         ("big_scanned_objects", ctypes.c_uint64),

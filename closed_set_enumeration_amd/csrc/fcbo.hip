@@ -94,9 +94,10 @@ struct fcbo_context {
     uint64_t cap_pass = 0, cap_nch = 0, cap_nob = 0, cap_cb = 0, cap_ob = 0, cap_bi = 0, cap_bn = 0, cap_bo = 0;
     uint64_t *pass = nullptr, *cbase = nullptr, *obase = nullptr, *big_off = nullptr;
     uint32_t *nchild = nullptr, *nobj = nullptr, *big_idx = nullptr, *big_n = nullptr;
-    uint64_t cap_bt = 0, cap_bts = 0;
+    uint64_t cap_bt = 0, cap_bts = 0, cap_task = 0, cap_pl = 0, cap_med = 0;
     uint32_t *bt_size = nullptr;
-    uint64_t *bt_sscan = nullptr;
+    uint64_t *bt_sscan = nullptr, *tasks = nullptr, *plist = nullptr;
+    uint32_t *med_idx = nullptr;
     uint64_t *scan_part = nullptr;  // 2 x kScanBlocks
     uint64_t *counters = nullptr;   // CNT_N
     uint64_t *h_counters = nullptr; // pinned, CNT_N
@@ -114,7 +115,8 @@ struct fcbo_context {
     bool have_result = false;
     bool have_perm = false;
     uint64_t K = 0, tests = 0, pairs = 0, sum_c = 0;
-    uint64_t local_parents = 0, local_objs = 0, big_parents = 0, big_tests = 0, big_scan = 0, sort_passes = 0;
+    uint64_t local_parents = 0, local_objs = 0, med_parents = 0, med_objs = 0;
+    uint64_t big_parents = 0, big_tests = 0, big_scan = 0, sort_passes = 0;
     std::vector<uint64_t> lev_concepts, lev_tests;
 
     // profiling
@@ -153,7 +155,8 @@ struct fcbo_context {
         dfree(intents); dfree(cursor); dfree(loff); dfree(objs);
         dfree(pass); dfree(cbase); dfree(obase); dfree(big_off);
         dfree(nchild); dfree(nobj); dfree(big_idx); dfree(big_n);
-        dfree(bt_size); dfree(bt_sscan); dfree(scan_part); dfree(counters);
+        dfree(bt_size); dfree(bt_sscan); dfree(tasks); dfree(plist); dfree(med_idx);
+        dfree(scan_part); dfree(counters);
         dfree(keys_a); dfree(keys_b); dfree(idx_a); dfree(idx_b); dfree(hist); dfree(hist_off);
         dfree(sort_red);
         if (h_counters) (void)hipHostFree(h_counters);
@@ -171,7 +174,10 @@ struct fcbo_context {
         A.intents = intents; A.cursor = cursor; A.loff = loff; A.objs = objs;
         A.pass = pass; A.nchild = nchild; A.nobj = nobj; A.cbase = cbase; A.obase = obase;
         A.big_idx = big_idx; A.big_n = big_n; A.big_off = big_off;
-        A.bt_size = bt_size; A.bt_sscan = bt_sscan; A.bt_cap = std::min(cap_bt, cap_bts);
+        A.bt_size = bt_size; A.bt_sscan = bt_sscan; A.tasks = tasks; A.plist = plist;
+        A.bt_cap = std::min(std::min(cap_bt, cap_bts - 1), std::min(cap_task, cap_pl));
+        A.med_idx = med_idx;
+        A.med_max = wm <= 8 ? kWave * kMedChunks : kSmallMax;
         A.counters = counters;
         return A;
     }
@@ -204,10 +210,21 @@ template <int WMC>
 void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
 {
     const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kWavesPerBlock)));
+    const unsigned gm = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(1024, div_up(P, kWavesPerBlock)));
     hipEvent_t b = c->prof_begin();
-    hipLaunchKernelGGL(k_local_test<WMC>, dim3(gl), dim3(kBlock), 0, c->stream, A);
+    hipLaunchKernelGGL(k_big_tasks<WMC>, dim3(gm), dim3(kBlock), 0, c->stream, A);
+    CK_LAUNCH();
+    c->prof_end(FCBO_K_TEST_BIG, b);
+    b = c->prof_begin();
+    hipLaunchKernelGGL((k_local_test<WMC, 1>), dim3(gl), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
     c->prof_end(FCBO_K_TEST_LOCAL, b);
+    if constexpr (WMC <= 8) {
+        b = c->prof_begin();
+        hipLaunchKernelGGL((k_local_test<WMC, kMedChunks>), dim3(gm), dim3(kBlock), 0, c->stream, A);
+        CK_LAUNCH();
+        c->prof_end(FCBO_K_TEST_MEDIUM, b);
+    }
     b = c->prof_begin();
     hipLaunchKernelGGL(k_big_test<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
@@ -218,10 +235,17 @@ template <int WMC>
 void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P)
 {
     const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kWavesPerBlock)));
+    const unsigned gm = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(1024, div_up(P, kWavesPerBlock)));
     hipEvent_t b = c->prof_begin();
-    hipLaunchKernelGGL(k_local_write<WMC>, dim3(gl), dim3(kBlock), 0, c->stream, A);
+    hipLaunchKernelGGL((k_local_write<WMC, 1>), dim3(gl), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
     c->prof_end(FCBO_K_WRITE_LOCAL, b);
+    if constexpr (WMC <= 8) {
+        b = c->prof_begin();
+        hipLaunchKernelGGL((k_local_write<WMC, kMedChunks>), dim3(gm), dim3(kBlock), 0, c->stream, A);
+        CK_LAUNCH();
+        c->prof_end(FCBO_K_WRITE_MEDIUM, b);
+    }
     b = c->prof_begin();
     hipLaunchKernelGGL(k_big_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
@@ -276,7 +300,7 @@ void fcbo_context::enumerate_levels()
     lev_concepts.clear();
     lev_tests.clear();
     tests = pairs = sum_c = 0;
-    local_parents = local_objs = big_parents = big_tests = big_scan = 0;
+    local_parents = local_objs = med_parents = med_objs = big_parents = big_tests = big_scan = 0;
     uint64_t lo = 0, P = 1, obj_hi = (uint64_t)n;  // parents [lo, lo+P); objects used so far
     while (P > 0) {
         if (P >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
@@ -290,10 +314,13 @@ void fcbo_context::enumerate_levels()
         ensure(big_idx, cap_bi, P, 0, stream, tiny ? 1 : 1024);
         ensure(big_n, cap_bn, P, 0, stream, tiny ? 1 : 1024);
         ensure(big_off, cap_bo, P + 1, 0, stream, tiny ? 1 : 1024);
+        ensure(med_idx, cap_med, P, 0, stream, tiny ? 1 : 1024);
         if (!bt_size) {
             const uint64_t first = tiny ? 1 : (1u << 20);
             ensure(bt_size, cap_bt, first, 0, stream, tiny ? 1 : 1024);
             ensure(bt_sscan, cap_bts, first + 1, 0, stream, tiny ? 1 : 1024);
+            ensure(tasks, cap_task, first, 0, stream, tiny ? 1 : 1024);
+            ensure(plist, cap_pl, first, 0, stream, tiny ? 1 : 1024);
         }
         bool redo;
         int redos = 0;
@@ -306,7 +333,6 @@ void fcbo_context::enumerate_levels()
             A.P = P;
             A.child_lo = lo + P;
             A.child_obj_lo = obj_hi;
-            A.bt_cap = std::min(cap_bt, cap_bts - 1);
             CK(hipMemsetAsync(counters, 0, CNT_N * sizeof(uint64_t), stream));
             hipEvent_t b = prof_begin();
             hipLaunchKernelGGL(k_count, dim3((unsigned)div_up(P, kBlock)), dim3(kBlock), 0, stream, A);
@@ -327,6 +353,8 @@ void fcbo_context::enumerate_levels()
                 uint64_t need = h_counters[CNT_TBIG];
                 ensure(bt_size, cap_bt, need, 0, stream, tiny ? 1 : 1024);
                 ensure(bt_sscan, cap_bts, need + 1, 0, stream, tiny ? 1 : 1024);
+                ensure(tasks, cap_task, need, 0, stream, tiny ? 1 : 1024);
+                ensure(plist, cap_pl, need, 0, stream, tiny ? 1 : 1024);
                 redo = true;
                 ++redos;
                 continue;
@@ -339,8 +367,10 @@ void fcbo_context::enumerate_levels()
             pairs += h_counters[CNT_PAIRS];
             sum_c += n_objs;
             big_parents += h_counters[CNT_BIG];
-            local_parents += P - h_counters[CNT_BIG];
+            med_parents += h_counters[CNT_MED];
+            local_parents += P - h_counters[CNT_BIG] - h_counters[CNT_MED];
             local_objs += h_counters[CNT_SMALL_OBJS];
+            med_objs += h_counters[CNT_MED_OBJS];
             big_tests += h_counters[CNT_TBIG];
             big_scan += h_counters[CNT_BIG_SCAN];
             // room for the children in the store
@@ -356,7 +386,6 @@ void fcbo_context::enumerate_levels()
                 A.P = P;
                 A.child_lo = lo + P;
                 A.child_obj_lo = obj_hi;
-                A.bt_cap = std::min(cap_bt, cap_bts - 1);
                 fns.writes(this, A, P);
             }
         } while (redo);
@@ -556,6 +585,8 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
     st.sum_child_objects = ctx->sum_c;
     st.local_parents = ctx->local_parents;
     st.local_parent_objects = ctx->local_objs;
+    st.medium_parents = ctx->med_parents;
+    st.medium_parent_objects = ctx->med_objs;
     st.big_parents = ctx->big_parents;
     st.big_tests = ctx->big_tests;
     st.big_scanned_objects = ctx->big_scan;

@@ -32,6 +32,7 @@ namespace fcbo {
 
 constexpr int kWave = 64;
 constexpr int kSmallMax = 64;       // parents with at most this many objects use the local path
+constexpr int kMedChunks = 4;       // medium parents: up to 64 * kMedChunks objects
 constexpr int kBlock = 256;         // threads per block for wave-per-item kernels
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kScanBlocks = 1024;   // blocks of the multi-block exclusive scan
@@ -47,9 +48,12 @@ enum {
     CNT_CHILDREN = 4,  // children of this level
     CNT_OBJS = 5,      // objects in the children's extents
     CNT_TBIG = 6,      // closure tests of the big parents
-    CNT_SMALL_OBJS = 7, // objects in the extents of parents with <= kSmallMax objects
+    CNT_SMALL_OBJS = 7, // objects in the extents of local parents (<= kSmallMax objects)
     CNT_BIG_SCAN = 8,  // sum over big parents of tests x objects (list entries the big tests read)
-    CNT_N = 10
+    CNT_MED = 9,       // number of medium parents
+    CNT_BIGPASS = 10,  // passing big tasks
+    CNT_MED_OBJS = 11, // objects in the extents of medium parents
+    CNT_N = 12
 };
 
 // The per-level arguments, passed by value.
@@ -77,7 +81,11 @@ struct LevelArgs {
     uint64_t *big_off;     // exclusive scan of big_n
     uint32_t *bt_size;     // per big test: |C| if it passed, else 0
     uint64_t *bt_sscan;    // exclusive scan of bt_size
-    uint64_t bt_cap;       // capacity of bt_size / bt_sscan
+    uint64_t *tasks;       // per big test: bi << 16 | j
+    uint64_t *plist;       // passing big tests
+    uint64_t bt_cap;       // capacity of bt_size / bt_sscan / tasks / plist
+    uint32_t *med_idx;     // medium parents (order not fixed)
+    int med_max;           // largest extent taken by the row-local kernels
     uint64_t *counters;    // CNT_*
 };
 
@@ -261,15 +269,41 @@ __global__ void __launch_bounds__(kBlock) k_root_and(const uint64_t *__restrict_
 
 // ---------------------------------------------------------------------------
 // per-level kernels
+//
+// Parents fall in three classes by extent size a:
+//   local   a <= 64          k_local_test<WMC, 1>, one 64-bit object mask
+//   medium  64 < a <= med_max k_local_test<WMC, kMedChunks> from a list
+//   big     a > med_max      one wavefront per (parent, candidate) task
 
-// One thread per parent: candidate count (tests), item pairs, big-parent list,
-// and zeroed outputs for the test kernels.
+// Append the values of the flagged lanes to list[*counter], one atomic per wavefront.
+__device__ __forceinline__ void wave_append(bool flag, uint32_t value, uint32_t *list, uint64_t *counter)
+{
+    const uint64_t bal = __ballot(flag);
+    if (!bal) return;
+    const int lane = lane_id();
+    const int leader = __ffsll((unsigned long long)bal) - 1;
+    uint64_t base = 0;
+    if (lane == leader) base = atomicAdd((unsigned long long *)counter, (unsigned long long)__popcll(bal));
+    base = __shfl(base, leader);
+    if (flag) list[base + __popcll(bal & below_mask(lane))] = value;
+}
+
+__device__ __forceinline__ uint64_t wave_or(uint64_t v)
+{
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) v |= __shfl_xor(v, s);
+    return v;
+}
+
+// One thread per parent: candidate count (tests), item pairs, the medium and
+// big parent lists, and zeroed outputs for the test kernels.
 __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
 {
-    __shared__ uint64_t s_red[4][kWavesPerBlock];
+    __shared__ uint64_t s_red[5][kWavesPerBlock];
     const uint64_t p = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     uint32_t tests = 0, pairs = 0;
-    uint64_t small_objs = 0, big_scan = 0;
+    uint64_t local_objs = 0, med_objs = 0, big_scan = 0;
+    bool is_med = false, is_big = false;
     if (p < A.P) {
         const uint64_t c = A.lo + p;
         const int y = A.cursor[c];
@@ -281,40 +315,56 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
         }
         pairs = (uint32_t)(A.m - 1 - y);
         const uint64_t a = A.loff[c + 1] - A.loff[c];
-        if (a > (uint64_t)kSmallMax) {
-            uint64_t pos = atomicAdd((unsigned long long *)&A.counters[CNT_BIG], 1ull);
-            A.big_idx[pos] = (uint32_t)p;
-            A.big_n[pos] = tests;
+        if (a > (uint64_t)A.med_max) {
+            is_big = true;
             big_scan = a * tests;
         } else {
-            small_objs = a;
+            is_med = a > (uint64_t)kSmallMax;
+            (is_med ? med_objs : local_objs) = a;
         }
         A.nchild[p] = 0;
         A.nobj[p] = 0;
     }
-    uint64_t v[4] = {tests, pairs, small_objs, big_scan};
+    {
+        const uint64_t bal = __ballot(is_big);
+        if (bal) {
+            const int lane = lane_id();
+            const int leader = __ffsll((unsigned long long)bal) - 1;
+            uint64_t base = 0;
+            if (lane == leader)
+                base = atomicAdd((unsigned long long *)&A.counters[CNT_BIG], (unsigned long long)__popcll(bal));
+            base = __shfl(base, leader);
+            if (is_big) {
+                const uint64_t pos = base + __popcll(bal & below_mask(lane));
+                A.big_idx[pos] = (uint32_t)p;
+                A.big_n[pos] = tests;
+            }
+        }
+    }
+    wave_append(is_med, (uint32_t)p, A.med_idx, &A.counters[CNT_MED]);
+    uint64_t v[5] = {tests, pairs, local_objs, med_objs, big_scan};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 5; ++i)
 #pragma unroll
         for (int s = 32; s > 0; s >>= 1) v[i] += __shfl_xor(v[i], s);
     if (lane_id() == 0)
-        for (int i = 0; i < 4; ++i) s_red[i][threadIdx.x / kWave] = v[i];
+        for (int i = 0; i < 5; ++i) s_red[i][threadIdx.x / kWave] = v[i];
     __syncthreads();
-    if (threadIdx.x < 4) {
+    if (threadIdx.x < 5) {
         uint64_t sum = 0;
         for (int w = 0; w < kWavesPerBlock; ++w) sum += s_red[threadIdx.x][w];
-        const int slot[4] = {CNT_TESTS, CNT_PAIRS, CNT_SMALL_OBJS, CNT_BIG_SCAN};
+        const int slot[5] = {CNT_TESTS, CNT_PAIRS, CNT_SMALL_OBJS, CNT_MED_OBJS, CNT_BIG_SCAN};
         if (sum) atomicAdd((unsigned long long *)&A.counters[slot[threadIdx.x]], (unsigned long long)sum);
     }
 }
 
-// Closure tests of one parent (A, B, y) with |A| <= 64, one wavefront.
+// Closure tests of one parent (A, B, y) with |A| <= 64 * NCH, one wavefront.
 //
-// Lane i stages the row of the i-th object of A in LDS.  For a candidate j
-// (j > y, j not in B) let c_j be the objects of A having j, as a bitmask over
-// the staged rows: C = A AND col[j] restricted to A.  Then D = C' is the AND of
-// their rows and the canonical test asks that D adds no attribute below j to
-// B (page 1, section 4.3: bits 0..j-1 compared, bit j excluded).
+// The rows of the objects of A are staged in LDS.  For a candidate j (j > y,
+// j not in B) let c_j be the objects of A having j, as a bitmask over the
+// staged rows: C = A AND col[j] restricted to A.  D = C' is the AND of their
+// rows, and the canonical test asks that D adds no attribute below j to B
+// (page 1, section 4.3: bits 0..j-1 compared, bit j excluded).
 //
 // Candidates split in two kinds:
 //   * j carried by some object of A (the set U): c_j is non-empty and is
@@ -324,21 +374,27 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
 //     in B.  That single candidate (if above y) yields the bottom concept.
 // Attribute-saturation pruning (page 1, section 2.3) is the j-in-B skip: with
 // B closed, A inside col[j] holds exactly when j is in B.
-template <int WMC>
+//
+// NCH == 1 walks all parents of the level and skips the others; NCH > 1 walks
+// the medium-parent list.
+template <int WMC, int NCH>
 __global__ void __launch_bounds__(kBlock) k_local_test(LevelArgs A)
 {
-    __shared__ uint64_t s_rows[kWavesPerBlock][kSmallMax * WMC];
+    constexpr int kMaxObj = kWave * NCH;
+    __shared__ uint64_t s_rows[kWavesPerBlock][kMaxObj * WMC];
     __shared__ uint64_t s_pm[kWavesPerBlock][WMC];
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     const int wm = words_of<WMC>(A.wm);
     uint64_t *R = s_rows[wv];
     uint64_t *PM = s_pm[wv];
-    for (uint64_t p = (uint64_t)blockIdx.x * kWavesPerBlock + wv; p < A.P;
-         p += (uint64_t)gridDim.x * kWavesPerBlock) {
+    const uint64_t count = (NCH == 1) ? A.P : A.counters[CNT_MED];
+    for (uint64_t it = (uint64_t)blockIdx.x * kWavesPerBlock + wv; it < count;
+         it += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t p = (NCH == 1) ? it : (uint64_t)A.med_idx[it];
         const uint64_t c0 = A.lo + p;
         const uint64_t o0 = A.loff[c0];
         const uint64_t a64 = A.loff[c0 + 1] - o0;
-        if (a64 > (uint64_t)kSmallMax) continue;
+        if (NCH == 1 && a64 > (uint64_t)kSmallMax) continue;
         const int a = (int)a64;
         const int y = A.cursor[c0];
         uint64_t Bx[WMC];  // B plus the padding bits past M
@@ -350,32 +406,38 @@ __global__ void __launch_bounds__(kBlock) k_local_test(LevelArgs A)
                 if (u == wm - 1) Bx[u] |= ~A.tail_m;
             }
         }
-        if (lane < a) {
-            const uint64_t g = A.objs[o0 + lane];
+        uint64_t U[WMC];  // attributes carried by some object of A
 #pragma unroll
-            for (int u = 0; u < WMC; ++u)
-                if (u < wm) R[lane * WMC + u] = A.rows[g * A.wm + u];
+        for (int u = 0; u < WMC; ++u) U[u] = 0;
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            const int i = lane + kWave * q;
+            if (i < a) {
+                const uint64_t g = A.objs[o0 + i];
+#pragma unroll
+                for (int u = 0; u < WMC; ++u) {
+                    if (u < wm) {
+                        const uint64_t r = A.rows[g * A.wm + u];
+                        R[i * WMC + u] = r;
+                        U[u] |= r;
+                    }
+                }
+            }
         }
         if (lane < wm) PM[lane] = 0;
+#pragma unroll
+        for (int u = 0; u < WMC; ++u)
+            if (u < wm) U[u] = wave_or(U[u]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // U = attributes outside B carried by some object of A, above y.
-        uint64_t U[WMC];
-#pragma unroll
-        for (int u = 0; u < WMC; ++u) U[u] = 0;
-        for (int i = 0; i < a; ++i) {
-#pragma unroll
-            for (int u = 0; u < WMC; ++u)
-                if (u < wm) U[u] |= R[i * WMC + u];
-        }
         int nU = 0;
         int j0 = -1;  // first attribute not in B
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
             if (u < wm) {
-                uint64_t nb = ~Bx[u];
+                const uint64_t nb = ~Bx[u];
                 if (j0 < 0 && nb) j0 = 64 * u + __ffsll((unsigned long long)nb) - 1;
                 U[u] &= nb & above_mask(y, u);
                 nU += __popcll(U[u]);
@@ -396,18 +458,29 @@ __global__ void __launch_bounds__(kBlock) k_local_test(LevelArgs A)
             const bool active = k < nU;
             const int j = active ? select_words<WMC>(U, wm, k) : 0;
             const int wj = j >> 6, bj = j & 63;
-            uint64_t cj = 0;
-            for (int i = 0; i < a; ++i) cj |= ((R[i * WMC + wj] >> bj) & 1ull) << i;
+            uint64_t cj[NCH];
+#pragma unroll
+            for (int q = 0; q < NCH; ++q) {
+                uint64_t cq = 0;
+                const int lim = a - kWave * q < kWave ? a - kWave * q : kWave;
+                for (int ii = 0; ii < lim; ++ii) cq |= ((R[(kWave * q + ii) * WMC + wj] >> bj) & 1ull) << ii;
+                cj[q] = cq;
+            }
             uint64_t Dn[WMC];  // attributes outside B shared by the objects of c_j
 #pragma unroll
             for (int u = 0; u < WMC; ++u) Dn[u] = ~Bx[u];
-            uint64_t cc = active ? cj : 0ull;
-            while (cc) {
-                const int i = __ffsll((unsigned long long)cc) - 1;
-                cc &= cc - 1ull;
+            uint32_t sz = 0;
 #pragma unroll
-                for (int u = 0; u < WMC; ++u)
-                    if (u < wm && u <= wj) Dn[u] &= R[i * WMC + u];
+            for (int q = 0; q < NCH; ++q) {
+                uint64_t cc = active ? cj[q] : 0ull;
+                sz += (uint32_t)__popcll(cc);
+                while (cc) {
+                    const int i = kWave * q + __ffsll((unsigned long long)cc) - 1;
+                    cc &= cc - 1ull;
+#pragma unroll
+                    for (int u = 0; u < WMC; ++u)
+                        if (u < wm && u <= wj) Dn[u] &= R[i * WMC + u];
+                }
             }
             uint64_t bad = 0;
 #pragma unroll
@@ -418,7 +491,7 @@ __global__ void __launch_bounds__(kBlock) k_local_test(LevelArgs A)
             const bool pass = active && bad == 0;
             const uint64_t bal = __ballot(pass);
             nch += (uint32_t)__popcll(bal);
-            nob += wave_sum(pass ? (uint32_t)__popcll(cj) : 0u);
+            nob += wave_sum(pass ? sz : 0u);
             if (pass) atomicOr((unsigned long long *)&PM[wj], (unsigned long long)(1ull << bj));
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -433,132 +506,44 @@ __global__ void __launch_bounds__(kBlock) k_local_test(LevelArgs A)
     }
 }
 
-// Map a big test index t to (big slot bi, parent p, candidate rank k).
-__device__ __forceinline__ bool big_locate(const LevelArgs &A, uint64_t t, uint64_t nbig, uint64_t &bi,
-                                           uint64_t &p, int &k)
-{
-    // largest bi with big_off[bi] <= t
-    uint64_t lo = 0, hi = nbig;  // big_off[nbig] = total > t
-    while (hi - lo > 1) {
-        uint64_t mid = (lo + hi) >> 1;
-        if (A.big_off[mid] <= t) lo = mid;
-        else hi = mid;
-    }
-    bi = lo;
-    p = A.big_idx[bi];
-    k = (int)(t - A.big_off[bi]);
-    return true;
-}
-
-// Closure tests of parents with more than 64 objects: one wavefront per
-// (parent, candidate j).  The extent list is read 64 objects at a time; an
-// object is in C when its bit in col[j] is set, and its row is ANDed into the
-// lane's partial D (page 1, section 4.2: set bits of the extent walked, rows
-// ANDed, then a wavefront AND-reduction).
-template <int WMC>
-__global__ void __launch_bounds__(kBlock) k_big_test(LevelArgs A)
-{
-    const int lane = lane_id();
-    const int wm = words_of<WMC>(A.wm);
-    const uint64_t nbig = A.counters[CNT_BIG];
-    const uint64_t tbig = A.big_off[nbig];
-    if (tbig > A.bt_cap) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) A.counters[CNT_OVERFLOW] = 1;
-        return;
-    }
-    for (uint64_t t = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < tbig;
-         t += (uint64_t)gridDim.x * kWavesPerBlock) {
-        uint64_t bi, p;
-        int k;
-        big_locate(A, t, nbig, bi, p, k);
-        const uint64_t c0 = A.lo + p;
-        const int y = A.cursor[c0];
-        uint64_t Bx[WMC], cand[WMC];
-#pragma unroll
-        for (int u = 0; u < WMC; ++u) {
-            Bx[u] = ~0ull;
-            cand[u] = 0;
-            if (u < wm) {
-                Bx[u] = A.intents[c0 * A.wm + u];
-                if (u == wm - 1) Bx[u] |= ~A.tail_m;
-                cand[u] = ~Bx[u] & above_mask(y, u);
-            }
-        }
-        const int j = select_words<WMC>(cand, wm, k);
-        const int wj = j >> 6, bj = j & 63;
-        const uint64_t o0 = A.loff[c0], o1 = A.loff[c0 + 1];
-        const uint64_t *col = A.cols + (uint64_t)j * A.wn;
-        uint64_t D[WMC];
-#pragma unroll
-        for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
-        uint32_t cnt = 0;
-        for (uint64_t o = o0; o < o1; o += kWave) {
-            bool in = false;
-            uint32_t g = 0;
-            if (o + lane < o1) {
-                g = A.objs[o + lane];
-                in = (col[g >> 6] >> (g & 63)) & 1ull;
-            }
-            cnt += (uint32_t)__popcll(__ballot(in));
-            if (in) {
-#pragma unroll
-                for (int u = 0; u < WMC; ++u)
-                    if (u < wm) D[u] &= A.rows[(uint64_t)g * A.wm + u];
-            }
-        }
-        uint64_t bad = 0;
-#pragma unroll
-        for (int u = 0; u < WMC; ++u) {
-            if (u < wm) {
-                uint64_t d = wave_and(D[u]);
-                uint64_t extra = d & ~Bx[u];
-                if (u < wj) bad |= extra;
-                else if (u == wj) bad |= extra & below_mask(bj);
-            }
-        }
-        const bool pass = bad == 0;
-        if (lane == 0) {
-            A.bt_size[t] = pass ? cnt : 0u;
-            if (pass) {
-                atomicOr((unsigned long long *)&A.pass[p * A.wm + wj], (unsigned long long)(1ull << bj));
-                atomicAdd(&A.nchild[p], 1u);
-                atomicAdd(&A.nobj[p], cnt);
-            }
-        }
-    }
-}
-
-// Children of parents with <= 64 objects, one wavefront per parent, one lane
-// per child: recompute c_j for the passing attributes, D = AND of their rows
-// (all of M when c_j is empty), write intent, cursor and extent list at the
-// offsets the scans gave.
-template <int WMC>
+// Children of the local and medium parents, one wavefront per parent, one
+// lane per child: recompute c_j for the passing attributes, D = AND of their
+// rows (all of M when c_j is empty), write intent, cursor and extent list at
+// the offsets the scans gave.
+template <int WMC, int NCH>
 __global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
 {
-    __shared__ uint64_t s_rows[kWavesPerBlock][kSmallMax * WMC];
-    __shared__ uint32_t s_obj[kWavesPerBlock][kSmallMax];
+    constexpr int kMaxObj = kWave * NCH;
+    __shared__ uint64_t s_rows[kWavesPerBlock][kMaxObj * WMC];
+    __shared__ uint32_t s_obj[kWavesPerBlock][kMaxObj];
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     const int wm = words_of<WMC>(A.wm);
     uint64_t *R = s_rows[wv];
     uint32_t *G = s_obj[wv];
-    for (uint64_t p = (uint64_t)blockIdx.x * kWavesPerBlock + wv; p < A.P;
-         p += (uint64_t)gridDim.x * kWavesPerBlock) {
+    const uint64_t count = (NCH == 1) ? A.P : A.counters[CNT_MED];
+    for (uint64_t it = (uint64_t)blockIdx.x * kWavesPerBlock + wv; it < count;
+         it += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t p = (NCH == 1) ? it : (uint64_t)A.med_idx[it];
         const uint32_t nch = A.nchild[p];
         if (nch == 0) continue;
         const uint64_t c0 = A.lo + p;
         const uint64_t o0 = A.loff[c0];
         const uint64_t a64 = A.loff[c0 + 1] - o0;
-        if (a64 > (uint64_t)kSmallMax) continue;
+        if (NCH == 1 && a64 > (uint64_t)kSmallMax) continue;
         const int a = (int)a64;
         uint64_t pm[WMC];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) pm[u] = (u < wm) ? A.pass[p * A.wm + u] : 0ull;
-        if (lane < a) {
-            const uint32_t g = A.objs[o0 + lane];
-            G[lane] = g;
 #pragma unroll
-            for (int u = 0; u < WMC; ++u)
-                if (u < wm) R[lane * WMC + u] = A.rows[(uint64_t)g * A.wm + u];
+        for (int q = 0; q < NCH; ++q) {
+            const int i = lane + kWave * q;
+            if (i < a) {
+                const uint32_t g = A.objs[o0 + i];
+                G[i] = g;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm) R[i * WMC + u] = A.rows[(uint64_t)g * A.wm + u];
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -570,21 +555,31 @@ __global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
             const bool active = k < nch;
             const int j = active ? select_words<WMC>(pm, wm, (int)k) : 0;
             const int wj = j >> 6, bj = j & 63;
-            uint64_t cj = 0;
-            if (active)
-                for (int i = 0; i < a; ++i) cj |= ((R[i * WMC + wj] >> bj) & 1ull) << i;
+            uint64_t cj[NCH];
+#pragma unroll
+            for (int q = 0; q < NCH; ++q) {
+                uint64_t cq = 0;
+                const int lim = a - kWave * q < kWave ? a - kWave * q : kWave;
+                if (active)
+                    for (int ii = 0; ii < lim; ++ii) cq |= ((R[(kWave * q + ii) * WMC + wj] >> bj) & 1ull) << ii;
+                cj[q] = cq;
+            }
             uint64_t D[WMC];
 #pragma unroll
             for (int u = 0; u < WMC; ++u) D[u] = (u == wm - 1) ? A.tail_m : ~0ull;
-            uint64_t cc = cj;
-            while (cc) {
-                const int i = __ffsll((unsigned long long)cc) - 1;
-                cc &= cc - 1ull;
+            uint32_t sz = 0;
 #pragma unroll
-                for (int u = 0; u < WMC; ++u)
-                    if (u < wm) D[u] &= R[i * WMC + u];
+            for (int q = 0; q < NCH; ++q) {
+                uint64_t cc = cj[q];
+                sz += (uint32_t)__popcll(cc);
+                while (cc) {
+                    const int i = kWave * q + __ffsll((unsigned long long)cc) - 1;
+                    cc &= cc - 1ull;
+#pragma unroll
+                    for (int u = 0; u < WMC; ++u)
+                        if (u < wm) D[u] &= R[i * WMC + u];
+                }
             }
-            const uint32_t sz = active ? (uint32_t)__popcll(cj) : 0u;
             const uint64_t o = run + wave_excl_scan(sz);
             run += wave_sum(sz);
             if (active) {
@@ -595,12 +590,15 @@ __global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
                 A.cursor[child] = j;
                 A.loff[child] = o;
                 A.loff[child + 1] = o + sz;
-                uint64_t q = o;
-                cc = cj;
-                while (cc) {
-                    const int i = __ffsll((unsigned long long)cc) - 1;
-                    cc &= cc - 1ull;
-                    A.objs[q++] = G[i];
+                uint64_t qo = o;
+#pragma unroll
+                for (int q = 0; q < NCH; ++q) {
+                    uint64_t cc = cj[q];
+                    while (cc) {
+                        const int i = kWave * q + __ffsll((unsigned long long)cc) - 1;
+                        cc &= cc - 1ull;
+                        A.objs[qo++] = G[i];
+                    }
                 }
             }
         }
@@ -608,12 +606,70 @@ __global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
     }
 }
 
-// Children of parents with more than 64 objects: one wavefront per big test,
-// only the passing ones do work.  The child's rank among its siblings is the
-// number of passing attributes below j; its list offset comes from the scan
-// of the passing tests' |C|.
+// Big parents: one task per (parent, candidate j), task = bi << 16 | j, laid
+// out at the scanned offsets big_off so the tests of a parent are adjacent.
 template <int WMC>
-__global__ void __launch_bounds__(kBlock) k_big_write(LevelArgs A)
+__global__ void __launch_bounds__(kBlock) k_big_tasks(LevelArgs A)
+{
+    const int lane = lane_id();
+    const int wm = words_of<WMC>(A.wm);
+    const uint64_t nbig = A.counters[CNT_BIG];
+    const uint64_t tbig = A.big_off[nbig];
+    if (tbig > A.bt_cap) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) A.counters[CNT_OVERFLOW] = 1;
+        return;
+    }
+    for (uint64_t bi = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; bi < nbig;
+         bi += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t c0 = A.lo + A.big_idx[bi];
+        const int y = A.cursor[c0];
+        uint64_t cand[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            cand[u] = 0;
+            if (u < wm) {
+                uint64_t bx = A.intents[c0 * A.wm + u];
+                if (u == wm - 1) bx |= ~A.tail_m;
+                cand[u] = ~bx & above_mask(y, u);
+            }
+        }
+        const uint32_t n = A.big_n[bi];
+        const uint64_t base = A.big_off[bi];
+        for (uint32_t k = lane; k < n; k += kWave)
+            A.tasks[base + k] = (bi << 16) | (uint64_t)select_words<WMC>(cand, wm, (int)k);
+    }
+}
+
+// Scan the extent list of a big parent for the objects having attribute j
+// (their bit in col[j]), four 64-entry chunks per step so the loads overlap.
+// Calls f(in, g, chunk_ballot) per chunk in list order.
+template <typename F>
+__device__ __forceinline__ void scan_list_for_attr(const LevelArgs &A, uint64_t o0, uint64_t o1, int j, F f)
+{
+    const int lane = lane_id();
+    const uint64_t *col = A.cols + (uint64_t)j * A.wn;
+    for (uint64_t o = o0; o < o1; o += 4 * kWave) {
+        uint32_t g[4];
+        bool in[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint64_t idx = o + (uint64_t)(s * kWave + lane);
+            g[s] = idx < o1 ? A.objs[idx] : 0xFFFFFFFFu;
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) in[s] = g[s] != 0xFFFFFFFFu && ((col[g[s] >> 6] >> (g[s] & 63)) & 1ull);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) f(in[s], g[s], __ballot(in[s]));
+    }
+}
+
+// Closure tests of the big parents, one wavefront per task.  The extent list
+// is read from HBM/L2, an object is in C when its bit in col[j] is set, and its
+// row is ANDed into the lane's partial D (page 1, section 4.2: set bits of the
+// extent walked, rows ANDed, then a wavefront AND-reduction).  Passing tasks
+// are appended to a list for the write kernel.
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_big_test(LevelArgs A)
 {
     const int lane = lane_id();
     const int wm = words_of<WMC>(A.wm);
@@ -622,60 +678,92 @@ __global__ void __launch_bounds__(kBlock) k_big_write(LevelArgs A)
     if (tbig > A.bt_cap) return;
     for (uint64_t t = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < tbig;
          t += (uint64_t)gridDim.x * kWavesPerBlock) {
-        uint64_t bi, p;
-        int k;
-        big_locate(A, t, nbig, bi, p, k);
+        const uint64_t task = A.tasks[t];
+        const uint64_t bi = task >> 16;
+        const int j = (int)(task & 0xFFFFu);
+        const uint64_t p = A.big_idx[bi];
         const uint64_t c0 = A.lo + p;
-        const int y = A.cursor[c0];
-        uint64_t cand[WMC], pm[WMC];
-#pragma unroll
-        for (int u = 0; u < WMC; ++u) {
-            cand[u] = 0;
-            pm[u] = 0;
-            if (u < wm) {
-                uint64_t bx = A.intents[c0 * A.wm + u];
-                if (u == wm - 1) bx |= ~A.tail_m;
-                cand[u] = ~bx & above_mask(y, u);
-                pm[u] = A.pass[p * A.wm + u];
-            }
-        }
-        const int j = select_words<WMC>(cand, wm, k);
         const int wj = j >> 6, bj = j & 63;
-        bool passed = false;
-        int rank = 0;
-#pragma unroll
-        for (int u = 0; u < WMC; ++u) {
-            if (u < wj) rank += __popcll(pm[u]);
-            else if (u == wj) {
-                rank += __popcll(pm[u] & below_mask(bj));
-                passed = (pm[u] >> bj) & 1ull;
-            }
-        }
-        if (!passed) continue;
-        const uint64_t child = A.child_lo + A.cbase[p] + (uint64_t)rank;
-        const uint64_t obeg = A.child_obj_lo + A.obase[p] + (A.bt_sscan[t] - A.bt_sscan[A.big_off[bi]]);
-        const uint64_t o0 = A.loff[c0], o1 = A.loff[c0 + 1];
-        const uint64_t *col = A.cols + (uint64_t)j * A.wn;
         uint64_t D[WMC];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
-        uint64_t q = obeg;
-        for (uint64_t o = o0; o < o1; o += kWave) {
-            bool in = false;
-            uint32_t g = 0;
-            if (o + lane < o1) {
-                g = A.objs[o + lane];
-                in = (col[g >> 6] >> (g & 63)) & 1ull;
-            }
-            const uint64_t bal = __ballot(in);
+        uint32_t cnt = 0;
+        scan_list_for_attr(A, A.loff[c0], A.loff[c0 + 1], j, [&](bool in, uint32_t g, uint64_t bal) {
+            cnt += (uint32_t)__popcll(bal);
             if (in) {
-                A.objs[q + __popcll(bal & below_mask(lane))] = g;
 #pragma unroll
                 for (int u = 0; u < WMC; ++u)
                     if (u < wm) D[u] &= A.rows[(uint64_t)g * A.wm + u];
             }
-            q += __popcll(bal);
+        });
+        uint64_t bad = 0;
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            if (u < wm && u <= wj) {
+                uint64_t bx = A.intents[c0 * A.wm + u];
+                if (u == wm - 1) bx |= ~A.tail_m;
+                const uint64_t extra = wave_and(D[u]) & ~bx;
+                if (u < wj) bad |= extra;
+                else bad |= extra & below_mask(bj);
+            }
         }
+        const bool pass = bad == 0;
+        if (lane == 0) {
+            A.bt_size[t] = pass ? cnt : 0u;
+            if (pass) {
+                atomicOr((unsigned long long *)&A.pass[p * A.wm + wj], (unsigned long long)(1ull << bj));
+                atomicAdd(&A.nchild[p], 1u);
+                atomicAdd(&A.nobj[p], cnt);
+                const uint64_t pos = atomicAdd((unsigned long long *)&A.counters[CNT_BIGPASS], 1ull);
+                A.plist[pos] = t;
+            }
+        }
+    }
+}
+
+// Children of big parents, one wavefront per passing task.  The child's rank
+// among its siblings is the number of passing attributes below j; its list
+// offset comes from the scan of the passing tasks' |C|.
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_big_write(LevelArgs A)
+{
+    const int lane = lane_id();
+    const int wm = words_of<WMC>(A.wm);
+    const uint64_t nbig = A.counters[CNT_BIG];
+    if (A.big_off[nbig] > A.bt_cap) return;
+    const uint64_t npass = A.counters[CNT_BIGPASS];
+    for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; i < npass;
+         i += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t t = A.plist[i];
+        const uint64_t task = A.tasks[t];
+        const uint64_t bi = task >> 16;
+        const int j = (int)(task & 0xFFFFu);
+        const uint64_t p = A.big_idx[bi];
+        const uint64_t c0 = A.lo + p;
+        const int wj = j >> 6, bj = j & 63;
+        int rank = 0;
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            if (u < wm && u <= wj) {
+                const uint64_t pm = A.pass[p * A.wm + u];
+                rank += __popcll(u < wj ? pm : (pm & below_mask(bj)));
+            }
+        }
+        const uint64_t child = A.child_lo + A.cbase[p] + (uint64_t)rank;
+        const uint64_t obeg = A.child_obj_lo + A.obase[p] + (A.bt_sscan[t] - A.bt_sscan[A.big_off[bi]]);
+        uint64_t D[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
+        uint64_t qo = obeg;
+        scan_list_for_attr(A, A.loff[c0], A.loff[c0 + 1], j, [&](bool in, uint32_t g, uint64_t bal) {
+            if (in) {
+                A.objs[qo + __popcll(bal & below_mask(lane))] = g;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm) D[u] &= A.rows[(uint64_t)g * A.wm + u];
+            }
+            qo += __popcll(bal);
+        });
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
             if (u < wm) {
@@ -687,7 +775,7 @@ __global__ void __launch_bounds__(kBlock) k_big_write(LevelArgs A)
         if (lane == 0) {
             A.cursor[child] = j;
             A.loff[child] = obeg;
-            A.loff[child + 1] = q;
+            A.loff[child + 1] = qo;
         }
     }
 }

@@ -57,15 +57,17 @@ enum {
 
 /* Kernel classes reported in fcbo_stats.kernel_ms / kernel_launches. */
 enum {
-    FCBO_K_COUNT = 0,       /* per-parent candidate count, big-parent list */
-    FCBO_K_TEST_LOCAL = 1,  /* closure tests of parents with <= 64 objects */
-    FCBO_K_TEST_BIG = 2,    /* closure tests of parents with > 64 objects */
-    FCBO_K_SCAN = 3,        /* exclusive scans (children, objects, big tests) */
-    FCBO_K_WRITE_LOCAL = 4, /* child write, small parents */
-    FCBO_K_WRITE_BIG = 5,   /* child write, big parents */
-    FCBO_K_SORT = 6,        /* intent radix sort */
-    FCBO_K_OUTPUT = 7,      /* sorted intents + extent bitmaps to the caller */
-    FCBO_K_NUM_CLASSES = 8
+    FCBO_K_COUNT = 0,        /* per-parent candidate count, parent classes */
+    FCBO_K_TEST_LOCAL = 1,   /* closure tests of parents with <= 64 objects */
+    FCBO_K_TEST_MEDIUM = 2,  /* closure tests of parents with 65..256 objects */
+    FCBO_K_TEST_BIG = 3,     /* closure tests of larger parents (tasks + tests) */
+    FCBO_K_SCAN = 4,         /* exclusive scans (children, objects, big tests) */
+    FCBO_K_WRITE_LOCAL = 5,  /* child write, parents with <= 64 objects */
+    FCBO_K_WRITE_MEDIUM = 6, /* child write, parents with 65..256 objects */
+    FCBO_K_WRITE_BIG = 7,    /* child write, larger parents */
+    FCBO_K_SORT = 8,         /* intent radix sort */
+    FCBO_K_OUTPUT = 9,       /* sorted intents + extent bitmaps to the caller */
+    FCBO_K_NUM_CLASSES = 10
 };
 
 typedef struct {
@@ -77,7 +79,9 @@ typedef struct {
     uint64_t output_bytes;  /* bytes written to the caller's buffers */
     uint64_t local_parents; /* parents with <= 64 objects (row-local test kernel) */
     uint64_t local_parent_objects; /* objects in their extents (rows staged) */
-    uint64_t big_parents;   /* parents with > 64 objects */
+    uint64_t medium_parents; /* parents with 65..256 objects (row-local, 4 mask words) */
+    uint64_t medium_parent_objects; /* objects in their extents */
+    uint64_t big_parents;   /* larger parents (one wavefront per closure test) */
     uint64_t big_tests;     /* closure tests made by them */
     uint64_t big_scanned_objects; /* extent-list entries read by those tests */
     uint64_t sort_passes;   /* radix passes run by the last sort */

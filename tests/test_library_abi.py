@@ -47,8 +47,9 @@ def test_error_strings(lib):
 
 
 def test_stats_struct_matches_header():
-    # 12 u64 counters, 4 doubles, 8 doubles, 8 u64 launch counts
-    assert ctypes.sizeof(fca.FcboStats) == 12 * 8 + 4 * 8 + 8 * 8 + 8 * 8
+    # 14 u64 counters, 4 doubles, then per kernel class one double and one u64
+    n = len(fca.KERNEL_CLASSES)
+    assert ctypes.sizeof(fca.FcboStats) == 14 * 8 + 4 * 8 + n * 8 + n * 8
     text = open(HEADER).read()
     assert "FCBO_K_NUM_CLASSES = %d" % len(fca.KERNEL_CLASSES) in text
 
