@@ -71,6 +71,43 @@ void ensure(T *&p, uint64_t &cap, uint64_t need, uint64_t keep, hipStream_t s, u
 
 constexpr int kGridCap = 4096;  // blocks for grid-stride wave kernels
 
+// Device storage of one BigSet (see fcbo_device.h).
+struct BigStore {
+    uint64_t cap_idx = 0, cap_n = 0, cap_off = 0, cap_t = 0, cap_s = 0, cap_ss = 0, cap_p = 0, cap_bmp = 0;
+    uint32_t *idx = nullptr, *n = nullptr, *size = nullptr;
+    uint64_t *off = nullptr, *tasks = nullptr, *sscan = nullptr, *plist = nullptr, *bmp = nullptr;
+
+    void free_all()
+    {
+        dfree(idx); dfree(n); dfree(size); dfree(off); dfree(tasks); dfree(sscan); dfree(plist); dfree(bmp);
+        cap_idx = cap_n = cap_off = cap_t = cap_s = cap_ss = cap_p = cap_bmp = 0;
+    }
+    void ensure_members(uint64_t P, hipStream_t s, uint64_t mc)
+    {
+        ensure(idx, cap_idx, P, 0, s, mc);
+        ensure(n, cap_n, P, 0, s, mc);
+        ensure(off, cap_off, P + 1, 0, s, mc);
+    }
+    void ensure_tests(uint64_t need, hipStream_t s, uint64_t mc)
+    {
+        ensure(tasks, cap_t, need, 0, s, mc);
+        ensure(size, cap_s, need, 0, s, mc);
+        ensure(sscan, cap_ss, need + 1, 0, s, mc);
+        ensure(plist, cap_p, need, 0, s, mc);
+    }
+    uint64_t test_cap() const { return std::min(std::min(cap_t, cap_s), std::min(cap_ss ? cap_ss - 1 : 0, cap_p)); }
+    BigSet view(int cnt_slot, int tot_slot, int pass_slot, bool bitmaps) const
+    {
+        BigSet S;
+        S.idx = idx; S.n = n; S.off = off; S.tasks = tasks; S.size = size; S.sscan = sscan; S.plist = plist;
+        S.cap = test_cap();
+        S.bmp = bitmaps ? bmp : nullptr;
+        S.bmp_cap = cap_bmp;
+        S.cnt_slot = cnt_slot; S.tot_slot = tot_slot; S.pass_slot = pass_slot;
+        return S;
+    }
+};
+
 }  // namespace
 
 struct fcbo_context {
@@ -78,26 +115,27 @@ struct fcbo_context {
     hipStream_t stream = nullptr;
     int64_t n = 0, m = 0;
     int wn = 0, wm = 0;
-    uint64_t tail_m = 0;
+    uint64_t tail_m = 0, tail_n = 0;
     bool tiny = false;  // FCBO_TINY_BUFFERS: every buffer starts at its minimum size
     uint64_t *rows = nullptr;  // n x wm (+1 padding row)
     uint64_t *cols = nullptr;  // m x wn
 
     // concept store
-    uint64_t cap_k = 0, cap_int = 0, cap_cur = 0, cap_loff = 0, cap_o = 0;
+    uint64_t cap_int = 0, cap_cur = 0, cap_loff = 0, cap_o = 0;
     uint64_t *intents = nullptr;
     int32_t *cursor = nullptr;
     uint64_t *loff = nullptr;
     uint32_t *objs = nullptr;
 
     // level scratch
-    uint64_t cap_pass = 0, cap_nch = 0, cap_nob = 0, cap_cb = 0, cap_ob = 0, cap_bi = 0, cap_bn = 0, cap_bo = 0;
-    uint64_t *pass = nullptr, *cbase = nullptr, *obase = nullptr, *big_off = nullptr;
-    uint32_t *nchild = nullptr, *nobj = nullptr, *big_idx = nullptr, *big_n = nullptr;
-    uint64_t cap_bt = 0, cap_bts = 0, cap_task = 0, cap_pl = 0, cap_med = 0;
-    uint32_t *bt_size = nullptr;
-    uint64_t *bt_sscan = nullptr, *tasks = nullptr, *plist = nullptr;
-    uint32_t *med_idx = nullptr;
+    uint64_t cap_pass = 0, cap_nch = 0, cap_nob = 0, cap_cb = 0, cap_ob = 0, cap_mid = 0, cap_mrec = 0;
+    uint64_t *pass = nullptr, *cbase = nullptr, *obase = nullptr;
+    uint32_t *nchild = nullptr, *nobj = nullptr, *mid_idx = nullptr;
+    uint64_t *mrec = nullptr;  // child records of the mid parents (words)
+    BigStore huge;
+    uint64_t cap_dt = 0, cap_tcnt = 0, cap_icnt = 0;
+    uint64_t *dt = nullptr;                     // huge tests: D accumulators
+    uint32_t *tcnt = nullptr, *icnt = nullptr;  // huge tests: |C|, per-chunk counts
     uint64_t *scan_part = nullptr;  // 2 x kScanBlocks
     uint64_t *counters = nullptr;   // CNT_N
     uint64_t *h_counters = nullptr; // pinned, CNT_N
@@ -149,13 +187,17 @@ struct fcbo_context {
         marks.push_back({cls, {b, e}});
     }
 
+    uint64_t min_cap() const { return tiny ? 1 : 1024; }
+    bool use_bitmaps() const { return wn <= kBmpMaxWords; }
+    int nchunk() const { return (int)div_up((uint64_t)wn, kWave); }
+
     void free_all()
     {
         dfree(rows); dfree(cols);
         dfree(intents); dfree(cursor); dfree(loff); dfree(objs);
-        dfree(pass); dfree(cbase); dfree(obase); dfree(big_off);
-        dfree(nchild); dfree(nobj); dfree(big_idx); dfree(big_n);
-        dfree(bt_size); dfree(bt_sscan); dfree(tasks); dfree(plist); dfree(med_idx);
+        dfree(pass); dfree(cbase); dfree(obase); dfree(nchild); dfree(nobj); dfree(mid_idx); dfree(mrec);
+        huge.free_all();
+        dfree(dt); dfree(tcnt); dfree(icnt);
         dfree(scan_part); dfree(counters);
         dfree(keys_a); dfree(keys_b); dfree(idx_a); dfree(idx_b); dfree(hist); dfree(hist_off);
         dfree(sort_red);
@@ -165,19 +207,33 @@ struct fcbo_context {
         ev_pool.clear();
     }
 
-    LevelArgs level_args() const
+    // per-test buffers of the huge set (its BigStore plus the accumulators)
+    void ensure_huge_tests(uint64_t need)
+    {
+        huge.ensure_tests(need, stream, min_cap());
+        ensure(dt, cap_dt, need * wm, 0, stream, min_cap());
+        ensure(tcnt, cap_tcnt, need, 0, stream, min_cap());
+        ensure(icnt, cap_icnt, need * nchunk(), 0, stream, min_cap());
+    }
+
+    LevelArgs level_args(uint64_t lo, uint64_t P, uint64_t obj_hi) const
     {
         LevelArgs A;
         memset(&A, 0, sizeof(A));
         A.rows = rows; A.cols = cols;
-        A.n = (int)n; A.m = (int)m; A.wn = wn; A.wm = wm; A.tail_m = tail_m;
+        A.n = (int)n; A.m = (int)m; A.wn = wn; A.wm = wm; A.tail_m = tail_m; A.tail_n = tail_n;
         A.intents = intents; A.cursor = cursor; A.loff = loff; A.objs = objs;
+        A.lo = lo; A.P = P; A.child_lo = lo + P; A.child_obj_lo = obj_hi;
         A.pass = pass; A.nchild = nchild; A.nobj = nobj; A.cbase = cbase; A.obase = obase;
-        A.big_idx = big_idx; A.big_n = big_n; A.big_off = big_off;
-        A.bt_size = bt_size; A.bt_sscan = bt_sscan; A.tasks = tasks; A.plist = plist;
-        A.bt_cap = std::min(std::min(cap_bt, cap_bts - 1), std::min(cap_task, cap_pl));
-        A.med_idx = med_idx;
-        A.med_max = wm <= 8 ? kWave * kMedChunks : kSmallMax;
+        A.mid_idx = mid_idx;
+        A.mid_max = wm <= 8 ? kMidMax : kSmallMax;
+        A.mrec = mrec;
+        A.mrec_cap = cap_mrec / (3 + (uint64_t)wm);
+        const bool bm = use_bitmaps();
+        A.huge = huge.view(CNT_HUGE, CNT_THUGE, CNT_HUGEPASS, bm);
+        if (bm) A.huge.cap = std::min(A.huge.cap, std::min(std::min(cap_dt / wm, cap_tcnt), cap_icnt / nchunk()));
+        A.dt = dt; A.tcnt = tcnt; A.icnt = icnt;
+        A.nchunk = nchunk();
         A.counters = counters;
         return A;
     }
@@ -211,8 +267,9 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
 {
     const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kWavesPerBlock)));
     const unsigned gm = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(1024, div_up(P, kWavesPerBlock)));
+    const bool bm = A.huge.bmp != nullptr;
     hipEvent_t b = c->prof_begin();
-    hipLaunchKernelGGL(k_big_tasks<WMC>, dim3(gm), dim3(kBlock), 0, c->stream, A);
+    hipLaunchKernelGGL(k_huge_tasks<WMC>, dim3(gm), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
     c->prof_end(FCBO_K_TEST_BIG, b);
     b = c->prof_begin();
@@ -221,12 +278,19 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
     c->prof_end(FCBO_K_TEST_LOCAL, b);
     if constexpr (WMC <= 8) {
         b = c->prof_begin();
-        hipLaunchKernelGGL((k_local_test<WMC, kMedChunks>), dim3(gm), dim3(kBlock), 0, c->stream, A);
+        const unsigned gmid = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(2048, div_up(P, kMidWaves)));
+        hipLaunchKernelGGL(k_mid_test<WMC>, dim3(gmid), dim3(kWave * kMidWaves), 0, c->stream, A);
         CK_LAUNCH();
         c->prof_end(FCBO_K_TEST_MEDIUM, b);
     }
     b = c->prof_begin();
-    hipLaunchKernelGGL(k_big_test<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+    if (bm) {
+        hipLaunchKernelGGL(k_huge_partial<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+        CK_LAUNCH();
+        hipLaunchKernelGGL(k_huge_finalize, dim3(1024), dim3(kBlock), 0, c->stream, A);
+    } else {
+        hipLaunchKernelGGL(k_big_test_list<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+    }
     CK_LAUNCH();
     c->prof_end(FCBO_K_TEST_BIG, b);
 }
@@ -235,19 +299,21 @@ template <int WMC>
 void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P)
 {
     const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kWavesPerBlock)));
-    const unsigned gm = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(1024, div_up(P, kWavesPerBlock)));
     hipEvent_t b = c->prof_begin();
     hipLaunchKernelGGL((k_local_write<WMC, 1>), dim3(gl), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
     c->prof_end(FCBO_K_WRITE_LOCAL, b);
     if constexpr (WMC <= 8) {
         b = c->prof_begin();
-        hipLaunchKernelGGL((k_local_write<WMC, kMedChunks>), dim3(gm), dim3(kBlock), 0, c->stream, A);
+        hipLaunchKernelGGL(k_mid_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
         CK_LAUNCH();
         c->prof_end(FCBO_K_WRITE_MEDIUM, b);
     }
     b = c->prof_begin();
-    hipLaunchKernelGGL(k_big_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+    if (A.huge.bmp)
+        hipLaunchKernelGGL(k_huge_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+    else
+        hipLaunchKernelGGL(k_big_write_list<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
     c->prof_end(FCBO_K_WRITE_BIG, b);
 }
@@ -281,12 +347,13 @@ LevelFns pick_level_fns(int wm)
 void fcbo_context::enumerate_levels()
 {
     const LevelFns fns = pick_level_fns(wm);
+    const uint64_t mc = min_cap();
+    const bool bm = use_bitmaps();
     // root
-    ensure(intents, cap_int, (uint64_t)wm * 1024, 0, stream, tiny ? 1 : 1024);
-    ensure(cursor, cap_cur, 1024, 0, stream, tiny ? 1 : 1024);
-    ensure(loff, cap_loff, 1025, 0, stream, tiny ? 1 : 1024);
-    ensure(objs, cap_o, (uint64_t)n, 0, stream, tiny ? 1 : 1024);
-    cap_k = std::min(cap_int / wm, std::min(cap_cur, cap_loff - 1));
+    ensure(intents, cap_int, (uint64_t)wm * 1024, 0, stream, mc);
+    ensure(cursor, cap_cur, 1024, 0, stream, mc);
+    ensure(loff, cap_loff, 1025, 0, stream, mc);
+    ensure(objs, cap_o, (uint64_t)n, 0, stream, mc);
     {
         uint64_t t = std::max<uint64_t>((uint64_t)n, (uint64_t)wm);
         hipLaunchKernelGGL(k_root_init, dim3((unsigned)div_up(t, kBlock)), dim3(kBlock), 0, stream, intents, cursor,
@@ -301,60 +368,56 @@ void fcbo_context::enumerate_levels()
     lev_tests.clear();
     tests = pairs = sum_c = 0;
     local_parents = local_objs = med_parents = med_objs = big_parents = big_tests = big_scan = 0;
+    const uint64_t rstride = 3 + (uint64_t)wm;
+    if (!huge.tasks) {
+        if (bm) ensure_huge_tests(tiny ? 1 : (1u << 16));
+        else huge.ensure_tests(tiny ? 1 : (1u << 20), stream, mc);
+    }
+    if (bm && !huge.bmp) ensure(huge.bmp, huge.cap_bmp, (uint64_t)wn * (tiny ? 1 : 64), 0, stream, 1);
+    if (!mrec) ensure(mrec, cap_mrec, rstride * (tiny ? 1 : (1u << 18)), 0, stream, 1);
     uint64_t lo = 0, P = 1, obj_hi = (uint64_t)n;  // parents [lo, lo+P); objects used so far
     while (P > 0) {
         if (P >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
         // every level adds an attribute to the intent, so there are at most M + 1
         if (lev_concepts.size() > (size_t)m + 1) throw HipError{FCBO_ERR_DEVICE};
-        ensure(pass, cap_pass, P * (uint64_t)wm, 0, stream, tiny ? 1 : 1024);
-        ensure(nchild, cap_nch, P, 0, stream, tiny ? 1 : 1024);
-        ensure(nobj, cap_nob, P, 0, stream, tiny ? 1 : 1024);
-        ensure(cbase, cap_cb, P + 1, 0, stream, tiny ? 1 : 1024);
-        ensure(obase, cap_ob, P + 1, 0, stream, tiny ? 1 : 1024);
-        ensure(big_idx, cap_bi, P, 0, stream, tiny ? 1 : 1024);
-        ensure(big_n, cap_bn, P, 0, stream, tiny ? 1 : 1024);
-        ensure(big_off, cap_bo, P + 1, 0, stream, tiny ? 1 : 1024);
-        ensure(med_idx, cap_med, P, 0, stream, tiny ? 1 : 1024);
-        if (!bt_size) {
-            const uint64_t first = tiny ? 1 : (1u << 20);
-            ensure(bt_size, cap_bt, first, 0, stream, tiny ? 1 : 1024);
-            ensure(bt_sscan, cap_bts, first + 1, 0, stream, tiny ? 1 : 1024);
-            ensure(tasks, cap_task, first, 0, stream, tiny ? 1 : 1024);
-            ensure(plist, cap_pl, first, 0, stream, tiny ? 1 : 1024);
-        }
+        ensure(pass, cap_pass, P * (uint64_t)wm, 0, stream, mc);
+        ensure(nchild, cap_nch, P, 0, stream, mc);
+        ensure(nobj, cap_nob, P, 0, stream, mc);
+        ensure(cbase, cap_cb, P + 1, 0, stream, mc);
+        ensure(obase, cap_ob, P + 1, 0, stream, mc);
+        ensure(mid_idx, cap_mid, P, 0, stream, mc);
+        huge.ensure_members(P, stream, mc);
         bool redo;
         int redos = 0;
         uint64_t n_children = 0, n_objs = 0;
         do {
             redo = false;
             if (redos > 2) throw HipError{FCBO_ERR_DEVICE};  // a grown buffer always fits the redo
-            LevelArgs A = level_args();
-            A.lo = lo;
-            A.P = P;
-            A.child_lo = lo + P;
-            A.child_obj_lo = obj_hi;
+            LevelArgs A = level_args(lo, P, obj_hi);
             CK(hipMemsetAsync(counters, 0, CNT_N * sizeof(uint64_t), stream));
             hipEvent_t b = prof_begin();
             hipLaunchKernelGGL(k_count, dim3((unsigned)div_up(P, kBlock)), dim3(kBlock), 0, stream, A);
             CK_LAUNCH();
             prof_end(FCBO_K_COUNT, b);
             b = prof_begin();
-            // offsets of the big parents' tests; total -> counters[CNT_TBIG]
-            scan(big_n, nullptr, counters + CNT_BIG, 0, P, big_off, nullptr, counters + CNT_TBIG, nullptr);
+            // test offsets of the huge parents; total -> counters
+            scan(huge.n, nullptr, counters + CNT_HUGE, 0, P, huge.off, nullptr, counters + CNT_THUGE, nullptr);
             prof_end(FCBO_K_SCAN, b);
             fns.tests(this, A, P);
             b = prof_begin();
-            scan(bt_size, nullptr, counters + CNT_TBIG, 0, A.bt_cap, bt_sscan, nullptr, nullptr, nullptr);
+            scan(huge.size, nullptr, counters + CNT_THUGE, 0, A.huge.cap, huge.sscan, nullptr, nullptr, nullptr);
             scan(nchild, nobj, nullptr, P, P, cbase, obase, counters + CNT_CHILDREN, counters + CNT_OBJS);
             prof_end(FCBO_K_SCAN, b);
             CK(hipMemcpyAsync(h_counters, counters, CNT_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
             CK(hipStreamSynchronize(stream));
             if (h_counters[CNT_OVERFLOW]) {
-                uint64_t need = h_counters[CNT_TBIG];
-                ensure(bt_size, cap_bt, need, 0, stream, tiny ? 1 : 1024);
-                ensure(bt_sscan, cap_bts, need + 1, 0, stream, tiny ? 1 : 1024);
-                ensure(tasks, cap_task, need, 0, stream, tiny ? 1 : 1024);
-                ensure(plist, cap_pl, need, 0, stream, tiny ? 1 : 1024);
+                if (bm) {
+                    ensure_huge_tests(h_counters[CNT_THUGE]);
+                    ensure(huge.bmp, huge.cap_bmp, h_counters[CNT_HUGE] * (uint64_t)wn, 0, stream, 1);
+                } else {
+                    huge.ensure_tests(h_counters[CNT_THUGE], stream, mc);
+                }
+                ensure(mrec, cap_mrec, h_counters[CNT_MIDREC] * rstride, 0, stream, 1);
                 redo = true;
                 ++redos;
                 continue;
@@ -366,28 +429,21 @@ void fcbo_context::enumerate_levels()
             tests += h_counters[CNT_TESTS];
             pairs += h_counters[CNT_PAIRS];
             sum_c += n_objs;
-            big_parents += h_counters[CNT_BIG];
-            med_parents += h_counters[CNT_MED];
-            local_parents += P - h_counters[CNT_BIG] - h_counters[CNT_MED];
+            big_parents += h_counters[CNT_HUGE];
+            med_parents += h_counters[CNT_MID];
+            local_parents += P - h_counters[CNT_HUGE] - h_counters[CNT_MID];
             local_objs += h_counters[CNT_SMALL_OBJS];
-            med_objs += h_counters[CNT_MED_OBJS];
-            big_tests += h_counters[CNT_TBIG];
+            med_objs += h_counters[CNT_MID_OBJS];
+            big_tests += h_counters[CNT_THUGE];
             big_scan += h_counters[CNT_BIG_SCAN];
             // room for the children in the store
             const uint64_t k_end = lo + P + n_children;
             const uint64_t keep_k = lo + P;
-            ensure(intents, cap_int, k_end * wm, keep_k * wm, stream, tiny ? 1 : 1024);
-            ensure(cursor, cap_cur, k_end, keep_k, stream, tiny ? 1 : 1024);
-            ensure(loff, cap_loff, k_end + 1, keep_k + 1, stream, tiny ? 1 : 1024);
-            ensure(objs, cap_o, obj_hi + n_objs, obj_hi, stream, tiny ? 1 : 1024);
-            if (n_children) {
-                A = level_args();
-                A.lo = lo;
-                A.P = P;
-                A.child_lo = lo + P;
-                A.child_obj_lo = obj_hi;
-                fns.writes(this, A, P);
-            }
+            ensure(intents, cap_int, k_end * wm, keep_k * wm, stream, mc);
+            ensure(cursor, cap_cur, k_end, keep_k, stream, mc);
+            ensure(loff, cap_loff, k_end + 1, keep_k + 1, stream, mc);
+            ensure(objs, cap_o, obj_hi + n_objs, obj_hi, stream, mc);
+            if (n_children) fns.writes(this, level_args(lo, P, obj_hi), P);
         } while (redo);
         lo += P;
         P = n_children;
@@ -402,13 +458,14 @@ void fcbo_context::sort_intents()
 {
     const uint64_t n_keys = K;
     if (n_keys >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
-    ensure(keys_a, cap_ka, n_keys, 0, stream, tiny ? 1 : 1024);
-    ensure(keys_b, cap_kb, n_keys, 0, stream, tiny ? 1 : 1024);
-    ensure(idx_a, cap_ia, n_keys, 0, stream, tiny ? 1 : 1024);
-    ensure(idx_b, cap_ib, n_keys, 0, stream, tiny ? 1 : 1024);
+    const uint64_t mc = min_cap();
+    ensure(keys_a, cap_ka, n_keys, 0, stream, mc);
+    ensure(keys_b, cap_kb, n_keys, 0, stream, mc);
+    ensure(idx_a, cap_ia, n_keys, 0, stream, mc);
+    ensure(idx_b, cap_ib, n_keys, 0, stream, mc);
     const uint64_t ntiles = div_up(n_keys, kSortTile);
-    ensure(hist, cap_h, 256 * ntiles, 0, stream, tiny ? 1 : 1024);
-    ensure(hist_off, cap_ho, 256 * ntiles + 1, 0, stream, tiny ? 1 : 1024);
+    ensure(hist, cap_h, 256 * ntiles, 0, stream, mc);
+    ensure(hist_off, cap_ho, 256 * ntiles + 1, 0, stream, mc);
     hipEvent_t b = prof_begin();
     hipLaunchKernelGGL(k_iota, dim3((unsigned)div_up(n_keys, kBlock)), dim3(kBlock), 0, stream, idx_a, n_keys);
     CK_LAUNCH();
@@ -495,6 +552,7 @@ int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs
         c->wn = (int)((n_objects + 63) / 64);
         c->wm = (int)((n_attrs + 63) / 64);
         c->tail_m = (n_attrs & 63) ? ((1ull << (n_attrs & 63)) - 1ull) : ~0ull;
+        c->tail_n = (n_objects & 63) ? ((1ull << (n_objects & 63)) - 1ull) : ~0ull;
         CK(hipMalloc((void **)&c->rows, ((uint64_t)n_objects + 1) * c->wm * sizeof(uint64_t)));
         CK(hipMalloc((void **)&c->cols, (uint64_t)n_attrs * c->wn * sizeof(uint64_t)));
         CK(hipMalloc((void **)&c->scan_part, 2 * kScanBlocks * sizeof(uint64_t)));

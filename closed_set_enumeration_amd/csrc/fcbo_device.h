@@ -32,28 +32,48 @@ namespace fcbo {
 
 constexpr int kWave = 64;
 constexpr int kSmallMax = 64;       // parents with at most this many objects use the local path
-constexpr int kMedChunks = 4;       // medium parents: up to 64 * kMedChunks objects
 constexpr int kBlock = 256;         // threads per block for wave-per-item kernels
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kScanBlocks = 1024;   // blocks of the multi-block exclusive scan
 constexpr int kSortTile = 2048;     // keys per block in a radix pass (256 threads x 8)
 constexpr int kOutTileWords = 1024; // extent words staged in LDS per output tile
+constexpr int kBmpMaxWords = 16384; // big parents use extent bitmaps when N <= 64 * this
+constexpr int kMidMax = 4096;       // parents with more objects are huge (tested a chunk at a time)
+constexpr int kMidWaves = 2;        // wavefronts per block of the incidence kernel
 
 // Device counters shared by the kernels of one level.
 enum {
-    CNT_BIG = 0,       // number of parents with more than kSmallMax objects
+    CNT_HUGE = 0,      // number of huge parents
     CNT_TESTS = 1,     // closure tests of this level
     CNT_PAIRS = 2,     // (parent, j > cursor) pairs of this level
-    CNT_OVERFLOW = 3,  // big-test buffers too small: the level is redone
+    CNT_OVERFLOW = 3,  // a per-test or record buffer was too small: the level is redone
     CNT_CHILDREN = 4,  // children of this level
     CNT_OBJS = 5,      // objects in the children's extents
-    CNT_TBIG = 6,      // closure tests of the big parents
-    CNT_SMALL_OBJS = 7, // objects in the extents of local parents (<= kSmallMax objects)
-    CNT_BIG_SCAN = 8,  // sum over big parents of tests x objects (list entries the big tests read)
-    CNT_MED = 9,       // number of medium parents
-    CNT_BIGPASS = 10,  // passing big tasks
-    CNT_MED_OBJS = 11, // objects in the extents of medium parents
-    CNT_N = 12
+    CNT_THUGE = 6,     // closure tests of the huge parents
+    CNT_SMALL_OBJS = 7, // objects in the extents of local parents
+    CNT_BIG_SCAN = 8,  // sum over huge parents of tests x objects
+    CNT_MID = 9,       // number of mid parents
+    CNT_HUGEPASS = 10, // passing huge tests
+    CNT_MID_OBJS = 11, // objects in the extents of mid parents
+    CNT_MIDREC = 12,   // child records written by the mid parents
+    CNT_N = 14
+};
+
+// Huge parents, tested one closure test at a time: one work item per (test,
+// 64-word chunk of the extent bitmap), or one wavefront per test scanning the
+// object list when N is too large for bitmaps.
+struct BigSet {
+    uint32_t *idx;     // parent index of each member (order not fixed)
+    uint32_t *n;       // closure tests (candidates) of each member
+    uint64_t *off;     // exclusive scan of n; off[members] = tests of the set
+    uint64_t *tasks;   // per test: member << 16 | j
+    uint32_t *size;    // per test: |C| if it passed, else 0
+    uint64_t *sscan;   // exclusive scan of size
+    uint64_t *plist;   // passing tests
+    uint64_t cap;      // capacity of tasks / size / sscan / plist (and the huge accumulators)
+    uint64_t *bmp;     // extent bitmap of each member (members x wn), or null: use the lists
+    uint64_t bmp_cap;  // words
+    int cnt_slot, tot_slot, pass_slot;  // counters: members, tests, passing tests
 };
 
 // The per-level arguments, passed by value.
@@ -76,16 +96,16 @@ struct LevelArgs {
     uint32_t *nobj;        // objects in the children's extents per parent
     uint64_t *cbase;       // exclusive scan of nchild (P + 1)
     uint64_t *obase;       // exclusive scan of nobj (P + 1)
-    uint32_t *big_idx;     // parents with > kSmallMax objects (order not fixed)
-    uint32_t *big_n;       // their candidate counts
-    uint64_t *big_off;     // exclusive scan of big_n
-    uint32_t *bt_size;     // per big test: |C| if it passed, else 0
-    uint64_t *bt_sscan;    // exclusive scan of bt_size
-    uint64_t *tasks;       // per big test: bi << 16 | j
-    uint64_t *plist;       // passing big tests
-    uint64_t bt_cap;       // capacity of bt_size / bt_sscan / tasks / plist
-    uint32_t *med_idx;     // medium parents (order not fixed)
-    int med_max;           // largest extent taken by the row-local kernels
+    uint32_t *mid_idx;     // mid parents (order not fixed)
+    int mid_max;           // parents with more objects are huge
+    uint64_t *mrec;        // child records of the mid parents (see k_mid_test)
+    uint64_t mrec_cap;     // records
+    BigSet huge;           // huge parents
+    uint64_t *dt;          // per huge test: AND of the rows of C, wm words
+    uint32_t *tcnt;        // per huge test: |C|
+    uint32_t *icnt;        // per (huge test, 64-word chunk): objects of C in the chunk, then offsets
+    int nchunk;            // ceil(wn / 64)
+    uint64_t tail_n;       // valid bits of the last extent word
     uint64_t *counters;    // CNT_*
 };
 
@@ -271,9 +291,10 @@ __global__ void __launch_bounds__(kBlock) k_root_and(const uint64_t *__restrict_
 // per-level kernels
 //
 // Parents fall in three classes by extent size a:
-//   local   a <= 64          k_local_test<WMC, 1>, one 64-bit object mask
-//   medium  64 < a <= med_max k_local_test<WMC, kMedChunks> from a list
-//   big     a > med_max      one wavefront per (parent, candidate) task
+//   local   a <= 64          k_local_test, one 64-bit object mask per candidate
+//   mid     64 < a <= mid_max k_mid_test, closure tests by incidence
+//   huge    a > mid_max      one work item per (test, 64-word chunk) of the
+//                            extent bitmap, or per test over the object list
 
 // Append the values of the flagged lanes to list[*counter], one atomic per wavefront.
 __device__ __forceinline__ void wave_append(bool flag, uint32_t value, uint32_t *list, uint64_t *counter)
@@ -302,8 +323,8 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
     __shared__ uint64_t s_red[5][kWavesPerBlock];
     const uint64_t p = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     uint32_t tests = 0, pairs = 0;
-    uint64_t local_objs = 0, med_objs = 0, big_scan = 0;
-    bool is_med = false, is_big = false;
+    uint64_t local_objs = 0, mid_objs = 0, big_scan = 0;
+    bool is_mid = false, is_huge = false;
     if (p < A.P) {
         const uint64_t c = A.lo + p;
         const int y = A.cursor[c];
@@ -315,34 +336,35 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
         }
         pairs = (uint32_t)(A.m - 1 - y);
         const uint64_t a = A.loff[c + 1] - A.loff[c];
-        if (a > (uint64_t)A.med_max) {
-            is_big = true;
+        if (a > (uint64_t)A.mid_max) {
+            is_huge = true;
             big_scan = a * tests;
         } else {
-            is_med = a > (uint64_t)kSmallMax;
-            (is_med ? med_objs : local_objs) = a;
+            is_mid = a > (uint64_t)kSmallMax;
+            (is_mid ? mid_objs : local_objs) = a;
         }
         A.nchild[p] = 0;
         A.nobj[p] = 0;
     }
     {
-        const uint64_t bal = __ballot(is_big);
+        const BigSet &S = A.huge;
+        const uint64_t bal = __ballot(is_huge);
         if (bal) {
             const int lane = lane_id();
             const int leader = __ffsll((unsigned long long)bal) - 1;
             uint64_t base = 0;
             if (lane == leader)
-                base = atomicAdd((unsigned long long *)&A.counters[CNT_BIG], (unsigned long long)__popcll(bal));
+                base = atomicAdd((unsigned long long *)&A.counters[S.cnt_slot], (unsigned long long)__popcll(bal));
             base = __shfl(base, leader);
-            if (is_big) {
+            if (is_huge) {
                 const uint64_t pos = base + __popcll(bal & below_mask(lane));
-                A.big_idx[pos] = (uint32_t)p;
-                A.big_n[pos] = tests;
+                S.idx[pos] = (uint32_t)p;
+                S.n[pos] = tests;
             }
         }
     }
-    wave_append(is_med, (uint32_t)p, A.med_idx, &A.counters[CNT_MED]);
-    uint64_t v[5] = {tests, pairs, local_objs, med_objs, big_scan};
+    wave_append(is_mid, (uint32_t)p, A.mid_idx, &A.counters[CNT_MID]);
+    uint64_t v[5] = {tests, pairs, local_objs, mid_objs, big_scan};
 #pragma unroll
     for (int i = 0; i < 5; ++i)
 #pragma unroll
@@ -353,7 +375,7 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
     if (threadIdx.x < 5) {
         uint64_t sum = 0;
         for (int w = 0; w < kWavesPerBlock; ++w) sum += s_red[threadIdx.x][w];
-        const int slot[5] = {CNT_TESTS, CNT_PAIRS, CNT_SMALL_OBJS, CNT_MED_OBJS, CNT_BIG_SCAN};
+        const int slot[5] = {CNT_TESTS, CNT_PAIRS, CNT_SMALL_OBJS, CNT_MID_OBJS, CNT_BIG_SCAN};
         if (sum) atomicAdd((unsigned long long *)&A.counters[slot[threadIdx.x]], (unsigned long long)sum);
     }
 }
@@ -375,26 +397,30 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
 // Attribute-saturation pruning (page 1, section 2.3) is the j-in-B skip: with
 // B closed, A inside col[j] holds exactly when j is in B.
 //
-// NCH == 1 walks all parents of the level and skips the others; NCH > 1 walks
-// the medium-parent list.
+// The kernel walks all parents of the level and skips those with more than
+// 64 * NCH objects.
+template <int NCH>
+struct LocalShape {
+    static constexpr int kWaves = kWavesPerBlock;  // wavefronts per block
+    static constexpr int kThreads = kWave * kWaves;
+};
+
 template <int WMC, int NCH>
-__global__ void __launch_bounds__(kBlock) k_local_test(LevelArgs A)
+__global__ void __launch_bounds__(LocalShape<NCH>::kThreads) k_local_test(LevelArgs A)
 {
     constexpr int kMaxObj = kWave * NCH;
-    __shared__ uint64_t s_rows[kWavesPerBlock][kMaxObj * WMC];
-    __shared__ uint64_t s_pm[kWavesPerBlock][WMC];
+    constexpr int kW = LocalShape<NCH>::kWaves;
+    __shared__ uint64_t s_rows[kW][kMaxObj * WMC];
+    __shared__ uint64_t s_pm[kW][WMC];
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     const int wm = words_of<WMC>(A.wm);
     uint64_t *R = s_rows[wv];
     uint64_t *PM = s_pm[wv];
-    const uint64_t count = (NCH == 1) ? A.P : A.counters[CNT_MED];
-    for (uint64_t it = (uint64_t)blockIdx.x * kWavesPerBlock + wv; it < count;
-         it += (uint64_t)gridDim.x * kWavesPerBlock) {
-        const uint64_t p = (NCH == 1) ? it : (uint64_t)A.med_idx[it];
+    for (uint64_t p = (uint64_t)blockIdx.x * kW + wv; p < A.P; p += (uint64_t)gridDim.x * kW) {
         const uint64_t c0 = A.lo + p;
         const uint64_t o0 = A.loff[c0];
         const uint64_t a64 = A.loff[c0 + 1] - o0;
-        if (NCH == 1 && a64 > (uint64_t)kSmallMax) continue;
+        if (a64 > (uint64_t)(kWave * NCH)) continue;
         const int a = (int)a64;
         const int y = A.cursor[c0];
         uint64_t Bx[WMC];  // B plus the padding bits past M
@@ -511,25 +537,23 @@ __global__ void __launch_bounds__(kBlock) k_local_test(LevelArgs A)
 // rows (all of M when c_j is empty), write intent, cursor and extent list at
 // the offsets the scans gave.
 template <int WMC, int NCH>
-__global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
+__global__ void __launch_bounds__(LocalShape<NCH>::kThreads) k_local_write(LevelArgs A)
 {
     constexpr int kMaxObj = kWave * NCH;
-    __shared__ uint64_t s_rows[kWavesPerBlock][kMaxObj * WMC];
-    __shared__ uint32_t s_obj[kWavesPerBlock][kMaxObj];
+    constexpr int kW = LocalShape<NCH>::kWaves;
+    __shared__ uint64_t s_rows[kW][kMaxObj * WMC];
+    __shared__ uint32_t s_obj[kW][kMaxObj];
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     const int wm = words_of<WMC>(A.wm);
     uint64_t *R = s_rows[wv];
     uint32_t *G = s_obj[wv];
-    const uint64_t count = (NCH == 1) ? A.P : A.counters[CNT_MED];
-    for (uint64_t it = (uint64_t)blockIdx.x * kWavesPerBlock + wv; it < count;
-         it += (uint64_t)gridDim.x * kWavesPerBlock) {
-        const uint64_t p = (NCH == 1) ? it : (uint64_t)A.med_idx[it];
+    for (uint64_t p = (uint64_t)blockIdx.x * kW + wv; p < A.P; p += (uint64_t)gridDim.x * kW) {
         const uint32_t nch = A.nchild[p];
         if (nch == 0) continue;
         const uint64_t c0 = A.lo + p;
         const uint64_t o0 = A.loff[c0];
         const uint64_t a64 = A.loff[c0 + 1] - o0;
-        if (NCH == 1 && a64 > (uint64_t)kSmallMax) continue;
+        if (a64 > (uint64_t)(kWave * NCH)) continue;
         const int a = (int)a64;
         uint64_t pm[WMC];
 #pragma unroll
@@ -606,39 +630,100 @@ __global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
     }
 }
 
-// Big parents: one task per (parent, candidate j), task = bi << 16 | j, laid
-// out at the scanned offsets big_off so the tests of a parent are adjacent.
+// Huge parents: one task per (parent, candidate j), task = member << 16 | j,
+// laid out at the scanned offsets so the tests of a parent are adjacent.
+//
+// With bitmaps enabled the wavefront also writes the member's extent as a
+// bitmap, straight from its intent: A = B' is the AND of the columns of the
+// attributes of B (all objects when B is empty), so no list is walked.  For the
+// chunked set it clears the per-test accumulators as well.
 template <int WMC>
-__global__ void __launch_bounds__(kBlock) k_big_tasks(LevelArgs A)
+__global__ void __launch_bounds__(kBlock) k_huge_tasks(LevelArgs A)
 {
+    const BigSet &S = A.huge;
     const int lane = lane_id();
     const int wm = words_of<WMC>(A.wm);
-    const uint64_t nbig = A.counters[CNT_BIG];
-    const uint64_t tbig = A.big_off[nbig];
-    if (tbig > A.bt_cap) {
+    const uint64_t nset = A.counters[S.cnt_slot];
+    const uint64_t tset = S.off[nset];
+    if (tset > S.cap || (S.bmp && nset * (uint64_t)A.wn > S.bmp_cap)) {
         if (blockIdx.x == 0 && threadIdx.x == 0) A.counters[CNT_OVERFLOW] = 1;
         return;
     }
-    for (uint64_t bi = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; bi < nbig;
+    for (uint64_t bi = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; bi < nset;
          bi += (uint64_t)gridDim.x * kWavesPerBlock) {
-        const uint64_t c0 = A.lo + A.big_idx[bi];
+        const uint64_t c0 = A.lo + S.idx[bi];
         const int y = A.cursor[c0];
-        uint64_t cand[WMC];
+        uint64_t cand[WMC], bset[WMC];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
             cand[u] = 0;
+            bset[u] = 0;
             if (u < wm) {
-                uint64_t bx = A.intents[c0 * A.wm + u];
+                bset[u] = A.intents[c0 * A.wm + u];
+                uint64_t bx = bset[u];
                 if (u == wm - 1) bx |= ~A.tail_m;
                 cand[u] = ~bx & above_mask(y, u);
             }
         }
-        const uint32_t n = A.big_n[bi];
-        const uint64_t base = A.big_off[bi];
-        for (uint32_t k = lane; k < n; k += kWave)
-            A.tasks[base + k] = (bi << 16) | (uint64_t)select_words<WMC>(cand, wm, (int)k);
+        if (S.bmp) {
+            uint64_t *row = S.bmp + bi * (uint64_t)A.wn;
+            for (int w = lane; w < A.wn; w += kWave) {
+                uint64_t v = (w == A.wn - 1) ? A.tail_n : ~0ull;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u) {
+                    if (u < wm) {
+                        uint64_t b = bset[u];
+                        while (b) {
+                            const int m = 64 * u + __ffsll((unsigned long long)b) - 1;
+                            b &= b - 1ull;
+                            v &= A.cols[(uint64_t)m * A.wn + w];
+                        }
+                    }
+                }
+                row[w] = v;
+            }
+        }
+        const uint32_t n = S.n[bi];
+        const uint64_t base = S.off[bi];
+        for (uint32_t k = lane; k < n; k += kWave) {
+            S.tasks[base + k] = (bi << 16) | (uint64_t)select_words<WMC>(cand, wm, (int)k);
+            if (S.bmp) {
+                A.tcnt[base + k] = 0;
+                for (int u = 0; u < wm; ++u) A.dt[(base + k) * A.wm + u] = ~0ull;
+            }
+        }
     }
 }
+
+// Mark a passing test of set S: pass bit, sibling count, object count, and
+// append it to the set's pass list.
+__device__ __forceinline__ void big_record_pass(const LevelArgs &A, const BigSet &S, uint64_t t, uint64_t p, int j,
+                                                uint32_t cnt)
+{
+    atomicOr((unsigned long long *)&A.pass[p * A.wm + (j >> 6)], (unsigned long long)(1ull << (j & 63)));
+    atomicAdd(&A.nchild[p], 1u);
+    atomicAdd(&A.nobj[p], cnt);
+    const uint64_t pos = atomicAdd((unsigned long long *)&A.counters[S.pass_slot], 1ull);
+    S.plist[pos] = t;
+}
+
+// Rank of attribute j among the passing attributes of parent p.
+template <int WMC>
+__device__ __forceinline__ int pass_rank(const LevelArgs &A, uint64_t p, int j)
+{
+    const int wj = j >> 6, bj = j & 63;
+    int rank = 0;
+#pragma unroll
+    for (int u = 0; u < WMC; ++u) {
+        if (u < words_of<WMC>(A.wm) && u <= wj) {
+            const uint64_t pm = A.pass[p * A.wm + u];
+            rank += __popcll(u < wj ? pm : (pm & below_mask(bj)));
+        }
+    }
+    return rank;
+}
+
+// --- list scan (any N): the parent's object list is read 256 entries a step -----
 
 // Scan the extent list of a big parent for the objects having attribute j
 // (their bit in col[j]), four 64-entry chunks per step so the loads overlap.
@@ -663,25 +748,227 @@ __device__ __forceinline__ void scan_list_for_attr(const LevelArgs &A, uint64_t 
     }
 }
 
-// Closure tests of the big parents, one wavefront per task.  The extent list
-// is read from HBM/L2, an object is in C when its bit in col[j] is set, and its
-// row is ANDed into the lane's partial D (page 1, section 4.2: set bits of the
-// extent walked, rows ANDed, then a wavefront AND-reduction).  Passing tasks
-// are appended to a list for the write kernel.
+// --- mid parents (64 < |A| <= mid_max): closure tests by incidence ------------
+//
+// For a parent (A, B, y) let J be the attributes outside B above y, and U the
+// members of J carried by some object of A.  Every incidence (object g of A,
+// attribute j in U that g has) ANDs row g into D_j and counts g into |C_j|,
+// with one D_j per member of U kept in LDS.  C_j is then exactly the objects of
+// A having j, D_j = C_j' (page 1, sections 2.1 and 4.2), and the canonical test
+// of j reads D_j (page 1, section 4.3).  Work per parent is the number of
+// incidences, not candidates x |A|.  A candidate of J outside U has C = {} and
+// D = M, so only the first attribute not in B can pass that way (the bottom).
+//
+// Passing children are emitted as records of 3 + wm words:
+//   [0] parent | j << 32, [1] sibling rank | |C| << 32, [2] object offset of
+//   the child's list inside the parent's children, [3..] D.
+
 template <int WMC>
-__global__ void __launch_bounds__(kBlock) k_big_test(LevelArgs A)
+__global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
+{
+    constexpr int kMaxCand = kWave * WMC;
+    __shared__ uint64_t s_d[kMidWaves][kMaxCand * WMC];
+    __shared__ uint32_t s_c[kMidWaves][kMaxCand];
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    const int wm = words_of<WMC>(A.wm);
+    uint64_t *Dt = s_d[wv];
+    uint32_t *Ct = s_c[wv];
+    const uint64_t count = A.counters[CNT_MID];
+    const uint64_t rstride = 3 + (uint64_t)A.wm;
+    for (uint64_t it = (uint64_t)blockIdx.x * kMidWaves + wv; it < count; it += (uint64_t)gridDim.x * kMidWaves) {
+        const uint64_t p = A.mid_idx[it];
+        const uint64_t c0 = A.lo + p;
+        const uint64_t o0 = A.loff[c0], o1 = A.loff[c0 + 1];
+        const int y = A.cursor[c0];
+        uint64_t Bx[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            Bx[u] = ~0ull;
+            if (u < wm) {
+                Bx[u] = A.intents[c0 * A.wm + u];
+                if (u == wm - 1) Bx[u] |= ~A.tail_m;
+            }
+        }
+        // U: candidates carried by some object of A
+        uint64_t U[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) U[u] = 0;
+        for (uint64_t o = o0 + lane; o < o1; o += kWave) {
+            const uint64_t g = A.objs[o];
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                if (u < wm) U[u] |= A.rows[g * A.wm + u];
+        }
+        int nU = 0, j0 = -1;
+        int pre[WMC];  // members of U in the words before u
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            pre[u] = nU;
+            if (u < wm) {
+                const uint64_t nb = ~Bx[u];
+                if (j0 < 0 && nb) j0 = 64 * u + __ffsll((unsigned long long)nb) - 1;
+                U[u] = wave_or(U[u]) & nb & above_mask(y, u);
+                nU += __popcll(U[u]);
+            }
+        }
+        for (int x = lane; x < nU * WMC; x += kWave) Dt[x] = ~0ull;
+        for (int x = lane; x < nU; x += kWave) Ct[x] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // incidences
+        for (uint64_t o = o0 + lane; o < o1; o += kWave) {
+            const uint64_t g = A.objs[o];
+            uint64_t row[WMC];
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) row[u] = (u < wm) ? A.rows[g * A.wm + u] : 0ull;
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) {
+                uint64_t x = row[u] & U[u];
+                while (x) {
+                    const int b = __ffsll((unsigned long long)x) - 1;
+                    x &= x - 1ull;
+                    const int r = pre[u] + __popcll(U[u] & below_mask(b));
+#pragma unroll
+                    for (int v = 0; v < WMC; ++v)
+                        if (v < wm) atomicAnd((unsigned long long *)&Dt[r * WMC + v], (unsigned long long)row[v]);
+                    atomicAdd(&Ct[r], 1u);
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // canonical tests and child records
+        uint32_t run_rank = 0, run_obj = 0;
+        bool bottom = false;
+        if (j0 > y) {
+            bottom = true;
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                if (u == (j0 >> 6) && ((U[u] >> (j0 & 63)) & 1ull)) bottom = false;
+        }
+        if (bottom) {  // the first attribute outside B: C = {}, D = M, rank 0
+            if (lane == 0) {
+                const uint64_t pos = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC], 1ull);
+                if (pos < A.mrec_cap) {
+                    uint64_t *rec = A.mrec + pos * rstride;
+                    rec[0] = p | ((uint64_t)j0 << 32);
+                    rec[1] = 0;
+                    rec[2] = 0;
+                    for (int u = 0; u < wm; ++u) rec[3 + u] = (u == wm - 1) ? A.tail_m : ~0ull;
+                } else {
+                    A.counters[CNT_OVERFLOW] = 1;
+                }
+            }
+            run_rank = 1;
+        }
+        for (int r0 = 0; r0 < nU; r0 += kWave) {
+            const int r = r0 + lane;
+            const bool active = r < nU;
+            const int j = active ? select_words<WMC>(U, wm, r) : 0;
+            const int wj = j >> 6, bj = j & 63;
+            uint64_t bad = 0;
+            if (active) {
+#pragma unroll
+                for (int u = 0; u < WMC; ++u) {
+                    if (u < wm && u <= wj) {
+                        const uint64_t extra = Dt[r * WMC + u] & ~Bx[u];
+                        bad |= (u < wj) ? extra : (extra & below_mask(bj));
+                    }
+                }
+            }
+            const bool pass = active && bad == 0;
+            const uint32_t cnt = pass ? Ct[r] : 0u;
+            const uint64_t bal = __ballot(pass);
+            if (!bal) continue;
+            const int leader = __ffsll((unsigned long long)bal) - 1;
+            uint64_t base = 0;
+            if (lane == leader)
+                base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC], (unsigned long long)__popcll(bal));
+            base = __shfl(base, leader);
+            const uint32_t before = (uint32_t)__popcll(bal & below_mask(lane));
+            const uint32_t objoff = run_obj + wave_excl_scan(cnt);
+            if (pass) {
+                const uint64_t pos = base + before;
+                if (pos < A.mrec_cap) {
+                    uint64_t *rec = A.mrec + pos * rstride;
+                    rec[0] = p | ((uint64_t)j << 32);
+                    rec[1] = (uint64_t)(run_rank + before) | ((uint64_t)cnt << 32);
+                    rec[2] = objoff;
+#pragma unroll
+                    for (int u = 0; u < WMC; ++u)
+                        if (u < wm) rec[3 + u] = (u == wm - 1) ? (Dt[r * WMC + u] & A.tail_m) : Dt[r * WMC + u];
+                } else {
+                    A.counters[CNT_OVERFLOW] = 1;
+                }
+            }
+            run_rank += (uint32_t)__popcll(bal);
+            run_obj += wave_sum(cnt);
+        }
+        if (lane == 0) {
+            A.nchild[p] = run_rank;
+            A.nobj[p] = run_obj;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// Children of the mid parents, one wavefront per record: intent and cursor
+// come from the record, the extent list from a scan of the parent's list for
+// the objects having j (ascending).
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
 {
     const int lane = lane_id();
+    if (A.counters[CNT_OVERFLOW]) return;
+    const uint64_t nrec = A.counters[CNT_MIDREC];
+    const uint64_t rstride = 3 + (uint64_t)A.wm;
+    for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; i < nrec;
+         i += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t *rec = A.mrec + i * rstride;
+        const uint64_t w0 = rec[0], w1 = rec[1];
+        const uint64_t p = w0 & 0xFFFFFFFFull;
+        const int j = (int)(w0 >> 32);
+        const uint32_t cnt = (uint32_t)(w1 >> 32);
+        const uint64_t c0 = A.lo + p;
+        const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
+        const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
+        for (int u = lane; u < A.wm; u += kWave) A.intents[child * A.wm + u] = rec[3 + u];
+        if (lane == 0) {
+            A.cursor[child] = j;
+            A.loff[child] = obeg;
+            A.loff[child + 1] = obeg + cnt;
+        }
+        if (cnt == 0) continue;
+        uint64_t qo = obeg;
+        scan_list_for_attr(A, A.loff[c0], A.loff[c0 + 1], j, [&](bool in, uint32_t g, uint64_t bal) {
+            if (in) A.objs[qo + __popcll(bal & below_mask(lane))] = g;
+            qo += __popcll(bal);
+        });
+    }
+}
+
+// Closure tests of huge parents through their object lists, one wavefront per
+// task: an object is in C when its bit in col[j] is set, and its row is ANDed
+// into the lane's partial D (page 1, section 4.2: the extent's set bits are
+// walked, rows ANDed, then a wavefront AND-reduction).
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_big_test_list(LevelArgs A)
+{
+    const BigSet &S = A.huge;
+    const int lane = lane_id();
     const int wm = words_of<WMC>(A.wm);
-    const uint64_t nbig = A.counters[CNT_BIG];
-    const uint64_t tbig = A.big_off[nbig];
-    if (tbig > A.bt_cap) return;
-    for (uint64_t t = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < tbig;
+    if (A.counters[CNT_OVERFLOW]) return;
+    const uint64_t tset = S.off[A.counters[S.cnt_slot]];
+    for (uint64_t t = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < tset;
          t += (uint64_t)gridDim.x * kWavesPerBlock) {
-        const uint64_t task = A.tasks[t];
+        const uint64_t task = S.tasks[t];
         const uint64_t bi = task >> 16;
         const int j = (int)(task & 0xFFFFu);
-        const uint64_t p = A.big_idx[bi];
+        const uint64_t p = S.idx[bi];
         const uint64_t c0 = A.lo + p;
         const int wj = j >> 6, bj = j & 63;
         uint64_t D[WMC];
@@ -703,54 +990,39 @@ __global__ void __launch_bounds__(kBlock) k_big_test(LevelArgs A)
                 uint64_t bx = A.intents[c0 * A.wm + u];
                 if (u == wm - 1) bx |= ~A.tail_m;
                 const uint64_t extra = wave_and(D[u]) & ~bx;
-                if (u < wj) bad |= extra;
-                else bad |= extra & below_mask(bj);
+                bad |= (u < wj) ? extra : (extra & below_mask(bj));
             }
         }
         const bool pass = bad == 0;
         if (lane == 0) {
-            A.bt_size[t] = pass ? cnt : 0u;
-            if (pass) {
-                atomicOr((unsigned long long *)&A.pass[p * A.wm + wj], (unsigned long long)(1ull << bj));
-                atomicAdd(&A.nchild[p], 1u);
-                atomicAdd(&A.nobj[p], cnt);
-                const uint64_t pos = atomicAdd((unsigned long long *)&A.counters[CNT_BIGPASS], 1ull);
-                A.plist[pos] = t;
-            }
+            S.size[t] = pass ? cnt : 0u;
+            if (pass) big_record_pass(A, S, t, p, j, cnt);
         }
     }
 }
 
-// Children of big parents, one wavefront per passing task.  The child's rank
-// among its siblings is the number of passing attributes below j; its list
-// offset comes from the scan of the passing tasks' |C|.
+// Children of huge parents through their object lists, one wavefront per
+// passing task.  The child's rank among its siblings is the number of passing
+// attributes below j; its list offset comes from the scan of the passing
+// tasks' |C|.
 template <int WMC>
-__global__ void __launch_bounds__(kBlock) k_big_write(LevelArgs A)
+__global__ void __launch_bounds__(kBlock) k_big_write_list(LevelArgs A)
 {
+    const BigSet &S = A.huge;
     const int lane = lane_id();
     const int wm = words_of<WMC>(A.wm);
-    const uint64_t nbig = A.counters[CNT_BIG];
-    if (A.big_off[nbig] > A.bt_cap) return;
-    const uint64_t npass = A.counters[CNT_BIGPASS];
+    if (A.counters[CNT_OVERFLOW]) return;
+    const uint64_t npass = A.counters[S.pass_slot];
     for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; i < npass;
          i += (uint64_t)gridDim.x * kWavesPerBlock) {
-        const uint64_t t = A.plist[i];
-        const uint64_t task = A.tasks[t];
+        const uint64_t t = S.plist[i];
+        const uint64_t task = S.tasks[t];
         const uint64_t bi = task >> 16;
         const int j = (int)(task & 0xFFFFu);
-        const uint64_t p = A.big_idx[bi];
+        const uint64_t p = S.idx[bi];
         const uint64_t c0 = A.lo + p;
-        const int wj = j >> 6, bj = j & 63;
-        int rank = 0;
-#pragma unroll
-        for (int u = 0; u < WMC; ++u) {
-            if (u < wm && u <= wj) {
-                const uint64_t pm = A.pass[p * A.wm + u];
-                rank += __popcll(u < wj ? pm : (pm & below_mask(bj)));
-            }
-        }
-        const uint64_t child = A.child_lo + A.cbase[p] + (uint64_t)rank;
-        const uint64_t obeg = A.child_obj_lo + A.obase[p] + (A.bt_sscan[t] - A.bt_sscan[A.big_off[bi]]);
+        const uint64_t child = A.child_lo + A.cbase[p] + (uint64_t)pass_rank<WMC>(A, p, j);
+        const uint64_t obeg = A.child_obj_lo + A.obase[p] + (S.sscan[t] - S.sscan[S.off[bi]]);
         uint64_t D[WMC];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
@@ -776,6 +1048,141 @@ __global__ void __launch_bounds__(kBlock) k_big_write(LevelArgs A)
             A.cursor[child] = j;
             A.loff[child] = obeg;
             A.loff[child + 1] = qo;
+        }
+    }
+}
+
+// --- extent bitmaps, one work item per (test, 64-word chunk) (huge set) ------------
+//
+// A closure test of a huge parent is split over the 64-word chunks of the
+// extent bitmap: each item forms its part of C = A AND col[j] with one
+// coalesced load per lane, ANDs the rows of its objects and folds the partial
+// D and |C| into the test's accumulators.  Every item is short, so levels with
+// a handful of huge parents (the root: every object) still fill the chip.
+
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_huge_partial(LevelArgs A)
+{
+    const BigSet &S = A.huge;
+    const int lane = lane_id();
+    const int wm = words_of<WMC>(A.wm);
+    if (A.counters[CNT_OVERFLOW]) return;
+    const uint64_t items = S.off[A.counters[S.cnt_slot]] * (uint64_t)A.nchunk;
+    for (uint64_t it = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; it < items;
+         it += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t t = it / (uint64_t)A.nchunk;
+        const int k = (int)(it - t * (uint64_t)A.nchunk);
+        const uint64_t task = S.tasks[t];
+        const uint64_t bi = task >> 16;
+        const int j = (int)(task & 0xFFFFu);
+        const int w = kWave * k + lane;
+        uint64_t c = 0;
+        if (w < A.wn) c = S.bmp[bi * (uint64_t)A.wn + w] & A.cols[(uint64_t)j * A.wn + w];
+        const uint32_t tot = wave_sum((uint32_t)__popcll(c));
+        if (lane == 0) A.icnt[it] = tot;
+        if (tot == 0) continue;
+        uint64_t D[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
+        const uint64_t base = (uint64_t)w * 64;
+        while (c) {
+            const uint64_t g0 = base + (uint64_t)(__ffsll((unsigned long long)c) - 1);
+            c &= c - 1ull;
+            uint64_t g1 = g0;
+            if (c) {
+                g1 = base + (uint64_t)(__ffsll((unsigned long long)c) - 1);
+                c &= c - 1ull;
+            }
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                if (u < wm) D[u] &= A.rows[g0 * A.wm + u] & A.rows[g1 * A.wm + u];
+        }
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            if (u < wm) {
+                const uint64_t d = wave_and(D[u]);
+                if (lane == 0 && d != ~0ull) atomicAnd((unsigned long long *)&A.dt[t * A.wm + u], (unsigned long long)d);
+            }
+        }
+        if (lane == 0) atomicAdd(&A.tcnt[t], tot);
+    }
+}
+
+// One thread per huge test: the canonical test on the accumulated D (all of M
+// when C is empty); a passing test turns its chunk counts into offsets inside
+// the child's list.
+__global__ void __launch_bounds__(kBlock) k_huge_finalize(LevelArgs A)
+{
+    const BigSet &S = A.huge;
+    if (A.counters[CNT_OVERFLOW]) return;
+    const uint64_t tset = S.off[A.counters[S.cnt_slot]];
+    for (uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tset; t += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t task = S.tasks[t];
+        const uint64_t bi = task >> 16;
+        const int j = (int)(task & 0xFFFFu);
+        const uint64_t p = S.idx[bi];
+        const uint64_t c0 = A.lo + p;
+        const int wj = j >> 6, bj = j & 63;
+        uint64_t bad = 0;
+        for (int u = 0; u <= wj; ++u) {
+            uint64_t bx = A.intents[c0 * A.wm + u];
+            if (u == A.wm - 1) bx |= ~A.tail_m;
+            const uint64_t extra = A.dt[t * A.wm + u] & ~bx;
+            bad |= (u < wj) ? extra : (extra & below_mask(bj));
+        }
+        const uint32_t cnt = A.tcnt[t];
+        const bool pass = bad == 0;
+        S.size[t] = pass ? cnt : 0u;
+        if (!pass) continue;
+        big_record_pass(A, S, t, p, j, cnt);
+        uint32_t run = 0;
+        for (int k = 0; k < A.nchunk; ++k) {
+            const uint32_t v = A.icnt[t * A.nchunk + k];
+            A.icnt[t * A.nchunk + k] = run;
+            run += v;
+        }
+    }
+}
+
+// Children of huge parents, one item per (passing test, chunk): the chunk's
+// objects go to their place in the child's list (ascending); chunk 0 also
+// writes the intent (the accumulated D), cursor and list bounds.
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_huge_write(LevelArgs A)
+{
+    const BigSet &S = A.huge;
+    const int lane = lane_id();
+    if (A.counters[CNT_OVERFLOW]) return;
+    const uint64_t items = A.counters[S.pass_slot] * (uint64_t)A.nchunk;
+    for (uint64_t it = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; it < items;
+         it += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t pi = it / (uint64_t)A.nchunk;
+        const int k = (int)(it - pi * (uint64_t)A.nchunk);
+        const uint64_t t = S.plist[pi];
+        const uint64_t task = S.tasks[t];
+        const uint64_t bi = task >> 16;
+        const int j = (int)(task & 0xFFFFu);
+        const uint64_t p = S.idx[bi];
+        const uint64_t obeg = A.child_obj_lo + A.obase[p] + (S.sscan[t] - S.sscan[S.off[bi]]);
+        const int w = kWave * k + lane;
+        uint64_t c = 0;
+        if (w < A.wn) c = S.bmp[bi * (uint64_t)A.wn + w] & A.cols[(uint64_t)j * A.wn + w];
+        uint64_t q = obeg + A.icnt[t * A.nchunk + k] + wave_excl_scan((uint32_t)__popcll(c));
+        const uint32_t base = (uint32_t)w * 64u;
+        while (c) {
+            A.objs[q++] = base + (uint32_t)(__ffsll((unsigned long long)c) - 1);
+            c &= c - 1ull;
+        }
+        if (k == 0 && lane == 0) {
+            const uint64_t child = A.child_lo + A.cbase[p] + (uint64_t)pass_rank<WMC>(A, p, j);
+            for (int u = 0; u < A.wm; ++u) {
+                uint64_t d = A.dt[t * A.wm + u];
+                if (u == A.wm - 1) d &= A.tail_m;
+                A.intents[child * A.wm + u] = d;
+            }
+            A.cursor[child] = j;
+            A.loff[child] = obeg;
+            A.loff[child + 1] = obeg + A.tcnt[t];
         }
     }
 }

@@ -101,6 +101,17 @@ def test_wide_attribute_sets(n, m, d):
     assert_parity(synth.random_context(n * m, n, m, d))
 
 
+def test_many_objects():
+    # large extents: big parents split into 64-word chunks of their extent bitmap
+    assert_parity(synth.random_context(70024, 70000, 24, 0.08))
+    assert_parity(synth.random_context(70040, 70000, 40, 0.05), flags=fca.FCBO_TINY_BUFFERS)
+
+
+def test_over_a_million_objects_list_path():
+    # more than 2^20 objects: big parents are scanned through their object lists
+    assert_parity(synth.random_context(1100006, 1_100_000, 6, 0.3), extents=False)
+
+
 @pytest.mark.parametrize("n,m", [(65, 130), (130, 5), (1, 1), (300, 64)])
 def test_all_zero(n, m):
     # the bottom ({}, M) comes from a parent with more than 64 objects when n > 64
