@@ -132,6 +132,9 @@ struct fcbo_context {
     uint64_t *pass = nullptr, *cbase = nullptr, *obase = nullptr;
     uint32_t *nchild = nullptr, *nobj = nullptr, *mid_idx = nullptr;
     uint64_t *mrec = nullptr;  // child records of the mid parents (words)
+    uint64_t cap_lrec = 0, cap_lfill = 0;
+    uint64_t *lrec = nullptr;  // child records of the local parents (words)
+    uint32_t *lfill = nullptr; // records per 64-slot chunk
     BigStore huge;
     uint64_t cap_dt = 0, cap_tcnt = 0, cap_icnt = 0;
     uint64_t *dt = nullptr;                     // huge tests: D accumulators
@@ -195,7 +198,7 @@ struct fcbo_context {
     {
         dfree(rows); dfree(cols);
         dfree(intents); dfree(cursor); dfree(loff); dfree(objs);
-        dfree(pass); dfree(cbase); dfree(obase); dfree(nchild); dfree(nobj); dfree(mid_idx); dfree(mrec);
+        dfree(pass); dfree(cbase); dfree(obase); dfree(nchild); dfree(nobj); dfree(mid_idx); dfree(mrec); dfree(lrec); dfree(lfill);
         huge.free_all();
         dfree(dt); dfree(tcnt); dfree(icnt);
         dfree(scan_part); dfree(counters);
@@ -228,7 +231,10 @@ struct fcbo_context {
         A.mid_idx = mid_idx;
         A.mid_max = wm <= 8 ? kMidMax : kSmallMax;
         A.mrec = mrec;
-        A.mrec_cap = cap_mrec / (3 + (uint64_t)wm);
+        A.mrec_cap = cap_mrec / (4 + (uint64_t)wm);
+        A.lrec = lrec;
+        A.lfill = lfill;
+        A.lrec_cap = std::min(cap_lrec / (4 + (uint64_t)wm), cap_lfill * kWave);
         const bool bm = use_bitmaps();
         A.huge = huge.view(CNT_HUGE, CNT_THUGE, CNT_HUGEPASS, bm);
         if (bm) A.huge.cap = std::min(A.huge.cap, std::min(std::min(cap_dt / wm, cap_tcnt), cap_icnt / nchunk()));
@@ -255,6 +261,13 @@ struct fcbo_context {
         CK_LAUNCH();
     }
 
+    // local child records: `slots` rounded up to whole 64-slot chunks
+    void ensure_local_records(uint64_t slots)
+    {
+        const uint64_t chunks = div_up(slots, kWave) + 1;
+        ensure(lrec, cap_lrec, chunks * kWave * (4 + (uint64_t)wm), 0, stream, 1);
+        ensure(lfill, cap_lfill, chunks, 0, stream, 1);
+    }
     void enumerate_levels();
     void sort_intents();
     void write_output(uint64_t *intents_out, uint64_t *extents_out);
@@ -265,7 +278,6 @@ namespace {
 template <int WMC>
 void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
 {
-    const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kWavesPerBlock)));
     const unsigned gm = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(1024, div_up(P, kWavesPerBlock)));
     const bool bm = A.huge.bmp != nullptr;
     hipEvent_t b = c->prof_begin();
@@ -273,7 +285,11 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
     CK_LAUNCH();
     c->prof_end(FCBO_K_TEST_BIG, b);
     b = c->prof_begin();
-    hipLaunchKernelGGL((k_local_test<WMC, 1>), dim3(gl), dim3(kBlock), 0, c->stream, A);
+    {
+        constexpr int kW = LocalCfg<WMC>::kWaves;
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap * 4 / kW, div_up(P, kW)));
+        hipLaunchKernelGGL(k_local_test<WMC>, dim3(g), dim3(LocalCfg<WMC>::kThreads), 0, c->stream, A);
+    }
     CK_LAUNCH();
     c->prof_end(FCBO_K_TEST_LOCAL, b);
     if constexpr (WMC <= 8) {
@@ -298,9 +314,9 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
 template <int WMC>
 void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P)
 {
-    const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kWavesPerBlock)));
+    const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kBlock)));
     hipEvent_t b = c->prof_begin();
-    hipLaunchKernelGGL((k_local_write<WMC, 1>), dim3(gl), dim3(kBlock), 0, c->stream, A);
+    hipLaunchKernelGGL(k_local_write, dim3(gl), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
     c->prof_end(FCBO_K_WRITE_LOCAL, b);
     if constexpr (WMC <= 8) {
@@ -368,13 +384,14 @@ void fcbo_context::enumerate_levels()
     lev_tests.clear();
     tests = pairs = sum_c = 0;
     local_parents = local_objs = med_parents = med_objs = big_parents = big_tests = big_scan = 0;
-    const uint64_t rstride = 3 + (uint64_t)wm;
+    const uint64_t rstride = 4 + (uint64_t)wm;
     if (!huge.tasks) {
         if (bm) ensure_huge_tests(tiny ? 1 : (1u << 16));
         else huge.ensure_tests(tiny ? 1 : (1u << 20), stream, mc);
     }
     if (bm && !huge.bmp) ensure(huge.bmp, huge.cap_bmp, (uint64_t)wn * (tiny ? 1 : 64), 0, stream, 1);
     if (!mrec) ensure(mrec, cap_mrec, rstride * (tiny ? 1 : (1u << 18)), 0, stream, 1);
+    if (!lrec) ensure_local_records(tiny ? kWave : (1u << 21));
     uint64_t lo = 0, P = 1, obj_hi = (uint64_t)n;  // parents [lo, lo+P); objects used so far
     while (P > 0) {
         if (P >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
@@ -418,6 +435,7 @@ void fcbo_context::enumerate_levels()
                     huge.ensure_tests(h_counters[CNT_THUGE], stream, mc);
                 }
                 ensure(mrec, cap_mrec, h_counters[CNT_MIDREC] * rstride, 0, stream, 1);
+                ensure_local_records(h_counters[CNT_LOCREC]);
                 redo = true;
                 ++redos;
                 continue;

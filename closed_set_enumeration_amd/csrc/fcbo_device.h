@@ -56,6 +56,7 @@ enum {
     CNT_HUGEPASS = 10, // passing huge tests
     CNT_MID_OBJS = 11, // objects in the extents of mid parents
     CNT_MIDREC = 12,   // child records written by the mid parents
+    CNT_LOCREC = 13,   // record slots reserved by the local parents (64 per chunk)
     CNT_N = 14
 };
 
@@ -100,6 +101,9 @@ struct LevelArgs {
     int mid_max;           // parents with more objects are huge
     uint64_t *mrec;        // child records of the mid parents (see k_mid_test)
     uint64_t mrec_cap;     // records
+    uint64_t *lrec;        // child records of the local parents, in chunks of 64 slots
+    uint32_t *lfill;       // records used in each chunk of lrec
+    uint64_t lrec_cap;     // slots (a multiple of 64)
     BigSet huge;           // huge parents
     uint64_t *dt;          // per huge test: AND of the rows of C, wm words
     uint32_t *tcnt;        // per huge test: |C|
@@ -380,10 +384,10 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
     }
 }
 
-// Closure tests of one parent (A, B, y) with |A| <= 64 * NCH, one wavefront.
+// --- local parents (|A| <= 64): closure tests in one wavefront ------------------
 //
 // The rows of the objects of A are staged in LDS.  For a candidate j (j > y,
-// j not in B) let c_j be the objects of A having j, as a bitmask over the
+// j not in B) let c_j be the objects of A having j, as a 64-bit mask over the
 // staged rows: C = A AND col[j] restricted to A.  D = C' is the AND of their
 // rows, and the canonical test asks that D adds no attribute below j to B
 // (page 1, section 4.3: bits 0..j-1 compared, bit j excluded).
@@ -397,78 +401,135 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
 // Attribute-saturation pruning (page 1, section 2.3) is the j-in-B skip: with
 // B closed, A inside col[j] holds exactly when j is in B.
 //
-// The kernel walks all parents of the level and skips those with more than
-// 64 * NCH objects.
-template <int NCH>
-struct LocalShape {
-    static constexpr int kWaves = kWavesPerBlock;  // wavefronts per block
+// Per-parent values are wave-uniform (read once, kept in scalar registers).
+// Passing children leave records (layout in k_mid_test) with the object mask
+// c_j in word 3, so the child write needs no recomputation.
+
+template <int WMC>
+struct LocalCfg {
+    static constexpr int kWaves = WMC <= 8 ? kWavesPerBlock : 1;  // wavefronts per block
     static constexpr int kThreads = kWave * kWaves;
 };
 
-template <int WMC, int NCH>
-__global__ void __launch_bounds__(LocalShape<NCH>::kThreads) k_local_test(LevelArgs A)
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
 {
-    constexpr int kMaxObj = kWave * NCH;
-    constexpr int kW = LocalShape<NCH>::kWaves;
-    __shared__ uint64_t s_rows[kW][kMaxObj * WMC];
-    __shared__ uint64_t s_pm[kW][WMC];
-    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Set bits of a uniform mask below the calling lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Reserve `n = popcount(bal)` consecutive slots of a device counter for the
+// flagged lanes of a wavefront; returns this lane's slot.
+__device__ __forceinline__ uint64_t wave_slot(uint64_t bal, uint64_t *counter)
+{
+    const int leader = __ffsll((unsigned long long)bal) - 1;
+    uint64_t base = 0;
+    if (lane_id() == leader) base = atomicAdd((unsigned long long *)counter, (unsigned long long)__popcll(bal));
+    base = __shfl(base, leader);
+    return base + lanes_below(bal);
+}
+
+template <int WMC>
+__global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArgs A)
+{
+    constexpr int kW = LocalCfg<WMC>::kWaves;
+    __shared__ uint64_t s_rows[kW][kSmallMax * WMC];
+    __shared__ uint64_t s_u[kW][WMC];
+    __shared__ uint32_t s_cand[kW][kWave * WMC];
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = words_of<WMC>(A.wm);
     uint64_t *R = s_rows[wv];
-    uint64_t *PM = s_pm[wv];
-    for (uint64_t p = (uint64_t)blockIdx.x * kW + wv; p < A.P; p += (uint64_t)gridDim.x * kW) {
-        const uint64_t c0 = A.lo + p;
-        const uint64_t o0 = A.loff[c0];
-        const uint64_t a64 = A.loff[c0 + 1] - o0;
-        if (a64 > (uint64_t)(kWave * NCH)) continue;
-        const int a = (int)a64;
-        const int y = A.cursor[c0];
+    const uint32_t *R32 = (const uint32_t *)R;
+    uint64_t *SU = s_u[wv];
+    uint32_t *CAND = s_cand[wv];
+    const uint64_t rstride = 4 + (uint64_t)A.wm;
+    // Record slots are reserved 64 at a time per wavefront; a round's passing
+    // children go to one chunk (a chunk that cannot hold them is closed).
+    uint64_t chunk = ~0ull;  // first slot of the current chunk
+    uint32_t fill = kWave;   // slots used in it
+    auto reserve = [&](uint32_t n) -> uint64_t {
+        if (fill + n > (uint32_t)kWave) {
+            if (chunk != ~0ull && lane == 0 && chunk < A.lrec_cap) A.lfill[chunk / kWave] = fill;
+            uint64_t c = 0;
+            if (lane == 0) c = atomicAdd((unsigned long long *)&A.counters[CNT_LOCREC], (unsigned long long)kWave);
+            chunk = uniform64(c);
+            fill = 0;
+            if (chunk + kWave > A.lrec_cap && lane == 0) A.counters[CNT_OVERFLOW] = 1;
+        }
+        const uint64_t at = chunk + fill;
+        fill += n;
+        return at;
+    };
+    if (lane < WMC) SU[lane] = 0;
+    // The parent's offsets, cursor and intent are loaded one parent ahead, so
+    // their latency overlaps the work on the current parent.
+    const uint64_t stride = (uint64_t)gridDim.x * kW;
+    uint64_t p = (uint64_t)blockIdx.x * kW + wv;
+    uint64_t n_o0 = 0, n_o1 = 0, n_b[WMC];
+    int32_t n_y = 0;
+    auto fetch = [&](uint64_t q) {
+        if (q < A.P) {
+            const uint64_t c = A.lo + q;
+            n_o0 = A.loff[c];
+            n_o1 = A.loff[c + 1];
+            n_y = A.cursor[c];
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) n_b[u] = (u < wm) ? A.intents[c * A.wm + u] : 0ull;
+        }
+    };
+    fetch(p);
+    for (; p < A.P; p += stride) {
+        const uint64_t o0 = uniform64(n_o0);
+        const uint64_t o1 = uniform64(n_o1);
+        const int y = (int)__builtin_amdgcn_readfirstlane((uint32_t)n_y);
         uint64_t Bx[WMC];  // B plus the padding bits past M
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
             Bx[u] = ~0ull;
-            if (u < wm) {
-                Bx[u] = A.intents[c0 * A.wm + u];
-                if (u == wm - 1) Bx[u] |= ~A.tail_m;
-            }
+            if (u < wm) Bx[u] = uniform64(n_b[u]) | ((u == wm - 1) ? ~A.tail_m : 0ull);
         }
-        uint64_t U[WMC];  // attributes carried by some object of A
+        fetch(p + stride);
+        if (o1 - o0 > (uint64_t)kSmallMax) continue;
+        const int a = (int)(o1 - o0);
+        if (lane < a) {
+            const uint64_t g = A.objs[o0 + lane];
 #pragma unroll
-        for (int u = 0; u < WMC; ++u) U[u] = 0;
-#pragma unroll
-        for (int q = 0; q < NCH; ++q) {
-            const int i = lane + kWave * q;
-            if (i < a) {
-                const uint64_t g = A.objs[o0 + i];
-#pragma unroll
-                for (int u = 0; u < WMC; ++u) {
-                    if (u < wm) {
-                        const uint64_t r = A.rows[g * A.wm + u];
-                        R[i * WMC + u] = r;
-                        U[u] |= r;
-                    }
+            for (int u = 0; u < WMC; ++u) {
+                if (u < wm) {
+                    const uint64_t r = A.rows[g * A.wm + u];
+                    R[lane * WMC + u] = r;
+                    atomicOr((unsigned long long *)&SU[u], (unsigned long long)r);
                 }
             }
         }
-        if (lane < wm) PM[lane] = 0;
-#pragma unroll
-        for (int u = 0; u < WMC; ++u)
-            if (u < wm) U[u] = wave_or(U[u]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        int nU = 0;
-        int j0 = -1;  // first attribute not in B
+        // U, its prefix counts, the first attribute outside B; candidate list in LDS
+        uint64_t U[WMC];
+        int nU = 0, j0 = -1;
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
+            U[u] = 0;
             if (u < wm) {
                 const uint64_t nb = ~Bx[u];
                 if (j0 < 0 && nb) j0 = 64 * u + __ffsll((unsigned long long)nb) - 1;
-                U[u] &= nb & above_mask(y, u);
+                U[u] = uniform64(SU[u]) & nb & above_mask(y, u);
+                if ((U[u] >> lane) & 1ull) CAND[nU + lanes_below(U[u])] = (uint32_t)(64 * u + lane);
                 nU += __popcll(U[u]);
             }
         }
+        if (lane < WMC) SU[lane] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         bool bottom = false;
         if (j0 > y) {
             bottom = true;
@@ -476,157 +537,116 @@ __global__ void __launch_bounds__(LocalShape<NCH>::kThreads) k_local_test(LevelA
             for (int u = 0; u < WMC; ++u)
                 if (u == (j0 >> 6) && ((U[u] >> (j0 & 63)) & 1ull)) bottom = false;
         }
-        uint32_t nch = bottom ? 1u : 0u, nob = 0;
-        if (bottom && lane == 0) PM[j0 >> 6] |= 1ull << (j0 & 63);
-
-        for (int r = 0; r < nU; r += kWave) {
-            const int k = r + lane;
-            const bool active = k < nU;
-            const int j = active ? select_words<WMC>(U, wm, k) : 0;
-            const int wj = j >> 6, bj = j & 63;
-            uint64_t cj[NCH];
-#pragma unroll
-            for (int q = 0; q < NCH; ++q) {
-                uint64_t cq = 0;
-                const int lim = a - kWave * q < kWave ? a - kWave * q : kWave;
-                for (int ii = 0; ii < lim; ++ii) cq |= ((R[(kWave * q + ii) * WMC + wj] >> bj) & 1ull) << ii;
-                cj[q] = cq;
-            }
-            uint64_t Dn[WMC];  // attributes outside B shared by the objects of c_j
-#pragma unroll
-            for (int u = 0; u < WMC; ++u) Dn[u] = ~Bx[u];
-            uint32_t sz = 0;
-#pragma unroll
-            for (int q = 0; q < NCH; ++q) {
-                uint64_t cc = active ? cj[q] : 0ull;
-                sz += (uint32_t)__popcll(cc);
-                while (cc) {
-                    const int i = kWave * q + __ffsll((unsigned long long)cc) - 1;
-                    cc &= cc - 1ull;
-#pragma unroll
-                    for (int u = 0; u < WMC; ++u)
-                        if (u < wm && u <= wj) Dn[u] &= R[i * WMC + u];
+        uint32_t run_rank = 0, run_obj = 0;
+        if (bottom) {  // C = {}, D = M, the first child in j order
+            const uint64_t pos = reserve(1);
+            if (lane == 0) {
+                if (pos < A.lrec_cap) {
+                    uint64_t *rec = A.lrec + pos * rstride;
+                    rec[0] = p | ((uint64_t)j0 << 32);
+                    rec[1] = 0;
+                    rec[2] = 0;
+                    rec[3] = 0;
+                    for (int u = 0; u < wm; ++u) rec[4 + u] = (u == wm - 1) ? A.tail_m : ~0ull;
                 }
             }
-            uint64_t bad = 0;
-#pragma unroll
-            for (int u = 0; u < WMC; ++u) {
-                if (u < wj) bad |= Dn[u];
-                else if (u == wj) bad |= Dn[u] & below_mask(bj);
-            }
-            const bool pass = active && bad == 0;
-            const uint64_t bal = __ballot(pass);
-            nch += (uint32_t)__popcll(bal);
-            nob += wave_sum(pass ? sz : 0u);
-            if (pass) atomicOr((unsigned long long *)&PM[wj], (unsigned long long)(1ull << bj));
+            run_rank = 1;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < wm) A.pass[p * A.wm + lane] = PM[lane];
+        for (int r0 = 0; r0 < nU; r0 += kWave) {
+            const int k = r0 + lane;
+            const bool active = k < nU;
+            const int j = active ? (int)CAND[k] : 0;
+            const int wj = j >> 6, bj = j & 63;
+            // c_j: objects of A having j (32-bit LDS reads, one bit each)
+            uint32_t clo = 0, chi = 0;
+            if (active) {
+                const uint32_t *col32 = R32 + 2 * wj + (bj >> 5);
+                const uint32_t sh = (uint32_t)(bj & 31);
+                const int alo = a < 32 ? a : 32;
+                for (int i = 0; i < alo; ++i) clo |= ((col32[2 * WMC * i] >> sh) & 1u) << i;
+                for (int i = 32; i < a; ++i) chi |= ((col32[2 * WMC * i] >> sh) & 1u) << (i - 32);
+            }
+            const uint64_t c = ((uint64_t)chi << 32) | clo;
+            // D = AND of the rows of c_j
+            uint64_t D[WMC];
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
+            uint64_t cc = c;
+            while (cc) {
+                const int i = __ffsll((unsigned long long)cc) - 1;
+                cc &= cc - 1ull;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm) D[u] &= R[i * WMC + u];
+            }
+            // canonical test: the first attribute of D outside B must be j itself
+            int fu = WMC;
+            uint64_t fx = 0;
+#pragma unroll
+            for (int u = WMC - 1; u >= 0; --u) {
+                const uint64_t x = (u < wm) ? (D[u] & ~Bx[u]) : 0ull;
+                if (x) {
+                    fu = u;
+                    fx = x;
+                }
+            }
+            const bool pass = active && fu == wj && (__ffsll((unsigned long long)fx) - 1) == bj;
+            const uint64_t bal = __ballot(pass);
+            if (!bal) continue;
+            const uint32_t sz = pass ? (uint32_t)__popcll(c) : 0u;
+            const uint32_t ex = wave_excl_scan(sz);
+            const uint64_t pos = reserve((uint32_t)__popcll(bal)) + lanes_below(bal);
+            if (pass) {
+                if (pos < A.lrec_cap) {
+                    uint64_t *rec = A.lrec + pos * rstride;
+                    rec[0] = p | ((uint64_t)j << 32);
+                    rec[1] = (uint64_t)(run_rank + lanes_below(bal)) | ((uint64_t)sz << 32);
+                    rec[2] = run_obj + ex;
+                    rec[3] = c;
+#pragma unroll
+                    for (int u = 0; u < WMC; ++u)
+                        if (u < wm) rec[4 + u] = (u == wm - 1) ? (D[u] & A.tail_m) : D[u];
+                }
+            }
+            run_rank += (uint32_t)__popcll(bal);
+            run_obj += __shfl(ex + sz, kWave - 1);
+        }
         if (lane == 0) {
-            A.nchild[p] = nch;
-            A.nobj[p] = nob;
+            A.nchild[p] = run_rank;
+            A.nobj[p] = run_obj;
         }
         __builtin_amdgcn_wave_barrier();
     }
+    if (chunk != ~0ull && lane == 0 && chunk < A.lrec_cap) A.lfill[chunk / kWave] = fill;
 }
 
-// Children of the local and medium parents, one wavefront per parent, one
-// lane per child: recompute c_j for the passing attributes, D = AND of their
-// rows (all of M when c_j is empty), write intent, cursor and extent list at
-// the offsets the scans gave.
-template <int WMC, int NCH>
-__global__ void __launch_bounds__(LocalShape<NCH>::kThreads) k_local_write(LevelArgs A)
+// Children of the local parents, one thread per record slot: intent, cursor and
+// list bounds from the record, the extent list picked from the parent's list by
+// the object mask.
+__global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
 {
-    constexpr int kMaxObj = kWave * NCH;
-    constexpr int kW = LocalShape<NCH>::kWaves;
-    __shared__ uint64_t s_rows[kW][kMaxObj * WMC];
-    __shared__ uint32_t s_obj[kW][kMaxObj];
-    const int lane = lane_id(), wv = threadIdx.x / kWave;
-    const int wm = words_of<WMC>(A.wm);
-    uint64_t *R = s_rows[wv];
-    uint32_t *G = s_obj[wv];
-    for (uint64_t p = (uint64_t)blockIdx.x * kW + wv; p < A.P; p += (uint64_t)gridDim.x * kW) {
-        const uint32_t nch = A.nchild[p];
-        if (nch == 0) continue;
-        const uint64_t c0 = A.lo + p;
-        const uint64_t o0 = A.loff[c0];
-        const uint64_t a64 = A.loff[c0 + 1] - o0;
-        if (a64 > (uint64_t)(kWave * NCH)) continue;
-        const int a = (int)a64;
-        uint64_t pm[WMC];
-#pragma unroll
-        for (int u = 0; u < WMC; ++u) pm[u] = (u < wm) ? A.pass[p * A.wm + u] : 0ull;
-#pragma unroll
-        for (int q = 0; q < NCH; ++q) {
-            const int i = lane + kWave * q;
-            if (i < a) {
-                const uint32_t g = A.objs[o0 + i];
-                G[i] = g;
-#pragma unroll
-                for (int u = 0; u < WMC; ++u)
-                    if (u < wm) R[i * WMC + u] = A.rows[(uint64_t)g * A.wm + u];
-            }
+    if (A.counters[CNT_OVERFLOW]) return;
+    const uint64_t nrec = A.counters[CNT_LOCREC];
+    const uint64_t rstride = 4 + (uint64_t)A.wm;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nrec; i += (uint64_t)gridDim.x * blockDim.x) {
+        if ((uint32_t)(i % kWave) >= A.lfill[i / kWave]) continue;  // unused slot of a closed chunk
+        const uint64_t *rec = A.lrec + i * rstride;
+        const uint64_t w0 = rec[0], w1 = rec[1];
+        const uint64_t p = w0 & 0xFFFFFFFFull;
+        const uint32_t cnt = (uint32_t)(w1 >> 32);
+        const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
+        const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
+        for (int u = 0; u < A.wm; ++u) A.intents[child * A.wm + u] = rec[4 + u];
+        A.cursor[child] = (int32_t)(w0 >> 32);
+        A.loff[child] = obeg;
+        A.loff[child + 1] = obeg + cnt;
+        const uint32_t *src = A.objs + A.loff[A.lo + p];
+        uint64_t c = rec[3];
+        uint64_t q = obeg;
+        while (c) {
+            A.objs[q++] = src[__ffsll((unsigned long long)c) - 1];
+            c &= c - 1ull;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint64_t cb = A.child_lo + A.cbase[p];
-        uint64_t run = A.child_obj_lo + A.obase[p];
-        for (uint32_t r = 0; r < nch; r += kWave) {
-            const uint32_t k = r + lane;
-            const bool active = k < nch;
-            const int j = active ? select_words<WMC>(pm, wm, (int)k) : 0;
-            const int wj = j >> 6, bj = j & 63;
-            uint64_t cj[NCH];
-#pragma unroll
-            for (int q = 0; q < NCH; ++q) {
-                uint64_t cq = 0;
-                const int lim = a - kWave * q < kWave ? a - kWave * q : kWave;
-                if (active)
-                    for (int ii = 0; ii < lim; ++ii) cq |= ((R[(kWave * q + ii) * WMC + wj] >> bj) & 1ull) << ii;
-                cj[q] = cq;
-            }
-            uint64_t D[WMC];
-#pragma unroll
-            for (int u = 0; u < WMC; ++u) D[u] = (u == wm - 1) ? A.tail_m : ~0ull;
-            uint32_t sz = 0;
-#pragma unroll
-            for (int q = 0; q < NCH; ++q) {
-                uint64_t cc = cj[q];
-                sz += (uint32_t)__popcll(cc);
-                while (cc) {
-                    const int i = kWave * q + __ffsll((unsigned long long)cc) - 1;
-                    cc &= cc - 1ull;
-#pragma unroll
-                    for (int u = 0; u < WMC; ++u)
-                        if (u < wm) D[u] &= R[i * WMC + u];
-                }
-            }
-            const uint64_t o = run + wave_excl_scan(sz);
-            run += wave_sum(sz);
-            if (active) {
-                const uint64_t child = cb + k;
-#pragma unroll
-                for (int u = 0; u < WMC; ++u)
-                    if (u < wm) A.intents[child * A.wm + u] = D[u];
-                A.cursor[child] = j;
-                A.loff[child] = o;
-                A.loff[child + 1] = o + sz;
-                uint64_t qo = o;
-#pragma unroll
-                for (int q = 0; q < NCH; ++q) {
-                    uint64_t cc = cj[q];
-                    while (cc) {
-                        const int i = kWave * q + __ffsll((unsigned long long)cc) - 1;
-                        cc &= cc - 1ull;
-                        A.objs[qo++] = G[i];
-                    }
-                }
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -759,9 +779,10 @@ __device__ __forceinline__ void scan_list_for_attr(const LevelArgs &A, uint64_t 
 // incidences, not candidates x |A|.  A candidate of J outside U has C = {} and
 // D = M, so only the first attribute not in B can pass that way (the bottom).
 //
-// Passing children are emitted as records of 3 + wm words:
+// Passing children are emitted as records of 4 + wm words:
 //   [0] parent | j << 32, [1] sibling rank | |C| << 32, [2] object offset of
-//   the child's list inside the parent's children, [3..] D.
+//   the child's list inside the parent's children, [3] the objects of C as a
+//   mask over the parent's list (local parents only, else 0), [4..] D.
 
 template <int WMC>
 __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
@@ -774,7 +795,7 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
     uint64_t *Dt = s_d[wv];
     uint32_t *Ct = s_c[wv];
     const uint64_t count = A.counters[CNT_MID];
-    const uint64_t rstride = 3 + (uint64_t)A.wm;
+    const uint64_t rstride = 4 + (uint64_t)A.wm;
     for (uint64_t it = (uint64_t)blockIdx.x * kMidWaves + wv; it < count; it += (uint64_t)gridDim.x * kMidWaves) {
         const uint64_t p = A.mid_idx[it];
         const uint64_t c0 = A.lo + p;
@@ -856,7 +877,8 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
                     rec[0] = p | ((uint64_t)j0 << 32);
                     rec[1] = 0;
                     rec[2] = 0;
-                    for (int u = 0; u < wm; ++u) rec[3 + u] = (u == wm - 1) ? A.tail_m : ~0ull;
+                    rec[3] = 0;
+                    for (int u = 0; u < wm; ++u) rec[4 + u] = (u == wm - 1) ? A.tail_m : ~0ull;
                 } else {
                     A.counters[CNT_OVERFLOW] = 1;
                 }
@@ -896,9 +918,10 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
                     rec[0] = p | ((uint64_t)j << 32);
                     rec[1] = (uint64_t)(run_rank + before) | ((uint64_t)cnt << 32);
                     rec[2] = objoff;
+                    rec[3] = 0;
 #pragma unroll
                     for (int u = 0; u < WMC; ++u)
-                        if (u < wm) rec[3 + u] = (u == wm - 1) ? (Dt[r * WMC + u] & A.tail_m) : Dt[r * WMC + u];
+                        if (u < wm) rec[4 + u] = (u == wm - 1) ? (Dt[r * WMC + u] & A.tail_m) : Dt[r * WMC + u];
                 } else {
                     A.counters[CNT_OVERFLOW] = 1;
                 }
@@ -925,7 +948,7 @@ __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
     const int lane = lane_id();
     if (A.counters[CNT_OVERFLOW]) return;
     const uint64_t nrec = A.counters[CNT_MIDREC];
-    const uint64_t rstride = 3 + (uint64_t)A.wm;
+    const uint64_t rstride = 4 + (uint64_t)A.wm;
     for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; i < nrec;
          i += (uint64_t)gridDim.x * kWavesPerBlock) {
         const uint64_t *rec = A.mrec + i * rstride;
@@ -936,7 +959,7 @@ __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
         const uint64_t c0 = A.lo + p;
         const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
         const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
-        for (int u = lane; u < A.wm; u += kWave) A.intents[child * A.wm + u] = rec[3 + u];
+        for (int u = lane; u < A.wm; u += kWave) A.intents[child * A.wm + u] = rec[4 + u];
         if (lane == 0) {
             A.cursor[child] = j;
             A.loff[child] = obeg;
