@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <numeric>
 #include <new>
 #include <vector>
 
@@ -112,6 +113,7 @@ struct BigStore {
 
 struct fcbo_context {
     int device = 0;
+    int n_cu = 256;                // compute units of the device
     hipStream_t stream = nullptr;
     int64_t n = 0, m = 0;
     int wn = 0, wm = 0;
@@ -527,9 +529,37 @@ void fcbo_context::sort_intents()
 void fcbo_context::write_output(uint64_t *intents_out, uint64_t *extents_out)
 {
     hipEvent_t b = prof_begin();
-    const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(8192, div_up(K, kWavesPerBlock)));
-    hipLaunchKernelGGL(k_output, dim3(g), dim3(kBlock), 0, stream, (const uint64_t *)intents, (const uint64_t *)loff,
-                       (const uint32_t *)objs, (const uint32_t *)perm, K, wm, wn, intents_out, extents_out);
+    const uint64_t row_bytes = (uint64_t)wn * 8;
+    if (extents_out && row_bytes > (uint64_t)kOutBlockBytes) {
+        // rows wider than the LDS tile: one wavefront per row, tile by tile
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(8192, div_up(K, kWavesPerBlock)));
+        hipLaunchKernelGGL(k_output, dim3(g), dim3(kBlock), 0, stream, (const uint64_t *)intents,
+                           (const uint64_t *)loff, (const uint32_t *)objs, (const uint32_t *)perm, K, wm, wn,
+                           intents_out, extents_out);
+        CK_LAUNCH();
+        prof_end(FCBO_K_OUTPUT, b);
+        return;
+    }
+    // Rows per block: a multiple of 16/gcd(wn,16) makes the block's region a
+    // whole number of 128-byte lines; aim for about 40 KiB of LDS per block.
+    int R = kWave;
+    if (extents_out) {
+        const int al = 16 / std::gcd(wn, 16);
+        const uint64_t al_bytes = (uint64_t)al * row_bytes;
+        if (al_bytes <= (uint64_t)kOutBlockBytes)
+            R = al * (int)std::max<uint64_t>(1, 40960 / al_bytes);
+        else
+            R = (int)(kOutBlockBytes / row_bytes);
+        R = std::min(R, kWave);
+    }
+    const size_t lds = extents_out ? (size_t)R * wn * 8 : 0;
+    int per_cu = 1;
+    CK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_output_block, kBlock, lds));
+    const uint64_t nblk = div_up(K, (uint64_t)R);
+    const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(nblk, (uint64_t)n_cu * std::max(1, per_cu)));
+    hipLaunchKernelGGL(k_output_block, dim3(g), dim3(kBlock), lds, stream, (const uint64_t *)intents,
+                       (const uint64_t *)loff, (const uint32_t *)objs, (const uint32_t *)perm, K, wm, wn, R,
+                       intents_out, extents_out);
     CK_LAUNCH();
     prof_end(FCBO_K_OUTPUT, b);
 }
@@ -563,6 +593,7 @@ int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs
     if (!c) return FCBO_ERR_OUT_OF_MEMORY;
     try {
         CK(hipGetDevice(&c->device));
+        CK(hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device));
         c->stream = (hipStream_t)hip_stream;
         c->tiny = (flags & FCBO_TINY_BUFFERS) != 0;
         c->n = n_objects;

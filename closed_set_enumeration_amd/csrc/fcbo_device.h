@@ -1498,4 +1498,102 @@ __global__ void __launch_bounds__(kBlock) k_output(const uint64_t *__restrict__ 
     }
 }
 
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+
+// Largest LDS tile, in bytes, of the row-block output kernel.
+constexpr int kOutBlockBytes = 65536;
+
+// k_output_block: one workgroup writes R consecutive output rows.  Their extent
+// bitmaps are assembled together in one dynamic LDS tile of R*wn words (the
+// object lists OR-ed in with LDS atomics), then the tile goes out as a single
+// contiguous region of the extent array: each wavefront stores 1 KiB runs, so
+// when R*wn*8 is a multiple of 128 bytes every store covers whole, aligned cache
+// lines.  The tile is cleared as it is read.  Intent rows of the block are copied
+// alongside.  The grid is persistent: a workgroup walks blocks with the grid
+// stride and loads the next block's row sources (permutation entry and list
+// bounds, one row per lane) while it streams the current one.  With no extent
+// buffer only the intents are copied.
+__global__ void __launch_bounds__(kBlock) k_output_block(const uint64_t *__restrict__ intents,
+                                                          const uint64_t *__restrict__ loff,
+                                                          const uint32_t *__restrict__ objs,
+                                                          const uint32_t *__restrict__ perm, uint64_t K, int wm,
+                                                          int wn, int R, uint64_t *__restrict__ intents_out,
+                                                          uint64_t *__restrict__ extents_out)
+{
+    extern __shared__ __attribute__((aligned(16))) uint64_t s_rows[];
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const bool ext = extents_out != nullptr;
+    const int words = R * wn;
+    if (ext)
+        for (int w = threadIdx.x; w < words; w += kBlock) s_rows[w] = 0;
+    // stores of two words at a time need a 16-byte aligned region start
+    const bool pairs = ((reinterpret_cast<uintptr_t>(extents_out) & 15) == 0) && (words & 1) == 0;
+    const uint64_t nblk = (K + R - 1) / R;
+    uint64_t src = 0, lo = 0, hi = 0;  // this lane's row in the block being fetched
+    auto fetch = [&](uint64_t blk) {
+        const uint64_t r = blk * (uint64_t)R + lane;
+        src = lo = hi = 0;
+        if (blk < nblk && lane < R && r < K) {
+            src = perm[r];
+            if (ext) {
+                lo = loff[src];
+                hi = loff[src + 1];
+            }
+        }
+    };
+    uint64_t b = blockIdx.x;
+    fetch(b);
+    __syncthreads();
+    for (; b < nblk; b += gridDim.x) {
+        const uint64_t r0 = b * (uint64_t)R;
+        const int nr = (int)((K - r0) < (uint64_t)R ? (K - r0) : (uint64_t)R);
+        // intents: nr*wm consecutive output words; every lane takes part in the shuffle
+        for (int t0 = 0; t0 < nr * wm; t0 += kBlock) {
+            const int t = t0 + (int)threadIdx.x;
+            int row = t / wm;
+            row = row < nr ? row : nr - 1;
+            const uint64_t s = __shfl(src, row);
+            if (t < nr * wm) intents_out[r0 * wm + t] = intents[s * wm + (t - row * wm)];
+        }
+        if (!ext) {
+            fetch(b + gridDim.x);
+            continue;
+        }
+        for (int rr = wv; rr < nr; rr += kWavesPerBlock) {
+            const uint64_t o = __shfl(lo, rr), e = __shfl(hi, rr);
+            uint64_t *T = s_rows + rr * wn;
+            for (uint64_t p = o + lane; p < e; p += kWave) {
+                const uint32_t g = objs[p];
+                atomicOr((unsigned long long *)&T[g >> 6], (unsigned long long)(1ull << (g & 63)));
+            }
+        }
+        __syncthreads();
+        fetch(b + gridDim.x);
+        const uint64_t base = r0 * (uint64_t)wn;
+        const int cnt = nr * wn;
+        if (pairs) {
+            u64x2 *S = reinterpret_cast<u64x2 *>(s_rows);
+            u64x2 *D = reinterpret_cast<u64x2 *>(extents_out + base);
+            const u64x2 z = {0, 0};
+            for (int e = threadIdx.x; e < (cnt >> 1); e += kBlock) {
+                const u64x2 v = S[e];
+                S[e] = z;
+                __builtin_nontemporal_store(v, &D[e]);
+            }
+            if ((cnt & 1) && threadIdx.x == 0) {
+                extents_out[base + cnt - 1] = s_rows[cnt - 1];
+                s_rows[cnt - 1] = 0;
+            }
+        } else {
+            for (int e = threadIdx.x; e < cnt; e += kBlock) {
+                const uint64_t v = s_rows[e];
+                s_rows[e] = 0;
+                __builtin_nontemporal_store(v, &extents_out[base + e]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace fcbo

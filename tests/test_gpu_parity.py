@@ -108,8 +108,9 @@ def test_many_objects():
 
 
 def test_over_a_million_objects_list_path():
-    # more than 2^20 objects: big parents are scanned through their object lists
-    assert_parity(synth.random_context(1100006, 1_100_000, 6, 0.3), extents=False)
+    # more than 2^20 objects: big parents are scanned through their object lists,
+    # and extent rows wider than the output kernel's LDS tile are written tile by tile
+    assert_parity(synth.random_context(1100006, 1_100_000, 6, 0.3), extents=True)
 
 
 @pytest.mark.parametrize("n,m", [(65, 130), (130, 5), (1, 1), (300, 64)])
@@ -216,6 +217,29 @@ def test_capacity_error_and_reuse():
         rc, _, _ = ctx.enumerate_into(ints, None)
         assert rc == fca.FCBO_OK
         assert np.array_equal(ints.cpu().numpy().view(np.uint64), want.intents)
+    finally:
+        ctx.close()
+
+
+@pytest.mark.parametrize("n", [129, 2000])
+def test_extent_buffer_only_word_aligned(n):
+    # an extent buffer starting 8 bytes past a 16-byte boundary: single-word stores
+    cells = synth.random_context(79 + n, n, 40, 0.1)
+    rows = synth.pack_rows(cells)
+    want = oracle.cbo(rows, 40)
+    k, wn = want.n_concepts, (n + 63) // 64
+    ctx = fca.Context(rows, 40)
+    try:
+        ints, _ = ctx.alloc_outputs(k, False)
+        flat = torch.full((k * wn + 1,), -3, dtype=torch.int64, device="cuda")
+        exts = flat[1:].view(k, wn)
+        assert exts.data_ptr() % 16 == 8
+        rc, k_seen, _ = ctx.enumerate_into(ints, exts)
+        assert rc == fca.FCBO_OK and k_seen == k
+        torch.cuda.synchronize()
+        assert int(flat[0]) == -3
+        assert np.array_equal(ints.cpu().numpy().view(np.uint64), want.intents)
+        assert np.array_equal(exts.cpu().numpy().view(np.uint64), want.extents)
     finally:
         ctx.close()
 
