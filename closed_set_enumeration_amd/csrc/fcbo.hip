@@ -289,7 +289,8 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
     b = c->prof_begin();
     {
         constexpr int kW = LocalCfg<WMC>::kWaves;
-        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap * 4 / kW, div_up(P, kW)));
+        const uint64_t chunks = div_up(P, (uint64_t)LocalCfg<WMC>::kChunk);
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(chunks, kW)));
         hipLaunchKernelGGL(k_local_test<WMC>, dim3(g), dim3(LocalCfg<WMC>::kThreads), 0, c->stream, A);
     }
     CK_LAUNCH();

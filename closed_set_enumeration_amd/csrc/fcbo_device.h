@@ -384,31 +384,40 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
     }
 }
 
-// --- local parents (|A| <= 64): closure tests in one wavefront ------------------
+// --- local parents (|A| <= 64): closure tests packed across parents -----------
 //
-// The rows of the objects of A are staged in LDS.  For a candidate j (j > y,
-// j not in B) let c_j be the objects of A having j, as a 64-bit mask over the
-// staged rows: C = A AND col[j] restricted to A.  D = C' is the AND of their
-// rows, and the canonical test asks that D adds no attribute below j to B
-// (page 1, section 4.3: bits 0..j-1 compared, bit j excluded).
+// For a candidate j (j > y, j not in B) let c_j be the objects of A having j.
+// C = A AND col[j] restricted to A is c_j; D = C' is the AND of their rows, and
+// the canonical test asks that D adds no attribute below j to B (page 1,
+// section 4.3: bits 0..j-1 compared, bit j excluded).
 //
 // Candidates split in two kinds:
-//   * j carried by some object of A (the set U): c_j is non-empty and is
-//     tested in full, one lane per candidate;
+//   * j carried by some object of A (the set U): c_j is non-empty and is tested
+//     in full;
 //   * j carried by no object of A: C is empty, D = M, so the test passes only
-//     when every attribute below j is in B, i.e. j is the first attribute not
-//     in B.  That single candidate (if above y) yields the bottom concept.
-// Attribute-saturation pruning (page 1, section 2.3) is the j-in-B skip: with
-// B closed, A inside col[j] holds exactly when j is in B.
+//     when every attribute below j is in B, i.e. j is the first attribute not in
+//     B (called j0 below).  That single candidate, when above y, yields the
+//     bottom concept; it is tested like the others with c_j empty.
+// Attribute-saturation pruning (page 1, section 2.3) is the j-in-B skip: with B
+// closed, A inside col[j] holds exactly when j is in B.
 //
-// Per-parent values are wave-uniform (read once, kept in scalar registers).
-// Passing children leave records (layout in k_mid_test) with the object mask
-// c_j in word 3, so the child write needs no recomputation.
+// Local parents have a handful of objects and about as many candidates, so one
+// wavefront serves many of them at once.  A wavefront takes a chunk of
+// consecutive parents (one per lane for the metadata, intents staged in LDS) and
+// cuts it into groups whose objects fit 64 LDS row slots and whose (parent,
+// intent word) pairs fit 64 lanes.  Per group: one lane per object slot stages
+// its row and ORs it into its parent's U; one lane per (parent, word) turns U
+// into candidate bits; the candidates, in parent-major and ascending j order, are
+// then tested 64 at a time, one per lane, and passing children leave records
+// (layout in k_mid_test) with the object mask c_j in word 3, so the child write
+// needs no recomputation.  Child ranks and object offsets within a parent are
+// segmented scans over the lanes plus a per-parent carry between rounds.
 
 template <int WMC>
 struct LocalCfg {
     static constexpr int kWaves = WMC <= 8 ? kWavesPerBlock : 1;  // wavefronts per block
     static constexpr int kThreads = kWave * kWaves;
+    static constexpr int kChunk = WMC <= 8 ? kWave : 512 / WMC;    // parents per chunk
 };
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t v)
@@ -435,189 +444,250 @@ __device__ __forceinline__ uint64_t wave_slot(uint64_t bal, uint64_t *counter)
     return base + lanes_below(bal);
 }
 
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bits 0 .. b of a word (b in [0, 63]).
+__device__ __forceinline__ uint64_t upto_mask(int b) { return (2ull << b) - 1ull; }
+
 template <int WMC>
 __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArgs A)
 {
     constexpr int kW = LocalCfg<WMC>::kWaves;
-    __shared__ uint64_t s_rows[kW][kSmallMax * WMC];
-    __shared__ uint64_t s_u[kW][WMC];
-    __shared__ uint32_t s_cand[kW][kWave * WMC];
+    constexpr int CH = LocalCfg<WMC>::kChunk;
+    __shared__ uint64_t s_rows[kW][kSmallMax * WMC];  // the group's object rows, slot-major
+    __shared__ uint64_t s_b[kW][CH * WMC];            // the chunk's intents, padding bits past M set
+    __shared__ uint64_t s_u[kW][kWave];               // per (group parent, word): OR of its rows
+    __shared__ uint32_t s_cand[kW][kWave];            // this round's candidates: parent << 16 | j
+    __shared__ uint32_t s_seg[kW][kWave];             // per group parent: first slot | objects << 8
+    __shared__ uint32_t s_run[kW][2 * kWave];         // per group parent: children, their objects
+    __shared__ uint8_t s_owner[kW][kWave];            // group parent whose slots start here
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = words_of<WMC>(A.wm);
+    const int gmax = kWave / wm;  // parents per group: one lane per (parent, word)
     uint64_t *R = s_rows[wv];
     const uint32_t *R32 = (const uint32_t *)R;
+    uint64_t *SB = s_b[wv];
     uint64_t *SU = s_u[wv];
     uint32_t *CAND = s_cand[wv];
+    uint32_t *SEG = s_seg[wv];
+    uint32_t *RUN = s_run[wv];
+    uint8_t *OWN = s_owner[wv];
     const uint64_t rstride = 4 + (uint64_t)A.wm;
     // Record slots are reserved 64 at a time per wavefront; a round's passing
-    // children go to one chunk (a chunk that cannot hold them is closed).
-    uint64_t chunk = ~0ull;  // first slot of the current chunk
-    uint32_t fill = kWave;   // slots used in it
+    // children go to one chunk of slots (a chunk that cannot hold them is closed).
+    uint64_t rchunk = ~0ull;  // first slot of the current record chunk
+    uint32_t fill = kWave;    // slots used in it
     auto reserve = [&](uint32_t n) -> uint64_t {
         if (fill + n > (uint32_t)kWave) {
-            if (chunk != ~0ull && lane == 0 && chunk < A.lrec_cap) A.lfill[chunk / kWave] = fill;
+            if (rchunk != ~0ull && lane == 0 && rchunk < A.lrec_cap) A.lfill[rchunk / kWave] = fill;
             uint64_t c = 0;
             if (lane == 0) c = atomicAdd((unsigned long long *)&A.counters[CNT_LOCREC], (unsigned long long)kWave);
-            chunk = uniform64(c);
+            rchunk = uniform64(c);
             fill = 0;
-            if (chunk + kWave > A.lrec_cap && lane == 0) A.counters[CNT_OVERFLOW] = 1;
+            if (rchunk + kWave > A.lrec_cap && lane == 0) A.counters[CNT_OVERFLOW] = 1;
         }
-        const uint64_t at = chunk + fill;
+        const uint64_t at = rchunk + fill;
         fill += n;
         return at;
     };
-    if (lane < WMC) SU[lane] = 0;
-    // The parent's offsets, cursor and intent are loaded one parent ahead, so
-    // their latency overlaps the work on the current parent.
-    const uint64_t stride = (uint64_t)gridDim.x * kW;
-    uint64_t p = (uint64_t)blockIdx.x * kW + wv;
-    uint64_t n_o0 = 0, n_o1 = 0, n_b[WMC];
-    int32_t n_y = 0;
-    auto fetch = [&](uint64_t q) {
-        if (q < A.P) {
-            const uint64_t c = A.lo + q;
-            n_o0 = A.loff[c];
-            n_o1 = A.loff[c + 1];
-            n_y = A.cursor[c];
-#pragma unroll
-            for (int u = 0; u < WMC; ++u) n_b[u] = (u < wm) ? A.intents[c * A.wm + u] : 0ull;
+    SU[lane] = 0;
+    const uint64_t nchunks = (A.P + CH - 1) / CH;
+    for (uint64_t ch = (uint64_t)blockIdx.x * kW + wv; ch < nchunks; ch += (uint64_t)gridDim.x * kW) {
+        const uint64_t p0 = ch * CH;
+        const int nq = (int)((A.P - p0) < (uint64_t)CH ? (A.P - p0) : (uint64_t)CH);
+        // parent lanes: list start, size (0 unless local), cursor
+        uint64_t o0 = 0;
+        int a = 0, y = 0;
+        bool act = false;
+        if (lane < nq) {
+            const uint64_t c = A.lo + p0 + lane;
+            o0 = A.loff[c];
+            const uint64_t sz = A.loff[c + 1] - o0;
+            y = A.cursor[c];
+            act = sz <= (uint64_t)kSmallMax;
+            a = act ? (int)sz : 0;
         }
-    };
-    fetch(p);
-    for (; p < A.P; p += stride) {
-        const uint64_t o0 = uniform64(n_o0);
-        const uint64_t o1 = uniform64(n_o1);
-        const int y = (int)__builtin_amdgcn_readfirstlane((uint32_t)n_y);
-        uint64_t Bx[WMC];  // B plus the padding bits past M
-#pragma unroll
-        for (int u = 0; u < WMC; ++u) {
-            Bx[u] = ~0ull;
-            if (u < wm) Bx[u] = uniform64(n_b[u]) | ((u == wm - 1) ? ~A.tail_m : 0ull);
+        {
+            const uint64_t *src = A.intents + (A.lo + p0) * (uint64_t)A.wm;
+            for (int t = lane; t < nq * wm; t += kWave) {
+                uint64_t b = src[t];
+                if (t % wm == wm - 1) b |= ~A.tail_m;
+                SB[t] = b;
+            }
         }
-        fetch(p + stride);
-        if (o1 - o0 > (uint64_t)kSmallMax) continue;
-        const int a = (int)(o1 - o0);
-        if (lane < a) {
-            const uint64_t g = A.objs[o0 + lane];
-#pragma unroll
-            for (int u = 0; u < WMC; ++u) {
-                if (u < wm) {
-                    const uint64_t r = A.rows[g * A.wm + u];
-                    R[lane * WMC + u] = r;
-                    atomicOr((unsigned long long *)&SU[u], (unsigned long long)r);
+        wave_sync();
+        int j0 = -1;  // first attribute outside B, when above y
+        if (act) {
+            for (int u = 0; u < wm; ++u) {
+                const uint64_t nb = ~SB[lane * wm + u];
+                if (nb) {
+                    j0 = 64 * u + __ffsll((unsigned long long)nb) - 1;
+                    break;
                 }
             }
+            if (j0 <= y) j0 = -1;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // U, its prefix counts, the first attribute outside B; candidate list in LDS
-        uint64_t U[WMC];
-        int nU = 0, j0 = -1;
-#pragma unroll
-        for (int u = 0; u < WMC; ++u) {
-            U[u] = 0;
-            if (u < wm) {
-                const uint64_t nb = ~Bx[u];
-                if (j0 < 0 && nb) j0 = 64 * u + __ffsll((unsigned long long)nb) - 1;
-                U[u] = uniform64(SU[u]) & nb & above_mask(y, u);
-                if ((U[u] >> lane) & 1ull) CAND[nU + lanes_below(U[u])] = (uint32_t)(64 * u + lane);
-                nU += __popcll(U[u]);
+        const uint32_t pre = wave_excl_scan((uint32_t)a);
+        for (int s = 0; s < nq;) {
+            // the group: parents [s, e), their objects in slots [0, S)
+            const uint32_t base = __shfl(pre, s);
+            const bool in = lane >= s && lane < s + gmax && lane < nq && pre + (uint32_t)a - base <= (uint32_t)kSmallMax;
+            const int e = s + __popcll(__ballot(in));
+            const int S = (int)(__shfl(pre, e - 1) + (uint32_t)__shfl(a, e - 1) - base);
+            if (in) {
+                SEG[lane - s] = (pre - base) | ((uint32_t)a << 8);
+                if (a > 0) OWN[pre - base] = (uint8_t)(lane - s);
+                RUN[2 * (lane - s)] = 0;
+                RUN[2 * (lane - s) + 1] = 0;
             }
-        }
-        if (lane < WMC) SU[lane] = 0;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        bool bottom = false;
-        if (j0 > y) {
-            bottom = true;
+            const uint64_t starts = wave_or(in && a > 0 ? (1ull << (pre - base)) : 0ull);
+            wave_sync();
+            {
+                // object slots: stage the row, OR it into the parent's U
+                const uint64_t below = starts & upto_mask(lane);
+                const int st = below ? 63 - __clzll((long long)below) : 0;
+                const int q = OWN[st];
+                const uint64_t oq = __shfl(o0, s + q);
+                if (lane < S) {
+                    const uint64_t g = A.objs[oq + (uint64_t)(lane - st)];
 #pragma unroll
-            for (int u = 0; u < WMC; ++u)
-                if (u == (j0 >> 6) && ((U[u] >> (j0 & 63)) & 1ull)) bottom = false;
-        }
-        uint32_t run_rank = 0, run_obj = 0;
-        if (bottom) {  // C = {}, D = M, the first child in j order
-            const uint64_t pos = reserve(1);
-            if (lane == 0) {
-                if (pos < A.lrec_cap) {
-                    uint64_t *rec = A.lrec + pos * rstride;
-                    rec[0] = p | ((uint64_t)j0 << 32);
-                    rec[1] = 0;
-                    rec[2] = 0;
-                    rec[3] = 0;
-                    for (int u = 0; u < wm; ++u) rec[4 + u] = (u == wm - 1) ? A.tail_m : ~0ull;
+                    for (int u = 0; u < WMC; ++u) {
+                        if (u < wm) {
+                            const uint64_t r = A.rows[g * A.wm + u];
+                            R[lane * WMC + u] = r;
+                            atomicOr((unsigned long long *)&SU[q * wm + u], (unsigned long long)r);
+                        }
+                    }
                 }
             }
-            run_rank = 1;
-        }
-        for (int r0 = 0; r0 < nU; r0 += kWave) {
-            const int k = r0 + lane;
-            const bool active = k < nU;
-            const int j = active ? (int)CAND[k] : 0;
-            const int wj = j >> 6, bj = j & 63;
-            // c_j: objects of A having j (32-bit LDS reads, one bit each)
-            uint32_t clo = 0, chi = 0;
-            if (active) {
-                const uint32_t *col32 = R32 + 2 * wj + (bj >> 5);
-                const uint32_t sh = (uint32_t)(bj & 31);
-                const int alo = a < 32 ? a : 32;
-                for (int i = 0; i < alo; ++i) clo |= ((col32[2 * WMC * i] >> sh) & 1u) << i;
-                for (int i = 32; i < a; ++i) chi |= ((col32[2 * WMC * i] >> sh) & 1u) << (i - 32);
-            }
-            const uint64_t c = ((uint64_t)chi << 32) | clo;
-            // D = AND of the rows of c_j
-            uint64_t D[WMC];
-#pragma unroll
-            for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
-            uint64_t cc = c;
-            while (cc) {
-                const int i = __ffsll((unsigned long long)cc) - 1;
-                cc &= cc - 1ull;
-#pragma unroll
-                for (int u = 0; u < WMC; ++u)
-                    if (u < wm) D[u] &= R[i * WMC + u];
-            }
-            // canonical test: the first attribute of D outside B must be j itself
-            int fu = WMC;
-            uint64_t fx = 0;
-#pragma unroll
-            for (int u = WMC - 1; u >= 0; --u) {
-                const uint64_t x = (u < wm) ? (D[u] & ~Bx[u]) : 0ull;
-                if (x) {
-                    fu = u;
-                    fx = x;
+            wave_sync();
+            // (parent, word) lanes: candidate bits, their place in the group's list
+            const int G = e - s;
+            const int pq = lane / wm < G ? lane / wm : G - 1;
+            const int pu = lane - pq * wm;
+            const int yq = __shfl(y, s + pq);
+            const int j0q = __shfl(j0, s + pq);
+            const bool actq = __shfl((int)act, s + pq) != 0;
+            uint64_t x = 0;
+            if (lane < G * wm) {
+                x = SU[lane];
+                SU[lane] = 0;
+                if (actq) {
+                    x &= ~SB[(s + pq) * wm + pu] & above_mask(yq, pu);
+                    if (j0q >= 0 && (j0q >> 6) == pu) x |= 1ull << (j0q & 63);
+                } else {
+                    x = 0;
                 }
             }
-            const bool pass = active && fu == wj && (__ffsll((unsigned long long)fx) - 1) == bj;
-            const uint64_t bal = __ballot(pass);
-            if (!bal) continue;
-            const uint32_t sz = pass ? (uint32_t)__popcll(c) : 0u;
-            const uint32_t ex = wave_excl_scan(sz);
-            const uint64_t pos = reserve((uint32_t)__popcll(bal)) + lanes_below(bal);
-            if (pass) {
-                if (pos < A.lrec_cap) {
-                    uint64_t *rec = A.lrec + pos * rstride;
-                    rec[0] = p | ((uint64_t)j << 32);
-                    rec[1] = (uint64_t)(run_rank + lanes_below(bal)) | ((uint64_t)sz << 32);
-                    rec[2] = run_obj + ex;
-                    rec[3] = c;
+            const uint32_t cnt = (uint32_t)__popcll(x);
+            uint32_t pos = wave_excl_scan(cnt);
+            const uint32_t total = __shfl(pos + cnt, kWave - 1);
+            for (uint32_t r0 = 0; r0 < total; r0 += kWave) {
+                while (x && pos < r0 + kWave) {
+                    const int bit = __ffsll((unsigned long long)x) - 1;
+                    x &= x - 1ull;
+                    CAND[pos - r0] = ((uint32_t)pq << 16) | (uint32_t)(64 * pu + bit);
+                    ++pos;
+                }
+                wave_sync();
+                const bool live = r0 + (uint32_t)lane < total;
+                const uint32_t cj = live ? CAND[lane] : 0xFFFF0000u;
+                const int qc = live ? (int)(cj >> 16) : 0;
+                const int j = (int)(cj & 0xFFFFu);
+                const int wj = j >> 6, bj = j & 63;
+                const uint32_t sg = SEG[qc];
+                const int first = (int)(sg & 0xFFu), na = live ? (int)(sg >> 8) : 0;
+                // c_j: objects of the parent having j (32-bit LDS reads, one bit each)
+                uint32_t clo = 0, chi = 0;
+                {
+                    const uint32_t *col32 = R32 + 2 * (first * WMC + wj) + (bj >> 5);
+                    const uint32_t sh = (uint32_t)(bj & 31);
+                    const int alo = na < 32 ? na : 32;
+                    for (int i = 0; i < alo; ++i) clo |= ((col32[2 * WMC * i] >> sh) & 1u) << i;
+                    for (int i = 32; i < na; ++i) chi |= ((col32[2 * WMC * i] >> sh) & 1u) << (i - 32);
+                }
+                const uint64_t c = ((uint64_t)chi << 32) | clo;
+                // D = AND of the rows of c_j
+                uint64_t D[WMC];
+#pragma unroll
+                for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
+                uint64_t cc = c;
+                while (cc) {
+                    const int i = __ffsll((unsigned long long)cc) - 1;
+                    cc &= cc - 1ull;
 #pragma unroll
                     for (int u = 0; u < WMC; ++u)
-                        if (u < wm) rec[4 + u] = (u == wm - 1) ? (D[u] & A.tail_m) : D[u];
+                        if (u < wm) D[u] &= R[(first + i) * WMC + u];
+                }
+                // canonical test: the first attribute of D outside B must be j itself
+                int fu = WMC;
+                uint64_t fx = 0;
+                const uint64_t *Bq = SB + (s + qc) * wm;
+#pragma unroll
+                for (int u = WMC - 1; u >= 0; --u) {
+                    const uint64_t xb = (u < wm) ? (D[u] & ~Bq[u]) : 0ull;
+                    if (xb) {
+                        fu = u;
+                        fx = xb;
+                    }
+                }
+                const bool pass = live && fu == wj && (__ffsll((unsigned long long)fx) - 1) == bj;
+                const uint64_t bal = __ballot(pass);
+                // segments of equal parent among the live lanes
+                const int prevq = __shfl(qc, lane > 0 ? lane - 1 : 0);
+                const int nextq = __shfl(qc, lane < kWave - 1 ? lane + 1 : lane);
+                const bool head = live && (lane == 0 || prevq != qc);
+                const bool tail = live && (lane == kWave - 1 || r0 + (uint32_t)lane + 1 >= total || nextq != qc);
+                const uint64_t heads = __ballot(head);
+                const uint64_t hb = heads & upto_mask(lane);
+                const int hl = hb ? 63 - __clzll((long long)hb) : 0;
+                const uint64_t inseg = upto_mask(lane) & ~below_mask(hl);
+                const uint32_t sz = pass ? (uint32_t)__popcll(c) : 0u;
+                const uint32_t ex = wave_excl_scan(sz);
+                const uint32_t exh = __shfl(ex, hl);
+                if (bal) {
+                    const uint64_t at = reserve((uint32_t)__popcll(bal));
+                    if (pass) {
+                        const uint64_t slot = at + lanes_below(bal);
+                        if (slot < A.lrec_cap) {
+                            const uint32_t rank = RUN[2 * qc] + (uint32_t)__popcll(bal & inseg & ~(1ull << lane));
+                            const uint32_t objoff = RUN[2 * qc + 1] + (ex - exh);
+                            uint64_t *rec = A.lrec + slot * rstride;
+                            rec[0] = (p0 + (uint64_t)(s + qc)) | ((uint64_t)j << 32);
+                            rec[1] = (uint64_t)rank | ((uint64_t)sz << 32);
+                            rec[2] = objoff;
+                            rec[3] = c;
+#pragma unroll
+                            for (int u = 0; u < WMC; ++u)
+                                if (u < wm) rec[4 + u] = (u == wm - 1) ? (D[u] & A.tail_m) : D[u];
+                        }
+                    }
+                    if (tail) {
+                        RUN[2 * qc] += (uint32_t)__popcll(bal & inseg);
+                        RUN[2 * qc + 1] += ex - exh + sz;
+                    }
+                }
+                wave_sync();
+            }
+            // per-parent totals (the count kernel zeroed them)
+            if (in && act) {
+                const uint32_t nc = RUN[2 * (lane - s)];
+                if (nc) {
+                    A.nchild[p0 + lane] = nc;
+                    A.nobj[p0 + lane] = RUN[2 * (lane - s) + 1];
                 }
             }
-            run_rank += (uint32_t)__popcll(bal);
-            run_obj += __shfl(ex + sz, kWave - 1);
+            wave_sync();
+            s = e;
         }
-        if (lane == 0) {
-            A.nchild[p] = run_rank;
-            A.nobj[p] = run_obj;
-        }
-        __builtin_amdgcn_wave_barrier();
     }
-    if (chunk != ~0ull && lane == 0 && chunk < A.lrec_cap) A.lfill[chunk / kWave] = fill;
+    if (rchunk != ~0ull && lane == 0 && rchunk < A.lrec_cap) A.lfill[rchunk / kWave] = fill;
 }
 
 // Children of the local parents, one thread per record slot: intent, cursor and
