@@ -94,7 +94,7 @@ class OracleResult:
     truncated: bool
     level_concepts: np.ndarray  # int64 [n_levels]
     level_tests: np.ndarray     # int64 [n_levels]
-    intents: np.ndarray         # uint64 [K, wm], sorted by word tuple
+    intents: np.ndarray         # uint64 [K, wm], lexicographic over attributes 0..M-1
     extents: np.ndarray | None  # uint64 [K, wn] in the same order
     seconds_enum: float
     seconds_sort: float

@@ -73,10 +73,9 @@ def closed_intents_by_row_meets(ctx: Context) -> set[int]:
     return fam
 
 
-def intent_key(b: int, wm: int) -> tuple:
-    """Sort key: the intent as 64-bit words, word 0 first."""
-    mask = (1 << 64) - 1
-    return tuple((b >> (64 * w)) & mask for w in range(wm))
+def intent_key(b: int, m: int) -> str:
+    """Sort key: the intent as its characteristic string over attributes 0..m-1."""
+    return "".join("1" if (b >> e) & 1 else "0" for e in range(m))
 
 
 def to_words(sets, nbits: int) -> np.ndarray:
@@ -91,9 +90,8 @@ def to_words(sets, nbits: int) -> np.ndarray:
 
 
 def sorted_concepts(ctx: Context, intents: set[int]):
-    """(intents uint64 [K, wm], extents uint64 [K, wn]) sorted by intent words."""
-    wm = (ctx.m + 63) // 64
-    order = sorted(intents, key=lambda b: intent_key(b, wm))
+    """(intents uint64 [K, wm], extents uint64 [K, wn]) in lexicographic intent order."""
+    order = sorted(intents, key=lambda b: intent_key(b, ctx.m))
     return to_words(order, ctx.m), to_words([ctx.objects_of(b) for b in order], ctx.n)
 
 
@@ -108,6 +106,8 @@ class TreeStats:
     sum_c: int = 0
     level_concepts: list = field(default_factory=list)
     level_tests: list = field(default_factory=list)
+    parent: dict = field(default_factory=dict)  # intent -> parent intent (None for the top)
+    cursor: dict = field(default_factory=dict)  # intent -> generating attribute (-1 for the top)
 
 
 def _nonzero_words(x: int) -> int:
@@ -162,7 +162,7 @@ def cbo_tree(ctx: Context, intents: set[int]) -> TreeStats:
             level[x] = base + i + 1
         return level[path[0]] if path else base
 
-    st = TreeStats(n_concepts=len(intents))
+    st = TreeStats(n_concepts=len(intents), parent=parent, cursor=cursor)
     for d in intents:
         depth(d)
     nlev = max(level.values()) + 1

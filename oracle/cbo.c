@@ -20,9 +20,12 @@
  *     the objects in C); the child (C, D, j) is kept iff D and B agree on the
  *     attributes 0..j-1 (bit j itself excluded, page 1 section 4.3), and the
  *     search recurses into it.
- * Afterwards the concepts are sorted by intent as a tuple of unsigned 64-bit
- * words, word 0 first (page 1 section 6.2 asks for a lexicographic intent key;
- * this word order is the reading taken here).
+ * Afterwards the concepts are sorted by intent in lexicographic order of the
+ * intent read as a bit string over the attributes 0, 1, ..., M-1: of two
+ * intents, the one holding the smallest attribute in which they differ comes
+ * later (page 1 section 6.2 asks for a lexicographic intent key; reading the
+ * intent as its characteristic string in attribute index order is the reading
+ * taken here).
  *
  * Bit layout: element e of a set is bit (e & 63) of 64-bit word (e >> 6);
  * bits past N or M in the last word are always zero.
@@ -190,9 +193,13 @@ static int cmp_intent(const void *pa, const void *pb)
     int64_t ia = *(const int64_t *)pa, ib = *(const int64_t *)pb;
     const uint64_t *x = g_sort_state->intents + ia * g_sort_state->wm;
     const uint64_t *y = g_sort_state->intents + ib * g_sort_state->wm;
+    /* attributes in index order: word by word, bit 0 of a word first */
     for (int64_t w = 0; w < g_sort_state->wm; ++w) {
-        if (x[w] < y[w]) return -1;
-        if (x[w] > y[w]) return 1;
+        uint64_t diff = x[w] ^ y[w];
+        if (diff) {
+            int e = __builtin_ctzll(diff);  /* smallest differing attribute in this word */
+            return ((x[w] >> e) & 1u) ? 1 : -1;
+        }
     }
     return 0;
 }

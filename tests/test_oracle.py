@@ -62,7 +62,26 @@ def check_against_brute(cells, tree=True, subsets=None):
         assert list(r.level_tests) == st.level_tests
         assert r.sum_nzw == st.sum_nzw
         assert r.sum_c == st.sum_c
+        assert as_sets(r.intents) == preorder_descending(st)
     return r
+
+
+def preorder_descending(st):
+    """Intents of the CbO tree in pre-order, children visited by descending cursor."""
+    kids = {}
+    top = None
+    for d, p in st.parent.items():
+        if p is None:
+            top = d
+        else:
+            kids.setdefault(p, []).append(d)
+    out, stack = [], [top]
+    while stack:
+        d = stack.pop()
+        out.append(d)
+        # push ascending so that the largest cursor is popped first
+        stack.extend(sorted(kids.get(d, []), key=lambda c: st.cursor[c]))
+    return out
 
 
 # --- worked examples -----------------------------------------------------------
@@ -218,13 +237,14 @@ def _check_invariants(cells, r, sample=2000, seed=0):
     n, m = cells.shape
     k = r.n_concepts
     ints = r.intents
-    # strictly increasing word tuples: sorted and no duplicates
-    order = np.lexsort(ints.T[::-1])
-    assert np.array_equal(order, np.arange(k))
-    if k > 1:
-        diff = np.any(ints[1:] != ints[:-1], axis=1)
-        assert diff.all()
+    # strictly increasing in lexicographic order over attributes 0..m-1: at the
+    # first attribute where neighbours differ, the later one has it
     ib = synth.unpack_rows(ints, m)
+    if k > 1:
+        ne = ib[1:] != ib[:-1]
+        assert ne.any(axis=1).all()
+        first = ne.argmax(axis=1)
+        assert ib[1:][np.arange(k - 1), first].all()
     top = cells.all(axis=0)
     assert (ib == top).all(axis=1).any()
     assert ib.all(axis=1).any()  # bottom intent M
