@@ -1,8 +1,8 @@
 """Benchmark: concept enumeration throughput on one MI355X.
 
 One step = one full call of fcbo_enumerate on the seeded 50,000 x 400 context:
-root, every level of closure tests and child writes, the intent sort and the
-sorted intents plus extent bitmaps written to preallocated device buffers.
+root, every level of closure tests and child writes, the output ordering and the
+ordered intents plus extent bitmaps written to preallocated device buffers.
 Inputs (the context) are resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--workload ctx50000x400]
@@ -41,8 +41,39 @@ def kernel_bytes(cls, st, wm, wn, n, k, extents):
         reads = k * (4 + 8 * wm + 16) + (n + st["sum_child_objects"]) * 4
         writes = k * 8 * wm + (k * 8 * wn if extents else 0)
         return reads + writes
-    if cls == "sort":
-        return st["sort_passes"] * k * (8 + 12 + 12) + wm * k * (4 + 8 + 8)
+    if cls == "order":
+        # subtree sizes: first-child offset, the children's sizes, the size out; positions:
+        # offset, own position, the children's sizes in and positions out; inverse: position in,
+        # concept index out
+        return k * (4 + 4 + 4) + k * (4 + 4 + 4 + 4) + k * (4 + 4)
+    return None
+
+
+def source_sha256():
+    """SHA-256 of the device sources (kernels and their launch code)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("closed_set_enumeration_amd/csrc/fcbo_device.h", "closed_set_enumeration_amd/csrc/fcbo.hip"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(cls, workload):
+    """HBM bytes per launch of a kernel class from the committed rocprofv3 counter summary,
+    or None when there is none or the device sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "%s_output_traffic.md" % workload)
+    if not os.path.exists(path):
+        return None
+    sha = source_sha256()
+    with open(path) as f:
+        for line in f:
+            if not line.startswith("traffic-record:"):
+                continue
+            kv = dict(x.split("=", 1) for x in line.split()[1:])
+            if kv.get("class") == cls and kv.get("source_sha256") == sha:
+                return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
     return None
 
 
@@ -139,7 +170,8 @@ def main():
         avg_ms = kernel_ms[dominant] / launches[dominant]
         achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dominant, args.workload),
                 "bytes_per_launch": int(per_launch_bytes), "avg_launch_ms": round(avg_ms, 4)}
 
     tests = st0["closure_tests"]
@@ -161,7 +193,7 @@ def main():
         "closure_tests_per_s": round(tests / (ms_per_step * 1e-3), 1),
         "device_ms": {"enumerate": round(sum(s["enumerate_ms"] for s in per_step) / args.steps, 4),
                       "levels": round(sum(s["levels_ms"] for s in per_step) / args.steps, 4),
-                      "sort": round(sum(s["sort_ms"] for s in per_step) / args.steps, 4),
+                      "order": round(sum(s["order_ms"] for s in per_step) / args.steps, 4),
                       "output": round(sum(s["output_ms"] for s in per_step) / args.steps, 4)},
         "kernel_ms": {c: round(v, 4) for c, v in kernel_ms.items()},
         "kernel_launches": launches,

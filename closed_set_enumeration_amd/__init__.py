@@ -32,7 +32,7 @@ FCBO_REUSE_RESULT = 1
 FCBO_PROFILE = 2
 
 KERNEL_CLASSES = ("count", "test_local", "test_medium", "test_big", "scan", "write_local", "write_medium",
-                  "write_big", "sort", "output")
+                  "write_big", "order", "output")
 
 EXPORTED = (
     "fcbo_context_create",
@@ -59,10 +59,10 @@ class FcboStats(ctypes.Structure):
         ("big_parents", ctypes.c_uint64),
         ("big_tests", ctypes.c_uint64),
         ("big_scanned_objects", ctypes.c_uint64),
-        ("sort_passes", ctypes.c_uint64),
+        ("order_launches", ctypes.c_uint64),
         ("enumerate_ms", ctypes.c_double),
         ("levels_ms", ctypes.c_double),
-        ("sort_ms", ctypes.c_double),
+        ("order_ms", ctypes.c_double),
         ("output_ms", ctypes.c_double),
         ("kernel_ms", ctypes.c_double * len(KERNEL_CLASSES)),
         ("kernel_launches", ctypes.c_uint64 * len(KERNEL_CLASSES)),

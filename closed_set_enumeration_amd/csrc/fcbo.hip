@@ -123,11 +123,12 @@ struct fcbo_context {
     uint64_t *cols = nullptr;  // m x wn
 
     // concept store
-    uint64_t cap_int = 0, cap_cur = 0, cap_loff = 0, cap_o = 0;
+    uint64_t cap_int = 0, cap_cur = 0, cap_loff = 0, cap_o = 0, cap_fch = 0;
     uint64_t *intents = nullptr;
     int32_t *cursor = nullptr;
     uint64_t *loff = nullptr;
     uint32_t *objs = nullptr;
+    uint32_t *fchild = nullptr;  // K + 1: first child of each concept (children are contiguous)
 
     // level scratch
     uint64_t cap_pass = 0, cap_nch = 0, cap_nob = 0, cap_cb = 0, cap_ob = 0, cap_mid = 0, cap_mrec = 0;
@@ -145,21 +146,17 @@ struct fcbo_context {
     uint64_t *counters = nullptr;   // CNT_N
     uint64_t *h_counters = nullptr; // pinned, CNT_N
 
-    // sort scratch
-    uint64_t cap_ka = 0, cap_kb = 0, cap_ia = 0, cap_ib = 0, cap_h = 0, cap_ho = 0;
-    uint64_t *keys_a = nullptr, *keys_b = nullptr;
-    uint32_t *idx_a = nullptr, *idx_b = nullptr;
-    uint32_t *hist = nullptr;
-    uint64_t *hist_off = nullptr;
-    uint64_t *sort_red = nullptr;  // 2 words
-    uint32_t *perm = nullptr;      // points at idx_a or idx_b after the sort
+    // output order
+    uint64_t cap_rank = 0, cap_perm = 0;
+    uint32_t *rank = nullptr;  // subtree size, then position, of every concept
+    uint32_t *perm = nullptr;  // concept at every output position
 
     // result of the last enumeration
     bool have_result = false;
     bool have_perm = false;
     uint64_t K = 0, tests = 0, pairs = 0, sum_c = 0;
     uint64_t local_parents = 0, local_objs = 0, med_parents = 0, med_objs = 0;
-    uint64_t big_parents = 0, big_tests = 0, big_scan = 0, sort_passes = 0;
+    uint64_t big_parents = 0, big_tests = 0, big_scan = 0, order_launches = 0;
     std::vector<uint64_t> lev_concepts, lev_tests;
 
     // profiling
@@ -199,13 +196,12 @@ struct fcbo_context {
     void free_all()
     {
         dfree(rows); dfree(cols);
-        dfree(intents); dfree(cursor); dfree(loff); dfree(objs);
+        dfree(intents); dfree(cursor); dfree(loff); dfree(objs); dfree(fchild);
         dfree(pass); dfree(cbase); dfree(obase); dfree(nchild); dfree(nobj); dfree(mid_idx); dfree(mrec); dfree(lrec); dfree(lfill);
         huge.free_all();
         dfree(dt); dfree(tcnt); dfree(icnt);
         dfree(scan_part); dfree(counters);
-        dfree(keys_a); dfree(keys_b); dfree(idx_a); dfree(idx_b); dfree(hist); dfree(hist_off);
-        dfree(sort_red);
+        dfree(rank); dfree(perm);
         if (h_counters) (void)hipHostFree(h_counters);
         h_counters = nullptr;
         for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
@@ -271,7 +267,7 @@ struct fcbo_context {
         ensure(lfill, cap_lfill, chunks, 0, stream, 1);
     }
     void enumerate_levels();
-    void sort_intents();
+    void order_concepts();
     void write_output(uint64_t *intents_out, uint64_t *extents_out);
 };
 
@@ -464,6 +460,10 @@ void fcbo_context::enumerate_levels()
             ensure(cursor, cap_cur, k_end, keep_k, stream, mc);
             ensure(loff, cap_loff, k_end + 1, keep_k + 1, stream, mc);
             ensure(objs, cap_o, obj_hi + n_objs, obj_hi, stream, mc);
+            ensure(fchild, cap_fch, k_end + 1, keep_k + 1, stream, mc);
+            hipLaunchKernelGGL(k_first_child, dim3((unsigned)div_up(P + 1, kBlock)), dim3(kBlock), 0, stream,
+                               (const uint64_t *)cbase, lo, P, (const uint64_t *)counters, fchild);
+            CK_LAUNCH();
             if (n_children) fns.writes(this, level_args(lo, P, obj_hi), P);
         } while (redo);
         lo += P;
@@ -475,55 +475,34 @@ void fcbo_context::enumerate_levels()
     have_perm = false;
 }
 
-void fcbo_context::sort_intents()
+void fcbo_context::order_concepts()
 {
-    const uint64_t n_keys = K;
-    if (n_keys >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
+    if (K >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
     const uint64_t mc = min_cap();
-    ensure(keys_a, cap_ka, n_keys, 0, stream, mc);
-    ensure(keys_b, cap_kb, n_keys, 0, stream, mc);
-    ensure(idx_a, cap_ia, n_keys, 0, stream, mc);
-    ensure(idx_b, cap_ib, n_keys, 0, stream, mc);
-    const uint64_t ntiles = div_up(n_keys, kSortTile);
-    ensure(hist, cap_h, 256 * ntiles, 0, stream, mc);
-    ensure(hist_off, cap_ho, 256 * ntiles + 1, 0, stream, mc);
+    ensure(rank, cap_rank, K, 0, stream, mc);
+    ensure(perm, cap_perm, K, 0, stream, mc);
+    const size_t nlev = lev_concepts.size();
+    std::vector<uint64_t> lev_lo(nlev + 1, 0);
+    for (size_t l = 0; l < nlev; ++l) lev_lo[l + 1] = lev_lo[l] + lev_concepts[l];
+    auto grid = [](uint64_t n) { return (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(n, kBlock))); };
     hipEvent_t b = prof_begin();
-    hipLaunchKernelGGL(k_iota, dim3((unsigned)div_up(n_keys, kBlock)), dim3(kBlock), 0, stream, idx_a, n_keys);
-    CK_LAUNCH();
-    prof_end(FCBO_K_SORT, b);
-    sort_passes = 0;
-    uint64_t *ka = keys_a, *kb = keys_b;
-    uint32_t *ia = idx_a, *ib = idx_b;
-    const unsigned gk = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(2048, div_up(n_keys, kBlock)));
-    for (int u = wm - 1; u >= 0; --u) {
-        CK(hipMemsetAsync(sort_red, 0, sizeof(uint64_t), stream));          // OR of the keys
-        CK(hipMemsetAsync(sort_red + 1, 0xFF, sizeof(uint64_t), stream));   // AND of the keys
-        b = prof_begin();
-        hipLaunchKernelGGL(k_gather_key, dim3(gk), dim3(kBlock), 0, stream, (const uint64_t *)intents, wm, u,
-                           (const uint32_t *)ia, ka, n_keys, sort_red);
+    order_launches = 0;
+    for (size_t l = nlev; l-- > 0;) {  // sizes, deepest level first
+        hipLaunchKernelGGL(k_subtree_size, dim3(grid(lev_concepts[l])), dim3(kBlock), 0, stream,
+                           (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
         CK_LAUNCH();
-        prof_end(FCBO_K_SORT, b);
-        CK(hipMemcpyAsync(h_counters, sort_red, 2 * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
-        CK(hipStreamSynchronize(stream));
-        const uint64_t varying = h_counters[0] ^ h_counters[1];
-        for (int d = 0; d < 8; ++d) {
-            const int shift = 8 * d;
-            if (((varying >> shift) & 0xFFu) == 0) continue;  // every key has the same digit
-            b = prof_begin();
-            hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)ntiles), dim3(kBlock), 0, stream, (const uint64_t *)ka,
-                               n_keys, shift, hist, ntiles);
-            CK_LAUNCH();
-            scan(hist, nullptr, nullptr, 256 * ntiles, 256 * ntiles, hist_off, nullptr, nullptr, nullptr);
-            hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)ntiles), dim3(kBlock), 0, stream, (const uint64_t *)ka,
-                               (const uint32_t *)ia, n_keys, shift, (const uint64_t *)hist_off, ntiles, kb, ib);
-            CK_LAUNCH();
-            prof_end(FCBO_K_SORT, b);
-            std::swap(ka, kb);
-            std::swap(ia, ib);
-            ++sort_passes;
-        }
+        ++order_launches;
     }
-    perm = ia;
+    for (size_t l = 0; l + 1 < nlev; ++l) {  // positions, root level first
+        hipLaunchKernelGGL(k_child_position, dim3(grid(lev_concepts[l])), dim3(kBlock), 0, stream,
+                           (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
+        CK_LAUNCH();
+        ++order_launches;
+    }
+    hipLaunchKernelGGL(k_invert, dim3(grid(K)), dim3(kBlock), 0, stream, (const uint32_t *)rank, K, perm);
+    CK_LAUNCH();
+    ++order_launches;
+    prof_end(FCBO_K_ORDER, b);
     have_perm = true;
 }
 
@@ -607,7 +586,6 @@ int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs
         CK(hipMalloc((void **)&c->cols, (uint64_t)n_attrs * c->wn * sizeof(uint64_t)));
         CK(hipMalloc((void **)&c->scan_part, 2 * kScanBlocks * sizeof(uint64_t)));
         CK(hipMalloc((void **)&c->counters, CNT_N * sizeof(uint64_t)));
-        CK(hipMalloc((void **)&c->sort_red, 2 * sizeof(uint64_t)));
         CK(hipHostMalloc((void **)&c->h_counters, CNT_N * sizeof(uint64_t), hipHostMallocDefault));
         CK(hipMemsetAsync(c->rows, 0, ((uint64_t)n_objects + 1) * c->wm * sizeof(uint64_t), c->stream));
         const hipMemcpyKind kind = (flags & FCBO_ROWS_ON_DEVICE) ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
@@ -660,7 +638,7 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
             rc = FCBO_ERR_CAPACITY;
             CK(hipStreamSynchronize(ctx->stream));
         } else {
-            if (!(reuse && ctx->have_perm)) ctx->sort_intents();
+            if (!(reuse && ctx->have_perm)) ctx->order_concepts();
             CK(hipEventRecord(e2, ctx->stream));
             ctx->write_output(intents_out, extents_out);
             CK(hipEventRecord(e3, ctx->stream));
@@ -669,7 +647,7 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
             CK(hipEventElapsedTime(&ms, e0, e3));
             st.enumerate_ms = ms;
             CK(hipEventElapsedTime(&ms, e1, e2));
-            st.sort_ms = ms;
+            st.order_ms = ms;
             CK(hipEventElapsedTime(&ms, e2, e3));
             st.output_ms = ms;
         }
@@ -698,7 +676,7 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
     st.big_parents = ctx->big_parents;
     st.big_tests = ctx->big_tests;
     st.big_scanned_objects = ctx->big_scan;
-    st.sort_passes = ctx->sort_passes;
+    st.order_launches = ctx->order_launches;
     if (rc == FCBO_OK)
         st.output_bytes = ctx->K * (uint64_t)ctx->wm * 8 + (extents_out ? ctx->K * (uint64_t)ctx->wn * 8 : 0);
     if (stats_out) *stats_out = st;

@@ -15,14 +15,18 @@
 // handful of objects, so a list is hundreds of times smaller than a bitmap of
 // N bits.
 //
-// Per level:
-//   k_count        candidates per parent, list of parents with > 64 objects
-//   k_local_test   one wavefront per parent with <= 64 objects: the parent's
-//                  rows are staged in LDS, one lane per candidate attribute
-//   k_big_test     one wavefront per (big parent, candidate attribute)
-//   scans          child and object offsets per parent (exact sizes, so no
-//                  overflow and no atomics on the output)
-//   k_*_write      children (C, D, j) written in parent order, then j order
+// Per level (parents in three classes by extent size a, see k_count):
+//   k_count          candidates per parent, item pairs, the mid and huge lists
+//   k_local_test     a <= 64: parents packed into wavefronts, one lane per
+//                    candidate, rows staged in LDS; child records
+//   k_mid_test       64 < a <= 4096 (intents up to 8 words): closure tests by
+//                    incidence, one D per carried attribute in LDS; records
+//   k_huge_*         larger parents: one item per (test, 64-word chunk of the
+//                    extent bitmap), or per test over the object list
+//   scans            child and object offsets per parent (exact sizes)
+//   k_*_write        children (C, D, j) stored in parent order, then j order
+// After the last level the output order comes from the CbO tree (subtree sizes
+// bottom-up, positions top-down) and k_output_block writes the caller's rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,7 +39,6 @@ constexpr int kSmallMax = 64;       // parents with at most this many objects us
 constexpr int kBlock = 256;         // threads per block for wave-per-item kernels
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kScanBlocks = 1024;   // blocks of the multi-block exclusive scan
-constexpr int kSortTile = 2048;     // keys per block in a radix pass (256 threads x 8)
 constexpr int kOutTileWords = 1024; // extent words staged in LDS per output tile
 constexpr int kBmpMaxWords = 16384; // big parents use extent bitmaps when N <= 64 * this
 constexpr int kMidMax = 4096;       // parents with more objects are huge (tested a chunk at a time)
@@ -1396,126 +1399,68 @@ __global__ void __launch_bounds__(kBlock) k_scan_down(const uint32_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// intent sort: LSD radix sort of a permutation, one 64-bit intent word at a
-// time from the last word to word 0, 8-bit digits, stable passes.
+// output order.  Concepts are listed in lexicographic order of the intent read
+// as a bit string over attributes 0..M-1 (of two intents, the one holding the
+// smallest attribute where they differ comes later; page 1, section 6.2 asks
+// for a lexicographic intent key).  In the CbO tree this order is a pre-order
+// walk that visits the children of a node by descending generating attribute:
+//   * a child D of B (generated at j) agrees with B below j and holds j, which
+//     B lacks, so it follows B;
+//   * children D_j, D_k with j < k agree below j, and only D_j holds j, so D_j
+//     follows D_k; every descendant of D_k agrees with D_k below k, so the
+//     whole subtree of D_k precedes D_j.
+// Hence the position of a concept is its parent's position, plus one, plus the
+// subtree sizes of its siblings with a larger attribute.  Children of a concept
+// are stored contiguously by ascending attribute, as [fchild[c], fchild[c+1]).
 
-__global__ void k_iota(uint32_t *idx, uint64_t n)
+// Children of the parents [lo, lo + P): their first index, and the end.
+__global__ void __launch_bounds__(kBlock) k_first_child(const uint64_t *__restrict__ cbase, uint64_t lo, uint64_t P,
+                                                         const uint64_t *__restrict__ counters,
+                                                         uint32_t *__restrict__ fchild)
 {
-    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) idx[i] = (uint32_t)i;
+    const uint64_t p = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p > P) return;
+    const uint64_t rel = p < P ? cbase[p] : counters[CNT_CHILDREN];
+    fchild[lo + p] = (uint32_t)(lo + P + rel);
 }
 
-// keys[i] = word u of the intent idx[i]; OR and AND of all keys into red[0..1].
-__global__ void __launch_bounds__(kBlock) k_gather_key(const uint64_t *__restrict__ intents, int wm, int u,
-                                                        const uint32_t *__restrict__ idx, uint64_t *__restrict__ keys,
-                                                        uint64_t n, uint64_t *red)
+// Subtree sizes of the concepts [lo, lo + P); their children's sizes are final.
+__global__ void __launch_bounds__(kBlock) k_subtree_size(const uint32_t *__restrict__ fchild, uint64_t lo,
+                                                          uint64_t P, uint32_t *__restrict__ rank)
 {
-    __shared__ uint64_t s_or[kWavesPerBlock], s_and[kWavesPerBlock];
-    uint64_t vor = 0, vand = ~0ull;
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
-        const uint64_t k = intents[(uint64_t)idx[i] * wm + u];
-        keys[i] = k;
-        vor |= k;
-        vand &= k;
-    }
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) {
-        vor |= __shfl_xor(vor, s);
-        vand &= __shfl_xor(vand, s);
-    }
-    if (lane_id() == 0) {
-        s_or[threadIdx.x / kWave] = vor;
-        s_and[threadIdx.x / kWave] = vand;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < kWavesPerBlock; ++w) {
-            vor |= s_or[w];
-            vand &= s_and[w];
-        }
-        vor |= s_or[0];
-        vand &= s_and[0];
-        atomicOr((unsigned long long *)&red[0], (unsigned long long)vor);
-        atomicAnd((unsigned long long *)&red[1], (unsigned long long)vand);
+    for (uint64_t p = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; p < P; p += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t c = lo + p;
+        const uint32_t k0 = fchild[c], k1 = fchild[c + 1];
+        uint32_t s = 1;
+#pragma unroll 4
+        for (uint32_t k = k0; k < k1; ++k) s += rank[k];
+        rank[c] = s;
     }
 }
 
-// Digit histogram of one tile: hist[d * ntiles + tile].
-__global__ void __launch_bounds__(kBlock) k_radix_hist(const uint64_t *__restrict__ keys, uint64_t n, int shift,
-                                                        uint32_t *__restrict__ hist, uint64_t ntiles)
+// Positions of the children of the concepts [lo, lo + P), whose own positions
+// are final (the root's is 0); a child's size is replaced by its position.
+__global__ void __launch_bounds__(kBlock) k_child_position(const uint32_t *__restrict__ fchild, uint64_t lo,
+                                                            uint64_t P, uint32_t *__restrict__ rank)
 {
-    __shared__ uint32_t s_h[256];
-    s_h[threadIdx.x] = 0;
-    __syncthreads();
-    const uint64_t base = (uint64_t)blockIdx.x * kSortTile;
-    for (int it = 0; it < kSortTile / kBlock; ++it) {
-        const uint64_t i = base + (uint64_t)it * kBlock + threadIdx.x;
-        if (i < n) atomicAdd(&s_h[(keys[i] >> shift) & 0xFFu], 1u);
+    for (uint64_t p = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; p < P; p += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t c = lo + p;
+        const uint32_t k0 = fchild[c], k1 = fchild[c + 1];
+        uint32_t run = (c == 0 ? 0u : rank[c]) + 1u;
+        for (uint32_t k = k1; k > k0; --k) {
+            const uint32_t sz = rank[k - 1];
+            rank[k - 1] = run;
+            run += sz;
+        }
     }
-    __syncthreads();
-    hist[(uint64_t)threadIdx.x * ntiles + blockIdx.x] = s_h[threadIdx.x];
 }
 
-// Stable scatter of one tile.  Items are taken in order, 256 at a time; the
-// rank of an item among equal digits of its wavefront comes from eight
-// ballots (lanes whose digit matches on every bit), the wavefronts of the
-// block are ordered through LDS counters.
-__global__ void __launch_bounds__(kBlock) k_radix_scatter(const uint64_t *__restrict__ keys_in,
-                                                           const uint32_t *__restrict__ idx_in, uint64_t n, int shift,
-                                                           const uint64_t *__restrict__ hist_off, uint64_t ntiles,
-                                                           uint64_t *__restrict__ keys_out,
-                                                           uint32_t *__restrict__ idx_out)
+// perm[position] = concept
+__global__ void __launch_bounds__(kBlock) k_invert(const uint32_t *__restrict__ rank, uint64_t K,
+                                                    uint32_t *__restrict__ perm)
 {
-    __shared__ uint32_t s_run[256];
-    __shared__ uint32_t s_wc[kWavesPerBlock][256];
-    const int lane = lane_id(), wv = threadIdx.x / kWave;
-    s_run[threadIdx.x] = 0;
-    for (int w = 0; w < kWavesPerBlock; ++w) s_wc[w][threadIdx.x] = 0;
-    __syncthreads();
-    const uint64_t gbase = hist_off[(uint64_t)threadIdx.x * ntiles + blockIdx.x];
-    __shared__ uint64_t s_gbase[256];
-    s_gbase[threadIdx.x] = gbase;
-    __syncthreads();
-    const uint64_t base = (uint64_t)blockIdx.x * kSortTile;
-    for (int it = 0; it < kSortTile / kBlock; ++it) {
-        const uint64_t i = base + (uint64_t)it * kBlock + threadIdx.x;
-        const bool ok = i < n;
-        uint64_t key = 0;
-        uint32_t id = 0;
-        if (ok) {
-            key = keys_in[i];
-            id = idx_in[i];
-        }
-        const uint32_t d = (uint32_t)((key >> shift) & 0xFFu);
-        uint64_t peers = __ballot(ok);
-#pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-            const bool v = (d >> bit) & 1u;
-            const uint64_t bal = __ballot(v);
-            peers &= v ? bal : ~bal;
-        }
-        const uint32_t rank = (uint32_t)__popcll(peers & below_mask(lane));
-        const bool last = ok && ((peers >> lane) >> 1) == 0ull;  // highest lane of the group
-        if (last) s_wc[wv][d] = rank + 1;
-        __syncthreads();
-        if (ok) {
-            uint32_t before = s_run[d];
-            for (int w = 0; w < wv; ++w) before += s_wc[w][d];
-            const uint64_t pos = s_gbase[d] + before + rank;
-            keys_out[pos] = key;
-            idx_out[pos] = id;
-        }
-        __syncthreads();
-        {
-            uint32_t add = 0;
-            for (int w = 0; w < kWavesPerBlock; ++w) {
-                add += s_wc[w][threadIdx.x];
-                s_wc[w][threadIdx.x] = 0;
-            }
-            s_run[threadIdx.x] += add;
-        }
-        __syncthreads();
-    }
+    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < K; c += (uint64_t)gridDim.x * blockDim.x)
+        perm[c == 0 ? 0 : rank[c]] = (uint32_t)c;
 }
 
 // ---------------------------------------------------------------------------

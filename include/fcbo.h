@@ -18,9 +18,12 @@
  * (e >> 6), least significant bit first.  Bits past the last object or the
  * last attribute are zero in everything the library writes.
  *
- * Output order: concepts are sorted ascending by their intent read as a tuple
- * of unsigned 64-bit words, word 0 compared first.  Intents are pairwise
- * distinct, so the order is total and the output is byte-for-byte unique.
+ * Output order: concepts are listed in lexicographic order of the intent read
+ * as a bit string over the attributes 0, 1, ..., M-1: of two intents, the one
+ * holding the smallest attribute in which they differ comes later (so the
+ * root, whose intent is contained in every other, is first).  Intents are
+ * pairwise distinct, so the order is total and the output is byte-for-byte
+ * unique.
  *
  * Errors are reported only by return code; no call aborts or throws.  A HIP
  * failure maps to FCBO_ERR_DEVICE (FCBO_ERR_OUT_OF_MEMORY for allocation) and
@@ -59,14 +62,14 @@ enum {
 enum {
     FCBO_K_COUNT = 0,        /* per-parent candidate count, parent classes */
     FCBO_K_TEST_LOCAL = 1,   /* closure tests of parents with <= 64 objects */
-    FCBO_K_TEST_MEDIUM = 2,  /* closure tests of parents with 65..256 objects */
-    FCBO_K_TEST_BIG = 3,     /* closure tests of larger parents (tasks + tests) */
+    FCBO_K_TEST_MEDIUM = 2,  /* closure tests of parents with 65..4096 objects (M <= 512 only) */
+    FCBO_K_TEST_BIG = 3,     /* closure tests of the larger parents (tasks + tests) */
     FCBO_K_SCAN = 4,         /* exclusive scans (children, objects, big tests) */
     FCBO_K_WRITE_LOCAL = 5,  /* child write, parents with <= 64 objects */
-    FCBO_K_WRITE_MEDIUM = 6, /* child write, parents with 65..256 objects */
+    FCBO_K_WRITE_MEDIUM = 6, /* child write, parents of the medium class */
     FCBO_K_WRITE_BIG = 7,    /* child write, larger parents */
-    FCBO_K_SORT = 8,         /* intent radix sort */
-    FCBO_K_OUTPUT = 9,       /* sorted intents + extent bitmaps to the caller */
+    FCBO_K_ORDER = 8,        /* output positions from the CbO tree (sizes, positions, inverse) */
+    FCBO_K_OUTPUT = 9,       /* ordered intents + extent bitmaps to the caller */
     FCBO_K_NUM_CLASSES = 10
 };
 
@@ -77,17 +80,17 @@ typedef struct {
     uint64_t n_levels;      /* levels of the CbO tree, root level included */
     uint64_t sum_child_objects; /* sum of |C| over all concepts except the root */
     uint64_t output_bytes;  /* bytes written to the caller's buffers */
-    uint64_t local_parents; /* parents with <= 64 objects (row-local test kernel) */
+    uint64_t local_parents; /* parents with <= 64 objects (packed local test kernel) */
     uint64_t local_parent_objects; /* objects in their extents (rows staged) */
-    uint64_t medium_parents; /* parents with 65..256 objects (row-local, 4 mask words) */
+    uint64_t medium_parents; /* parents of the medium class (tests by incidence) */
     uint64_t medium_parent_objects; /* objects in their extents */
-    uint64_t big_parents;   /* larger parents (one wavefront per closure test) */
+    uint64_t big_parents;   /* larger parents (tests split in 64-word extent chunks or list scans) */
     uint64_t big_tests;     /* closure tests made by them */
     uint64_t big_scanned_objects; /* extent-list entries read by those tests */
-    uint64_t sort_passes;   /* radix passes run by the last sort */
+    uint64_t order_launches; /* kernel launches of the last output ordering */
     double enumerate_ms;    /* whole call on the device stream (HIP events) */
     double levels_ms;       /* enumeration part (root to last level) */
-    double sort_ms;         /* intent sort */
+    double order_ms;        /* output ordering (subtree sizes, positions) */
     double output_ms;       /* writing the caller's buffers */
     double kernel_ms[FCBO_K_NUM_CLASSES];       /* with FCBO_PROFILE only */
     uint64_t kernel_launches[FCBO_K_NUM_CLASSES];
@@ -114,8 +117,8 @@ int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs
                         fcbo_context **out);
 
 /*
- * Enumerate all concepts and write them, sorted by intent, to caller-owned
- * device buffers on the context's device.
+ * Enumerate all concepts and write them, in the output order above, to
+ * caller-owned device buffers on the context's device.
  *   intents_out   K x ceil(M/64) words, row i = intent of concept i
  *   extents_out   K x ceil(N/64) words in the same order, or NULL to skip
  *   capacity      rows available in the output buffers
@@ -124,7 +127,7 @@ int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs
  *   stats_out     optional statistics, or NULL
  * If intents_out is NULL or capacity < K the call returns FCBO_ERR_CAPACITY,
  * stores K and writes nothing; the concepts stay in the context, so a second
- * call with FCBO_REUSE_RESULT and large enough buffers only sorts and writes.
+ * call with FCBO_REUSE_RESULT and large enough buffers only orders and writes.
  * The call returns after the stream has finished the work.
  */
 int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_out,
