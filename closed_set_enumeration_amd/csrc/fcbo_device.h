@@ -339,7 +339,6 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
             uint64_t cand = ~A.intents[c * A.wm + u] & above_mask(y, u);
             if (u == A.wm - 1) cand &= A.tail_m;
             tests += __popcll(cand);
-            A.pass[p * A.wm + u] = 0;
         }
         pairs = (uint32_t)(A.m - 1 - y);
         const uint64_t a = A.loff[c + 1] - A.loff[c];
@@ -409,8 +408,8 @@ __global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
 // consecutive parents (one per lane for the metadata, intents staged in LDS) and
 // cuts it into groups whose objects fit 64 LDS row slots and whose (parent,
 // intent word) pairs fit 64 lanes.  Per group: one lane per object slot stages
-// its row and ORs it into its parent's U; one lane per (parent, word) turns U
-// into candidate bits; the candidates, in parent-major and ascending j order, are
+// its row; one lane per (parent, word) ORs the parent's staged rows into U and
+// turns U into candidate bits; the candidates, in parent-major and ascending j order, are
 // then tested 64 at a time, one per lane, and passing children leave records
 // (layout in k_mid_test) with the object mask c_j in word 3, so the child write
 // needs no recomputation.  Child ranks and object offsets within a parent are
@@ -464,7 +463,6 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     constexpr int CH = LocalCfg<WMC>::kChunk;
     __shared__ uint64_t s_rows[kW][kSmallMax * WMC];  // the group's object rows, slot-major
     __shared__ uint64_t s_b[kW][CH * WMC];            // the chunk's intents, padding bits past M set
-    __shared__ uint64_t s_u[kW][kWave];               // per (group parent, word): OR of its rows
     __shared__ uint32_t s_cand[kW][kWave];            // this round's candidates: parent << 16 | j
     __shared__ uint32_t s_seg[kW][kWave];             // per group parent: first slot | objects << 8
     __shared__ uint32_t s_run[kW][2 * kWave];         // per group parent: children, their objects
@@ -476,7 +474,6 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     uint64_t *R = s_rows[wv];
     const uint32_t *R32 = (const uint32_t *)R;
     uint64_t *SB = s_b[wv];
-    uint64_t *SU = s_u[wv];
     uint32_t *CAND = s_cand[wv];
     uint32_t *SEG = s_seg[wv];
     uint32_t *RUN = s_run[wv];
@@ -499,7 +496,6 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
         fill += n;
         return at;
     };
-    SU[lane] = 0;
     const uint64_t nchunks = (A.P + CH - 1) / CH;
     for (uint64_t ch = (uint64_t)blockIdx.x * kW + wv; ch < nchunks; ch += (uint64_t)gridDim.x * kW) {
         const uint64_t p0 = ch * CH;
@@ -552,7 +548,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
             const uint64_t starts = wave_or(in && a > 0 ? (1ull << (pre - base)) : 0ull);
             wave_sync();
             {
-                // object slots: stage the row, OR it into the parent's U
+                // object slots: stage the row
                 const uint64_t below = starts & upto_mask(lane);
                 const int st = below ? 63 - __clzll((long long)below) : 0;
                 const int q = OWN[st];
@@ -560,17 +556,13 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
                 if (lane < S) {
                     const uint64_t g = A.objs[oq + (uint64_t)(lane - st)];
 #pragma unroll
-                    for (int u = 0; u < WMC; ++u) {
-                        if (u < wm) {
-                            const uint64_t r = A.rows[g * A.wm + u];
-                            R[lane * WMC + u] = r;
-                            atomicOr((unsigned long long *)&SU[q * wm + u], (unsigned long long)r);
-                        }
-                    }
+                    for (int u = 0; u < WMC; ++u)
+                        if (u < wm) R[lane * WMC + u] = A.rows[g * A.wm + u];
                 }
             }
             wave_sync();
-            // (parent, word) lanes: candidate bits, their place in the group's list
+            // (parent, word) lanes: U = OR of the parent's staged rows, candidate
+            // bits, their place in the group's list
             const int G = e - s;
             const int pq = lane / wm < G ? lane / wm : G - 1;
             const int pu = lane - pq * wm;
@@ -579,8 +571,9 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
             const bool actq = __shfl((int)act, s + pq) != 0;
             uint64_t x = 0;
             if (lane < G * wm) {
-                x = SU[lane];
-                SU[lane] = 0;
+                const uint32_t sgq = SEG[pq];
+                const int fq = (int)(sgq & 0xFFu), nq = (int)(sgq >> 8);
+                for (int i = 0; i < nq; ++i) x |= R[(fq + i) * WMC + pu];
                 if (actq) {
                     x &= ~SB[(s + pq) * wm + pu] & above_mask(yq, pu);
                     if (j0q >= 0 && (j0q >> 6) == pu) x |= 1ull << (j0q & 63);
@@ -746,6 +739,7 @@ __global__ void __launch_bounds__(kBlock) k_huge_tasks(LevelArgs A)
          bi += (uint64_t)gridDim.x * kWavesPerBlock) {
         const uint64_t c0 = A.lo + S.idx[bi];
         const int y = A.cursor[c0];
+        if (lane < wm) A.pass[(uint64_t)S.idx[bi] * A.wm + lane] = 0;  // passing attributes, set by the tests
         uint64_t cand[WMC], bset[WMC];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
@@ -1515,8 +1509,14 @@ __global__ void __launch_bounds__(kBlock) k_output(const uint64_t *__restrict__ 
 
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
-// Largest LDS tile, in bytes, of the row-block output kernel.
+// Row-block output kernel: largest LDS tile in bytes, the tile size it aims
+// for, threads per workgroup (512 measured best on MI355X against 256, 384 and
+// 1024), and the words of a cache line its regions are aligned to.
 constexpr int kOutBlockBytes = 65536;
+constexpr int kOutTargetBytes = 40960;
+constexpr int kOutThreads = 512;
+constexpr int kOutWaves = kOutThreads / kWave;
+constexpr int kOutLineWords = 128 / 8;
 
 // k_output_block: one workgroup writes R consecutive output rows.  Their extent
 // bitmaps are assembled together in one dynamic LDS tile of R*wn words (the
@@ -1528,7 +1528,7 @@ constexpr int kOutBlockBytes = 65536;
 // stride and loads the next block's row sources (permutation entry and list
 // bounds, one row per lane) while it streams the current one.  With no extent
 // buffer only the intents are copied.
-__global__ void __launch_bounds__(kBlock) k_output_block(const uint64_t *__restrict__ intents,
+__global__ void __launch_bounds__(kOutThreads) k_output_block(const uint64_t *__restrict__ intents,
                                                           const uint64_t *__restrict__ loff,
                                                           const uint32_t *__restrict__ objs,
                                                           const uint32_t *__restrict__ perm, uint64_t K, int wm,
@@ -1541,7 +1541,7 @@ __global__ void __launch_bounds__(kBlock) k_output_block(const uint64_t *__restr
     const bool ext = extents_out != nullptr;
     const int words = R * wn;
     if (ext)
-        for (int w = threadIdx.x; w < words; w += kBlock) s_rows[w] = 0;
+        for (int w = threadIdx.x; w < words; w += kOutThreads) s_rows[w] = 0;
     // stores of two words at a time need a 16-byte aligned region start
     const bool pairs = ((reinterpret_cast<uintptr_t>(extents_out) & 15) == 0) && (words & 1) == 0;
     const uint64_t nblk = (K + R - 1) / R;
@@ -1564,7 +1564,7 @@ __global__ void __launch_bounds__(kBlock) k_output_block(const uint64_t *__restr
         const uint64_t r0 = b * (uint64_t)R;
         const int nr = (int)((K - r0) < (uint64_t)R ? (K - r0) : (uint64_t)R);
         // intents: nr*wm consecutive output words; every lane takes part in the shuffle
-        for (int t0 = 0; t0 < nr * wm; t0 += kBlock) {
+        for (int t0 = 0; t0 < nr * wm; t0 += kOutThreads) {
             const int t = t0 + (int)threadIdx.x;
             int row = t / wm;
             row = row < nr ? row : nr - 1;
@@ -1575,7 +1575,7 @@ __global__ void __launch_bounds__(kBlock) k_output_block(const uint64_t *__restr
             fetch(b + gridDim.x);
             continue;
         }
-        for (int rr = wv; rr < nr; rr += kWavesPerBlock) {
+        for (int rr = wv; rr < nr; rr += kOutWaves) {
             const uint64_t o = __shfl(lo, rr), e = __shfl(hi, rr);
             uint64_t *T = s_rows + rr * wn;
             for (uint64_t p = o + lane; p < e; p += kWave) {
@@ -1591,7 +1591,7 @@ __global__ void __launch_bounds__(kBlock) k_output_block(const uint64_t *__restr
             u64x2 *S = reinterpret_cast<u64x2 *>(s_rows);
             u64x2 *D = reinterpret_cast<u64x2 *>(extents_out + base);
             const u64x2 z = {0, 0};
-            for (int e = threadIdx.x; e < (cnt >> 1); e += kBlock) {
+            for (int e = threadIdx.x; e < (cnt >> 1); e += kOutThreads) {
                 const u64x2 v = S[e];
                 S[e] = z;
                 __builtin_nontemporal_store(v, &D[e]);
@@ -1601,7 +1601,7 @@ __global__ void __launch_bounds__(kBlock) k_output_block(const uint64_t *__restr
                 s_rows[cnt - 1] = 0;
             }
         } else {
-            for (int e = threadIdx.x; e < cnt; e += kBlock) {
+            for (int e = threadIdx.x; e < cnt; e += kOutThreads) {
                 const uint64_t v = s_rows[e];
                 s_rows[e] = 0;
                 __builtin_nontemporal_store(v, &extents_out[base + e]);
