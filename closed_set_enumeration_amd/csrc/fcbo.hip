@@ -278,11 +278,9 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
 {
     const unsigned gm = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(1024, div_up(P, kWavesPerBlock)));
     const bool bm = A.huge.bmp != nullptr;
+    // local tests; the same pass counts every parent's tests and lists the mid
+    // and huge parents
     hipEvent_t b = c->prof_begin();
-    hipLaunchKernelGGL(k_huge_tasks<WMC>, dim3(gm), dim3(kBlock), 0, c->stream, A);
-    CK_LAUNCH();
-    c->prof_end(FCBO_K_TEST_BIG, b);
-    b = c->prof_begin();
     {
         constexpr int kW = LocalCfg<WMC>::kWaves;
         const uint64_t chunks = div_up(P, (uint64_t)LocalCfg<WMC>::kChunk);
@@ -291,6 +289,14 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
     }
     CK_LAUNCH();
     c->prof_end(FCBO_K_TEST_LOCAL, b);
+    // test offsets of the huge parents; total -> counters
+    b = c->prof_begin();
+    c->scan(c->huge.n, nullptr, c->counters + CNT_HUGE, 0, P, c->huge.off, nullptr, c->counters + CNT_THUGE, nullptr);
+    c->prof_end(FCBO_K_SCAN, b);
+    b = c->prof_begin();
+    hipLaunchKernelGGL(k_huge_tasks<WMC>, dim3(gm), dim3(kBlock), 0, c->stream, A);
+    CK_LAUNCH();
+    c->prof_end(FCBO_K_TEST_BIG, b);
     if constexpr (WMC <= 8) {
         b = c->prof_begin();
         const unsigned gmid = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(2048, div_up(P, kMidWaves)));
@@ -411,16 +417,8 @@ void fcbo_context::enumerate_levels()
             if (redos > 2) throw HipError{FCBO_ERR_DEVICE};  // a grown buffer always fits the redo
             LevelArgs A = level_args(lo, P, obj_hi);
             CK(hipMemsetAsync(counters, 0, CNT_N * sizeof(uint64_t), stream));
-            hipEvent_t b = prof_begin();
-            hipLaunchKernelGGL(k_count, dim3((unsigned)div_up(P, kBlock)), dim3(kBlock), 0, stream, A);
-            CK_LAUNCH();
-            prof_end(FCBO_K_COUNT, b);
-            b = prof_begin();
-            // test offsets of the huge parents; total -> counters
-            scan(huge.n, nullptr, counters + CNT_HUGE, 0, P, huge.off, nullptr, counters + CNT_THUGE, nullptr);
-            prof_end(FCBO_K_SCAN, b);
             fns.tests(this, A, P);
-            b = prof_begin();
+            hipEvent_t b = prof_begin();
             scan(huge.size, nullptr, counters + CNT_THUGE, 0, A.huge.cap, huge.sscan, nullptr, nullptr, nullptr);
             scan(nchild, nobj, nullptr, P, P, cbase, obase, counters + CNT_CHILDREN, counters + CNT_OBJS);
             prof_end(FCBO_K_SCAN, b);

@@ -15,10 +15,10 @@
 // handful of objects, so a list is hundreds of times smaller than a bitmap of
 // N bits.
 //
-// Per level (parents in three classes by extent size a, see k_count):
-//   k_count          candidates per parent, item pairs, the mid and huge lists
-//   k_local_test     a <= 64: parents packed into wavefronts, one lane per
-//                    candidate, rows staged in LDS; child records
+// Per level (parents in three classes by extent size a):
+//   k_local_test     every parent: closure tests counted, item pairs, the mid
+//                    and huge lists; a <= 64: parents packed into wavefronts,
+//                    one lane per candidate, rows staged in LDS; child records
 //   k_mid_test       64 < a <= 4096 (intents up to 8 words): closure tests by
 //                    incidence, one D per carried attribute in LDS; records
 //   k_huge_*         larger parents: one item per (test, 64-word chunk of the
@@ -160,6 +160,13 @@ __device__ __forceinline__ uint64_t wave_and(uint64_t v)
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
+{
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) v += __shfl_xor(v, s);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum64(uint64_t v)
 {
 #pragma unroll
     for (int s = 32; s > 0; s >>= 1) v += __shfl_xor(v, s);
@@ -323,69 +330,6 @@ __device__ __forceinline__ uint64_t wave_or(uint64_t v)
     return v;
 }
 
-// One thread per parent: candidate count (tests), item pairs, the medium and
-// big parent lists, and zeroed outputs for the test kernels.
-__global__ void __launch_bounds__(kBlock) k_count(LevelArgs A)
-{
-    __shared__ uint64_t s_red[5][kWavesPerBlock];
-    const uint64_t p = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    uint32_t tests = 0, pairs = 0;
-    uint64_t local_objs = 0, mid_objs = 0, big_scan = 0;
-    bool is_mid = false, is_huge = false;
-    if (p < A.P) {
-        const uint64_t c = A.lo + p;
-        const int y = A.cursor[c];
-        for (int u = 0; u < A.wm; ++u) {
-            uint64_t cand = ~A.intents[c * A.wm + u] & above_mask(y, u);
-            if (u == A.wm - 1) cand &= A.tail_m;
-            tests += __popcll(cand);
-        }
-        pairs = (uint32_t)(A.m - 1 - y);
-        const uint64_t a = A.loff[c + 1] - A.loff[c];
-        if (a > (uint64_t)A.mid_max) {
-            is_huge = true;
-            big_scan = a * tests;
-        } else {
-            is_mid = a > (uint64_t)kSmallMax;
-            (is_mid ? mid_objs : local_objs) = a;
-        }
-        A.nchild[p] = 0;
-        A.nobj[p] = 0;
-    }
-    {
-        const BigSet &S = A.huge;
-        const uint64_t bal = __ballot(is_huge);
-        if (bal) {
-            const int lane = lane_id();
-            const int leader = __ffsll((unsigned long long)bal) - 1;
-            uint64_t base = 0;
-            if (lane == leader)
-                base = atomicAdd((unsigned long long *)&A.counters[S.cnt_slot], (unsigned long long)__popcll(bal));
-            base = __shfl(base, leader);
-            if (is_huge) {
-                const uint64_t pos = base + __popcll(bal & below_mask(lane));
-                S.idx[pos] = (uint32_t)p;
-                S.n[pos] = tests;
-            }
-        }
-    }
-    wave_append(is_mid, (uint32_t)p, A.mid_idx, &A.counters[CNT_MID]);
-    uint64_t v[5] = {tests, pairs, local_objs, mid_objs, big_scan};
-#pragma unroll
-    for (int i = 0; i < 5; ++i)
-#pragma unroll
-        for (int s = 32; s > 0; s >>= 1) v[i] += __shfl_xor(v[i], s);
-    if (lane_id() == 0)
-        for (int i = 0; i < 5; ++i) s_red[i][threadIdx.x / kWave] = v[i];
-    __syncthreads();
-    if (threadIdx.x < 5) {
-        uint64_t sum = 0;
-        for (int w = 0; w < kWavesPerBlock; ++w) sum += s_red[threadIdx.x][w];
-        const int slot[5] = {CNT_TESTS, CNT_PAIRS, CNT_SMALL_OBJS, CNT_MID_OBJS, CNT_BIG_SCAN};
-        if (sum) atomicAdd((unsigned long long *)&A.counters[slot[threadIdx.x]], (unsigned long long)sum);
-    }
-}
-
 // --- local parents (|A| <= 64): closure tests packed across parents -----------
 //
 // For a candidate j (j > y, j not in B) let c_j be the objects of A having j.
@@ -467,10 +411,14 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     __shared__ uint32_t s_seg[kW][kWave];             // per group parent: first slot | objects << 8
     __shared__ uint32_t s_run[kW][2 * kWave];         // per group parent: children, their objects
     __shared__ uint8_t s_owner[kW][kWave];            // group parent whose slots start here
+    __shared__ uint64_t s_sum[5][kW];                 // level counters, per wavefront
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = words_of<WMC>(A.wm);
     const int gmax = kWave / wm;  // parents per group: one lane per (parent, word)
+    // this lane's share of the level counters: tests, item pairs, objects of
+    // local and of mid parents, list entries the huge tests would scan
+    uint64_t n_tests = 0, n_pairs = 0, n_local_objs = 0, n_mid_objs = 0, n_big_scan = 0;
     uint64_t *R = s_rows[wv];
     const uint32_t *R32 = (const uint32_t *)R;
     uint64_t *SB = s_b[wv];
@@ -501,13 +449,13 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
         const uint64_t p0 = ch * CH;
         const int nq = (int)((A.P - p0) < (uint64_t)CH ? (A.P - p0) : (uint64_t)CH);
         // parent lanes: list start, size (0 unless local), cursor
-        uint64_t o0 = 0;
+        uint64_t o0 = 0, sz = 0;
         int a = 0, y = 0;
         bool act = false;
         if (lane < nq) {
             const uint64_t c = A.lo + p0 + lane;
             o0 = A.loff[c];
-            const uint64_t sz = A.loff[c + 1] - o0;
+            sz = A.loff[c + 1] - o0;
             y = A.cursor[c];
             act = sz <= (uint64_t)kSmallMax;
             a = act ? (int)sz : 0;
@@ -521,6 +469,37 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
             }
         }
         wave_sync();
+        {
+            // every parent of the chunk: closure tests (attributes above the
+            // cursor outside B), item pairs, class; mid and huge parents go to
+            // their lists, with counts cleared for their test kernels
+            uint32_t nt = 0;
+            if (lane < nq)
+                for (int u = 0; u < wm; ++u) nt += (uint32_t)__popcll(~SB[lane * wm + u] & above_mask(y, u));
+            const bool is_huge = lane < nq && sz > (uint64_t)A.mid_max;
+            const bool is_mid = lane < nq && !is_huge && !act;
+            if (lane < nq) {
+                n_tests += nt;
+                n_pairs += (uint64_t)(A.m - 1 - y);
+                if (act) n_local_objs += sz;
+                if (is_mid) n_mid_objs += sz;
+                if (is_huge) n_big_scan += sz * nt;
+            }
+            const BigSet &S = A.huge;
+            const uint64_t hb = __ballot(is_huge);
+            if (hb) {
+                const uint64_t hpos = wave_slot(hb, &A.counters[S.cnt_slot]);
+                if (is_huge) {
+                    S.idx[hpos] = (uint32_t)(p0 + lane);
+                    S.n[hpos] = nt;
+                }
+            }
+            wave_append(is_mid, (uint32_t)(p0 + lane), A.mid_idx, &A.counters[CNT_MID]);
+            if (is_mid || is_huge) {
+                A.nchild[p0 + lane] = 0;
+                A.nobj[p0 + lane] = 0;
+            }
+        }
         int j0 = -1;  // first attribute outside B, when above y
         if (act) {
             for (int u = 0; u < wm; ++u) {
@@ -671,19 +650,30 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
                 }
                 wave_sync();
             }
-            // per-parent totals (the count kernel zeroed them)
+            // per-parent totals
             if (in && act) {
-                const uint32_t nc = RUN[2 * (lane - s)];
-                if (nc) {
-                    A.nchild[p0 + lane] = nc;
-                    A.nobj[p0 + lane] = RUN[2 * (lane - s) + 1];
-                }
+                A.nchild[p0 + lane] = RUN[2 * (lane - s)];
+                A.nobj[p0 + lane] = RUN[2 * (lane - s) + 1];
             }
             wave_sync();
             s = e;
         }
     }
     if (rchunk != ~0ull && lane == 0 && rchunk < A.lrec_cap) A.lfill[rchunk / kWave] = fill;
+    // level counters: wavefront sums, then one atomic per workgroup and counter
+    uint64_t v[5] = {n_tests, n_pairs, n_local_objs, n_mid_objs, n_big_scan};
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        v[i] = wave_sum64(v[i]);
+        if (lane == 0) s_sum[i][wv] = v[i];
+    }
+    __syncthreads();
+    if (threadIdx.x < 5) {
+        uint64_t sum = 0;
+        for (int w = 0; w < kW; ++w) sum += s_sum[threadIdx.x][w];
+        const int slot[5] = {CNT_TESTS, CNT_PAIRS, CNT_SMALL_OBJS, CNT_MID_OBJS, CNT_BIG_SCAN};
+        if (sum) atomicAdd((unsigned long long *)&A.counters[slot[threadIdx.x]], (unsigned long long)sum);
+    }
 }
 
 // Children of the local parents, one thread per record slot: intent, cursor and

@@ -60,7 +60,8 @@ enum {
 
 /* Kernel classes reported in fcbo_stats.kernel_ms / kernel_launches. */
 enum {
-    FCBO_K_COUNT = 0,        /* per-parent candidate count, parent classes */
+    FCBO_K_COUNT = 0,        /* reserved: the per-parent counts and classes are made by the
+                                local test kernel and timed under FCBO_K_TEST_LOCAL */
     FCBO_K_TEST_LOCAL = 1,   /* closure tests of parents with <= 64 objects */
     FCBO_K_TEST_MEDIUM = 2,  /* closure tests of parents with 65..4096 objects (M <= 512 only) */
     FCBO_K_TEST_BIG = 3,     /* closure tests of the larger parents (tasks + tests) */
