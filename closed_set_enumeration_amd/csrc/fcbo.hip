@@ -143,7 +143,8 @@ struct fcbo_context {
     uint64_t *dt = nullptr;                     // huge tests: D accumulators
     uint32_t *tcnt = nullptr, *icnt = nullptr;  // huge tests: |C|, per-chunk counts
     uint64_t *scan_part = nullptr;  // 2 x kScanBlocks
-    uint64_t *counters = nullptr;   // CNT_N
+    uint64_t *counters = nullptr;   // 2 x CNT_N: levels alternate between the halves
+    int ctr = 0;                    // half of the current level
     uint64_t *h_counters = nullptr; // pinned, CNT_N
 
     // output order
@@ -238,24 +239,32 @@ struct fcbo_context {
         if (bm) A.huge.cap = std::min(A.huge.cap, std::min(std::min(cap_dt / wm, cap_tcnt), cap_icnt / nchunk()));
         A.dt = dt; A.tcnt = tcnt; A.icnt = icnt;
         A.nchunk = nchunk();
-        A.counters = counters;
+        A.counters = counters + (uint64_t)ctr * CNT_N;
+        A.counters_next = counters + (uint64_t)(1 - ctr) * CNT_N;
         return A;
     }
 
     // exclusive scan (see k_scan_*): a (and b) -> out_a (and out_b), n from the
-    // device or the host.
+    // device or the host; fch (optional) receives fbase + out_a as u32.
     void scan(const uint32_t *a, const uint32_t *b, const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
-              uint64_t *out_a, uint64_t *out_b, uint64_t *tot_a, uint64_t *tot_b)
+              uint64_t *out_a, uint64_t *out_b, uint64_t *tot_a, uint64_t *tot_b, uint32_t *fch = nullptr,
+              uint64_t fbase = 0)
     {
+        if (!n_dev && n_host <= kScanSmallMax) {
+            hipLaunchKernelGGL(k_scan_small, dim3(1), dim3(kScanBlocks), 0, stream, a, b, std::min(n_host, n_cap),
+                               out_a, out_b, tot_a, tot_b, fch, fbase);
+            CK_LAUNCH();
+            return;
+        }
         int nb = kScanBlocks;
         if (!n_dev) nb = (int)std::min<uint64_t>(kScanBlocks, std::max<uint64_t>(1, div_up(n_host, 4 * kBlock)));
         hipLaunchKernelGGL(k_scan_up, dim3(nb), dim3(kBlock), 0, stream, a, b, n_dev, n_host, n_cap, scan_part);
         CK_LAUNCH();
         hipLaunchKernelGGL(k_scan_mid, dim3(1), dim3(kScanBlocks), 0, stream, scan_part, nb, n_dev, n_host, n_cap,
-                           out_a, out_b, tot_a, tot_b);
+                           out_a, out_b, tot_a, tot_b, fch, fbase);
         CK_LAUNCH();
         hipLaunchKernelGGL(k_scan_down, dim3(nb), dim3(kBlock), 0, stream, a, b, n_dev, n_host, n_cap,
-                           (const uint64_t *)scan_part, out_a, out_b);
+                           (const uint64_t *)scan_part, out_a, out_b, fch, fbase);
         CK_LAUNCH();
     }
 
@@ -273,8 +282,13 @@ struct fcbo_context {
 
 namespace {
 
+// Which parent classes a level has: the local test kernel always runs (it also
+// counts and classifies); the mid and huge kernels only when the level holds
+// such parents.
+enum { kLevelMid = 1, kLevelHuge = 2 };
+
 template <int WMC>
-void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
+void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigned classes)
 {
     const unsigned gm = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(1024, div_up(P, kWavesPerBlock)));
     const bool bm = A.huge.bmp != nullptr;
@@ -289,21 +303,27 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
     }
     CK_LAUNCH();
     c->prof_end(FCBO_K_TEST_LOCAL, b);
-    // test offsets of the huge parents; total -> counters
-    b = c->prof_begin();
-    c->scan(c->huge.n, nullptr, c->counters + CNT_HUGE, 0, P, c->huge.off, nullptr, c->counters + CNT_THUGE, nullptr);
-    c->prof_end(FCBO_K_SCAN, b);
-    b = c->prof_begin();
-    hipLaunchKernelGGL(k_huge_tasks<WMC>, dim3(gm), dim3(kBlock), 0, c->stream, A);
-    CK_LAUNCH();
-    c->prof_end(FCBO_K_TEST_BIG, b);
-    if constexpr (WMC <= 8) {
+    if (classes & kLevelHuge) {
+        // test offsets of the huge parents; total -> counters
         b = c->prof_begin();
-        const unsigned gmid = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(2048, div_up(P, kMidWaves)));
-        hipLaunchKernelGGL(k_mid_test<WMC>, dim3(gmid), dim3(kWave * kMidWaves), 0, c->stream, A);
+        c->scan(c->huge.n, nullptr, A.counters + CNT_HUGE, 0, P, c->huge.off, nullptr, A.counters + CNT_THUGE,
+                nullptr);
+        c->prof_end(FCBO_K_SCAN, b);
+        b = c->prof_begin();
+        hipLaunchKernelGGL(k_huge_tasks<WMC>, dim3(gm), dim3(kBlock), 0, c->stream, A);
         CK_LAUNCH();
-        c->prof_end(FCBO_K_TEST_MEDIUM, b);
+        c->prof_end(FCBO_K_TEST_BIG, b);
     }
+    if constexpr (WMC <= 8) {
+        if (classes & kLevelMid) {
+            b = c->prof_begin();
+            const unsigned gmid = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(2048, div_up(P, kMidWaves)));
+            hipLaunchKernelGGL(k_mid_test<WMC>, dim3(gmid), dim3(kWave * kMidWaves), 0, c->stream, A);
+            CK_LAUNCH();
+            c->prof_end(FCBO_K_TEST_MEDIUM, b);
+        }
+    }
+    if (!(classes & kLevelHuge)) return;
     b = c->prof_begin();
     if (bm) {
         hipLaunchKernelGGL(k_huge_partial<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
@@ -314,10 +334,14 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P)
     }
     CK_LAUNCH();
     c->prof_end(FCBO_K_TEST_BIG, b);
+    // sibling offsets of the passing huge tests
+    b = c->prof_begin();
+    c->scan(c->huge.size, nullptr, A.counters + CNT_THUGE, 0, A.huge.cap, c->huge.sscan, nullptr, nullptr, nullptr);
+    c->prof_end(FCBO_K_SCAN, b);
 }
 
 template <int WMC>
-void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P)
+void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigned classes)
 {
     const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kBlock)));
     hipEvent_t b = c->prof_begin();
@@ -325,11 +349,14 @@ void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P)
     CK_LAUNCH();
     c->prof_end(FCBO_K_WRITE_LOCAL, b);
     if constexpr (WMC <= 8) {
-        b = c->prof_begin();
-        hipLaunchKernelGGL(k_mid_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
-        CK_LAUNCH();
-        c->prof_end(FCBO_K_WRITE_MEDIUM, b);
+        if (classes & kLevelMid) {
+            b = c->prof_begin();
+            hipLaunchKernelGGL(k_mid_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+            CK_LAUNCH();
+            c->prof_end(FCBO_K_WRITE_MEDIUM, b);
+        }
     }
+    if (!(classes & kLevelHuge)) return;
     b = c->prof_begin();
     if (A.huge.bmp)
         hipLaunchKernelGGL(k_huge_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
@@ -339,7 +366,7 @@ void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P)
     c->prof_end(FCBO_K_WRITE_BIG, b);
 }
 
-typedef void (*level_fn)(fcbo_context *, const LevelArgs &, uint64_t);
+typedef void (*level_fn)(fcbo_context *, const LevelArgs &, uint64_t, unsigned);
 
 struct LevelFns {
     level_fn tests, writes;
@@ -398,6 +425,13 @@ void fcbo_context::enumerate_levels()
     if (!mrec) ensure(mrec, cap_mrec, rstride * (tiny ? 1 : (1u << 18)), 0, stream, 1);
     if (!lrec) ensure_local_records(tiny ? kWave : (1u << 21));
     uint64_t lo = 0, P = 1, obj_hi = (uint64_t)n;  // parents [lo, lo+P); objects used so far
+    const uint64_t mid_max = wm <= 8 ? (uint64_t)kMidMax : (uint64_t)kSmallMax;
+    // parents of each class on the level about to run (the root: N objects);
+    // later levels learn them from the children counted by the test kernels
+    uint64_t next_mid = ((uint64_t)n > (uint64_t)kSmallMax && (uint64_t)n <= mid_max) ? 1 : 0;
+    uint64_t next_huge = (uint64_t)n > mid_max ? 1 : 0;
+    ctr = 0;
+    CK(hipMemsetAsync(counters, 0, 2 * CNT_N * sizeof(uint64_t), stream));
     while (P > 0) {
         if (P >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
         // every level adds an attribute to the intent, so there are at most M + 1
@@ -408,22 +442,33 @@ void fcbo_context::enumerate_levels()
         ensure(cbase, cap_cb, P + 1, 0, stream, mc);
         ensure(obase, cap_ob, P + 1, 0, stream, mc);
         ensure(mid_idx, cap_mid, P, 0, stream, mc);
+        ensure(fchild, cap_fch, lo + P + 1, lo + 1, stream, mc);
         huge.ensure_members(P, stream, mc);
+        unsigned classes = (next_mid ? kLevelMid : 0u) | (next_huge ? kLevelHuge : 0u);
         bool redo;
         int redos = 0;
         uint64_t n_children = 0, n_objs = 0;
         do {
             redo = false;
-            if (redos > 2) throw HipError{FCBO_ERR_DEVICE};  // a grown buffer always fits the redo
+            // a grown buffer always fits the redo; a class miss turns every kernel on
+            if (redos > 3) throw HipError{FCBO_ERR_DEVICE};
             LevelArgs A = level_args(lo, P, obj_hi);
-            CK(hipMemsetAsync(counters, 0, CNT_N * sizeof(uint64_t), stream));
-            fns.tests(this, A, P);
+            if (redos) CK(hipMemsetAsync(A.counters, 0, CNT_N * sizeof(uint64_t), stream));
+            fns.tests(this, A, P, classes);
             hipEvent_t b = prof_begin();
-            scan(huge.size, nullptr, counters + CNT_THUGE, 0, A.huge.cap, huge.sscan, nullptr, nullptr, nullptr);
-            scan(nchild, nobj, nullptr, P, P, cbase, obase, counters + CNT_CHILDREN, counters + CNT_OBJS);
+            // child offsets per parent, and the first child of every parent
+            scan(nchild, nobj, nullptr, P, P, cbase, obase, A.counters + CNT_CHILDREN, A.counters + CNT_OBJS,
+                 fchild + lo, lo + P);
             prof_end(FCBO_K_SCAN, b);
-            CK(hipMemcpyAsync(h_counters, counters, CNT_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+            CK(hipMemcpyAsync(h_counters, A.counters, CNT_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
             CK(hipStreamSynchronize(stream));
+            const unsigned found = (h_counters[CNT_MID] ? kLevelMid : 0u) | (h_counters[CNT_HUGE] ? kLevelHuge : 0u);
+            if (found & ~classes) {  // parents of a class whose kernels did not run
+                classes |= found;
+                redo = true;
+                ++redos;
+                continue;
+            }
             if (h_counters[CNT_OVERFLOW]) {
                 if (bm) {
                     ensure_huge_tests(h_counters[CNT_THUGE]);
@@ -439,6 +484,8 @@ void fcbo_context::enumerate_levels()
             }
             n_children = h_counters[CNT_CHILDREN];
             n_objs = h_counters[CNT_OBJS];
+            next_mid = h_counters[CNT_NEXT_MID];
+            next_huge = h_counters[CNT_NEXT_HUGE];
             lev_concepts.push_back(P);
             lev_tests.push_back(h_counters[CNT_TESTS]);
             tests += h_counters[CNT_TESTS];
@@ -459,11 +506,9 @@ void fcbo_context::enumerate_levels()
             ensure(loff, cap_loff, k_end + 1, keep_k + 1, stream, mc);
             ensure(objs, cap_o, obj_hi + n_objs, obj_hi, stream, mc);
             ensure(fchild, cap_fch, k_end + 1, keep_k + 1, stream, mc);
-            hipLaunchKernelGGL(k_first_child, dim3((unsigned)div_up(P + 1, kBlock)), dim3(kBlock), 0, stream,
-                               (const uint64_t *)cbase, lo, P, (const uint64_t *)counters, fchild);
-            CK_LAUNCH();
-            if (n_children) fns.writes(this, level_args(lo, P, obj_hi), P);
+            if (n_children) fns.writes(this, level_args(lo, P, obj_hi), P, classes);
         } while (redo);
+        ctr ^= 1;
         lo += P;
         P = n_children;
         obj_hi += n_objs;
@@ -585,7 +630,7 @@ int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs
         CK(hipMalloc((void **)&c->rows, ((uint64_t)n_objects + 1) * c->wm * sizeof(uint64_t)));
         CK(hipMalloc((void **)&c->cols, (uint64_t)n_attrs * c->wn * sizeof(uint64_t)));
         CK(hipMalloc((void **)&c->scan_part, 2 * kScanBlocks * sizeof(uint64_t)));
-        CK(hipMalloc((void **)&c->counters, CNT_N * sizeof(uint64_t)));
+        CK(hipMalloc((void **)&c->counters, 2 * CNT_N * sizeof(uint64_t)));
         CK(hipHostMalloc((void **)&c->h_counters, CNT_N * sizeof(uint64_t), hipHostMallocDefault));
         CK(hipMemsetAsync(c->rows, 0, ((uint64_t)n_objects + 1) * c->wm * sizeof(uint64_t), c->stream));
         const hipMemcpyKind kind = (flags & FCBO_ROWS_ON_DEVICE) ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;

@@ -39,6 +39,7 @@ constexpr int kSmallMax = 64;       // parents with at most this many objects us
 constexpr int kBlock = 256;         // threads per block for wave-per-item kernels
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kScanBlocks = 1024;   // blocks of the multi-block exclusive scan
+constexpr uint64_t kScanSmallMax = 8192; // host-known lengths up to this are scanned by one workgroup
 constexpr int kOutTileWords = 1024; // extent words staged in LDS per output tile
 constexpr int kBmpMaxWords = 16384; // big parents use extent bitmaps when N <= 64 * this
 constexpr int kMidMax = 4096;       // parents with more objects are huge (tested a chunk at a time)
@@ -60,7 +61,9 @@ enum {
     CNT_MID_OBJS = 11, // objects in the extents of mid parents
     CNT_MIDREC = 12,   // child records written by the mid parents
     CNT_LOCREC = 13,   // record slots reserved by the local parents (64 per chunk)
-    CNT_N = 14
+    CNT_NEXT_MID = 14, // children that will be mid parents (64 < |C| <= mid_max)
+    CNT_NEXT_HUGE = 15, // children that will be huge parents (|C| > mid_max)
+    CNT_N = 16
 };
 
 // Huge parents, tested one closure test at a time: one work item per (test,
@@ -113,7 +116,8 @@ struct LevelArgs {
     uint32_t *icnt;        // per (huge test, 64-word chunk): objects of C in the chunk, then offsets
     int nchunk;            // ceil(wn / 64)
     uint64_t tail_n;       // valid bits of the last extent word
-    uint64_t *counters;    // CNT_*
+    uint64_t *counters;    // CNT_* of this level
+    uint64_t *counters_next; // CNT_* of the next level, cleared by the local test kernel
 };
 
 // ---------------------------------------------------------------------------
@@ -444,6 +448,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
         fill += n;
         return at;
     };
+    if (blockIdx.x == 0 && threadIdx.x < CNT_N) A.counters_next[threadIdx.x] = 0;
     const uint64_t nchunks = (A.P + CH - 1) / CH;
     for (uint64_t ch = (uint64_t)blockIdx.x * kW + wv; ch < nchunks; ch += (uint64_t)gridDim.x * kW) {
         const uint64_t p0 = ch * CH;
@@ -782,6 +787,10 @@ __device__ __forceinline__ void big_record_pass(const LevelArgs &A, const BigSet
     atomicAdd(&A.nobj[p], cnt);
     const uint64_t pos = atomicAdd((unsigned long long *)&A.counters[S.pass_slot], 1ull);
     S.plist[pos] = t;
+    if (cnt > (uint32_t)A.mid_max)
+        atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_HUGE], 1ull);
+    else if (cnt > (uint32_t)kSmallMax)
+        atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_MID], 1ull);
 }
 
 // Rank of attribute j among the passing attributes of parent p.
@@ -851,6 +860,7 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
     const int wm = words_of<WMC>(A.wm);
     uint64_t *Dt = s_d[wv];
     uint32_t *Ct = s_c[wv];
+    uint32_t next_mid = 0;
     const uint64_t count = A.counters[CNT_MID];
     const uint64_t rstride = 4 + (uint64_t)A.wm;
     for (uint64_t it = (uint64_t)blockIdx.x * kMidWaves + wv; it < count; it += (uint64_t)gridDim.x * kMidWaves) {
@@ -962,6 +972,9 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
             const uint64_t bal = __ballot(pass);
             if (!bal) continue;
             const int leader = __ffsll((unsigned long long)bal) - 1;
+            // children that are mid parents on the next level (fewer objects
+            // than this parent, so never huge), added up per wavefront
+            next_mid += (uint32_t)__popcll(__ballot(pass && cnt > (uint32_t)kSmallMax));
             uint64_t base = 0;
             if (lane == leader)
                 base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC], (unsigned long long)__popcll(bal));
@@ -994,6 +1007,7 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    if (next_mid && lane == 0) atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_MID], (unsigned long long)next_mid);
 }
 
 // Children of the mid parents, one wavefront per record: intent and cursor
@@ -1316,7 +1330,8 @@ __global__ void __launch_bounds__(kBlock) k_scan_up(const uint32_t *__restrict__
 // One block of kScanBlocks threads: exclusive scan of the block partials.
 __global__ void __launch_bounds__(kScanBlocks) k_scan_mid(uint64_t *part, int nblocks, const uint64_t *n_dev,
                                                           uint64_t n_host, uint64_t n_cap, uint64_t *out_a,
-                                                          uint64_t *out_b, uint64_t *tot_a, uint64_t *tot_b)
+                                                          uint64_t *out_b, uint64_t *tot_a, uint64_t *tot_b,
+                                                          uint32_t *fch, uint64_t fbase)
 {
     __shared__ uint64_t s_w[2][kScanBlocks / kWave];
     const int t = threadIdx.x, lane = lane_id(), wv = t / kWave;
@@ -1354,12 +1369,14 @@ __global__ void __launch_bounds__(kScanBlocks) k_scan_mid(uint64_t *part, int nb
         if (out_b) out_b[n] = tb;
         if (tot_a) *tot_a = ta;
         if (tot_b) *tot_b = tb;
+        if (fch) fch[n] = (uint32_t)(fbase + ta);
     }
 }
 
 __global__ void __launch_bounds__(kBlock) k_scan_down(const uint32_t *__restrict__ a, const uint32_t *__restrict__ b,
                                                        const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
-                                                       const uint64_t *part, uint64_t *out_a, uint64_t *out_b)
+                                                       const uint64_t *part, uint64_t *out_a, uint64_t *out_b,
+                                                       uint32_t *fch, uint64_t fbase)
 {
     __shared__ uint64_t s_wave[kWavesPerBlock];
     const uint64_t n = scan_count(n_dev, n_host, n_cap);
@@ -1372,13 +1389,70 @@ __global__ void __launch_bounds__(kBlock) k_scan_down(const uint32_t *__restrict
         const bool ok = i < e;
         uint64_t tot;
         const uint64_t xa = block_excl_scan(ok ? (uint64_t)a[i] : 0ull, s_wave, tot);
-        if (ok) out_a[i] = carry_a + xa;
+        if (ok) {
+            out_a[i] = carry_a + xa;
+            if (fch) fch[i] = (uint32_t)(fbase + carry_a + xa);
+        }
         carry_a += tot;
         if (b) {
             const uint64_t xb = block_excl_scan(ok ? (uint64_t)b[i] : 0ull, s_wave, tot);
             if (ok) out_b[i] = carry_b + xb;
             carry_b += tot;
         }
+    }
+}
+
+// The same scan in one workgroup of kScanBlocks threads, for short arrays
+// whose length the host knows.
+__global__ void __launch_bounds__(kScanBlocks) k_scan_small(const uint32_t *__restrict__ a,
+                                                            const uint32_t *__restrict__ b, uint64_t n,
+                                                            uint64_t *out_a, uint64_t *out_b, uint64_t *tot_a,
+                                                            uint64_t *tot_b, uint32_t *fch, uint64_t fbase)
+{
+    __shared__ uint64_t s_w[kScanBlocks / kWave];
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    auto block_scan = [&](uint64_t v, uint64_t &total) -> uint64_t {
+        uint64_t x = v;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const uint64_t t = __shfl_up(x, s);
+            if (lane >= s) x += t;
+        }
+        if (lane == kWave - 1) s_w[wv] = x;
+        __syncthreads();
+        uint64_t before = 0, all = 0;
+        for (int w = 0; w < kScanBlocks / kWave; ++w) {
+            const uint64_t sw = s_w[w];
+            before += (w < wv) ? sw : 0ull;
+            all += sw;
+        }
+        __syncthreads();
+        total = all;
+        return before + x - v;
+    };
+    uint64_t carry_a = 0, carry_b = 0;
+    for (uint64_t base = 0; base < n; base += kScanBlocks) {
+        const uint64_t i = base + threadIdx.x;
+        const bool ok = i < n;
+        uint64_t tot;
+        const uint64_t xa = block_scan(ok ? (uint64_t)a[i] : 0ull, tot);
+        if (ok) {
+            out_a[i] = carry_a + xa;
+            if (fch) fch[i] = (uint32_t)(fbase + carry_a + xa);
+        }
+        carry_a += tot;
+        if (b) {
+            const uint64_t xb = block_scan(ok ? (uint64_t)b[i] : 0ull, tot);
+            if (ok) out_b[i] = carry_b + xb;
+            carry_b += tot;
+        }
+    }
+    if (threadIdx.x == 0) {
+        out_a[n] = carry_a;
+        if (out_b) out_b[n] = carry_b;
+        if (tot_a) *tot_a = carry_a;
+        if (tot_b) *tot_b = carry_b;
+        if (fch) fch[n] = (uint32_t)(fbase + carry_a);
     }
 }
 
@@ -1396,17 +1470,6 @@ __global__ void __launch_bounds__(kBlock) k_scan_down(const uint32_t *__restrict
 // Hence the position of a concept is its parent's position, plus one, plus the
 // subtree sizes of its siblings with a larger attribute.  Children of a concept
 // are stored contiguously by ascending attribute, as [fchild[c], fchild[c+1]).
-
-// Children of the parents [lo, lo + P): their first index, and the end.
-__global__ void __launch_bounds__(kBlock) k_first_child(const uint64_t *__restrict__ cbase, uint64_t lo, uint64_t P,
-                                                         const uint64_t *__restrict__ counters,
-                                                         uint32_t *__restrict__ fchild)
-{
-    const uint64_t p = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p > P) return;
-    const uint64_t rel = p < P ? cbase[p] : counters[CNT_CHILDREN];
-    fchild[lo + p] = (uint32_t)(lo + P + rel);
-}
 
 // Subtree sizes of the concepts [lo, lo + P); their children's sizes are final.
 __global__ void __launch_bounds__(kBlock) k_subtree_size(const uint32_t *__restrict__ fchild, uint64_t lo,
