@@ -927,8 +927,7 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // canonical tests and child records
-        uint32_t run_rank = 0, run_obj = 0;
+        // canonical tests: a passing candidate keeps its |C| with the top bit set
         bool bottom = false;
         if (j0 > y) {
             bottom = true;
@@ -936,22 +935,7 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
             for (int u = 0; u < WMC; ++u)
                 if (u == (j0 >> 6) && ((U[u] >> (j0 & 63)) & 1ull)) bottom = false;
         }
-        if (bottom) {  // the first attribute outside B: C = {}, D = M, rank 0
-            if (lane == 0) {
-                const uint64_t pos = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC], 1ull);
-                if (pos < A.mrec_cap) {
-                    uint64_t *rec = A.mrec + pos * rstride;
-                    rec[0] = p | ((uint64_t)j0 << 32);
-                    rec[1] = 0;
-                    rec[2] = 0;
-                    rec[3] = 0;
-                    for (int u = 0; u < wm; ++u) rec[4 + u] = (u == wm - 1) ? A.tail_m : ~0ull;
-                } else {
-                    A.counters[CNT_OVERFLOW] = 1;
-                }
-            }
-            run_rank = 1;
-        }
+        uint32_t n_pass = bottom ? 1u : 0u, n_obj = 0;
         for (int r0 = 0; r0 < nU; r0 += kWave) {
             const int r = r0 + lane;
             const bool active = r < nU;
@@ -969,43 +953,63 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
             }
             const bool pass = active && bad == 0;
             const uint32_t cnt = pass ? Ct[r] : 0u;
-            const uint64_t bal = __ballot(pass);
-            if (!bal) continue;
-            const int leader = __ffsll((unsigned long long)bal) - 1;
+            if (pass) Ct[r] = cnt | 0x80000000u;
+            n_pass += (uint32_t)__popcll(__ballot(pass));
+            n_obj += wave_sum(cnt);
             // children that are mid parents on the next level (fewer objects
             // than this parent, so never huge), added up per wavefront
             next_mid += (uint32_t)__popcll(__ballot(pass && cnt > (uint32_t)kSmallMax));
-            uint64_t base = 0;
-            if (lane == leader)
-                base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC], (unsigned long long)__popcll(bal));
-            base = __shfl(base, leader);
-            const uint32_t before = (uint32_t)__popcll(bal & below_mask(lane));
-            const uint32_t objoff = run_obj + wave_excl_scan(cnt);
-            if (pass) {
-                const uint64_t pos = base + before;
-                if (pos < A.mrec_cap) {
-                    uint64_t *rec = A.mrec + pos * rstride;
+        }
+        wave_sync();
+        // child records: one contiguous block per parent, in rank (ascending j)
+        // order, reserved with a single atomic
+        uint64_t base = 0;
+        if (lane == 0 && n_pass) base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC], (unsigned long long)n_pass);
+        base = uniform64(base);
+        const bool fits = base + n_pass <= A.mrec_cap;
+        if (!fits && lane == 0) A.counters[CNT_OVERFLOW] = 1;
+        if (lane == 0) {
+            A.nchild[p] = n_pass;
+            A.nobj[p] = n_obj;
+        }
+        if (fits && n_pass) {
+            uint32_t rank = 0, objoff = 0;
+            if (bottom) {  // the first attribute outside B: C = {}, D = M, rank 0
+                if (lane == 0) {
+                    uint64_t *rec = A.mrec + base * rstride;
+                    rec[0] = p | ((uint64_t)j0 << 32);
+                    rec[1] = 0;
+                    rec[2] = 0;
+                    rec[3] = 0;
+                    for (int u = 0; u < wm; ++u) rec[4 + u] = (u == wm - 1) ? A.tail_m : ~0ull;
+                }
+                rank = 1;
+            }
+            for (int r0 = 0; r0 < nU; r0 += kWave) {
+                const int r = r0 + lane;
+                const uint32_t cv = r < nU ? Ct[r] : 0u;
+                const bool pass = (cv >> 31) != 0;
+                const uint32_t cnt = pass ? (cv & 0x7FFFFFFFu) : 0u;
+                const uint64_t bal = __ballot(pass);
+                if (!bal) continue;
+                const uint32_t before = (uint32_t)__popcll(bal & below_mask(lane));
+                const uint32_t off = objoff + wave_excl_scan(cnt);
+                if (pass) {
+                    const int j = select_words<WMC>(U, wm, r);
+                    uint64_t *rec = A.mrec + (base + rank + before) * rstride;
                     rec[0] = p | ((uint64_t)j << 32);
-                    rec[1] = (uint64_t)(run_rank + before) | ((uint64_t)cnt << 32);
-                    rec[2] = objoff;
+                    rec[1] = (uint64_t)(rank + before) | ((uint64_t)cnt << 32);
+                    rec[2] = off;
                     rec[3] = 0;
 #pragma unroll
                     for (int u = 0; u < WMC; ++u)
                         if (u < wm) rec[4 + u] = (u == wm - 1) ? (Dt[r * WMC + u] & A.tail_m) : Dt[r * WMC + u];
-                } else {
-                    A.counters[CNT_OVERFLOW] = 1;
                 }
+                rank += (uint32_t)__popcll(bal);
+                objoff += wave_sum(cnt);
             }
-            run_rank += (uint32_t)__popcll(bal);
-            run_obj += wave_sum(cnt);
         }
-        if (lane == 0) {
-            A.nchild[p] = run_rank;
-            A.nobj[p] = run_obj;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_sync();
     }
     if (next_mid && lane == 0) atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_MID], (unsigned long long)next_mid);
 }
