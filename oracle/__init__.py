@@ -7,6 +7,9 @@ leg of the benchmark do.  It shares no code with the GPU path.
 * :func:`cbo` runs the serial Close-by-One in ``cbo.c`` (built with gcc into
   ``liboracle_cbo.so`` next to it) and returns sorted intents, extents and the
   work counters.
+* :func:`cbo_digest` runs the same search from ``cbo_digest.c`` with object
+  lists and no concept store, returning the counters and an order-independent
+  digest of the intents (for contexts whose concepts do not fit in memory).
 * :mod:`oracle.brute` holds two brute-force enumerations written straight from
   the definition of a concept, plus the CbO generation tree derived from the
   closed sets alone; they pin the C oracle on small contexts.
@@ -23,6 +26,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "cbo.c")
+_SRC_DIGEST = os.path.join(_HERE, "cbo_digest.c")
 _LIB = os.path.join(_HERE, "liboracle_cbo.so")
 
 
@@ -47,15 +51,31 @@ class _Result(ctypes.Structure):
     ]
 
 
+class _Digest(ctypes.Structure):
+    _fields_ = [
+        ("n_concepts", ctypes.c_int64),
+        ("tests", ctypes.c_int64),
+        ("pairs", ctypes.c_int64),
+        ("sum_c", ctypes.c_int64),
+        ("n_levels", ctypes.c_int32),
+        ("threads", ctypes.c_int32),
+        ("level_concepts", ctypes.POINTER(ctypes.c_int64)),
+        ("level_tests", ctypes.POINTER(ctypes.c_int64)),
+        ("digest", ctypes.c_uint64),
+        ("seconds", ctypes.c_double),
+    ]
+
+
 def build(force: bool = False) -> str:
-    """Compile ``cbo.c`` into ``liboracle_cbo.so`` (plain gcc, -O2, no SIMD flags)."""
+    """Compile ``cbo.c`` and ``cbo_digest.c`` into ``liboracle_cbo.so`` (plain gcc, -O2, no SIMD flags)."""
+    srcs = [_SRC, _SRC_DIGEST]
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
-        os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "oracle_cbo.h"))
+        [os.path.getmtime(x) for x in srcs] + [os.path.getmtime(os.path.join(_HERE, "oracle_cbo.h"))]
     ):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-D_POSIX_C_SOURCE=199309L", "-fPIC", "-shared",
-             "-Wall", "-Wextra", "-o", tmp, _SRC],
+            ["gcc", "-O2", "-std=c11", "-D_POSIX_C_SOURCE=199309L", "-fPIC", "-shared", "-pthread",
+             "-Wall", "-Wextra", "-o", tmp] + srcs,
             cwd=_HERE,
         )
         os.replace(tmp, _LIB)
@@ -76,6 +96,13 @@ def _load():
         lib.oracle_cbo.restype = ctypes.c_int
         lib.oracle_free.argtypes = [ctypes.POINTER(_Result)]
         lib.oracle_free.restype = None
+        lib.oracle_cbo_digest.argtypes = [
+            ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+            ctypes.POINTER(_Digest),
+        ]
+        lib.oracle_cbo_digest.restype = ctypes.c_int
+        lib.oracle_digest_free.argtypes = [ctypes.POINTER(_Digest)]
+        lib.oracle_digest_free.restype = None
         _lib = lib
     return _lib
 
@@ -141,3 +168,42 @@ def cbo(rows: np.ndarray, n_attrs: int, keep_extents: bool = True, max_tests: in
         )
     finally:
         lib.oracle_free(ctypes.byref(res))
+
+
+@dataclass
+class DigestResult:
+    n_concepts: int
+    tests: int
+    pairs: int
+    sum_c: int
+    n_levels: int
+    level_concepts: np.ndarray  # int64 [n_levels]
+    level_tests: np.ndarray     # int64 [n_levels]
+    digest: int                 # sum of the SplitMix64 chains of the intents, mod 2^64
+    threads: int
+    seconds: float
+
+
+def cbo_digest(rows: np.ndarray, n_attrs: int, threads: int = 1) -> DigestResult:
+    """Counters and intent digest of the CbO search, with no concept store."""
+    lib = _load()
+    rows = np.ascontiguousarray(rows, dtype=np.uint64)
+    if rows.ndim != 2:
+        raise ValueError("rows must be 2-D")
+    res = _Digest()
+    rc = lib.oracle_cbo_digest(
+        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), rows.shape[0], int(n_attrs), rows.shape[1],
+        int(threads), ctypes.byref(res),
+    )
+    if rc != 0:
+        raise RuntimeError("oracle_cbo_digest failed with %d" % rc)
+    try:
+        nl = res.n_levels
+        return DigestResult(
+            n_concepts=res.n_concepts, tests=res.tests, pairs=res.pairs, sum_c=res.sum_c, n_levels=nl,
+            level_concepts=np.ctypeslib.as_array(res.level_concepts, shape=(nl,)).copy(),
+            level_tests=np.ctypeslib.as_array(res.level_tests, shape=(nl,)).copy(),
+            digest=int(res.digest), threads=res.threads, seconds=res.seconds,
+        )
+    finally:
+        lib.oracle_digest_free(ctypes.byref(res))

@@ -1,11 +1,21 @@
 """Write the oracle's expected values for the full-size seeded workloads.
 
 Runs only the CPU oracle (oracle/) on the named workloads and stores, per
-workload, the concept count, closure tests, item pairs, per-level counts, the
-byte-model sums and a SHA-256 of the sorted intent array.  The GPU tests
-compare against these files; nothing here touches the GPU library.
+workload, the concept count, closure tests, item pairs, per-level counts and
+the byte-model sums, plus
 
-    python tests/golden/make_golden.py ctx50000x400
+* for workloads whose concepts fit in host memory: a SHA-256 of the sorted
+  intent array (oracle.cbo);
+* for larger ones: the order-independent intent digest of the store-free
+  search (oracle.cbo_digest, all host cores), and slices: for a few attribute
+  sets S, the sorted intents of the sub-context of the objects having all of
+  S, which are exactly the workload's intents containing S (count and
+  SHA-256).
+
+The GPU tests compare against these files; nothing here touches the GPU
+library.
+
+    python tests/golden/make_golden.py ctx50000x400 ctx20000x256
 """
 
 import hashlib
@@ -23,7 +33,52 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 
 
+# workloads checked through the store-free oracle, with their attribute slices
+DIGEST_SLICES = {
+    "ctx20000x256": [[149, 61], [139, 95], [3, 77], [10, 200, 255], [149]],
+}
+
+
+def sha_of(intents) -> str:
+    return hashlib.sha256(np.ascontiguousarray(intents, dtype="<u8").tobytes()).hexdigest()
+
+
+def golden_digest(name: str) -> dict:
+    cells = synth.make_config(name, packed=False)
+    rows = synth.pack_rows(cells)
+    n, m, _ = synth.CONFIGS[name]
+    t0 = time.time()
+    d = oracle.cbo_digest(rows, m, threads=os.cpu_count() or 1)
+    wall = time.time() - t0
+    slices = []
+    for attrs in DIGEST_SLICES[name]:
+        sub = cells[cells[:, attrs].all(axis=1)]
+        r = oracle.cbo(synth.pack_rows(sub), m, keep_extents=False)
+        slices.append({"attributes": attrs, "objects": int(sub.shape[0]), "n_concepts": int(r.n_concepts),
+                       "intents_sha256": sha_of(r.intents)})
+    return {
+        "workload": name,
+        "objects": n,
+        "attributes": m,
+        "generator_version": synth.GENERATOR_VERSION,
+        "rows_sha256": synth.rows_sha256(rows),
+        "n_concepts": int(d.n_concepts),
+        "closure_tests": int(d.tests),
+        "item_pairs": int(d.pairs),
+        "sum_c": int(d.sum_c),
+        "level_concepts": [int(x) for x in d.level_concepts],
+        "level_tests": [int(x) for x in d.level_tests],
+        "intent_digest": str(d.digest),
+        "slices": slices,
+        "oracle_threads": d.threads,
+        "oracle_seconds": d.seconds,
+        "oracle_wall_seconds": wall,
+    }
+
+
 def golden(name: str) -> dict:
+    if name in DIGEST_SLICES:
+        return golden_digest(name)
     rows = synth.make_config(name)
     n, m, _ = synth.CONFIGS[name]
     t0 = time.time()
@@ -42,7 +97,7 @@ def golden(name: str) -> dict:
         "sum_c": int(r.sum_c),
         "level_concepts": [int(x) for x in r.level_concepts],
         "level_tests": [int(x) for x in r.level_tests],
-        "intents_sha256": hashlib.sha256(np.ascontiguousarray(r.intents, dtype="<u8").tobytes()).hexdigest(),
+        "intents_sha256": sha_of(r.intents),
         "oracle_enum_seconds": r.seconds_enum,
         "oracle_sort_seconds": r.seconds_sort,
         "oracle_wall_seconds": wall,

@@ -292,3 +292,54 @@ def test_truncation_budget():
     cells = synth.make_config("ctx2000x64", packed=False)
     r = oracle.cbo(synth.pack_rows(cells), 64, keep_extents=False, max_tests=1000)
     assert r.truncated and r.tests == 1000
+
+
+# --- the store-free oracle and the intent digest -----------------------------------
+
+def test_splitmix_output_function_reference_values():
+    # SplitMix64 seeded with 0 (state advanced by the golden gamma before each
+    # output) starts with these three outputs in the reference implementation
+    from tests import intent_digest as dg
+
+    state, outs = 0, []
+    for _ in range(3):
+        outs.append(dg.mix_py(state))
+        state = (state + dg.GOLDEN) & dg.MASK
+    assert outs == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_digest_implementations_agree():
+    from tests import intent_digest as dg
+
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    a = rng.integers(0, 1 << 63, size=(257, 3), dtype=np.uint64) * np.uint64(2) + np.uint64(1)
+    want = dg.digest_py(a)
+    assert dg.digest_np(a, chunk=100) == want
+    assert dg.digest_torch(torch.from_numpy(a.view(np.int64)), chunk=64) == want
+
+
+@pytest.mark.parametrize("case", ["ctx64x16", "ctx2000x64", "multiword", "contranominal", "all_zero"])
+def test_store_free_oracle_matches_the_stored_search(case):
+    from tests import intent_digest as dg
+
+    if case in ("ctx64x16", "ctx2000x64"):
+        cells = synth.make_config(case, packed=False)
+    elif case == "multiword":
+        cells = synth.random_context(913, 300, 150, 0.05)
+    elif case == "contranominal":
+        cells = synth.pad_with_full(synth.contranominal(10), extra_objects=70, extra_attrs=60)
+    else:
+        cells = synth.all_zero(70, 65)
+    rows = synth.pack_rows(cells)
+    m = cells.shape[1]
+    r = oracle.cbo(rows, m, keep_extents=False)
+    for threads in (1, 3):
+        d = oracle.cbo_digest(rows, m, threads=threads)
+        assert d.n_concepts == r.n_concepts
+        assert (d.tests, d.pairs, d.sum_c) == (r.tests, r.pairs, r.sum_c)
+        assert list(d.level_concepts) == list(r.level_concepts)
+        assert list(d.level_tests) == list(r.level_tests)
+        assert d.digest == dg.digest_np(r.intents)
+    if r.n_concepts <= 5000:
+        assert d.digest == dg.digest_py(r.intents)
