@@ -191,6 +191,7 @@ struct fcbo_context {
     }
 
     uint64_t min_cap() const { return tiny ? 1 : 1024; }
+
     bool use_bitmaps() const { return wn <= kBmpMaxWords; }
     int nchunk() const { return (int)div_up((uint64_t)wn, kWave); }
 
@@ -226,7 +227,7 @@ struct fcbo_context {
         A.n = (int)n; A.m = (int)m; A.wn = wn; A.wm = wm; A.tail_m = tail_m; A.tail_n = tail_n;
         A.intents = intents; A.cursor = cursor; A.loff = loff; A.objs = objs;
         A.lo = lo; A.P = P; A.child_lo = lo + P; A.child_obj_lo = obj_hi;
-        A.pass = pass; A.nchild = nchild; A.nobj = nobj; A.cbase = cbase; A.obase = obase;
+        A.pass = pass; A.pass_cap = cap_pass / (uint64_t)wm; A.nchild = nchild; A.nobj = nobj; A.cbase = cbase; A.obase = obase;
         A.mid_idx = mid_idx;
         A.mid_max = wm <= 8 ? kMidMax : kSmallMax;
         A.mrec = mrec;
@@ -436,7 +437,7 @@ void fcbo_context::enumerate_levels()
         if (P >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
         // every level adds an attribute to the intent, so there are at most M + 1
         if (lev_concepts.size() > (size_t)m + 1) throw HipError{FCBO_ERR_DEVICE};
-        ensure(pass, cap_pass, P * (uint64_t)wm, 0, stream, mc);
+        ensure(pass, cap_pass, std::max<uint64_t>(1, next_huge) * wm, 0, stream, mc);
         ensure(nchild, cap_nch, P, 0, stream, mc);
         ensure(nobj, cap_nob, P, 0, stream, mc);
         ensure(cbase, cap_cb, P + 1, 0, stream, mc);
@@ -465,6 +466,7 @@ void fcbo_context::enumerate_levels()
             const unsigned found = (h_counters[CNT_MID] ? kLevelMid : 0u) | (h_counters[CNT_HUGE] ? kLevelHuge : 0u);
             if (found & ~classes) {  // parents of a class whose kernels did not run
                 classes |= found;
+                ensure(pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
                 redo = true;
                 ++redos;
                 continue;
@@ -477,6 +479,7 @@ void fcbo_context::enumerate_levels()
                     huge.ensure_tests(h_counters[CNT_THUGE], stream, mc);
                 }
                 ensure(mrec, cap_mrec, h_counters[CNT_MIDREC] * rstride, 0, stream, 1);
+                ensure(pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
                 ensure_local_records(h_counters[CNT_LOCREC]);
                 redo = true;
                 ++redos;

@@ -98,7 +98,8 @@ struct LevelArgs {
     uint64_t child_lo;     // index of the first child (= lo + P)
     uint64_t child_obj_lo; // offset in objs of the first child's list
     // per-level scratch, indexed by parent p in [0, P)
-    uint64_t *pass;        // P x wm, passing attributes of each parent
+    uint64_t *pass;        // per huge parent (member index), wm words: its passing attributes
+    uint64_t pass_cap;     // huge parents pass can hold
     uint32_t *nchild;      // children per parent
     uint32_t *nobj;        // objects in the children's extents per parent
     uint64_t *cbase;       // exclusive scan of nchild (P + 1)
@@ -726,7 +727,7 @@ __global__ void __launch_bounds__(kBlock) k_huge_tasks(LevelArgs A)
     const int wm = words_of<WMC>(A.wm);
     const uint64_t nset = A.counters[S.cnt_slot];
     const uint64_t tset = S.off[nset];
-    if (tset > S.cap || (S.bmp && nset * (uint64_t)A.wn > S.bmp_cap)) {
+    if (tset > S.cap || (S.bmp && nset * (uint64_t)A.wn > S.bmp_cap) || nset > A.pass_cap) {
         if (blockIdx.x == 0 && threadIdx.x == 0) A.counters[CNT_OVERFLOW] = 1;
         return;
     }
@@ -734,7 +735,7 @@ __global__ void __launch_bounds__(kBlock) k_huge_tasks(LevelArgs A)
          bi += (uint64_t)gridDim.x * kWavesPerBlock) {
         const uint64_t c0 = A.lo + S.idx[bi];
         const int y = A.cursor[c0];
-        if (lane < wm) A.pass[(uint64_t)S.idx[bi] * A.wm + lane] = 0;  // passing attributes, set by the tests
+        if (lane < wm) A.pass[bi * A.wm + lane] = 0;  // passing attributes, set by the tests
         uint64_t cand[WMC], bset[WMC];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
@@ -779,10 +780,10 @@ __global__ void __launch_bounds__(kBlock) k_huge_tasks(LevelArgs A)
 
 // Mark a passing test of set S: pass bit, sibling count, object count, and
 // append it to the set's pass list.
-__device__ __forceinline__ void big_record_pass(const LevelArgs &A, const BigSet &S, uint64_t t, uint64_t p, int j,
-                                                uint32_t cnt)
+__device__ __forceinline__ void big_record_pass(const LevelArgs &A, const BigSet &S, uint64_t t, uint64_t bi,
+                                                uint64_t p, int j, uint32_t cnt)
 {
-    atomicOr((unsigned long long *)&A.pass[p * A.wm + (j >> 6)], (unsigned long long)(1ull << (j & 63)));
+    atomicOr((unsigned long long *)&A.pass[bi * A.wm + (j >> 6)], (unsigned long long)(1ull << (j & 63)));
     atomicAdd(&A.nchild[p], 1u);
     atomicAdd(&A.nobj[p], cnt);
     const uint64_t pos = atomicAdd((unsigned long long *)&A.counters[S.pass_slot], 1ull);
@@ -793,16 +794,16 @@ __device__ __forceinline__ void big_record_pass(const LevelArgs &A, const BigSet
         atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_MID], 1ull);
 }
 
-// Rank of attribute j among the passing attributes of parent p.
+// Rank of attribute j among the passing attributes of huge parent bi.
 template <int WMC>
-__device__ __forceinline__ int pass_rank(const LevelArgs &A, uint64_t p, int j)
+__device__ __forceinline__ int pass_rank(const LevelArgs &A, uint64_t bi, int j)
 {
     const int wj = j >> 6, bj = j & 63;
     int rank = 0;
 #pragma unroll
     for (int u = 0; u < WMC; ++u) {
         if (u < words_of<WMC>(A.wm) && u <= wj) {
-            const uint64_t pm = A.pass[p * A.wm + u];
+            const uint64_t pm = A.pass[bi * A.wm + u];
             rank += __popcll(u < wj ? pm : (pm & below_mask(bj)));
         }
     }
@@ -1094,7 +1095,7 @@ __global__ void __launch_bounds__(kBlock) k_big_test_list(LevelArgs A)
         const bool pass = bad == 0;
         if (lane == 0) {
             S.size[t] = pass ? cnt : 0u;
-            if (pass) big_record_pass(A, S, t, p, j, cnt);
+            if (pass) big_record_pass(A, S, t, bi, p, j, cnt);
         }
     }
 }
@@ -1119,7 +1120,7 @@ __global__ void __launch_bounds__(kBlock) k_big_write_list(LevelArgs A)
         const int j = (int)(task & 0xFFFFu);
         const uint64_t p = S.idx[bi];
         const uint64_t c0 = A.lo + p;
-        const uint64_t child = A.child_lo + A.cbase[p] + (uint64_t)pass_rank<WMC>(A, p, j);
+        const uint64_t child = A.child_lo + A.cbase[p] + (uint64_t)pass_rank<WMC>(A, bi, j);
         const uint64_t obeg = A.child_obj_lo + A.obase[p] + (S.sscan[t] - S.sscan[S.off[bi]]);
         uint64_t D[WMC];
 #pragma unroll
@@ -1232,7 +1233,7 @@ __global__ void __launch_bounds__(kBlock) k_huge_finalize(LevelArgs A)
         const bool pass = bad == 0;
         S.size[t] = pass ? cnt : 0u;
         if (!pass) continue;
-        big_record_pass(A, S, t, p, j, cnt);
+        big_record_pass(A, S, t, bi, p, j, cnt);
         uint32_t run = 0;
         for (int k = 0; k < A.nchunk; ++k) {
             const uint32_t v = A.icnt[t * A.nchunk + k];
@@ -1272,7 +1273,7 @@ __global__ void __launch_bounds__(kBlock) k_huge_write(LevelArgs A)
             c &= c - 1ull;
         }
         if (k == 0 && lane == 0) {
-            const uint64_t child = A.child_lo + A.cbase[p] + (uint64_t)pass_rank<WMC>(A, p, j);
+            const uint64_t child = A.child_lo + A.cbase[p] + (uint64_t)pass_rank<WMC>(A, bi, j);
             for (int u = 0; u < A.wm; ++u) {
                 uint64_t d = A.dt[t * A.wm + u];
                 if (u == A.wm - 1) d &= A.tail_m;

@@ -18,6 +18,7 @@ import pytest
 import oracle
 import synth
 from tests.golden_io import read_fixture
+from tests.intent_digest import digest_torch
 
 torch = pytest.importorskip("torch")
 import closed_set_enumeration_amd as fca  # noqa: E402
@@ -312,3 +313,56 @@ def test_full_ctx50000x400_against_stored_oracle():
         _sample_extents_match(cells, ints, res.extents, 1500, 4)
     finally:
         ctx.close()
+
+
+def _assert_lectic_increasing(ints, chunk=1 << 26):
+    """Consecutive rows strictly increase in lexicographic order over the
+    attributes: at the first attribute where two rows differ, the later row
+    has it (checked on the device, chunk by chunk)."""
+    k, w = ints.shape
+    for s in range(0, k - 1, chunk):
+        a = ints[s:min(s + chunk, k - 1)]
+        b = ints[s + 1:min(s + chunk, k - 1) + 1]
+        x = a ^ b
+        nz = x != 0
+        assert bool(nz.any(dim=1).all()), "equal neighbouring intents"
+        first = nz.int().argmax(dim=1)  # first differing word
+        xw = x.gather(1, first[:, None]).squeeze(1)
+        bw = b.gather(1, first[:, None]).squeeze(1)
+        low = xw & (-xw)  # lowest differing bit of that word
+        assert bool(((bw & low) != 0).all()), "rows out of lexicographic order"
+
+
+def test_full_ctx20000x256_intents_against_store_free_oracle():
+    # 1.4e9 concepts: the extents (N/8 bytes each) do not fit, so intents only.
+    # Checked: counts, per-level numbers, the order-independent intent digest,
+    # the lexicographic order, and slices compared byte for byte.
+    path = os.path.join(GOLDEN, "ctx20000x256.json")
+    if not os.path.exists(path):
+        pytest.skip("stored oracle values not generated")
+    g = json.load(open(path))
+    rows = synth.make_config("ctx20000x256")
+    assert synth.rows_sha256(rows) == g["rows_sha256"]
+    ctx = fca.Context(rows, 256)
+    try:
+        res = ctx.enumerate(extents=False)
+        torch.cuda.synchronize()
+        conc, tests = ctx.level_counts()
+    finally:
+        ctx.close()
+    assert res.n_concepts == g["n_concepts"]
+    assert res.stats["closure_tests"] == g["closure_tests"]
+    assert res.stats["item_pairs"] == g["item_pairs"]
+    assert res.stats["sum_child_objects"] == g["sum_c"]
+    assert [int(x) for x in conc] == g["level_concepts"]
+    assert [int(x) for x in tests] == g["level_tests"]
+    ints = res.intents
+    assert digest_torch(ints) == int(g["intent_digest"])
+    _assert_lectic_increasing(ints)
+    for sl in g["slices"]:
+        keep = torch.ones(ints.shape[0], dtype=torch.bool, device=ints.device)
+        for a in sl["attributes"]:
+            keep &= ((ints[:, a >> 6] >> (a & 63)) & 1) != 0
+        sel = ints[keep].cpu().numpy().view(np.uint64)
+        assert sel.shape[0] == sl["n_concepts"], sl["attributes"]
+        assert hashlib.sha256(np.ascontiguousarray(sel, dtype="<u8").tobytes()).hexdigest() == sl["intents_sha256"]
