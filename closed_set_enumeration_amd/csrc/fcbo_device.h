@@ -412,7 +412,6 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     constexpr int CH = LocalCfg<WMC>::kChunk;
     __shared__ uint64_t s_rows[kW][kSmallMax * WMC];  // the group's object rows, slot-major
     __shared__ uint64_t s_b[kW][CH * WMC];            // the chunk's intents, padding bits past M set
-    __shared__ uint32_t s_cand[kW][kWave];            // this round's candidates: parent << 16 | j
     __shared__ uint32_t s_seg[kW][kWave];             // per group parent: first slot | objects << 8
     __shared__ uint32_t s_run[kW][2 * kWave];         // per group parent: children, their objects
     __shared__ uint8_t s_owner[kW][kWave];            // group parent whose slots start here
@@ -427,7 +426,6 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     uint64_t *R = s_rows[wv];
     const uint32_t *R32 = (const uint32_t *)R;
     uint64_t *SB = s_b[wv];
-    uint32_t *CAND = s_cand[wv];
     uint32_t *SEG = s_seg[wv];
     uint32_t *RUN = s_run[wv];
     uint8_t *OWN = s_owner[wv];
@@ -567,20 +565,24 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
                 }
             }
             const uint32_t cnt = (uint32_t)__popcll(x);
-            uint32_t pos = wave_excl_scan(cnt);
+            const uint32_t pos = wave_excl_scan(cnt);
             const uint32_t total = __shfl(pos + cnt, kWave - 1);
             for (uint32_t r0 = 0; r0 < total; r0 += kWave) {
-                while (x && pos < r0 + kWave) {
-                    const int bit = __ffsll((unsigned long long)x) - 1;
-                    x &= x - 1ull;
-                    CAND[pos - r0] = ((uint32_t)pq << 16) | (uint32_t)(64 * pu + bit);
-                    ++pos;
+                // this lane's candidate: number r0 + lane of the list, held by the
+                // (parent, word) lane whose prefix is the last one not above it
+                const uint32_t gidx = r0 + (uint32_t)lane;
+                const bool live = gidx < total;
+                int t = 0;
+#pragma unroll
+                for (int step = kWave / 2; step > 0; step >>= 1) {
+                    const uint32_t pv = __shfl(pos, (t + step) & (kWave - 1));
+                    if (t + step < kWave && pv <= gidx) t += step;
                 }
-                wave_sync();
-                const bool live = r0 + (uint32_t)lane < total;
-                const uint32_t cj = live ? CAND[lane] : 0xFFFF0000u;
-                const int qc = live ? (int)(cj >> 16) : 0;
-                const int j = (int)(cj & 0xFFFFu);
+                const uint64_t xt = __shfl(x, t);
+                const uint32_t rank = gidx - __shfl(pos, t);
+                const int tq = t / wm;
+                const int qc = live ? tq : 0;
+                const int j = live ? 64 * (t - tq * wm) + select64(xt, (int)rank) : 0;
                 const int wj = j >> 6, bj = j & 63;
                 const uint32_t sg = SEG[qc];
                 const int first = (int)(sg & 0xFFu), na = live ? (int)(sg >> 8) : 0;
