@@ -157,50 +157,104 @@ __device__ __forceinline__ int select64(uint64_t x, int k)
     return pos;
 }
 
+// --- wavefront collectives on the DPP network ------------------------------------
+//
+// Data-parallel-primitive moves shift values between lanes inside the VALU:
+// row_shr:n within each row of 16 lanes, row_bcast:15 / :31 from the last lane
+// of a row (or of rows 0-1) to the following rows, and whole-wave shifts by
+// one lane.  A 64-lane inclusive scan is six such steps (Hillis-Steele inside
+// the rows, then the two row broadcasts) with no trip through the LDS permute
+// unit; a reduction is the scan read back from lane 63.
+namespace dpp {
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+constexpr int kWaveShl1 = 0x130, kWaveShr1 = 0x138;
+}  // namespace dpp
+
+// v from the lane the DPP control selects; lanes without a source (or outside
+// the row mask) get `fill`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v, uint32_t fill)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_move64(uint64_t v, uint64_t fill)
+{
+    const uint32_t lo = dpp_move<CTRL, ROWS>((uint32_t)v, (uint32_t)fill);
+    const uint32_t hi = dpp_move<CTRL, ROWS>((uint32_t)(v >> 32), (uint32_t)(fill >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive scan with an associative op whose identity is `id`.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_incl_scan_op(T x, T id, Op op)
+{
+    if constexpr (sizeof(T) == 8) {
+        x = op(x, dpp_move64<dpp::kRowShr1, 0xF>(x, id));
+        x = op(x, dpp_move64<dpp::kRowShr2, 0xF>(x, id));
+        x = op(x, dpp_move64<dpp::kRowShr4, 0xF>(x, id));
+        x = op(x, dpp_move64<dpp::kRowShr8, 0xF>(x, id));
+        x = op(x, dpp_move64<dpp::kRowBcast15, 0xA>(x, id));
+        x = op(x, dpp_move64<dpp::kRowBcast31, 0xC>(x, id));
+    } else {
+        x = op(x, (T)dpp_move<dpp::kRowShr1, 0xF>(x, id));
+        x = op(x, (T)dpp_move<dpp::kRowShr2, 0xF>(x, id));
+        x = op(x, (T)dpp_move<dpp::kRowShr4, 0xF>(x, id));
+        x = op(x, (T)dpp_move<dpp::kRowShr8, 0xF>(x, id));
+        x = op(x, (T)dpp_move<dpp::kRowBcast15, 0xA>(x, id));
+        x = op(x, (T)dpp_move<dpp::kRowBcast31, 0xC>(x, id));
+    }
+    return x;
+}
+
+// Value of a wave-uniform lane, for every lane.
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int l)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+__device__ __forceinline__ uint64_t lane_value64(uint64_t v, int l)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ uint64_t wave_and(uint64_t v)
 {
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) v &= __shfl_xor(v, s);
-    return v;
+    return lane_value64(wave_incl_scan_op<uint64_t>(v, ~0ull, [](uint64_t x, uint64_t y) { return x & y; }),
+                        kWave - 1);
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
 {
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) v += __shfl_xor(v, s);
-    return v;
+    return lane_value(wave_incl_scan_op<uint32_t>(v, 0u, [](uint32_t x, uint32_t y) { return x + y; }), kWave - 1);
 }
 
 __device__ __forceinline__ uint64_t wave_sum64(uint64_t v)
 {
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) v += __shfl_xor(v, s);
-    return v;
+    return lane_value64(wave_incl_scan_op<uint64_t>(v, 0ull, [](uint64_t x, uint64_t y) { return x + y; }),
+                        kWave - 1);
+}
+
+__device__ __forceinline__ uint64_t wave_incl_scan64(uint64_t v)
+{
+    return wave_incl_scan_op<uint64_t>(v, 0ull, [](uint64_t x, uint64_t y) { return x + y; });
 }
 
 // Exclusive prefix sum over the lanes of a wavefront.
 __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v)
 {
-    const int lane = lane_id();
-    uint32_t x = v;
-#pragma unroll
-    for (int s = 1; s < kWave; s <<= 1) {
-        uint32_t t = __shfl_up(x, s);
-        if (lane >= s) x += t;
-    }
-    return x - v;
+    return wave_incl_scan_op<uint32_t>(v, 0u, [](uint32_t x, uint32_t y) { return x + y; }) - v;
 }
 
 // Exclusive prefix sum over a 256-thread block (u64); returns the block total.
 __device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t *s_wave, uint64_t &total)
 {
     const int lane = lane_id(), wv = threadIdx.x / kWave;
-    uint64_t x = v;
-#pragma unroll
-    for (int s = 1; s < kWave; s <<= 1) {
-        uint64_t t = __shfl_up(x, s);
-        if (lane >= s) x += t;
-    }
+    const uint64_t x = wave_incl_scan64(v);
     if (lane == kWave - 1) s_wave[wv] = x;
     __syncthreads();
     uint64_t before = 0, all = 0;
@@ -324,15 +378,14 @@ __device__ __forceinline__ void wave_append(bool flag, uint32_t value, uint32_t 
     const int leader = __ffsll((unsigned long long)bal) - 1;
     uint64_t base = 0;
     if (lane == leader) base = atomicAdd((unsigned long long *)counter, (unsigned long long)__popcll(bal));
-    base = __shfl(base, leader);
+    base = lane_value64(base, leader);
     if (flag) list[base + __popcll(bal & below_mask(lane))] = value;
 }
 
 __device__ __forceinline__ uint64_t wave_or(uint64_t v)
 {
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) v |= __shfl_xor(v, s);
-    return v;
+    return lane_value64(wave_incl_scan_op<uint64_t>(v, 0ull, [](uint64_t x, uint64_t y) { return x | y; }),
+                        kWave - 1);
 }
 
 // --- local parents (|A| <= 64): closure tests packed across parents -----------
@@ -391,7 +444,7 @@ __device__ __forceinline__ uint64_t wave_slot(uint64_t bal, uint64_t *counter)
     const int leader = __ffsll((unsigned long long)bal) - 1;
     uint64_t base = 0;
     if (lane_id() == leader) base = atomicAdd((unsigned long long *)counter, (unsigned long long)__popcll(bal));
-    base = __shfl(base, leader);
+    base = lane_value64(base, leader);
     return base + lanes_below(bal);
 }
 
@@ -518,10 +571,10 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
         const uint32_t pre = wave_excl_scan((uint32_t)a);
         for (int s = 0; s < nq;) {
             // the group: parents [s, e), their objects in slots [0, S)
-            const uint32_t base = __shfl(pre, s);
+            const uint32_t base = lane_value(pre, s);
             const bool in = lane >= s && lane < s + gmax && lane < nq && pre + (uint32_t)a - base <= (uint32_t)kSmallMax;
             const int e = s + __popcll(__ballot(in));
-            const int S = (int)(__shfl(pre, e - 1) + (uint32_t)__shfl(a, e - 1) - base);
+            const int S = (int)(lane_value(pre, e - 1) + lane_value((uint32_t)a, e - 1) - base);
             if (in) {
                 SEG[lane - s] = (pre - base) | ((uint32_t)a << 8);
                 if (a > 0) OWN[pre - base] = (uint8_t)(lane - s);
@@ -566,7 +619,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
             }
             const uint32_t cnt = (uint32_t)__popcll(x);
             const uint32_t pos = wave_excl_scan(cnt);
-            const uint32_t total = __shfl(pos + cnt, kWave - 1);
+            const uint32_t total = lane_value(pos + cnt, kWave - 1);
             for (uint32_t r0 = 0; r0 < total; r0 += kWave) {
                 // this lane's candidate: number r0 + lane of the list, held by the
                 // (parent, word) lane whose prefix is the last one not above it
@@ -623,8 +676,10 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
                 const bool pass = live && fu == wj && (__ffsll((unsigned long long)fx) - 1) == bj;
                 const uint64_t bal = __ballot(pass);
                 // segments of equal parent among the live lanes
-                const int prevq = __shfl(qc, lane > 0 ? lane - 1 : 0);
-                const int nextq = __shfl(qc, lane < kWave - 1 ? lane + 1 : lane);
+                // neighbours' parents (whole-wave shifts by one lane; the ends only
+                // matter through `lane == 0` and `lane == kWave - 1` below)
+                const int prevq = (int)dpp_move<dpp::kWaveShr1, 0xF>((uint32_t)qc, 0u);
+                const int nextq = (int)dpp_move<dpp::kWaveShl1, 0xF>((uint32_t)qc, 0u);
                 const bool head = live && (lane == 0 || prevq != qc);
                 const bool tail = live && (lane == kWave - 1 || r0 + (uint32_t)lane + 1 >= total || nextq != qc);
                 const uint64_t heads = __ballot(head);
@@ -1313,11 +1368,8 @@ __global__ void __launch_bounds__(kBlock) k_scan_up(const uint32_t *__restrict__
         sa += a[i];
         if (b) sb += b[i];
     }
-#pragma unroll
-    for (int k = 32; k > 0; k >>= 1) {
-        sa += __shfl_xor(sa, k);
-        sb += __shfl_xor(sb, k);
-    }
+    sa = wave_sum64(sa);
+    sb = wave_sum64(sb);
     if (lane_id() == 0) {
         s_red[0][threadIdx.x / kWave] = sa;
         s_red[1][threadIdx.x / kWave] = sb;
@@ -1343,15 +1395,7 @@ __global__ void __launch_bounds__(kScanBlocks) k_scan_mid(uint64_t *part, int nb
     __shared__ uint64_t s_w[2][kScanBlocks / kWave];
     const int t = threadIdx.x, lane = lane_id(), wv = t / kWave;
     uint64_t va = t < nblocks ? part[t] : 0, vb = t < nblocks ? part[kScanBlocks + t] : 0;
-    uint64_t xa = va, xb = vb;
-#pragma unroll
-    for (int s = 1; s < kWave; s <<= 1) {
-        uint64_t ya = __shfl_up(xa, s), yb = __shfl_up(xb, s);
-        if (lane >= s) {
-            xa += ya;
-            xb += yb;
-        }
-    }
+    const uint64_t xa = wave_incl_scan64(va), xb = wave_incl_scan64(vb);
     if (lane == kWave - 1) {
         s_w[0][wv] = xa;
         s_w[1][wv] = xb;
@@ -1419,12 +1463,7 @@ __global__ void __launch_bounds__(kScanBlocks) k_scan_small(const uint32_t *__re
     __shared__ uint64_t s_w[kScanBlocks / kWave];
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     auto block_scan = [&](uint64_t v, uint64_t &total) -> uint64_t {
-        uint64_t x = v;
-#pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) {
-            const uint64_t t = __shfl_up(x, s);
-            if (lane >= s) x += t;
-        }
+        const uint64_t x = wave_incl_scan64(v);
         if (lane == kWave - 1) s_w[wv] = x;
         __syncthreads();
         uint64_t before = 0, all = 0;
@@ -1636,7 +1675,7 @@ __global__ void __launch_bounds__(kOutThreads) k_output_block(const uint64_t *__
             continue;
         }
         for (int rr = wv; rr < nr; rr += kOutWaves) {
-            const uint64_t o = __shfl(lo, rr), e = __shfl(hi, rr);
+            const uint64_t o = lane_value64(lo, rr), e = lane_value64(hi, rr);
             uint64_t *T = s_rows + rr * wn;
             for (uint64_t p = o + lane; p < e; p += kWave) {
                 const uint32_t g = objs[p];
