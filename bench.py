@@ -10,6 +10,9 @@ Inputs (the context) are resident in HBM before timing starts.
 Prints one JSON line.  `value` is concepts per second; closure tests per
 second, per-kernel times (HIP events on the library's stream), the roofline of
 the dominant kernel and the CPU oracle timed on a bounded sample are added.
+`closure_column_equivalent` restates the closure kernels' speed in the terms of
+a column-streaming closure: the bandwidth such a kernel would need to make the
+same closure tests in the same time.
 """
 
 import argparse
@@ -75,6 +78,25 @@ def measured_traffic(cls, workload):
             if kv.get("class") == cls and kv.get("source_sha256") == sha:
                 return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
     return None
+
+
+def column_stream_equivalent(workload, closure_ms):
+    """Bandwidth a column-streaming closure kernel would need for the same closure
+    tests in the time the closure kernels here took: each test reads the non-zero
+    words of the parent extent (8 bytes each; the oracle's sum_nzw, stored by
+    tests/golden/make_golden.py) once."""
+    path = os.path.join(ROOT, "tests", "golden", "%s.json" % workload)
+    if not os.path.exists(path) or closure_ms <= 0:
+        return None
+    with open(path) as f:
+        g = json.load(f)
+    if "sum_nzw" not in g:
+        return None
+    gbytes = 8.0 * g["sum_nzw"] / 1e9
+    gbs = gbytes / (closure_ms * 1e-3)
+    return {"bytes_GB": round(gbytes, 2), "closure_ms": round(closure_ms, 4), "equivalent_GBps": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "kernels": ["test_local", "test_medium", "test_big"]}
 
 
 def cpu_baseline(rows, m, max_tests):
@@ -198,6 +220,8 @@ def main():
         "kernel_ms": {c: round(v, 4) for c, v in kernel_ms.items()},
         "kernel_launches": launches,
         "roofline": roof,
+        "closure_column_equivalent": column_stream_equivalent(
+            args.workload, sum(kernel_ms[c] for c in ("test_local", "test_medium", "test_big"))),
         "cpu_baseline": None,
     }
     ctx.close()
