@@ -298,9 +298,13 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigne
     hipEvent_t b = c->prof_begin();
     {
         constexpr int kW = LocalCfg<WMC>::kWaves;
-        const uint64_t chunks = div_up(P, (uint64_t)LocalCfg<WMC>::kChunk);
+        LevelArgs L = A;
+        L.chunk = LocalCfg<WMC>::kChunk;
+        const uint64_t want = (uint64_t)c->n_cu * kLocalChunksPerCu;
+        while (L.chunk / 2 >= kLocalMinChunk && div_up(P, (uint64_t)L.chunk) < want) L.chunk /= 2;
+        const uint64_t chunks = div_up(P, (uint64_t)L.chunk);
         const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(chunks, kW)));
-        hipLaunchKernelGGL(k_local_test<WMC>, dim3(g), dim3(LocalCfg<WMC>::kThreads), 0, c->stream, A);
+        hipLaunchKernelGGL(k_local_test<WMC>, dim3(g), dim3(LocalCfg<WMC>::kThreads), 0, c->stream, L);
     }
     CK_LAUNCH();
     c->prof_end(FCBO_K_TEST_LOCAL, b);

@@ -119,6 +119,7 @@ struct LevelArgs {
     uint64_t tail_n;       // valid bits of the last extent word
     uint64_t *counters;    // CNT_* of this level
     uint64_t *counters_next; // CNT_* of the next level, cleared by the local test kernel
+    int chunk;             // parents per chunk of the local test (at most LocalCfg::kChunk)
 };
 
 // ---------------------------------------------------------------------------
@@ -417,6 +418,13 @@ __device__ __forceinline__ uint64_t wave_or(uint64_t v)
 // needs no recomputation.  Child ranks and object offsets within a parent are
 // segmented scans over the lanes plus a per-parent carry between rounds.
 
+// A level with few parents gets smaller chunks, halved down to kLocalMinChunk
+// until there are kLocalChunksPerCu chunks per compute unit: with 64 parents
+// per chunk the shallow levels (tens of thousands of parents, each with
+// hundreds of candidates) would occupy a fraction of the wavefront slots.
+constexpr int kLocalChunksPerCu = 16;
+constexpr int kLocalMinChunk = 8;
+
 template <int WMC>
 struct LocalCfg {
     static constexpr int kWaves = WMC <= 8 ? kWavesPerBlock : 1;  // wavefronts per block
@@ -501,10 +509,11 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
         return at;
     };
     if (blockIdx.x == 0 && threadIdx.x < CNT_N) A.counters_next[threadIdx.x] = 0;
-    const uint64_t nchunks = (A.P + CH - 1) / CH;
+    const int chunk = (A.chunk >= 1 && A.chunk < CH) ? A.chunk : CH;
+    const uint64_t nchunks = (A.P + chunk - 1) / chunk;
     for (uint64_t ch = (uint64_t)blockIdx.x * kW + wv; ch < nchunks; ch += (uint64_t)gridDim.x * kW) {
-        const uint64_t p0 = ch * CH;
-        const int nq = (int)((A.P - p0) < (uint64_t)CH ? (A.P - p0) : (uint64_t)CH);
+        const uint64_t p0 = ch * chunk;
+        const int nq = (int)((A.P - p0) < (uint64_t)chunk ? (A.P - p0) : (uint64_t)chunk);
         // parent lanes: list start, size (0 unless local), cursor
         uint64_t o0 = 0, sz = 0;
         int a = 0, y = 0;
