@@ -325,6 +325,9 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigne
             const unsigned gmid = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(2048, div_up(P, kMidWaves)));
             hipLaunchKernelGGL(k_mid_test<WMC>, dim3(gmid), dim3(kWave * kMidWaves), 0, c->stream, A);
             CK_LAUNCH();
+            const unsigned gw = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(P, 4 * (uint64_t)c->n_cu));
+            hipLaunchKernelGGL(k_mid_test_wide<WMC>, dim3(gw), dim3(kWideThreads), 0, c->stream, A);
+            CK_LAUNCH();
             c->prof_end(FCBO_K_TEST_MEDIUM, b);
         }
     }
@@ -467,7 +470,8 @@ void fcbo_context::enumerate_levels()
             prof_end(FCBO_K_SCAN, b);
             CK(hipMemcpyAsync(h_counters, A.counters, CNT_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
             CK(hipStreamSynchronize(stream));
-            const unsigned found = (h_counters[CNT_MID] ? kLevelMid : 0u) | (h_counters[CNT_HUGE] ? kLevelHuge : 0u);
+            const uint64_t n_mid = h_counters[CNT_MID] + h_counters[CNT_MIDW];
+            const unsigned found = (n_mid ? kLevelMid : 0u) | (h_counters[CNT_HUGE] ? kLevelHuge : 0u);
             if (found & ~classes) {  // parents of a class whose kernels did not run
                 classes |= found;
                 ensure(pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
@@ -499,8 +503,8 @@ void fcbo_context::enumerate_levels()
             pairs += h_counters[CNT_PAIRS];
             sum_c += n_objs;
             big_parents += h_counters[CNT_HUGE];
-            med_parents += h_counters[CNT_MID];
-            local_parents += P - h_counters[CNT_HUGE] - h_counters[CNT_MID];
+            med_parents += n_mid;
+            local_parents += P - h_counters[CNT_HUGE] - n_mid;
             local_objs += h_counters[CNT_SMALL_OBJS];
             med_objs += h_counters[CNT_MID_OBJS];
             big_tests += h_counters[CNT_THUGE];

@@ -20,7 +20,9 @@
 //                    and huge lists; a <= 64: parents packed into wavefronts,
 //                    one lane per candidate, rows staged in LDS; child records
 //   k_mid_test       64 < a <= 4096 (intents up to 8 words): closure tests by
-//                    incidence, one D per carried attribute in LDS; records
+//                    incidence, one D per carried attribute in LDS; records;
+//                    a wavefront per parent up to 512 objects, a workgroup
+//                    per parent above (k_mid_test_wide)
 //   k_huge_*         larger parents: one item per (test, 64-word chunk of the
 //                    extent bitmap), or per test over the object list
 //   scans            child and object offsets per parent (exact sizes)
@@ -44,6 +46,9 @@ constexpr int kOutTileWords = 1024; // extent words staged in LDS per output til
 constexpr int kBmpMaxWords = 16384; // big parents use extent bitmaps when N <= 64 * this
 constexpr int kMidMax = 4096;       // parents with more objects are huge (tested a chunk at a time)
 constexpr int kMidWaves = 2;        // wavefronts per block of the incidence kernel
+constexpr int kMidWide = 512;       // mid parents with more objects get a whole workgroup each
+constexpr int kWideThreads = 512;   // threads of that workgroup (at least 64 x 8 candidates)
+constexpr int kWideWaves = kWideThreads / kWave;
 
 // Device counters shared by the kernels of one level.
 enum {
@@ -63,7 +68,8 @@ enum {
     CNT_LOCREC = 13,   // record slots reserved by the local parents (64 per chunk)
     CNT_NEXT_MID = 14, // children that will be mid parents (64 < |C| <= mid_max)
     CNT_NEXT_HUGE = 15, // children that will be huge parents (|C| > mid_max)
-    CNT_N = 16
+    CNT_MIDW = 16,     // number of wide mid parents (kept at the back of mid_idx)
+    CNT_N = 17
 };
 
 // Huge parents, tested one closure test at a time: one work item per (test,
@@ -560,7 +566,15 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
                     S.n[hpos] = nt;
                 }
             }
-            wave_append(is_mid, (uint32_t)(p0 + lane), A.mid_idx, &A.counters[CNT_MID]);
+            // mid parents: the narrow ones from the front of mid_idx, the wide
+            // ones (more than kMidWide objects) from the back
+            const bool is_wide = is_mid && sz > (uint64_t)kMidWide;
+            wave_append(is_mid && !is_wide, (uint32_t)(p0 + lane), A.mid_idx, &A.counters[CNT_MID]);
+            const uint64_t wb = __ballot(is_wide);
+            if (wb) {
+                const uint64_t wpos = wave_slot(wb, &A.counters[CNT_MIDW]);
+                if (is_wide) A.mid_idx[A.P - 1 - wpos] = (uint32_t)(p0 + lane);
+            }
             if (is_mid || is_huge) {
                 A.nchild[p0 + lane] = 0;
                 A.nobj[p0 + lane] = 0;
@@ -1077,6 +1091,181 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
             }
         }
         wave_sync();
+    }
+    if (next_mid && lane == 0) atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_MID], (unsigned long long)next_mid);
+}
+
+// Wide mid parents (more than kMidWide objects): the same incidence method with
+// one workgroup per parent.  Its wavefronts split the object list and share one
+// D table (LDS atomics are atomic across the workgroup), so the longest parent
+// no longer sets the length of the launch; every candidate of U then gets a
+// thread of its own for the canonical test, and ranks and object offsets come
+// from a workgroup scan.  Records as in k_mid_test, one block per parent.
+template <int WMC>
+__global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
+{
+    constexpr int kMaxCand = kWave * WMC;
+    static_assert(kMaxCand <= kWideThreads, "one thread per candidate");
+    __shared__ uint64_t s_d[kMaxCand * WMC];
+    __shared__ uint32_t s_c[kMaxCand];
+    __shared__ uint64_t s_u[WMC];
+    __shared__ uint32_t s_wsum[2][kWideWaves];  // per wavefront: passing tests, their objects
+    __shared__ uint64_t s_base;
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int tid = (int)threadIdx.x;
+    const int wm = words_of<WMC>(A.wm);
+    uint32_t next_mid = 0;
+    const uint64_t count = A.counters[CNT_MIDW];
+    const uint64_t rstride = 4 + (uint64_t)A.wm;
+    for (uint64_t it = blockIdx.x; it < count; it += gridDim.x) {
+        const uint64_t p = A.mid_idx[A.P - 1 - it];
+        const uint64_t c0 = A.lo + p;
+        const uint64_t o0 = A.loff[c0], o1 = A.loff[c0 + 1];
+        const int y = A.cursor[c0];
+        uint64_t Bx[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            Bx[u] = ~0ull;
+            if (u < wm) {
+                Bx[u] = A.intents[c0 * A.wm + u];
+                if (u == wm - 1) Bx[u] |= ~A.tail_m;
+            }
+        }
+        if (tid < WMC) s_u[tid] = 0;
+        __syncthreads();
+        // U: candidates carried by some object of A
+        uint64_t U[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) U[u] = 0;
+        for (uint64_t o = o0 + tid; o < o1; o += kWideThreads) {
+            const uint64_t g = A.objs[o];
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                if (u < wm) U[u] |= A.rows[g * A.wm + u];
+        }
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            if (u < wm) {
+                const uint64_t v = wave_or(U[u]);
+                if (lane == 0 && v) atomicOr((unsigned long long *)&s_u[u], (unsigned long long)v);
+            }
+        }
+        __syncthreads();
+        int nU = 0, j0 = -1;
+        int pre[WMC];  // members of U in the words before u
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            pre[u] = nU;
+            U[u] = 0;
+            if (u < wm) {
+                const uint64_t nb = ~Bx[u];
+                if (j0 < 0 && nb) j0 = 64 * u + __ffsll((unsigned long long)nb) - 1;
+                U[u] = s_u[u] & nb & above_mask(y, u);
+                nU += __popcll(U[u]);
+            }
+        }
+        for (int x = tid; x < nU * WMC; x += kWideThreads) s_d[x] = ~0ull;
+        for (int x = tid; x < nU; x += kWideThreads) s_c[x] = 0;
+        __syncthreads();
+        // incidences
+        for (uint64_t o = o0 + tid; o < o1; o += kWideThreads) {
+            const uint64_t g = A.objs[o];
+            uint64_t row[WMC];
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) row[u] = (u < wm) ? A.rows[g * A.wm + u] : 0ull;
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) {
+                uint64_t x = row[u] & U[u];
+                while (x) {
+                    const int b = __ffsll((unsigned long long)x) - 1;
+                    x &= x - 1ull;
+                    const int r = pre[u] + __popcll(U[u] & below_mask(b));
+#pragma unroll
+                    for (int v = 0; v < WMC; ++v)
+                        if (v < wm) atomicAnd((unsigned long long *)&s_d[r * WMC + v], (unsigned long long)row[v]);
+                    atomicAdd(&s_c[r], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        // the first attribute outside B, carried by no object: C = {}, D = M, rank 0
+        bool bottom = false;
+        if (j0 > y) {
+            bottom = true;
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                if (u == (j0 >> 6) && ((U[u] >> (j0 & 63)) & 1ull)) bottom = false;
+        }
+        // canonical tests: thread r takes member r of U (ascending j)
+        const int r = tid;
+        const bool active = r < nU;
+        const int j = active ? select_words<WMC>(U, wm, r) : 0;
+        const int wj = j >> 6, bj = j & 63;
+        uint64_t bad = 0;
+        if (active) {
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) {
+                if (u < wm && u <= wj) {
+                    const uint64_t extra = s_d[r * WMC + u] & ~Bx[u];
+                    bad |= (u < wj) ? extra : (extra & below_mask(bj));
+                }
+            }
+        }
+        const bool pass = active && bad == 0;
+        const uint32_t cnt = pass ? s_c[r] : 0u;
+        const uint64_t bal = __ballot(pass);
+        next_mid += (uint32_t)__popcll(__ballot(pass && cnt > (uint32_t)kSmallMax));
+        const uint32_t before = (uint32_t)__popcll(bal & below_mask(lane));
+        const uint32_t ex = wave_excl_scan(cnt);
+        const uint32_t wobj = wave_sum(cnt);
+        if (lane == 0) {
+            s_wsum[0][wv] = (uint32_t)__popcll(bal);
+            s_wsum[1][wv] = wobj;
+        }
+        __syncthreads();
+        uint32_t pbase = bottom ? 1u : 0u, obase = 0, npass = pbase, nobj = 0;
+        for (int w = 0; w < kWideWaves; ++w) {
+            const uint32_t a = s_wsum[0][w], o = s_wsum[1][w];
+            if (w < wv) {
+                pbase += a;
+                obase += o;
+            }
+            npass += a;
+            nobj += o;
+        }
+        if (tid == 0) {
+            uint64_t base = 0;
+            if (npass) base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC], (unsigned long long)npass);
+            if (base + npass > A.mrec_cap) A.counters[CNT_OVERFLOW] = 1;
+            s_base = base;
+            A.nchild[p] = npass;
+            A.nobj[p] = nobj;
+        }
+        __syncthreads();
+        const uint64_t base = s_base;
+        if (base + npass <= A.mrec_cap) {
+            if (bottom && tid == 0) {
+                uint64_t *rec = A.mrec + base * rstride;
+                rec[0] = p | ((uint64_t)j0 << 32);
+                rec[1] = 0;
+                rec[2] = 0;
+                rec[3] = 0;
+                for (int u = 0; u < wm; ++u) rec[4 + u] = (u == wm - 1) ? A.tail_m : ~0ull;
+            }
+            if (pass) {
+                const uint32_t rank = pbase + before;
+                uint64_t *rec = A.mrec + (base + rank) * rstride;
+                rec[0] = p | ((uint64_t)j << 32);
+                rec[1] = (uint64_t)rank | ((uint64_t)cnt << 32);
+                rec[2] = obase + ex;
+                rec[3] = 0;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm) rec[4 + u] = (u == wm - 1) ? (s_d[r * WMC + u] & A.tail_m) : s_d[r * WMC + u];
+            }
+        }
+        __syncthreads();  // the table, s_u and s_base are reused by the next parent
     }
     if (next_mid && lane == 0) atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_MID], (unsigned long long)next_mid);
 }
