@@ -231,10 +231,10 @@ struct fcbo_context {
         A.mid_idx = mid_idx;
         A.mid_max = wm <= 8 ? kMidMax : kSmallMax;
         A.mrec = mrec;
-        A.mrec_cap = cap_mrec / (4 + (uint64_t)wm);
+        A.mrec_region = cap_mrec / (4 + (uint64_t)wm) / kRecStripes;
         A.lrec = lrec;
         A.lfill = lfill;
-        A.lrec_cap = std::min(cap_lrec / (4 + (uint64_t)wm), cap_lfill * kWave);
+        A.lrec_region = std::min(cap_lrec / (4 + (uint64_t)wm), cap_lfill * kWave) / kRecStripes / kWave * kWave;
         const bool bm = use_bitmaps();
         A.huge = huge.view(CNT_HUGE, CNT_THUGE, CNT_HUGEPASS, bm);
         if (bm) A.huge.cap = std::min(A.huge.cap, std::min(std::min(cap_dt / wm, cap_tcnt), cap_icnt / nchunk()));
@@ -486,9 +486,16 @@ void fcbo_context::enumerate_levels()
                 } else {
                     huge.ensure_tests(h_counters[CNT_THUGE], stream, mc);
                 }
-                ensure(mrec, cap_mrec, h_counters[CNT_MIDREC] * rstride, 0, stream, 1);
+                uint64_t stripe_max = 0;
+                for (int t = 0; t < kRecStripes; ++t)
+                    stripe_max = std::max<uint64_t>(stripe_max, h_counters[CNT_MIDREC + t * kCntPad]);
+                // headroom: the split of records over stripes varies from run to run
+                ensure(mrec, cap_mrec, stripe_max * kRecStripes * rstride / 4 * 5, 0, stream, 1);
                 ensure(pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
-                ensure_local_records(h_counters[CNT_LOCREC]);
+                uint64_t lstripe_max = 0;
+                for (int t = 0; t < kRecStripes; ++t)
+                    lstripe_max = std::max<uint64_t>(lstripe_max, h_counters[CNT_LOCREC + t * kCntPad]);
+                ensure_local_records(lstripe_max * kRecStripes / 4 * 5);
                 redo = true;
                 ++redos;
                 continue;

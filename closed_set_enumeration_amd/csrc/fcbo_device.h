@@ -50,26 +50,34 @@ constexpr int kMidWide = 512;       // mid parents with more objects get a whole
 constexpr int kWideThreads = 512;   // threads of that workgroup (at least 64 x 8 candidates)
 constexpr int kWideWaves = kWideThreads / kWave;
 
-// Device counters shared by the kernels of one level.
+// Device counters shared by the kernels of one level, each in a 128-byte line
+// of its own: atomics on one 64-byte segment are serialised by the memory
+// system (about 12 ns each on MI355X), so counters that share a segment slow
+// each other down.  The values below are word offsets.
+constexpr int kCntPad = 16;
+// Child records (of the mid parents, and of the local parents) are reserved
+// through this many counters, each owning an equal region of its record buffer
+// (a wavefront or workgroup picks one by its index).
+constexpr int kRecStripes = 32;
 enum {
-    CNT_HUGE = 0,      // number of huge parents
-    CNT_TESTS = 1,     // closure tests of this level
-    CNT_PAIRS = 2,     // (parent, j > cursor) pairs of this level
-    CNT_OVERFLOW = 3,  // a per-test or record buffer was too small: the level is redone
-    CNT_CHILDREN = 4,  // children of this level
-    CNT_OBJS = 5,      // objects in the children's extents
-    CNT_THUGE = 6,     // closure tests of the huge parents
-    CNT_SMALL_OBJS = 7, // objects in the extents of local parents
-    CNT_BIG_SCAN = 8,  // sum over huge parents of tests x objects
-    CNT_MID = 9,       // number of mid parents
-    CNT_HUGEPASS = 10, // passing huge tests
-    CNT_MID_OBJS = 11, // objects in the extents of mid parents
-    CNT_MIDREC = 12,   // child records written by the mid parents
-    CNT_LOCREC = 13,   // record slots reserved by the local parents (64 per chunk)
-    CNT_NEXT_MID = 14, // children that will be mid parents (64 < |C| <= mid_max)
-    CNT_NEXT_HUGE = 15, // children that will be huge parents (|C| > mid_max)
-    CNT_MIDW = 16,     // number of wide mid parents (kept at the back of mid_idx)
-    CNT_N = 17
+    CNT_HUGE = 0 * kCntPad,      // number of huge parents
+    CNT_TESTS = 1 * kCntPad,     // closure tests of this level
+    CNT_PAIRS = 2 * kCntPad,     // (parent, j > cursor) pairs of this level
+    CNT_OVERFLOW = 3 * kCntPad,  // a per-test or record buffer was too small: the level is redone
+    CNT_CHILDREN = 4 * kCntPad,  // children of this level
+    CNT_OBJS = 5 * kCntPad,      // objects in the children's extents
+    CNT_THUGE = 6 * kCntPad,     // closure tests of the huge parents
+    CNT_SMALL_OBJS = 7 * kCntPad, // objects in the extents of local parents
+    CNT_BIG_SCAN = 8 * kCntPad,  // sum over huge parents of tests x objects
+    CNT_MID = 9 * kCntPad,       // number of mid parents
+    CNT_HUGEPASS = 10 * kCntPad, // passing huge tests
+    CNT_MID_OBJS = 11 * kCntPad, // objects in the extents of mid parents
+    CNT_MIDW = 12 * kCntPad,     // number of wide mid parents (kept at the back of mid_idx)
+    CNT_NEXT_MID = 13 * kCntPad, // children that will be mid parents (64 < |C| <= mid_max)
+    CNT_NEXT_HUGE = 14 * kCntPad, // children that will be huge parents (|C| > mid_max)
+    CNT_MIDREC = 15 * kCntPad,   // kRecStripes counters, one line each: mid record slots per stripe
+    CNT_LOCREC = (15 + kRecStripes) * kCntPad,  // kRecStripes counters: local record slots per stripe
+    CNT_N = (15 + 2 * kRecStripes) * kCntPad  // words of one level's counters
 };
 
 // Huge parents, tested one closure test at a time: one work item per (test,
@@ -113,10 +121,10 @@ struct LevelArgs {
     uint32_t *mid_idx;     // mid parents (order not fixed)
     int mid_max;           // parents with more objects are huge
     uint64_t *mrec;        // child records of the mid parents (see k_mid_test)
-    uint64_t mrec_cap;     // records
+    uint64_t mrec_region;  // records per stripe: stripe s owns [s * mrec_region, (s + 1) * mrec_region)
     uint64_t *lrec;        // child records of the local parents, in chunks of 64 slots
     uint32_t *lfill;       // records used in each chunk of lrec
-    uint64_t lrec_cap;     // slots (a multiple of 64)
+    uint64_t lrec_region;  // slots per stripe (a multiple of 64), laid out like mrec
     BigSet huge;           // huge parents
     uint64_t *dt;          // per huge test: AND of the rows of C, wm words
     uint32_t *tcnt;        // per huge test: |C|
@@ -499,22 +507,27 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     const uint64_t rstride = 4 + (uint64_t)A.wm;
     // Record slots are reserved 64 at a time per wavefront; a round's passing
     // children go to one chunk of slots (a chunk that cannot hold them is closed).
+    // The wavefront's stripe owns slots [rlo, rhi).
+    const int stripe = (int)(((uint64_t)blockIdx.x * kW + wv) % kRecStripes);
+    const uint64_t rlo = (uint64_t)stripe * A.lrec_region, rhi = rlo + A.lrec_region;
     uint64_t rchunk = ~0ull;  // first slot of the current record chunk
     uint32_t fill = kWave;    // slots used in it
     auto reserve = [&](uint32_t n) -> uint64_t {
         if (fill + n > (uint32_t)kWave) {
-            if (rchunk != ~0ull && lane == 0 && rchunk < A.lrec_cap) A.lfill[rchunk / kWave] = fill;
+            if (rchunk != ~0ull && lane == 0 && rchunk < rhi) A.lfill[rchunk / kWave] = fill;
             uint64_t c = 0;
-            if (lane == 0) c = atomicAdd((unsigned long long *)&A.counters[CNT_LOCREC], (unsigned long long)kWave);
-            rchunk = uniform64(c);
+            if (lane == 0)
+                c = atomicAdd((unsigned long long *)&A.counters[CNT_LOCREC + stripe * kCntPad], (unsigned long long)kWave);
+            rchunk = rlo + uniform64(c);
             fill = 0;
-            if (rchunk + kWave > A.lrec_cap && lane == 0) A.counters[CNT_OVERFLOW] = 1;
+            if (rchunk + kWave > rhi && lane == 0) A.counters[CNT_OVERFLOW] = 1;
         }
         const uint64_t at = rchunk + fill;
         fill += n;
         return at;
     };
-    if (blockIdx.x == 0 && threadIdx.x < CNT_N) A.counters_next[threadIdx.x] = 0;
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < CNT_N; i += blockDim.x) A.counters_next[i] = 0;
     const int chunk = (A.chunk >= 1 && A.chunk < CH) ? A.chunk : CH;
     const uint64_t nchunks = (A.P + chunk - 1) / chunk;
     for (uint64_t ch = (uint64_t)blockIdx.x * kW + wv; ch < nchunks; ch += (uint64_t)gridDim.x * kW) {
@@ -716,7 +729,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
                     const uint64_t at = reserve((uint32_t)__popcll(bal));
                     if (pass) {
                         const uint64_t slot = at + lanes_below(bal);
-                        if (slot < A.lrec_cap) {
+                        if (slot < rhi) {
                             const uint32_t rank = RUN[2 * qc] + (uint32_t)__popcll(bal & inseg & ~(1ull << lane));
                             const uint32_t objoff = RUN[2 * qc + 1] + (ex - exh);
                             uint64_t *rec = A.lrec + slot * rstride;
@@ -745,7 +758,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
             s = e;
         }
     }
-    if (rchunk != ~0ull && lane == 0 && rchunk < A.lrec_cap) A.lfill[rchunk / kWave] = fill;
+    if (rchunk != ~0ull && lane == 0 && rchunk < rhi) A.lfill[rchunk / kWave] = fill;
     // level counters: wavefront sums, then one atomic per workgroup and counter
     uint64_t v[5] = {n_tests, n_pairs, n_local_objs, n_mid_objs, n_big_scan};
 #pragma unroll
@@ -768,26 +781,45 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
 __global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
 {
     if (A.counters[CNT_OVERFLOW]) return;
-    const uint64_t nrec = A.counters[CNT_LOCREC];
     const uint64_t rstride = 4 + (uint64_t)A.wm;
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nrec; i += (uint64_t)gridDim.x * blockDim.x) {
-        if ((uint32_t)(i % kWave) >= A.lfill[i / kWave]) continue;  // unused slot of a closed chunk
-        const uint64_t *rec = A.lrec + i * rstride;
-        const uint64_t w0 = rec[0], w1 = rec[1];
-        const uint64_t p = w0 & 0xFFFFFFFFull;
-        const uint32_t cnt = (uint32_t)(w1 >> 32);
-        const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
-        const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
-        for (int u = 0; u < A.wm; ++u) A.intents[child * A.wm + u] = rec[4 + u];
-        A.cursor[child] = (int32_t)(w0 >> 32);
-        A.loff[child] = obeg;
-        A.loff[child + 1] = obeg + cnt;
-        const uint32_t *src = A.objs + A.loff[A.lo + p];
-        uint64_t c = rec[3];
-        uint64_t q = obeg;
-        while (c) {
-            A.objs[q++] = src[__ffsll((unsigned long long)c) - 1];
-            c &= c - 1ull;
+    // Slots of stripe st: [st * region, st * region + count_st), in chunks of
+    // 64.  The chunks are walked interleaved, chunk c of every stripe before
+    // chunk c + 1 of any (their reservation order, roughly): flat slot f lies in
+    // chunk f / 64 / kRecStripes of stripe (f / 64) % kRecStripes.
+    const uint64_t nt = (uint64_t)gridDim.x * blockDim.x;
+    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = lane_id();
+    // the stripe counts, one per lane, loaded together
+    const uint64_t counts = lane < kRecStripes ? A.counters[CNT_LOCREC + lane * kCntPad] : 0ull;
+    uint64_t smax = 0;
+    for (int st = 0; st < kRecStripes; ++st) smax = max(smax, lane_value64(counts, st));
+    for (uint64_t f = t; f < smax * kRecStripes; f += nt) {
+        {
+            // a wavefront's 64 threads share the chunk (t starts at a multiple
+            // of 64 and the thread count is one), so st is uniform
+            const uint64_t ch = f / kWave;
+            const int st = __builtin_amdgcn_readfirstlane((int)(ch % kRecStripes));
+            const uint64_t k = (ch / kRecStripes) * kWave + f % kWave;  // slot within the stripe
+            if (k >= lane_value64(counts, st)) continue;
+            const uint64_t i = (uint64_t)st * A.lrec_region + k;
+            if ((uint32_t)(i % kWave) >= A.lfill[i / kWave]) continue;  // unused slot of a closed chunk
+            const uint64_t *rec = A.lrec + i * rstride;
+            const uint64_t w0 = rec[0], w1 = rec[1];
+            const uint64_t p = w0 & 0xFFFFFFFFull;
+            const uint32_t cnt = (uint32_t)(w1 >> 32);
+            const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
+            const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
+            for (int u = 0; u < A.wm; ++u) A.intents[child * A.wm + u] = rec[4 + u];
+            A.cursor[child] = (int32_t)(w0 >> 32);
+            A.loff[child] = obeg;
+            A.loff[child + 1] = obeg + cnt;
+            const uint32_t *src = A.objs + A.loff[A.lo + p];
+            uint64_t c = rec[3];
+            uint64_t q = obeg;
+            while (c) {
+                A.objs[q++] = src[__ffsll((unsigned long long)c) - 1];
+                c &= c - 1ull;
+            }
         }
     }
 }
@@ -1044,10 +1076,13 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
         wave_sync();
         // child records: one contiguous block per parent, in rank (ascending j)
         // order, reserved with a single atomic
+        const int stripe = (int)(((uint64_t)blockIdx.x * kMidWaves + wv) % kRecStripes);
         uint64_t base = 0;
-        if (lane == 0 && n_pass) base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC], (unsigned long long)n_pass);
+        if (lane == 0 && n_pass)
+            base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC + stripe * kCntPad], (unsigned long long)n_pass);
         base = uniform64(base);
-        const bool fits = base + n_pass <= A.mrec_cap;
+        const bool fits = base + n_pass <= A.mrec_region;
+        base += (uint64_t)stripe * A.mrec_region;  // first record slot of this parent
         if (!fits && lane == 0) A.counters[CNT_OVERFLOW] = 1;
         if (lane == 0) {
             A.nchild[p] = n_pass;
@@ -1235,16 +1270,23 @@ __global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
             nobj += o;
         }
         if (tid == 0) {
+            const int stripe = (int)(blockIdx.x % kRecStripes);
             uint64_t base = 0;
-            if (npass) base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC], (unsigned long long)npass);
-            if (base + npass > A.mrec_cap) A.counters[CNT_OVERFLOW] = 1;
+            if (npass)
+                base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC + stripe * kCntPad], (unsigned long long)npass);
+            if (base + npass > A.mrec_region) {
+                A.counters[CNT_OVERFLOW] = 1;
+                base = ~0ull;  // nothing is written
+            } else {
+                base += (uint64_t)stripe * A.mrec_region;
+            }
             s_base = base;
             A.nchild[p] = npass;
             A.nobj[p] = nobj;
         }
         __syncthreads();
         const uint64_t base = s_base;
-        if (base + npass <= A.mrec_cap) {
+        if (base != ~0ull) {
             if (bottom && tid == 0) {
                 uint64_t *rec = A.mrec + base * rstride;
                 rec[0] = p | ((uint64_t)j0 << 32);
@@ -1278,30 +1320,43 @@ __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
 {
     const int lane = lane_id();
     if (A.counters[CNT_OVERFLOW]) return;
-    const uint64_t nrec = A.counters[CNT_MIDREC];
+    // Records of stripe st sit in slots [st * region, st * region + count_st).
+    // They are walked interleaved, record k of every stripe before record k + 1
+    // of any (the order in which they were reserved, roughly): flat index f is
+    // record f / kRecStripes of stripe f % kRecStripes.
     const uint64_t rstride = 4 + (uint64_t)A.wm;
-    for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; i < nrec;
-         i += (uint64_t)gridDim.x * kWavesPerBlock) {
-        const uint64_t *rec = A.mrec + i * rstride;
-        const uint64_t w0 = rec[0], w1 = rec[1];
-        const uint64_t p = w0 & 0xFFFFFFFFull;
-        const int j = (int)(w0 >> 32);
-        const uint32_t cnt = (uint32_t)(w1 >> 32);
-        const uint64_t c0 = A.lo + p;
-        const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
-        const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
-        for (int u = lane; u < A.wm; u += kWave) A.intents[child * A.wm + u] = rec[4 + u];
-        if (lane == 0) {
-            A.cursor[child] = j;
-            A.loff[child] = obeg;
-            A.loff[child + 1] = obeg + cnt;
+    const uint64_t nw = (uint64_t)gridDim.x * kWavesPerBlock;
+    const uint64_t w = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    // the stripe counts, one per lane, loaded together
+    const uint64_t counts = lane < kRecStripes ? A.counters[CNT_MIDREC + lane * kCntPad] : 0ull;
+    uint64_t kmax = 0;
+    for (int st = 0; st < kRecStripes; ++st) kmax = max(kmax, lane_value64(counts, st));
+    for (uint64_t f = w; f < kmax * kRecStripes; f += nw) {
+        {
+            const int st = __builtin_amdgcn_readfirstlane((int)(f % kRecStripes));  // f is per wavefront
+            const uint64_t k = f / kRecStripes;
+            if (k >= lane_value64(counts, st)) continue;
+            const uint64_t *rec = A.mrec + ((uint64_t)st * A.mrec_region + k) * rstride;
+            const uint64_t w0 = rec[0], w1 = rec[1];
+            const uint64_t p = w0 & 0xFFFFFFFFull;
+            const int j = (int)(w0 >> 32);
+            const uint32_t cnt = (uint32_t)(w1 >> 32);
+            const uint64_t c0 = A.lo + p;
+            const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
+            const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
+            for (int u = lane; u < A.wm; u += kWave) A.intents[child * A.wm + u] = rec[4 + u];
+            if (lane == 0) {
+                A.cursor[child] = j;
+                A.loff[child] = obeg;
+                A.loff[child + 1] = obeg + cnt;
+            }
+            if (cnt == 0) continue;
+            uint64_t qo = obeg;
+            scan_list_for_attr(A, A.loff[c0], A.loff[c0 + 1], j, [&](bool in, uint32_t g, uint64_t bal) {
+                if (in) A.objs[qo + __popcll(bal & below_mask(lane))] = g;
+                qo += __popcll(bal);
+            });
         }
-        if (cnt == 0) continue;
-        uint64_t qo = obeg;
-        scan_list_for_attr(A, A.loff[c0], A.loff[c0 + 1], j, [&](bool in, uint32_t g, uint64_t bal) {
-            if (in) A.objs[qo + __popcll(bal & below_mask(lane))] = g;
-            qo += __popcll(bal);
-        });
     }
 }
 
