@@ -490,6 +490,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     __shared__ uint32_t s_seg[kW][kWave];             // per group parent: first slot | objects << 8
     __shared__ uint32_t s_run[kW][2 * kWave];         // per group parent: children, their objects
     __shared__ uint8_t s_owner[kW][kWave];            // group parent whose slots start here
+    __shared__ uint8_t s_mark[kW][kWave];             // per round: (parent, word) lane whose candidates start here
     __shared__ uint64_t s_sum[5][kW];                 // level counters, per wavefront
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -504,6 +505,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     uint32_t *SEG = s_seg[wv];
     uint32_t *RUN = s_run[wv];
     uint8_t *OWN = s_owner[wv];
+    uint8_t *MARK = s_mark[wv];
     const uint64_t rstride = 4 + (uint64_t)A.wm;
     // Record slots are reserved 64 at a time per wavefront; a round's passing
     // children go to one chunk of slots (a chunk that cannot hold them is closed).
@@ -661,12 +663,20 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
                 // (parent, word) lane whose prefix is the last one not above it
                 const uint32_t gidx = r0 + (uint32_t)lane;
                 const bool live = gidx < total;
-                int t = 0;
-#pragma unroll
-                for (int step = kWave / 2; step > 0; step >>= 1) {
-                    const uint32_t pv = __shfl(pos, (t + step) & (kWave - 1));
-                    if (t + step < kWave && pv <= gidx) t += step;
-                }
+                // The (parent, word) lane t owning candidate gidx: a lane whose
+                // range starts inside the round marks its first position (the
+                // wavefront's LDS writes land in program order, so the marks
+                // overwrite the clearing), an inclusive max-scan carries every
+                // mark to the end of its range, and positions before the first
+                // mark belong to the last lane whose range starts at or before
+                // r0 (every marking lane lies above it).
+                MARK[lane] = 0;
+                if (cnt > 0 && pos > r0 && pos < r0 + (uint32_t)kWave) MARK[pos - r0] = (uint8_t)lane;
+                wave_sync();
+                const int own0 = 63 - __clzll((long long)__ballot(pos <= r0));
+                int t = (int)wave_incl_scan_op<uint32_t>((uint32_t)MARK[lane], 0u,
+                                                         [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+                t = t > own0 ? t : own0;
                 const uint64_t xt = __shfl(x, t);
                 const uint32_t rank = gidx - __shfl(pos, t);
                 const int tq = t / wm;
@@ -676,15 +686,20 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
                 const uint32_t sg = SEG[qc];
                 const int first = (int)(sg & 0xFFu), na = live ? (int)(sg >> 8) : 0;
                 // c_j: objects of the parent having j (32-bit LDS reads, one bit each)
-                uint32_t clo = 0, chi = 0;
+                // (reads issued kCb at a time, so their LDS latencies overlap)
+                uint64_t c = 0;
                 {
+                    constexpr int kCb = 8;
                     const uint32_t *col32 = R32 + 2 * (first * WMC + wj) + (bj >> 5);
                     const uint32_t sh = (uint32_t)(bj & 31);
-                    const int alo = na < 32 ? na : 32;
-                    for (int i = 0; i < alo; ++i) clo |= ((col32[2 * WMC * i] >> sh) & 1u) << i;
-                    for (int i = 32; i < na; ++i) chi |= ((col32[2 * WMC * i] >> sh) & 1u) << (i - 32);
+                    for (int i0 = 0; i0 < na; i0 += kCb) {
+                        uint32_t v[kCb];
+#pragma unroll
+                        for (int k = 0; k < kCb; ++k) v[k] = (i0 + k < na) ? col32[2 * WMC * (i0 + k)] : 0u;
+#pragma unroll
+                        for (int k = 0; k < kCb; ++k) c |= (uint64_t)((v[k] >> sh) & 1u) << (i0 + k);
+                    }
                 }
-                const uint64_t c = ((uint64_t)chi << 32) | clo;
                 // D = AND of the rows of c_j
                 uint64_t D[WMC];
 #pragma unroll
