@@ -353,7 +353,7 @@ void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsign
 {
     const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kBlock)));
     hipEvent_t b = c->prof_begin();
-    hipLaunchKernelGGL(k_local_write, dim3(gl), dim3(kBlock), 0, c->stream, A);
+    hipLaunchKernelGGL(k_local_write<WMC>, dim3(gl), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
     c->prof_end(FCBO_K_WRITE_LOCAL, b);
     if constexpr (WMC <= 8) {

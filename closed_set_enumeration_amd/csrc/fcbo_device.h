@@ -792,10 +792,15 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
 
 // Children of the local parents, one thread per record slot: intent, cursor and
 // list bounds from the record, the extent list picked from the parent's list by
-// the object mask.
+// the object mask.  Every load of a slot is issued before its stores (the
+// record in full, then the parent's offsets, then the object ids eight at a
+// time), so a thread waits for three memory latencies per child rather than
+// one per word.
+template <int WMC>
 __global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
 {
     if (A.counters[CNT_OVERFLOW]) return;
+    const int wm = words_of<WMC>(A.wm);
     const uint64_t rstride = 4 + (uint64_t)A.wm;
     // Slots of stripe st: [st * region, st * region + count_st), in chunks of
     // 64.  The chunks are walked interleaved, chunk c of every stripe before
@@ -809,33 +814,52 @@ __global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
     uint64_t smax = 0;
     for (int st = 0; st < kRecStripes; ++st) smax = max(smax, lane_value64(counts, st));
     for (uint64_t f = t; f < smax * kRecStripes; f += nt) {
-        {
-            // a wavefront's 64 threads share the chunk (t starts at a multiple
-            // of 64 and the thread count is one), so st is uniform
-            const uint64_t ch = f / kWave;
-            const int st = __builtin_amdgcn_readfirstlane((int)(ch % kRecStripes));
-            const uint64_t k = (ch / kRecStripes) * kWave + f % kWave;  // slot within the stripe
-            if (k >= lane_value64(counts, st)) continue;
-            const uint64_t i = (uint64_t)st * A.lrec_region + k;
-            if ((uint32_t)(i % kWave) >= A.lfill[i / kWave]) continue;  // unused slot of a closed chunk
-            const uint64_t *rec = A.lrec + i * rstride;
-            const uint64_t w0 = rec[0], w1 = rec[1];
-            const uint64_t p = w0 & 0xFFFFFFFFull;
-            const uint32_t cnt = (uint32_t)(w1 >> 32);
-            const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
-            const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
-            for (int u = 0; u < A.wm; ++u) A.intents[child * A.wm + u] = rec[4 + u];
-            A.cursor[child] = (int32_t)(w0 >> 32);
-            A.loff[child] = obeg;
-            A.loff[child + 1] = obeg + cnt;
-            const uint32_t *src = A.objs + A.loff[A.lo + p];
-            uint64_t c = rec[3];
-            uint64_t q = obeg;
-            while (c) {
-                A.objs[q++] = src[__ffsll((unsigned long long)c) - 1];
+        // a wavefront's 64 threads share the chunk (t starts at a multiple
+        // of 64 and the thread count is one), so st is uniform
+        const uint64_t ch = f / kWave;
+        const int st = __builtin_amdgcn_readfirstlane((int)(ch % kRecStripes));
+        const uint64_t k = (ch / kRecStripes) * kWave + f % kWave;  // slot within the stripe
+        if (k >= lane_value64(counts, st)) continue;
+        const uint64_t i = (uint64_t)st * A.lrec_region + k;
+        if ((uint32_t)(i % kWave) >= A.lfill[i / kWave]) continue;  // unused slot of a closed chunk
+        const uint64_t *rec = A.lrec + i * rstride;
+        const uint64_t w0 = rec[0], w1 = rec[1], w2 = rec[2];
+        uint64_t c = rec[3];
+        uint64_t d[WMC <= 8 ? WMC : 1];
+#pragma unroll
+        for (int u = 0; u < (WMC <= 8 ? WMC : 1); ++u) d[u] = (WMC <= 8 && u < wm) ? rec[4 + u] : 0ull;
+        const uint64_t p = w0 & 0xFFFFFFFFull;
+        const uint64_t cb = A.cbase[p], ob = A.obase[p], so = A.loff[A.lo + p];
+        const uint32_t cnt = (uint32_t)(w1 >> 32);
+        const uint64_t child = A.child_lo + cb + (w1 & 0xFFFFFFFFull);
+        const uint64_t obeg = A.child_obj_lo + ob + w2;
+        const uint32_t *src = A.objs + so;
+        uint64_t q = obeg;
+        while (c) {
+            uint32_t v[8];
+            int nv = 0;
+#pragma unroll
+            for (int k8 = 0; k8 < 8; ++k8) {
+                const int idx = c ? __ffsll((unsigned long long)c) - 1 : 0;  // src[0] exists: c was not empty
+                v[k8] = src[idx];
+                nv += c ? 1 : 0;
                 c &= c - 1ull;
             }
+#pragma unroll
+            for (int k8 = 0; k8 < 8; ++k8)
+                if (k8 < nv) A.objs[q + k8] = v[k8];
+            q += (uint64_t)nv;
         }
+        if constexpr (WMC <= 8) {
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                if (u < wm) A.intents[child * A.wm + u] = d[u];
+        } else {
+            for (int u = 0; u < A.wm; ++u) A.intents[child * A.wm + u] = rec[4 + u];
+        }
+        A.cursor[child] = (int32_t)(w0 >> 32);
+        A.loff[child] = obeg;
+        A.loff[child + 1] = obeg + cnt;
     }
 }
 
