@@ -163,6 +163,7 @@ struct fcbo_context {
     // profiling
     bool profile = false;
     std::vector<hipEvent_t> ev_pool;
+    hipEvent_t ev_counts = nullptr;  // a level's counters have reached the host
     size_t ev_used = 0;
     std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> marks;
 
@@ -208,6 +209,8 @@ struct fcbo_context {
         h_counters = nullptr;
         for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
         ev_pool.clear();
+        if (ev_counts) (void)hipEventDestroy(ev_counts);
+        ev_counts = nullptr;
     }
 
     // per-test buffers of the huge set (its BigStore plus the accumulators)
@@ -242,6 +245,8 @@ struct fcbo_context {
         A.nchunk = nchunk();
         A.counters = counters + (uint64_t)ctr * CNT_N;
         A.counters_next = counters + (uint64_t)(1 - ctr) * CNT_N;
+        A.child_cap = std::min(std::min(cap_int / (uint64_t)wm, cap_cur), cap_loff ? cap_loff - 1 : 0);
+        A.obj_cap = cap_o;
         return A;
     }
 
@@ -469,7 +474,14 @@ void fcbo_context::enumerate_levels()
                  fchild + lo, lo + P);
             prof_end(FCBO_K_SCAN, b);
             CK(hipMemcpyAsync(h_counters, A.counters, CNT_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
-            CK(hipStreamSynchronize(stream));
+            if (!ev_counts) CK(hipEventCreateWithFlags(&ev_counts, hipEventDisableTiming));
+            CK(hipEventRecord(ev_counts, stream));
+            // The children are written before the host has read the counts, so the
+            // device works on while the host prepares the next level.  The write
+            // kernels do nothing when the level overflowed or the store has no
+            // room; both cases are handled below.
+            fns.writes(this, A, P, classes);
+            CK(hipEventSynchronize(ev_counts));
             const uint64_t n_mid = h_counters[CNT_MID] + h_counters[CNT_MIDW];
             const unsigned found = (n_mid ? kLevelMid : 0u) | (h_counters[CNT_HUGE] ? kLevelHuge : 0u);
             if (found & ~classes) {  // parents of a class whose kernels did not run
@@ -516,15 +528,17 @@ void fcbo_context::enumerate_levels()
             med_objs += h_counters[CNT_MID_OBJS];
             big_tests += h_counters[CNT_THUGE];
             big_scan += h_counters[CNT_BIG_SCAN];
-            // room for the children in the store
+            // room for the children in the store; the writes issued above did
+            // nothing if it had to grow
             const uint64_t k_end = lo + P + n_children;
             const uint64_t keep_k = lo + P;
+            const bool had_room = k_end <= A.child_cap && obj_hi + n_objs <= A.obj_cap;
             ensure(intents, cap_int, k_end * wm, keep_k * wm, stream, mc);
             ensure(cursor, cap_cur, k_end, keep_k, stream, mc);
             ensure(loff, cap_loff, k_end + 1, keep_k + 1, stream, mc);
             ensure(objs, cap_o, obj_hi + n_objs, obj_hi, stream, mc);
             ensure(fchild, cap_fch, k_end + 1, keep_k + 1, stream, mc);
-            if (n_children) fns.writes(this, level_args(lo, P, obj_hi), P, classes);
+            if (n_children && !had_room) fns.writes(this, level_args(lo, P, obj_hi), P, classes);
         } while (redo);
         ctr ^= 1;
         lo += P;

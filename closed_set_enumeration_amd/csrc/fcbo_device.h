@@ -134,10 +134,22 @@ struct LevelArgs {
     uint64_t *counters;    // CNT_* of this level
     uint64_t *counters_next; // CNT_* of the next level, cleared by the local test kernel
     int chunk;             // parents per chunk of the local test (at most LocalCfg::kChunk)
+    uint64_t child_cap;    // concepts the store can hold (intents, cursors, list offsets)
+    uint64_t obj_cap;      // list entries the store can hold
 };
 
 // ---------------------------------------------------------------------------
 // small helpers
+
+// Whether the store has room for the children this level counted.  The child
+// writes are issued before the host has read the counts, so every write kernel
+// checks this first and does nothing when the store must grow (the host then
+// grows it and issues the writes again).
+__device__ __forceinline__ bool store_has_room(const LevelArgs &A)
+{
+    return A.child_lo + A.counters[CNT_CHILDREN] <= A.child_cap &&
+           A.child_obj_lo + A.counters[CNT_OBJS] <= A.obj_cap;
+}
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
@@ -799,7 +811,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
 template <int WMC>
 __global__ void __launch_bounds__(kBlock) k_local_write(LevelArgs A)
 {
-    if (A.counters[CNT_OVERFLOW]) return;
+    if (A.counters[CNT_OVERFLOW] || !store_has_room(A)) return;
     const int wm = words_of<WMC>(A.wm);
     const uint64_t rstride = 4 + (uint64_t)A.wm;
     // Slots of stripe st: [st * region, st * region + count_st), in chunks of
@@ -1358,7 +1370,7 @@ template <int WMC>
 __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
 {
     const int lane = lane_id();
-    if (A.counters[CNT_OVERFLOW]) return;
+    if (A.counters[CNT_OVERFLOW] || !store_has_room(A)) return;
     // Records of stripe st sit in slots [st * region, st * region + count_st).
     // They are walked interleaved, record k of every stripe before record k + 1
     // of any (the order in which they were reserved, roughly): flat index f is
@@ -1459,7 +1471,7 @@ __global__ void __launch_bounds__(kBlock) k_big_write_list(LevelArgs A)
     const BigSet &S = A.huge;
     const int lane = lane_id();
     const int wm = words_of<WMC>(A.wm);
-    if (A.counters[CNT_OVERFLOW]) return;
+    if (A.counters[CNT_OVERFLOW] || !store_has_room(A)) return;
     const uint64_t npass = A.counters[S.pass_slot];
     for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; i < npass;
          i += (uint64_t)gridDim.x * kWavesPerBlock) {
@@ -1600,7 +1612,7 @@ __global__ void __launch_bounds__(kBlock) k_huge_write(LevelArgs A)
 {
     const BigSet &S = A.huge;
     const int lane = lane_id();
-    if (A.counters[CNT_OVERFLOW]) return;
+    if (A.counters[CNT_OVERFLOW] || !store_has_room(A)) return;
     const uint64_t items = A.counters[S.pass_slot] * (uint64_t)A.nchunk;
     for (uint64_t it = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; it < items;
          it += (uint64_t)gridDim.x * kWavesPerBlock) {
