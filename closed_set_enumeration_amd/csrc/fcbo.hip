@@ -134,7 +134,9 @@ struct fcbo_context {
     uint64_t cap_pass = 0, cap_nch = 0, cap_nob = 0, cap_cb = 0, cap_ob = 0, cap_mid = 0, cap_mrec = 0;
     uint64_t *pass = nullptr, *cbase = nullptr, *obase = nullptr;
     uint32_t *nchild = nullptr, *nobj = nullptr, *mid_idx = nullptr;
-    uint64_t *mrec = nullptr;  // child records of the mid parents (words)
+    uint64_t *mrec = nullptr;  // child records of the narrow mid parents (words)
+    uint64_t *wrec = nullptr;  // child records of the wide mid parents (words)
+    uint64_t cap_wrec = 0;
     uint64_t cap_lrec = 0, cap_lfill = 0;
     uint64_t *lrec = nullptr;  // child records of the local parents (words)
     uint32_t *lfill = nullptr; // records per 64-slot chunk
@@ -200,7 +202,7 @@ struct fcbo_context {
     {
         dfree(rows); dfree(cols);
         dfree(intents); dfree(cursor); dfree(loff); dfree(objs); dfree(fchild);
-        dfree(pass); dfree(cbase); dfree(obase); dfree(nchild); dfree(nobj); dfree(mid_idx); dfree(mrec); dfree(lrec); dfree(lfill);
+        dfree(pass); dfree(cbase); dfree(obase); dfree(nchild); dfree(nobj); dfree(mid_idx); dfree(mrec); dfree(wrec); dfree(lrec); dfree(lfill);
         huge.free_all();
         dfree(dt); dfree(tcnt); dfree(icnt);
         dfree(scan_part); dfree(counters);
@@ -235,6 +237,8 @@ struct fcbo_context {
         A.mid_max = wm <= 8 ? kMidMax : kSmallMax;
         A.mrec = mrec;
         A.mrec_region = cap_mrec / (4 + (uint64_t)wm) / kRecStripes;
+        A.wrec = wrec;
+        A.wrec_cap = cap_wrec / (4 + (uint64_t)wm);
         A.lrec = lrec;
         A.lfill = lfill;
         A.lrec_region = std::min(cap_lrec / (4 + (uint64_t)wm), cap_lfill * kWave) / kRecStripes / kWave * kWave;
@@ -366,6 +370,8 @@ void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsign
             b = c->prof_begin();
             hipLaunchKernelGGL(k_mid_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
             CK_LAUNCH();
+            hipLaunchKernelGGL(k_mid_write_wide, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+            CK_LAUNCH();
             c->prof_end(FCBO_K_WRITE_MEDIUM, b);
         }
     }
@@ -436,6 +442,7 @@ void fcbo_context::enumerate_levels()
     }
     if (bm && !huge.bmp) ensure(huge.bmp, huge.cap_bmp, (uint64_t)wn * (tiny ? 1 : 64), 0, stream, 1);
     if (!mrec) ensure(mrec, cap_mrec, rstride * (tiny ? 1 : (1u << 18)), 0, stream, 1);
+    if (!wrec) ensure(wrec, cap_wrec, rstride * (tiny ? 1 : (1u << 16)), 0, stream, 1);
     if (!lrec) ensure_local_records(tiny ? kWave : (1u << 21));
     uint64_t lo = 0, P = 1, obj_hi = (uint64_t)n;  // parents [lo, lo+P); objects used so far
     const uint64_t mid_max = wm <= 8 ? (uint64_t)kMidMax : (uint64_t)kSmallMax;
@@ -503,6 +510,7 @@ void fcbo_context::enumerate_levels()
                     stripe_max = std::max<uint64_t>(stripe_max, h_counters[CNT_MIDREC + t * kCntPad]);
                 // headroom: the split of records over stripes varies from run to run
                 ensure(mrec, cap_mrec, stripe_max * kRecStripes * rstride / 4 * 5, 0, stream, 1);
+                ensure(wrec, cap_wrec, h_counters[CNT_WIDEREC] * rstride, 0, stream, 1);
                 ensure(pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
                 uint64_t lstripe_max = 0;
                 for (int t = 0; t < kRecStripes; ++t)

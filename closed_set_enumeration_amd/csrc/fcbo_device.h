@@ -75,9 +75,10 @@ enum {
     CNT_MIDW = 12 * kCntPad,     // number of wide mid parents (kept at the back of mid_idx)
     CNT_NEXT_MID = 13 * kCntPad, // children that will be mid parents (64 < |C| <= mid_max)
     CNT_NEXT_HUGE = 14 * kCntPad, // children that will be huge parents (|C| > mid_max)
-    CNT_MIDREC = 15 * kCntPad,   // kRecStripes counters, one line each: mid record slots per stripe
-    CNT_LOCREC = (15 + kRecStripes) * kCntPad,  // kRecStripes counters: local record slots per stripe
-    CNT_N = (15 + 2 * kRecStripes) * kCntPad  // words of one level's counters
+    CNT_WIDEREC = 15 * kCntPad,  // child records of the wide mid parents
+    CNT_MIDREC = 16 * kCntPad,   // kRecStripes counters, one line each: mid record slots per stripe
+    CNT_LOCREC = (16 + kRecStripes) * kCntPad,  // kRecStripes counters: local record slots per stripe
+    CNT_N = (16 + 2 * kRecStripes) * kCntPad  // words of one level's counters
 };
 
 // Huge parents, tested one closure test at a time: one work item per (test,
@@ -122,6 +123,8 @@ struct LevelArgs {
     int mid_max;           // parents with more objects are huge
     uint64_t *mrec;        // child records of the mid parents (see k_mid_test)
     uint64_t mrec_region;  // records per stripe: stripe s owns [s * mrec_region, (s + 1) * mrec_region)
+    uint64_t *wrec;        // child records of the wide mid parents, same layout
+    uint64_t wrec_cap;     // records
     uint64_t *lrec;        // child records of the local parents, in chunks of 64 slots
     uint32_t *lfill;       // records used in each chunk of lrec
     uint64_t lrec_region;  // slots per stripe (a multiple of 64), laid out like mrec
@@ -1321,15 +1324,12 @@ __global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
             nobj += o;
         }
         if (tid == 0) {
-            const int stripe = (int)(blockIdx.x % kRecStripes);
+            // (one counter: a level has a few thousand wide parents at most)
             uint64_t base = 0;
-            if (npass)
-                base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC + stripe * kCntPad], (unsigned long long)npass);
-            if (base + npass > A.mrec_region) {
+            if (npass) base = atomicAdd((unsigned long long *)&A.counters[CNT_WIDEREC], (unsigned long long)npass);
+            if (base + npass > A.wrec_cap) {
                 A.counters[CNT_OVERFLOW] = 1;
                 base = ~0ull;  // nothing is written
-            } else {
-                base += (uint64_t)stripe * A.mrec_region;
             }
             s_base = base;
             A.nchild[p] = npass;
@@ -1339,7 +1339,7 @@ __global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
         const uint64_t base = s_base;
         if (base != ~0ull) {
             if (bottom && tid == 0) {
-                uint64_t *rec = A.mrec + base * rstride;
+                uint64_t *rec = A.wrec + base * rstride;
                 rec[0] = p | ((uint64_t)j0 << 32);
                 rec[1] = 0;
                 rec[2] = 0;
@@ -1348,7 +1348,7 @@ __global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
             }
             if (pass) {
                 const uint32_t rank = pbase + before;
-                uint64_t *rec = A.mrec + (base + rank) * rstride;
+                uint64_t *rec = A.wrec + (base + rank) * rstride;
                 rec[0] = p | ((uint64_t)j << 32);
                 rec[1] = (uint64_t)rank | ((uint64_t)cnt << 32);
                 rec[2] = obase + ex;
@@ -1363,18 +1363,20 @@ __global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
     if (next_mid && lane == 0) atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_MID], (unsigned long long)next_mid);
 }
 
-// Children of the mid parents, one wavefront per record: intent and cursor
-// come from the record, the extent list from a scan of the parent's list for
-// the objects having j (ascending).
+// Children of the narrow mid parents.  A wavefront takes kMidRun consecutive records
+// of a stripe (a parent's records are consecutive, in rank order): their
+// intents, cursors and list bounds come from the records, and every run of
+// records with the same parent shares one pass over the parent's object list,
+// in which each object's row is read once and tested for the attribute j of
+// every record of the run (the objects of C_j, ascending).
+constexpr int kMidRun = 8;
+
 template <int WMC>
 __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
 {
     const int lane = lane_id();
     if (A.counters[CNT_OVERFLOW] || !store_has_room(A)) return;
-    // Records of stripe st sit in slots [st * region, st * region + count_st).
-    // They are walked interleaved, record k of every stripe before record k + 1
-    // of any (the order in which they were reserved, roughly): flat index f is
-    // record f / kRecStripes of stripe f % kRecStripes.
+    const int wm = words_of<WMC>(A.wm);
     const uint64_t rstride = 4 + (uint64_t)A.wm;
     const uint64_t nw = (uint64_t)gridDim.x * kWavesPerBlock;
     const uint64_t w = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
@@ -1382,32 +1384,124 @@ __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
     const uint64_t counts = lane < kRecStripes ? A.counters[CNT_MIDREC + lane * kCntPad] : 0ull;
     uint64_t kmax = 0;
     for (int st = 0; st < kRecStripes; ++st) kmax = max(kmax, lane_value64(counts, st));
-    for (uint64_t f = w; f < kmax * kRecStripes; f += nw) {
-        {
-            const int st = __builtin_amdgcn_readfirstlane((int)(f % kRecStripes));  // f is per wavefront
-            const uint64_t k = f / kRecStripes;
-            if (k >= lane_value64(counts, st)) continue;
-            const uint64_t *rec = A.mrec + ((uint64_t)st * A.mrec_region + k) * rstride;
-            const uint64_t w0 = rec[0], w1 = rec[1];
-            const uint64_t p = w0 & 0xFFFFFFFFull;
-            const int j = (int)(w0 >> 32);
-            const uint32_t cnt = (uint32_t)(w1 >> 32);
-            const uint64_t c0 = A.lo + p;
-            const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
-            const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
-            for (int u = lane; u < A.wm; u += kWave) A.intents[child * A.wm + u] = rec[4 + u];
-            if (lane == 0) {
-                A.cursor[child] = j;
-                A.loff[child] = obeg;
-                A.loff[child + 1] = obeg + cnt;
-            }
-            if (cnt == 0) continue;
-            uint64_t qo = obeg;
-            scan_list_for_attr(A, A.loff[c0], A.loff[c0 + 1], j, [&](bool in, uint32_t g, uint64_t bal) {
-                if (in) A.objs[qo + __popcll(bal & below_mask(lane))] = g;
-                qo += __popcll(bal);
-            });
+    // Items of kMidRun records, walked interleaved over the stripes (item i of
+    // every stripe before item i + 1 of any: roughly the order of reservation).
+    const uint64_t items = (kmax + kMidRun - 1) / kMidRun;
+    for (uint64_t f = w; f < items * kRecStripes; f += nw) {
+        const int st = __builtin_amdgcn_readfirstlane((int)(f % kRecStripes));  // f is per wavefront
+        const uint64_t k0 = (f / kRecStripes) * kMidRun;
+        const uint64_t nst = lane_value64(counts, st);
+        if (k0 >= nst) continue;
+        const int nr = (int)(nst - k0 < (uint64_t)kMidRun ? nst - k0 : (uint64_t)kMidRun);
+        const uint64_t *rec0 = A.mrec + ((uint64_t)st * A.mrec_region + k0) * rstride;
+        // lane r < nr: record r's header, child and list start
+        uint64_t w0 = 0, w1 = 0, w2 = 0;
+        if (lane < nr) {
+            const uint64_t *rec = rec0 + (uint64_t)lane * rstride;
+            w0 = rec[0];
+            w1 = rec[1];
+            w2 = rec[2];
         }
+        const uint64_t pl = w0 & 0xFFFFFFFFull;
+        uint64_t child = 0, qo = 0;
+        if (lane < nr) {
+            child = A.child_lo + A.cbase[pl] + (w1 & 0xFFFFFFFFull);
+            qo = A.child_obj_lo + A.obase[pl] + w2;
+        }
+        // intents: one lane per (record, word)
+        for (int x0 = 0; x0 < nr * wm; x0 += kWave) {
+            const int x = x0 + lane;
+            int r = x / wm;
+            r = r < nr ? r : nr - 1;
+            const uint64_t ch = __shfl(child, r);
+            if (x < nr * wm) A.intents[ch * A.wm + (x - r * wm)] = rec0[(uint64_t)r * rstride + 4 + (x - r * wm)];
+        }
+        if (lane < nr) {
+            const uint32_t cnt = (uint32_t)(w1 >> 32);
+            A.cursor[child] = (int32_t)(w0 >> 32);
+            A.loff[child] = qo;
+            A.loff[child + 1] = qo + cnt;
+        }
+        // extent lists, one pass over each parent's list per run of records
+        for (int r = 0; r < nr;) {
+            const uint64_t p = lane_value64(w0, r) & 0xFFFFFFFFull;
+            int r1 = r + 1;
+            while (r1 < nr && (lane_value64(w0, r1) & 0xFFFFFFFFull) == p) ++r1;
+            const uint64_t c0 = A.lo + p;
+            const uint64_t l0 = A.loff[c0], l1 = A.loff[c0 + 1];
+            // intent words holding the attributes of the run (C non-empty)
+            uint32_t need = 0;
+            for (int ri = r; ri < r1; ++ri)
+                if ((lane_value64(w1, ri) >> 32) != 0) need |= 1u << ((lane_value64(w0, ri) >> 32) >> 6);
+            // four chunks of 64 objects per step, so that their loads overlap
+            for (uint64_t o = l0; o < l1; o += 4 * kWave) {
+                uint32_t g[4];
+                bool valid[4];
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const uint64_t idx = o + (uint64_t)(c4 * kWave + lane);
+                    valid[c4] = idx < l1;
+                    g[c4] = valid[c4] ? A.objs[idx] : 0u;
+                }
+                uint64_t row[4][WMC];
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+                    for (int u = 0; u < WMC; ++u)
+                        row[c4][u] = (valid[c4] && u < wm && ((need >> u) & 1u)) ? A.rows[(uint64_t)g[c4] * A.wm + u] : 0ull;
+                for (int ri = r; ri < r1; ++ri) {
+                    if ((lane_value64(w1, ri) >> 32) == 0) continue;  // C empty (the bottom child)
+                    const int j = (int)(lane_value64(w0, ri) >> 32);
+#pragma unroll
+                    for (int c4 = 0; c4 < 4; ++c4) {
+                        uint64_t word = 0;
+#pragma unroll
+                        for (int u = 0; u < WMC; ++u)
+                            if (u == (j >> 6)) word = row[c4][u];
+                        const bool in = (word >> (j & 63)) & 1ull;
+                        const uint64_t bal = __ballot(in);
+                        const uint64_t at = lane_value64(qo, ri);
+                        if (in) A.objs[at + __popcll(bal & below_mask(lane))] = g[c4];
+                        if (lane == ri) qo += (uint64_t)__popcll(bal);
+                    }
+                }
+            }
+            r = r1;
+        }
+    }
+}
+
+// Children of the wide mid parents, one wavefront per record: the parent's
+// list is scanned for the objects having j, 256 entries a step.  (Their lists
+// are long, so a record is enough work for a wavefront.)
+__global__ void __launch_bounds__(kBlock) k_mid_write_wide(LevelArgs A)
+{
+    const int lane = lane_id();
+    if (A.counters[CNT_OVERFLOW] || !store_has_room(A)) return;
+    const uint64_t nrec = A.counters[CNT_WIDEREC];
+    const uint64_t rstride = 4 + (uint64_t)A.wm;
+    for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; i < nrec;
+         i += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t *rec = A.wrec + i * rstride;
+        const uint64_t w0 = rec[0], w1 = rec[1];
+        const uint64_t p = w0 & 0xFFFFFFFFull;
+        const int j = (int)(w0 >> 32);
+        const uint32_t cnt = (uint32_t)(w1 >> 32);
+        const uint64_t c0 = A.lo + p;
+        const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
+        const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
+        for (int u = lane; u < A.wm; u += kWave) A.intents[child * A.wm + u] = rec[4 + u];
+        if (lane == 0) {
+            A.cursor[child] = j;
+            A.loff[child] = obeg;
+            A.loff[child + 1] = obeg + cnt;
+        }
+        if (cnt == 0) continue;
+        uint64_t qo = obeg;
+        scan_list_for_attr(A, A.loff[c0], A.loff[c0 + 1], j, [&](bool in, uint32_t g, uint64_t bal) {
+            if (in) A.objs[qo + __popcll(bal & below_mask(lane))] = g;
+            qo += __popcll(bal);
+        });
     }
 }
 
