@@ -45,7 +45,8 @@ constexpr uint64_t kScanSmallMax = 8192; // host-known lengths up to this are sc
 constexpr int kOutTileWords = 1024; // extent words staged in LDS per output tile
 constexpr int kBmpMaxWords = 16384; // big parents use extent bitmaps when N <= 64 * this
 constexpr int kMidMax = 4096;       // parents with more objects are huge (tested a chunk at a time)
-constexpr int kMidWaves = 2;        // wavefronts per block of the incidence kernel
+constexpr int kMidWaves = 4;        // wavefronts per block of the incidence kernel
+constexpr int kMidCand = 128;       // candidates whose D a wavefront keeps in LDS at a time
 constexpr int kMidWide = 512;       // mid parents with more objects get a whole workgroup each
 constexpr int kWideThreads = 512;   // threads of that workgroup (at least 64 x 8 candidates)
 constexpr int kWideWaves = kWideThreads / kWave;
@@ -1016,20 +1017,35 @@ __device__ __forceinline__ void scan_list_for_attr(const LevelArgs &A, uint64_t 
 //   [0] parent | j << 32, [1] sibling rank | |C| << 32, [2] object offset of
 //   the child's list inside the parent's children, [3] the objects of C as a
 //   mask over the parent's list (local parents only, else 0), [4..] D.
+//
+// A wavefront keeps the D of kMidCand members of U at a time (small tables,
+// so that many wavefronts fit a compute unit); a parent with more members is
+// tested a slice of U per pass over its list.  Records are reserved per round
+// of 64 tests and carry their rank and object offset.
 
 template <int WMC>
 __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
 {
-    constexpr int kMaxCand = kWave * WMC;
-    __shared__ uint64_t s_d[kMidWaves][kMaxCand * WMC];
-    __shared__ uint32_t s_c[kMidWaves][kMaxCand];
-    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    __shared__ uint64_t s_d[kMidWaves][kMidCand * WMC];
+    __shared__ uint32_t s_c[kMidWaves][kMidCand];
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = words_of<WMC>(A.wm);
     uint64_t *Dt = s_d[wv];
     uint32_t *Ct = s_c[wv];
     uint32_t next_mid = 0;
+    bool overflow = false;
+    const int stripe = (int)(((uint64_t)blockIdx.x * kMidWaves + wv) % kRecStripes);
     const uint64_t count = A.counters[CNT_MID];
     const uint64_t rstride = 4 + (uint64_t)A.wm;
+    auto reserve = [&](uint32_t n) -> uint64_t {  // record slots, uniform
+        uint64_t base = 0;
+        if (lane == 0) base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC + stripe * kCntPad], (unsigned long long)n);
+        base = uniform64(base);
+        if (base + n > A.mrec_region) overflow = true;
+        return (uint64_t)stripe * A.mrec_region + base;
+    };
+    const uint64_t rhi = (uint64_t)(stripe + 1) * A.mrec_region;
     for (uint64_t it = (uint64_t)blockIdx.x * kMidWaves + wv; it < count; it += (uint64_t)gridDim.x * kMidWaves) {
         const uint64_t p = A.mid_idx[it];
         const uint64_t c0 = A.lo + p;
@@ -1044,7 +1060,6 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
                 if (u == wm - 1) Bx[u] |= ~A.tail_m;
             }
         }
-        // U: candidates carried by some object of A
         uint64_t U[WMC];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) U[u] = 0;
@@ -1055,7 +1070,7 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
                 if (u < wm) U[u] |= A.rows[g * A.wm + u];
         }
         int nU = 0, j0 = -1;
-        int pre[WMC];  // members of U in the words before u
+        int pre[WMC];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
             pre[u] = nU;
@@ -1066,35 +1081,6 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
                 nU += __popcll(U[u]);
             }
         }
-        for (int x = lane; x < nU * WMC; x += kWave) Dt[x] = ~0ull;
-        for (int x = lane; x < nU; x += kWave) Ct[x] = 0;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // incidences
-        for (uint64_t o = o0 + lane; o < o1; o += kWave) {
-            const uint64_t g = A.objs[o];
-            uint64_t row[WMC];
-#pragma unroll
-            for (int u = 0; u < WMC; ++u) row[u] = (u < wm) ? A.rows[g * A.wm + u] : 0ull;
-#pragma unroll
-            for (int u = 0; u < WMC; ++u) {
-                uint64_t x = row[u] & U[u];
-                while (x) {
-                    const int b = __ffsll((unsigned long long)x) - 1;
-                    x &= x - 1ull;
-                    const int r = pre[u] + __popcll(U[u] & below_mask(b));
-#pragma unroll
-                    for (int v = 0; v < WMC; ++v)
-                        if (v < wm) atomicAnd((unsigned long long *)&Dt[r * WMC + v], (unsigned long long)row[v]);
-                    atomicAdd(&Ct[r], 1u);
-                }
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // canonical tests: a passing candidate keeps its |C| with the top bit set
         bool bottom = false;
         if (j0 > y) {
             bottom = true;
@@ -1102,85 +1088,104 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
             for (int u = 0; u < WMC; ++u)
                 if (u == (j0 >> 6) && ((U[u] >> (j0 & 63)) & 1ull)) bottom = false;
         }
-        uint32_t n_pass = bottom ? 1u : 0u, n_obj = 0;
-        for (int r0 = 0; r0 < nU; r0 += kWave) {
-            const int r = r0 + lane;
-            const bool active = r < nU;
-            const int j = active ? select_words<WMC>(U, wm, r) : 0;
-            const int wj = j >> 6, bj = j & 63;
-            uint64_t bad = 0;
-            if (active) {
+        uint32_t rank = 0, objoff = 0;
+        if (bottom) {
+            const uint64_t at = reserve(1);
+            if (lane == 0 && at < rhi) {
+                uint64_t *rec = A.mrec + at * rstride;
+                rec[0] = p | ((uint64_t)j0 << 32);
+                rec[1] = 0;
+                rec[2] = 0;
+                rec[3] = 0;
+                for (int u = 0; u < wm; ++u) rec[4 + u] = (u == wm - 1) ? A.tail_m : ~0ull;
+            }
+            rank = 1;
+        }
+        for (int lo = 0; lo < nU; lo += kMidCand) {
+            const int nc = nU - lo < kMidCand ? nU - lo : kMidCand;
+            uint64_t Us[WMC];
 #pragma unroll
-                for (int u = 0; u < WMC; ++u) {
-                    if (u < wm && u <= wj) {
-                        const uint64_t extra = Dt[r * WMC + u] & ~Bx[u];
-                        bad |= (u < wj) ? extra : (extra & below_mask(bj));
+            for (int u = 0; u < WMC; ++u) {
+                Us[u] = 0;
+                if (u < wm) {
+                    const int cu = __popcll(U[u]);
+                    const int klo = lo - pre[u], khi = lo + nc - pre[u];
+                    if (klo < cu && khi > 0) {
+                        uint64_t m = U[u];
+                        if (klo > 0) m &= ~below_mask(select64(U[u], klo));
+                        if (khi < cu) m &= below_mask(select64(U[u], khi));
+                        Us[u] = m;
                     }
                 }
             }
-            const bool pass = active && bad == 0;
-            const uint32_t cnt = pass ? Ct[r] : 0u;
-            if (pass) Ct[r] = cnt | 0x80000000u;
-            n_pass += (uint32_t)__popcll(__ballot(pass));
-            n_obj += wave_sum(cnt);
-            // children that are mid parents on the next level (fewer objects
-            // than this parent, so never huge), added up per wavefront
-            next_mid += (uint32_t)__popcll(__ballot(pass && cnt > (uint32_t)kSmallMax));
-        }
-        wave_sync();
-        // child records: one contiguous block per parent, in rank (ascending j)
-        // order, reserved with a single atomic
-        const int stripe = (int)(((uint64_t)blockIdx.x * kMidWaves + wv) % kRecStripes);
-        uint64_t base = 0;
-        if (lane == 0 && n_pass)
-            base = atomicAdd((unsigned long long *)&A.counters[CNT_MIDREC + stripe * kCntPad], (unsigned long long)n_pass);
-        base = uniform64(base);
-        const bool fits = base + n_pass <= A.mrec_region;
-        base += (uint64_t)stripe * A.mrec_region;  // first record slot of this parent
-        if (!fits && lane == 0) A.counters[CNT_OVERFLOW] = 1;
-        if (lane == 0) {
-            A.nchild[p] = n_pass;
-            A.nobj[p] = n_obj;
-        }
-        if (fits && n_pass) {
-            uint32_t rank = 0, objoff = 0;
-            if (bottom) {  // the first attribute outside B: C = {}, D = M, rank 0
-                if (lane == 0) {
-                    uint64_t *rec = A.mrec + base * rstride;
-                    rec[0] = p | ((uint64_t)j0 << 32);
-                    rec[1] = 0;
-                    rec[2] = 0;
-                    rec[3] = 0;
-                    for (int u = 0; u < wm; ++u) rec[4 + u] = (u == wm - 1) ? A.tail_m : ~0ull;
+            for (int x = lane; x < nc * WMC; x += kWave) Dt[x] = ~0ull;
+            for (int x = lane; x < nc; x += kWave) Ct[x] = 0;
+            wave_sync();
+            for (uint64_t o = o0 + lane; o < o1; o += kWave) {
+                const uint64_t g = A.objs[o];
+                uint64_t row[WMC];
+#pragma unroll
+                for (int u = 0; u < WMC; ++u) row[u] = (u < wm) ? A.rows[g * A.wm + u] : 0ull;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u) {
+                    uint64_t x = row[u] & Us[u];
+                    while (x) {
+                        const int b = __ffsll((unsigned long long)x) - 1;
+                        x &= x - 1ull;
+                        const int r = pre[u] + __popcll(U[u] & below_mask(b)) - lo;
+#pragma unroll
+                        for (int v = 0; v < WMC; ++v)
+                            if (v < wm) atomicAnd((unsigned long long *)&Dt[r * WMC + v], (unsigned long long)row[v]);
+                        atomicAdd(&Ct[r], 1u);
+                    }
                 }
-                rank = 1;
             }
-            for (int r0 = 0; r0 < nU; r0 += kWave) {
-                const int r = r0 + lane;
-                const uint32_t cv = r < nU ? Ct[r] : 0u;
-                const bool pass = (cv >> 31) != 0;
-                const uint32_t cnt = pass ? (cv & 0x7FFFFFFFu) : 0u;
+            wave_sync();
+            for (int r0 = 0; r0 < nc; r0 += kWave) {
+                const int rl = r0 + lane;
+                const bool active = rl < nc;
+                const int j = active ? select_words<WMC>(U, wm, lo + rl) : 0;
+                const int wj = j >> 6, bj = j & 63;
+                uint64_t bad = 0;
+                if (active) {
+#pragma unroll
+                    for (int u = 0; u < WMC; ++u) {
+                        if (u < wm && u <= wj) {
+                            const uint64_t extra = Dt[rl * WMC + u] & ~Bx[u];
+                            bad |= (u < wj) ? extra : (extra & below_mask(bj));
+                        }
+                    }
+                }
+                const bool pass = active && bad == 0;
+                const uint32_t cnt = pass ? Ct[rl] : 0u;
+                next_mid += (uint32_t)__popcll(__ballot(pass && cnt > (uint32_t)kSmallMax));
                 const uint64_t bal = __ballot(pass);
                 if (!bal) continue;
+                const uint32_t np = (uint32_t)__popcll(bal);
+                const uint64_t base = reserve(np);
                 const uint32_t before = (uint32_t)__popcll(bal & below_mask(lane));
                 const uint32_t off = objoff + wave_excl_scan(cnt);
-                if (pass) {
-                    const int j = select_words<WMC>(U, wm, r);
-                    uint64_t *rec = A.mrec + (base + rank + before) * rstride;
+                if (pass && base + before < rhi) {
+                    uint64_t *rec = A.mrec + (base + before) * rstride;
                     rec[0] = p | ((uint64_t)j << 32);
                     rec[1] = (uint64_t)(rank + before) | ((uint64_t)cnt << 32);
                     rec[2] = off;
                     rec[3] = 0;
 #pragma unroll
                     for (int u = 0; u < WMC; ++u)
-                        if (u < wm) rec[4 + u] = (u == wm - 1) ? (Dt[r * WMC + u] & A.tail_m) : Dt[r * WMC + u];
+                        if (u < wm) rec[4 + u] = (u == wm - 1) ? (Dt[rl * WMC + u] & A.tail_m) : Dt[rl * WMC + u];
                 }
-                rank += (uint32_t)__popcll(bal);
+                rank += np;
                 objoff += wave_sum(cnt);
             }
+            wave_sync();
         }
-        wave_sync();
+        if (lane == 0) {
+            A.nchild[p] = rank;
+            A.nobj[p] = objoff;
+        }
     }
+    if (overflow && lane == 0) A.counters[CNT_OVERFLOW] = 1;
     if (next_mid && lane == 0) atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_MID], (unsigned long long)next_mid);
 }
 
