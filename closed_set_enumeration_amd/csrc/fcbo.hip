@@ -178,19 +178,42 @@ struct fcbo_context {
         }
         return ev_pool[ev_used++];
     }
-    hipEvent_t prof_begin()
+    hipEvent_t prof_begin(hipStream_t s = nullptr)
     {
         if (!profile) return nullptr;
         hipEvent_t e = ev_get();
-        CK(hipEventRecord(e, stream));
+        CK(hipEventRecord(e, s ? s : stream));
         return e;
     }
-    void prof_end(int cls, hipEvent_t b)
+    void prof_end(int cls, hipEvent_t b, hipStream_t s = nullptr)
     {
         if (!profile) return;
         hipEvent_t e = ev_get();
-        CK(hipEventRecord(e, stream));
+        CK(hipEventRecord(e, s ? s : stream));
         marks.push_back({cls, {b, e}});
+    }
+
+    // Side streams for work of a level that is independent of the main
+    // stream's (different parents, different counters: the huge and the wide
+    // mid parents' tests beside the narrow ones, the writers of the classes
+    // beside each other); forked from and joined back to the main stream
+    // through events.  Default priority, like the caller's stream.
+    static constexpr int kSide = 2;
+    hipStream_t aux[kSide] = {nullptr, nullptr};
+    hipEvent_t ev_fork[kSide] = {nullptr, nullptr}, ev_join[kSide] = {nullptr, nullptr};
+    hipStream_t fork(int i)
+    {
+        if (!aux[i]) CK(hipStreamCreateWithFlags(&aux[i], hipStreamNonBlocking));
+        if (!ev_fork[i]) CK(hipEventCreateWithFlags(&ev_fork[i], hipEventDisableTiming));
+        if (!ev_join[i]) CK(hipEventCreateWithFlags(&ev_join[i], hipEventDisableTiming));
+        CK(hipEventRecord(ev_fork[i], stream));
+        CK(hipStreamWaitEvent(aux[i], ev_fork[i], 0));
+        return aux[i];
+    }
+    void join(int i)
+    {
+        CK(hipEventRecord(ev_join[i], aux[i]));
+        CK(hipStreamWaitEvent(stream, ev_join[i], 0));
     }
 
     uint64_t min_cap() const { return tiny ? 1 : 1024; }
@@ -213,6 +236,13 @@ struct fcbo_context {
         ev_pool.clear();
         if (ev_counts) (void)hipEventDestroy(ev_counts);
         ev_counts = nullptr;
+        for (int i = 0; i < kSide; ++i) {
+            if (ev_fork[i]) (void)hipEventDestroy(ev_fork[i]);
+            if (ev_join[i]) (void)hipEventDestroy(ev_join[i]);
+            if (aux[i]) (void)hipStreamDestroy(aux[i]);
+            ev_fork[i] = ev_join[i] = nullptr;
+            aux[i] = nullptr;
+        }
     }
 
     // per-test buffers of the huge set (its BigStore plus the accumulators)
@@ -258,8 +288,9 @@ struct fcbo_context {
     // device or the host; fch (optional) receives fbase + out_a as u32.
     void scan(const uint32_t *a, const uint32_t *b, const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
               uint64_t *out_a, uint64_t *out_b, uint64_t *tot_a, uint64_t *tot_b, uint32_t *fch = nullptr,
-              uint64_t fbase = 0)
+              uint64_t fbase = 0, hipStream_t s = nullptr)
     {
+        const hipStream_t stream = s ? s : this->stream;
         if (!n_dev && n_host <= kScanSmallMax) {
             hipLaunchKernelGGL(k_scan_small, dim3(1), dim3(kScanBlocks), 0, stream, a, b, std::min(n_host, n_cap),
                                out_a, out_b, tot_a, tot_b, fch, fbase);
@@ -317,62 +348,86 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigne
     }
     CK_LAUNCH();
     c->prof_end(FCBO_K_TEST_LOCAL, b);
+    // With mid parents on the level too, the huge parents' tests (a few
+    // under-filled launches) run on the second stream beside the mid tests:
+    // the two touch different parents and different counters.
+    const bool mid = (classes & kLevelMid) && WMC <= 8;
+    const bool side = (classes & kLevelHuge) && mid;
+    const hipStream_t hs = side ? c->fork(0) : c->stream;
     if (classes & kLevelHuge) {
         // test offsets of the huge parents; total -> counters
-        b = c->prof_begin();
+        b = c->prof_begin(hs);
         c->scan(c->huge.n, nullptr, A.counters + CNT_HUGE, 0, P, c->huge.off, nullptr, A.counters + CNT_THUGE,
-                nullptr);
-        c->prof_end(FCBO_K_SCAN, b);
-        b = c->prof_begin();
-        hipLaunchKernelGGL(k_huge_tasks<WMC>, dim3(gm), dim3(kBlock), 0, c->stream, A);
+                nullptr, nullptr, 0, hs);
+        c->prof_end(FCBO_K_SCAN, b, hs);
+        b = c->prof_begin(hs);
+        hipLaunchKernelGGL(k_huge_tasks<WMC>, dim3(gm), dim3(kBlock), 0, hs, A);
         CK_LAUNCH();
-        c->prof_end(FCBO_K_TEST_BIG, b);
+        c->prof_end(FCBO_K_TEST_BIG, b, hs);
     }
     if constexpr (WMC <= 8) {
         if (classes & kLevelMid) {
+            // wide parents on a side stream, narrow ones on the main stream
+            const hipStream_t ws = c->fork(1);
+            b = c->prof_begin(ws);
+            const unsigned gw = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(P, 4 * (uint64_t)c->n_cu));
+            hipLaunchKernelGGL(k_mid_test_wide<WMC>, dim3(gw), dim3(kWideThreads), 0, ws, A);
+            CK_LAUNCH();
+            c->prof_end(FCBO_K_TEST_MEDIUM, b, ws);
             b = c->prof_begin();
             const unsigned gmid = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(2048, div_up(P, kMidWaves)));
             hipLaunchKernelGGL(k_mid_test<WMC>, dim3(gmid), dim3(kWave * kMidWaves), 0, c->stream, A);
             CK_LAUNCH();
-            const unsigned gw = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(P, 4 * (uint64_t)c->n_cu));
-            hipLaunchKernelGGL(k_mid_test_wide<WMC>, dim3(gw), dim3(kWideThreads), 0, c->stream, A);
-            CK_LAUNCH();
             c->prof_end(FCBO_K_TEST_MEDIUM, b);
+            c->join(1);
         }
     }
     if (!(classes & kLevelHuge)) return;
-    b = c->prof_begin();
+    b = c->prof_begin(hs);
     if (bm) {
-        hipLaunchKernelGGL(k_huge_partial<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+        hipLaunchKernelGGL(k_huge_partial<WMC>, dim3(kGridCap), dim3(kBlock), 0, hs, A);
         CK_LAUNCH();
-        hipLaunchKernelGGL(k_huge_finalize, dim3(1024), dim3(kBlock), 0, c->stream, A);
+        hipLaunchKernelGGL(k_huge_finalize, dim3(1024), dim3(kBlock), 0, hs, A);
     } else {
-        hipLaunchKernelGGL(k_big_test_list<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+        hipLaunchKernelGGL(k_big_test_list<WMC>, dim3(kGridCap), dim3(kBlock), 0, hs, A);
     }
     CK_LAUNCH();
-    c->prof_end(FCBO_K_TEST_BIG, b);
+    c->prof_end(FCBO_K_TEST_BIG, b, hs);
     // sibling offsets of the passing huge tests
-    b = c->prof_begin();
-    c->scan(c->huge.size, nullptr, A.counters + CNT_THUGE, 0, A.huge.cap, c->huge.sscan, nullptr, nullptr, nullptr);
-    c->prof_end(FCBO_K_SCAN, b);
+    b = c->prof_begin(hs);
+    c->scan(c->huge.size, nullptr, A.counters + CNT_THUGE, 0, A.huge.cap, c->huge.sscan, nullptr, nullptr, nullptr,
+            nullptr, 0, hs);
+    c->prof_end(FCBO_K_SCAN, b, hs);
+    if (side) c->join(0);
 }
 
 template <int WMC>
 void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigned classes)
 {
     const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kBlock)));
+    // the mid parents' writers run beside the local one (different children)
+    const bool mid = (classes & kLevelMid) && WMC <= 8;
+    hipStream_t s0 = nullptr, s1 = nullptr;
+    if (mid) {
+        s0 = c->fork(0);
+        s1 = c->fork(1);
+    }
     hipEvent_t b = c->prof_begin();
     hipLaunchKernelGGL(k_local_write<WMC>, dim3(gl), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
     c->prof_end(FCBO_K_WRITE_LOCAL, b);
     if constexpr (WMC <= 8) {
-        if (classes & kLevelMid) {
-            b = c->prof_begin();
-            hipLaunchKernelGGL(k_mid_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+        if (mid) {
+            b = c->prof_begin(s0);
+            hipLaunchKernelGGL(k_mid_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, s0, A);
             CK_LAUNCH();
-            hipLaunchKernelGGL(k_mid_write_wide, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+            c->prof_end(FCBO_K_WRITE_MEDIUM, b, s0);
+            b = c->prof_begin(s1);
+            hipLaunchKernelGGL(k_mid_write_wide, dim3(kGridCap), dim3(kBlock), 0, s1, A);
             CK_LAUNCH();
-            c->prof_end(FCBO_K_WRITE_MEDIUM, b);
+            c->prof_end(FCBO_K_WRITE_MEDIUM, b, s1);
+            c->join(0);
+            c->join(1);
         }
     }
     if (!(classes & kLevelHuge)) return;

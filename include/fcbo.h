@@ -107,7 +107,10 @@ typedef struct {
  *   n_objects         N, 1 <= N <= 2^31 - 1
  *   n_attrs           M, 1 <= M <= 4096
  *   row_stride_words  >= ceil(M / 64)
- *   hip_stream        hipStream_t for all device work, or NULL for the null stream
+ *   hip_stream        hipStream_t the calls are ordered on, or NULL for the null
+ *                     stream.  Independent parts of a level also run on two
+ *                     internal streams of the context (default priority) that
+ *                     fork from and join back to this one through events.
  *   out               receives the context
  * The device holds the rows (N x ceil(M/64) words) and their transpose, the
  * columns (M x ceil(N/64) words, column j = objects having attribute j).
