@@ -326,7 +326,11 @@ namespace {
 // Which parent classes a level has: the local test kernel always runs (it also
 // counts and classifies); the mid and huge kernels only when the level holds
 // such parents.
-enum { kLevelMid = 1, kLevelHuge = 2 };
+enum { kLevelMid = 1, kLevelHuge = 2, kLevelSide = 4 };
+// A level runs independent parts on the side streams only when it has huge
+// parents (the shallow levels, whose huge and wide tests under-fill the
+// device): a fork and join cost the main stream some 20 us of idle time, more
+// than the overlap gains on the deeper levels.
 
 template <int WMC>
 void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigned classes)
@@ -352,7 +356,8 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigne
     // under-filled launches) run on the second stream beside the mid tests:
     // the two touch different parents and different counters.
     const bool mid = (classes & kLevelMid) && WMC <= 8;
-    const bool side = (classes & kLevelHuge) && mid;
+    const bool use_side = (classes & kLevelSide) != 0;
+    const bool side = (classes & kLevelHuge) && mid && use_side;
     const hipStream_t hs = side ? c->fork(0) : c->stream;
     if (classes & kLevelHuge) {
         // test offsets of the huge parents; total -> counters
@@ -368,7 +373,7 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigne
     if constexpr (WMC <= 8) {
         if (classes & kLevelMid) {
             // wide parents on a side stream, narrow ones on the main stream
-            const hipStream_t ws = c->fork(1);
+            const hipStream_t ws = use_side ? c->fork(1) : c->stream;
             b = c->prof_begin(ws);
             const unsigned gw = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(P, 4 * (uint64_t)c->n_cu));
             hipLaunchKernelGGL(k_mid_test_wide<WMC>, dim3(gw), dim3(kWideThreads), 0, ws, A);
@@ -379,7 +384,7 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigne
             hipLaunchKernelGGL(k_mid_test<WMC>, dim3(gmid), dim3(kWave * kMidWaves), 0, c->stream, A);
             CK_LAUNCH();
             c->prof_end(FCBO_K_TEST_MEDIUM, b);
-            c->join(1);
+            if (use_side) c->join(1);
         }
     }
     if (!(classes & kLevelHuge)) return;
@@ -407,8 +412,9 @@ void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsign
     const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kBlock)));
     // the mid parents' writers run beside the local one (different children)
     const bool mid = (classes & kLevelMid) && WMC <= 8;
-    hipStream_t s0 = nullptr, s1 = nullptr;
-    if (mid) {
+    const bool use_side = mid && (classes & kLevelSide) != 0;
+    hipStream_t s0 = c->stream, s1 = c->stream;
+    if (use_side) {
         s0 = c->fork(0);
         s1 = c->fork(1);
     }
@@ -426,8 +432,10 @@ void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsign
             hipLaunchKernelGGL(k_mid_write_wide, dim3(kGridCap), dim3(kBlock), 0, s1, A);
             CK_LAUNCH();
             c->prof_end(FCBO_K_WRITE_MEDIUM, b, s1);
-            c->join(0);
-            c->join(1);
+            if (use_side) {
+                c->join(0);
+                c->join(1);
+            }
         }
     }
     if (!(classes & kLevelHuge)) return;
@@ -519,7 +527,7 @@ void fcbo_context::enumerate_levels()
         ensure(mid_idx, cap_mid, P, 0, stream, mc);
         ensure(fchild, cap_fch, lo + P + 1, lo + 1, stream, mc);
         huge.ensure_members(P, stream, mc);
-        unsigned classes = (next_mid ? kLevelMid : 0u) | (next_huge ? kLevelHuge : 0u);
+        unsigned classes = (next_mid ? kLevelMid : 0u) | (next_huge ? kLevelHuge : 0u) | (next_huge ? kLevelSide : 0u);
         bool redo;
         int redos = 0;
         uint64_t n_children = 0, n_objs = 0;
