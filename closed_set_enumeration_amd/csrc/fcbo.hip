@@ -288,12 +288,15 @@ struct fcbo_context {
     // device or the host; fch (optional) receives fbase + out_a as u32.
     void scan(const uint32_t *a, const uint32_t *b, const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
               uint64_t *out_a, uint64_t *out_b, uint64_t *tot_a, uint64_t *tot_b, uint32_t *fch = nullptr,
-              uint64_t fbase = 0, hipStream_t s = nullptr)
+              uint64_t fbase = 0, hipStream_t s = nullptr, bool small = false)
     {
+        // One workgroup when the length is known to be small, or expected to
+        // be (`small`, with the length in device memory: correct for any
+        // length, only slower if the expectation fails).
         const hipStream_t stream = s ? s : this->stream;
-        if (!n_dev && n_host <= kScanSmallMax) {
-            hipLaunchKernelGGL(k_scan_small, dim3(1), dim3(kScanBlocks), 0, stream, a, b, std::min(n_host, n_cap),
-                               out_a, out_b, tot_a, tot_b, fch, fbase);
+        if ((!n_dev && n_host <= kScanSmallMax) || (n_dev && small)) {
+            hipLaunchKernelGGL(k_scan_small, dim3(1), dim3(kScanBlocks), 0, stream, a, b, n_dev,
+                               n_dev ? n_cap : std::min(n_host, n_cap), out_a, out_b, tot_a, tot_b, fch, fbase);
             CK_LAUNCH();
             return;
         }
@@ -333,8 +336,12 @@ enum { kLevelMid = 1, kLevelHuge = 2, kLevelSide = 4 };
 // than the overlap gains on the deeper levels.
 
 template <int WMC>
-void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigned classes)
+void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigned classes, uint64_t n_huge)
 {
+    // n_huge: the huge parents expected on the level (the previous level's
+    // count of such children); their scans take one workgroup when few
+    const bool huge_small = n_huge <= kScanSmallMax;
+    const bool tests_small = n_huge * (uint64_t)c->m <= kScanSmallMax;
     const unsigned gm = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(1024, div_up(P, kWavesPerBlock)));
     const bool bm = A.huge.bmp != nullptr;
     // local tests; the same pass counts every parent's tests and lists the mid
@@ -363,7 +370,7 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigne
         // test offsets of the huge parents; total -> counters
         b = c->prof_begin(hs);
         c->scan(c->huge.n, nullptr, A.counters + CNT_HUGE, 0, P, c->huge.off, nullptr, A.counters + CNT_THUGE,
-                nullptr, nullptr, 0, hs);
+                nullptr, nullptr, 0, hs, huge_small);
         c->prof_end(FCBO_K_SCAN, b, hs);
         b = c->prof_begin(hs);
         hipLaunchKernelGGL(k_huge_tasks<WMC>, dim3(gm), dim3(kBlock), 0, hs, A);
@@ -401,13 +408,13 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigne
     // sibling offsets of the passing huge tests
     b = c->prof_begin(hs);
     c->scan(c->huge.size, nullptr, A.counters + CNT_THUGE, 0, A.huge.cap, c->huge.sscan, nullptr, nullptr, nullptr,
-            nullptr, 0, hs);
+            nullptr, 0, hs, tests_small);
     c->prof_end(FCBO_K_SCAN, b, hs);
     if (side) c->join(0);
 }
 
 template <int WMC>
-void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigned classes)
+void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigned classes, uint64_t)
 {
     const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(kGridCap, div_up(P, kBlock)));
     // the mid parents' writers run beside the local one (different children)
@@ -422,6 +429,15 @@ void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsign
     hipLaunchKernelGGL(k_local_write<WMC>, dim3(gl), dim3(kBlock), 0, c->stream, A);
     CK_LAUNCH();
     c->prof_end(FCBO_K_WRITE_LOCAL, b);
+    if (classes & kLevelHuge) {  // main stream, beside the mid writers
+        b = c->prof_begin();
+        if (A.huge.bmp)
+            hipLaunchKernelGGL(k_huge_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+        else
+            hipLaunchKernelGGL(k_big_write_list<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
+        CK_LAUNCH();
+        c->prof_end(FCBO_K_WRITE_BIG, b);
+    }
     if constexpr (WMC <= 8) {
         if (mid) {
             b = c->prof_begin(s0);
@@ -438,17 +454,9 @@ void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsign
             }
         }
     }
-    if (!(classes & kLevelHuge)) return;
-    b = c->prof_begin();
-    if (A.huge.bmp)
-        hipLaunchKernelGGL(k_huge_write<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
-    else
-        hipLaunchKernelGGL(k_big_write_list<WMC>, dim3(kGridCap), dim3(kBlock), 0, c->stream, A);
-    CK_LAUNCH();
-    c->prof_end(FCBO_K_WRITE_BIG, b);
 }
 
-typedef void (*level_fn)(fcbo_context *, const LevelArgs &, uint64_t, unsigned);
+typedef void (*level_fn)(fcbo_context *, const LevelArgs &, uint64_t, unsigned, uint64_t);
 
 struct LevelFns {
     level_fn tests, writes;
@@ -530,6 +538,7 @@ void fcbo_context::enumerate_levels()
         unsigned classes = (next_mid ? kLevelMid : 0u) | (next_huge ? kLevelHuge : 0u) | (next_huge ? kLevelSide : 0u);
         bool redo;
         int redos = 0;
+        uint64_t huge_seen = next_huge;  // huge parents counted by the last attempt
         uint64_t n_children = 0, n_objs = 0;
         do {
             redo = false;
@@ -537,7 +546,7 @@ void fcbo_context::enumerate_levels()
             if (redos > 3) throw HipError{FCBO_ERR_DEVICE};
             LevelArgs A = level_args(lo, P, obj_hi);
             if (redos) CK(hipMemsetAsync(A.counters, 0, CNT_N * sizeof(uint64_t), stream));
-            fns.tests(this, A, P, classes);
+            fns.tests(this, A, P, classes, redos ? huge_seen : next_huge);
             hipEvent_t b = prof_begin();
             // child offsets per parent, and the first child of every parent
             scan(nchild, nobj, nullptr, P, P, cbase, obase, A.counters + CNT_CHILDREN, A.counters + CNT_OBJS,
@@ -550,10 +559,11 @@ void fcbo_context::enumerate_levels()
             // device works on while the host prepares the next level.  The write
             // kernels do nothing when the level overflowed or the store has no
             // room; both cases are handled below.
-            fns.writes(this, A, P, classes);
+            fns.writes(this, A, P, classes, 0);
             CK(hipEventSynchronize(ev_counts));
             const uint64_t n_mid = h_counters[CNT_MID] + h_counters[CNT_MIDW];
             const unsigned found = (n_mid ? kLevelMid : 0u) | (h_counters[CNT_HUGE] ? kLevelHuge : 0u);
+            huge_seen = h_counters[CNT_HUGE];
             if (found & ~classes) {  // parents of a class whose kernels did not run
                 classes |= found;
                 ensure(pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
@@ -609,7 +619,7 @@ void fcbo_context::enumerate_levels()
             ensure(loff, cap_loff, k_end + 1, keep_k + 1, stream, mc);
             ensure(objs, cap_o, obj_hi + n_objs, obj_hi, stream, mc);
             ensure(fchild, cap_fch, k_end + 1, keep_k + 1, stream, mc);
-            if (n_children && !had_room) fns.writes(this, level_args(lo, P, obj_hi), P, classes);
+            if (n_children && !had_room) fns.writes(this, level_args(lo, P, obj_hi), P, classes, 0);
         } while (redo);
         ctr ^= 1;
         lo += P;

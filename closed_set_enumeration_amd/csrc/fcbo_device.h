@@ -1859,10 +1859,13 @@ __global__ void __launch_bounds__(kBlock) k_scan_down(const uint32_t *__restrict
 // The same scan in one workgroup of kScanBlocks threads, for short arrays
 // whose length the host knows.
 __global__ void __launch_bounds__(kScanBlocks) k_scan_small(const uint32_t *__restrict__ a,
-                                                            const uint32_t *__restrict__ b, uint64_t n,
-                                                            uint64_t *out_a, uint64_t *out_b, uint64_t *tot_a,
-                                                            uint64_t *tot_b, uint32_t *fch, uint64_t fbase)
+                                                            const uint32_t *__restrict__ b, const uint64_t *n_dev,
+                                                            uint64_t n_arg, uint64_t *out_a, uint64_t *out_b,
+                                                            uint64_t *tot_a, uint64_t *tot_b, uint32_t *fch,
+                                                            uint64_t fbase)
 {
+    // n_dev: the length in device memory, at most n_arg; else n_arg itself
+    const uint64_t n = n_dev ? (*n_dev < n_arg ? *n_dev : n_arg) : n_arg;
     __shared__ uint64_t s_w[kScanBlocks / kWave];
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     auto block_scan = [&](uint64_t v, uint64_t &total) -> uint64_t {
