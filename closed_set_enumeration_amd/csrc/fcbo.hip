@@ -71,6 +71,9 @@ void ensure(T *&p, uint64_t &cap, uint64_t need, uint64_t keep, hipStream_t s, u
 }
 
 constexpr int kGridCap = 4096;  // blocks for grid-stride wave kernels
+// Average children per concept from which the order passes take a wavefront
+// per concept (measured: 8 against 4 and 16 on both full-size workloads).
+constexpr uint64_t kOrderWaveFanout = 8;
 
 // Device storage of one BigSet (see fcbo_device.h).
 struct BigStore {
@@ -641,17 +644,30 @@ void fcbo_context::order_concepts()
     std::vector<uint64_t> lev_lo(nlev + 1, 0);
     for (size_t l = 0; l < nlev; ++l) lev_lo[l + 1] = lev_lo[l] + lev_concepts[l];
     auto grid = [](uint64_t n) { return (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(n, kBlock))); };
+    auto wgrid = [](uint64_t n) {
+        return (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(n, kWavesPerBlock)));
+    };
+    // levels whose concepts average many children take a wavefront per concept
+    auto wide_level = [&](size_t l) { return l + 1 < nlev && lev_concepts[l + 1] >= kOrderWaveFanout * lev_concepts[l]; };
     hipEvent_t b = prof_begin();
     order_launches = 0;
     for (size_t l = nlev; l-- > 0;) {  // sizes, deepest level first
-        hipLaunchKernelGGL(k_subtree_size, dim3(grid(lev_concepts[l])), dim3(kBlock), 0, stream,
-                           (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
+        if (wide_level(l))
+            hipLaunchKernelGGL(k_subtree_size_wave, dim3(wgrid(lev_concepts[l])), dim3(kBlock), 0, stream,
+                               (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
+        else
+            hipLaunchKernelGGL(k_subtree_size, dim3(grid(lev_concepts[l])), dim3(kBlock), 0, stream,
+                               (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
         CK_LAUNCH();
         ++order_launches;
     }
     for (size_t l = 0; l + 1 < nlev; ++l) {  // positions, root level first
-        hipLaunchKernelGGL(k_child_position, dim3(grid(lev_concepts[l])), dim3(kBlock), 0, stream,
-                           (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
+        if (wide_level(l))
+            hipLaunchKernelGGL(k_child_position_wave, dim3(wgrid(lev_concepts[l])), dim3(kBlock), 0, stream,
+                               (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
+        else
+            hipLaunchKernelGGL(k_child_position, dim3(grid(lev_concepts[l])), dim3(kBlock), 0, stream,
+                               (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
         CK_LAUNCH();
         ++order_launches;
     }

@@ -1954,6 +1954,47 @@ __global__ void __launch_bounds__(kBlock) k_child_position(const uint32_t *__res
     }
 }
 
+// The same two passes for levels whose concepts have many children (the top
+// of the tree): one wavefront per concept.  Sizes are summed across the
+// lanes; positions come from an exclusive scan of the sizes taken in
+// descending child order, 64 children a step.
+__global__ void __launch_bounds__(kBlock) k_subtree_size_wave(const uint32_t *__restrict__ fchild, uint64_t lo,
+                                                               uint64_t P, uint32_t *__restrict__ rank)
+{
+    const int lane = lane_id();
+    for (uint64_t p = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; p < P;
+         p += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t c = lo + p;
+        const uint32_t k0 = fchild[c], k1 = fchild[c + 1];
+        uint32_t s = 0;
+        for (uint32_t k = k0 + (uint32_t)lane; k < k1; k += kWave) s += rank[k];
+        s = wave_sum(s);
+        if (lane == 0) rank[c] = s + 1u;
+    }
+}
+
+__global__ void __launch_bounds__(kBlock) k_child_position_wave(const uint32_t *__restrict__ fchild, uint64_t lo,
+                                                                 uint64_t P, uint32_t *__restrict__ rank)
+{
+    const int lane = lane_id();
+    for (uint64_t p = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; p < P;
+         p += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t c = lo + p;
+        const uint32_t k0 = fchild[c], k1 = fchild[c + 1];
+        uint32_t run = (c == 0 ? 0u : rank[c]) + 1u;
+        for (uint32_t top = k1; top > k0;) {
+            const uint32_t n = top - k0 < (uint32_t)kWave ? top - k0 : (uint32_t)kWave;
+            const bool ok = (uint32_t)lane < n;
+            const uint32_t k = top - 1u - (uint32_t)lane;  // lane 0 takes the last child
+            const uint32_t sz = ok ? rank[k] : 0u;
+            const uint32_t ex = wave_excl_scan(sz);
+            if (ok) rank[k] = run + ex;
+            run += wave_sum(sz);
+            top -= n;
+        }
+    }
+}
+
 // perm[position] = concept
 __global__ void __launch_bounds__(kBlock) k_invert(const uint32_t *__restrict__ rank, uint64_t K,
                                                     uint32_t *__restrict__ perm)
