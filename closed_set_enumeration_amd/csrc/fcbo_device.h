@@ -504,7 +504,9 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     __shared__ uint64_t s_rows[kW][kSmallMax * WMC];  // the group's object rows, slot-major
     __shared__ uint64_t s_b[kW][CH * WMC];            // the chunk's intents, padding bits past M set
     __shared__ uint32_t s_seg[kW][kWave];             // per group parent: first slot | objects << 8
-    __shared__ uint32_t s_run[kW][2 * kWave];         // per group parent: children, their objects
+    // per group parent: children, their objects; before the tests, per (parent,
+    // word) lane the first attributes of the objects (below)
+    __shared__ __align__(8) uint32_t s_run[kW][2 * kWave];
     __shared__ uint8_t s_owner[kW][kWave];            // group parent whose slots start here
     __shared__ uint8_t s_mark[kW][kWave];             // per round: (parent, word) lane whose candidates start here
     __shared__ uint64_t s_sum[5][kW];                 // level counters, per wavefront
@@ -512,8 +514,9 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = words_of<WMC>(A.wm);
     const int gmax = kWave / wm;  // parents per group: one lane per (parent, word)
-    // this lane's share of the level counters: tests, item pairs, objects of
-    // local and of mid parents, list entries the huge tests would scan
+    // the wavefront's level counters (uniform, summed once per chunk): tests,
+    // item pairs, objects of local and of mid parents, list entries the huge
+    // tests would scan
     uint64_t n_tests = 0, n_pairs = 0, n_local_objs = 0, n_mid_objs = 0, n_big_scan = 0;
     uint64_t *R = s_rows[wv];
     const uint32_t *R32 = (const uint32_t *)R;
@@ -523,26 +526,36 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
     uint8_t *OWN = s_owner[wv];
     uint8_t *MARK = s_mark[wv];
     const uint64_t rstride = 4 + (uint64_t)A.wm;
-    // Record slots are reserved 64 at a time per wavefront; a round's passing
-    // children go to one chunk of slots (a chunk that cannot hold them is closed).
-    // The wavefront's stripe owns slots [rlo, rhi).
+    // Record slots are reserved 64 at a time per wavefront (a chunk) and filled
+    // in order: a round's passing children take the rest of the current chunk
+    // and go on at the start of a new one, so only a wavefront's last chunk is
+    // left part-filled.  The wavefront's stripe owns slots [rlo, rhi).
     const int stripe = (int)(((uint64_t)blockIdx.x * kW + wv) % kRecStripes);
     const uint64_t rlo = (uint64_t)stripe * A.lrec_region, rhi = rlo + A.lrec_region;
     uint64_t rchunk = ~0ull;  // first slot of the current record chunk
     uint32_t fill = kWave;    // slots used in it
-    auto reserve = [&](uint32_t n) -> uint64_t {
-        if (fill + n > (uint32_t)kWave) {
-            if (rchunk != ~0ull && lane == 0 && rchunk < rhi) A.lfill[rchunk / kWave] = fill;
-            uint64_t c = 0;
-            if (lane == 0)
-                c = atomicAdd((unsigned long long *)&A.counters[CNT_LOCREC + stripe * kCntPad], (unsigned long long)kWave);
-            rchunk = rlo + uniform64(c);
-            fill = 0;
-            if (rchunk + kWave > rhi && lane == 0) A.counters[CNT_OVERFLOW] = 1;
+    auto next_chunk = [&]() {
+        if (rchunk != ~0ull && lane == 0 && rchunk < rhi) A.lfill[rchunk / kWave] = fill;
+        uint64_t c = 0;
+        if (lane == 0)
+            c = atomicAdd((unsigned long long *)&A.counters[CNT_LOCREC + stripe * kCntPad], (unsigned long long)kWave);
+        rchunk = rlo + uniform64(c);
+        fill = 0;
+        if (rchunk + kWave > rhi && lane == 0) A.counters[CNT_OVERFLOW] = 1;
+    };
+    // slot of record k of a round's n (uniform n in [1, 64], k < n)
+    auto reserve = [&](uint32_t n, uint32_t k) -> uint64_t {
+        if (fill == (uint32_t)kWave) next_chunk();
+        const uint32_t room = (uint32_t)kWave - fill;
+        const uint64_t at = rchunk + fill + k;
+        if (n <= room) {
+            fill += n;
+            return at;
         }
-        const uint64_t at = rchunk + fill;
-        fill += n;
-        return at;
+        fill = kWave;
+        next_chunk();
+        fill = n - room;
+        return k < room ? at : rchunk + (k - room);
     };
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i < CNT_N; i += blockDim.x) A.counters_next[i] = 0;
@@ -581,13 +594,13 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
                 for (int u = 0; u < wm; ++u) nt += (uint32_t)__popcll(~SB[lane * wm + u] & above_mask(y, u));
             const bool is_huge = lane < nq && sz > (uint64_t)A.mid_max;
             const bool is_mid = lane < nq && !is_huge && !act;
-            if (lane < nq) {
-                n_tests += nt;
-                n_pairs += (uint64_t)(A.m - 1 - y);
-                if (act) n_local_objs += sz;
-                if (is_mid) n_mid_objs += sz;
-                if (is_huge) n_big_scan += sz * nt;
-            }
+            // per chunk the sums but the last fit 32 bits (at most 64 parents of
+            // at most M tests and mid_max objects each)
+            n_tests += wave_sum(nt);
+            n_pairs += wave_sum(lane < nq ? (uint32_t)(A.m - 1 - y) : 0u);
+            n_local_objs += wave_sum(act ? (uint32_t)sz : 0u);
+            n_mid_objs += wave_sum(is_mid ? (uint32_t)sz : 0u);
+            n_big_scan += wave_sum64(is_huge ? sz * nt : 0ull);
             const BigSet &S = A.huge;
             const uint64_t hb = __ballot(is_huge);
             if (hb) {
@@ -629,30 +642,55 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
             const bool in = lane >= s && lane < s + gmax && lane < nq && pre + (uint32_t)a - base <= (uint32_t)kSmallMax;
             const int e = s + __popcll(__ballot(in));
             const int S = (int)(lane_value(pre, e - 1) + lane_value((uint32_t)a, e - 1) - base);
+            // FIRST[(q, u)]: the first attributes outside B of the objects of
+            // group parent q that fall in word u (one bit per object); it lives
+            // in the RUN table until the candidates are known
+            uint64_t *FIRST = (uint64_t *)RUN;
+            FIRST[lane] = 0;
             if (in) {
                 SEG[lane - s] = (pre - base) | ((uint32_t)a << 8);
                 if (a > 0) OWN[pre - base] = (uint8_t)(lane - s);
-                RUN[2 * (lane - s)] = 0;
-                RUN[2 * (lane - s) + 1] = 0;
             }
             const uint64_t starts = wave_or(in && a > 0 ? (1ull << (pre - base)) : 0ull);
             wave_sync();
             {
-                // object slots: stage the row
+                // object slots: stage the row, mark its first attribute outside B
                 const uint64_t below = starts & upto_mask(lane);
                 const int st = below ? 63 - __clzll((long long)below) : 0;
                 const int q = OWN[st];
                 const uint64_t oq = __shfl(o0, s + q);
                 if (lane < S) {
                     const uint64_t g = A.objs[oq + (uint64_t)(lane - st)];
+                    uint64_t row[WMC];
 #pragma unroll
-                    for (int u = 0; u < WMC; ++u)
-                        if (u < wm) R[lane * WMC + u] = A.rows[g * A.wm + u];
+                    for (int u = 0; u < WMC; ++u) row[u] = (u < wm) ? A.rows[g * A.wm + u] : 0ull;
+                    int fu = -1;
+                    uint64_t fx = 0;
+#pragma unroll
+                    for (int u = WMC - 1; u >= 0; --u) {
+                        if (u < wm) {
+                            R[lane * WMC + u] = row[u];
+                            const uint64_t nb = row[u] & ~SB[(s + q) * wm + u];
+                            if (nb) {
+                                fu = u;
+                                fx = nb;
+                            }
+                        }
+                    }
+                    if (fu >= 0) atomicOr((unsigned long long *)&FIRST[q * wm + fu], (unsigned long long)(fx & (0ull - fx)));
                 }
             }
             wave_sync();
             // (parent, word) lanes: U = OR of the parent's staged rows, candidate
-            // bits, their place in the group's list
+            // bits, their place in the group's list.
+            //
+            // A candidate j carried by a single object i of A has c_j = {i} and
+            // D = row i, and it passes exactly when j is the first attribute of
+            // that row outside B.  So of the candidates carried once only the
+            // objects' first attributes can pass; the others are decided
+            // without a test and leave the list.  The candidates kept: those
+            // carried at least twice (TWO), the objects' first attributes, and
+            // j0 (carried by none).
             const int G = e - s;
             const int pq = lane / wm < G ? lane / wm : G - 1;
             const int pu = lane - pq * wm;
@@ -663,13 +701,23 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
             if (lane < G * wm) {
                 const uint32_t sgq = SEG[pq];
                 const int fq = (int)(sgq & 0xFFu), nq = (int)(sgq >> 8);
-                for (int i = 0; i < nq; ++i) x |= R[(fq + i) * WMC + pu];
+                uint64_t two = 0;
+                for (int i = 0; i < nq; ++i) {
+                    const uint64_t r = R[(fq + i) * WMC + pu];
+                    two |= x & r;
+                    x |= r;
+                }
                 if (actq) {
-                    x &= ~SB[(s + pq) * wm + pu] & above_mask(yq, pu);
+                    x &= ~SB[(s + pq) * wm + pu] & above_mask(yq, pu) & (two | FIRST[lane]);
                     if (j0q >= 0 && (j0q >> 6) == pu) x |= 1ull << (j0q & 63);
                 } else {
                     x = 0;
                 }
+            }
+            wave_sync();
+            if (in) {
+                RUN[2 * (lane - s)] = 0;
+                RUN[2 * (lane - s) + 1] = 0;
             }
             const uint32_t cnt = (uint32_t)__popcll(x);
             const uint32_t pos = wave_excl_scan(cnt);
@@ -757,9 +805,8 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
                 const uint32_t ex = wave_excl_scan(sz);
                 const uint32_t exh = __shfl(ex, hl);
                 if (bal) {
-                    const uint64_t at = reserve((uint32_t)__popcll(bal));
+                    const uint64_t slot = reserve((uint32_t)__popcll(bal), lanes_below(bal));
                     if (pass) {
-                        const uint64_t slot = at + lanes_below(bal);
                         if (slot < rhi) {
                             const uint32_t rank = RUN[2 * qc] + (uint32_t)__popcll(bal & inseg & ~(1ull << lane));
                             const uint32_t objoff = RUN[2 * qc + 1] + (ex - exh);
@@ -790,13 +837,11 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArg
         }
     }
     if (rchunk != ~0ull && lane == 0 && rchunk < rhi) A.lfill[rchunk / kWave] = fill;
-    // level counters: wavefront sums, then one atomic per workgroup and counter
-    uint64_t v[5] = {n_tests, n_pairs, n_local_objs, n_mid_objs, n_big_scan};
+    // level counters: one atomic per workgroup and counter
+    const uint64_t v[5] = {n_tests, n_pairs, n_local_objs, n_mid_objs, n_big_scan};
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        v[i] = wave_sum64(v[i]);
+    for (int i = 0; i < 5; ++i)
         if (lane == 0) s_sum[i][wv] = v[i];
-    }
     __syncthreads();
     if (threadIdx.x < 5) {
         uint64_t sum = 0;
