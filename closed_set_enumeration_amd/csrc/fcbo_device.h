@@ -496,8 +496,12 @@ __device__ __forceinline__ void wave_sync()
 // Bits 0 .. b of a word (b in [0, 63]).
 __device__ __forceinline__ uint64_t upto_mask(int b) { return (2ull << b) - 1ull; }
 
+// Intents of up to four words leave LDS for more than five wavefronts per SIMD;
+// the register budget of six (80 VGPRs, a few spilled bytes at four words) is
+// faster there than five without spills.
 template <int WMC>
-__global__ void __launch_bounds__(LocalCfg<WMC>::kThreads) k_local_test(LevelArgs A)
+__global__ void __launch_bounds__(LocalCfg<WMC>::kThreads)
+    __attribute__((amdgpu_waves_per_eu(WMC <= 4 ? 6 : 1))) k_local_test(LevelArgs A)
 {
     constexpr int kW = LocalCfg<WMC>::kWaves;
     constexpr int CH = LocalCfg<WMC>::kChunk;
