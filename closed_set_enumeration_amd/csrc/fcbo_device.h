@@ -1487,7 +1487,10 @@ __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
             uint32_t need = 0;
             for (int ri = r; ri < r1; ++ri)
                 if ((lane_value64(w1, ri) >> 32) != 0) need |= 1u << ((lane_value64(w0, ri) >> 32) >> 6);
-            // four chunks of 64 objects per step, so that their loads overlap
+            // four chunks of 64 objects per step, so that their loads overlap;
+            // per needed intent word, that word of the four rows, then the
+            // records whose attribute lies in it (each record's objects still
+            // come out in list order)
             for (uint64_t o = l0; o < l1; o += 4 * kWave) {
                 uint32_t g[4];
                 bool valid[4];
@@ -1497,26 +1500,23 @@ __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
                     valid[c4] = idx < l1;
                     g[c4] = valid[c4] ? A.objs[idx] : 0u;
                 }
-                uint64_t row[4][WMC];
+                for (uint32_t nm = need; nm; nm &= nm - 1u) {
+                    const int u = __ffs(nm) - 1;
+                    uint64_t row[4];
 #pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4)
+                    for (int c4 = 0; c4 < 4; ++c4) row[c4] = valid[c4] ? A.rows[(uint64_t)g[c4] * A.wm + u] : 0ull;
+                    for (int ri = r; ri < r1; ++ri) {
+                        if ((lane_value64(w1, ri) >> 32) == 0) continue;  // C empty (the bottom child)
+                        const int j = (int)(lane_value64(w0, ri) >> 32);
+                        if ((j >> 6) != u) continue;
 #pragma unroll
-                    for (int u = 0; u < WMC; ++u)
-                        row[c4][u] = (valid[c4] && u < wm && ((need >> u) & 1u)) ? A.rows[(uint64_t)g[c4] * A.wm + u] : 0ull;
-                for (int ri = r; ri < r1; ++ri) {
-                    if ((lane_value64(w1, ri) >> 32) == 0) continue;  // C empty (the bottom child)
-                    const int j = (int)(lane_value64(w0, ri) >> 32);
-#pragma unroll
-                    for (int c4 = 0; c4 < 4; ++c4) {
-                        uint64_t word = 0;
-#pragma unroll
-                        for (int u = 0; u < WMC; ++u)
-                            if (u == (j >> 6)) word = row[c4][u];
-                        const bool in = (word >> (j & 63)) & 1ull;
-                        const uint64_t bal = __ballot(in);
-                        const uint64_t at = lane_value64(qo, ri);
-                        if (in) A.objs[at + __popcll(bal & below_mask(lane))] = g[c4];
-                        if (lane == ri) qo += (uint64_t)__popcll(bal);
+                        for (int c4 = 0; c4 < 4; ++c4) {
+                            const bool in = (row[c4] >> (j & 63)) & 1ull;
+                            const uint64_t bal = __ballot(in);
+                            const uint64_t at = lane_value64(qo, ri);
+                            if (in) A.objs[at + __popcll(bal & below_mask(lane))] = g[c4];
+                            if (lane == ri) qo += (uint64_t)__popcll(bal);
+                        }
                     }
                 }
             }
