@@ -448,7 +448,7 @@ void launch_level_writes(fcbo_context *c, const LevelArgs &A, uint64_t P, unsign
             CK_LAUNCH();
             c->prof_end(FCBO_K_WRITE_MEDIUM, b, s0);
             b = c->prof_begin(s1);
-            hipLaunchKernelGGL(k_mid_write_wide, dim3(kGridCap), dim3(kBlock), 0, s1, A);
+            hipLaunchKernelGGL(k_mid_write_wide<WMC>, dim3(kGridCap), dim3(kBlock), 0, s1, A);
             CK_LAUNCH();
             c->prof_end(FCBO_K_WRITE_MEDIUM, b, s1);
             if (use_side) {

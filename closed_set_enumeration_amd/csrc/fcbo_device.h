@@ -1417,20 +1417,104 @@ __global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
     if (next_mid && lane == 0) atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_MID], (unsigned long long)next_mid);
 }
 
-// Children of the narrow mid parents.  A wavefront takes kMidRun consecutive records
-// of a stripe (a parent's records are consecutive, in rank order): their
+constexpr int kMidRun = 8;  // records per item of the mid writers
+
+// One item of the mid parents' child records: nr <= kMidRun consecutive
+// records at rec0 (a parent's records are consecutive, in rank order).  Their
 // intents, cursors and list bounds come from the records, and every run of
 // records with the same parent shares one pass over the parent's object list,
-// in which each object's row is read once and tested for the attribute j of
-// every record of the run (the objects of C_j, ascending).
-constexpr int kMidRun = 8;
+// in which each object's row is read once per needed intent word and tested
+// for the attribute j of every record of the run (the objects of C_j,
+// ascending).
+template <int WMC>
+__device__ __forceinline__ void mid_write_item(const LevelArgs &A, const uint64_t *rec0, int nr)
+{
+    const int lane = lane_id();
+    const int wm = words_of<WMC>(A.wm);
+    const uint64_t rstride = 4 + (uint64_t)A.wm;
+    // lane r < nr: record r's header, child and list start
+    uint64_t w0 = 0, w1 = 0, w2 = 0;
+    if (lane < nr) {
+        const uint64_t *rec = rec0 + (uint64_t)lane * rstride;
+        w0 = rec[0];
+        w1 = rec[1];
+        w2 = rec[2];
+    }
+    const uint64_t pl = w0 & 0xFFFFFFFFull;
+    uint64_t child = 0, qo = 0;
+    if (lane < nr) {
+        child = A.child_lo + A.cbase[pl] + (w1 & 0xFFFFFFFFull);
+        qo = A.child_obj_lo + A.obase[pl] + w2;
+    }
+    // intents: one lane per (record, word)
+    for (int x0 = 0; x0 < nr * wm; x0 += kWave) {
+        const int x = x0 + lane;
+        int r = x / wm;
+        r = r < nr ? r : nr - 1;
+        const uint64_t ch = __shfl(child, r);
+        if (x < nr * wm) A.intents[ch * A.wm + (x - r * wm)] = rec0[(uint64_t)r * rstride + 4 + (x - r * wm)];
+    }
+    if (lane < nr) {
+        const uint32_t cnt = (uint32_t)(w1 >> 32);
+        A.cursor[child] = (int32_t)(w0 >> 32);
+        A.loff[child] = qo;
+        A.loff[child + 1] = qo + cnt;
+    }
+    // extent lists, one pass over each parent's list per run of records
+    for (int r = 0; r < nr;) {
+        const uint64_t p = lane_value64(w0, r) & 0xFFFFFFFFull;
+        int r1 = r + 1;
+        while (r1 < nr && (lane_value64(w0, r1) & 0xFFFFFFFFull) == p) ++r1;
+        const uint64_t c0 = A.lo + p;
+        const uint64_t l0 = A.loff[c0], l1 = A.loff[c0 + 1];
+        // intent words holding the attributes of the run (C non-empty)
+        uint32_t need = 0;
+        for (int ri = r; ri < r1; ++ri)
+            if ((lane_value64(w1, ri) >> 32) != 0) need |= 1u << ((lane_value64(w0, ri) >> 32) >> 6);
+        // four chunks of 64 objects per step, so that their loads overlap;
+        // per needed intent word, that word of the four rows, then the
+        // records whose attribute lies in it (each record's objects still
+        // come out in list order)
+        for (uint64_t o = l0; o < l1; o += 4 * kWave) {
+            uint32_t g[4];
+            bool valid[4];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const uint64_t idx = o + (uint64_t)(c4 * kWave + lane);
+                valid[c4] = idx < l1;
+                g[c4] = valid[c4] ? A.objs[idx] : 0u;
+            }
+            for (uint32_t nm = need; nm; nm &= nm - 1u) {
+                const int u = __ffs(nm) - 1;
+                uint64_t row[4];
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) row[c4] = valid[c4] ? A.rows[(uint64_t)g[c4] * A.wm + u] : 0ull;
+                for (int ri = r; ri < r1; ++ri) {
+                    if ((lane_value64(w1, ri) >> 32) == 0) continue;  // C empty (the bottom child)
+                    const int j = (int)(lane_value64(w0, ri) >> 32);
+                    if ((j >> 6) != u) continue;
+#pragma unroll
+                    for (int c4 = 0; c4 < 4; ++c4) {
+                        const bool in = (row[c4] >> (j & 63)) & 1ull;
+                        const uint64_t bal = __ballot(in);
+                        const uint64_t at = lane_value64(qo, ri);
+                        if (in) A.objs[at + __popcll(bal & below_mask(lane))] = g[c4];
+                        if (lane == ri) qo += (uint64_t)__popcll(bal);
+                    }
+                }
+            }
+        }
+        r = r1;
+    }
+}
 
+// Children of the narrow mid parents: a wavefront takes kMidRun consecutive
+// records of a stripe at a time (mid_write_item).
 template <int WMC>
 __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
 {
     const int lane = lane_id();
     if (A.counters[CNT_OVERFLOW] || !store_has_room(A)) return;
-    const int wm = words_of<WMC>(A.wm);
     const uint64_t rstride = 4 + (uint64_t)A.wm;
     const uint64_t nw = (uint64_t)gridDim.x * kWavesPerBlock;
     const uint64_t w = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
@@ -1447,115 +1531,25 @@ __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
         const uint64_t nst = lane_value64(counts, st);
         if (k0 >= nst) continue;
         const int nr = (int)(nst - k0 < (uint64_t)kMidRun ? nst - k0 : (uint64_t)kMidRun);
-        const uint64_t *rec0 = A.mrec + ((uint64_t)st * A.mrec_region + k0) * rstride;
-        // lane r < nr: record r's header, child and list start
-        uint64_t w0 = 0, w1 = 0, w2 = 0;
-        if (lane < nr) {
-            const uint64_t *rec = rec0 + (uint64_t)lane * rstride;
-            w0 = rec[0];
-            w1 = rec[1];
-            w2 = rec[2];
-        }
-        const uint64_t pl = w0 & 0xFFFFFFFFull;
-        uint64_t child = 0, qo = 0;
-        if (lane < nr) {
-            child = A.child_lo + A.cbase[pl] + (w1 & 0xFFFFFFFFull);
-            qo = A.child_obj_lo + A.obase[pl] + w2;
-        }
-        // intents: one lane per (record, word)
-        for (int x0 = 0; x0 < nr * wm; x0 += kWave) {
-            const int x = x0 + lane;
-            int r = x / wm;
-            r = r < nr ? r : nr - 1;
-            const uint64_t ch = __shfl(child, r);
-            if (x < nr * wm) A.intents[ch * A.wm + (x - r * wm)] = rec0[(uint64_t)r * rstride + 4 + (x - r * wm)];
-        }
-        if (lane < nr) {
-            const uint32_t cnt = (uint32_t)(w1 >> 32);
-            A.cursor[child] = (int32_t)(w0 >> 32);
-            A.loff[child] = qo;
-            A.loff[child + 1] = qo + cnt;
-        }
-        // extent lists, one pass over each parent's list per run of records
-        for (int r = 0; r < nr;) {
-            const uint64_t p = lane_value64(w0, r) & 0xFFFFFFFFull;
-            int r1 = r + 1;
-            while (r1 < nr && (lane_value64(w0, r1) & 0xFFFFFFFFull) == p) ++r1;
-            const uint64_t c0 = A.lo + p;
-            const uint64_t l0 = A.loff[c0], l1 = A.loff[c0 + 1];
-            // intent words holding the attributes of the run (C non-empty)
-            uint32_t need = 0;
-            for (int ri = r; ri < r1; ++ri)
-                if ((lane_value64(w1, ri) >> 32) != 0) need |= 1u << ((lane_value64(w0, ri) >> 32) >> 6);
-            // four chunks of 64 objects per step, so that their loads overlap;
-            // per needed intent word, that word of the four rows, then the
-            // records whose attribute lies in it (each record's objects still
-            // come out in list order)
-            for (uint64_t o = l0; o < l1; o += 4 * kWave) {
-                uint32_t g[4];
-                bool valid[4];
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) {
-                    const uint64_t idx = o + (uint64_t)(c4 * kWave + lane);
-                    valid[c4] = idx < l1;
-                    g[c4] = valid[c4] ? A.objs[idx] : 0u;
-                }
-                for (uint32_t nm = need; nm; nm &= nm - 1u) {
-                    const int u = __ffs(nm) - 1;
-                    uint64_t row[4];
-#pragma unroll
-                    for (int c4 = 0; c4 < 4; ++c4) row[c4] = valid[c4] ? A.rows[(uint64_t)g[c4] * A.wm + u] : 0ull;
-                    for (int ri = r; ri < r1; ++ri) {
-                        if ((lane_value64(w1, ri) >> 32) == 0) continue;  // C empty (the bottom child)
-                        const int j = (int)(lane_value64(w0, ri) >> 32);
-                        if ((j >> 6) != u) continue;
-#pragma unroll
-                        for (int c4 = 0; c4 < 4; ++c4) {
-                            const bool in = (row[c4] >> (j & 63)) & 1ull;
-                            const uint64_t bal = __ballot(in);
-                            const uint64_t at = lane_value64(qo, ri);
-                            if (in) A.objs[at + __popcll(bal & below_mask(lane))] = g[c4];
-                            if (lane == ri) qo += (uint64_t)__popcll(bal);
-                        }
-                    }
-                }
-            }
-            r = r1;
-        }
+        mid_write_item<WMC>(A, A.mrec + ((uint64_t)st * A.mrec_region + k0) * rstride, nr);
     }
 }
 
-// Children of the wide mid parents, one wavefront per record: the parent's
-// list is scanned for the objects having j, 256 entries a step.  (Their lists
-// are long, so a record is enough work for a wavefront.)
+// Children of the wide mid parents: their records (one block of consecutive
+// records per parent, in rank order) taken kMidRun at a time as in k_mid_write,
+// so the records of a parent share the passes over its long list.
+template <int WMC>
 __global__ void __launch_bounds__(kBlock) k_mid_write_wide(LevelArgs A)
 {
-    const int lane = lane_id();
     if (A.counters[CNT_OVERFLOW] || !store_has_room(A)) return;
     const uint64_t nrec = A.counters[CNT_WIDEREC];
     const uint64_t rstride = 4 + (uint64_t)A.wm;
-    for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; i < nrec;
-         i += (uint64_t)gridDim.x * kWavesPerBlock) {
-        const uint64_t *rec = A.wrec + i * rstride;
-        const uint64_t w0 = rec[0], w1 = rec[1];
-        const uint64_t p = w0 & 0xFFFFFFFFull;
-        const int j = (int)(w0 >> 32);
-        const uint32_t cnt = (uint32_t)(w1 >> 32);
-        const uint64_t c0 = A.lo + p;
-        const uint64_t child = A.child_lo + A.cbase[p] + (w1 & 0xFFFFFFFFull);
-        const uint64_t obeg = A.child_obj_lo + A.obase[p] + rec[2];
-        for (int u = lane; u < A.wm; u += kWave) A.intents[child * A.wm + u] = rec[4 + u];
-        if (lane == 0) {
-            A.cursor[child] = j;
-            A.loff[child] = obeg;
-            A.loff[child + 1] = obeg + cnt;
-        }
-        if (cnt == 0) continue;
-        uint64_t qo = obeg;
-        scan_list_for_attr(A, A.loff[c0], A.loff[c0 + 1], j, [&](bool in, uint32_t g, uint64_t bal) {
-            if (in) A.objs[qo + __popcll(bal & below_mask(lane))] = g;
-            qo += __popcll(bal);
-        });
+    const uint64_t items = (nrec + kMidRun - 1) / kMidRun;
+    for (uint64_t f = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; f < items;
+         f += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t k0 = f * kMidRun;
+        const int nr = (int)(nrec - k0 < (uint64_t)kMidRun ? nrec - k0 : (uint64_t)kMidRun);
+        mid_write_item<WMC>(A, A.wrec + k0 * rstride, nr);
     }
 }
 
