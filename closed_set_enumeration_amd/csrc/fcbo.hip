@@ -357,7 +357,8 @@ void launch_level_tests(fcbo_context *c, const LevelArgs &A, uint64_t P, unsigne
         const uint64_t want = (uint64_t)c->n_cu * kLocalChunksPerCu;
         while (L.chunk / 2 >= kLocalMinChunk && div_up(P, (uint64_t)L.chunk) < want) L.chunk /= 2;
         const uint64_t chunks = div_up(P, (uint64_t)L.chunk);
-        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(chunks, kW)));
+        const uint64_t per_block = (uint64_t)kW * LocalCfg<WMC>::kChunksPerWave;
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(chunks, per_block)));
         hipLaunchKernelGGL(k_local_test<WMC>, dim3(g), dim3(LocalCfg<WMC>::kThreads), 0, c->stream, L);
     }
     CK_LAUNCH();

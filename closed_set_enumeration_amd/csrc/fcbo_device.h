@@ -455,11 +455,20 @@ __device__ __forceinline__ uint64_t wave_or(uint64_t v)
 constexpr int kLocalChunksPerCu = 16;
 constexpr int kLocalMinChunk = 8;
 
+// Occupancy: the per-wavefront LDS is the staged rows (64 x WMC words) plus the
+// chunk's intents (kChunk x WMC words).  Intents of 5 to 8 words take chunks of
+// 16 parents, two per wavefront, so that a workgroup's LDS leaves room for
+// seven wavefronts per SIMD; the register budget that allows (72 VGPRs, a few
+// dozen bytes spilled) is faster on them than five wavefronts without spills
+// (ctx50000x400: local test 2.30 -> 1.95 ms).  Up to four words the 64-parent
+// chunk leaves room for eight; seven (72 VGPRs) measured best there.
 template <int WMC>
 struct LocalCfg {
     static constexpr int kWaves = WMC <= 8 ? kWavesPerBlock : 1;  // wavefronts per block
     static constexpr int kThreads = kWave * kWaves;
-    static constexpr int kChunk = WMC <= 8 ? kWave : 512 / WMC;    // parents per chunk
+    static constexpr int kChunk = WMC <= 4 ? kWave : WMC <= 8 ? 16 : 512 / WMC;  // parents per chunk
+    static constexpr int kChunksPerWave = WMC <= 4 ? 1 : WMC <= 8 ? 2 : 1;      // at launch
+    static constexpr int kWavesPerEu = WMC <= 8 ? 7 : 1;                       // occupancy asked for
 };
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t v)
@@ -496,12 +505,9 @@ __device__ __forceinline__ void wave_sync()
 // Bits 0 .. b of a word (b in [0, 63]).
 __device__ __forceinline__ uint64_t upto_mask(int b) { return (2ull << b) - 1ull; }
 
-// Intents of up to four words leave LDS for more than five wavefronts per SIMD;
-// the register budget of six (80 VGPRs, a few spilled bytes at four words) is
-// faster there than five without spills.
 template <int WMC>
 __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads)
-    __attribute__((amdgpu_waves_per_eu(WMC <= 4 ? 6 : 1))) k_local_test(LevelArgs A)
+    __attribute__((amdgpu_waves_per_eu(LocalCfg<WMC>::kWavesPerEu))) k_local_test(LevelArgs A)
 {
     constexpr int kW = LocalCfg<WMC>::kWaves;
     constexpr int CH = LocalCfg<WMC>::kChunk;
