@@ -461,14 +461,15 @@ constexpr int kLocalMinChunk = 8;
 // seven wavefronts per SIMD; the register budget that allows (72 VGPRs, a few
 // dozen bytes spilled) is faster on them than five wavefronts without spills
 // (ctx50000x400: local test 2.30 -> 1.95 ms).  Up to four words the 64-parent
-// chunk leaves room for eight; seven (72 VGPRs) measured best there.
+// chunk leaves room for eight; seven (72 VGPRs) measured best there.  Eight
+// words cannot be held to the budget of seven and keep the compiler's choice.
 template <int WMC>
 struct LocalCfg {
     static constexpr int kWaves = WMC <= 8 ? kWavesPerBlock : 1;  // wavefronts per block
     static constexpr int kThreads = kWave * kWaves;
     static constexpr int kChunk = WMC <= 4 ? kWave : WMC <= 8 ? 16 : 512 / WMC;  // parents per chunk
     static constexpr int kChunksPerWave = WMC <= 4 ? 1 : WMC <= 8 ? 2 : 1;      // at launch
-    static constexpr int kWavesPerEu = WMC <= 8 ? 7 : 1;                       // occupancy asked for
+    static constexpr int kWavesPerEu = WMC <= 7 ? 7 : 1;                       // occupancy asked for
 };
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t v)
