@@ -14,8 +14,9 @@ and the CPU oracle timed on a bounded sample are added.
 The timed steps run without per-kernel events (recording an event pair around
 every kernel class costs about 0.6 ms a step on the 50,000 x 400 context); the
 library still times its phases with HIP events on its stream, and the output
-phase is exactly one launch of the output kernel, so that kernel's duration in
-the roofline is measured live on every timed step.  The per-class breakdown
+phase is the output kernels alone (with extents: the intent gather, then the
+row-block extent kernel), so the roofline's duration for them is measured live
+on every timed step.  The per-class breakdown
 (`kernel_ms`) comes from one extra, untimed step with per-kernel events.  Parts
 of a level run on the library's side streams, so the times of the classes that
 overlap there (mid and huge tests, the writers) include waiting and add up to
@@ -204,12 +205,14 @@ def main():
     if b is not None and launches[dominant] > 0:
         per_launch_bytes = b / launches[dominant]
         if dominant == "output" and launches[dominant] == 1:
-            # the output phase of every timed step is this one launch (HIP events on its stream)
+            # the output phase of every timed step is the output kernels alone (HIP events on its stream)
             avg_ms = sum(s["output_ms"] for s in per_step) / args.steps
         else:
             avg_ms = kernel_ms[dominant] / launches[dominant]
         achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
-        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        roof = {"kernel": dominant, "bound": "hbm",
+                "kernels": (["k_output_intents", "k_output_block"] if extents else ["k_output_block"])
+                if dominant == "output" else None, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dominant, args.workload),
                 "bytes_per_launch": int(per_launch_bytes), "avg_launch_ms": round(avg_ms, 4),

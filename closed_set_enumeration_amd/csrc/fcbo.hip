@@ -712,6 +712,11 @@ void fcbo_context::write_output(uint64_t *intents_out, uint64_t *extents_out)
     const uint64_t nblk = div_up(K, (uint64_t)R);
     const uint64_t slots = (uint64_t)n_cu * std::max(1, per_cu);
     const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(nblk, slots));
+    if (extents_out) {
+        hipLaunchKernelGGL(k_output_intents, dim3(kGridCap), dim3(kBlock), 0, stream, (const uint64_t *)intents,
+                           (const uint32_t *)perm, K, wm, intents_out);
+        CK_LAUNCH();
+    }
     hipLaunchKernelGGL(k_output_block, dim3(g), dim3(kOutThreads), lds, stream, (const uint64_t *)intents,
                        (const uint64_t *)loff, (const uint32_t *)objs, (const uint32_t *)perm, K, wm, wn, R,
                        intents_out, extents_out);
