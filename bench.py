@@ -211,7 +211,7 @@ def main():
             avg_ms = kernel_ms[dominant] / launches[dominant]
         achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm",
-                "kernels": (["k_output_intents", "k_output_block"] if extents else ["k_output_block"])
+                "kernels": (["k_output_intents", "k_output_block"] if extents else ["k_output_intents"])
                 if dominant == "output" else None, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dominant, args.workload),

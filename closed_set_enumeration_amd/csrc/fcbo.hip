@@ -693,34 +693,32 @@ void fcbo_context::write_output(uint64_t *intents_out, uint64_t *extents_out)
         prof_end(FCBO_K_OUTPUT, b);
         return;
     }
-    // Rows per block: a multiple of L/gcd(wn, L), L the words of a cache line,
-    // makes the block's region a whole number of lines; aim for
-    // kOutTargetBytes of LDS per block.
-    int R = kWave;
+    // the ordered intents, then (with an extent buffer) the extent row blocks
+    hipLaunchKernelGGL(k_output_intents, dim3(kGridCap), dim3(kBlock), 0, stream, (const uint64_t *)intents,
+                       (const uint32_t *)perm, K, wm, intents_out);
+    CK_LAUNCH();
     if (extents_out) {
+        // Rows per block: a multiple of L/gcd(wn, L), L the words of a cache
+        // line, makes the block's region a whole number of lines; aim for
+        // kOutTargetBytes of LDS per block.
         const int al = kOutLineWords / std::gcd(wn, kOutLineWords);
         const uint64_t al_bytes = (uint64_t)al * row_bytes;
+        int R;
         if (al_bytes <= (uint64_t)kOutBlockBytes)
             R = al * (int)std::max<uint64_t>(1, (uint64_t)kOutTargetBytes / al_bytes);
         else
             R = (int)(kOutBlockBytes / row_bytes);
         R = std::min(R, kWave);
-    }
-    const size_t lds = extents_out ? (size_t)R * wn * 8 : 0;
-    int per_cu = 1;
-    CK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_output_block, kOutThreads, lds));
-    const uint64_t nblk = div_up(K, (uint64_t)R);
-    const uint64_t slots = (uint64_t)n_cu * std::max(1, per_cu);
-    const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(nblk, slots));
-    if (extents_out) {
-        hipLaunchKernelGGL(k_output_intents, dim3(kGridCap), dim3(kBlock), 0, stream, (const uint64_t *)intents,
-                           (const uint32_t *)perm, K, wm, intents_out);
+        const size_t lds = (size_t)R * wn * 8;
+        int per_cu = 1;
+        CK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_output_block, kOutThreads, lds));
+        const uint64_t nblk = div_up(K, (uint64_t)R);
+        const uint64_t slots = (uint64_t)n_cu * std::max(1, per_cu);
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(nblk, slots));
+        hipLaunchKernelGGL(k_output_block, dim3(g), dim3(kOutThreads), lds, stream, (const uint64_t *)loff,
+                           (const uint32_t *)objs, (const uint32_t *)perm, K, wn, R, extents_out);
         CK_LAUNCH();
     }
-    hipLaunchKernelGGL(k_output_block, dim3(g), dim3(kOutThreads), lds, stream, (const uint64_t *)intents,
-                       (const uint64_t *)loff, (const uint32_t *)objs, (const uint32_t *)perm, K, wm, wn, R,
-                       intents_out, extents_out);
-    CK_LAUNCH();
     prof_end(FCBO_K_OUTPUT, b);
 }
 

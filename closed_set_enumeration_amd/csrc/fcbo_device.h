@@ -28,7 +28,8 @@
 //   scans            child and object offsets per parent (exact sizes)
 //   k_*_write        children (C, D, j) stored in parent order, then j order
 // After the last level the output order comes from the CbO tree (subtree sizes
-// bottom-up, positions top-down) and k_output_block writes the caller's rows.
+// bottom-up, positions top-down), k_output_intents and k_output_block write the
+// caller's rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -2103,17 +2104,18 @@ __global__ void __launch_bounds__(kBlock) k_output(const uint64_t *__restrict__ 
     }
 }
 
-// The ordered intents, one output word per thread: output row r is intent
-// perm[r].  Writes are whole consecutive lines; the reads gather W_M words a row.
+// The ordered intents: output row r is intent perm[r].  A workgroup writes
+// kBlock / wm consecutive rows a step, one word per thread (whole consecutive
+// lines); the reads gather W_M words a row.  W_M <= 64 < kBlock.
 __global__ void __launch_bounds__(kBlock) k_output_intents(const uint64_t *__restrict__ intents,
                                                            const uint32_t *__restrict__ perm, uint64_t K, int wm,
                                                            uint64_t *__restrict__ intents_out)
 {
-    const uint64_t n = K * (uint64_t)wm;
-    for (uint64_t t = (uint64_t)blockIdx.x * kBlock + threadIdx.x; t < n; t += (uint64_t)gridDim.x * kBlock) {
-        const uint64_t r = t / (uint64_t)wm;
-        intents_out[t] = intents[(uint64_t)perm[r] * wm + (t - r * wm)];
-    }
+    const int rows = kBlock / wm;  // rows a step
+    const int row = (int)threadIdx.x / wm, word = (int)threadIdx.x - row * wm;
+    if (row >= rows) return;
+    for (uint64_t r = (uint64_t)blockIdx.x * rows + row; r < K; r += (uint64_t)gridDim.x * rows)
+        intents_out[r * wm + word] = intents[(uint64_t)perm[r] * wm + word];
 }
 
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
@@ -2132,27 +2134,21 @@ constexpr int kOutLineWords = 128 / 8;
 // object lists OR-ed in with LDS atomics), then the tile goes out as a single
 // contiguous region of the extent array: each wavefront stores 1 KiB runs, so
 // when R*wn*8 is a multiple of 128 bytes every store covers whole, aligned cache
-// lines.  The tile is cleared as it is read.  With an extent buffer the intent
-// rows are written by k_output_intents beforehand (copying them inside this
-// kernel put a gather on every block's path: 0.13 ms of 5.9 on ctx50000x400);
-// without one only the intents are copied here.  The grid is persistent: a workgroup walks blocks with the grid
-// stride and loads the next block's row sources (permutation entry and list
-// bounds, one row per lane) while it streams the current one.  With no extent
-// buffer only the intents are copied.
-__global__ void __launch_bounds__(kOutThreads) k_output_block(const uint64_t *__restrict__ intents,
-                                                          const uint64_t *__restrict__ loff,
+// lines.  The tile is cleared as it is read.  The intent rows are written by
+// k_output_intents (copying them here put a gather on every block's path: 0.13
+// ms of 5.9 on ctx50000x400).  The grid is persistent: a workgroup walks blocks
+// with the grid stride and loads the next block's row sources (permutation
+// entry and list bounds, one row per lane) while it streams the current one.
+__global__ void __launch_bounds__(kOutThreads) k_output_block(const uint64_t *__restrict__ loff,
                                                           const uint32_t *__restrict__ objs,
-                                                          const uint32_t *__restrict__ perm, uint64_t K, int wm,
-                                                          int wn, int R, uint64_t *__restrict__ intents_out,
-                                                          uint64_t *__restrict__ extents_out)
+                                                          const uint32_t *__restrict__ perm, uint64_t K, int wn,
+                                                          int R, uint64_t *__restrict__ extents_out)
 {
     extern __shared__ __attribute__((aligned(16))) uint64_t s_rows[];
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const bool ext = extents_out != nullptr;
     const int words = R * wn;
-    if (ext)
-        for (int w = threadIdx.x; w < words; w += kOutThreads) s_rows[w] = 0;
+    for (int w = threadIdx.x; w < words; w += kOutThreads) s_rows[w] = 0;
     // stores of two words at a time need a 16-byte aligned region start
     const bool pairs = ((reinterpret_cast<uintptr_t>(extents_out) & 15) == 0) && (words & 1) == 0;
     const uint64_t nblk = (K + R - 1) / R;
@@ -2162,10 +2158,8 @@ __global__ void __launch_bounds__(kOutThreads) k_output_block(const uint64_t *__
         src = lo = hi = 0;
         if (blk < nblk && lane < R && r < K) {
             src = perm[r];
-            if (ext) {
-                lo = loff[src];
-                hi = loff[src + 1];
-            }
+            lo = loff[src];
+            hi = loff[src + 1];
         }
     };
     uint64_t b = blockIdx.x;
@@ -2174,19 +2168,6 @@ __global__ void __launch_bounds__(kOutThreads) k_output_block(const uint64_t *__
     for (; b < nblk; b += gridDim.x) {
         const uint64_t r0 = b * (uint64_t)R;
         const int nr = (int)((K - r0) < (uint64_t)R ? (K - r0) : (uint64_t)R);
-        // intents (no extent buffer): nr*wm consecutive output words; every lane
-        // takes part in the shuffle
-        for (int t0 = 0; t0 < nr * wm && !ext; t0 += kOutThreads) {
-            const int t = t0 + (int)threadIdx.x;
-            int row = t / wm;
-            row = row < nr ? row : nr - 1;
-            const uint64_t s = __shfl(src, row);
-            if (t < nr * wm) intents_out[r0 * wm + t] = intents[s * wm + (t - row * wm)];
-        }
-        if (!ext) {
-            fetch(b + gridDim.x);
-            continue;
-        }
         for (int rr = wv; rr < nr; rr += kOutWaves) {
             const uint64_t o = lane_value64(lo, rr), e = lane_value64(hi, rr);
             uint64_t *T = s_rows + rr * wn;
