@@ -1425,7 +1425,8 @@ __global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
     if (next_mid && lane == 0) atomicAdd((unsigned long long *)&A.counters[CNT_NEXT_MID], (unsigned long long)next_mid);
 }
 
-constexpr int kMidRun = 8;  // records per item of the mid writers
+constexpr int kMidRun = 8;   // records per item of the narrow mid writer
+constexpr int kWideRun = 4;  // of the wide one (1, 2, 4, 8 records: ctx50000x400 level loop 5.06, 4.69, 4.56, 4.63 ms)
 
 // One item of the mid parents' child records: nr <= kMidRun consecutive
 // records at rec0 (a parent's records are consecutive, in rank order).  Their
@@ -1544,7 +1545,7 @@ __global__ void __launch_bounds__(kBlock) k_mid_write(LevelArgs A)
 }
 
 // Children of the wide mid parents: their records (one block of consecutive
-// records per parent, in rank order) taken kMidRun at a time as in k_mid_write,
+// records per parent, in rank order) taken kWideRun at a time as in k_mid_write,
 // so the records of a parent share the passes over its long list.
 template <int WMC>
 __global__ void __launch_bounds__(kBlock) k_mid_write_wide(LevelArgs A)
@@ -1552,11 +1553,11 @@ __global__ void __launch_bounds__(kBlock) k_mid_write_wide(LevelArgs A)
     if (A.counters[CNT_OVERFLOW] || !store_has_room(A)) return;
     const uint64_t nrec = A.counters[CNT_WIDEREC];
     const uint64_t rstride = 4 + (uint64_t)A.wm;
-    const uint64_t items = (nrec + kMidRun - 1) / kMidRun;
+    const uint64_t items = (nrec + kWideRun - 1) / kWideRun;
     for (uint64_t f = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; f < items;
          f += (uint64_t)gridDim.x * kWavesPerBlock) {
-        const uint64_t k0 = f * kMidRun;
-        const int nr = (int)(nrec - k0 < (uint64_t)kMidRun ? nrec - k0 : (uint64_t)kMidRun);
+        const uint64_t k0 = f * kWideRun;
+        const int nr = (int)(nrec - k0 < (uint64_t)kWideRun ? nrec - k0 : (uint64_t)kWideRun);
         mid_write_item<WMC>(A, A.wrec + k0 * rstride, nr);
     }
 }
