@@ -96,6 +96,20 @@ def test_edge_shapes(n, m):
     assert_parity(cells)
 
 
+@pytest.mark.parametrize("m,d,flags", [(300, 0.05, 0), (380, 0.045, 0), (447, 0.04, 0), (512, 0.035, 0),
+                                         (447, 0.04, fca.FCBO_TINY_BUFFERS)])
+def test_five_to_eight_word_intents(m, d, flags):
+    # Intents of 5, 6, 7 and 8 words (the kernels' templates for these widths
+    # take 16-parent chunks in the local test).  1,000 objects with six dense
+    # attributes (density 0.6) besides the sparse ones, so the levels hold
+    # local, narrow mid (65..512 objects) and wide mid (513..4096) parents.
+    cells = synth.random_context(7919 * m + 1000, 1000, m, d)
+    rng = np.random.default_rng(m)
+    for a in rng.choice(m, 6, replace=False):
+        cells[:, a] |= rng.random(1000) < 0.6
+    assert_parity(cells, flags=flags)
+
+
 @pytest.mark.parametrize("n,m,d", [(40, 600, 0.01), (70, 1100, 0.004), (20, 4096, 0.001), (130, 520, 0.012)])
 def test_wide_attribute_sets(n, m, d):
     # more than 8 intent words: the generic word-count kernels
