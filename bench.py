@@ -53,9 +53,13 @@ def kernel_bytes(cls, st, wm, wn, n, k, extents):
         # per test: task, parent index, intent, list offsets, result; per list entry read: entry and column word
         return st["big_tests"] * (8 + 4 + 8 * wm + 16 + 4) + st["big_scanned_objects"] * (4 + 8)
     if cls == "output":
-        reads = k * (4 + 8 * wm + 16) + (n + st["sum_child_objects"]) * 4
-        writes = k * 8 * wm + (k * 8 * wn if extents else 0)
-        return reads + writes
+        # intents: permutation entry and intent in, intent out; extents: the
+        # permutation entry again, list bounds and the list in, extent row out
+        # (every concept's list: the root's N objects plus the children's)
+        b = k * (4 + 8 * wm) + k * 8 * wm
+        if extents:
+            b += k * (4 + 16) + (n + st["sum_child_objects"]) * 4 + k * 8 * wn
+        return b
     if cls == "order":
         # subtree sizes: first-child offset, the children's sizes, the size out; positions:
         # offset, own position, the children's sizes in and positions out; inverse: position in,
