@@ -513,7 +513,10 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads)
 {
     constexpr int kW = LocalCfg<WMC>::kWaves;
     constexpr int CH = LocalCfg<WMC>::kChunk;
-    __shared__ uint64_t s_rows[kW][kSmallMax * WMC];  // the group's object rows, slot-major
+    // the group's object rows, slot-major; up to four words, seven spare slots
+    // let the c_j reads below run past a group's last slot without a guard
+    constexpr int kRowPad = WMC <= 4 ? 7 : 0;
+    __shared__ uint64_t s_rows[kW][(kSmallMax + kRowPad) * WMC];
     __shared__ uint64_t s_b[kW][CH * WMC];            // the chunk's intents, padding bits past M set
     __shared__ uint32_t s_seg[kW][kWave];             // per group parent: first slot | objects << 8
     // per group parent: children, their objects; before the tests, per (parent,
@@ -771,10 +774,13 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads)
                     for (int i0 = 0; i0 < na; i0 += kCb) {
                         uint32_t v[kCb];
 #pragma unroll
-                        for (int k = 0; k < kCb; ++k) v[k] = (i0 + k < na) ? col32[2 * WMC * (i0 + k)] : 0u;
+                        for (int k = 0; k < kCb; ++k)
+                            v[k] = (kRowPad >= kCb - 1 || i0 + k < na) ? col32[2 * WMC * (i0 + k)] : 0u;
 #pragma unroll
                         for (int k = 0; k < kCb; ++k) c |= (uint64_t)((v[k] >> sh) & 1u) << (i0 + k);
                     }
+                    // bits past the parent's objects came from spare or other slots
+                    if (kRowPad >= kCb - 1) c &= (na >= 64) ? ~0ull : below_mask(na);
                 }
                 // D = AND of the rows of c_j
                 uint64_t D[WMC];
