@@ -513,9 +513,11 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads)
 {
     constexpr int kW = LocalCfg<WMC>::kWaves;
     constexpr int CH = LocalCfg<WMC>::kChunk;
-    // the group's object rows, slot-major; up to four words, seven spare slots
-    // let the c_j reads below run past a group's last slot without a guard
-    constexpr int kRowPad = WMC <= 4 ? 7 : 0;
+    // the group's object rows, slot-major; spare slots let the c_j reads below
+    // run past a group's last slot without a guard (seven for reads eight at a
+    // time up to four words, three for reads four at a time up to eight: the
+    // most that keeps seven workgroups per CU)
+    constexpr int kRowPad = WMC <= 4 ? 7 : WMC <= 8 ? 3 : 0;
     __shared__ uint64_t s_rows[kW][(kSmallMax + kRowPad) * WMC];
     __shared__ uint64_t s_b[kW][CH * WMC];            // the chunk's intents, padding bits past M set
     __shared__ uint32_t s_seg[kW][kWave];             // per group parent: first slot | objects << 8
@@ -768,7 +770,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads)
                 // (reads issued kCb at a time, so their LDS latencies overlap)
                 uint64_t c = 0;
                 {
-                    constexpr int kCb = 8;
+                    constexpr int kCb = (WMC <= 4 || WMC > 8) ? 8 : 4;
                     const uint32_t *col32 = R32 + 2 * (first * WMC + wj) + (bj >> 5);
                     const uint32_t sh = (uint32_t)(bj & 31);
                     for (int i0 = 0; i0 < na; i0 += kCb) {
