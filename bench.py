@@ -1,35 +1,43 @@
 """Benchmark: concept enumeration throughput on one MI355X.
 
-One step = one full call of fcbo_enumerate on the seeded 50,000 x 400 context:
-root, every level of closure tests and child writes, the output ordering and the
-ordered intents plus extent bitmaps written to preallocated device buffers.
-Inputs (the context) are resident in HBM before timing starts.
+One step = one full call of fcbo_enumerate on a seeded context: the root, every
+level of closure tests and child writes, the output ordering and the ordered
+intents (plus, when they fit in device memory, the extent bitmaps) written to
+preallocated device buffers.  The context is resident in HBM before timing
+starts.  The default workload is the 50,000 x 400 context.
 
     python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--workload ctx50000x400]
 
-Prints one JSON line.  `value` is concepts per second; closure tests per
-second, per-kernel-class times (HIP events), the roofline of the dominant kernel
-and the CPU oracle timed on a bounded sample are added.
+Prints one JSON line.  `value` is concepts per second; beside it:
+  * closure tests per second;
+  * `roofline`: the dominant kernel class (the output writer), its algorithmic
+    bytes over its launch time, measured live on every timed step with HIP
+    events on the library's stream, against the 8 TB/s HBM peak;
+  * `closure_roofline`: the level loop (root to last level: closure tests,
+    scans, child writes, the per-level host wait), the library's algorithmic
+    byte count `model_bytes` over its measured time;
+  * `hbm_probe`: a device copy and a fill timed in the same process, the
+    achievable bandwidth on this machine;
+  * `cpu_baseline`: the store-free CPU oracle over the whole workload on one
+    pinned host core, run before the GPU is touched; `cpu_baseline_all_cores`
+    the same search split over the host cores.
 
-The timed steps run without per-kernel events (recording an event pair around
-every kernel class costs about 0.6 ms a step on the 50,000 x 400 context); the
-library still times its phases with HIP events on its stream, and the output
-phase is the output kernels alone (with extents: the intent gather, then the
-row-block extent kernel), so the roofline's duration for them is measured live
-on every timed step.  The per-class breakdown
-(`kernel_ms`) comes from one extra, untimed step with per-kernel events.  Parts
-of a level run on the library's side streams, so the times of the classes that
-overlap there (mid and huge tests, the writers) include waiting and add up to
-more than the level loop; the output kernel runs alone.
-`closure_column_equivalent` restates the whole level loop's speed (all tests,
-scans and child writes, wall time) in the terms of a column-streaming closure:
-the bandwidth such a kernel would need to make the same closure tests in that
-time.
+The per-class breakdown (`kernel_ms`) comes from one extra, untimed step with
+an event pair around every kernel class (recording them costs about 0.6 ms a
+step on the 50,000 x 400 context, so the timed steps run without).  Parts of a
+level run on the library's side streams, so the classes that overlap there
+(mid and huge tests, the writers) include waiting and add up to more than the
+level loop; the output kernels run alone.
+
+    python bench.py --rocprof-summary <kernel_stats.csv or counter_collection.csv> ...
+
+turns rocprofv3 CSV files into the tables kept under profiles/ (see there).
 """
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -37,21 +45,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+LEVEL_LOOP_KERNELS = ("k_local_test", "k_mid_test", "k_mid_test_wide", "k_huge_tasks", "k_huge_partial",
+                      "k_huge_finalize", "k_big_test_list", "k_local_write", "k_mid_write", "k_mid_write_wide",
+                      "k_huge_write", "k_big_write_list", "k_scan_up", "k_scan_mid", "k_scan_down", "k_scan_small",
+                      "k_root_init", "k_root_and", "k_fill_u64")
 
 
 def kernel_bytes(cls, st, wm, wn, n, k, extents):
-    """Algorithmic bytes one step moves in a kernel class (see DESIGN.md)."""
-    if cls == "test_local":
-        # per parent: intent, cursor, two list offsets in; pass mask, child and object counts out;
-        # per object of the extent: its list entry and its row
-        return (st["local_parents"] * (8 * wm + 4 + 16 + 8 * wm + 8)
-                + st["local_parent_objects"] * (4 + 8 * wm))
-    if cls == "test_medium":
-        return (st["medium_parents"] * (4 + 8 * wm + 4 + 16 + 8 * wm + 8)
-                + st["medium_parent_objects"] * (4 + 8 * wm))
-    if cls == "test_big":
-        # per test: task, parent index, intent, list offsets, result; per list entry read: entry and column word
-        return st["big_tests"] * (8 + 4 + 8 * wm + 16 + 4) + st["big_scanned_objects"] * (4 + 8)
+    """Algorithmic bytes one step moves in a kernel class."""
     if cls == "output":
         # intents: permutation entry and intent in, intent out; extents: the
         # permutation entry again, list bounds and the list in, extent row out
@@ -79,57 +80,162 @@ def source_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(cls, workload):
-    """HBM bytes per launch of a kernel class from the committed rocprofv3 counter summary,
-    or None when there is none or the device sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "%s_output_traffic.md" % workload)
+def profile_records(workload):
+    """`traffic-record:` lines of the committed counter summary of a workload, keyed by class,
+    kept only while the device sources hash to the value they were taken on."""
+    path = os.path.join(ROOT, "profiles", "%s_traffic.md" % workload)
+    out = {}
     if not os.path.exists(path):
-        return None
+        return out
     sha = source_sha256()
     with open(path) as f:
         for line in f:
             if not line.startswith("traffic-record:"):
                 continue
             kv = dict(x.split("=", 1) for x in line.split()[1:])
-            if kv.get("class") == cls and kv.get("source_sha256") == sha:
-                return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
-    return None
+            if kv.get("source_sha256") == sha:
+                out[kv["class"]] = kv
+    return out
 
 
-def column_stream_equivalent(workload, closure_ms):
-    """Bandwidth a column-streaming closure kernel would need for the same closure
-    tests in `closure_ms` (the level loop's wall time): each test reads the non-zero
-    words of the parent extent (8 bytes each; the oracle's sum_nzw, stored by
-    tests/golden/make_golden.py) once."""
+def column_streaming_what_if(workload, loop_ms):
+    """The bandwidth a column-streaming closure (one read of col[j] at every
+    non-zero word of the parent extent per test, the pages' design) would need to
+    make the same closure tests in the measured level-loop time.  Not an achieved
+    rate: the kernels here read rows once per parent instead."""
     path = os.path.join(ROOT, "tests", "golden", "%s.json" % workload)
-    if not os.path.exists(path) or closure_ms <= 0:
+    if not os.path.exists(path) or loop_ms <= 0:
         return None
     with open(path) as f:
         g = json.load(f)
     if "sum_nzw" not in g:
         return None
     gbytes = 8.0 * g["sum_nzw"] / 1e9
-    gbs = gbytes / (closure_ms * 1e-3)
-    return {"bytes_GB": round(gbytes, 2), "closure_ms": round(closure_ms, 4), "equivalent_GBps": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "time": "level loop, wall"}
+    return {"column_bytes_GB": round(gbytes, 2), "level_loop_ms": round(loop_ms, 4),
+            "required_GBps": round(gbytes / (loop_ms * 1e-3), 1)}
 
 
-def cpu_baseline(rows, m, max_tests):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def host_cores():
+    try:
+        return sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        return list(range(os.cpu_count() or 1))
+
+
+def cpu_baselines(rows, m, threads_all, bitmap_tests):
+    """The oracle on the host cores, before the GPU is touched.  The store-free
+    search (object lists) covers the whole workload: once on one core (the calling
+    thread pinned to it, the worker it starts inherits that), once split over
+    `threads_all` cores.  The bitmap search runs a bounded depth-first prefix as a
+    labelled extra."""
     import oracle
 
+    cores = host_cores()
+    info = {"cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity_cores": len(cores)}
+    out = {}
+    old = None
+    try:
+        old = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {cores[0]})
+    except (AttributeError, OSError):
+        old = None
+    try:
+        t0 = time.perf_counter()
+        d = oracle.cbo_digest(rows, m, threads=1)
+        wall = time.perf_counter() - t0
+    finally:
+        if old is not None:
+            os.sched_setaffinity(0, old)
+    out["one"] = dict(info, **{
+        "value": round(d.n_concepts / d.seconds, 1), "unit": "concepts/s",
+        "closure_tests_per_s": round(d.tests / d.seconds, 1), "cores": 1, "kind": "oracle",
+        "sample": "whole workload: store-free CbO oracle (object-list extents), %d concepts, %d closure tests, "
+                  "%.2f s search (%.2f s wall), one pinned core" % (d.n_concepts, d.tests, d.seconds, wall),
+        "seconds": round(d.seconds, 3)})
     t0 = time.perf_counter()
-    r = oracle.cbo(rows, m, keep_extents=False, max_tests=max_tests)
+    d = oracle.cbo_digest(rows, m, threads=threads_all)
     wall = time.perf_counter() - t0
-    secs = r.seconds_enum + r.seconds_sort
-    return {
-        "value": r.n_concepts / secs,
-        "unit": "concepts/s",
-        "closure_tests_per_s": r.tests / secs,
-        "cores": 1,
-        "kind": "oracle",
-        "sample": "serial CbO oracle, depth-first prefix of the same workload stopped after %d closure tests "
-                  "(%d concepts, %.1f s enumerate+sort, %.1f s wall)" % (r.tests, r.n_concepts, secs, wall),
-    }
+    out["all"] = dict(info, **{
+        "value": round(d.n_concepts / d.seconds, 1), "unit": "concepts/s",
+        "closure_tests_per_s": round(d.tests / d.seconds, 1), "cores": d.threads, "kind": "oracle",
+        "sample": "whole workload: the same search, subtrees of the root's children over %d threads, "
+                  "%.2f s search (%.2f s wall)" % (d.threads, d.seconds, wall),
+        "seconds": round(d.seconds, 3)})
+    if bitmap_tests > 0:
+        r = oracle.cbo(rows, m, keep_extents=False, max_tests=bitmap_tests)
+        secs = r.seconds_enum + r.seconds_sort
+        out["bitmap"] = {
+            "value": round(r.n_concepts / secs, 1), "unit": "concepts/s",
+            "closure_tests_per_s": round(r.tests / secs, 1), "cores": 1, "kind": "oracle",
+            "sample": "bitmap CbO oracle (column AND per test), depth-first prefix stopped after %d closure "
+                      "tests (%d concepts, %.2f s); a prefix, not the whole workload" % (r.tests, r.n_concepts, secs)}
+    return out
+
+
+def hbm_probe(torch, gib):
+    """A device-to-device copy and a fill of `gib` GiB, HIP events around each."""
+    nel = int(gib * (1 << 30)) // 8
+    src = torch.ones(nel, dtype=torch.int64, device="cuda")
+    dst = torch.empty_like(src)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(2):  # first pass warms up
+        e[0].record()
+        dst.copy_(src)
+        e[1].record()
+        dst.zero_()
+        e[2].record()
+        torch.cuda.synchronize()
+    copy_ms, fill_ms = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+    nbytes = nel * 8
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "copy_GBps": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1),
+            "fill_GBps": round(nbytes / (fill_ms * 1e-3) / 1e9, 1)}
+
+
+# --- rocprofv3 CSV summaries ------------------------------------------------------------
+
+def rocprof_summary(paths):
+    """Print markdown tables from rocprofv3 CSVs: kernel_stats (name, calls, total,
+    average ns) or counter_collection (per kernel: dispatches, counter sums)."""
+    import csv
+
+    for path in paths:
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        if not rows:
+            continue
+        print("## %s\n" % os.path.basename(path))
+        if "Counter_Name" in rows[0]:
+            agg = {}
+            for r in rows:
+                name = r["Kernel_Name"].split("(")[0]
+                key = (name, r["Counter_Name"])
+                a = agg.setdefault(key, [0, 0.0, set()])
+                a[1] += float(r["Counter_Value"])
+                a[2].add(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            print("| kernel | counter | dispatches | sum | per dispatch |")
+            print("|---|---|---:|---:|---:|")
+            for (name, cnt), (_, tot, ids) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+                print("| `%s` | %s | %d | %.6g | %.6g |" % (name, cnt, len(ids), tot, tot / max(1, len(ids))))
+        else:
+            print("| kernel | calls | total ns | average ns | % |")
+            print("|---|---:|---:|---:|---:|")
+            for r in rows:
+                print("| `%s` | %s | %s | %s | %s |" % (r["Name"].split("(")[0], r["Calls"], r["TotalDurationNs"],
+                                                   r["AverageNs"], r["Percentage"]))
+        print()
 
 
 def main():
@@ -138,22 +244,41 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="ctx50000x400")
-    ap.add_argument("--no-extents", action="store_true")
-    ap.add_argument("--cpu-tests", type=int, default=8_000_000, help="closure-test budget of the CPU sample")
+    ap.add_argument("--extents", choices=("auto", "yes", "no"), default="auto",
+                    help="write the extent bitmaps (auto: when K x N/8 bytes fit in a third of device memory)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="threads of the all-core CPU baseline (0: the "
+                    "process's cores, at most 16)")
+    ap.add_argument("--cpu-bitmap-tests", type=int, default=2_000_000,
+                    help="closure-test budget of the bitmap oracle's prefix (0: skip)")
+    ap.add_argument("--hbm-probe-gib", type=float, default=4.0)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="run one device-to-device copy of this size first (counter calibration)")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar="CSV")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np  # noqa: F401
+    import synth
+
+    n, m, _ = synth.CONFIGS[args.workload]
+    rows = synth.make_config(args.workload)
+    wn, wm = (n + 63) // 64, (m + 63) // 64
+
+    cpu = None
+    if not args.no_cpu:
+        threads = args.cpu_threads or min(16, len(host_cores()))
+        cpu = cpu_baselines(rows, m, threads, args.cpu_bitmap_tests)
+        print("[bench] cpu baseline: %s" % json.dumps(cpu), file=sys.stderr, flush=True)
+
     import torch
 
     import closed_set_enumeration_amd as fca
-    import synth
 
     if not torch.cuda.is_available():
         print("no HIP device", file=sys.stderr)
@@ -169,13 +294,15 @@ def main():
         torch.cuda.synchronize()
         print("[bench] copy probe: %d bytes read, %d bytes written" % (nel * 8, nel * 8), file=sys.stderr, flush=True)
         del src, dst
-    n, m, _ = synth.CONFIGS[args.workload]
-    rows = synth.make_config(args.workload)
-    extents = not args.no_extents
-    wn, wm = (n + 63) // 64, (m + 63) // 64
+    probe = hbm_probe(torch, args.hbm_probe_gib) if args.hbm_probe_gib > 0 else None
 
     ctx = fca.Context(rows, m)
     k = ctx.count()
+    if args.extents == "auto":
+        free, _ = torch.cuda.mem_get_info()
+        extents = k * wn * 8 <= free / 3
+    else:
+        extents = args.extents == "yes"
     ints, exts = ctx.alloc_outputs(k, extents)
     print("[bench] %s: K=%d, output buffers %.2f GB" % (args.workload, k, (ints.numel() + (exts.numel() if extents else 0)) * 8 / 1e9),
           file=sys.stderr, flush=True)
@@ -200,28 +327,43 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     print("[bench] timed %d steps: %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
 
+    def avg(key):
+        return sum(s[key] for s in per_step) / len(per_step)
+
     st0 = per_step[-1]
     kernel_ms = dict(prof["kernel_ms"])
     launches = dict(prof["kernel_launches"])
-    dominant = max(kernel_ms, key=kernel_ms.get)
-    roof = None
-    b = kernel_bytes(dominant, st0, wm, wn, n, k, extents)
-    if b is not None and launches[dominant] > 0:
-        per_launch_bytes = b / launches[dominant]
-        if dominant == "output" and launches[dominant] == 1:
-            # the output phase of every timed step is the output kernels alone (HIP events on its stream)
-            avg_ms = sum(s["output_ms"] for s in per_step) / args.steps
-        else:
-            avg_ms = kernel_ms[dominant] / launches[dominant]
-        achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
-        roof = {"kernel": dominant, "bound": "hbm",
-                "kernels": (["k_output_intents", "k_output_block"] if extents else ["k_output_intents"])
-                if dominant == "output" else None, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dominant, args.workload),
-                "bytes_per_launch": int(per_launch_bytes), "avg_launch_ms": round(avg_ms, 4),
-                "timing": "timed steps, HIP events around the output phase" if dominant == "output"
-                          else "profiled step, HIP events per kernel class"}
+    records = profile_records(args.workload)
+
+    # the dominant kernel class: the output writer, one launch per step, timed
+    # live on every timed step (the output phase is its kernels alone)
+    out_bytes = kernel_bytes("output", st0, wm, wn, n, k, extents)
+    out_ms = avg("output_ms")
+    achieved = out_bytes / (out_ms * 1e-3) / 1e9
+    rec = records.get("output" if extents else "output_intents")
+    roof = {"kernel": "output", "bound": "hbm",
+            "kernels": ["k_output_intents", "k_output_block"] if extents else ["k_output_intents"],
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": (int(rec["fetch_bytes_per_launch"]) + int(rec["write_bytes_per_launch"])) if rec else None,
+            "bytes_per_launch": int(out_bytes), "avg_launch_ms": round(out_ms, 4),
+            "frac_of_fill_probe": round(achieved / probe["fill_GBps"], 4) if probe else None,
+            "timing": "timed steps, HIP events around the output phase"}
+
+    # the closure kernels: the level loop against the model byte count
+    loop_ms = avg("closure_kernel_ms")
+    model = st0["model_bytes"]
+    loop_gbs = model / (loop_ms * 1e-3) / 1e9
+    lrec = records.get("level_loop")
+    closure_roof = {
+        "kernels": "level loop: root, closure tests, scans, child writes, per-level host wait",
+        "bound": "hbm", "model_bytes": int(model), "ms": round(loop_ms, 4), "achieved": round(loop_gbs, 1),
+        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(loop_gbs / HBM_PEAK_GBS, 4),
+        "traffic": (int(lrec["fetch_bytes_per_step"]) + int(lrec["write_bytes_per_step"])) if lrec else None,
+        "valu_issue": json.loads(lrec["valu_issue"]) if lrec and "valu_issue" in lrec else None,
+        "timing": "timed steps, HIP events around the level loop"}
+    if closure_roof["traffic"]:
+        closure_roof["traffic_over_model"] = round(closure_roof["traffic"] / model, 3)
 
     tests = st0["closure_tests"]
     out = {
@@ -240,22 +382,21 @@ def main():
         "config": {"workload": args.workload, "objects": n, "attributes": m, "extents_out": extents,
                    "concepts": k, "closure_tests": tests, "levels": st0["n_levels"]},
         "closure_tests_per_s": round(tests / (ms_per_step * 1e-3), 1),
-        "device_ms": {"enumerate": round(sum(s["enumerate_ms"] for s in per_step) / args.steps, 4),
-                      "levels": round(sum(s["levels_ms"] for s in per_step) / args.steps, 4),
-                      "order": round(sum(s["order_ms"] for s in per_step) / args.steps, 4),
-                      "output": round(sum(s["output_ms"] for s in per_step) / args.steps, 4)},
+        "device_ms": {"enumerate": round(avg("enumerate_ms"), 4), "level_loop": round(loop_ms, 4),
+                      "sort": round(avg("sort_ms"), 4), "output": round(out_ms, 4)},
         "kernel_ms": {c: round(v, 4) for c, v in kernel_ms.items()},
         "kernel_launches": launches,
         "kernel_ms_from": "one untimed step with per-kernel events (%.3f ms)" % prof["enumerate_ms"],
         "roofline": roof,
-        "closure_column_equivalent": column_stream_equivalent(
-            args.workload, sum(s["levels_ms"] for s in per_step) / args.steps),
-        "cpu_baseline": None,
+        "closure_roofline": closure_roof,
+        "column_streaming_what_if": column_streaming_what_if(args.workload, loop_ms),
+        "hbm_probe": probe,
+        "cpu_baseline": cpu["one"] if cpu else None,
+        "cpu_baseline_all_cores": cpu["all"] if cpu else None,
+        "cpu_baseline_bitmap_oracle": cpu.get("bitmap") if cpu else None,
     }
     ctx.close()
     del ints, exts
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(rows, m, args.cpu_tests)
     print(json.dumps(out), flush=True)
 
 

@@ -1,8 +1,9 @@
 """Formal-concept enumeration on MI355X: Python binding of libfcbo.so.
 
 The functions named like the C ABI (``fcbo_context_create``, ``fcbo_enumerate``,
-``fcbo_level_counts``, ``fcbo_copy_columns``, ``fcbo_destroy``,
-``fcbo_error_string``) only marshal arguments; every step of the enumeration
+``fcbo_write_range``, ``fcbo_set_memory_limit``, ``fcbo_level_counts``,
+``fcbo_copy_columns``, ``fcbo_destroy``, ``fcbo_error_string``) only marshal
+arguments; every step of the enumeration
 runs in the HIP kernels of the library.  :class:`Context` is a convenience
 wrapper that takes device buffers and the stream from PyTorch.
 
@@ -25,6 +26,7 @@ FCBO_ERR_INVALID_ARGUMENT = -1
 FCBO_ERR_OUT_OF_MEMORY = -2
 FCBO_ERR_DEVICE = -3
 FCBO_ERR_CAPACITY = -4
+FCBO_ERR_LIMIT = -5
 
 FCBO_ROWS_ON_DEVICE = 1
 FCBO_TINY_BUFFERS = 2
@@ -37,6 +39,8 @@ KERNEL_CLASSES = ("count", "test_local", "test_medium", "test_big", "scan", "wri
 EXPORTED = (
     "fcbo_context_create",
     "fcbo_enumerate",
+    "fcbo_write_range",
+    "fcbo_set_memory_limit",
     "fcbo_level_counts",
     "fcbo_copy_columns",
     "fcbo_destroy",
@@ -50,6 +54,11 @@ class FcboStats(ctypes.Structure):
         ("closure_tests", ctypes.c_uint64),
         ("item_pairs", ctypes.c_uint64),
         ("n_levels", ctypes.c_uint64),
+        ("enumerate_ms", ctypes.c_double),
+        ("closure_kernel_ms", ctypes.c_double),
+        ("sort_ms", ctypes.c_double),
+        ("model_bytes", ctypes.c_uint64),
+        ("output_ms", ctypes.c_double),
         ("sum_child_objects", ctypes.c_uint64),
         ("output_bytes", ctypes.c_uint64),
         ("local_parents", ctypes.c_uint64),
@@ -59,11 +68,9 @@ class FcboStats(ctypes.Structure):
         ("big_parents", ctypes.c_uint64),
         ("big_tests", ctypes.c_uint64),
         ("big_scanned_objects", ctypes.c_uint64),
+        ("big_nonzero_words", ctypes.c_uint64),
+        ("big_child_objects", ctypes.c_uint64),
         ("order_launches", ctypes.c_uint64),
-        ("enumerate_ms", ctypes.c_double),
-        ("levels_ms", ctypes.c_double),
-        ("order_ms", ctypes.c_double),
-        ("output_ms", ctypes.c_double),
         ("kernel_ms", ctypes.c_double * len(KERNEL_CLASSES)),
         ("kernel_launches", ctypes.c_uint64 * len(KERNEL_CLASSES)),
     ]
@@ -106,6 +113,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         P(FcboStats),
     ]
     lib.fcbo_enumerate.restype = ctypes.c_int
+    lib.fcbo_write_range.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    lib.fcbo_write_range.restype = ctypes.c_int
+    lib.fcbo_set_memory_limit.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
+    lib.fcbo_set_memory_limit.restype = ctypes.c_int
     lib.fcbo_level_counts.argtypes = [
         ctypes.c_void_p, P(ctypes.c_uint64), P(ctypes.c_uint64), ctypes.c_uint64, P(ctypes.c_uint64),
     ]
@@ -150,6 +162,20 @@ def fcbo_enumerate(ctx: int, intents_out_ptr: int, extents_out_ptr: int, capacit
     if rc not in (FCBO_OK, FCBO_ERR_CAPACITY):
         raise FcboError(rc, "fcbo_enumerate")
     return rc, k.value, st
+
+
+def fcbo_write_range(ctx: int, first: int, count: int, intents_out_ptr: int, extents_out_ptr: int) -> None:
+    """Output rows [first, first + count) of the last enumeration; raises FcboError on failure."""
+    rc = load_library().fcbo_write_range(ctypes.c_void_p(ctx), first, count, ctypes.c_void_p(intents_out_ptr or None),
+                                         ctypes.c_void_p(extents_out_ptr or None))
+    if rc != FCBO_OK:
+        raise FcboError(rc, "fcbo_write_range")
+
+
+def fcbo_set_memory_limit(ctx: int, nbytes: int) -> None:
+    rc = load_library().fcbo_set_memory_limit(ctypes.c_void_p(ctx), int(nbytes))
+    if rc != FCBO_OK:
+        raise FcboError(rc, "fcbo_set_memory_limit")
 
 
 def fcbo_level_counts(ctx: int):
@@ -226,6 +252,7 @@ class Context:
             keep = rows
         self.wn = (self.n_objects + 63) // 64
         self.wm = (self.n_attrs + 63) // 64
+        self.device = torch.cuda.current_device()
         self.handle = fcbo_context_create(ptr, self.n_objects, self.n_attrs, stride, flags | extra,
                                           self.stream.cuda_stream)
         del keep
@@ -254,13 +281,48 @@ class Context:
         exts = torch.empty((max(capacity, 1), self.wn), dtype=torch.int64, device=dev) if extents else None
         return ints, exts
 
+    def _check_buffer(self, t, width, what):
+        """Shape, type, layout and device of a caller output buffer (before any launch)."""
+        torch = self._torch
+        if not isinstance(t, torch.Tensor):
+            raise ValueError("%s must be a torch tensor" % what)
+        if t.dim() != 2 or t.shape[1] != width:
+            raise ValueError("%s must be 2-D with %d words per row, got %s" % (what, width, tuple(t.shape)))
+        if t.element_size() != 8 or t.dtype.is_floating_point or t.dtype.is_complex:
+            raise ValueError("%s must hold 64-bit integer words, got %s" % (what, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % what)
+        if not t.is_cuda or t.device.index != self.device:
+            raise ValueError("%s must be on the context's device cuda:%d" % (what, self.device))
+        return t.shape[0]
+
     def enumerate_into(self, intents, extents, flags: int = 0):
         """One full call into preallocated buffers; returns (rc, K, stats dict)."""
-        cap = intents.shape[0]
+        cap = self._check_buffer(intents, self.wm, "intents")
+        if extents is not None:
+            cap = min(cap, self._check_buffer(extents, self.wn, "extents"))
         rc, k, st = fcbo_enumerate(
             self.handle, intents.data_ptr(), extents.data_ptr() if extents is not None else 0, cap, flags
         )
         return rc, k, st.as_dict()
+
+    def write_range(self, first: int, intents=None, extents=None):
+        """Output rows [first, first + rows) of the last enumeration into the given buffers."""
+        if intents is None and extents is None:
+            raise ValueError("give an intent or an extent buffer")
+        rows = None
+        if intents is not None:
+            rows = self._check_buffer(intents, self.wm, "intents")
+        if extents is not None:
+            r = self._check_buffer(extents, self.wn, "extents")
+            if rows is not None and r != rows:
+                raise ValueError("intent and extent buffers differ in rows")
+            rows = r
+        fcbo_write_range(self.handle, first, rows, intents.data_ptr() if intents is not None else 0,
+                         extents.data_ptr() if extents is not None else 0)
+
+    def set_memory_limit(self, nbytes: int) -> None:
+        fcbo_set_memory_limit(self.handle, nbytes)
 
     def enumerate(self, extents: bool = True, profile: bool = False) -> Result:
         k = self.count()

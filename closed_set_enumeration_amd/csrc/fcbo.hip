@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <numeric>
 #include <new>
 #include <vector>
@@ -40,35 +41,89 @@ inline int map_error(hipError_t e)
 
 inline uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
+// Where the enumeration buffers come from: hipMalloc, optionally under a cap
+// on the bytes held together (fcbo_set_memory_limit); or, for the entry point
+// that allocates nothing, consecutive pieces of a fixed device region that are
+// never handed back (the region is reused from its start by the next call).
+struct DeviceMemory {
+    uint64_t limit = 0;  // bytes the buffers may hold together; 0 = no cap
+    uint64_t held = 0;   // bytes they hold now
+    char *region = nullptr;  // the fixed region, or null
+    uint64_t region_size = 0, region_used = 0;
+
+    void *get(uint64_t bytes)
+    {
+        if (region) {
+            const uint64_t at = (region_used + 255) & ~255ull;
+            if (at > region_size || bytes > region_size - at) throw HipError{FCBO_ERR_OUT_OF_MEMORY};
+            region_used = at + bytes;
+            return region + at;
+        }
+        if (limit && held + bytes > limit) throw HipError{FCBO_ERR_OUT_OF_MEMORY};
+        void *q = nullptr;
+        CK(hipMalloc(&q, bytes));
+        held += bytes;
+        return q;
+    }
+    void put(void *p, uint64_t bytes)
+    {
+        if (!p || region) return;
+        (void)hipFree(p);
+        held -= std::min(held, bytes);
+    }
+};
+
 template <typename T>
-void dfree(T *&p)
+void dfree(DeviceMemory &dm, T *&p, uint64_t &cap)
 {
-    if (p) (void)hipFree((void *)p);
+    dm.put((void *)p, cap * sizeof(T));
     p = nullptr;
+    cap = 0;
 }
 
 // Grow a device array to hold at least `need` elements, keeping the first
 // `keep` elements.  Capacity grows at least by half to amortise copies.
 template <typename T>
-void ensure(T *&p, uint64_t &cap, uint64_t need, uint64_t keep, hipStream_t s, uint64_t min_cap = 1024)
+void ensure(DeviceMemory &dm, T *&p, uint64_t &cap, uint64_t need, uint64_t keep, hipStream_t s,
+            uint64_t min_cap = 1024)
 {
     if (need <= cap && p) return;
-    uint64_t ncap = std::max<uint64_t>(need, cap + cap / 2);
+    // (pieces of the fixed region are not reused: grow faster there)
+    uint64_t ncap = std::max<uint64_t>(need, dm.region ? 2 * cap : cap + cap / 2);
     ncap = std::max<uint64_t>(ncap, min_cap);
-    T *q = nullptr;
-    CK(hipMalloc((void **)&q, ncap * sizeof(T)));
+    T *q = (T *)dm.get(ncap * sizeof(T));
     if (p && keep) {
         hipError_t e = hipMemcpyAsync(q, p, keep * sizeof(T), hipMemcpyDeviceToDevice, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) {
-            (void)hipFree(q);
+            dm.put(q, ncap * sizeof(T));
             throw HipError{map_error(e)};
         }
     }
-    dfree(p);
+    dfree(dm, p, cap);
     p = q;
     cap = ncap;
 }
+
+// Per-level counts of an enumeration.  Every level adds an attribute to the
+// intent, so there are at most M + 1 <= 4097 levels.
+struct LevelLog {
+    static constexpr size_t kMax = 4098;
+    uint64_t concepts[kMax];  // concepts generated on level k
+    uint64_t tests[kMax];     // closure tests made by them
+    uint64_t lo[kMax + 1];    // index of level k's first concept (generation order)
+    size_t n = 0;
+    void clear() { n = 0; lo[0] = 0; }
+    size_t size() const { return n; }
+    void push(uint64_t c, uint64_t t)
+    {
+        if (n == kMax) throw HipError{FCBO_ERR_DEVICE};
+        concepts[n] = c;
+        tests[n] = t;
+        lo[n + 1] = lo[n] + c;
+        ++n;
+    }
+};
 
 constexpr int kGridCap = 4096;  // blocks for grid-stride wave kernels
 // Average children per concept from which the order passes take a wavefront
@@ -81,23 +136,23 @@ struct BigStore {
     uint32_t *idx = nullptr, *n = nullptr, *size = nullptr;
     uint64_t *off = nullptr, *tasks = nullptr, *sscan = nullptr, *plist = nullptr, *bmp = nullptr;
 
-    void free_all()
+    void free_all(DeviceMemory &dm)
     {
-        dfree(idx); dfree(n); dfree(size); dfree(off); dfree(tasks); dfree(sscan); dfree(plist); dfree(bmp);
-        cap_idx = cap_n = cap_off = cap_t = cap_s = cap_ss = cap_p = cap_bmp = 0;
+        dfree(dm, idx, cap_idx); dfree(dm, n, cap_n); dfree(dm, size, cap_s); dfree(dm, off, cap_off);
+        dfree(dm, tasks, cap_t); dfree(dm, sscan, cap_ss); dfree(dm, plist, cap_p); dfree(dm, bmp, cap_bmp);
     }
-    void ensure_members(uint64_t P, hipStream_t s, uint64_t mc)
+    void ensure_members(DeviceMemory &dm, uint64_t P, hipStream_t s, uint64_t mc)
     {
-        ensure(idx, cap_idx, P, 0, s, mc);
-        ensure(n, cap_n, P, 0, s, mc);
-        ensure(off, cap_off, P + 1, 0, s, mc);
+        ensure(dm, idx, cap_idx, P, 0, s, mc);
+        ensure(dm, n, cap_n, P, 0, s, mc);
+        ensure(dm, off, cap_off, P + 1, 0, s, mc);
     }
-    void ensure_tests(uint64_t need, hipStream_t s, uint64_t mc)
+    void ensure_tests(DeviceMemory &dm, uint64_t need, hipStream_t s, uint64_t mc)
     {
-        ensure(tasks, cap_t, need, 0, s, mc);
-        ensure(size, cap_s, need, 0, s, mc);
-        ensure(sscan, cap_ss, need + 1, 0, s, mc);
-        ensure(plist, cap_p, need, 0, s, mc);
+        ensure(dm, tasks, cap_t, need, 0, s, mc);
+        ensure(dm, size, cap_s, need, 0, s, mc);
+        ensure(dm, sscan, cap_ss, need + 1, 0, s, mc);
+        ensure(dm, plist, cap_p, need, 0, s, mc);
     }
     uint64_t test_cap() const { return std::min(std::min(cap_t, cap_s), std::min(cap_ss ? cap_ss - 1 : 0, cap_p)); }
     BigSet view(int cnt_slot, int tot_slot, int pass_slot, bool bitmaps) const
@@ -122,6 +177,9 @@ struct fcbo_context {
     int wn = 0, wm = 0;
     uint64_t tail_m = 0, tail_n = 0;
     bool tiny = false;  // FCBO_TINY_BUFFERS: every buffer starts at its minimum size
+    bool fixed = false; // buffers from the static scratch region: no allocation, no events,
+                        // no side streams
+    DeviceMemory dmem;  // source of the enumeration buffers below
     uint64_t *rows = nullptr;  // n x wm (+1 padding row)
     uint64_t *cols = nullptr;  // m x wn
 
@@ -136,7 +194,8 @@ struct fcbo_context {
     // level scratch
     uint64_t cap_pass = 0, cap_nch = 0, cap_nob = 0, cap_cb = 0, cap_ob = 0, cap_mid = 0, cap_mrec = 0;
     uint64_t *pass = nullptr, *cbase = nullptr, *obase = nullptr;
-    uint32_t *nchild = nullptr, *nobj = nullptr, *mid_idx = nullptr;
+    uint32_t *nchild = nullptr, *mid_idx = nullptr;
+    uint64_t *nobj = nullptr;
     uint64_t *mrec = nullptr;  // child records of the narrow mid parents (words)
     uint64_t *wrec = nullptr;  // child records of the wide mid parents (words)
     uint64_t cap_wrec = 0;
@@ -150,7 +209,8 @@ struct fcbo_context {
     uint64_t *scan_part = nullptr;  // 2 x kScanBlocks
     uint64_t *counters = nullptr;   // 2 x CNT_N: levels alternate between the halves
     int ctr = 0;                    // half of the current level
-    uint64_t *h_counters = nullptr; // pinned, CNT_N
+    uint64_t *h_counters = nullptr; // pinned, CNT_N (h_counters_own when fixed)
+    uint64_t h_counters_own[CNT_N];
 
     // output order
     uint64_t cap_rank = 0, cap_perm = 0;
@@ -162,8 +222,8 @@ struct fcbo_context {
     bool have_perm = false;
     uint64_t K = 0, tests = 0, pairs = 0, sum_c = 0;
     uint64_t local_parents = 0, local_objs = 0, med_parents = 0, med_objs = 0;
-    uint64_t big_parents = 0, big_tests = 0, big_scan = 0, order_launches = 0;
-    std::vector<uint64_t> lev_concepts, lev_tests;
+    uint64_t big_parents = 0, big_tests = 0, big_scan = 0, big_nzw = 0, big_cobjs = 0, order_launches = 0;
+    LevelLog lev;
 
     // profiling
     bool profile = false;
@@ -220,20 +280,45 @@ struct fcbo_context {
     }
 
     uint64_t min_cap() const { return tiny ? 1 : 1024; }
+    // first size of a buffer that normally starts at `normal` elements
+    uint64_t start_size(uint64_t normal) const
+    {
+        return tiny ? 1 : fixed ? std::max<uint64_t>(64, normal / 64) : normal;
+    }
+    void clear_words(uint64_t *p, uint64_t n)
+    {
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(1024, div_up(n, kBlock)));
+        hipLaunchKernelGGL(k_fill_u64, dim3(g), dim3(kBlock), 0, stream, p, n, 0ull);
+        CK_LAUNCH();
+    }
+    void setup(const uint64_t *rows_in, int64_t n_objects, int64_t n_attrs, int64_t row_stride_words,
+               bool rows_on_device);
 
     bool use_bitmaps() const { return wn <= kBmpMaxWords; }
     int nchunk() const { return (int)div_up((uint64_t)wn, kWave); }
 
+    // the enumeration's buffers (the context's rows, columns and counters stay)
+    void free_buffers()
+    {
+        dfree(dmem, intents, cap_int); dfree(dmem, cursor, cap_cur); dfree(dmem, loff, cap_loff);
+        dfree(dmem, objs, cap_o); dfree(dmem, fchild, cap_fch);
+        dfree(dmem, pass, cap_pass); dfree(dmem, cbase, cap_cb); dfree(dmem, obase, cap_ob);
+        dfree(dmem, nchild, cap_nch); dfree(dmem, nobj, cap_nob); dfree(dmem, mid_idx, cap_mid);
+        dfree(dmem, mrec, cap_mrec); dfree(dmem, wrec, cap_wrec); dfree(dmem, lrec, cap_lrec);
+        dfree(dmem, lfill, cap_lfill);
+        huge.free_all(dmem);
+        dfree(dmem, dt, cap_dt); dfree(dmem, tcnt, cap_tcnt); dfree(dmem, icnt, cap_icnt);
+        dfree(dmem, rank, cap_rank); dfree(dmem, perm, cap_perm);
+        have_result = have_perm = false;
+    }
+
     void free_all()
     {
-        dfree(rows); dfree(cols);
-        dfree(intents); dfree(cursor); dfree(loff); dfree(objs); dfree(fchild);
-        dfree(pass); dfree(cbase); dfree(obase); dfree(nchild); dfree(nobj); dfree(mid_idx); dfree(mrec); dfree(wrec); dfree(lrec); dfree(lfill);
-        huge.free_all();
-        dfree(dt); dfree(tcnt); dfree(icnt);
-        dfree(scan_part); dfree(counters);
-        dfree(rank); dfree(perm);
-        if (h_counters) (void)hipHostFree(h_counters);
+        free_buffers();
+        for (void *q : {(void *)rows, (void *)cols, (void *)scan_part, (void *)counters})
+            if (q) (void)hipFree(q);
+        rows = cols = scan_part = counters = nullptr;
+        if (h_counters && h_counters != h_counters_own) (void)hipHostFree(h_counters);
         h_counters = nullptr;
         for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
         ev_pool.clear();
@@ -251,10 +336,10 @@ struct fcbo_context {
     // per-test buffers of the huge set (its BigStore plus the accumulators)
     void ensure_huge_tests(uint64_t need)
     {
-        huge.ensure_tests(need, stream, min_cap());
-        ensure(dt, cap_dt, need * wm, 0, stream, min_cap());
-        ensure(tcnt, cap_tcnt, need, 0, stream, min_cap());
-        ensure(icnt, cap_icnt, need * nchunk(), 0, stream, min_cap());
+        huge.ensure_tests(dmem, need, stream, min_cap());
+        ensure(dmem, dt, cap_dt, need * wm, 0, stream, min_cap());
+        ensure(dmem, tcnt, cap_tcnt, need, 0, stream, min_cap());
+        ensure(dmem, icnt, cap_icnt, need * nchunk(), 0, stream, min_cap());
     }
 
     LevelArgs level_args(uint64_t lo, uint64_t P, uint64_t obj_hi) const
@@ -289,7 +374,7 @@ struct fcbo_context {
 
     // exclusive scan (see k_scan_*): a (and b) -> out_a (and out_b), n from the
     // device or the host; fch (optional) receives fbase + out_a as u32.
-    void scan(const uint32_t *a, const uint32_t *b, const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
+    void scan(const uint32_t *a, const uint64_t *b, const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
               uint64_t *out_a, uint64_t *out_b, uint64_t *tot_a, uint64_t *tot_b, uint32_t *fch = nullptr,
               uint64_t fbase = 0, hipStream_t s = nullptr, bool small = false)
     {
@@ -319,12 +404,13 @@ struct fcbo_context {
     void ensure_local_records(uint64_t slots)
     {
         const uint64_t chunks = div_up(slots, kWave) + 1;
-        ensure(lrec, cap_lrec, chunks * kWave * (4 + (uint64_t)wm), 0, stream, 1);
-        ensure(lfill, cap_lfill, chunks, 0, stream, 1);
+        ensure(dmem, lrec, cap_lrec, chunks * kWave * (4 + (uint64_t)wm), 0, stream, 1);
+        ensure(dmem, lfill, cap_lfill, chunks, 0, stream, 1);
     }
     void enumerate_levels();
     void order_concepts();
-    void write_output(uint64_t *intents_out, uint64_t *extents_out);
+    void write_output(uint64_t *intents_out, uint64_t *extents_out, uint64_t first, uint64_t count);
+    uint64_t model_bytes() const;
 };
 
 namespace {
@@ -494,11 +580,14 @@ void fcbo_context::enumerate_levels()
     const LevelFns fns = pick_level_fns(wm);
     const uint64_t mc = min_cap();
     const bool bm = use_bitmaps();
+    // nothing of an earlier result survives a failure part-way through
+    have_result = have_perm = false;
+    K = 0;
     // root
-    ensure(intents, cap_int, (uint64_t)wm * 1024, 0, stream, mc);
-    ensure(cursor, cap_cur, 1024, 0, stream, mc);
-    ensure(loff, cap_loff, 1025, 0, stream, mc);
-    ensure(objs, cap_o, (uint64_t)n, 0, stream, mc);
+    ensure(dmem, intents, cap_int, (uint64_t)wm * 1024, 0, stream, mc);
+    ensure(dmem, cursor, cap_cur, 1024, 0, stream, mc);
+    ensure(dmem, loff, cap_loff, 1025, 0, stream, mc);
+    ensure(dmem, objs, cap_o, (uint64_t)n, 0, stream, mc);
     {
         uint64_t t = std::max<uint64_t>((uint64_t)n, (uint64_t)wm);
         hipLaunchKernelGGL(k_root_init, dim3((unsigned)div_up(t, kBlock)), dim3(kBlock), 0, stream, intents, cursor,
@@ -509,19 +598,18 @@ void fcbo_context::enumerate_levels()
                            (int)n, wm);
         CK_LAUNCH();
     }
-    lev_concepts.clear();
-    lev_tests.clear();
+    lev.clear();
     tests = pairs = sum_c = 0;
-    local_parents = local_objs = med_parents = med_objs = big_parents = big_tests = big_scan = 0;
+    local_parents = local_objs = med_parents = med_objs = big_parents = big_tests = big_scan = big_nzw = big_cobjs = 0;
     const uint64_t rstride = 4 + (uint64_t)wm;
     if (!huge.tasks) {
-        if (bm) ensure_huge_tests(tiny ? 1 : (1u << 16));
-        else huge.ensure_tests(tiny ? 1 : (1u << 20), stream, mc);
+        if (bm) ensure_huge_tests(start_size(1u << 16));
+        else huge.ensure_tests(dmem, start_size(1u << 20), stream, mc);
     }
-    if (bm && !huge.bmp) ensure(huge.bmp, huge.cap_bmp, (uint64_t)wn * (tiny ? 1 : 64), 0, stream, 1);
-    if (!mrec) ensure(mrec, cap_mrec, rstride * (tiny ? 1 : (1u << 18)), 0, stream, 1);
-    if (!wrec) ensure(wrec, cap_wrec, rstride * (tiny ? 1 : (1u << 16)), 0, stream, 1);
-    if (!lrec) ensure_local_records(tiny ? kWave : (1u << 21));
+    if (bm && !huge.bmp) ensure(dmem, huge.bmp, huge.cap_bmp, (uint64_t)wn * start_size(64), 0, stream, 1);
+    if (!mrec) ensure(dmem, mrec, cap_mrec, rstride * start_size(1u << 18), 0, stream, 1);
+    if (!wrec) ensure(dmem, wrec, cap_wrec, rstride * start_size(1u << 16), 0, stream, 1);
+    if (!lrec) ensure_local_records(tiny ? kWave : start_size(1u << 21));
     uint64_t lo = 0, P = 1, obj_hi = (uint64_t)n;  // parents [lo, lo+P); objects used so far
     const uint64_t mid_max = wm <= 8 ? (uint64_t)kMidMax : (uint64_t)kSmallMax;
     // parents of each class on the level about to run (the root: N objects);
@@ -529,20 +617,21 @@ void fcbo_context::enumerate_levels()
     uint64_t next_mid = ((uint64_t)n > (uint64_t)kSmallMax && (uint64_t)n <= mid_max) ? 1 : 0;
     uint64_t next_huge = (uint64_t)n > mid_max ? 1 : 0;
     ctr = 0;
-    CK(hipMemsetAsync(counters, 0, 2 * CNT_N * sizeof(uint64_t), stream));
+    clear_words(counters, 2 * CNT_N);
     while (P > 0) {
-        if (P >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
+        if (lo + P >= (1ull << 32)) throw HipError{FCBO_ERR_LIMIT};  // concept indices are 32-bit
         // every level adds an attribute to the intent, so there are at most M + 1
-        if (lev_concepts.size() > (size_t)m + 1) throw HipError{FCBO_ERR_DEVICE};
-        ensure(pass, cap_pass, std::max<uint64_t>(1, next_huge) * wm, 0, stream, mc);
-        ensure(nchild, cap_nch, P, 0, stream, mc);
-        ensure(nobj, cap_nob, P, 0, stream, mc);
-        ensure(cbase, cap_cb, P + 1, 0, stream, mc);
-        ensure(obase, cap_ob, P + 1, 0, stream, mc);
-        ensure(mid_idx, cap_mid, P, 0, stream, mc);
-        ensure(fchild, cap_fch, lo + P + 1, lo + 1, stream, mc);
-        huge.ensure_members(P, stream, mc);
-        unsigned classes = (next_mid ? kLevelMid : 0u) | (next_huge ? kLevelHuge : 0u) | (next_huge ? kLevelSide : 0u);
+        if (lev.size() > (size_t)m + 1) throw HipError{FCBO_ERR_DEVICE};
+        ensure(dmem, pass, cap_pass, std::max<uint64_t>(1, next_huge) * wm, 0, stream, mc);
+        ensure(dmem, nchild, cap_nch, P, 0, stream, mc);
+        ensure(dmem, nobj, cap_nob, P, 0, stream, mc);
+        ensure(dmem, cbase, cap_cb, P + 1, 0, stream, mc);
+        ensure(dmem, obase, cap_ob, P + 1, 0, stream, mc);
+        ensure(dmem, mid_idx, cap_mid, P, 0, stream, mc);
+        ensure(dmem, fchild, cap_fch, lo + P + 1, lo + 1, stream, mc);
+        huge.ensure_members(dmem, P, stream, mc);
+        unsigned classes = (next_mid ? kLevelMid : 0u) | (next_huge ? kLevelHuge : 0u) |
+                           (next_huge && !fixed ? kLevelSide : 0u);
         bool redo;
         int redos = 0;
         uint64_t huge_seen = next_huge;  // huge parents counted by the last attempt
@@ -552,7 +641,7 @@ void fcbo_context::enumerate_levels()
             // a grown buffer always fits the redo; a class miss turns every kernel on
             if (redos > 3) throw HipError{FCBO_ERR_DEVICE};
             LevelArgs A = level_args(lo, P, obj_hi);
-            if (redos) CK(hipMemsetAsync(A.counters, 0, CNT_N * sizeof(uint64_t), stream));
+            if (redos) clear_words(A.counters, CNT_N);
             fns.tests(this, A, P, classes, redos ? huge_seen : next_huge);
             hipEvent_t b = prof_begin();
             // child offsets per parent, and the first child of every parent
@@ -560,20 +649,23 @@ void fcbo_context::enumerate_levels()
                  fchild + lo, lo + P);
             prof_end(FCBO_K_SCAN, b);
             CK(hipMemcpyAsync(h_counters, A.counters, CNT_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
-            if (!ev_counts) CK(hipEventCreateWithFlags(&ev_counts, hipEventDisableTiming));
-            CK(hipEventRecord(ev_counts, stream));
+            if (!fixed) {
+                if (!ev_counts) CK(hipEventCreateWithFlags(&ev_counts, hipEventDisableTiming));
+                CK(hipEventRecord(ev_counts, stream));
+            }
             // The children are written before the host has read the counts, so the
             // device works on while the host prepares the next level.  The write
             // kernels do nothing when the level overflowed or the store has no
             // room; both cases are handled below.
             fns.writes(this, A, P, classes, 0);
-            CK(hipEventSynchronize(ev_counts));
+            if (fixed) CK(hipStreamSynchronize(stream));
+            else CK(hipEventSynchronize(ev_counts));
             const uint64_t n_mid = h_counters[CNT_MID] + h_counters[CNT_MIDW];
             const unsigned found = (n_mid ? kLevelMid : 0u) | (h_counters[CNT_HUGE] ? kLevelHuge : 0u);
             huge_seen = h_counters[CNT_HUGE];
             if (found & ~classes) {  // parents of a class whose kernels did not run
                 classes |= found;
-                ensure(pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
+                ensure(dmem, pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
                 redo = true;
                 ++redos;
                 continue;
@@ -581,17 +673,17 @@ void fcbo_context::enumerate_levels()
             if (h_counters[CNT_OVERFLOW]) {
                 if (bm) {
                     ensure_huge_tests(h_counters[CNT_THUGE]);
-                    ensure(huge.bmp, huge.cap_bmp, h_counters[CNT_HUGE] * (uint64_t)wn, 0, stream, 1);
+                    ensure(dmem, huge.bmp, huge.cap_bmp, h_counters[CNT_HUGE] * (uint64_t)wn, 0, stream, 1);
                 } else {
-                    huge.ensure_tests(h_counters[CNT_THUGE], stream, mc);
+                    huge.ensure_tests(dmem, h_counters[CNT_THUGE], stream, mc);
                 }
                 uint64_t stripe_max = 0;
                 for (int t = 0; t < kRecStripes; ++t)
                     stripe_max = std::max<uint64_t>(stripe_max, h_counters[CNT_MIDREC + t * kCntPad]);
                 // headroom: the split of records over stripes varies from run to run
-                ensure(mrec, cap_mrec, stripe_max * kRecStripes * rstride / 4 * 5, 0, stream, 1);
-                ensure(wrec, cap_wrec, h_counters[CNT_WIDEREC] * rstride, 0, stream, 1);
-                ensure(pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
+                ensure(dmem, mrec, cap_mrec, stripe_max * kRecStripes * rstride / 4 * 5, 0, stream, 1);
+                ensure(dmem, wrec, cap_wrec, h_counters[CNT_WIDEREC] * rstride, 0, stream, 1);
+                ensure(dmem, pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
                 uint64_t lstripe_max = 0;
                 for (int t = 0; t < kRecStripes; ++t)
                     lstripe_max = std::max<uint64_t>(lstripe_max, h_counters[CNT_LOCREC + t * kCntPad]);
@@ -604,8 +696,7 @@ void fcbo_context::enumerate_levels()
             n_objs = h_counters[CNT_OBJS];
             next_mid = h_counters[CNT_NEXT_MID];
             next_huge = h_counters[CNT_NEXT_HUGE];
-            lev_concepts.push_back(P);
-            lev_tests.push_back(h_counters[CNT_TESTS]);
+            lev.push(P, h_counters[CNT_TESTS]);
             tests += h_counters[CNT_TESTS];
             pairs += h_counters[CNT_PAIRS];
             sum_c += n_objs;
@@ -616,16 +707,20 @@ void fcbo_context::enumerate_levels()
             med_objs += h_counters[CNT_MID_OBJS];
             big_tests += h_counters[CNT_THUGE];
             big_scan += h_counters[CNT_BIG_SCAN];
+            big_nzw += h_counters[CNT_HUGE_NZW];
+            big_cobjs += h_counters[CNT_HUGE_COBJS];
             // room for the children in the store; the writes issued above did
             // nothing if it had to grow
             const uint64_t k_end = lo + P + n_children;
             const uint64_t keep_k = lo + P;
+            // first-child offsets (u32) of this level already wrapped if so
+            if (k_end >= (1ull << 32)) throw HipError{FCBO_ERR_LIMIT};
             const bool had_room = k_end <= A.child_cap && obj_hi + n_objs <= A.obj_cap;
-            ensure(intents, cap_int, k_end * wm, keep_k * wm, stream, mc);
-            ensure(cursor, cap_cur, k_end, keep_k, stream, mc);
-            ensure(loff, cap_loff, k_end + 1, keep_k + 1, stream, mc);
-            ensure(objs, cap_o, obj_hi + n_objs, obj_hi, stream, mc);
-            ensure(fchild, cap_fch, k_end + 1, keep_k + 1, stream, mc);
+            ensure(dmem, intents, cap_int, k_end * wm, keep_k * wm, stream, mc);
+            ensure(dmem, cursor, cap_cur, k_end, keep_k, stream, mc);
+            ensure(dmem, loff, cap_loff, k_end + 1, keep_k + 1, stream, mc);
+            ensure(dmem, objs, cap_o, obj_hi + n_objs, obj_hi, stream, mc);
+            ensure(dmem, fchild, cap_fch, k_end + 1, keep_k + 1, stream, mc);
             if (n_children && !had_room) fns.writes(this, level_args(lo, P, obj_hi), P, classes, 0);
         } while (redo);
         ctr ^= 1;
@@ -640,13 +735,12 @@ void fcbo_context::enumerate_levels()
 
 void fcbo_context::order_concepts()
 {
-    if (K >= (1ull << 32)) throw HipError{FCBO_ERR_CAPACITY};
+    if (K >= (1ull << 32)) throw HipError{FCBO_ERR_LIMIT};
     const uint64_t mc = min_cap();
-    ensure(rank, cap_rank, K, 0, stream, mc);
-    ensure(perm, cap_perm, K, 0, stream, mc);
-    const size_t nlev = lev_concepts.size();
-    std::vector<uint64_t> lev_lo(nlev + 1, 0);
-    for (size_t l = 0; l < nlev; ++l) lev_lo[l + 1] = lev_lo[l] + lev_concepts[l];
+    ensure(dmem, rank, cap_rank, K, 0, stream, mc);
+    ensure(dmem, perm, cap_perm, K, 0, stream, mc);
+    const size_t nlev = lev.size();
+    const uint64_t *lev_concepts = lev.concepts, *lev_lo = lev.lo;
     auto grid = [](uint64_t n) { return (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(n, kBlock))); };
     auto wgrid = [](uint64_t n) {
         return (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(n, kWavesPerBlock)));
@@ -682,24 +776,29 @@ void fcbo_context::order_concepts()
     have_perm = true;
 }
 
-void fcbo_context::write_output(uint64_t *intents_out, uint64_t *extents_out)
+// Output rows [first, first + count): row r of the buffers gets the concept at
+// output position first + r.  Either buffer may be null.
+void fcbo_context::write_output(uint64_t *intents_out, uint64_t *extents_out, uint64_t first, uint64_t count)
 {
     hipEvent_t b = prof_begin();
+    const uint32_t *pm = perm + first;
     const uint64_t row_bytes = (uint64_t)wn * 8;
     if (extents_out && row_bytes > (uint64_t)kOutBlockBytes) {
         // rows wider than the LDS tile: one wavefront per row, tile by tile
-        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(8192, div_up(K, kWavesPerBlock)));
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(8192, div_up(count, kWavesPerBlock)));
         hipLaunchKernelGGL(k_output, dim3(g), dim3(kBlock), 0, stream, (const uint64_t *)intents,
-                           (const uint64_t *)loff, (const uint32_t *)objs, (const uint32_t *)perm, K, wm, wn,
-                           intents_out, extents_out);
+                           (const uint64_t *)loff, (const uint32_t *)objs, pm, count, wm, wn, intents_out,
+                           extents_out);
         CK_LAUNCH();
         prof_end(FCBO_K_OUTPUT, b);
         return;
     }
     // the ordered intents, then (with an extent buffer) the extent row blocks
-    hipLaunchKernelGGL(k_output_intents, dim3(kGridCap), dim3(kBlock), 0, stream, (const uint64_t *)intents,
-                       (const uint32_t *)perm, K, wm, intents_out);
-    CK_LAUNCH();
+    if (intents_out) {
+        hipLaunchKernelGGL(k_output_intents, dim3(kGridCap), dim3(kBlock), 0, stream, (const uint64_t *)intents, pm,
+                           count, wm, intents_out);
+        CK_LAUNCH();
+    }
     if (extents_out) {
         // Rows per block: a multiple of L/gcd(wn, L), L the words of a cache
         // line, makes the block's region a whole number of lines; aim for
@@ -715,14 +814,73 @@ void fcbo_context::write_output(uint64_t *intents_out, uint64_t *extents_out)
         const size_t lds = (size_t)R * wn * 8;
         int per_cu = 1;
         CK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_output_block, kOutThreads, lds));
-        const uint64_t nblk = div_up(K, (uint64_t)R);
+        const uint64_t nblk = div_up(count, (uint64_t)R);
         const uint64_t slots = (uint64_t)n_cu * std::max(1, per_cu);
         const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(nblk, slots));
         hipLaunchKernelGGL(k_output_block, dim3(g), dim3(kOutThreads), lds, stream, (const uint64_t *)loff,
-                           (const uint32_t *)objs, (const uint32_t *)perm, K, wn, R, extents_out);
+                           (const uint32_t *)objs, pm, count, wn, R, extents_out);
         CK_LAUNCH();
     }
     prof_end(FCBO_K_OUTPUT, b);
+}
+
+// Algorithmic bytes of the last enumeration (the formula in fcbo.h, with the
+// row-local threshold of the class split: 4096 objects up to eight intent
+// words, else 64).
+uint64_t fcbo_context::model_bytes() const
+{
+    if (!have_result) return 0;
+    const uint64_t W_M = (uint64_t)wm, W_N = (uint64_t)wn;
+    uint64_t b = K * (8 * W_M + 4 + 16);             // every concept read once as a parent
+    b += (local_objs + med_objs) * (4 + 8 * W_M);   // row-local parents: list entries and rows
+    b += big_parents * 8 * W_N;                      // larger parents: extent bitmap
+    b += big_nzw * 8;                                // their tests: non-zero column words
+    b += big_cobjs * 8 * W_M;                        // their children: rows of C
+    b += (K - 1) * (8 * W_M + 4 + 8) + 4 * sum_c;    // children written
+    b += (uint64_t)n * (8 * W_M + 4);                // the root
+    return b;
+}
+
+// The context on the device: rows copied and masked, columns transposed.
+// Fixed contexts take these buffers from the static region too and keep the
+// counters' host copy in the context itself.
+void fcbo_context::setup(const uint64_t *rows_in, int64_t n_objects, int64_t n_attrs, int64_t row_stride_words,
+                         bool rows_on_device)
+{
+    CK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device));
+    n = n_objects;
+    m = n_attrs;
+    wn = (int)((n_objects + 63) / 64);
+    wm = (int)((n_attrs + 63) / 64);
+    tail_m = (n_attrs & 63) ? ((1ull << (n_attrs & 63)) - 1ull) : ~0ull;
+    tail_n = (n_objects & 63) ? ((1ull << (n_objects & 63)) - 1ull) : ~0ull;
+    const uint64_t row_words = ((uint64_t)n_objects + 1) * wm;  // a zero row after the last
+    const uint64_t col_words = (uint64_t)n_attrs * wn;
+    if (fixed) {
+        rows = (uint64_t *)dmem.get(row_words * sizeof(uint64_t));
+        cols = (uint64_t *)dmem.get(col_words * sizeof(uint64_t));
+        scan_part = (uint64_t *)dmem.get(2 * kScanBlocks * sizeof(uint64_t));
+        counters = (uint64_t *)dmem.get(2 * CNT_N * sizeof(uint64_t));
+        h_counters = h_counters_own;
+    } else {
+        CK(hipMalloc((void **)&rows, row_words * sizeof(uint64_t)));
+        CK(hipMalloc((void **)&cols, col_words * sizeof(uint64_t)));
+        CK(hipMalloc((void **)&scan_part, 2 * kScanBlocks * sizeof(uint64_t)));
+        CK(hipMalloc((void **)&counters, 2 * CNT_N * sizeof(uint64_t)));
+        CK(hipHostMalloc((void **)&h_counters, CNT_N * sizeof(uint64_t), hipHostMallocDefault));
+    }
+    clear_words(rows, row_words);
+    const hipMemcpyKind kind = rows_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+    CK(hipMemcpy2DAsync(rows, (size_t)wm * sizeof(uint64_t), rows_in, (size_t)row_stride_words * sizeof(uint64_t),
+                        (size_t)wm * sizeof(uint64_t), (size_t)n_objects, kind, stream));
+    hipLaunchKernelGGL(k_mask_rows, dim3((unsigned)div_up((uint64_t)n_objects, kBlock)), dim3(kBlock), 0, stream, rows,
+                       (int)n_objects, wm, tail_m);
+    CK_LAUNCH();
+    const uint64_t waves = (uint64_t)wn * wm;
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)div_up(waves, kWavesPerBlock)), dim3(kBlock), 0, stream,
+                       (const uint64_t *)rows, cols, (int)n_objects, (int)n_attrs, wn, wm);
+    CK_LAUNCH();
+    CK(hipStreamSynchronize(stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -738,48 +896,36 @@ const char *fcbo_error_string(int code)
     case FCBO_ERR_OUT_OF_MEMORY: return "device out of memory";
     case FCBO_ERR_DEVICE: return "HIP device error";
     case FCBO_ERR_CAPACITY: return "output capacity too small";
+    case FCBO_ERR_LIMIT: return "2^32 concepts or more (beyond the 32-bit concept indices)";
     default: return "unknown error";
     }
 }
+
+namespace {
+
+bool valid_context_args(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, int64_t row_stride_words)
+{
+    return rows && n_objects >= 1 && n_objects <= INT32_MAX && n_attrs >= 1 && n_attrs <= 4096 &&
+           row_stride_words >= (n_attrs + 63) / 64;
+}
+
+}  // namespace
 
 int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, int64_t row_stride_words,
                         uint32_t flags, void *hip_stream, fcbo_context **out)
 {
     if (!out) return FCBO_ERR_INVALID_ARGUMENT;
     *out = nullptr;
-    if (!rows || n_objects < 1 || n_objects > INT32_MAX || n_attrs < 1 || n_attrs > 4096 ||
-        row_stride_words < (n_attrs + 63) / 64 || (flags & ~(FCBO_ROWS_ON_DEVICE | FCBO_TINY_BUFFERS)))
+    if (!valid_context_args(rows, n_objects, n_attrs, row_stride_words) ||
+        (flags & ~(FCBO_ROWS_ON_DEVICE | FCBO_TINY_BUFFERS)))
         return FCBO_ERR_INVALID_ARGUMENT;
     fcbo_context *c = new (std::nothrow) fcbo_context();
     if (!c) return FCBO_ERR_OUT_OF_MEMORY;
     try {
         CK(hipGetDevice(&c->device));
-        CK(hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device));
         c->stream = (hipStream_t)hip_stream;
         c->tiny = (flags & FCBO_TINY_BUFFERS) != 0;
-        c->n = n_objects;
-        c->m = n_attrs;
-        c->wn = (int)((n_objects + 63) / 64);
-        c->wm = (int)((n_attrs + 63) / 64);
-        c->tail_m = (n_attrs & 63) ? ((1ull << (n_attrs & 63)) - 1ull) : ~0ull;
-        c->tail_n = (n_objects & 63) ? ((1ull << (n_objects & 63)) - 1ull) : ~0ull;
-        CK(hipMalloc((void **)&c->rows, ((uint64_t)n_objects + 1) * c->wm * sizeof(uint64_t)));
-        CK(hipMalloc((void **)&c->cols, (uint64_t)n_attrs * c->wn * sizeof(uint64_t)));
-        CK(hipMalloc((void **)&c->scan_part, 2 * kScanBlocks * sizeof(uint64_t)));
-        CK(hipMalloc((void **)&c->counters, 2 * CNT_N * sizeof(uint64_t)));
-        CK(hipHostMalloc((void **)&c->h_counters, CNT_N * sizeof(uint64_t), hipHostMallocDefault));
-        CK(hipMemsetAsync(c->rows, 0, ((uint64_t)n_objects + 1) * c->wm * sizeof(uint64_t), c->stream));
-        const hipMemcpyKind kind = (flags & FCBO_ROWS_ON_DEVICE) ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
-        CK(hipMemcpy2DAsync(c->rows, (size_t)c->wm * sizeof(uint64_t), rows, (size_t)row_stride_words * sizeof(uint64_t),
-                            (size_t)c->wm * sizeof(uint64_t), (size_t)n_objects, kind, c->stream));
-        hipLaunchKernelGGL(k_mask_rows, dim3((unsigned)div_up((uint64_t)n_objects, kBlock)), dim3(kBlock), 0,
-                           c->stream, c->rows, (int)n_objects, c->wm, c->tail_m);
-        CK_LAUNCH();
-        const uint64_t waves = (uint64_t)c->wn * c->wm;
-        hipLaunchKernelGGL(k_transpose, dim3((unsigned)div_up(waves, kWavesPerBlock)), dim3(kBlock), 0, c->stream,
-                           (const uint64_t *)c->rows, c->cols, (int)n_objects, (int)n_attrs, c->wn, c->wm);
-        CK_LAUNCH();
-        CK(hipStreamSynchronize(c->stream));
+        c->setup(rows, n_objects, n_attrs, row_stride_words, (flags & FCBO_ROWS_ON_DEVICE) != 0);
     } catch (const HipError &e) {
         c->free_all();
         delete c;
@@ -821,34 +967,37 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
         } else {
             if (!(reuse && ctx->have_perm)) ctx->order_concepts();
             CK(hipEventRecord(e2, ctx->stream));
-            ctx->write_output(intents_out, extents_out);
+            ctx->write_output(intents_out, extents_out, 0, ctx->K);
             CK(hipEventRecord(e3, ctx->stream));
             CK(hipStreamSynchronize(ctx->stream));
             float ms = 0;
             CK(hipEventElapsedTime(&ms, e0, e3));
             st.enumerate_ms = ms;
             CK(hipEventElapsedTime(&ms, e1, e2));
-            st.order_ms = ms;
+            st.sort_ms = ms;
             CK(hipEventElapsedTime(&ms, e2, e3));
             st.output_ms = ms;
         }
         float ms = 0;
         CK(hipEventElapsedTime(&ms, e0, e1));
-        st.levels_ms = ms;
+        st.closure_kernel_ms = ms;
         for (auto &mk : ctx->marks) {
             CK(hipEventElapsedTime(&ms, mk.second.first, mk.second.second));
             st.kernel_ms[mk.first] += ms;
             st.kernel_launches[mk.first] += 1;
         }
     } catch (const HipError &e) {
+        ctx->have_result = ctx->have_perm = false;
         return e.code;
     } catch (const std::bad_alloc &) {
+        ctx->have_result = ctx->have_perm = false;
         return FCBO_ERR_OUT_OF_MEMORY;
     }
     st.n_concepts = ctx->K;
+    st.model_bytes = ctx->model_bytes();
     st.closure_tests = ctx->tests;
     st.item_pairs = ctx->pairs;
-    st.n_levels = ctx->lev_concepts.size();
+    st.n_levels = ctx->lev.size();
     st.sum_child_objects = ctx->sum_c;
     st.local_parents = ctx->local_parents;
     st.local_parent_objects = ctx->local_objs;
@@ -857,6 +1006,8 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
     st.big_parents = ctx->big_parents;
     st.big_tests = ctx->big_tests;
     st.big_scanned_objects = ctx->big_scan;
+    st.big_nonzero_words = ctx->big_nzw;
+    st.big_child_objects = ctx->big_cobjs;
     st.order_launches = ctx->order_launches;
     if (rc == FCBO_OK)
         st.output_bytes = ctx->K * (uint64_t)ctx->wm * 8 + (extents_out ? ctx->K * (uint64_t)ctx->wn * 8 : 0);
@@ -864,15 +1015,50 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
     return rc;
 }
 
+int fcbo_write_range(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_t *intents_out,
+                     uint64_t *extents_out)
+{
+    if (!ctx || (!intents_out && !extents_out) || !ctx->have_result || first > ctx->K || count > ctx->K - first)
+        return FCBO_ERR_INVALID_ARGUMENT;
+    try {
+        CK(hipSetDevice(ctx->device));
+        ctx->profile = false;
+        ctx->ev_used = 0;
+        ctx->marks.clear();
+        if (!ctx->have_perm) ctx->order_concepts();
+        if (count) ctx->write_output(intents_out, extents_out, first, count);
+        CK(hipStreamSynchronize(ctx->stream));
+    } catch (const HipError &e) {
+        return e.code;
+    } catch (const std::bad_alloc &) {
+        return FCBO_ERR_OUT_OF_MEMORY;
+    }
+    return FCBO_OK;
+}
+
+int fcbo_set_memory_limit(fcbo_context *ctx, uint64_t bytes)
+{
+    if (!ctx) return FCBO_ERR_INVALID_ARGUMENT;
+    ctx->dmem.limit = bytes;
+    if (bytes && ctx->dmem.held > bytes) {
+        // the cap holds from now on: the buffers (and the result in them) go
+        hipError_t e = hipSetDevice(ctx->device);
+        if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+        if (e != hipSuccess) return map_error(e);
+        ctx->free_buffers();
+    }
+    return FCBO_OK;
+}
+
 int fcbo_level_counts(const fcbo_context *ctx, uint64_t *concepts_per_level, uint64_t *tests_per_level,
                       uint64_t max_levels, uint64_t *n_levels_out)
 {
     if (!ctx || !ctx->have_result) return FCBO_ERR_INVALID_ARGUMENT;
-    const uint64_t nl = ctx->lev_concepts.size();
+    const uint64_t nl = ctx->lev.size();
     if (n_levels_out) *n_levels_out = nl;
     for (uint64_t i = 0; i < nl && i < max_levels; ++i) {
-        if (concepts_per_level) concepts_per_level[i] = ctx->lev_concepts[i];
-        if (tests_per_level) tests_per_level[i] = ctx->lev_tests[i];
+        if (concepts_per_level) concepts_per_level[i] = ctx->lev.concepts[i];
+        if (tests_per_level) tests_per_level[i] = ctx->lev.tests[i];
     }
     return FCBO_OK;
 }

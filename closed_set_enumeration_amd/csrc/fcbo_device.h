@@ -78,9 +78,11 @@ enum {
     CNT_NEXT_MID = 13 * kCntPad, // children that will be mid parents (64 < |C| <= mid_max)
     CNT_NEXT_HUGE = 14 * kCntPad, // children that will be huge parents (|C| > mid_max)
     CNT_WIDEREC = 15 * kCntPad,  // child records of the wide mid parents
-    CNT_MIDREC = 16 * kCntPad,   // kRecStripes counters, one line each: mid record slots per stripe
-    CNT_LOCREC = (16 + kRecStripes) * kCntPad,  // kRecStripes counters: local record slots per stripe
-    CNT_N = (16 + 2 * kRecStripes) * kCntPad  // words of one level's counters
+    CNT_HUGE_NZW = 16 * kCntPad, // sum over huge parents of tests x non-zero words of the extent
+    CNT_HUGE_COBJS = 17 * kCntPad, // objects of the huge parents' children
+    CNT_MIDREC = 18 * kCntPad,   // kRecStripes counters, one line each: mid record slots per stripe
+    CNT_LOCREC = (18 + kRecStripes) * kCntPad,  // kRecStripes counters: local record slots per stripe
+    CNT_N = (18 + 2 * kRecStripes) * kCntPad  // words of one level's counters
 };
 
 // Huge parents, tested one closure test at a time: one work item per (test,
@@ -118,7 +120,8 @@ struct LevelArgs {
     uint64_t *pass;        // per huge parent (member index), wm words: its passing attributes
     uint64_t pass_cap;     // huge parents pass can hold
     uint32_t *nchild;      // children per parent
-    uint32_t *nobj;        // objects in the children's extents per parent
+    uint64_t *nobj;        // objects in the children's extents per parent (a huge parent's
+                           // children can hold more than 2^32 objects together)
     uint64_t *cbase;       // exclusive scan of nchild (P + 1)
     uint64_t *obase;       // exclusive scan of nobj (P + 1)
     uint32_t *mid_idx;     // mid parents (order not fixed)
@@ -328,6 +331,14 @@ __device__ __forceinline__ int select_words(const uint64_t (&x)[WMC], int wm, in
 
 // ---------------------------------------------------------------------------
 // context construction
+
+// p[0, n) = v.  Used wherever a buffer must start cleared (a kernel rather
+// than a memset node, so the clears behave the same in any launch context).
+__global__ void __launch_bounds__(kBlock) k_fill_u64(uint64_t *p, uint64_t n, uint64_t v)
+{
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
 
 // Clear the bits past the last attribute in every row.
 __global__ void k_mask_rows(uint64_t *rows, int n, int wm, uint64_t tail_m)
@@ -980,6 +991,9 @@ __global__ void __launch_bounds__(kBlock) k_huge_tasks(LevelArgs A)
                 cand[u] = ~bx & above_mask(y, u);
             }
         }
+        // non-zero words of the extent (the column words a test needs), for
+        // the statistics' byte count
+        uint32_t nzw = 0;
         if (S.bmp) {
             uint64_t *row = S.bmp + bi * (uint64_t)A.wn;
             for (int w = lane; w < A.wn; w += kWave) {
@@ -996,9 +1010,17 @@ __global__ void __launch_bounds__(kBlock) k_huge_tasks(LevelArgs A)
                     }
                 }
                 row[w] = v;
+                nzw += v != 0 ? 1u : 0u;
             }
+        } else {
+            // the sorted list: one word per run of objects with equal g >> 6
+            const uint64_t o0 = A.loff[c0], o1 = A.loff[c0 + 1];
+            for (uint64_t o = o0 + lane; o < o1; o += kWave)
+                nzw += (o == o0 || (A.objs[o - 1] >> 6) != (A.objs[o] >> 6)) ? 1u : 0u;
         }
         const uint32_t n = S.n[bi];
+        const uint64_t znz = (uint64_t)wave_sum(nzw) * n;
+        if (lane == 0 && znz) atomicAdd((unsigned long long *)&A.counters[CNT_HUGE_NZW], (unsigned long long)znz);
         const uint64_t base = S.off[bi];
         for (uint32_t k = lane; k < n; k += kWave) {
             S.tasks[base + k] = (bi << 16) | (uint64_t)select_words<WMC>(cand, wm, (int)k);
@@ -1017,7 +1039,8 @@ __device__ __forceinline__ void big_record_pass(const LevelArgs &A, const BigSet
 {
     atomicOr((unsigned long long *)&A.pass[bi * A.wm + (j >> 6)], (unsigned long long)(1ull << (j & 63)));
     atomicAdd(&A.nchild[p], 1u);
-    atomicAdd(&A.nobj[p], cnt);
+    atomicAdd((unsigned long long *)&A.nobj[p], (unsigned long long)cnt);
+    atomicAdd((unsigned long long *)&A.counters[CNT_HUGE_COBJS], (unsigned long long)cnt);
     const uint64_t pos = atomicAdd((unsigned long long *)&A.counters[S.pass_slot], 1ull);
     S.plist[pos] = t;
     if (cnt > (uint32_t)A.mid_max)
@@ -1807,7 +1830,7 @@ __global__ void __launch_bounds__(kBlock) k_huge_write(LevelArgs A)
 }
 
 // ---------------------------------------------------------------------------
-// exclusive scan of one or two u32 arrays into u64 offsets, n read from the
+// exclusive scan of a u32 array (and optionally a u64 one) into u64 offsets, n read from the
 // device (n_dev, clamped to n_cap) or given by the host (n_dev == nullptr).
 // out[n] receives the total; *tot (optional) too.
 
@@ -1817,7 +1840,7 @@ __device__ __forceinline__ uint64_t scan_count(const uint64_t *n_dev, uint64_t n
     return n < n_cap ? n : n_cap;
 }
 
-__global__ void __launch_bounds__(kBlock) k_scan_up(const uint32_t *__restrict__ a, const uint32_t *__restrict__ b,
+__global__ void __launch_bounds__(kBlock) k_scan_up(const uint32_t *__restrict__ a, const uint64_t *__restrict__ b,
                                                      const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
                                                      uint64_t *part)
 {
@@ -1887,7 +1910,7 @@ __global__ void __launch_bounds__(kScanBlocks) k_scan_mid(uint64_t *part, int nb
     }
 }
 
-__global__ void __launch_bounds__(kBlock) k_scan_down(const uint32_t *__restrict__ a, const uint32_t *__restrict__ b,
+__global__ void __launch_bounds__(kBlock) k_scan_down(const uint32_t *__restrict__ a, const uint64_t *__restrict__ b,
                                                        const uint64_t *n_dev, uint64_t n_host, uint64_t n_cap,
                                                        const uint64_t *part, uint64_t *out_a, uint64_t *out_b,
                                                        uint32_t *fch, uint64_t fbase)
@@ -1919,7 +1942,7 @@ __global__ void __launch_bounds__(kBlock) k_scan_down(const uint32_t *__restrict
 // The same scan in one workgroup of kScanBlocks threads, for short arrays
 // whose length the host knows.
 __global__ void __launch_bounds__(kScanBlocks) k_scan_small(const uint32_t *__restrict__ a,
-                                                            const uint32_t *__restrict__ b, const uint64_t *n_dev,
+                                                            const uint64_t *__restrict__ b, const uint64_t *n_dev,
                                                             uint64_t n_arg, uint64_t *out_a, uint64_t *out_b,
                                                             uint64_t *tot_a, uint64_t *tot_b, uint32_t *fch,
                                                             uint64_t fbase)
@@ -2080,7 +2103,8 @@ __global__ void __launch_bounds__(kBlock) k_output(const uint64_t *__restrict__ 
     uint64_t *T = s_tile[wv];
     for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + wv; i < K; i += (uint64_t)gridDim.x * kWavesPerBlock) {
         const uint64_t src = perm[i];
-        for (int u = lane; u < wm; u += kWave) intents_out[i * wm + u] = intents[src * wm + u];
+        if (intents_out)
+            for (int u = lane; u < wm; u += kWave) intents_out[i * wm + u] = intents[src * wm + u];
         if (!extents_out) continue;
         uint64_t o = loff[src];
         const uint64_t o1 = loff[src + 1];

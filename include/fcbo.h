@@ -23,12 +23,16 @@
  * holding the smallest attribute in which they differ comes later (so the
  * root, whose intent is contained in every other, is first).  Intents are
  * pairwise distinct, so the order is total and the output is byte-for-byte
- * unique.
+ * unique.  "Output position" below means the index of a concept in this order.
  *
  * Errors are reported only by return code; no call aborts or throws.  A HIP
  * failure maps to FCBO_ERR_DEVICE (FCBO_ERR_OUT_OF_MEMORY for allocation) and
- * leaves the context safe to destroy.  A context must not be used from two
- * host threads at once.
+ * leaves the context safe to destroy.  After any error from fcbo_enumerate the
+ * context holds no result (a later FCBO_REUSE_RESULT call enumerates again).
+ * A context must not be used from two host threads at once.
+ *
+ * Limits: 1 <= N <= 2^31 - 1 objects, 1 <= M <= 4096 attributes, fewer than
+ * 2^32 concepts (concept indices are 32-bit on the device).
  */
 #ifndef FCBO_H
 #define FCBO_H
@@ -43,20 +47,21 @@ typedef struct fcbo_context fcbo_context; /* opaque, owned by the library */
 
 enum {
     FCBO_OK = 0,
-    FCBO_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, bad flag */
-    FCBO_ERR_OUT_OF_MEMORY = -2,    /* a device allocation failed */
+    FCBO_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, bad flag, no result yet */
+    FCBO_ERR_OUT_OF_MEMORY = -2,    /* a device allocation failed or the memory limit was hit */
     FCBO_ERR_DEVICE = -3,           /* any other HIP runtime failure */
-    FCBO_ERR_CAPACITY = -4          /* output buffers hold fewer rows than concepts */
+    FCBO_ERR_CAPACITY = -4,         /* output buffers hold fewer rows than concepts (or edges) */
+    FCBO_ERR_LIMIT = -5             /* 2^32 concepts or more: beyond the 32-bit concept indices */
 };
 
 /* fcbo_context_create flags */
 #define FCBO_ROWS_ON_DEVICE 1u /* rows is a device pointer (else host memory) */
-#define FCBO_TINY_BUFFERS 2u   /* start every device buffer at its minimum size, so growth
-                                  and the level redo run on any input (for tests) */
+#define FCBO_TINY_BUFFERS 2u   /* test hook: start every device buffer at its minimum size, so
+                                  growth and the level redo run on any input */
 
 /* fcbo_enumerate flags */
 #define FCBO_REUSE_RESULT 1u /* reuse the concepts of the previous call if any */
-#define FCBO_PROFILE 2u      /* time every kernel with HIP events (fills kernel_ms) */
+#define FCBO_PROFILE 2u      /* time every kernel class with HIP events (fills kernel_ms) */
 
 /* Kernel classes reported in fcbo_stats.kernel_ms / kernel_launches. */
 enum {
@@ -74,31 +79,67 @@ enum {
     FCBO_K_NUM_CLASSES = 10
 };
 
+/*
+ * Statistics of one fcbo_enumerate call.  The first eight fields are the
+ * measurement record of the method (concept count, closure tests, item pairs,
+ * levels, times, algorithmic bytes); the rest break the work down by the
+ * library's parent classes.
+ *
+ * A closure test is one (parent, j) with j > cursor and j not in B (page 1,
+ * section 2.1; saturated j in B are skipped without a test, section 2.3); an
+ * item pair is one (parent, j) with j > cursor (page 4, section 2.1 counts
+ * parents x attributes).
+ *
+ * model_bytes: the algorithmic bytes of the enumeration (root to last level),
+ * independent of how the kernels are scheduled.  Parents whose extent has at
+ * most T objects are tested row-locally (T = 4096 when M <= 512, else 64):
+ *     K * (8 W_M + 4 + 16)                  every concept read once as a parent:
+ *                                           intent, cursor, extent-list bounds
+ *   + S_rl * (4 + 8 W_M)                    row-local parents: each object's list
+ *                                           entry and row, once
+ *   + P_col * 8 W_N                         larger parents: extent bitmap, once
+ *   + Z_col * 8                             their tests: the words of col[j] where
+ *                                           the extent is non-zero (page 1 section
+ *                                           4.2 skips the zero words)
+ *   + C_col * 8 W_M                         their children: the rows of C
+ *   + (K - 1) * (8 W_M + 4 + 8) + 4 sum|C|  every child written: intent, cursor,
+ *                                           list offset, extent list
+ *   + N * (8 W_M + 4)                       the root: all rows read, its list
+ * with W_N = ceil(N/64), W_M = ceil(M/64), S_rl the objects of the row-local
+ * parents' extents, P_col the larger parents, Z_col the sum over their tests
+ * of the non-zero words of their extent, C_col the objects of their children.
+ */
 typedef struct {
-    uint64_t n_concepts;    /* K */
-    uint64_t closure_tests; /* (parent, j) with j > cursor and j not in B */
-    uint64_t item_pairs;    /* (parent, j) with j > cursor */
-    uint64_t n_levels;      /* levels of the CbO tree, root level included */
+    uint64_t n_concepts;        /* K */
+    uint64_t closure_tests;     /* (parent, j) with j > cursor and j not in B */
+    uint64_t item_pairs;        /* (parent, j) with j > cursor */
+    uint64_t n_levels;          /* levels of the CbO tree, root level included */
+    double enumerate_ms;        /* whole call on the device stream (HIP events) */
+    double closure_kernel_ms;   /* the level loop: root to last level, closure tests, scans,
+                                   child writes and the per-level host wait (HIP events) */
+    double sort_ms;             /* output order: positions from the CbO tree */
+    uint64_t model_bytes;       /* algorithmic bytes of the level loop (formula above) */
+    double output_ms;           /* writing the caller's buffers */
     uint64_t sum_child_objects; /* sum of |C| over all concepts except the root */
-    uint64_t output_bytes;  /* bytes written to the caller's buffers */
-    uint64_t local_parents; /* parents with <= 64 objects (packed local test kernel) */
-    uint64_t local_parent_objects; /* objects in their extents (rows staged) */
-    uint64_t medium_parents; /* parents of the medium class (tests by incidence) */
+    uint64_t output_bytes;      /* bytes written to the caller's buffers */
+    uint64_t local_parents;     /* parents with <= 64 objects (packed local test kernel) */
+    uint64_t local_parent_objects;  /* objects in their extents (rows staged) */
+    uint64_t medium_parents;    /* parents of the medium class (tests by incidence) */
     uint64_t medium_parent_objects; /* objects in their extents */
-    uint64_t big_parents;   /* larger parents (tests split in 64-word extent chunks or list scans) */
-    uint64_t big_tests;     /* closure tests made by them */
-    uint64_t big_scanned_objects; /* extent-list entries read by those tests */
-    uint64_t order_launches; /* kernel launches of the last output ordering */
-    double enumerate_ms;    /* whole call on the device stream (HIP events) */
-    double levels_ms;       /* enumeration part (root to last level) */
-    double order_ms;        /* output ordering (subtree sizes, positions) */
-    double output_ms;       /* writing the caller's buffers */
+    uint64_t big_parents;       /* larger parents (tests split in 64-word extent chunks or list scans) */
+    uint64_t big_tests;         /* closure tests made by them */
+    uint64_t big_scanned_objects;   /* extent-list entries read by those tests */
+    uint64_t big_nonzero_words; /* Z_col above: sum over their tests of the extent's non-zero words */
+    uint64_t big_child_objects; /* C_col above: objects of their children */
+    uint64_t order_launches;    /* kernel launches of the last output ordering */
     double kernel_ms[FCBO_K_NUM_CLASSES];       /* with FCBO_PROFILE only */
     uint64_t kernel_launches[FCBO_K_NUM_CLASSES];
 } fcbo_stats;
 
 /*
- * Build a context from the 0/1 row bitmap.
+ * Build a context from the 0/1 object x attribute table (page 1 section 1.1,
+ * page 4 section 1.1), kept on the device as rows and as their transpose, the
+ * columns (page 1 section 3.1, page 4 sections 2.3 and 3.1).
  *   rows              row g (the attributes of object g) starts at
  *                     rows + g * row_stride_words; host memory, or device
  *                     memory on the current HIP device with FCBO_ROWS_ON_DEVICE.
@@ -107,40 +148,72 @@ typedef struct {
  *   n_objects         N, 1 <= N <= 2^31 - 1
  *   n_attrs           M, 1 <= M <= 4096
  *   row_stride_words  >= ceil(M / 64)
+ *   flags             FCBO_ROWS_ON_DEVICE, FCBO_TINY_BUFFERS
  *   hip_stream        hipStream_t the calls are ordered on, or NULL for the null
  *                     stream.  Independent parts of a level also run on two
  *                     internal streams of the context (default priority) that
  *                     fork from and join back to this one through events.
  *   out               receives the context
- * The device holds the rows (N x ceil(M/64) words) and their transpose, the
- * columns (M x ceil(N/64) words, column j = objects having attribute j).
- * Returns FCBO_OK or an error code; *out is NULL on error.
+ * The device holds the rows (N x ceil(M/64) words) and the columns
+ * (M x ceil(N/64) words, column j = objects having attribute j).
+ * Returns FCBO_OK, FCBO_ERR_INVALID_ARGUMENT (bad sizes or flags, null
+ * pointers), FCBO_ERR_OUT_OF_MEMORY or FCBO_ERR_DEVICE; *out is NULL on error.
  */
 int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs,
                         int64_t row_stride_words, uint32_t flags, void *hip_stream,
                         fcbo_context **out);
 
 /*
- * Enumerate all concepts and write them, in the output order above, to
- * caller-owned device buffers on the context's device.
+ * Enumerate all concepts with Close-by-One (page 1 sections 2.1-2.3 and
+ * 4.2-4.4; page 4 sections 1.2, 2.1 and 3.2; level by level as page 4 section
+ * 2.1 expands the tree, with page 1's canonical test so no concept repeats)
+ * and write them in the output order (page 1 section 6.2) to caller-owned
+ * device buffers on the context's device.
  *   intents_out   K x ceil(M/64) words, row i = intent of concept i
  *   extents_out   K x ceil(N/64) words in the same order, or NULL to skip
  *   capacity      rows available in the output buffers
  *   flags         FCBO_REUSE_RESULT, FCBO_PROFILE
- *   n_concepts_out receives K (also on FCBO_ERR_CAPACITY)
+ *   n_concepts_out receives K (also on FCBO_ERR_CAPACITY); may be NULL
  *   stats_out     optional statistics, or NULL
  * If intents_out is NULL or capacity < K the call returns FCBO_ERR_CAPACITY,
  * stores K and writes nothing; the concepts stay in the context, so a second
  * call with FCBO_REUSE_RESULT and large enough buffers only orders and writes.
- * The call returns after the stream has finished the work.
+ * Device buffers grow as the levels need (page 4 section 4.1); a failed
+ * allocation or the memory limit gives FCBO_ERR_OUT_OF_MEMORY, 2^32 concepts
+ * or more FCBO_ERR_LIMIT.  The call returns after the stream has finished.
  */
 int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_out,
                    uint64_t capacity, uint32_t flags, uint64_t *n_concepts_out,
                    fcbo_stats *stats_out);
 
 /*
- * Per-level counts of the last enumeration: concepts generated on level k
- * (level 0 is the root) and closure tests made by the concepts of level k.
+ * Write the output rows [first, first + count) of the last enumeration: row r
+ * of intents_out / extents_out receives the concept at output position
+ * first + r.  Either buffer may be NULL (not both).  With it a caller pages
+ * the output through bounded device buffers (page 1 section 6.1 moves
+ * concepts off the device in batches when they do not fit at once), e.g. the
+ * extent bitmaps of a context whose K x N/8 bytes exceed device memory.
+ * FCBO_ERR_INVALID_ARGUMENT if nothing was enumerated or first + count > K.
+ * Returns after the stream has finished.
+ */
+int fcbo_write_range(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_t *intents_out,
+                     uint64_t *extents_out);
+
+/*
+ * Cap the device memory the context's enumeration buffers may hold (bytes;
+ * 0 = no cap).  An enumeration that would need more fails with
+ * FCBO_ERR_OUT_OF_MEMORY at the allocation that crosses the cap, as a full
+ * device would (page 4 section 4.1: pool overflow; page 1 section 6.1: device
+ * memory budget).  If the buffers already hold more than the new cap they are
+ * released, and the last result with them.  The rows and columns built at
+ * creation are not counted.
+ */
+int fcbo_set_memory_limit(fcbo_context *ctx, uint64_t bytes);
+
+/*
+ * Diagnostic: per-level counts of the last enumeration, concepts generated on
+ * level k (level 0 is the root) and closure tests made by the concepts of
+ * level k (page 4 section 6 checks exactly these against a serial run).
  * Copies min(n_levels, max_levels) entries; *n_levels_out gets n_levels.
  * Either array may be NULL.  FCBO_ERR_INVALID_ARGUMENT if nothing was
  * enumerated yet.
@@ -149,9 +222,10 @@ int fcbo_level_counts(const fcbo_context *ctx, uint64_t *concepts_per_level,
                       uint64_t *tests_per_level, uint64_t max_levels, uint64_t *n_levels_out);
 
 /*
- * Copy the device column bitmap (M x ceil(N/64) words, column j = objects
- * having attribute j) into a host buffer of at least that many words.  It is
- * the transpose built by fcbo_context_create.
+ * Test hook: copy the device column bitmap (M x ceil(N/64) words, column j =
+ * objects having attribute j; page 1 section 3.1) into a host buffer of at
+ * least that many words, so tests can check the transpose.
+ * FCBO_ERR_CAPACITY if capacity_words is too small.
  */
 int fcbo_copy_columns(const fcbo_context *ctx, uint64_t *host_cols, uint64_t capacity_words);
 

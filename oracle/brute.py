@@ -104,6 +104,11 @@ class TreeStats:
     pairs: int = 0
     sum_nzw: int = 0
     sum_c: int = 0
+    # the same sums split by a threshold T on the parent's extent size
+    sum_rl_objs: int = 0      # objects of the parents with |A| <= T
+    col_parents: int = 0      # parents with |A| > T
+    col_nzw: int = 0          # sum over their tests of the non-zero words of A
+    col_child_objs: int = 0   # objects of their children
     level_concepts: list = field(default_factory=list)
     level_tests: list = field(default_factory=list)
     parent: dict = field(default_factory=dict)  # intent -> parent intent (None for the top)
@@ -119,7 +124,7 @@ def _nonzero_words(x: int) -> int:
     return c
 
 
-def cbo_tree(ctx: Context, intents: set[int]) -> TreeStats:
+def cbo_tree(ctx: Context, intents: set[int], rowlocal_max: int = 1 << 62) -> TreeStats:
     """The Close-by-One tree over a complete set of intents, without searching.
 
     For a closed D other than the top intent T = {}'' let
@@ -130,7 +135,8 @@ def cbo_tree(ctx: Context, intents: set[int]) -> TreeStats:
     of B at j has D n {0..j-1} = B n {0..j-1}, hence D = (D n {0..j})'' and
     B = (D n {0..j-1})'', and j is then forced to be the least such m.)
     From the cursors follow the closure tests (j > y, j not in B), the item
-    pairs (j > y), the level of every concept and the byte-model sums.
+    pairs (j > y), the level of every concept and the byte-model sums, also
+    split by the size of the parent's extent against ``rowlocal_max``.
     """
     top = ctx.close(0)
     cursor, parent = {}, {}
@@ -172,6 +178,12 @@ def cbo_tree(ctx: Context, intents: set[int]) -> TreeStats:
         lv = level[d]
         st.level_concepts[lv] += 1
         ext = ctx.objects_of(d)
+        size = bin(ext).count("1")
+        col = size > rowlocal_max
+        if col:
+            st.col_parents += 1
+        else:
+            st.sum_rl_objs += size
         y = cursor[d]
         for j in range(y + 1, ctx.m):
             st.pairs += 1
@@ -180,6 +192,10 @@ def cbo_tree(ctx: Context, intents: set[int]) -> TreeStats:
             st.tests += 1
             st.level_tests[lv] += 1
             st.sum_nzw += _nonzero_words(ext)
+            if col:
+                st.col_nzw += _nonzero_words(ext)
         if parent[d] is not None:
-            st.sum_c += bin(ext).count("1")
+            st.sum_c += size
+            if bin(ctx.objects_of(parent[d])).count("1") > rowlocal_max:
+                st.col_child_objs += size
     return st

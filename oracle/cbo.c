@@ -33,7 +33,18 @@
  * Besides the concepts it counts what the byte model of the GPU path needs:
  * closure tests, item pairs, concepts and tests per depth, the sum over tests
  * of the non-zero words of the parent extent, and the sum over kept children
- * of |C|.
+ * of |C|; and the same split by a threshold T on the parent's extent size:
+ * the objects of the parents with |A| <= T, the number of parents with
+ * |A| > T, the sum over their tests of the non-zero words of A, and the
+ * objects of their children.
+ *
+ * On request every concept's extent is also reduced to a 64-bit hash,
+ *     g(A) = sum over words k of f(a_k XOR f(k)) mod 2^64,
+ * with a_k the 64-bit words of the extent bitmap and f the SplitMix64 output
+ * function (Steele, Lea and Flood, "Fast splittable pseudorandom number
+ * generators", OOPSLA 2014; constants as in Vigna's public splitmix64.c),
+ * and the hashes follow the concepts through the final sort.  They let a test
+ * compare extents of contexts whose K x N/8 bytes do not fit in memory.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -52,9 +63,12 @@ typedef struct {
     /* concept store */
     int64_t count, cap;
     uint64_t *intents, *extents;
-    int keep_extents;
+    int keep_extents, hash_extents;
+    uint64_t *ehash;   /* extent hash of every stored concept (hash_extents) */
+    uint64_t *wkey;    /* f(k) for every extent word k */
     /* counters */
     int64_t tests, pairs, sum_nzw, sum_c, violations;
+    int64_t rowlocal_max, sum_rl_objs, col_parents, col_nzw, col_child_objs;
     int64_t *level_concepts, *level_tests;
     int32_t max_depth;
     int64_t max_tests;
@@ -66,6 +80,23 @@ static double now_seconds(void)
     struct timespec ts;
     clock_gettime(CLOCK_MONOTONIC, &ts);
     return (double)ts.tv_sec + 1e-9 * (double)ts.tv_nsec;
+}
+
+static uint64_t splitmix64_f(uint64_t z)
+{
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* g(A) of an extent bitmap (see the file comment). */
+static uint64_t extent_hash(const cbo_state *s, const uint64_t *a)
+{
+    uint64_t h = 0;
+    for (int64_t k = 0; k < s->wn; ++k)
+        h += splitmix64_f(a[k] ^ s->wkey[k]);
+    return h;
 }
 
 static int has_bit(const uint64_t *set, int64_t e)
@@ -127,6 +158,11 @@ static int store(cbo_state *s, const uint64_t *a, const uint64_t *b, int32_t dep
         uint64_t *ni = realloc(s->intents, (size_t)ncap * s->wm * sizeof(uint64_t));
         if (!ni) { s->oom = 1; return 0; }
         s->intents = ni;
+        if (s->hash_extents) {
+            uint64_t *nh = realloc(s->ehash, (size_t)ncap * sizeof(uint64_t));
+            if (!nh) { s->oom = 1; return 0; }
+            s->ehash = nh;
+        }
         if (s->keep_extents) {
             uint64_t *ne = realloc(s->extents, (size_t)ncap * s->wn * sizeof(uint64_t));
             if (!ne) { s->oom = 1; return 0; }
@@ -137,6 +173,8 @@ static int store(cbo_state *s, const uint64_t *a, const uint64_t *b, int32_t dep
     memcpy(s->intents + s->count * s->wm, b, (size_t)s->wm * sizeof(uint64_t));
     if (s->keep_extents)
         memcpy(s->extents + s->count * s->wn, a, (size_t)s->wn * sizeof(uint64_t));
+    if (s->hash_extents)
+        s->ehash[s->count] = extent_hash(s, a);
     s->count += 1;
     s->level_concepts[depth] += 1;
     if (depth > s->max_depth)
@@ -150,6 +188,14 @@ static void generate(cbo_state *s, const uint64_t *a, uint64_t *b, int64_t y, in
 {
     uint64_t *c = s->stack + (size_t)(depth + 1) * (s->wn + s->wm);
     uint64_t *d = c + s->wn;
+    /* the byte-model class of this node as a parent */
+    const int64_t size_a = popcount_words(a, s->wn);
+    const int col_class = size_a > s->rowlocal_max;
+    const int64_t nzw_a = nonzero_words(a, s->wn);
+    if (col_class)
+        s->col_parents += 1;
+    else
+        s->sum_rl_objs += size_a;
     for (int64_t j = y + 1; j < s->m; ++j) {
         if (s->truncated || s->oom)
             return;
@@ -162,7 +208,9 @@ static void generate(cbo_state *s, const uint64_t *a, uint64_t *b, int64_t y, in
         }
         s->tests += 1;
         s->level_tests[depth] += 1;
-        s->sum_nzw += nonzero_words(a, s->wn);
+        s->sum_nzw += nzw_a;
+        if (col_class)
+            s->col_nzw += nzw_a;
         const uint64_t *col = s->cols + j * s->wn;
         int shrinks = 0;
         for (int64_t w = 0; w < s->wn; ++w) {
@@ -179,7 +227,10 @@ static void generate(cbo_state *s, const uint64_t *a, uint64_t *b, int64_t y, in
         derive_objects(s, c, d);
         if (!same_prefix(d, b, j))
             continue;
-        s->sum_c += popcount_words(c, s->wn);
+        const int64_t size_c = popcount_words(c, s->wn);
+        s->sum_c += size_c;
+        if (col_class)
+            s->col_child_objs += size_c;
         if (!store(s, c, d, depth + 1))
             return;
         generate(s, c, d, j, depth + 1);
@@ -212,8 +263,9 @@ static int sort_concepts(cbo_state *s)
     int64_t *perm = malloc((size_t)k * sizeof(int64_t));
     uint64_t *ni = malloc((size_t)k * s->wm * sizeof(uint64_t));
     uint64_t *ne = s->keep_extents ? malloc((size_t)k * s->wn * sizeof(uint64_t)) : NULL;
-    if (!perm || !ni || (s->keep_extents && !ne)) {
-        free(perm); free(ni); free(ne);
+    uint64_t *nh = s->hash_extents ? malloc((size_t)k * sizeof(uint64_t)) : NULL;
+    if (!perm || !ni || (s->keep_extents && !ne) || (s->hash_extents && !nh)) {
+        free(perm); free(ni); free(ne); free(nh);
         return 0;
     }
     for (int64_t i = 0; i < k; ++i)
@@ -225,6 +277,8 @@ static int sort_concepts(cbo_state *s)
         memcpy(ni + i * s->wm, s->intents + perm[i] * s->wm, (size_t)s->wm * sizeof(uint64_t));
         if (ne)
             memcpy(ne + i * s->wn, s->extents + perm[i] * s->wn, (size_t)s->wn * sizeof(uint64_t));
+        if (nh)
+            nh[i] = s->ehash[perm[i]];
     }
     free(perm);
     free(s->intents);
@@ -233,11 +287,15 @@ static int sort_concepts(cbo_state *s)
         free(s->extents);
         s->extents = ne;
     }
+    if (nh) {
+        free(s->ehash);
+        s->ehash = nh;
+    }
     return 1;
 }
 
 int oracle_cbo(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, int64_t row_stride,
-               int keep_extents, int64_t max_tests, oracle_result *out)
+               int flags, int64_t max_tests, int64_t rowlocal_max, oracle_result *out)
 {
     if (!rows || !out || n_objects < 1 || n_attrs < 1 || row_stride < (n_attrs + 63) / 64)
         return -1;
@@ -250,19 +308,24 @@ int oracle_cbo(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, int64_t
     s.wm = (n_attrs + 63) / 64;
     s.tail_n = (n_objects & 63) ? (((uint64_t)1 << (n_objects & 63)) - 1u) : ~(uint64_t)0;
     s.tail_m = (n_attrs & 63) ? (((uint64_t)1 << (n_attrs & 63)) - 1u) : ~(uint64_t)0;
-    s.keep_extents = keep_extents;
+    s.keep_extents = (flags & ORACLE_KEEP_EXTENTS) != 0;
+    s.hash_extents = (flags & ORACLE_HASH_EXTENTS) != 0;
     s.max_tests = max_tests;
+    s.rowlocal_max = rowlocal_max;
 
     s.rows = calloc((size_t)s.n * s.wm, sizeof(uint64_t));
     s.cols = calloc((size_t)s.m * s.wn, sizeof(uint64_t));
     s.stack = calloc((size_t)(s.m + 2) * (s.wn + s.wm), sizeof(uint64_t));
     s.level_concepts = calloc((size_t)s.m + 2, sizeof(int64_t));
     s.level_tests = calloc((size_t)s.m + 2, sizeof(int64_t));
+    s.wkey = calloc((size_t)s.wn, sizeof(uint64_t));
     uint64_t *a0 = calloc((size_t)s.wn, sizeof(uint64_t));
     uint64_t *b0 = calloc((size_t)s.wm, sizeof(uint64_t));
     int rc = -2;
-    if (!s.rows || !s.cols || !s.stack || !s.level_concepts || !s.level_tests || !a0 || !b0)
+    if (!s.rows || !s.cols || !s.stack || !s.level_concepts || !s.level_tests || !s.wkey || !a0 || !b0)
         goto fail;
+    for (int64_t k = 0; k < s.wn; ++k)
+        s.wkey[k] = splitmix64_f((uint64_t)k);
 
     /* The context in both layouts; bits past M are dropped. */
     for (int64_t g = 0; g < s.n; ++g) {
@@ -303,6 +366,11 @@ int oracle_cbo(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, int64_t
     out->level_tests = s.level_tests;
     out->intents = s.intents;
     out->extents = s.extents;
+    out->extent_hashes = s.ehash;
+    out->sum_rl_objs = s.sum_rl_objs;
+    out->col_parents = s.col_parents;
+    out->col_nzw = s.col_nzw;
+    out->col_child_objs = s.col_child_objs;
     out->wn = s.wn;
     out->wm = s.wm;
     out->seconds_enum = t1 - t0;
@@ -310,6 +378,7 @@ int oracle_cbo(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, int64_t
     free(s.rows);
     free(s.cols);
     free(s.stack);
+    free(s.wkey);
     free(a0);
     free(b0);
     return 0;
@@ -322,6 +391,8 @@ fail:
     free(s.level_tests);
     free(s.intents);
     free(s.extents);
+    free(s.ehash);
+    free(s.wkey);
     free(a0);
     free(b0);
     return rc;
@@ -335,5 +406,6 @@ void oracle_free(oracle_result *r)
     free(r->level_tests);
     free(r->intents);
     free(r->extents);
+    free(r->extent_hashes);
     memset(r, 0, sizeof(*r));
 }

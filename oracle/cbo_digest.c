@@ -7,27 +7,49 @@
  *
  * The search is the one of cbo.c (page "hnwysp.cn/news/97538", sections 2.1
  * and 2.3; page "hotelren.com/news/5603750", section 1.2): from the root
- * (G, G'), cursor -1, every node (A, B, y) tries each attribute j > y; j in B
- * is skipped (saturation), otherwise C = the objects of A having j, D = C' (the
- * AND of their rows, all of M when C is empty), and (C, D, j) is a child iff D
- * and B agree on attributes 0..j-1 (page 1, section 4.3).  Only the
- * representation differs: an extent is the ascending list of its objects
- * rather than a bitmap, which is what makes contexts with 10^9 concepts
- * tractable (page 1, section 4.2 walks the set bits of the extent for the same
- * reason).
+ * (G, G'), cursor -1, every node (A, B, y) tries each attribute j > y in
+ * ascending order; j in B is skipped (saturation), otherwise C = the objects
+ * of A having j, D = C' (the AND of their rows, all of M when C is empty), and
+ * (C, D, j) is a child iff D and B agree on attributes 0..j-1 (page 1,
+ * section 4.3).  Only the representation differs: an extent is the ascending
+ * list of its objects rather than a bitmap, which is what makes contexts with
+ * 10^9 concepts tractable (page 1, section 4.2 walks the set bits of the
+ * extent for the same reason).
  *
  * Nothing is stored.  Per concept the search adds to the counters of cbo.c
- * (tests, item pairs, sum of |C|, concepts and tests per level) and to an
- * order-independent digest of the intents:
- *     digest = sum over concepts of h(B) mod 2^64,
- *     h(B)   = f(... f(f(0 ^ w_0) ^ w_1) ... ^ w_{W-1}),
- * with w_k the 64-bit words of B (bit layout of cbo.c) and f the SplitMix64
- * output function (Steele, Lea and Flood, "Fast splittable pseudorandom number
- * generators", OOPSLA 2014; constants as in Vigna's public splitmix64.c).
+ * (tests, item pairs, sum of |C|, concepts and tests per level) and hashes the
+ * concept:
+ *     h(B) = f(... f(f(0 ^ w_0) ^ w_1) ... ^ w_{W_M-1})   (intent words w_k)
+ *     g(A) = sum over k < W_N of f(a_k ^ f(k)) mod 2^64  (extent bitmap words a_k)
+ * with f the SplitMix64 output function (Steele, Lea and Flood, "Fast
+ * splittable pseudorandom number generators", OOPSLA 2014; constants as in
+ * Vigna's public splitmix64.c).  g is computed from the list: the words that
+ * hold no object contribute f(f(k)) each, so
+ *     g(A) = Z + sum over the non-zero words k of (f(a_k ^ f(k)) - f(f(k))),
+ * Z = sum over all k of f(f(k)).
+ *
+ * Digests (all mod 2^64):
+ *     digest            = sum over concepts of h(B)          (order-free)
+ *     intent_positional = sum over concepts of i * h(B_i)
+ *     extent_positional = sum over concepts of i * g(A_i)
+ * where i is the concept's position in the output order: intents in
+ * lexicographic order over the attributes 0..M-1, the one holding the
+ * smallest attribute where two differ coming later.  In that order the CbO
+ * tree is listed in pre-order with the children of a node taken by
+ * descending generating attribute (a child agrees with its parent below its
+ * attribute and adds it; of two children the one made at the smaller
+ * attribute holds it and the other does not, so it and its whole subtree come
+ * later).  The search walks children by ascending attribute, as the pages do,
+ * so positions are not known on the way down; instead every subtree returns
+ * (size, sum of hashes, sum of local position x hash) with its root at local
+ * position 0, and a node places its children's subtrees after itself in
+ * descending attribute order: a child subtree starting at offset o adds
+ * o x (its hash sum) to the node's position-weighted sum.
  *
  * The subtrees below the root's children are independent (canonicity is a
  * property of a node and its parent only, page 1 section 2.2), so they are
- * handed out to worker threads one at a time; counters are summed at the end.
+ * handed out to worker threads one at a time; their summaries are combined in
+ * the output order at the end.
  */
 #include <pthread.h>
 #include <stdint.h>
@@ -37,7 +59,7 @@
 
 #include "oracle_cbo.h"
 
-static uint64_t splitmix64_mix(uint64_t z)
+static uint64_t splitmix64_f(uint64_t z)
 {
     z += 0x9E3779B97F4A7C15ull;
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -49,15 +71,32 @@ static uint64_t intent_hash(const uint64_t *b, int64_t wm)
 {
     uint64_t h = 0;
     for (int64_t k = 0; k < wm; ++k)
-        h = splitmix64_mix(h ^ b[k]);
+        h = splitmix64_f(h ^ b[k]);
     return h;
 }
 
 typedef struct {
-    int64_t n, m, wm;
+    int64_t n, m, wm, wn;
     const uint64_t *rows; /* n x wm */
     uint64_t tail_m;
+    uint64_t *wkey;       /* f(k) for every extent word k */
+    uint64_t zero_sum;    /* Z: g of the empty extent */
 } context;
+
+/* g(A) of an ascending object list (see the file comment). */
+static uint64_t extent_hash(const context *x, const int32_t *a, int64_t na)
+{
+    uint64_t h = x->zero_sum;
+    int64_t i = 0;
+    while (i < na) {
+        const int64_t k = a[i] >> 6;
+        uint64_t word = 0;
+        for (; i < na && (a[i] >> 6) == k; ++i)
+            word |= (uint64_t)1 << (a[i] & 63);
+        h += splitmix64_f(word ^ x->wkey[k]) - splitmix64_f(x->wkey[k]);
+    }
+    return h;
+}
 
 typedef struct {
     int64_t concepts, tests, pairs, sum_c;
@@ -83,28 +122,33 @@ static int same_prefix(const uint64_t *d, const uint64_t *b, int64_t j)
     return (d[word] & mask) == (b[word] & mask);
 }
 
-static void count_concept(const context *x, counters *c, const uint64_t *b, int32_t depth)
+/* Place the subtree `kid` after the `off` concepts already in `to`. */
+static void append_subtree(oracle_subtree *to, const oracle_subtree *kid)
 {
-    c->concepts += 1;
-    c->level_concepts[depth] += 1;
-    if (depth > c->max_depth)
-        c->max_depth = depth;
-    c->digest += intent_hash(b, x->wm);
+    const uint64_t off = (uint64_t)to->size;
+    to->hi1 += kid->hi1 + off * kid->hi0;
+    to->he1 += kid->he1 + off * kid->he0;
+    to->hi0 += kid->hi0;
+    to->he0 += kid->he0;
+    to->size += kid->size;
 }
 
-/* The children of node (A, B, y): C as an object list, D = C'.  With `only_j`
- * >= 0 just that attribute is tried (the root's children are split this way
- * between threads); `count_node` says whether this call also counts the
- * node's own tests and pairs (every attribute of the node is tried by
- * exactly one call). */
-static void expand(const context *x, counters *c, const int32_t *a, int64_t na, const uint64_t *b, int64_t y,
-                   int32_t depth, int64_t only_j)
+typedef struct {
+    int64_t j;
+    oracle_subtree sub;
+} child_summary;
+
+static oracle_subtree subtree(const context *x, counters *c, const int32_t *a, int64_t na, const uint64_t *b,
+                              int64_t y, int32_t depth);
+
+/* The children of node (A, B) at `depth` made at the attributes j in [j_lo,
+ * j_hi) (ascending), each with its subtree searched; their summaries go to
+ * kids[] in ascending j.  The node's tests and item pairs for these j are
+ * counted here.  Returns the number of children. */
+static int64_t children(const context *x, counters *c, const int32_t *a, int64_t na, const uint64_t *b, int32_t depth,
+                        int64_t j_lo, int64_t j_hi, child_summary *kids)
 {
-    int64_t j_lo = y + 1, j_hi = x->m;
-    if (only_j >= 0) {
-        j_lo = only_j;
-        j_hi = only_j + 1;
-    }
+    int64_t nk = 0;
     int32_t *cl = NULL;
     uint64_t *d = malloc((size_t)x->wm * sizeof(uint64_t));
     if (na > 0)
@@ -113,7 +157,7 @@ static void expand(const context *x, counters *c, const int32_t *a, int64_t na, 
         c->oom = 1;
         free(d);
         free(cl);
-        return;
+        return 0;
     }
     for (int64_t j = j_lo; j < j_hi && !c->oom; ++j) {
         c->pairs += 1;
@@ -134,11 +178,40 @@ static void expand(const context *x, counters *c, const int32_t *a, int64_t na, 
         if (!same_prefix(d, b, j))
             continue;
         c->sum_c += nc;
-        count_concept(x, c, d, depth + 1);
-        expand(x, c, cl, nc, d, j, depth + 1, -1);
+        kids[nk].j = j;
+        kids[nk].sub = subtree(x, c, cl, nc, d, j, depth + 1);
+        ++nk;
     }
     free(d);
     free(cl);
+    return nk;
+}
+
+/* Count the node (A, B) with cursor y at `depth` and search its subtree;
+ * returns the subtree's summary with the node at local position 0. */
+static oracle_subtree subtree(const context *x, counters *c, const int32_t *a, int64_t na, const uint64_t *b,
+                              int64_t y, int32_t depth)
+{
+    const uint64_t hi = intent_hash(b, x->wm), he = extent_hash(x, a, na);
+    c->concepts += 1;
+    c->level_concepts[depth] += 1;
+    if (depth > c->max_depth)
+        c->max_depth = depth;
+    c->digest += hi;
+    oracle_subtree s = {1, hi, 0, he, 0};
+    const int64_t span = x->m - (y + 1);
+    if (span <= 0)
+        return s;
+    child_summary *kids = malloc((size_t)span * sizeof(child_summary));
+    if (!kids) {
+        c->oom = 1;
+        return s;
+    }
+    const int64_t nk = children(x, c, a, na, b, depth, y + 1, x->m, kids);
+    for (int64_t k = nk; k-- > 0;) /* descending attribute: the output order */
+        append_subtree(&s, &kids[k].sub);
+    free(kids);
+    return s;
 }
 
 typedef struct {
@@ -146,9 +219,11 @@ typedef struct {
     const int32_t *a0;
     int64_t n0;
     const uint64_t *b0;
-    int64_t next_j; /* next root attribute to hand out */
+    int64_t next_j;          /* next root attribute to hand out */
     pthread_mutex_t lock;
-    counters part;  /* summed results of finished workers */
+    counters part;           /* summed results of finished workers */
+    child_summary *slot;     /* [m]: the root's child made at j, if any */
+    unsigned char *has_slot; /* [m] */
     int oom;
 } pool;
 
@@ -199,7 +274,11 @@ static void *worker(void *arg)
         pthread_mutex_unlock(&p->lock);
         if (j >= p->x->m)
             break;
-        expand(p->x, &c, p->a0, p->n0, p->b0, -1, 0, j);
+        child_summary kid;
+        if (children(p->x, &c, p->a0, p->n0, p->b0, 0, j, j + 1, &kid) == 1) {
+            p->slot[j] = kid; /* each j is handed to one worker only */
+            p->has_slot[j] = 1;
+        }
     }
     pthread_mutex_lock(&p->lock);
     counters_add(&p->part, &c, p->x->m);
@@ -219,14 +298,20 @@ int oracle_cbo_digest(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, 
     x.n = n_objects;
     x.m = n_attrs;
     x.wm = (n_attrs + 63) / 64;
+    x.wn = (n_objects + 63) / 64;
     x.tail_m = (n_attrs & 63) ? (((uint64_t)1 << (n_attrs & 63)) - 1u) : ~(uint64_t)0;
     uint64_t *r = malloc((size_t)x.n * x.wm * sizeof(uint64_t));
     int32_t *a0 = malloc((size_t)x.n * sizeof(int32_t));
     uint64_t *b0 = malloc((size_t)x.wm * sizeof(uint64_t));
+    x.wkey = malloc((size_t)x.wn * sizeof(uint64_t));
     pool p;
     memset(&p, 0, sizeof(p));
+    p.slot = malloc((size_t)x.m * sizeof(child_summary));
+    p.has_slot = calloc((size_t)x.m, 1);
+    int32_t *child_attr = NULL;
+    oracle_subtree *child_sub = NULL;
     int rc = -2;
-    if (!r || !a0 || !b0 || !counters_init(&p.part, x.m))
+    if (!r || !a0 || !b0 || !x.wkey || !p.slot || !p.has_slot || !counters_init(&p.part, x.m))
         goto done;
     for (int64_t g = 0; g < x.n; ++g) {
         for (int64_t w = 0; w < x.wm; ++w)
@@ -234,6 +319,11 @@ int oracle_cbo_digest(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, 
         r[g * x.wm + x.wm - 1] &= x.tail_m; /* bits past M are dropped */
     }
     x.rows = r;
+    x.zero_sum = 0;
+    for (int64_t k = 0; k < x.wn; ++k) {
+        x.wkey[k] = splitmix64_f((uint64_t)k);
+        x.zero_sum += splitmix64_f(x.wkey[k]);
+    }
 
     struct timespec t0, t1;
     clock_gettime(CLOCK_MONOTONIC, &t0);
@@ -246,7 +336,10 @@ int oracle_cbo_digest(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, 
     for (int64_t g = 0; g < x.n; ++g)
         for (int64_t w = 0; w < x.wm; ++w)
             b0[w] &= r[g * x.wm + w];
-    count_concept(&x, &p.part, b0, 0);
+    const uint64_t root_hi = intent_hash(b0, x.wm), root_he = extent_hash(&x, a0, x.n);
+    p.part.concepts = 1;
+    p.part.level_concepts[0] = 1;
+    p.part.digest = root_hi;
 
     p.x = &x;
     p.a0 = a0;
@@ -271,6 +364,25 @@ int oracle_cbo_digest(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, 
     if (p.oom || p.part.oom)
         goto done;
 
+    /* the root, then its children's subtrees by descending attribute */
+    oracle_subtree whole = {1, root_hi, 0, root_he, 0};
+    int32_t nroot = 0;
+    for (int64_t j = 0; j < x.m; ++j)
+        nroot += p.has_slot[j];
+    child_attr = malloc((size_t)(nroot ? nroot : 1) * sizeof(int32_t));
+    child_sub = malloc((size_t)(nroot ? nroot : 1) * sizeof(oracle_subtree));
+    if (!child_attr || !child_sub)
+        goto done;
+    int32_t k = 0;
+    for (int64_t j = x.m; j-- > 0;) {
+        if (!p.has_slot[j])
+            continue;
+        child_attr[k] = (int32_t)j;
+        child_sub[k] = p.slot[j].sub;
+        append_subtree(&whole, &p.slot[j].sub);
+        ++k;
+    }
+
     out->n_concepts = p.part.concepts;
     out->tests = p.part.tests;
     out->pairs = p.part.pairs;
@@ -281,12 +393,27 @@ int oracle_cbo_digest(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, 
     p.part.level_concepts = NULL;
     p.part.level_tests = NULL;
     out->digest = p.part.digest;
+    out->subtree_size = whole.size;
+    out->intent_digest = whole.hi0;
+    out->intent_positional = whole.hi1;
+    out->extent_digest = whole.he0;
+    out->extent_positional = whole.he1;
+    out->n_root_children = nroot;
+    out->root_child_attr = child_attr;
+    out->root_child = child_sub;
+    child_attr = NULL;
+    child_sub = NULL;
     out->threads = started ? started : 1;
     out->seconds = (double)(t1.tv_sec - t0.tv_sec) + 1e-9 * (double)(t1.tv_nsec - t0.tv_nsec);
     rc = 0;
 
 done:
     counters_free(&p.part);
+    free(child_attr);
+    free(child_sub);
+    free(p.slot);
+    free(p.has_slot);
+    free(x.wkey);
     free(r);
     free(a0);
     free(b0);
@@ -299,6 +426,10 @@ void oracle_digest_free(oracle_digest *d)
         return;
     free(d->level_concepts);
     free(d->level_tests);
+    free(d->root_child_attr);
+    free(d->root_child);
     d->level_concepts = NULL;
     d->level_tests = NULL;
+    d->root_child_attr = NULL;
+    d->root_child = NULL;
 }

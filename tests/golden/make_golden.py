@@ -5,17 +5,22 @@ workload, the concept count, closure tests, item pairs, per-level counts and
 the byte-model sums, plus
 
 * for workloads whose concepts fit in host memory: a SHA-256 of the sorted
-  intent array (oracle.cbo);
-* for larger ones: the order-independent intent digest of the store-free
-  search (oracle.cbo_digest, all host cores), and slices: for a few attribute
-  sets S, the sorted intents of the sub-context of the objects having all of
-  S, which are exactly the workload's intents containing S (count and
-  SHA-256).
+  intent array and a SHA-256 of the array of extent hashes in the same order
+  (oracle.cbo; the extent bitmaps themselves would not fit), and the class
+  sums of the byte model;
+* for every workload: the positional digests of the store-free search
+  (oracle.cbo_digest, all host cores): intents and extents hashed and
+  weighted by their output position, in total and per subtree of the root's
+  children (consecutive ranges of the output);
+* for the larger ones also the order-independent intent digest and slices:
+  for a few attribute sets S, the sorted intents of the sub-context of the
+  objects having all of S, which are exactly the workload's intents
+  containing S (count and SHA-256).
 
 The GPU tests compare against these files; nothing here touches the GPU
 library.
 
-    python tests/golden/make_golden.py ctx50000x400 ctx20000x256
+    python tests/golden/make_golden.py ctx10000x128 ctx50000x400 ctx20000x256
 """
 
 import hashlib
@@ -43,20 +48,35 @@ def sha_of(intents) -> str:
     return hashlib.sha256(np.ascontiguousarray(intents, dtype="<u8").tobytes()).hexdigest()
 
 
+def positional(rows, m) -> dict:
+    t0 = time.time()
+    d = oracle.cbo_digest(rows, m, threads=os.cpu_count() or 1)
+    wall = time.time() - t0
+    return d, {
+        "intent_digest": str(d.digest),
+        "intent_positional": str(d.intent_positional),
+        "extent_digest": str(d.extent_digest),
+        "extent_positional": str(d.extent_positional),
+        "root_children": [[c["attr"], c["size"], str(c["hi0"]), str(c["hi1"]), str(c["he0"]), str(c["he1"])]
+                          for c in d.root_children],
+        "digest_oracle_threads": d.threads,
+        "digest_oracle_seconds": d.seconds,
+        "digest_oracle_wall_seconds": wall,
+    }
+
+
 def golden_digest(name: str) -> dict:
     cells = synth.make_config(name, packed=False)
     rows = synth.pack_rows(cells)
     n, m, _ = synth.CONFIGS[name]
-    t0 = time.time()
-    d = oracle.cbo_digest(rows, m, threads=os.cpu_count() or 1)
-    wall = time.time() - t0
+    d, pos = positional(rows, m)
     slices = []
     for attrs in DIGEST_SLICES[name]:
         sub = cells[cells[:, attrs].all(axis=1)]
         r = oracle.cbo(synth.pack_rows(sub), m, keep_extents=False)
         slices.append({"attributes": attrs, "objects": int(sub.shape[0]), "n_concepts": int(r.n_concepts),
                        "intents_sha256": sha_of(r.intents)})
-    return {
+    out = {
         "workload": name,
         "objects": n,
         "attributes": m,
@@ -68,12 +88,11 @@ def golden_digest(name: str) -> dict:
         "sum_c": int(d.sum_c),
         "level_concepts": [int(x) for x in d.level_concepts],
         "level_tests": [int(x) for x in d.level_tests],
-        "intent_digest": str(d.digest),
         "slices": slices,
-        "oracle_threads": d.threads,
-        "oracle_seconds": d.seconds,
-        "oracle_wall_seconds": wall,
+        "oracle_wall_seconds": pos["digest_oracle_wall_seconds"],
     }
+    out.update(pos)
+    return out
 
 
 def golden(name: str) -> dict:
@@ -82,9 +101,11 @@ def golden(name: str) -> dict:
     rows = synth.make_config(name)
     n, m, _ = synth.CONFIGS[name]
     t0 = time.time()
-    r = oracle.cbo(rows, m, keep_extents=False)
+    r = oracle.cbo(rows, m, keep_extents=False, hash_extents=True)
     wall = time.time() - t0
-    return {
+    d, pos = positional(rows, m)
+    assert d.n_concepts == r.n_concepts and d.tests == r.tests
+    out = {
         "workload": name,
         "objects": n,
         "attributes": m,
@@ -98,10 +119,19 @@ def golden(name: str) -> dict:
         "level_concepts": [int(x) for x in r.level_concepts],
         "level_tests": [int(x) for x in r.level_tests],
         "intents_sha256": sha_of(r.intents),
+        "extent_hashes_sha256": sha_of(r.extent_hashes),
+        "rowlocal_max": r.rowlocal_max,
+        "sum_rl_objs": int(r.sum_rl_objs),
+        "col_parents": int(r.col_parents),
+        "col_nzw": int(r.col_nzw),
+        "col_child_objs": int(r.col_child_objs),
+        "model_bytes": int(oracle.model_bytes(r)),
         "oracle_enum_seconds": r.seconds_enum,
         "oracle_sort_seconds": r.seconds_sort,
         "oracle_wall_seconds": wall,
     }
+    out.update(pos)
+    return out
 
 
 def main(names):

@@ -17,6 +17,7 @@ import pytest
 
 import oracle
 import synth
+from tests import intent_digest as dg
 from tests.golden_io import read_fixture
 from tests.intent_digest import digest_torch
 
@@ -41,12 +42,22 @@ def gpu_run(rows, m, extents=True, flags=0):
         ctx.close()
 
 
+def assert_model_counters(st, want):
+    """The byte-model inputs counted on the device equal the oracle's class sums."""
+    assert st["local_parent_objects"] + st["medium_parent_objects"] == want.sum_rl_objs
+    assert st["big_parents"] == want.col_parents
+    assert st["big_nonzero_words"] == want.col_nzw
+    assert st["big_child_objects"] == want.col_child_objs
+    assert st["model_bytes"] == oracle.model_bytes(want)
+
+
 def assert_parity(cells, extents=True, flags=0):
     cells = np.asarray(cells, dtype=bool)
     rows = synth.pack_rows(cells)
     m = cells.shape[1]
     want = oracle.cbo(rows, m, keep_extents=extents)
     res, ints, exts, conc, tests = gpu_run(rows, m, extents=extents, flags=flags)
+    assert_model_counters(res.stats, want)
     assert res.n_concepts == want.n_concepts
     assert ints.shape == want.intents.shape
     assert np.array_equal(ints, want.intents)
@@ -236,6 +247,99 @@ def test_capacity_error_and_reuse():
         ctx.close()
 
 
+def test_write_range_pages_the_output():
+    # output rows fetched piece by piece through small buffers, ragged last piece
+    cells = synth.make_config("ctx2000x64", packed=False)
+    rows = synth.pack_rows(cells)
+    want = oracle.cbo(rows, 64)
+    k = want.n_concepts
+    ctx = fca.Context(rows, 64)
+    try:
+        assert ctx.count() == k
+        got_i = np.zeros_like(want.intents)
+        got_e = np.zeros_like(want.extents)
+        piece = 7777
+        bi, be = ctx.alloc_outputs(piece, True)
+        for first in range(0, k, piece):
+            cnt = min(piece, k - first)
+            ctx.write_range(first, bi[:cnt], be[:cnt])
+            got_i[first:first + cnt] = bi[:cnt].cpu().numpy().view(np.uint64)
+            got_e[first:first + cnt] = be[:cnt].cpu().numpy().view(np.uint64)
+        assert np.array_equal(got_i, want.intents)
+        assert np.array_equal(got_e, want.extents)
+        # one buffer at a time, from the middle
+        ctx.write_range(1234, extents=be[:100])
+        assert np.array_equal(be[:100].cpu().numpy().view(np.uint64), want.extents[1234:1334])
+        ctx.write_range(k - 50, intents=bi[:50])
+        assert np.array_equal(bi[:50].cpu().numpy().view(np.uint64), want.intents[k - 50:])
+        with pytest.raises(fca.FcboError) as e:
+            ctx.write_range(k - 49, intents=bi[:50])
+        assert e.value.code == fca.FCBO_ERR_INVALID_ARGUMENT
+        fca.fcbo_write_range(ctx.handle, k, 0, bi.data_ptr(), 0)  # empty range at the end
+    finally:
+        ctx.close()
+
+
+def test_memory_limit_fails_part_way_and_leaves_no_stale_result():
+    cells = synth.make_config("ctx2000x64", packed=False)
+    rows = synth.pack_rows(cells)
+    want = oracle.cbo(rows, 64)
+    k = want.n_concepts
+    ctx = fca.Context(rows, 64, flags=fca.FCBO_TINY_BUFFERS)  # buffers grow level by level
+    try:
+        ints, exts = ctx.alloc_outputs(k, True)
+        rc, kk, _ = ctx.enumerate_into(ints, exts)
+        assert rc == fca.FCBO_OK and kk == k
+        conc, _ = ctx.level_counts()
+        # a cap below what the enumeration holds: the buffers and the result go
+        ctx.set_memory_limit(1 << 20)
+        with pytest.raises(fca.FcboError):
+            ctx.level_counts()
+        for _ in range(2):
+            ints.fill_(-5)
+            exts.fill_(-5)
+            with pytest.raises(fca.FcboError) as e:
+                ctx.enumerate_into(ints, exts, fca.FCBO_REUSE_RESULT)
+            assert e.value.code == fca.FCBO_ERR_OUT_OF_MEMORY
+            torch.cuda.synchronize()
+            assert bool((ints == -5).all()) and bool((exts == -5).all())  # nothing stale written
+            with pytest.raises(fca.FcboError):
+                ctx.level_counts()
+        ctx.set_memory_limit(0)
+        rc, kk, st = ctx.enumerate_into(ints, exts, fca.FCBO_REUSE_RESULT)
+        assert rc == fca.FCBO_OK and kk == k
+        assert np.array_equal(ints.cpu().numpy().view(np.uint64), want.intents)
+        assert np.array_equal(exts.cpu().numpy().view(np.uint64), want.extents)
+        assert [int(x) for x in ctx.level_counts()[0]] == [int(x) for x in conc]
+    finally:
+        ctx.close()
+
+
+def test_output_buffers_are_checked_before_any_launch():
+    rows = synth.make_config("ctx64x16")
+    ctx = fca.Context(rows, 16)
+    try:
+        k = ctx.count()
+        ints, exts = ctx.alloc_outputs(k, True)
+        for bad_i, bad_e in [(ints[:, :0], exts), (ints.float(), exts),
+                             (ints.t(), exts), (ints.cpu(), exts), (ints, exts.view(-1)[:k])]:
+            with pytest.raises(ValueError):
+                ctx.enumerate_into(bad_i, bad_e)
+        # capacity is the smaller of the two buffers
+        rc, kk, _ = ctx.enumerate_into(ints, exts[: k - 1])
+        assert rc == fca.FCBO_ERR_CAPACITY and kk == k
+    finally:
+        ctx.close()
+
+
+def test_fifty_thousand_objects_all_extents_compared():
+    # N = 50,000 gives extent rows of 782 words, written eight rows per output
+    # tile (the benchmark's tile shape); every row compared
+    cells = synth.random_context(50020, 50_000, 20, 0.05)
+    res = assert_parity(cells, extents=True)
+    assert res.n_concepts > 1000
+
+
 @pytest.mark.parametrize("n", [129, 2000])
 def test_extent_buffer_only_word_aligned(n):
     # an extent buffer starting 8 bytes past a 16-byte boundary: single-word stores
@@ -302,6 +406,10 @@ def _sample_extents_match(cells, ints, exts_t, sample, seed):
 
 
 def test_full_ctx50000x400_against_stored_oracle():
+    # The benchmark's configuration (extents written).  Stored oracle values:
+    # counts, SHA-256 of the ordered intents and of the ordered extent hashes
+    # (every one of the 4.9 million extent rows hashed on the device), and the
+    # positional digests of the store-free oracle.
     path = os.path.join(GOLDEN, "ctx50000x400.json")
     if not os.path.exists(path):
         pytest.skip("stored oracle values not generated")
@@ -322,11 +430,35 @@ def test_full_ctx50000x400_against_stored_oracle():
         assert res.stats["sum_child_objects"] == g["sum_c"]
         assert [int(x) for x in conc] == g["level_concepts"]
         assert [int(x) for x in tests] == g["level_tests"]
-        # every extent bit accounted for: |G| for the root plus |C| of every child
+        st = res.stats
+        assert st["local_parent_objects"] + st["medium_parent_objects"] == g["sum_rl_objs"]
+        assert (st["big_parents"], st["big_nonzero_words"], st["big_child_objects"]) == (
+            g["col_parents"], g["col_nzw"], g["col_child_objs"])
+        assert st["model_bytes"] == g["model_bytes"]
+        eh = dg.extent_hashes_torch(res.extents)
+        ehs = eh.cpu().numpy().view(np.uint64)
+        assert hashlib.sha256(np.ascontiguousarray(ehs, dtype="<u8").tobytes()).hexdigest() == g["extent_hashes_sha256"]
+        assert dg.positional_torch(eh) == int(g["extent_positional"])
+        assert dg.positional_torch(dg.intent_hashes_torch(res.intents)) == int(g["intent_positional"])
+        # extras: every extent bit accounted for (|G| for the root plus |C| of
+        # every child), and sampled rows against B' and closedness
         assert _popcount_rows(res.extents) == 50000 + g["sum_c"]
-        _sample_extents_match(cells, ints, res.extents, 1500, 4)
+        _sample_extents_match(cells, ints, res.extents, 300, 4)
     finally:
         ctx.close()
+
+
+def _check_root_subtrees(g, hashes, which):
+    """Every child of the root owns one consecutive output range, by descending
+    attribute, with the stored size, hash sum and position-weighted hash sum."""
+    start = 1
+    lo = 2 if which == "intent" else 4
+    for attr, size, *sums in g["root_children"]:
+        part = hashes[start:start + size]
+        assert (int(part.sum()) & dg.MASK) == int(sums[lo - 2]), (which, attr)
+        assert dg.positional_torch(part) == int(sums[lo - 1]), (which, attr)
+        start += size
+    assert start == hashes.shape[0]
 
 
 def _assert_lectic_increasing(ints, chunk=1 << 26):
@@ -347,10 +479,12 @@ def _assert_lectic_increasing(ints, chunk=1 << 26):
         assert bool(((bw & low) != 0).all()), "rows out of lexicographic order"
 
 
-def test_full_ctx20000x256_intents_against_store_free_oracle():
-    # 1.4e9 concepts: the extents (N/8 bytes each) do not fit, so intents only.
-    # Checked: counts, per-level numbers, the order-independent intent digest,
-    # the lexicographic order, and slices compared byte for byte.
+def test_full_ctx20000x256_against_store_free_oracle():
+    # 1.4e9 concepts.  Intents: counts, per-level numbers, the order-free and
+    # the positional intent digests, the root's subtrees as output ranges, the
+    # lexicographic order and slices compared byte for byte.  Extents (3.5 TB in
+    # all) are paged through a bounded buffer with fcbo_write_range and every
+    # row hashed on the device: positional extent digest and the root's subtrees.
     path = os.path.join(GOLDEN, "ctx20000x256.json")
     if not os.path.exists(path):
         pytest.skip("stored oracle values not generated")
@@ -362,21 +496,42 @@ def test_full_ctx20000x256_intents_against_store_free_oracle():
         res = ctx.enumerate(extents=False)
         torch.cuda.synchronize()
         conc, tests = ctx.level_counts()
+        k = res.n_concepts
+        assert k == g["n_concepts"]
+        assert res.stats["closure_tests"] == g["closure_tests"]
+        assert res.stats["item_pairs"] == g["item_pairs"]
+        assert res.stats["sum_child_objects"] == g["sum_c"]
+        assert [int(x) for x in conc] == g["level_concepts"]
+        assert [int(x) for x in tests] == g["level_tests"]
+        ints = res.intents
+        step = 1 << 27
+        ih = torch.empty(k, dtype=torch.int64, device=ints.device)
+        for s0 in range(0, k, step):
+            ih[s0:s0 + step] = dg.intent_hashes_torch(ints[s0:s0 + step])
+        assert (int(ih.sum()) & dg.MASK) == int(g["intent_digest"])
+        assert digest_torch(ints[:1 << 20]) == (int(ih[:1 << 20].sum()) & dg.MASK)
+        assert dg.positional_torch(ih) == int(g["intent_positional"])
+        _check_root_subtrees(g, ih, "intent")
+        _assert_lectic_increasing(ints)
+        for sl in g["slices"]:
+            keep = torch.ones(k, dtype=torch.bool, device=ints.device)
+            for a in sl["attributes"]:
+                keep &= ((ints[:, a >> 6] >> (a & 63)) & 1) != 0
+            sel = ints[keep].cpu().numpy().view(np.uint64)
+            assert sel.shape[0] == sl["n_concepts"], sl["attributes"]
+            assert hashlib.sha256(np.ascontiguousarray(sel, dtype="<u8").tobytes()).hexdigest() == sl["intents_sha256"]
+        del ints, res, ih, keep
+        torch.cuda.empty_cache()
+        # extents, 2^22 rows (10.5 GB) at a time
+        page = 1 << 22
+        buf = torch.empty((page, 313), dtype=torch.int64, device="cuda")
+        eh = torch.empty(k, dtype=torch.int64, device="cuda")
+        for first in range(0, k, page):
+            cnt = min(page, k - first)
+            ctx.write_range(first, extents=buf[:cnt])
+            eh[first:first + cnt] = dg.extent_hashes_torch(buf[:cnt])
+        assert (int(eh.sum()) & dg.MASK) == int(g["extent_digest"])
+        assert dg.positional_torch(eh) == int(g["extent_positional"])
+        _check_root_subtrees(g, eh, "extent")
     finally:
         ctx.close()
-    assert res.n_concepts == g["n_concepts"]
-    assert res.stats["closure_tests"] == g["closure_tests"]
-    assert res.stats["item_pairs"] == g["item_pairs"]
-    assert res.stats["sum_child_objects"] == g["sum_c"]
-    assert [int(x) for x in conc] == g["level_concepts"]
-    assert [int(x) for x in tests] == g["level_tests"]
-    ints = res.intents
-    assert digest_torch(ints) == int(g["intent_digest"])
-    _assert_lectic_increasing(ints)
-    for sl in g["slices"]:
-        keep = torch.ones(ints.shape[0], dtype=torch.bool, device=ints.device)
-        for a in sl["attributes"]:
-            keep &= ((ints[:, a >> 6] >> (a & 63)) & 1) != 0
-        sel = ints[keep].cpu().numpy().view(np.uint64)
-        assert sel.shape[0] == sl["n_concepts"], sl["attributes"]
-        assert hashlib.sha256(np.ascontiguousarray(sel, dtype="<u8").tobytes()).hexdigest() == sl["intents_sha256"]

@@ -46,12 +46,46 @@ def test_error_strings(lib):
     assert fca.fcbo_error_string(12345) == "unknown error"
 
 
-def test_stats_struct_matches_header():
-    # 14 u64 counters, 4 doubles, then per kernel class one double and one u64
-    n = len(fca.KERNEL_CLASSES)
-    assert ctypes.sizeof(fca.FcboStats) == 14 * 8 + 4 * 8 + n * 8 + n * 8
+def header_stats_fields():
+    """(name, type, count) of every field of fcbo_stats as the header declares it."""
     text = open(HEADER).read()
-    assert "FCBO_K_NUM_CLASSES = %d" % len(fca.KERNEL_CLASSES) in text
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} fcbo_stats;", text, flags=re.S).group(1)
+    consts = {"FCBO_K_NUM_CLASSES": int(re.search(r"FCBO_K_NUM_CLASSES = (\d+)", text).group(1))}
+    out = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        m = re.fullmatch(r"(uint64_t|double)\s+(\w+)(?:\[(\w+)\])?", decl)
+        assert m, decl
+        out.append((m.group(2), m.group(1), consts[m.group(3)] if m.group(3) else 1))
+    return out
+
+
+def test_stats_struct_matches_header():
+    ctype = {"uint64_t": ctypes.c_uint64, "double": ctypes.c_double}
+    want = header_stats_fields()
+    got = []
+    for name, t in fca.FcboStats._fields_:
+        if issubclass(t, ctypes.Array):
+            got.append((name, t._type_, t._length_))
+        else:
+            got.append((name, t, 1))
+    assert [(n, ctype[t], c) for n, t, c in want] == got
+    assert len(fca.KERNEL_CLASSES) == dict((n, c) for n, _, c in want)["kernel_ms"]
+    # the measurement record comes first, as the header documents
+    assert [n for n, _, _ in want[:8]] == ["n_concepts", "closure_tests", "item_pairs", "n_levels", "enumerate_ms",
+                                          "closure_kernel_ms", "sort_ms", "model_bytes"]
+
+
+def test_error_codes_match_header():
+    text = open(HEADER).read()
+    for name in ("FCBO_OK", "FCBO_ERR_INVALID_ARGUMENT", "FCBO_ERR_OUT_OF_MEMORY", "FCBO_ERR_DEVICE",
+                 "FCBO_ERR_CAPACITY", "FCBO_ERR_LIMIT"):
+        v = int(re.search(r"\b%s = (-?\d+)" % name, text).group(1))
+        assert getattr(fca, name) == v, name
+    assert "32-bit" in fca.fcbo_error_string(fca.FCBO_ERR_LIMIT)
 
 
 def test_null_arguments_are_rejected_without_a_device(lib):
@@ -64,4 +98,8 @@ def test_null_arguments_are_rejected_without_a_device(lib):
     assert out.value is None
     lib.fcbo_enumerate.restype = ctypes.c_int
     assert lib.fcbo_enumerate(None, None, None, 0, 0, None, None) == fca.FCBO_ERR_INVALID_ARGUMENT
+    lib.fcbo_write_range.restype = ctypes.c_int
+    assert lib.fcbo_write_range(None, ctypes.c_uint64(0), ctypes.c_uint64(0), None, None) == fca.FCBO_ERR_INVALID_ARGUMENT
+    lib.fcbo_set_memory_limit.restype = ctypes.c_int
+    assert lib.fcbo_set_memory_limit(None, ctypes.c_uint64(1)) == fca.FCBO_ERR_INVALID_ARGUMENT
     lib.fcbo_destroy(None)

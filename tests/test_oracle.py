@@ -343,3 +343,114 @@ def test_store_free_oracle_matches_the_stored_search(case):
         assert d.digest == dg.digest_np(r.intents)
     if r.n_concepts <= 5000:
         assert d.digest == dg.digest_py(r.intents)
+
+
+# --- byte-model class split, extent hashes, positional digests ---------------------------
+
+def test_class_split_sums_against_the_cbo_tree():
+    # the oracle's split of the byte-model sums at a threshold T on |A| against
+    # the CbO tree rebuilt from the closed sets; several T so both classes occur
+    rng = np.random.default_rng(2024)
+    for case in range(60):
+        n = int(rng.integers(2, 90))
+        m = int(rng.integers(2, 12))
+        cells = synth.random_context(5000 + case, n, m, float(rng.uniform(0.1, 0.8)))
+        ctx = brute.Context(cells)
+        fam = brute.closed_intents_by_row_meets(ctx)
+        if len(fam) > 800:
+            continue
+        rows = synth.pack_rows(cells)
+        for t in (0, 1, n // 3, n // 2, n):
+            st = brute.cbo_tree(ctx, fam, rowlocal_max=t)
+            r = oracle.cbo(rows, m, keep_extents=False, rowlocal_max=t)
+            assert (r.sum_rl_objs, r.col_parents, r.col_nzw, r.col_child_objs) == (
+                st.sum_rl_objs, st.col_parents, st.col_nzw, st.col_child_objs), (case, t)
+    # every parent in exactly one class: the row-local objects plus the larger
+    # parents' objects are all objects of all concepts (|G| + sum |C|)
+    cells = synth.make_config("ctx2000x64", packed=False)
+    r = oracle.cbo(synth.pack_rows(cells), 64, keep_extents=True, rowlocal_max=100)
+    sizes = np.unpackbits(r.extents.view(np.uint8), axis=1).sum(axis=1)
+    assert r.sum_rl_objs == int(sizes[sizes <= 100].sum())
+    assert r.col_parents == int((sizes > 100).sum())
+    assert r.sum_rl_objs + int(sizes[sizes > 100].sum()) == cells.shape[0] + r.sum_c
+
+
+@pytest.mark.parametrize("shape", [(64, 16, 0.3), (130, 40, 0.1), (200, 70, 0.05), (2000, 30, 0.1)])
+def test_extent_hashes_follow_the_sorted_extents(shape):
+    from tests import intent_digest as dg
+
+    n, m, d = shape
+    cells = synth.random_context(31 * n + m, n, m, d)
+    r = oracle.cbo(synth.pack_rows(cells), m, keep_extents=True, hash_extents=True)
+    want = dg.extent_hashes_np(r.extents)
+    assert np.array_equal(r.extent_hashes, want)
+    for i in range(0, r.n_concepts, max(1, r.n_concepts // 40)):
+        assert int(r.extent_hashes[i]) == dg.extent_hash_py(r.extents[i])
+
+
+def test_extent_hash_distinguishes_word_order_and_bits():
+    from tests import intent_digest as dg
+
+    a = np.array([5, 0, 9], dtype=np.uint64)
+    assert dg.extent_hash_py(a) != dg.extent_hash_py(a[[2, 1, 0]])
+    b = a.copy()
+    b[1] = np.uint64(1 << 63)
+    assert dg.extent_hash_py(a) != dg.extent_hash_py(b)
+    # a word's term is f(word ^ f(index)): the empty one-word extent
+    assert dg.extent_hash_py(np.zeros(1, dtype=np.uint64)) == dg.mix_py(dg.mix_py(0))
+
+
+@pytest.mark.parametrize("case", ["ctx64x16", "ctx2000x64", "multiword", "contranominal", "all_zero", "one_object"])
+def test_positional_digests_of_the_store_free_oracle(case):
+    from tests import intent_digest as dg
+
+    if case in ("ctx64x16", "ctx2000x64"):
+        cells = synth.make_config(case, packed=False)
+    elif case == "multiword":
+        cells = synth.random_context(917, 300, 150, 0.05)
+    elif case == "contranominal":
+        cells = synth.pad_with_full(synth.contranominal(9), extra_objects=70, extra_attrs=60)
+    elif case == "all_zero":
+        cells = synth.all_zero(70, 65)
+    else:
+        cells = synth.random_context(3, 1, 20, 0.5)
+    rows = synth.pack_rows(cells)
+    m = cells.shape[1]
+    r = oracle.cbo(rows, m, keep_extents=True, hash_extents=True)
+    hi = dg.intent_hashes_np(r.intents)
+    he = dg.extent_hashes_np(r.extents)
+    assert np.array_equal(he, r.extent_hashes)
+    for threads in (1, 3):
+        d = oracle.cbo_digest(rows, m, threads=threads)
+        assert d.subtree_size == d.n_concepts == r.n_concepts
+        assert d.intent_digest == d.digest == int(hi.sum(dtype=np.uint64))
+        assert d.intent_positional == dg.positional_np(hi)
+        assert d.extent_digest == int(he.sum(dtype=np.uint64))
+        assert d.extent_positional == dg.positional_np(he)
+        # the root's children's subtrees: consecutive ranges after the root, by
+        # descending attribute, each starting with the child itself
+        start = 1
+        attrs = [c["attr"] for c in d.root_children]
+        assert attrs == sorted(attrs, reverse=True)
+        for c in d.root_children:
+            sl = slice(start, start + c["size"])
+            assert c["hi0"] == int(hi[sl].sum(dtype=np.uint64))
+            assert c["hi1"] == dg.positional_np(hi[sl])
+            assert c["he0"] == int(he[sl].sum(dtype=np.uint64))
+            assert c["he1"] == dg.positional_np(he[sl])
+            first = synth.unpack_rows(r.intents[start:start + 1], m)[0]
+            assert first[c["attr"]]
+            start += c["size"]
+        assert start == r.n_concepts
+    if r.n_concepts <= 3000:
+        assert d.intent_positional == dg.positional_py(hi)
+        assert d.extent_positional == dg.positional_py([dg.extent_hash_py(x) for x in r.extents])
+
+
+def test_model_bytes_inputs_are_the_class_sums():
+    # model_bytes is the byte count stated with fcbo_stats; its inputs are the
+    # pinned counters above.  All-ones 3 x 2: one concept, the root, row-local.
+    r = oracle.cbo(synth.pack_rows(synth.all_ones(3, 2)), 2, keep_extents=False)
+    assert (r.n_concepts, r.sum_rl_objs, r.col_parents, r.sum_c) == (1, 3, 0, 0)
+    # parent read (8 + 4 + 16) + 3 objects x (4 + 8) + root rows and list 3 x (8 + 4)
+    assert oracle.model_bytes(r) == 28 + 36 + 36
