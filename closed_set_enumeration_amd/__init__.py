@@ -40,6 +40,7 @@ EXPORTED = (
     "fcbo_context_create",
     "fcbo_enumerate",
     "fcbo_write_range",
+    "fcbo_cover_edges",
     "fcbo_set_memory_limit",
     "fcbo_level_counts",
     "fcbo_copy_columns",
@@ -116,6 +117,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fcbo_write_range.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
                                      ctypes.c_void_p]
     lib.fcbo_write_range.restype = ctypes.c_int
+    lib.fcbo_cover_edges.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                     P(ctypes.c_uint64), P(ctypes.c_double)]
+    lib.fcbo_cover_edges.restype = ctypes.c_int
     lib.fcbo_set_memory_limit.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
     lib.fcbo_set_memory_limit.restype = ctypes.c_int
     lib.fcbo_level_counts.argtypes = [
@@ -170,6 +174,18 @@ def fcbo_write_range(ctx: int, first: int, count: int, intents_out_ptr: int, ext
                                          ctypes.c_void_p(extents_out_ptr or None))
     if rc != FCBO_OK:
         raise FcboError(rc, "fcbo_write_range")
+
+
+def fcbo_cover_edges(ctx: int, offsets_out_ptr: int, targets_out_ptr: int, capacity: int):
+    """Returns (rc, n_edges, device ms); FCBO_ERR_CAPACITY is returned, not raised."""
+    e = ctypes.c_uint64(0)
+    ms = ctypes.c_double(0.0)
+    rc = load_library().fcbo_cover_edges(ctypes.c_void_p(ctx), ctypes.c_void_p(offsets_out_ptr or None),
+                                         ctypes.c_void_p(targets_out_ptr or None), capacity, ctypes.byref(e),
+                                         ctypes.byref(ms))
+    if rc not in (FCBO_OK, FCBO_ERR_CAPACITY):
+        raise FcboError(rc, "fcbo_cover_edges")
+    return rc, e.value, ms.value
 
 
 def fcbo_set_memory_limit(ctx: int, nbytes: int) -> None:
@@ -320,6 +336,21 @@ class Context:
             rows = r
         fcbo_write_range(self.handle, first, rows, intents.data_ptr() if intents is not None else 0,
                          extents.data_ptr() if extents is not None else 0)
+
+    def cover_edges(self):
+        """Lower covers of every concept of the last enumeration: (offsets int64 [K + 1],
+        targets int32 [E]) on the device, in output positions."""
+        torch = self._torch
+        rc, e, _ = fcbo_cover_edges(self.handle, 0, 0, 0)
+        assert rc == FCBO_ERR_CAPACITY
+        dev = torch.device("cuda", self.device)
+        k = fcbo_level_counts(self.handle)[0].sum()
+        offsets = torch.empty(int(k) + 1, dtype=torch.int64, device=dev)
+        targets = torch.empty(max(e, 1), dtype=torch.int32, device=dev)
+        rc, e2, ms = fcbo_cover_edges(self.handle, offsets.data_ptr(), targets.data_ptr(), targets.shape[0])
+        if rc != FCBO_OK or e2 != e:
+            raise FcboError(rc, "fcbo_cover_edges")
+        return offsets, targets[:e], ms
 
     def set_memory_limit(self, nbytes: int) -> None:
         fcbo_set_memory_limit(self.handle, nbytes)

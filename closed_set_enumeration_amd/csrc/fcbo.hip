@@ -217,6 +217,14 @@ struct fcbo_context {
     uint32_t *rank = nullptr;  // subtree size, then position, of every concept
     uint32_t *perm = nullptr;  // concept at every output position
 
+    // cover edges
+    uint64_t cap_csorted = 0, cap_ccount = 0, cap_coff = 0, cap_cbig = 0, cap_cctr = 0;
+    uint64_t *csorted = nullptr;  // intents in output order
+    uint32_t *ccount = nullptr;   // covers per output position
+    uint64_t *coff = nullptr;     // their exclusive scan
+    uint32_t *cbig = nullptr;     // positions of the concepts with more than 64 objects
+    uint64_t *cctr = nullptr;     // [0] their number, [1] covers not found
+
     // result of the last enumeration
     bool have_result = false;
     bool have_perm = false;
@@ -309,6 +317,8 @@ struct fcbo_context {
         huge.free_all(dmem);
         dfree(dmem, dt, cap_dt); dfree(dmem, tcnt, cap_tcnt); dfree(dmem, icnt, cap_icnt);
         dfree(dmem, rank, cap_rank); dfree(dmem, perm, cap_perm);
+        dfree(dmem, csorted, cap_csorted); dfree(dmem, ccount, cap_ccount); dfree(dmem, coff, cap_coff);
+        dfree(dmem, cbig, cap_cbig); dfree(dmem, cctr, cap_cctr);
         have_result = have_perm = false;
     }
 
@@ -411,6 +421,7 @@ struct fcbo_context {
     void order_concepts();
     void write_output(uint64_t *intents_out, uint64_t *extents_out, uint64_t first, uint64_t count);
     uint64_t model_bytes() const;
+    uint64_t cover_edges(uint64_t *offsets_out, uint32_t *targets_out, uint64_t capacity);
 };
 
 namespace {
@@ -883,6 +894,83 @@ void fcbo_context::setup(const uint64_t *rows_in, int64_t n_objects, int64_t n_a
     CK(hipStreamSynchronize(stream));
 }
 
+namespace {
+
+typedef void (*cover_fn)(const CoverArgs &, int, hipStream_t, int);
+
+template <int WMC>
+void launch_cover(const CoverArgs &C, int pass, hipStream_t s, int n_cu)
+{
+    if constexpr (WMC <= 8) {
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(16384, div_up(C.K, kWavesPerBlock)));
+        hipLaunchKernelGGL(k_cover_local<WMC>, dim3(g), dim3(kBlock), 0, s, C, pass);
+        CK_LAUNCH();
+    }
+    hipLaunchKernelGGL(k_cover_big<WMC>, dim3((unsigned)(4 * n_cu)), dim3(kCoverThreads), 0, s, C, pass);
+    CK_LAUNCH();
+}
+
+cover_fn pick_cover_fn(int wm)
+{
+    switch (wm) {
+    case 1: return launch_cover<1>;
+    case 2: return launch_cover<2>;
+    case 3: return launch_cover<3>;
+    case 4: return launch_cover<4>;
+    case 5: return launch_cover<5>;
+    case 6: return launch_cover<6>;
+    case 7: return launch_cover<7>;
+    case 8: return launch_cover<8>;
+    default:
+        if (wm <= 16) return launch_cover<16>;
+        if (wm <= 32) return launch_cover<32>;
+        return launch_cover<64>;
+    }
+}
+
+}  // namespace
+
+// Lower covers of every concept (see k_cover_local): the sorted intents for
+// the searches, the large concepts listed, a counting pass, the scan, and (when
+// the caller's buffer holds all E edges) the writing pass.  Returns E.
+uint64_t fcbo_context::cover_edges(uint64_t *offsets_out, uint32_t *targets_out, uint64_t capacity)
+{
+    if (!have_perm) order_concepts();
+    const uint64_t mc = min_cap();
+    ensure(dmem, csorted, cap_csorted, K * (uint64_t)wm, 0, stream, mc);
+    ensure(dmem, ccount, cap_ccount, K, 0, stream, mc);
+    ensure(dmem, coff, cap_coff, K + 1, 0, stream, mc);
+    ensure(dmem, cbig, cap_cbig, K, 0, stream, mc);
+    ensure(dmem, cctr, cap_cctr, 2, 0, stream, 2);
+    hipLaunchKernelGGL(k_output_intents, dim3(kGridCap), dim3(kBlock), 0, stream, (const uint64_t *)intents,
+                       (const uint32_t *)perm, K, wm, csorted);
+    CK_LAUNCH();
+    clear_words(cctr, 2);
+    CoverArgs C;
+    memset(&C, 0, sizeof(C));
+    C.rows = rows; C.intents = intents; C.loff = loff; C.objs = objs; C.perm = perm; C.sorted = csorted;
+    C.K = K; C.m = (int)m; C.wm = wm; C.tail_m = tail_m;
+    C.small_max = wm <= 8 ? kSmallMax : -1;
+    C.big = cbig; C.ctr = cctr; C.count = ccount; C.offsets = coff; C.targets = targets_out;
+    const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(4096, div_up(K, kBlock)));
+    hipLaunchKernelGGL(k_cover_list_big, dim3(gl), dim3(kBlock), 0, stream, C);
+    CK_LAUNCH();
+    const cover_fn fn = pick_cover_fn(wm);
+    fn(C, 1, stream, n_cu);
+    scan(ccount, nullptr, nullptr, K, K, coff, nullptr, nullptr, nullptr);
+    uint64_t e = 0;
+    CK(hipMemcpyAsync(&e, coff + K, sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+    CK(hipStreamSynchronize(stream));
+    if (!offsets_out || !targets_out || capacity < e) return e;
+    fn(C, 2, stream, n_cu);
+    CK(hipMemcpyAsync(offsets_out, coff, (K + 1) * sizeof(uint64_t), hipMemcpyDeviceToDevice, stream));
+    uint64_t missing = 0;
+    CK(hipMemcpyAsync(&missing, cctr + 1, sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+    CK(hipStreamSynchronize(stream));
+    if (missing) throw HipError{FCBO_ERR_DEVICE};  // a cover that is not a concept: cannot happen
+    return e;
+}
+
 // ---------------------------------------------------------------------------
 // C ABI
 
@@ -1034,6 +1122,37 @@ int fcbo_write_range(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_t
         return FCBO_ERR_OUT_OF_MEMORY;
     }
     return FCBO_OK;
+}
+
+int fcbo_cover_edges(fcbo_context *ctx, uint64_t *offsets_out, uint32_t *targets_out, uint64_t capacity,
+                     uint64_t *n_edges_out, double *elapsed_ms)
+{
+    if (!ctx || !ctx->have_result) return FCBO_ERR_INVALID_ARGUMENT;
+    if (ctx->m > kCoverMaxM) return FCBO_ERR_INVALID_ARGUMENT;
+    int rc = FCBO_OK;
+    try {
+        CK(hipSetDevice(ctx->device));
+        ctx->profile = false;
+        ctx->ev_used = 0;
+        ctx->marks.clear();
+        hipEvent_t e0 = ctx->ev_get(), e1 = ctx->ev_get();
+        CK(hipEventRecord(e0, ctx->stream));
+        const uint64_t e = ctx->cover_edges(offsets_out, targets_out, capacity);
+        CK(hipEventRecord(e1, ctx->stream));
+        CK(hipStreamSynchronize(ctx->stream));
+        if (n_edges_out) *n_edges_out = e;
+        if (!offsets_out || !targets_out || capacity < e) rc = FCBO_ERR_CAPACITY;
+        if (elapsed_ms) {
+            float ms = 0;
+            CK(hipEventElapsedTime(&ms, e0, e1));
+            *elapsed_ms = ms;
+        }
+    } catch (const HipError &err) {
+        return err.code;
+    } catch (const std::bad_alloc &) {
+        return FCBO_ERR_OUT_OF_MEMORY;
+    }
+    return rc;
 }
 
 int fcbo_set_memory_limit(fcbo_context *ctx, uint64_t bytes)

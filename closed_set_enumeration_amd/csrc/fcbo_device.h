@@ -2238,3 +2238,352 @@ __global__ void __launch_bounds__(kOutThreads) k_output_block(const uint64_t *__
 }
 
 }  // namespace fcbo
+
+namespace fcbo {
+
+// ---------------------------------------------------------------------------
+// Lattice cover edges.  The concepts ordered by extent inclusion form the
+// concept lattice; the lower covers of (A, B) are the concepts right below it
+// (page "hnwysp.cn/news/97538", section 4.4 and page "hotelren.com/news/5603750",
+// section 3.4 rebuild these edges after the enumeration).
+//
+// For an attribute n outside B let c_n = A AND col[n] (the objects of A having
+// n) and D_n = c_n' = (B + {n})''.  Every lower cover is some D_n, and D_n is a
+// lower cover exactly when no c_k (k outside B) strictly contains c_n.  The
+// attributes k of D_n outside B are exactly those with c_n inside c_k, so:
+//     D_n is a lower cover  <=>  |c_k| = |c_n| for every k in D_n \ B.
+// Each cover is generated by all of its attributes outside B; it is emitted
+// once, by the smallest of them (n = the first attribute of D_n outside B, the
+// form of the canonical test).  Of two covers the one emitted by the smaller
+// attribute holds it and the other does not, while both agree with B below it,
+// so it comes later in the output order: emitters in descending order give the
+// covers' output positions in ascending order.
+//
+// Output, per concept at output position i: its lower covers' positions,
+// ascending, at [offsets[i], offsets[i + 1]).  Two passes over the concepts:
+// counting, then (after a scan) writing.
+
+// Position of the intent d (wm words) in the sorted intents, or 0xFFFFFFFF.
+__device__ __forceinline__ uint32_t find_intent(const uint64_t *__restrict__ sorted, uint64_t K, int wm,
+                                                const uint64_t *d)
+{
+    uint64_t lo = 0, hi = K;
+    while (lo < hi) {
+        const uint64_t mid = lo + (hi - lo) / 2;
+        const uint64_t *x = sorted + mid * wm;
+        int c = 0;
+        for (int u = 0; u < wm && c == 0; ++u) {
+            const uint64_t diff = x[u] ^ d[u];
+            if (diff) c = ((x[u] >> (__ffsll((unsigned long long)diff) - 1)) & 1ull) ? 1 : -1;
+        }
+        if (c == 0) return (uint32_t)mid;
+        if (c < 0) lo = mid + 1;
+        else hi = mid;
+    }
+    return 0xFFFFFFFFu;
+}
+
+struct CoverArgs {
+    const uint64_t *rows;     // N x wm
+    const uint64_t *intents;  // generation order
+    const uint64_t *loff;
+    const uint32_t *objs;
+    const uint32_t *perm;     // output position -> concept
+    const uint64_t *sorted;   // K x wm intents in output order
+    uint64_t K;
+    int m, wm;
+    int64_t small_max;        // concepts with at most this many objects take the wavefront kernel
+    uint64_t tail_m;
+    uint32_t *big;            // output positions of the other concepts
+    uint64_t *ctr;            // [0]: their number, [1]: covers not found among the intents (stays 0)
+    uint32_t *count;          // pass 1: covers per output position
+    const uint64_t *offsets;  // pass 2: their exclusive scan
+    uint32_t *targets;        // pass 2: output positions of the covers
+};
+
+// The output positions whose concept has more than small_max objects.
+__global__ void __launch_bounds__(kBlock) k_cover_list_big(CoverArgs C)
+{
+    const uint64_t nt = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x; i0 < C.K; i0 += nt) {
+        const uint64_t i = i0 + threadIdx.x;
+        bool big = false;
+        if (i < C.K) {
+            const uint64_t c = C.perm[i];
+            big = (int64_t)(C.loff[c + 1] - C.loff[c]) > C.small_max;
+        }
+        wave_append(big, (uint32_t)i, C.big, &C.ctr[0]);
+    }
+}
+
+// Concepts with at most 64 objects, one wavefront each.  The object rows are
+// staged in LDS; for every intent word u, 64 ballots turn the rows around so
+// that lane b holds c_{64u+b} as a mask over the concept's objects.
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_cover_local(CoverArgs C, int pass)
+{
+    static_assert(WMC <= 8, "the wavefront cover kernel keeps rows of at most 8 words in LDS");
+    __shared__ uint64_t s_rows[kWavesPerBlock][kWave * WMC];
+    __shared__ uint8_t s_cnt[kWavesPerBlock][64 * WMC];
+    const int lane = lane_id();
+    const int wv = threadIdx.x / kWave;
+    const int wm = words_of<WMC>(C.wm);
+    uint64_t *R = s_rows[wv];
+    uint8_t *CN = s_cnt[wv];
+    for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + wv; i < C.K; i += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t c = C.perm[i];
+        const uint64_t o0 = C.loff[c], a = C.loff[c + 1] - o0;
+        if ((int64_t)a > C.small_max) continue;  // the workgroup kernel's
+        uint64_t B[WMC];
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            B[u] = ~0ull;
+            if (u < wm) {
+                B[u] = C.intents[c * C.wm + u];
+                if (u == wm - 1) B[u] |= ~C.tail_m;  // attributes past M count as in B
+            }
+        }
+        uint64_t row[WMC];
+        const bool mine = (uint64_t)lane < a;
+        const uint64_t g = mine ? C.objs[o0 + lane] : 0;
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            row[u] = (mine && u < wm) ? C.rows[g * C.wm + u] : 0ull;
+            R[lane * WMC + u] = row[u];
+        }
+        // lane b: cm[u] = the objects having attribute 64u + b; counts to LDS
+        uint64_t cm[WMC];
+        uint64_t carried = 0;  // some attribute outside B is carried by an object
+#pragma unroll
+        for (int u = 0; u < WMC; ++u) {
+            cm[u] = 0;
+            if (u < wm) {
+                for (int b = 0; b < 64; ++b) {
+                    const uint64_t bal = __ballot((row[u] >> b) & 1ull);
+                    if (lane == b) cm[u] = bal;
+                }
+                CN[u * 64 + lane] = (uint8_t)__popcll(cm[u]);
+                carried |= __ballot(!((B[u] >> lane) & 1ull) && cm[u] != 0);
+            }
+        }
+        wave_sync();
+        uint32_t base = 0;  // covers of larger emitters, placed before
+#pragma unroll
+        for (int u = WMC - 1; u >= 0; --u) {
+            if (u >= wm) continue;
+            // candidates: attributes outside B, the uncarried ones only when no
+            // attribute is carried (then every one gives the bottom)
+            bool cand = !((B[u] >> lane) & 1ull) && (cm[u] != 0 || carried == 0);
+            uint64_t D[WMC];
+#pragma unroll
+            for (int v = 0; v < WMC; ++v) D[v] = ~0ull;
+            if (cand) {
+                uint64_t mm = cm[u];
+                while (mm) {
+                    const int o = __ffsll((unsigned long long)mm) - 1;
+                    mm &= mm - 1ull;
+#pragma unroll
+                    for (int v = 0; v < WMC; ++v)
+                        if (v < wm) D[v] &= R[o * WMC + v];
+                }
+                D[wm - 1] &= C.tail_m;
+                // emitted by its first attribute outside B; a cover when every
+                // attribute outside B has n's object count
+                const int cnt_n = __popcll(cm[u]);
+                bool first = true;
+#pragma unroll
+                for (int v = 0; v < WMC; ++v) {
+                    if (v >= wm) continue;
+                    uint64_t x = D[v] & ~B[v];
+                    if (first && x) {
+                        if (v != u || (__ffsll((unsigned long long)x) - 1) != lane) cand = false;
+                        first = false;
+                    }
+                    while (x && cand) {
+                        const int k = __ffsll((unsigned long long)x) - 1;
+                        x &= x - 1ull;
+                        if ((int)CN[v * 64 + k] != cnt_n) cand = false;
+                    }
+                }
+            }
+            const uint64_t emit = __ballot(cand);
+            if (pass == 2 && cand) {
+                const uint32_t pos = find_intent(C.sorted, C.K, wm, D);
+                if (pos == 0xFFFFFFFFu) atomicAdd((unsigned long long *)&C.ctr[1], 1ull);
+                C.targets[C.offsets[i] + base + (uint32_t)__popcll(emit & ~upto_mask(lane))] = pos;
+            }
+            base += (uint32_t)__popcll(emit);
+        }
+        if (pass == 1 && lane == 0) C.count[i] = base;
+        wave_sync();
+    }
+}
+
+// Concepts with more objects, one workgroup each (from the list): object
+// counts of all attributes by incidence (LDS atomics); then the carried
+// candidates in slices of kCoverSlice, each slice's D_n accumulated in one pass
+// over the extent list (LDS AND atomics) and tested one per thread.  The
+// covers' positions go to an LDS table indexed by emitter and leave in
+// descending emitter order.
+constexpr int kCoverThreads = 256;
+constexpr int kCoverSlice = 64;
+constexpr int kCoverMaxM = 4096;
+
+template <int WMC>
+__global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pass)
+{
+    constexpr int WS = WMC <= 8 ? WMC : 64;  // words of a D entry kept in LDS
+    __shared__ uint32_t s_cnt[kCoverMaxM];   // |c_n|
+    __shared__ uint32_t s_pos[kCoverMaxM];   // position of the cover emitted by n, else ~0
+    __shared__ int16_t s_slot[kCoverMaxM];   // slot of n in the current slice, else -1
+    __shared__ uint64_t s_d[kCoverSlice * WS];
+    __shared__ uint64_t s_mask[WS];          // the current slice's attributes
+    __shared__ uint32_t s_sum[kCoverThreads / kWave];
+    __shared__ uint32_t s_nc, s_slice[kCoverSlice];
+    const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+    const int wm = words_of<WMC>(C.wm);
+    const uint64_t nbig = C.ctr[0];
+    for (uint64_t it = blockIdx.x; it < nbig; it += gridDim.x) {
+        const uint64_t i = C.big[it];
+        const uint64_t c = C.perm[i];
+        const uint64_t o0 = C.loff[c], o1 = C.loff[c + 1];
+        const uint64_t *Bp = C.intents + c * C.wm;
+        auto in_b = [&](int n) -> bool { return ((Bp[n >> 6] >> (n & 63)) & 1ull) != 0; };
+        for (int n = tid; n < C.m; n += kCoverThreads) {
+            s_cnt[n] = 0;
+            s_pos[n] = 0xFFFFFFFFu;
+            s_slot[n] = -1;
+        }
+        __syncthreads();
+        for (uint64_t o = o0 + tid; o < o1; o += kCoverThreads) {
+            const uint64_t g = C.objs[o];
+            for (int u = 0; u < wm; ++u) {
+                uint64_t x = C.rows[g * C.wm + u] & ~Bp[u];
+                while (x) {
+                    const int b = __ffsll((unsigned long long)x) - 1;
+                    x &= x - 1ull;
+                    atomicAdd(&s_cnt[64 * u + b], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        uint32_t carried = 0;
+        for (int n = tid; n < C.m; n += kCoverThreads) carried += (!in_b(n) && s_cnt[n]) ? 1u : 0u;
+        carried = wave_sum(carried);
+        if (lane == 0) s_sum[wv] = carried;
+        __syncthreads();
+        uint32_t total = 0;
+        for (int w = 0; w < kCoverThreads / kWave; ++w) total += s_sum[w];
+        __syncthreads();
+        uint32_t found = 0;
+        if (total == 0) {
+            // nothing outside B is carried: every attribute outside B gives the
+            // bottom, emitted by the first of them (none: this is the bottom)
+            if (tid == 0) {
+                int j0 = -1;
+                for (int n = 0; n < C.m && j0 < 0; ++n)
+                    if (!in_b(n)) j0 = n;
+                if (j0 >= 0) {
+                    found = 1;
+                    if (pass == 2) {
+                        uint64_t d[WS];
+                        for (int v = 0; v < wm; ++v) d[v] = (v == wm - 1) ? C.tail_m : ~0ull;
+                        const uint32_t pos = find_intent(C.sorted, C.K, wm, d);
+                        if (pos == 0xFFFFFFFFu) atomicAdd((unsigned long long *)&C.ctr[1], 1ull);
+                        C.targets[C.offsets[i]] = pos;
+                    }
+                }
+            }
+        } else {
+            int next = 0;  // first attribute not yet sliced
+            while (true) {
+                if (tid == 0) {
+                    uint32_t nc = 0;
+                    for (int n = next; n < C.m && nc < (uint32_t)kCoverSlice; ++n)
+                        if (!in_b(n) && s_cnt[n]) s_slice[nc++] = (uint32_t)n;
+                    s_nc = nc;
+                }
+                if (tid < WS) s_mask[tid] = 0;
+                __syncthreads();
+                const uint32_t nc = s_nc;
+                if (nc == 0) break;
+                next = (int)s_slice[nc - 1] + 1;
+                for (uint32_t x = tid; x < nc * WS; x += kCoverThreads) s_d[x] = ~0ull;
+                if ((uint32_t)tid < nc) {
+                    const uint32_t n = s_slice[tid];
+                    s_slot[n] = (int16_t)tid;
+                    atomicOr((unsigned long long *)&s_mask[n >> 6], (unsigned long long)(1ull << (n & 63)));
+                }
+                __syncthreads();
+                for (uint64_t o = o0 + tid; o < o1; o += kCoverThreads) {
+                    const uint64_t *row = C.rows + C.objs[o] * (uint64_t)C.wm;
+                    for (int u = 0; u < wm; ++u) {
+                        uint64_t x = row[u] & s_mask[u];
+                        while (x) {
+                            const int r = s_slot[64 * u + __ffsll((unsigned long long)x) - 1];
+                            x &= x - 1ull;
+                            for (int v = 0; v < wm; ++v)
+                                atomicAnd((unsigned long long *)&s_d[r * WS + v], (unsigned long long)row[v]);
+                        }
+                    }
+                }
+                __syncthreads();
+                if ((uint32_t)tid < nc) {
+                    const int n = (int)s_slice[tid];
+                    const uint64_t *D = s_d + tid * WS;
+                    const uint32_t cnt_n = s_cnt[n];
+                    bool ok = true, first = true;
+                    for (int v = 0; v < wm && ok; ++v) {
+                        uint64_t x = D[v] & ~Bp[v];
+                        if (v == wm - 1) x &= C.tail_m;
+                        if (first && x) {
+                            ok = (64 * v + __ffsll((unsigned long long)x) - 1) == n;
+                            first = false;
+                        }
+                        while (x && ok) {
+                            const int k = 64 * v + __ffsll((unsigned long long)x) - 1;
+                            x &= x - 1ull;
+                            if (s_cnt[k] != cnt_n) ok = false;
+                        }
+                    }
+                    if (ok) {
+                        uint32_t pos = 0;
+                        if (pass == 2) {
+                            uint64_t d[WS];
+                            for (int v = 0; v < wm; ++v) d[v] = (v == wm - 1) ? (D[v] & C.tail_m) : D[v];
+                            pos = find_intent(C.sorted, C.K, wm, d);
+                            if (pos == 0xFFFFFFFFu) atomicAdd((unsigned long long *)&C.ctr[1], 1ull);
+                        }
+                        s_pos[n] = pos;
+                    }
+                    s_slot[n] = -1;
+                }
+                __syncthreads();
+            }
+            // covers in descending emitter order: thread t takes a block of
+            // attributes from the top down
+            const int per = (C.m + kCoverThreads - 1) / kCoverThreads;
+            const int hi = C.m - tid * per, lo = hi - per > 0 ? hi - per : 0;
+            uint32_t mine = 0;
+            for (int n = hi - 1; n >= lo; --n) mine += s_pos[n] != 0xFFFFFFFFu ? 1u : 0u;
+            const uint32_t ex = wave_excl_scan(mine);
+            if (lane == kWave - 1) s_sum[wv] = ex + mine;
+            __syncthreads();
+            uint32_t before = 0, all = 0;
+            for (int w = 0; w < kCoverThreads / kWave; ++w) {
+                before += w < wv ? s_sum[w] : 0u;
+                all += s_sum[w];
+            }
+            if (pass == 2) {
+                uint64_t at = C.offsets[i] + before + ex;
+                for (int n = hi - 1; n >= lo; --n)
+                    if (s_pos[n] != 0xFFFFFFFFu) C.targets[at++] = s_pos[n];
+            }
+            found = all;
+        }
+        if (pass == 1 && tid == 0) C.count[i] = found;
+        __syncthreads();
+    }
+}
+
+}  // namespace fcbo

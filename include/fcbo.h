@@ -200,6 +200,24 @@ int fcbo_write_range(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_t
                      uint64_t *extents_out);
 
 /*
+ * Lattice cover edges of the last enumeration (page 1 section 4.4 and page 4
+ * section 3.4 rebuild them after the concepts are found): for the concept at
+ * output position i, the output positions of its lower covers (the concepts
+ * right below it in the lattice: extent strictly inside, nothing between), in
+ * ascending order, at targets_out[offsets_out[i] .. offsets_out[i + 1]).
+ *   offsets_out   K + 1 words, device
+ *   targets_out   E 32-bit positions, device
+ *   capacity      entries available in targets_out
+ *   n_edges_out   receives E (also on FCBO_ERR_CAPACITY); may be NULL
+ *   elapsed_ms    device time of the call (HIP events), or NULL
+ * If either buffer is NULL or capacity < E the call returns FCBO_ERR_CAPACITY,
+ * stores E and writes nothing.  FCBO_ERR_INVALID_ARGUMENT if nothing was
+ * enumerated.  Returns after the stream has finished.
+ */
+int fcbo_cover_edges(fcbo_context *ctx, uint64_t *offsets_out, uint32_t *targets_out, uint64_t capacity,
+                     uint64_t *n_edges_out, double *elapsed_ms);
+
+/*
  * Cap the device memory the context's enumeration buffers may hold (bytes;
  * 0 = no cap).  An enumeration that would need more fails with
  * FCBO_ERR_OUT_OF_MEMORY at the allocation that crosses the cap, as a full

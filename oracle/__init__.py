@@ -12,6 +12,8 @@ leg of the benchmark do.  It shares no code with the GPU path.
   digest of the intents and positional digests of intents and extents (every
   concept weighted by its output position), also per subtree of the root's
   children (for contexts whose concepts do not fit in memory).
+* :func:`cover_edges` lists the lattice's cover edges (``cover.c``): the lower
+  covers of every concept of a sorted concept list, as output positions.
 * :func:`model_bytes` evaluates the algorithmic byte count of an enumeration
   (the formula documented with ``fcbo_stats`` in the library header) from the
   oracle's counters.
@@ -32,6 +34,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "cbo.c")
 _SRC_DIGEST = os.path.join(_HERE, "cbo_digest.c")
+_SRC_COVER = os.path.join(_HERE, "cover.c")
 _LIB = os.path.join(_HERE, "liboracle_cbo.so")
 
 
@@ -96,7 +99,7 @@ class _Digest(ctypes.Structure):
 
 def build(force: bool = False) -> str:
     """Compile ``cbo.c`` and ``cbo_digest.c`` into ``liboracle_cbo.so`` (plain gcc, -O2, no SIMD flags)."""
-    srcs = [_SRC, _SRC_DIGEST]
+    srcs = [_SRC, _SRC_DIGEST, _SRC_COVER]
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
         [os.path.getmtime(x) for x in srcs] + [os.path.getmtime(os.path.join(_HERE, "oracle_cbo.h"))]
     ):
@@ -131,6 +134,14 @@ def _load():
         lib.oracle_cbo_digest.restype = ctypes.c_int
         lib.oracle_digest_free.argtypes = [ctypes.POINTER(_Digest)]
         lib.oracle_digest_free.restype = None
+        lib.oracle_cover_edges.argtypes = [
+            ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
+            ctypes.POINTER(ctypes.POINTER(ctypes.c_int64)), ctypes.POINTER(ctypes.c_int64),
+        ]
+        lib.oracle_cover_edges.restype = ctypes.c_int
+        lib.oracle_cover_free.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+        lib.oracle_cover_free.restype = None
         _lib = lib
     return _lib
 
@@ -294,3 +305,29 @@ def model_bytes(r: OracleResult) -> int:
     b += (k - 1) * (8 * wm + 4 + 8) + 4 * r.sum_c
     b += r.n_objects * (8 * wm + 4)
     return b
+
+
+def cover_edges(rows: np.ndarray, n_attrs: int, intents: np.ndarray):
+    """Lower covers of every concept of a complete, sorted concept list.
+
+    Returns (offsets int64 [K + 1], targets int64 [E]): the lower covers of the
+    concept at position i are targets[offsets[i]:offsets[i + 1]], ascending."""
+    lib = _load()
+    rows = np.ascontiguousarray(rows, dtype=np.uint64)
+    intents = np.ascontiguousarray(intents, dtype=np.uint64)
+    k = intents.shape[0]
+    offsets = np.zeros(k + 1, dtype=np.int64)
+    tg = ctypes.POINTER(ctypes.c_int64)()
+    ne = ctypes.c_int64(0)
+    rc = lib.oracle_cover_edges(
+        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), rows.shape[0], int(n_attrs), rows.shape[1],
+        intents.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), k,
+        offsets.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ctypes.byref(tg), ctypes.byref(ne),
+    )
+    if rc != 0:
+        raise RuntimeError("oracle_cover_edges failed with %d" % rc)
+    try:
+        targets = np.ctypeslib.as_array(tg, shape=(ne.value,)).copy() if ne.value else np.zeros(0, np.int64)
+    finally:
+        lib.oracle_cover_free(tg)
+    return offsets, targets

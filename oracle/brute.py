@@ -199,3 +199,19 @@ def cbo_tree(ctx: Context, intents: set[int], rowlocal_max: int = 1 << 62) -> Tr
             if bin(ctx.objects_of(parent[d])).count("1") > rowlocal_max:
                 st.col_child_objs += size
     return st
+
+
+def hasse_lower_covers(intents_in_order: list[int]) -> list[list[int]]:
+    """The cover relation from the definition: for every concept i (intents as
+    Python-int sets, in some fixed order) the positions j of the concepts right
+    below it: B_i strictly inside B_j with no B_k strictly between."""
+    below = [[j for j, d in enumerate(intents_in_order) if d != b and (b & ~d) == 0] for b in intents_in_order]
+    out = []
+    for i, js in enumerate(below):
+        covers = []
+        for j in js:
+            dj = intents_in_order[j]
+            if not any(k != j and (dk := intents_in_order[k]) != dj and (dk & ~dj) == 0 for k in js):
+                covers.append(j)
+        out.append(sorted(covers))
+    return out

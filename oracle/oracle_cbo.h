@@ -83,4 +83,16 @@ int oracle_cbo_digest(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, 
 
 void oracle_digest_free(oracle_digest *d);
 
+/* Lower covers of every concept of a complete concept list (cover.c): the
+ * intents, K x wm words, in the output order of oracle_cbo.  offsets gets
+ * K + 1 entries; *targets_out (free with oracle_cover_free) the positions of
+ * the lower covers of concept i at [offsets[i], offsets[i + 1]), ascending.
+ * Returns 0, -1 on bad arguments, -2 when memory runs out, -3 if a closure is
+ * missing from the list. */
+int oracle_cover_edges(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, int64_t row_stride,
+                       const uint64_t *intents, int64_t k, int64_t *offsets, int64_t **targets_out,
+                       int64_t *n_edges_out);
+
+void oracle_cover_free(int64_t *targets);
+
 #endif

@@ -405,6 +405,10 @@ def _sample_extents_match(cells, ints, exts_t, sample, seed):
         assert np.array_equal(synth.unpack_rows(got[r:r + 1], n)[0], ext), i
 
 
+def _say(msg):
+    print("[full-size] %s" % msg, flush=True)
+
+
 def test_full_ctx50000x400_against_stored_oracle():
     # The benchmark's configuration (extents written).  Stored oracle values:
     # counts, SHA-256 of the ordered intents and of the ordered extent hashes
@@ -435,6 +439,7 @@ def test_full_ctx50000x400_against_stored_oracle():
         assert (st["big_parents"], st["big_nonzero_words"], st["big_child_objects"]) == (
             g["col_parents"], g["col_nzw"], g["col_child_objs"])
         assert st["model_bytes"] == g["model_bytes"]
+        _say("ctx50000x400: counts and intents match; hashing extents")
         eh = dg.extent_hashes_torch(res.extents)
         ehs = eh.cpu().numpy().view(np.uint64)
         assert hashlib.sha256(np.ascontiguousarray(ehs, dtype="<u8").tobytes()).hexdigest() == g["extent_hashes_sha256"]
@@ -504,6 +509,7 @@ def test_full_ctx20000x256_against_store_free_oracle():
         assert [int(x) for x in conc] == g["level_concepts"]
         assert [int(x) for x in tests] == g["level_tests"]
         ints = res.intents
+        _say("ctx20000x256: counts match; hashing intents")
         step = 1 << 27
         ih = torch.empty(k, dtype=torch.int64, device=ints.device)
         for s0 in range(0, k, step):
@@ -512,24 +518,34 @@ def test_full_ctx20000x256_against_store_free_oracle():
         assert digest_torch(ints[:1 << 20]) == (int(ih[:1 << 20].sum()) & dg.MASK)
         assert dg.positional_torch(ih) == int(g["intent_positional"])
         _check_root_subtrees(g, ih, "intent")
-        _assert_lectic_increasing(ints)
+        del ih
+        torch.cuda.empty_cache()
+        _say("ctx20000x256: intent digests match; order and slices")
+        _assert_lectic_increasing(ints, chunk=1 << 24)
         for sl in g["slices"]:
-            keep = torch.ones(k, dtype=torch.bool, device=ints.device)
-            for a in sl["attributes"]:
-                keep &= ((ints[:, a >> 6] >> (a & 63)) & 1) != 0
-            sel = ints[keep].cpu().numpy().view(np.uint64)
+            parts = []
+            for s0 in range(0, k, 1 << 26):
+                block = ints[s0:s0 + (1 << 26)]
+                keep = torch.ones(block.shape[0], dtype=torch.bool, device=ints.device)
+                for a in sl["attributes"]:
+                    keep &= ((block[:, a >> 6] >> (a & 63)) & 1) != 0
+                parts.append(block[keep].cpu().numpy().view(np.uint64))
+            sel = np.concatenate(parts)
             assert sel.shape[0] == sl["n_concepts"], sl["attributes"]
             assert hashlib.sha256(np.ascontiguousarray(sel, dtype="<u8").tobytes()).hexdigest() == sl["intents_sha256"]
-        del ints, res, ih, keep
+        del ints, res, block, keep
         torch.cuda.empty_cache()
         # extents, 2^22 rows (10.5 GB) at a time
         page = 1 << 22
         buf = torch.empty((page, 313), dtype=torch.int64, device="cuda")
         eh = torch.empty(k, dtype=torch.int64, device="cuda")
+        _say("ctx20000x256: paging extents")
         for first in range(0, k, page):
             cnt = min(page, k - first)
             ctx.write_range(first, extents=buf[:cnt])
             eh[first:first + cnt] = dg.extent_hashes_torch(buf[:cnt])
+            if (first // page) % 32 == 0:
+                _say("ctx20000x256: extents of rows %d.. hashed" % first)
         assert (int(eh.sum()) & dg.MASK) == int(g["extent_digest"])
         assert dg.positional_torch(eh) == int(g["extent_positional"])
         _check_root_subtrees(g, eh, "extent")

@@ -454,3 +454,76 @@ def test_model_bytes_inputs_are_the_class_sums():
     assert (r.n_concepts, r.sum_rl_objs, r.col_parents, r.sum_c) == (1, 3, 0, 0)
     # parent read (8 + 4 + 16) + 3 objects x (4 + 8) + root rows and list 3 x (8 + 4)
     assert oracle.model_bytes(r) == 28 + 36 + 36
+
+
+# --- lattice cover edges ---------------------------------------------------------------
+
+def _edges_as_lists(offsets, targets):
+    return [list(targets[offsets[i]:offsets[i + 1]]) for i in range(len(offsets) - 1)]
+
+
+def test_cover_edges_against_the_hasse_diagram():
+    rng = np.random.default_rng(777)
+    for case in range(150):
+        n = int(rng.integers(1, 40))
+        m = int(rng.integers(1, 11))
+        cells = synth.random_context(9000 + case, n, m, float(rng.uniform(0.1, 0.9)))
+        r = run(cells, keep_extents=False)
+        off, tg = oracle.cover_edges(synth.pack_rows(cells), m, r.intents)
+        want = brute.hasse_lower_covers(as_sets(r.intents))
+        assert _edges_as_lists(off, tg) == want, case
+
+
+@pytest.mark.parametrize("k", [2, 3, 10, 70])
+def test_cover_edges_diagonal(k):
+    # top -> each atom -> bottom
+    cells = synth.diagonal(k)
+    r = run(cells, keep_extents=False)
+    off, tg = oracle.cover_edges(synth.pack_rows(cells), k, r.intents)
+    assert len(tg) == 2 * k
+
+
+@pytest.mark.parametrize("k", [1, 4, 9])
+def test_cover_edges_contranominal(k):
+    # the Boolean lattice of k atoms: k * 2^(k-1) edges, every set covers its k - |B| one-larger supersets
+    cells = synth.contranominal(k)
+    r = run(cells, keep_extents=False)
+    off, tg = oracle.cover_edges(synth.pack_rows(cells), k, r.intents)
+    assert len(tg) == k * 2 ** (k - 1)
+    sets = as_sets(r.intents)
+    for i, b in enumerate(sets):
+        assert [sets[t] for t in tg[off[i]:off[i + 1]]] == sorted(
+            [b | (1 << a) for a in range(k) if not (b >> a) & 1], key=lambda d: brute.intent_key(d, k))
+
+
+def test_cover_edges_chain_and_trivial_lattices():
+    # staircase: object i has attributes 0..i, the lattice is a chain
+    n = 70
+    cells = np.tril(np.ones((n, n), dtype=bool))
+    r = run(cells, keep_extents=False)
+    off, tg = oracle.cover_edges(synth.pack_rows(cells), n, r.intents)
+    assert len(tg) == r.n_concepts - 1
+    for cells, edges in [(synth.all_zero(5, 4), 1), (synth.all_ones(5, 4), 0)]:
+        r = run(cells, keep_extents=False)
+        off, tg = oracle.cover_edges(synth.pack_rows(cells), cells.shape[1], r.intents)
+        assert len(tg) == edges
+
+
+def test_cover_edges_invariants_ctx2000x64():
+    cells = synth.make_config("ctx2000x64", packed=False)
+    r = run(cells, keep_extents=False)
+    off, tg = oracle.cover_edges(synth.pack_rows(cells), 64, r.intents)
+    k = r.n_concepts
+    deg = np.diff(off)
+    ib = synth.unpack_rows(r.intents, 64)
+    bottom = int(np.flatnonzero(ib.all(axis=1))[0])
+    assert (deg[np.arange(k) != bottom] > 0).all() and deg[bottom] == 0
+    hit = np.zeros(k, dtype=bool)
+    hit[tg] = True
+    assert not hit[0] and hit[1:].all()  # every concept but the top has an upper cover
+    src = np.repeat(np.arange(k), deg)
+    # each edge goes to a strictly larger intent (every source attribute kept)
+    sample = np.random.default_rng(5).choice(len(tg), size=3000, replace=False)
+    for e in sample:
+        a, b = ib[src[e]], ib[tg[e]]
+        assert (b | ~a).all() and (b != a).any()
