@@ -18,6 +18,8 @@ Prints one JSON line.  `value` is concepts per second; beside it:
     byte count `model_bytes` over its measured time;
   * `hbm_probe`: a device copy and a fill timed in the same process, the
     achievable bandwidth on this box;
+  * `cover_edges`: the lattice's cover edges of the same result
+    (fcbo_cover_edges), timed once after the steps;
   * `cpu_baseline`: the store-free CPU oracle over the whole workload on one
     pinned host core, run before the GPU is touched; `cpu_baseline_all_cores`
     the same search split over the host cores.
@@ -247,6 +249,7 @@ def main():
     ap.add_argument("--extents", choices=("auto", "yes", "no"), default="auto",
                     help="write the extent bitmaps (auto: when K x N/8 bytes fit in a third of device memory)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cover", action="store_true", help="skip the cover-edge measurement")
     ap.add_argument("--cpu-threads", type=int, default=0, help="threads of the all-core CPU baseline (0: the "
                     "process's cores, at most 16)")
     ap.add_argument("--cpu-bitmap-tests", type=int, default=2_000_000,
@@ -365,6 +368,16 @@ def main():
     if closure_roof["traffic"]:
         closure_roof["traffic_over_model"] = round(closure_roof["traffic"] / model, 3)
 
+    # the lattice's cover edges of the same result (not part of the step)
+    cover = None
+    if not args.no_cover:
+        _, e, _ = ctx.cover_edges()
+        _, e, cms = ctx.cover_edges()
+        cover = {"edges": int(e.shape[0]), "ms": round(cms, 4), "edges_per_s": round(e.shape[0] / (cms * 1e-3), 1),
+                 "concepts_per_s": round(k / (cms * 1e-3), 1), "timing": "second call, HIP events on the stream"}
+        del e
+        print("[bench] cover edges: %s" % json.dumps(cover), file=sys.stderr, flush=True)
+
     tests = st0["closure_tests"]
     out = {
         "metric": "concepts/sec and closure tests/sec at 1 GPU; % of HBM roofline",
@@ -394,6 +407,7 @@ def main():
         "cpu_baseline": cpu["one"] if cpu else None,
         "cpu_baseline_all_cores": cpu["all"] if cpu else None,
         "cpu_baseline_bitmap_oracle": cpu.get("bitmap") if cpu else None,
+        "cover_edges": cover,
     }
     ctx.close()
     del ints, exts
