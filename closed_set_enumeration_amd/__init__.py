@@ -27,6 +27,8 @@ FCBO_ERR_OUT_OF_MEMORY = -2
 FCBO_ERR_DEVICE = -3
 FCBO_ERR_CAPACITY = -4
 FCBO_ERR_LIMIT = -5
+FCBO_ERR_SCRATCH = -6
+FCBO_STATIC_SCRATCH_BYTES = 64 << 20
 
 FCBO_ROWS_ON_DEVICE = 1
 FCBO_TINY_BUFFERS = 2
@@ -42,6 +44,7 @@ EXPORTED = (
     "fcbo_write_range",
     "fcbo_cover_edges",
     "fcbo_set_memory_limit",
+    "fcbo_enumerate_static",
     "fcbo_level_counts",
     "fcbo_copy_columns",
     "fcbo_destroy",
@@ -122,6 +125,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fcbo_cover_edges.restype = ctypes.c_int
     lib.fcbo_set_memory_limit.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
     lib.fcbo_set_memory_limit.restype = ctypes.c_int
+    lib.fcbo_enumerate_static.argtypes = [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, P(ctypes.c_uint64), P(FcboStats),
+    ]
+    lib.fcbo_enumerate_static.restype = ctypes.c_int
     lib.fcbo_level_counts.argtypes = [
         ctypes.c_void_p, P(ctypes.c_uint64), P(ctypes.c_uint64), ctypes.c_uint64, P(ctypes.c_uint64),
     ]
@@ -192,6 +200,22 @@ def fcbo_set_memory_limit(ctx: int, nbytes: int) -> None:
     rc = load_library().fcbo_set_memory_limit(ctypes.c_void_p(ctx), int(nbytes))
     if rc != FCBO_OK:
         raise FcboError(rc, "fcbo_set_memory_limit")
+
+
+def fcbo_enumerate_static(rows_ptr: int, n_objects: int, n_attrs: int, row_stride_words: int, flags: int,
+                          hip_stream: int, intents_out_ptr: int, extents_out_ptr: int, capacity: int):
+    """The allocation-free call.  Returns (rc, n_concepts, FcboStats); FCBO_ERR_CAPACITY and
+    FCBO_ERR_SCRATCH are returned, other errors raised."""
+    k = ctypes.c_uint64(0)
+    st = FcboStats()
+    rc = load_library().fcbo_enumerate_static(
+        ctypes.c_void_p(rows_ptr), n_objects, n_attrs, row_stride_words, flags, ctypes.c_void_p(hip_stream),
+        ctypes.c_void_p(intents_out_ptr or None), ctypes.c_void_p(extents_out_ptr or None), capacity,
+        ctypes.byref(k), ctypes.byref(st),
+    )
+    if rc not in (FCBO_OK, FCBO_ERR_CAPACITY, FCBO_ERR_SCRATCH):
+        raise FcboError(rc, "fcbo_enumerate_static")
+    return rc, k.value, st
 
 
 def fcbo_level_counts(ctx: int):

@@ -55,7 +55,7 @@ struct DeviceMemory {
     {
         if (region) {
             const uint64_t at = (region_used + 255) & ~255ull;
-            if (at > region_size || bytes > region_size - at) throw HipError{FCBO_ERR_OUT_OF_MEMORY};
+            if (at > region_size || bytes > region_size - at) throw HipError{FCBO_ERR_SCRATCH};
             region_used = at + bytes;
             return region + at;
         }
@@ -972,6 +972,35 @@ uint64_t fcbo_context::cover_edges(uint64_t *offsets_out, uint32_t *targets_out,
 }
 
 // ---------------------------------------------------------------------------
+// Static device scratch of fcbo_enumerate_static: one copy per GPU, held until
+// the process ends.  Host code never takes its name as an address (that is a
+// host-side stand-in): the device address comes from hipGetSymbolAddress, once
+// per device with that device current, and is kept per device.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[FCBO_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+char *g_scratch_ptr[kMaxDevices] = {};
+
+char *scratch_on_device(int device)
+{
+    if (device < 0 || device >= kMaxDevices) throw HipError{FCBO_ERR_DEVICE};
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[device]) {
+        void *p = nullptr;
+        CK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) throw HipError{FCBO_ERR_DEVICE};
+        g_scratch_ptr[device] = (char *)p;
+    }
+    return g_scratch_ptr[device];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // C ABI
 
 extern "C" {
@@ -985,6 +1014,7 @@ const char *fcbo_error_string(int code)
     case FCBO_ERR_DEVICE: return "HIP device error";
     case FCBO_ERR_CAPACITY: return "output capacity too small";
     case FCBO_ERR_LIMIT: return "2^32 concepts or more (beyond the 32-bit concept indices)";
+    case FCBO_ERR_SCRATCH: return "the work does not fit the static scratch of fcbo_enumerate_static";
     default: return "unknown error";
     }
 }
@@ -1099,6 +1129,69 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
     st.order_launches = ctx->order_launches;
     if (rc == FCBO_OK)
         st.output_bytes = ctx->K * (uint64_t)ctx->wm * 8 + (extents_out ? ctx->K * (uint64_t)ctx->wn * 8 : 0);
+    if (stats_out) *stats_out = st;
+    return rc;
+}
+
+int fcbo_enumerate_static(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, int64_t row_stride_words,
+                          uint32_t flags, void *hip_stream, uint64_t *intents_out, uint64_t *extents_out,
+                          uint64_t capacity, uint64_t *n_concepts_out, fcbo_stats *stats_out)
+{
+    if (!valid_context_args(rows, n_objects, n_attrs, row_stride_words) || (flags & ~FCBO_ROWS_ON_DEVICE))
+        return FCBO_ERR_INVALID_ARGUMENT;
+    {
+        // the context alone (rows with the zero row, columns, scan partials,
+        // counters) must leave at least half of the scratch to the enumeration
+        const uint64_t wn = ((uint64_t)n_objects + 63) / 64, wm = ((uint64_t)n_attrs + 63) / 64;
+        const uint64_t words = ((uint64_t)n_objects + 1) * wm + (uint64_t)n_attrs * wn + 2 * kScanBlocks + 2 * CNT_N;
+        if (words * 8 + 4 * 256 > (uint64_t)FCBO_STATIC_SCRATCH_BYTES / 2) return FCBO_ERR_SCRATCH;
+    }
+    fcbo_stats st;
+    memset(&st, 0, sizeof(st));
+    hipStream_t stream = (hipStream_t)hip_stream;
+    int rc = FCBO_OK;
+    try {
+        fcbo_context c;
+        CK(hipGetDevice(&c.device));
+        c.stream = stream;
+        c.fixed = true;
+        c.dmem.region = scratch_on_device(c.device);
+        c.dmem.region_size = FCBO_STATIC_SCRATCH_BYTES;
+        c.setup(rows, n_objects, n_attrs, row_stride_words, (flags & FCBO_ROWS_ON_DEVICE) != 0);
+        c.enumerate_levels();
+        if (n_concepts_out) *n_concepts_out = c.K;
+        if (!intents_out || capacity < c.K) {
+            rc = FCBO_ERR_CAPACITY;
+        } else {
+            c.order_concepts();
+            c.write_output(intents_out, extents_out, 0, c.K);
+        }
+        CK(hipStreamSynchronize(stream));
+        st.n_concepts = c.K;
+        st.closure_tests = c.tests;
+        st.item_pairs = c.pairs;
+        st.n_levels = c.lev.size();
+        st.model_bytes = c.model_bytes();
+        st.sum_child_objects = c.sum_c;
+        st.local_parents = c.local_parents;
+        st.local_parent_objects = c.local_objs;
+        st.medium_parents = c.med_parents;
+        st.medium_parent_objects = c.med_objs;
+        st.big_parents = c.big_parents;
+        st.big_tests = c.big_tests;
+        st.big_scanned_objects = c.big_scan;
+        st.big_nonzero_words = c.big_nzw;
+        st.big_child_objects = c.big_cobjs;
+        st.order_launches = c.order_launches;
+        if (rc == FCBO_OK)
+            st.output_bytes = c.K * (uint64_t)c.wm * 8 + (extents_out ? c.K * (uint64_t)c.wn * 8 : 0);
+    } catch (const HipError &e) {
+        (void)hipStreamSynchronize(stream);  // nothing of this call runs on after it returns
+        return e.code;
+    } catch (const std::bad_alloc &) {
+        (void)hipStreamSynchronize(stream);
+        return FCBO_ERR_OUT_OF_MEMORY;
+    }
     if (stats_out) *stats_out = st;
     return rc;
 }

@@ -51,8 +51,12 @@ enum {
     FCBO_ERR_OUT_OF_MEMORY = -2,    /* a device allocation failed or the memory limit was hit */
     FCBO_ERR_DEVICE = -3,           /* any other HIP runtime failure */
     FCBO_ERR_CAPACITY = -4,         /* output buffers hold fewer rows than concepts (or edges) */
-    FCBO_ERR_LIMIT = -5             /* 2^32 concepts or more: beyond the 32-bit concept indices */
+    FCBO_ERR_LIMIT = -5,            /* 2^32 concepts or more: beyond the 32-bit concept indices */
+    FCBO_ERR_SCRATCH = -6           /* fcbo_enumerate_static: the work does not fit the static scratch */
 };
+
+/* Bytes of the static device scratch of fcbo_enumerate_static (one per GPU). */
+#define FCBO_STATIC_SCRATCH_BYTES (64u << 20)
 
 /* fcbo_context_create flags */
 #define FCBO_ROWS_ON_DEVICE 1u /* rows is a device pointer (else host memory) */
@@ -246,6 +250,34 @@ int fcbo_level_counts(const fcbo_context *ctx, uint64_t *concepts_per_level,
  * FCBO_ERR_CAPACITY if capacity_words is too small.
  */
 int fcbo_copy_columns(const fcbo_context *ctx, uint64_t *host_cols, uint64_t capacity_words);
+
+/*
+ * For callers that cannot allocate device memory (tight serving loops,
+ * harnesses that forbid hipMalloc): the whole of fcbo_context_create +
+ * fcbo_enumerate + fcbo_destroy in one call that allocates nothing.  Every
+ * device buffer of the enumeration (rows, columns, concept store, level
+ * buffers, output order) is carved from a static device array of
+ * FCBO_STATIC_SCRATCH_BYTES (64 MiB), one per GPU, held until the process
+ * ends; no hipMalloc, hipFree, pinned host memory, event or stream is created,
+ * and the per-level wait synchronises the caller's stream.
+ *   rows ... row_stride_words, flags   as for fcbo_context_create (flags:
+ *                                      FCBO_ROWS_ON_DEVICE only)
+ *   hip_stream                         the stream the work runs on (NULL: the
+ *                                      null stream)
+ *   intents_out ... stats_out          as for fcbo_enumerate (stats without
+ *                                      times)
+ * Returns FCBO_ERR_SCRATCH if the context or its enumeration needs more than
+ * the scratch (up front when the rows and columns alone take more than half
+ * of it), FCBO_ERR_CAPACITY with K if the outputs are too small (nothing is
+ * kept: a second call enumerates again).  All calls on one GPU share its
+ * scratch: calls that overlap on one GPU (two host threads, or two streams
+ * not ordered with each other) race.  The scratch keeps the last call's
+ * contents; a call clears or writes everything it reads first.  Returns after
+ * the stream has finished.
+ */
+int fcbo_enumerate_static(const uint64_t *rows, int64_t n_objects, int64_t n_attrs, int64_t row_stride_words,
+                          uint32_t flags, void *hip_stream, uint64_t *intents_out, uint64_t *extents_out,
+                          uint64_t capacity, uint64_t *n_concepts_out, fcbo_stats *stats_out);
 
 /* Free the context and everything it owns.  NULL is allowed. */
 void fcbo_destroy(fcbo_context *ctx);

@@ -82,10 +82,12 @@ def test_stats_struct_matches_header():
 def test_error_codes_match_header():
     text = open(HEADER).read()
     for name in ("FCBO_OK", "FCBO_ERR_INVALID_ARGUMENT", "FCBO_ERR_OUT_OF_MEMORY", "FCBO_ERR_DEVICE",
-                 "FCBO_ERR_CAPACITY", "FCBO_ERR_LIMIT"):
+                 "FCBO_ERR_CAPACITY", "FCBO_ERR_LIMIT", "FCBO_ERR_SCRATCH"):
         v = int(re.search(r"\b%s = (-?\d+)" % name, text).group(1))
         assert getattr(fca, name) == v, name
     assert "32-bit" in fca.fcbo_error_string(fca.FCBO_ERR_LIMIT)
+    assert "static scratch" in fca.fcbo_error_string(fca.FCBO_ERR_SCRATCH)
+    assert "(64u << 20)" in text and fca.FCBO_STATIC_SCRATCH_BYTES == 64 << 20
 
 
 def test_null_arguments_are_rejected_without_a_device(lib):
@@ -102,4 +104,12 @@ def test_null_arguments_are_rejected_without_a_device(lib):
     assert lib.fcbo_write_range(None, ctypes.c_uint64(0), ctypes.c_uint64(0), None, None) == fca.FCBO_ERR_INVALID_ARGUMENT
     lib.fcbo_set_memory_limit.restype = ctypes.c_int
     assert lib.fcbo_set_memory_limit(None, ctypes.c_uint64(1)) == fca.FCBO_ERR_INVALID_ARGUMENT
+    lib.fcbo_enumerate_static.restype = ctypes.c_int
+    assert lib.fcbo_enumerate_static(None, ctypes.c_int64(10), ctypes.c_int64(10), ctypes.c_int64(1), 0, None,
+                                     None, None, ctypes.c_uint64(0), None, None) == fca.FCBO_ERR_INVALID_ARGUMENT
+    # a context whose rows and columns alone take more than half the scratch is
+    # refused before any device call (4,000,000 x 64: 32 MB of rows, 32 MB of columns)
+    assert lib.fcbo_enumerate_static(ctypes.c_void_p(8), ctypes.c_int64(4_000_000), ctypes.c_int64(64),
+                                     ctypes.c_int64(1), 1, None, None, None, ctypes.c_uint64(0), None,
+                                     None) == fca.FCBO_ERR_SCRATCH
     lib.fcbo_destroy(None)
