@@ -240,6 +240,97 @@ def rocprof_summary(paths):
         print()
 
 
+def _counter_rows(path):
+    import csv
+
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def rocprof_traffic(fetch_csv, write_csv, enumerations, output_launches, copy_gib):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of one bench process, scaled by
+    what they read for the plain copy (FETCH) and fill (WRITE) of `copy_gib` GiB run
+    first, per kernel per dispatch; plus the records bench.py reads: the output
+    kernels per launch, the level loop per enumeration."""
+    nbytes = copy_gib * (1 << 30)
+    per = {}
+    factors = {}
+    for which, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path)
+        calib = None
+        for r in rows:
+            name = r["Kernel_Name"]
+            if which == "FETCH_SIZE" and "copy" in name.lower() and calib is None:
+                calib = float(r["Counter_Value"]) * 1024
+            if which == "WRITE_SIZE" and "FillFunctor" in name and calib is None:
+                calib = float(r["Counter_Value"]) * 1024
+        factors[which] = nbytes / calib
+        for r in rows:
+            name = _short(r["Kernel_Name"])
+            if not name.startswith("fcbo::"):
+                continue
+            d = per.setdefault(name, {"FETCH_SIZE": [], "WRITE_SIZE": []})
+            d[which].append(float(r["Counter_Value"]) * 1024 * factors[which])
+    print("Calibration: the %g GiB copy reads %.3f x its bytes in FETCH_SIZE (factor %.3f); the %g GiB fill "
+          "writes %.3f x in WRITE_SIZE (factor %.3f).\n" % (copy_gib, 1 / factors["FETCH_SIZE"], factors["FETCH_SIZE"],
+                                                           copy_gib, 1 / factors["WRITE_SIZE"], factors["WRITE_SIZE"]))
+    print("| kernel | dispatches | fetch GB per dispatch | write GB per dispatch | fetch GB per step | write GB per step |")
+    print("|---|---:|---:|---:|---:|---:|")
+    loop_f = loop_w = 0.0
+    out_f = out_w = 0.0
+    for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1]["FETCH_SIZE"]) - sum(kv[1]["WRITE_SIZE"])):
+        n = max(len(d["FETCH_SIZE"]), 1)
+        f, w = sum(d["FETCH_SIZE"]), sum(d["WRITE_SIZE"])
+        base = name.split("::")[1].split("<")[0]
+        if base in ("k_output_block", "k_output_intents"):
+            out_f += f / output_launches
+            out_w += w / output_launches
+            steps = output_launches
+        else:
+            steps = enumerations
+            if base in LEVEL_LOOP_KERNELS:
+                loop_f += f / enumerations
+                loop_w += w / enumerations
+        print("| `%s` | %d | %.4f | %.4f | %.4f | %.4f |" % (name, n, f / n / 1e9, w / n / 1e9, f / steps / 1e9,
+                                                          w / steps / 1e9))
+    print()
+    return out_f, out_w, loop_f, loop_w
+
+
+def rocprof_sq(a_csv, b_csv, n_cu=256, ghz=2.4):
+    """VALU issue share, wait share and LDS bank conflicts per kernel from the two SQ passes."""
+    agg = {}
+    for path in (a_csv, b_csv):
+        for r in _counter_rows(path):
+            name = _short(r["Kernel_Name"])
+            if not name.startswith("fcbo::"):
+                continue
+            d = agg.setdefault(name, {"ns": {}, "c": {}})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            key = (path, r["Dispatch_Id"])
+            d["ns"][key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    print("| kernel | ms | VALU instr | VALU issue | LDS instr | VALU active | waiting | LDS bank conflict cycles |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|")
+    issue = {}
+    for name, d in sorted(agg.items(), key=lambda kv: -sum(v for (p, _), v in kv[1]["ns"].items() if p == a_csv)):
+        c = d["c"]
+        ms = sum(v for (p, _), v in d["ns"].items() if p == a_csv) / 1e6
+        valu = c.get("SQ_INSTS_VALU", 0.0)
+        frac = valu * 4 / (ms * 1e-3 * ghz * 1e9 * n_cu * 4) if ms else 0.0
+        cyc = c.get("SQ_WAVE_CYCLES", 0.0)
+        active = c.get("SQ_ACTIVE_INST_VALU", 0.0) / cyc if cyc else 0.0
+        wait = c.get("SQ_WAIT_ANY", 0.0) / cyc if cyc else 0.0
+        issue[name.split("::")[1]] = round(frac, 3)
+        print("| `%s` | %.3f | %.3g | %.2f | %.3g | %.2f | %.2f | %.3g |" % (
+            name, ms, valu, frac, c.get("SQ_INSTS_LDS", 0.0), active, wait, c.get("SQ_LDS_BANK_CONFLICT", 0.0)))
+    print()
+    return issue
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,9 +349,28 @@ def main():
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="run one device-to-device copy of this size first (counter calibration)")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="CSV")
+    ap.add_argument("--rocprof-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--rocprof-sq", nargs=2, metavar=("SQ_A_CSV", "SQ_B_CSV"))
+    ap.add_argument("--enumerations", type=int, default=3, help="enumerations in the profiled process")
+    ap.add_argument("--output-launches", type=int, default=2, help="output phases in the profiled process")
     args = ap.parse_args()
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
+        return
+    if args.rocprof_traffic or args.rocprof_sq:
+        sha = source_sha256()
+        issue = rocprof_sq(*args.rocprof_sq) if args.rocprof_sq else None
+        if args.rocprof_traffic:
+            of, ow, lf, lw = rocprof_traffic(*args.rocprof_traffic, args.enumerations, args.output_launches,
+                                             args.copy_probe_gib or 1.0)
+            print("```")
+            print("traffic-record: class=output kernel=k_output_intents+k_output_block source_sha256=%s "
+                  "fetch_bytes_per_launch=%d write_bytes_per_launch=%d" % (sha, of, ow))
+            loop_issue = {k: v for k, v in (issue or {}).items() if k.split("<")[0] in LEVEL_LOOP_KERNELS}
+            extra = " valu_issue=%s" % json.dumps(loop_issue, separators=(",", ":")) if loop_issue else ""
+            print("traffic-record: class=level_loop source_sha256=%s fetch_bytes_per_step=%d write_bytes_per_step=%d%s"
+                  % (sha, lf, lw, extra))
+            print("```")
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
