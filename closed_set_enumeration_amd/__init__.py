@@ -363,9 +363,10 @@ class Context:
 
     def cover_edges(self):
         """Lower covers of every concept of the last enumeration: (offsets int64 [K + 1],
-        targets int32 [E]) on the device, in output positions."""
+        targets int32 [E]) on the device, in output positions, and the device ms of the
+        counting and the writing call together."""
         torch = self._torch
-        rc, e, _ = fcbo_cover_edges(self.handle, 0, 0, 0)
+        rc, e, ms_count = fcbo_cover_edges(self.handle, 0, 0, 0)
         assert rc == FCBO_ERR_CAPACITY
         dev = torch.device("cuda", self.device)
         k = fcbo_level_counts(self.handle)[0].sum()
@@ -374,7 +375,7 @@ class Context:
         rc, e2, ms = fcbo_cover_edges(self.handle, offsets.data_ptr(), targets.data_ptr(), targets.shape[0])
         if rc != FCBO_OK or e2 != e:
             raise FcboError(rc, "fcbo_cover_edges")
-        return offsets, targets[:e], ms
+        return offsets, targets[:e], ms_count + ms
 
     def set_memory_limit(self, nbytes: int) -> None:
         fcbo_set_memory_limit(self.handle, nbytes)

@@ -218,12 +218,14 @@ struct fcbo_context {
     uint32_t *perm = nullptr;  // concept at every output position
 
     // cover edges
-    uint64_t cap_csorted = 0, cap_ccount = 0, cap_coff = 0, cap_cbig = 0, cap_cctr = 0;
-    uint64_t *csorted = nullptr;  // intents in output order
+    uint64_t cap_ctable = 0, cap_ccount = 0, cap_coff = 0, cap_cbig = 0, cap_cctr = 0;
+    uint32_t *ctable = nullptr;   // concept index by intent (open addressing)
     uint32_t *ccount = nullptr;   // covers per output position
     uint64_t *coff = nullptr;     // their exclusive scan
     uint32_t *cbig = nullptr;     // positions of the concepts with more than 64 objects
     uint64_t *cctr = nullptr;     // [0] their number, [1] covers not found
+    bool have_cover_counts = false;  // ccount / coff / cbig hold the last result's
+    uint64_t cover_total = 0;
 
     // result of the last enumeration
     bool have_result = false;
@@ -317,9 +319,9 @@ struct fcbo_context {
         huge.free_all(dmem);
         dfree(dmem, dt, cap_dt); dfree(dmem, tcnt, cap_tcnt); dfree(dmem, icnt, cap_icnt);
         dfree(dmem, rank, cap_rank); dfree(dmem, perm, cap_perm);
-        dfree(dmem, csorted, cap_csorted); dfree(dmem, ccount, cap_ccount); dfree(dmem, coff, cap_coff);
+        dfree(dmem, ctable, cap_ctable); dfree(dmem, ccount, cap_ccount); dfree(dmem, coff, cap_coff);
         dfree(dmem, cbig, cap_cbig); dfree(dmem, cctr, cap_cctr);
-        have_result = have_perm = false;
+        have_result = have_perm = have_cover_counts = false;
     }
 
     void free_all()
@@ -592,7 +594,7 @@ void fcbo_context::enumerate_levels()
     const uint64_t mc = min_cap();
     const bool bm = use_bitmaps();
     // nothing of an earlier result survives a failure part-way through
-    have_result = have_perm = false;
+    have_result = have_perm = have_cover_counts = false;
     K = 0;
     // root
     ensure(dmem, intents, cap_int, (uint64_t)wm * 1024, 0, stream, mc);
@@ -901,6 +903,12 @@ typedef void (*cover_fn)(const CoverArgs &, int, hipStream_t, int);
 template <int WMC>
 void launch_cover(const CoverArgs &C, int pass, hipStream_t s, int n_cu)
 {
+    if (pass == 0) {
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(16384, div_up(C.K, kBlock)));
+        hipLaunchKernelGGL(k_cover_table<WMC>, dim3(g), dim3(kBlock), 0, s, C);
+        CK_LAUNCH();
+        return;
+    }
     if constexpr (WMC <= 8) {
         const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(16384, div_up(C.K, kWavesPerBlock)));
         hipLaunchKernelGGL(k_cover_local<WMC>, dim3(g), dim3(kBlock), 0, s, C, pass);
@@ -930,38 +938,54 @@ cover_fn pick_cover_fn(int wm)
 
 }  // namespace
 
-// Lower covers of every concept (see k_cover_local): the sorted intents for
-// the searches, the large concepts listed, a counting pass, the scan, and (when
-// the caller's buffer holds all E edges) the writing pass.  Returns E.
+// Lower covers of every concept (see k_cover_local): the large concepts listed,
+// a counting pass, the scan, and (when the caller's buffer holds all E edges)
+// the table of concepts by intent and the writing pass.  Returns E.
 uint64_t fcbo_context::cover_edges(uint64_t *offsets_out, uint32_t *targets_out, uint64_t capacity)
 {
     if (!have_perm) order_concepts();
     const uint64_t mc = min_cap();
-    ensure(dmem, csorted, cap_csorted, K * (uint64_t)wm, 0, stream, mc);
-    ensure(dmem, ccount, cap_ccount, K, 0, stream, mc);
-    ensure(dmem, coff, cap_coff, K + 1, 0, stream, mc);
-    ensure(dmem, cbig, cap_cbig, K, 0, stream, mc);
-    ensure(dmem, cctr, cap_cctr, 2, 0, stream, 2);
-    hipLaunchKernelGGL(k_output_intents, dim3(kGridCap), dim3(kBlock), 0, stream, (const uint64_t *)intents,
-                       (const uint32_t *)perm, K, wm, csorted);
-    CK_LAUNCH();
-    clear_words(cctr, 2);
+    if (!have_cover_counts) {
+        ensure(dmem, ccount, cap_ccount, K, 0, stream, mc);
+        ensure(dmem, coff, cap_coff, K + 1, 0, stream, mc);
+        ensure(dmem, cbig, cap_cbig, K, 0, stream, mc);
+        ensure(dmem, cctr, cap_cctr, 2, 0, stream, 2);
+        clear_words(cctr, 2);
+    }
     CoverArgs C;
     memset(&C, 0, sizeof(C));
-    C.rows = rows; C.intents = intents; C.loff = loff; C.objs = objs; C.perm = perm; C.sorted = csorted;
+    C.rows = rows; C.intents = intents; C.cursor = cursor; C.fchild = fchild; C.rank = rank;
+    C.loff = loff; C.objs = objs; C.perm = perm;
     C.K = K; C.m = (int)m; C.wm = wm; C.tail_m = tail_m;
     C.small_max = wm <= 8 ? kSmallMax : -1;
     C.big = cbig; C.ctr = cctr; C.count = ccount; C.offsets = coff; C.targets = targets_out;
-    const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(4096, div_up(K, kBlock)));
-    hipLaunchKernelGGL(k_cover_list_big, dim3(gl), dim3(kBlock), 0, stream, C);
-    CK_LAUNCH();
     const cover_fn fn = pick_cover_fn(wm);
-    fn(C, 1, stream, n_cu);
-    scan(ccount, nullptr, nullptr, K, K, coff, nullptr, nullptr, nullptr);
-    uint64_t e = 0;
-    CK(hipMemcpyAsync(&e, coff + K, sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
-    CK(hipStreamSynchronize(stream));
+    if (!have_cover_counts) {
+        // counts kept until the next enumeration: a count call and the call
+        // that writes take one counting pass together
+        const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(4096, div_up(K, kBlock)));
+        hipLaunchKernelGGL(k_cover_list_big, dim3(gl), dim3(kBlock), 0, stream, C);
+        CK_LAUNCH();
+        fn(C, 1, stream, n_cu);
+        scan(ccount, nullptr, nullptr, K, K, coff, nullptr, nullptr, nullptr);
+        CK(hipMemcpyAsync(&cover_total, coff + K, sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+        CK(hipStreamSynchronize(stream));
+        have_cover_counts = true;
+    }
+    const uint64_t e = cover_total;
     if (!offsets_out || !targets_out || capacity < e) return e;
+    clear_words(cctr + 1, 1);
+    uint64_t slots = 1024;
+    while (slots < 2 * K) slots *= 2;
+    ensure(dmem, ctable, cap_ctable, slots, 0, stream, mc);
+    {
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(16384, div_up(slots, kBlock)));
+        hipLaunchKernelGGL(k_fill_u64, dim3(g), dim3(kBlock), 0, stream, (uint64_t *)ctable, slots / 2, ~0ull);
+        CK_LAUNCH();
+    }
+    C.table = ctable;
+    C.table_mask = slots - 1;
+    fn(C, 0, stream, n_cu);
     fn(C, 2, stream, n_cu);
     CK(hipMemcpyAsync(offsets_out, coff, (K + 1) * sizeof(uint64_t), hipMemcpyDeviceToDevice, stream));
     uint64_t missing = 0;

@@ -2263,33 +2263,43 @@ namespace fcbo {
 // ascending, at [offsets[i], offsets[i + 1]).  Two passes over the concepts:
 // counting, then (after a scan) writing.
 
-// Position of the intent d (wm words) in the sorted intents, or 0xFFFFFFFF.
-__device__ __forceinline__ uint32_t find_intent(const uint64_t *__restrict__ sorted, uint64_t K, int wm,
-                                                const uint64_t *d)
+// Concepts are located by intent through an open-addressing hash table (linear
+// probing, at most half full) of concept indices.  The hash folds the intent
+// words with multiply-xorshift steps and finishes with the 64-bit finalizer of
+// MurmurHash3 (Appleby).
+constexpr uint32_t kCoverEmpty = 0xFFFFFFFFu;
+
+template <int WMC>
+__device__ __forceinline__ uint64_t intent_slot_hash(const uint64_t (&d)[WMC], int wm)
 {
-    uint64_t lo = 0, hi = K;
-    while (lo < hi) {
-        const uint64_t mid = lo + (hi - lo) / 2;
-        const uint64_t *x = sorted + mid * wm;
-        int c = 0;
-        for (int u = 0; u < wm && c == 0; ++u) {
-            const uint64_t diff = x[u] ^ d[u];
-            if (diff) c = ((x[u] >> (__ffsll((unsigned long long)diff) - 1)) & 1ull) ? 1 : -1;
+    uint64_t h = 0x2545F4914F6CDD1Dull;
+#pragma unroll
+    for (int u = 0; u < WMC; ++u) {
+        if (u < wm) {
+            h ^= d[u];
+            h *= 0xFF51AFD7ED558CCDull;
+            h ^= h >> 32;
         }
-        if (c == 0) return (uint32_t)mid;
-        if (c < 0) lo = mid + 1;
-        else hi = mid;
     }
-    return 0xFFFFFFFFu;
+    h ^= h >> 33;
+    h *= 0xFF51AFD7ED558CCDull;
+    h ^= h >> 33;
+    h *= 0xC4CEB9FE1A85EC53ull;
+    h ^= h >> 33;
+    return h;
 }
 
 struct CoverArgs {
     const uint64_t *rows;     // N x wm
     const uint64_t *intents;  // generation order
+    const int32_t *cursor;    // generation order
+    const uint32_t *fchild;   // first child of every concept (children contiguous, ascending cursor)
+    const uint32_t *rank;     // output position of every concept but the root
     const uint64_t *loff;
     const uint32_t *objs;
     const uint32_t *perm;     // output position -> concept
-    const uint64_t *sorted;   // K x wm intents in output order
+    uint32_t *table;          // concept index by intent (open addressing), kCoverEmpty when free
+    uint64_t table_mask;      // slots - 1 (a power of two, at least 2K slots)
     uint64_t K;
     int m, wm;
     int64_t small_max;        // concepts with at most this many objects take the wavefront kernel
@@ -2300,6 +2310,25 @@ struct CoverArgs {
     const uint64_t *offsets;  // pass 2: their exclusive scan
     uint32_t *targets;        // pass 2: output positions of the covers
 };
+
+// Every concept into the table, keyed by its intent.
+template <int WMC>
+__global__ void __launch_bounds__(kBlock) k_cover_table(CoverArgs C)
+{
+    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < C.K; c += (uint64_t)gridDim.x * blockDim.x) {
+        constexpr int DW = WMC <= 8 ? WMC : 64;
+        uint64_t d[DW];
+#pragma unroll
+        for (int u = 0; u < DW; ++u) d[u] = u < C.wm ? C.intents[c * C.wm + u] : 0ull;
+        uint64_t h = intent_slot_hash<DW>(d, C.wm) & C.table_mask;
+        // the table has at least twice as many slots as concepts: a free slot is
+        // reached within K probes
+        for (uint64_t probe = 0; probe <= C.K; ++probe) {
+            if (atomicCAS(&C.table[h], kCoverEmpty, (uint32_t)c) == kCoverEmpty) break;
+            h = (h + 1) & C.table_mask;
+        }
+    }
+}
 
 // The output positions whose concept has more than small_max objects.
 __global__ void __launch_bounds__(kBlock) k_cover_list_big(CoverArgs C)
@@ -2316,9 +2345,43 @@ __global__ void __launch_bounds__(kBlock) k_cover_list_big(CoverArgs C)
     }
 }
 
+// Output position of the lower cover D (wm words) of concept c, emitted by n.
+// When n lies above c's cursor, D is c's CbO child made at n (it passes the
+// canonical test: D agrees with B below n), already placed by the order pass;
+// otherwise the table gives the concept with intent D.
+template <int WMC>
+__device__ __forceinline__ uint32_t cover_position(const CoverArgs &C, uint64_t c, int n, const uint64_t (&D)[WMC])
+{
+    if (n > C.cursor[c]) {
+        uint32_t lo = C.fchild[c], hi = C.fchild[c + 1];
+        while (lo < hi) {
+            const uint32_t mid = lo + (hi - lo) / 2;
+            const int cm = C.cursor[mid];
+            if (cm == n) return C.rank[mid];
+            if (cm < n) lo = mid + 1;
+            else hi = mid;
+        }
+    }
+    uint64_t h = intent_slot_hash<WMC>(D, C.wm) & C.table_mask;
+    for (uint64_t probe = 0; probe <= C.K; ++probe) {
+        const uint32_t e = C.table[h];
+        if (e == kCoverEmpty) break;
+        bool same = true;
+#pragma unroll
+        for (int u = 0; u < WMC; ++u)
+            if (u < C.wm) same = same && C.intents[(uint64_t)e * C.wm + u] == D[u];
+        if (same) return e == 0 ? 0u : C.rank[e];
+        h = (h + 1) & C.table_mask;
+    }
+    atomicAdd((unsigned long long *)&C.ctr[1], 1ull);  // not a concept: cannot happen
+    return kCoverEmpty;
+}
+
 // Concepts with at most 64 objects, one wavefront each.  The object rows are
-// staged in LDS; for every intent word u, 64 ballots turn the rows around so
-// that lane b holds c_{64u+b} as a mask over the concept's objects.
+// staged in LDS; lane b builds, for every intent word u, the mask of the
+// objects having attribute 64u + b from broadcast reads of the staged rows.
+// When no object carries an attribute outside B the one lower cover is the
+// bottom (for every concept but the bottom itself).
 template <int WMC>
 __global__ void __launch_bounds__(kBlock) k_cover_local(CoverArgs C, int pass)
 {
@@ -2332,102 +2395,126 @@ __global__ void __launch_bounds__(kBlock) k_cover_local(CoverArgs C, int pass)
     uint8_t *CN = s_cnt[wv];
     for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + wv; i < C.K; i += (uint64_t)gridDim.x * kWavesPerBlock) {
         const uint64_t c = C.perm[i];
-        const uint64_t o0 = C.loff[c], a = C.loff[c + 1] - o0;
-        if ((int64_t)a > C.small_max) continue;  // the workgroup kernel's
+        const uint64_t o0 = C.loff[c], a64 = C.loff[c + 1] - o0;
+        if ((int64_t)a64 > C.small_max) continue;  // the workgroup kernel's
+        const int a = (int)a64;
         uint64_t B[WMC];
+        bool full = true;  // B = M: the bottom, no lower cover
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
             B[u] = ~0ull;
             if (u < wm) {
                 B[u] = C.intents[c * C.wm + u];
                 if (u == wm - 1) B[u] |= ~C.tail_m;  // attributes past M count as in B
+                full = full && B[u] == ~0ull;
             }
         }
-        uint64_t row[WMC];
-        const bool mine = (uint64_t)lane < a;
+        const bool mine = lane < a;
         const uint64_t g = mine ? C.objs[o0 + lane] : 0;
+        uint64_t cand[WMC];  // attributes outside B carried by some object
+        uint64_t any = 0;
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
-            row[u] = (mine && u < wm) ? C.rows[g * C.wm + u] : 0ull;
-            R[lane * WMC + u] = row[u];
+            const uint64_t r = (mine && u < wm) ? C.rows[g * C.wm + u] : 0ull;
+            R[lane * WMC + u] = r;
+            cand[u] = (u < wm) ? (wave_or(r) & ~B[u]) : 0ull;
+            any |= cand[u];
         }
-        // lane b: cm[u] = the objects having attribute 64u + b; counts to LDS
-        uint64_t cm[WMC];
-        uint64_t carried = 0;  // some attribute outside B is carried by an object
+        uint32_t ncov = 0;
+        if (!any) {
+            // every attribute outside B gives the bottom
+            ncov = full ? 0u : 1u;
+            if (pass == 2 && ncov && lane == 0) C.targets[C.offsets[i]] = (uint32_t)(C.K - 1);
+        } else {
+            wave_sync();
+            // lane b: cm[u] = the objects having attribute 64u + b; counts to LDS
+            uint64_t cm[WMC];
 #pragma unroll
-        for (int u = 0; u < WMC; ++u) {
-            cm[u] = 0;
-            if (u < wm) {
-                for (int b = 0; b < 64; ++b) {
-                    const uint64_t bal = __ballot((row[u] >> b) & 1ull);
-                    if (lane == b) cm[u] = bal;
-                }
-                CN[u * 64 + lane] = (uint8_t)__popcll(cm[u]);
-                carried |= __ballot(!((B[u] >> lane) & 1ull) && cm[u] != 0);
+            for (int u = 0; u < WMC; ++u) cm[u] = 0;
+            for (int o = 0; o < a; ++o) {
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm && cand[u]) cm[u] |= ((R[o * WMC + u] >> lane) & 1ull) << o;
             }
-        }
-        wave_sync();
-        uint32_t base = 0;  // covers of larger emitters, placed before
 #pragma unroll
-        for (int u = WMC - 1; u >= 0; --u) {
-            if (u >= wm) continue;
-            // candidates: attributes outside B, the uncarried ones only when no
-            // attribute is carried (then every one gives the bottom)
-            bool cand = !((B[u] >> lane) & 1ull) && (cm[u] != 0 || carried == 0);
-            uint64_t D[WMC];
+            for (int u = 0; u < WMC; ++u)
+                if (u < wm) CN[u * 64 + lane] = (uint8_t)__popcll(cm[u]);
+            wave_sync();
 #pragma unroll
-            for (int v = 0; v < WMC; ++v) D[v] = ~0ull;
-            if (cand) {
-                uint64_t mm = cm[u];
-                while (mm) {
-                    const int o = __ffsll((unsigned long long)mm) - 1;
-                    mm &= mm - 1ull;
+            for (int u = WMC - 1; u >= 0; --u) {
+                if (u >= wm || !cand[u]) continue;
+                bool is_cover = (cand[u] >> lane) & 1ull;
+                uint64_t D[WMC];
 #pragma unroll
-                    for (int v = 0; v < WMC; ++v)
-                        if (v < wm) D[v] &= R[o * WMC + v];
-                }
-                D[wm - 1] &= C.tail_m;
-                // emitted by its first attribute outside B; a cover when every
-                // attribute outside B has n's object count
-                const int cnt_n = __popcll(cm[u]);
-                bool first = true;
+                for (int v = 0; v < WMC; ++v) D[v] = ~0ull;
+                if (is_cover) {
+                    uint64_t mm = cm[u];
+                    while (mm) {
+                        const int o = __ffsll((unsigned long long)mm) - 1;
+                        mm &= mm - 1ull;
 #pragma unroll
-                for (int v = 0; v < WMC; ++v) {
-                    if (v >= wm) continue;
-                    uint64_t x = D[v] & ~B[v];
-                    if (first && x) {
-                        if (v != u || (__ffsll((unsigned long long)x) - 1) != lane) cand = false;
-                        first = false;
+                        for (int v = 0; v < WMC; ++v)
+                            if (v < wm) D[v] &= R[o * WMC + v];
                     }
-                    while (x && cand) {
-                        const int k = __ffsll((unsigned long long)x) - 1;
-                        x &= x - 1ull;
-                        if ((int)CN[v * 64 + k] != cnt_n) cand = false;
+                    D[wm - 1] &= C.tail_m;
+                    // emitted by its first attribute outside B; a cover when every
+                    // attribute outside B has the object count of n = 64u + lane
+                    const int cnt_n = __popcll(cm[u]);
+                    bool first = true;
+#pragma unroll
+                    for (int v = 0; v < WMC; ++v) {
+                        if (v >= wm) continue;
+                        uint64_t x = D[v] & ~B[v];
+                        if (first && x) {
+                            if (v != u || (__ffsll((unsigned long long)x) - 1) != lane) is_cover = false;
+                            first = false;
+                        }
+                        while (x && is_cover) {
+                            const int k = __ffsll((unsigned long long)x) - 1;
+                            x &= x - 1ull;
+                            if ((int)CN[v * 64 + k] != cnt_n) is_cover = false;
+                        }
                     }
                 }
+                const uint64_t emit = __ballot(is_cover);
+                if (pass == 2 && is_cover) {
+                    const uint32_t pos = cover_position<WMC>(C, c, 64 * u + lane, D);
+                    C.targets[C.offsets[i] + ncov + (uint32_t)__popcll(emit & ~upto_mask(lane))] = pos;
+                }
+                ncov += (uint32_t)__popcll(emit);
             }
-            const uint64_t emit = __ballot(cand);
-            if (pass == 2 && cand) {
-                const uint32_t pos = find_intent(C.sorted, C.K, wm, D);
-                if (pos == 0xFFFFFFFFu) atomicAdd((unsigned long long *)&C.ctr[1], 1ull);
-                C.targets[C.offsets[i] + base + (uint32_t)__popcll(emit & ~upto_mask(lane))] = pos;
-            }
-            base += (uint32_t)__popcll(emit);
         }
-        if (pass == 1 && lane == 0) C.count[i] = base;
+        if (pass == 1 && lane == 0) C.count[i] = ncov;
         wave_sync();
     }
 }
 
 // Concepts with more objects, one workgroup each (from the list): object
-// counts of all attributes by incidence (LDS atomics); then the carried
-// candidates in slices of kCoverSlice, each slice's D_n accumulated in one pass
-// over the extent list (LDS AND atomics) and tested one per thread.  The
-// covers' positions go to an LDS table indexed by emitter and leave in
-// descending emitter order.
+// counts of all attributes by incidence (LDS atomics); the carried candidates
+// listed in ascending order; then slices of kCoverSlice of them, each slice's
+// D_n accumulated in one pass over the extent list (LDS AND atomics) and tested
+// one per thread.  The covers' positions go to an LDS table indexed by emitter
+// and leave in descending emitter order.
 constexpr int kCoverThreads = 256;
 constexpr int kCoverSlice = 64;
 constexpr int kCoverMaxM = 4096;
+
+// Exclusive scan over a kCoverThreads-thread workgroup; returns the total.
+__device__ __forceinline__ uint32_t cover_block_scan(uint32_t v, uint32_t &excl, uint32_t *s_sum)
+{
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    const uint32_t ex = wave_excl_scan(v);
+    if (lane == kWave - 1) s_sum[wv] = ex + v;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (int w = 0; w < kCoverThreads / kWave; ++w) {
+        before += w < wv ? s_sum[w] : 0u;
+        all += s_sum[w];
+    }
+    __syncthreads();
+    excl = before + ex;
+    return all;
+}
 
 template <int WMC>
 __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pass)
@@ -2435,13 +2522,14 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
     constexpr int WS = WMC <= 8 ? WMC : 64;  // words of a D entry kept in LDS
     __shared__ uint32_t s_cnt[kCoverMaxM];   // |c_n|
     __shared__ uint32_t s_pos[kCoverMaxM];   // position of the cover emitted by n, else ~0
+    __shared__ uint16_t s_cand[kCoverMaxM];  // the carried candidates, ascending
     __shared__ int16_t s_slot[kCoverMaxM];   // slot of n in the current slice, else -1
     __shared__ uint64_t s_d[kCoverSlice * WS];
     __shared__ uint64_t s_mask[WS];          // the current slice's attributes
     __shared__ uint32_t s_sum[kCoverThreads / kWave];
-    __shared__ uint32_t s_nc, s_slice[kCoverSlice];
-    const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+    const int tid = threadIdx.x;
     const int wm = words_of<WMC>(C.wm);
+    const int per = (C.m + kCoverThreads - 1) / kCoverThreads;  // attributes per thread, in blocks
     const uint64_t nbig = C.ctr[0];
     for (uint64_t it = blockIdx.x; it < nbig; it += gridDim.x) {
         const uint64_t i = C.big[it];
@@ -2467,50 +2555,32 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
             }
         }
         __syncthreads();
-        uint32_t carried = 0;
-        for (int n = tid; n < C.m; n += kCoverThreads) carried += (!in_b(n) && s_cnt[n]) ? 1u : 0u;
-        carried = wave_sum(carried);
-        if (lane == 0) s_sum[wv] = carried;
-        __syncthreads();
-        uint32_t total = 0;
-        for (int w = 0; w < kCoverThreads / kWave; ++w) total += s_sum[w];
-        __syncthreads();
+        // the carried candidates in ascending order: thread t lists the block of
+        // attributes [t * per, (t + 1) * per)
+        const int lo_a = tid * per, hi_a = lo_a + per < C.m ? lo_a + per : C.m;
+        uint32_t mine = 0;
+        for (int n = lo_a; n < hi_a; ++n) mine += (!in_b(n) && s_cnt[n]) ? 1u : 0u;
+        uint32_t at;
+        const uint32_t ncand = cover_block_scan(mine, at, s_sum);
+        for (int n = lo_a; n < hi_a; ++n)
+            if (!in_b(n) && s_cnt[n]) s_cand[at++] = (uint16_t)n;
         uint32_t found = 0;
-        if (total == 0) {
-            // nothing outside B is carried: every attribute outside B gives the
-            // bottom, emitted by the first of them (none: this is the bottom)
-            if (tid == 0) {
-                int j0 = -1;
-                for (int n = 0; n < C.m && j0 < 0; ++n)
-                    if (!in_b(n)) j0 = n;
-                if (j0 >= 0) {
-                    found = 1;
-                    if (pass == 2) {
-                        uint64_t d[WS];
-                        for (int v = 0; v < wm; ++v) d[v] = (v == wm - 1) ? C.tail_m : ~0ull;
-                        const uint32_t pos = find_intent(C.sorted, C.K, wm, d);
-                        if (pos == 0xFFFFFFFFu) atomicAdd((unsigned long long *)&C.ctr[1], 1ull);
-                        C.targets[C.offsets[i]] = pos;
-                    }
-                }
-            }
+        if (ncand == 0) {
+            // nothing outside B is carried: the bottom is the one lower cover
+            // (none when B is already every attribute)
+            bool full = true;
+            for (int u = 0; u < wm; ++u) full = full && (Bp[u] == (u == wm - 1 ? C.tail_m : ~0ull));
+            found = full ? 0u : 1u;
+            if (pass == 2 && found && tid == 0) C.targets[C.offsets[i]] = (uint32_t)(C.K - 1);
         } else {
-            int next = 0;  // first attribute not yet sliced
-            while (true) {
-                if (tid == 0) {
-                    uint32_t nc = 0;
-                    for (int n = next; n < C.m && nc < (uint32_t)kCoverSlice; ++n)
-                        if (!in_b(n) && s_cnt[n]) s_slice[nc++] = (uint32_t)n;
-                    s_nc = nc;
-                }
+            __syncthreads();
+            for (uint32_t s0 = 0; s0 < ncand; s0 += kCoverSlice) {
+                const uint32_t nc = ncand - s0 < (uint32_t)kCoverSlice ? ncand - s0 : (uint32_t)kCoverSlice;
                 if (tid < WS) s_mask[tid] = 0;
-                __syncthreads();
-                const uint32_t nc = s_nc;
-                if (nc == 0) break;
-                next = (int)s_slice[nc - 1] + 1;
                 for (uint32_t x = tid; x < nc * WS; x += kCoverThreads) s_d[x] = ~0ull;
+                __syncthreads();
                 if ((uint32_t)tid < nc) {
-                    const uint32_t n = s_slice[tid];
+                    const uint32_t n = s_cand[s0 + tid];
                     s_slot[n] = (int16_t)tid;
                     atomicOr((unsigned long long *)&s_mask[n >> 6], (unsigned long long)(1ull << (n & 63)));
                 }
@@ -2529,7 +2599,7 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
                 }
                 __syncthreads();
                 if ((uint32_t)tid < nc) {
-                    const int n = (int)s_slice[tid];
+                    const int n = (int)s_cand[s0 + tid];
                     const uint64_t *D = s_d + tid * WS;
                     const uint32_t cnt_n = s_cnt[n];
                     bool ok = true, first = true;
@@ -2551,8 +2621,7 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
                         if (pass == 2) {
                             uint64_t d[WS];
                             for (int v = 0; v < wm; ++v) d[v] = (v == wm - 1) ? (D[v] & C.tail_m) : D[v];
-                            pos = find_intent(C.sorted, C.K, wm, d);
-                            if (pos == 0xFFFFFFFFu) atomicAdd((unsigned long long *)&C.ctr[1], 1ull);
+                            pos = cover_position<WS>(C, c, n, d);
                         }
                         s_pos[n] = pos;
                     }
@@ -2560,26 +2629,18 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
                 }
                 __syncthreads();
             }
-            // covers in descending emitter order: thread t takes a block of
-            // attributes from the top down
-            const int per = (C.m + kCoverThreads - 1) / kCoverThreads;
+            // covers in descending emitter order: thread t takes the t-th block
+            // of attributes from the top down
             const int hi = C.m - tid * per, lo = hi - per > 0 ? hi - per : 0;
-            uint32_t mine = 0;
-            for (int n = hi - 1; n >= lo; --n) mine += s_pos[n] != 0xFFFFFFFFu ? 1u : 0u;
-            const uint32_t ex = wave_excl_scan(mine);
-            if (lane == kWave - 1) s_sum[wv] = ex + mine;
-            __syncthreads();
-            uint32_t before = 0, all = 0;
-            for (int w = 0; w < kCoverThreads / kWave; ++w) {
-                before += w < wv ? s_sum[w] : 0u;
-                all += s_sum[w];
-            }
+            uint32_t nmine = 0;
+            for (int n = hi - 1; n >= lo; --n) nmine += s_pos[n] != 0xFFFFFFFFu ? 1u : 0u;
+            uint32_t before;
+            found = cover_block_scan(nmine, before, s_sum);
             if (pass == 2) {
-                uint64_t at = C.offsets[i] + before + ex;
+                uint64_t w = C.offsets[i] + before;
                 for (int n = hi - 1; n >= lo; --n)
-                    if (s_pos[n] != 0xFFFFFFFFu) C.targets[at++] = s_pos[n];
+                    if (s_pos[n] != 0xFFFFFFFFu) C.targets[w++] = s_pos[n];
             }
-            found = all;
         }
         if (pass == 1 && tid == 0) C.count[i] = found;
         __syncthreads();
