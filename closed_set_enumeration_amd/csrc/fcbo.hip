@@ -307,6 +307,19 @@ struct fcbo_context {
     bool use_bitmaps() const { return wn <= kBmpMaxWords; }
     int nchunk() const { return (int)div_up((uint64_t)wn, kWave); }
 
+    // the per-level scratch of the level loop (the concept store and the
+    // output order stay): released where later work needs the memory, grown
+    // again by the next enumeration
+    void free_level_scratch()
+    {
+        dfree(dmem, pass, cap_pass); dfree(dmem, cbase, cap_cb); dfree(dmem, obase, cap_ob);
+        dfree(dmem, nchild, cap_nch); dfree(dmem, nobj, cap_nob); dfree(dmem, mid_idx, cap_mid);
+        dfree(dmem, mrec, cap_mrec); dfree(dmem, wrec, cap_wrec); dfree(dmem, lrec, cap_lrec);
+        dfree(dmem, lfill, cap_lfill);
+        huge.free_all(dmem);
+        dfree(dmem, dt, cap_dt); dfree(dmem, tcnt, cap_tcnt); dfree(dmem, icnt, cap_icnt);
+    }
+
     // the enumeration's buffers (the context's rows, columns and counters stay)
     void free_buffers()
     {
@@ -380,7 +393,7 @@ struct fcbo_context {
         A.counters = counters + (uint64_t)ctr * CNT_N;
         A.counters_next = counters + (uint64_t)(1 - ctr) * CNT_N;
         A.child_cap = std::min(std::min(cap_int / (uint64_t)wm, cap_cur), cap_loff ? cap_loff - 1 : 0);
-        A.obj_cap = cap_o;
+        A.obj_cap = cap_o > kObjSlack ? cap_o - kObjSlack : 0;  // the output kernel reads past the last list
         return A;
     }
 
@@ -600,7 +613,7 @@ void fcbo_context::enumerate_levels()
     ensure(dmem, intents, cap_int, (uint64_t)wm * 1024, 0, stream, mc);
     ensure(dmem, cursor, cap_cur, 1024, 0, stream, mc);
     ensure(dmem, loff, cap_loff, 1025, 0, stream, mc);
-    ensure(dmem, objs, cap_o, (uint64_t)n, 0, stream, mc);
+    ensure(dmem, objs, cap_o, (uint64_t)n + kObjSlack, 0, stream, mc);
     {
         uint64_t t = std::max<uint64_t>((uint64_t)n, (uint64_t)wm);
         hipLaunchKernelGGL(k_root_init, dim3((unsigned)div_up(t, kBlock)), dim3(kBlock), 0, stream, intents, cursor,
@@ -732,7 +745,7 @@ void fcbo_context::enumerate_levels()
             ensure(dmem, intents, cap_int, k_end * wm, keep_k * wm, stream, mc);
             ensure(dmem, cursor, cap_cur, k_end, keep_k, stream, mc);
             ensure(dmem, loff, cap_loff, k_end + 1, keep_k + 1, stream, mc);
-            ensure(dmem, objs, cap_o, obj_hi + n_objs, obj_hi, stream, mc);
+            ensure(dmem, objs, cap_o, obj_hi + n_objs + kObjSlack, obj_hi, stream, mc);
             ensure(dmem, fchild, cap_fch, k_end + 1, keep_k + 1, stream, mc);
             if (n_children && !had_room) fns.writes(this, level_args(lo, P, obj_hi), P, classes, 0);
         } while (redo);
@@ -944,6 +957,8 @@ cover_fn pick_cover_fn(int wm)
 uint64_t fcbo_context::cover_edges(uint64_t *offsets_out, uint32_t *targets_out, uint64_t capacity)
 {
     if (!have_perm) order_concepts();
+    CK(hipStreamSynchronize(stream));
+    free_level_scratch();  // the cover buffers of 10^9 concepts need that room
     const uint64_t mc = min_cap();
     if (!have_cover_counts) {
         ensure(dmem, ccount, cap_ccount, K, 0, stream, mc);

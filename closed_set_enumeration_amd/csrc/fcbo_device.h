@@ -2162,16 +2162,38 @@ constexpr int kOutThreads = 512;
 constexpr int kOutWaves = kOutThreads / kWave;
 constexpr int kOutLineWords = 128 / 8;
 
+// Entries of slack after the last extent list, so that the output kernel can
+// read object ids sixteen at a time past a list's end.
+constexpr uint64_t kObjSlack = 16;
+
+// Workgroup barrier for LDS only: the waves' LDS operations are done and
+// visible after it, while their global stores stay in flight (a full barrier
+// waits for those too).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // k_output_block: one workgroup writes R consecutive output rows.  Their extent
 // bitmaps are assembled together in one dynamic LDS tile of R*wn words (the
 // object lists OR-ed in with LDS atomics), then the tile goes out as a single
 // contiguous region of the extent array: each wavefront stores 1 KiB runs, so
 // when R*wn*8 is a multiple of 128 bytes every store covers whole, aligned cache
 // lines.  The tile is cleared as it is read.  The intent rows are written by
-// k_output_intents (copying them here put a gather on every block's path: 0.13
-// ms of 5.9 on ctx50000x400).  The grid is persistent: a workgroup walks blocks
-// with the grid stride and loads the next block's row sources (permutation
-// entry and list bounds, one row per lane) while it streams the current one.
+// k_output_intents.  The grid is persistent: a workgroup walks blocks with the
+// grid stride.
+//
+// The stores of one block and the assembly of the next overlap: gfx950 counts
+// vector loads and stores on one in-order counter, so a vector load issued
+// after a block's stores can only be waited for once those stores are done.
+// The row sources (permutation entry, list bounds) and lists of up to 256
+// objects are therefore read with scalar loads (a counter of their own, the
+// ids sixteen at a time, uniform per wavefront), and the barriers wait for LDS
+// work only.  Longer lists (a few large extents) use vector loads.
+constexpr int kOutScalarList = 256;
+
 __global__ void __launch_bounds__(kOutThreads) k_output_block(const uint64_t *__restrict__ loff,
                                                           const uint32_t *__restrict__ objs,
                                                           const uint32_t *__restrict__ perm, uint64_t K, int wn,
@@ -2185,32 +2207,33 @@ __global__ void __launch_bounds__(kOutThreads) k_output_block(const uint64_t *__
     // stores of two words at a time need a 16-byte aligned region start
     const bool pairs = ((reinterpret_cast<uintptr_t>(extents_out) & 15) == 0) && (words & 1) == 0;
     const uint64_t nblk = (K + R - 1) / R;
-    uint64_t src = 0, lo = 0, hi = 0;  // this lane's row in the block being fetched
-    auto fetch = [&](uint64_t blk) {
-        const uint64_t r = blk * (uint64_t)R + lane;
-        src = lo = hi = 0;
-        if (blk < nblk && lane < R && r < K) {
-            src = perm[r];
-            lo = loff[src];
-            hi = loff[src + 1];
-        }
-    };
-    uint64_t b = blockIdx.x;
-    fetch(b);
-    __syncthreads();
-    for (; b < nblk; b += gridDim.x) {
+    lds_barrier();
+    for (uint64_t b = blockIdx.x; b < nblk; b += gridDim.x) {
         const uint64_t r0 = b * (uint64_t)R;
         const int nr = (int)((K - r0) < (uint64_t)R ? (K - r0) : (uint64_t)R);
         for (int rr = wv; rr < nr; rr += kOutWaves) {
-            const uint64_t o = lane_value64(lo, rr), e = lane_value64(hi, rr);
+            const uint32_t src = perm[r0 + rr];
+            const uint64_t o = loff[src], e = loff[src + 1];
             uint64_t *T = s_rows + rr * wn;
-            for (uint64_t p = o + lane; p < e; p += kWave) {
-                const uint32_t g = objs[p];
-                atomicOr((unsigned long long *)&T[g >> 6], (unsigned long long)(1ull << (g & 63)));
+            if (e - o <= (uint64_t)kOutScalarList) {
+                for (uint64_t p = o; p < e; p += 16) {
+                    uint32_t v[16];
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) v[k] = objs[p + k];  // kObjSlack entries follow the last list
+                    uint32_t g = 0;
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) g = lane == k ? v[k] : g;
+                    if (lane < 16 && (uint64_t)lane < e - p)
+                        atomicOr((unsigned long long *)&T[g >> 6], (unsigned long long)(1ull << (g & 63)));
+                }
+            } else {
+                for (uint64_t p = o + lane; p < e; p += kWave) {
+                    const uint32_t g = objs[p];
+                    atomicOr((unsigned long long *)&T[g >> 6], (unsigned long long)(1ull << (g & 63)));
+                }
             }
         }
-        __syncthreads();
-        fetch(b + gridDim.x);
+        lds_barrier();
         const uint64_t base = r0 * (uint64_t)wn;
         const int cnt = nr * wn;
         if (pairs) {
@@ -2233,7 +2256,7 @@ __global__ void __launch_bounds__(kOutThreads) k_output_block(const uint64_t *__
                 __builtin_nontemporal_store(v, &extents_out[base + e]);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
