@@ -20,6 +20,9 @@ Prints one JSON line.  `value` is concepts per second; beside it:
     achievable bandwidth on this box;
   * `cover_edges`: the lattice's cover edges of the same result
     (fcbo_cover_edges), timed once after the steps;
+  * `host_stream`: the first rows of the ordered output streamed to pinned
+    host memory through two device staging buffers (fcbo_copy_to_host), a
+    PCIe-inclusive rate, never the headline value;
   * `cpu_baseline`: the store-free CPU oracle over the whole workload on one
     pinned host core, run before the GPU is touched; `cpu_baseline_all_cores`
     the same search split over the host cores.
@@ -341,6 +344,8 @@ def main():
                     help="write the extent bitmaps (auto: when K x N/8 bytes fit in a third of device memory)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-cover", action="store_true", help="skip the cover-edge measurement")
+    ap.add_argument("--host-stream-rows", type=int, default=1 << 20,
+                    help="rows of the ordered output streamed to pinned host memory after the steps (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="threads of the all-core CPU baseline (0: the "
                     "process's cores, at most 16)")
     ap.add_argument("--cpu-bitmap-tests", type=int, default=2_000_000,
@@ -478,6 +483,21 @@ def main():
     if closure_roof["traffic"]:
         closure_roof["traffic_over_model"] = round(closure_roof["traffic"] / model, 3)
 
+    # the ordered output streamed to pinned host memory through two staging
+    # buffers (not part of the step; includes the PCIe transfer)
+    stream_host = None
+    if args.host_stream_rows > 0:
+        nrow = min(args.host_stream_rows, k)
+        hi = torch.empty((nrow, wm), dtype=torch.int64).pin_memory()
+        he = torch.empty((nrow, wn), dtype=torch.int64).pin_memory() if extents else None
+        ctx.copy_to_host(0, nrow, hi, he, staging_rows=1 << 18)
+        t_h = ctx.copy_to_host(0, nrow, hi, he, staging_rows=1 << 18)
+        nb = nrow * 8 * (wm + (wn if extents else 0))
+        stream_host = {"rows": nrow, "bytes": nb, "ms": round(t_h, 3), "GBps": round(nb / (t_h * 1e-3) / 1e9, 1),
+                       "staging_rows": 1 << 18, "timing": "second call, HIP events; device-to-host over PCIe"}
+        del hi, he
+        print("[bench] host stream: %s" % json.dumps(stream_host), file=sys.stderr, flush=True)
+
     # the lattice's cover edges of the same result (not part of the step)
     cover = None
     if not args.no_cover:
@@ -527,6 +547,7 @@ def main():
         "cpu_baseline_all_cores": cpu["all"] if cpu else None,
         "cpu_baseline_bitmap_oracle": cpu.get("bitmap") if cpu else None,
         "cover_edges": cover,
+        "host_stream": stream_host,
     }
     ctx.close()
     del ints, exts  # noqa: F821

@@ -42,6 +42,7 @@ EXPORTED = (
     "fcbo_context_create",
     "fcbo_enumerate",
     "fcbo_write_range",
+    "fcbo_copy_to_host",
     "fcbo_cover_edges",
     "fcbo_set_memory_limit",
     "fcbo_enumerate_static",
@@ -120,6 +121,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fcbo_write_range.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
                                      ctypes.c_void_p]
     lib.fcbo_write_range.restype = ctypes.c_int
+    lib.fcbo_copy_to_host.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_uint64, P(ctypes.c_double)]
+    lib.fcbo_copy_to_host.restype = ctypes.c_int
     lib.fcbo_cover_edges.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                      P(ctypes.c_uint64), P(ctypes.c_double)]
     lib.fcbo_cover_edges.restype = ctypes.c_int
@@ -182,6 +186,17 @@ def fcbo_write_range(ctx: int, first: int, count: int, intents_out_ptr: int, ext
                                          ctypes.c_void_p(extents_out_ptr or None))
     if rc != FCBO_OK:
         raise FcboError(rc, "fcbo_write_range")
+
+
+def fcbo_copy_to_host(ctx: int, first: int, count: int, host_intents_ptr: int, host_extents_ptr: int,
+                      staging_rows: int) -> float:
+    """Output rows [first, first + count) into host memory; returns the device ms."""
+    ms = ctypes.c_double(0.0)
+    rc = load_library().fcbo_copy_to_host(ctypes.c_void_p(ctx), first, count, ctypes.c_void_p(host_intents_ptr or None),
+                                          ctypes.c_void_p(host_extents_ptr or None), staging_rows, ctypes.byref(ms))
+    if rc != FCBO_OK:
+        raise FcboError(rc, "fcbo_copy_to_host")
+    return ms.value
 
 
 def fcbo_cover_edges(ctx: int, offsets_out_ptr: int, targets_out_ptr: int, capacity: int):
@@ -376,6 +391,27 @@ class Context:
         if rc != FCBO_OK or e2 != e:
             raise FcboError(rc, "fcbo_cover_edges")
         return offsets, targets[:e], ms_count + ms
+
+    def copy_to_host(self, first: int, count: int, intents=None, extents=None, staging_rows: int = 1 << 20):
+        """Output rows [first, first + count) into host arrays (numpy uint64 or CPU torch
+        tensors, C-contiguous, count x W words); returns the device ms."""
+        def ptr(a, width, what):
+            if a is None:
+                return 0
+            if isinstance(a, np.ndarray):
+                ok = a.dtype == np.uint64 and a.flags["C_CONTIGUOUS"] and a.ndim == 2
+                p = a.ctypes.data
+            else:
+                ok = (not a.is_cuda) and a.element_size() == 8 and a.is_contiguous() and a.dim() == 2
+                p = a.data_ptr()
+            if not ok or a.shape[0] < count or a.shape[1] != width:
+                raise ValueError("%s must be a C-contiguous host array of at least %d x %d 64-bit words"
+                                 % (what, count, width))
+            return p
+        if intents is None and extents is None:
+            raise ValueError("give an intent or an extent array")
+        return fcbo_copy_to_host(self.handle, first, count, ptr(intents, self.wm, "intents"),
+                                 ptr(extents, self.wn, "extents"), staging_rows)
 
     def set_memory_limit(self, nbytes: int) -> None:
         fcbo_set_memory_limit(self.handle, nbytes)

@@ -217,6 +217,11 @@ struct fcbo_context {
     uint32_t *rank = nullptr;  // subtree size, then position, of every concept
     uint32_t *perm = nullptr;  // concept at every output position
 
+    // staging buffers of fcbo_copy_to_host (two of each)
+    uint64_t cap_hs_int[2] = {0, 0}, cap_hs_ext[2] = {0, 0};
+    uint64_t *hs_int[2] = {nullptr, nullptr}, *hs_ext[2] = {nullptr, nullptr};
+    hipEvent_t hs_written[2] = {nullptr, nullptr}, hs_copied[2] = {nullptr, nullptr};
+
     // cover edges
     uint64_t cap_ctable = 0, cap_ccount = 0, cap_coff = 0, cap_cbig = 0, cap_cctr = 0;
     uint32_t *ctable = nullptr;   // concept index by intent (open addressing)
@@ -334,6 +339,10 @@ struct fcbo_context {
         dfree(dmem, rank, cap_rank); dfree(dmem, perm, cap_perm);
         dfree(dmem, ctable, cap_ctable); dfree(dmem, ccount, cap_ccount); dfree(dmem, coff, cap_coff);
         dfree(dmem, cbig, cap_cbig); dfree(dmem, cctr, cap_cctr);
+        for (int b = 0; b < 2; ++b) {
+            dfree(dmem, hs_int[b], cap_hs_int[b]);
+            dfree(dmem, hs_ext[b], cap_hs_ext[b]);
+        }
         have_result = have_perm = have_cover_counts = false;
     }
 
@@ -349,6 +358,11 @@ struct fcbo_context {
         ev_pool.clear();
         if (ev_counts) (void)hipEventDestroy(ev_counts);
         ev_counts = nullptr;
+        for (int b = 0; b < 2; ++b) {
+            if (hs_written[b]) (void)hipEventDestroy(hs_written[b]);
+            if (hs_copied[b]) (void)hipEventDestroy(hs_copied[b]);
+            hs_written[b] = hs_copied[b] = nullptr;
+        }
         for (int i = 0; i < kSide; ++i) {
             if (ev_fork[i]) (void)hipEventDestroy(ev_fork[i]);
             if (ev_join[i]) (void)hipEventDestroy(ev_join[i]);
@@ -437,6 +451,8 @@ struct fcbo_context {
     void write_output(uint64_t *intents_out, uint64_t *extents_out, uint64_t first, uint64_t count);
     uint64_t model_bytes() const;
     uint64_t cover_edges(uint64_t *offsets_out, uint32_t *targets_out, uint64_t capacity);
+    void copy_to_host(uint64_t first, uint64_t count, uint64_t *host_intents, uint64_t *host_extents,
+                      uint64_t staging_rows);
 };
 
 namespace {
@@ -1010,6 +1026,49 @@ uint64_t fcbo_context::cover_edges(uint64_t *offsets_out, uint32_t *targets_out,
     return e;
 }
 
+// Output rows [first, first + count) into host memory, staging_rows at a time
+// through two device buffers: the output kernels fill one buffer on the
+// context's stream while the other is copied to the host on the side stream
+// (events order a buffer's reuse after its copy).
+void fcbo_context::copy_to_host(uint64_t first, uint64_t count, uint64_t *host_intents, uint64_t *host_extents,
+                                uint64_t staging_rows)
+{
+    if (!have_perm) order_concepts();
+    const uint64_t rows_per = std::min(staging_rows, count);
+    for (int b = 0; b < 2; ++b) {
+        if (host_intents) ensure(dmem, hs_int[b], cap_hs_int[b], rows_per * (uint64_t)wm, 0, stream, 1);
+        if (host_extents) ensure(dmem, hs_ext[b], cap_hs_ext[b], rows_per * (uint64_t)wn, 0, stream, 1);
+        if (!hs_written[b]) CK(hipEventCreateWithFlags(&hs_written[b], hipEventDisableTiming));
+        if (!hs_copied[b]) CK(hipEventCreateWithFlags(&hs_copied[b], hipEventDisableTiming));
+    }
+    if (!aux[0]) CK(hipStreamCreateWithFlags(&aux[0], hipStreamNonBlocking));
+    hipStream_t cs = aux[0];
+    // the copy stream starts after what the caller's stream holds
+    if (!ev_fork[0]) CK(hipEventCreateWithFlags(&ev_fork[0], hipEventDisableTiming));
+    CK(hipEventRecord(ev_fork[0], stream));
+    CK(hipStreamWaitEvent(cs, ev_fork[0], 0));
+    bool used[2] = {false, false};
+    uint64_t i = 0;
+    for (uint64_t at = 0; at < count; at += rows_per, ++i) {
+        const int b = (int)(i & 1);
+        const uint64_t n = std::min(rows_per, count - at);
+        if (used[b]) CK(hipStreamWaitEvent(stream, hs_copied[b], 0));  // its last copy is done
+        write_output(host_intents ? hs_int[b] : nullptr, host_extents ? hs_ext[b] : nullptr, first + at, n);
+        CK(hipEventRecord(hs_written[b], stream));
+        CK(hipStreamWaitEvent(cs, hs_written[b], 0));
+        if (host_intents)
+            CK(hipMemcpyAsync(host_intents + at * (uint64_t)wm, hs_int[b], n * (uint64_t)wm * sizeof(uint64_t),
+                              hipMemcpyDeviceToHost, cs));
+        if (host_extents)
+            CK(hipMemcpyAsync(host_extents + at * (uint64_t)wn, hs_ext[b], n * (uint64_t)wn * sizeof(uint64_t),
+                              hipMemcpyDeviceToHost, cs));
+        CK(hipEventRecord(hs_copied[b], cs));
+        used[b] = true;
+    }
+    CK(hipStreamSynchronize(cs));
+    CK(hipStreamSynchronize(stream));
+}
+
 // ---------------------------------------------------------------------------
 // Static device scratch of fcbo_enumerate_static: one copy per GPU, held until
 // the process ends.  Host code never takes its name as an address (that is a
@@ -1285,6 +1344,35 @@ int fcbo_cover_edges(fcbo_context *ctx, uint64_t *offsets_out, uint32_t *targets
         return FCBO_ERR_OUT_OF_MEMORY;
     }
     return rc;
+}
+
+int fcbo_copy_to_host(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_t *host_intents,
+                      uint64_t *host_extents, uint64_t staging_rows, double *elapsed_ms)
+{
+    if (!ctx || (!host_intents && !host_extents) || !ctx->have_result || first > ctx->K ||
+        count > ctx->K - first || staging_rows == 0)
+        return FCBO_ERR_INVALID_ARGUMENT;
+    try {
+        CK(hipSetDevice(ctx->device));
+        ctx->profile = false;
+        ctx->ev_used = 0;
+        ctx->marks.clear();
+        hipEvent_t e0 = ctx->ev_get(), e1 = ctx->ev_get();
+        CK(hipEventRecord(e0, ctx->stream));
+        if (count) ctx->copy_to_host(first, count, host_intents, host_extents, staging_rows);
+        CK(hipEventRecord(e1, ctx->stream));
+        CK(hipStreamSynchronize(ctx->stream));
+        if (elapsed_ms) {
+            float ms = 0;
+            CK(hipEventElapsedTime(&ms, e0, e1));
+            *elapsed_ms = ms;
+        }
+    } catch (const HipError &e) {
+        return e.code;
+    } catch (const std::bad_alloc &) {
+        return FCBO_ERR_OUT_OF_MEMORY;
+    }
+    return FCBO_OK;
 }
 
 int fcbo_set_memory_limit(fcbo_context *ctx, uint64_t bytes)

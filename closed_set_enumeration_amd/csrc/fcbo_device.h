@@ -1148,15 +1148,26 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
                 if (u == wm - 1) Bx[u] |= ~A.tail_m;
             }
         }
+        // the parent's object ids, 64 a step, loaded together once (lanes past
+        // the list take the zero row after the last object); then all their
+        // rows for U at once, so a parent waits for two loads, not two per step
+        constexpr int kSteps = kMidWide / kWave;
+        const int nsteps = (int)((o1 - o0 + kWave - 1) / kWave);
+        uint32_t ids[kSteps];
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+            const uint64_t o = o0 + (uint64_t)(st * kWave + lane);
+            ids[st] = (st < nsteps && o < o1) ? A.objs[o] : (uint32_t)A.n;
+        }
         uint64_t U[WMC];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) U[u] = 0;
-        for (uint64_t o = o0 + lane; o < o1; o += kWave) {
-            const uint64_t g = A.objs[o];
 #pragma unroll
-            for (int u = 0; u < WMC; ++u)
-                if (u < wm) U[u] |= A.rows[g * A.wm + u];
-        }
+        for (int st = 0; st < kSteps; ++st)
+            if (st < nsteps)
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm) U[u] |= A.rows[(uint64_t)ids[st] * A.wm + u];
         int nU = 0, j0 = -1;
         int pre[WMC];
 #pragma unroll
@@ -1209,11 +1220,20 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
             for (int x = lane; x < nc * WMC; x += kWave) Dt[x] = ~0ull;
             for (int x = lane; x < nc; x += kWave) Ct[x] = 0;
             wave_sync();
-            for (uint64_t o = o0 + lane; o < o1; o += kWave) {
-                const uint64_t g = A.objs[o];
-                uint64_t row[WMC];
+            // incidences, a step of 64 objects at a time; the next step's rows
+            // are loaded while this step's incidences run
+            uint64_t row[WMC];
 #pragma unroll
-                for (int u = 0; u < WMC; ++u) row[u] = (u < wm) ? A.rows[g * A.wm + u] : 0ull;
+            for (int u = 0; u < WMC; ++u) row[u] = (u < wm) ? A.rows[(uint64_t)ids[0] * A.wm + u] : 0ull;
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st) {
+                if (st >= nsteps) break;
+                uint64_t nxt[WMC];
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    nxt[u] = (st + 1 < kSteps && st + 1 < nsteps && u < wm)
+                                 ? A.rows[(uint64_t)ids[st + 1 < kSteps ? st + 1 : st] * A.wm + u]
+                                 : 0ull;
 #pragma unroll
                 for (int u = 0; u < WMC; ++u) {
                     uint64_t x = row[u] & Us[u];
@@ -1227,6 +1247,8 @@ __global__ void __launch_bounds__(kWave * kMidWaves) k_mid_test(LevelArgs A)
                         atomicAdd(&Ct[r], 1u);
                     }
                 }
+#pragma unroll
+                for (int u = 0; u < WMC; ++u) row[u] = nxt[u];
             }
             wave_sync();
             for (int r0 = 0; r0 < nc; r0 += kWave) {
@@ -1317,15 +1339,25 @@ __global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
         if (tid < WMC) s_u[tid] = 0;
         __syncthreads();
         // U: candidates carried by some object of A
+        // the parent's object ids, kWideThreads a step, loaded together once
+        // (threads past the list take the zero row after the last object)
+        constexpr int kSteps = kMidMax / kWideThreads;
+        const int nsteps = (int)((o1 - o0 + kWideThreads - 1) / kWideThreads);
+        uint32_t ids[kSteps];
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+            const uint64_t o = o0 + (uint64_t)(st * kWideThreads + tid);
+            ids[st] = (st < nsteps && o < o1) ? A.objs[o] : (uint32_t)A.n;
+        }
         uint64_t U[WMC];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) U[u] = 0;
-        for (uint64_t o = o0 + tid; o < o1; o += kWideThreads) {
-            const uint64_t g = A.objs[o];
 #pragma unroll
-            for (int u = 0; u < WMC; ++u)
-                if (u < wm) U[u] |= A.rows[g * A.wm + u];
-        }
+        for (int st = 0; st < kSteps; ++st)
+            if (st < nsteps)
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u < wm) U[u] |= A.rows[(uint64_t)ids[st] * A.wm + u];
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
             if (u < wm) {
@@ -1350,12 +1382,19 @@ __global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
         for (int x = tid; x < nU * WMC; x += kWideThreads) s_d[x] = ~0ull;
         for (int x = tid; x < nU; x += kWideThreads) s_c[x] = 0;
         __syncthreads();
-        // incidences
-        for (uint64_t o = o0 + tid; o < o1; o += kWideThreads) {
-            const uint64_t g = A.objs[o];
-            uint64_t row[WMC];
+        // incidences, a step at a time, the next step's rows loaded meanwhile
+        uint64_t row[WMC];
 #pragma unroll
-            for (int u = 0; u < WMC; ++u) row[u] = (u < wm) ? A.rows[g * A.wm + u] : 0ull;
+        for (int u = 0; u < WMC; ++u) row[u] = (u < wm) ? A.rows[(uint64_t)ids[0] * A.wm + u] : 0ull;
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+            if (st >= nsteps) break;
+            uint64_t nxt[WMC];
+#pragma unroll
+            for (int u = 0; u < WMC; ++u)
+                nxt[u] = (st + 1 < kSteps && st + 1 < nsteps && u < wm)
+                             ? A.rows[(uint64_t)ids[st + 1 < kSteps ? st + 1 : st] * A.wm + u]
+                             : 0ull;
 #pragma unroll
             for (int u = 0; u < WMC; ++u) {
                 uint64_t x = row[u] & U[u];
@@ -1369,6 +1408,8 @@ __global__ void __launch_bounds__(kWideThreads) k_mid_test_wide(LevelArgs A)
                     atomicAdd(&s_c[r], 1u);
                 }
             }
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) row[u] = nxt[u];
         }
         __syncthreads();
         // the first attribute outside B, carried by no object: C = {}, D = M, rank 0

@@ -204,6 +204,24 @@ int fcbo_write_range(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_t
                      uint64_t *extents_out);
 
 /*
+ * Output rows [first, first + count) of the last enumeration into host memory
+ * (row r of host_intents / host_extents = output position first + r; either may
+ * be NULL, not both), staging_rows rows at a time through two device buffers:
+ * the output kernels fill one on the context's stream while the other is copied
+ * to the host on an internal stream, so writing and copying overlap (page 1
+ * section 6.1 moves concepts to the host in batches with copy and compute
+ * staggered; page 4 section 5.2 overlaps transfers with streams).  Device
+ * memory for the output stays bounded by 2 x staging_rows rows, whatever K is.
+ * Pinned host memory (hipHostMalloc) lets the copies run asynchronously;
+ * pageable memory works but the runtime then stages each copy.
+ * elapsed_ms (optional) receives the call's time on the context's stream.
+ * FCBO_ERR_INVALID_ARGUMENT if nothing was enumerated, first + count > K or
+ * staging_rows is 0.  Returns after the copies have finished.
+ */
+int fcbo_copy_to_host(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_t *host_intents,
+                      uint64_t *host_extents, uint64_t staging_rows, double *elapsed_ms);
+
+/*
  * Lattice cover edges of the last enumeration (page 1 section 4.4 and page 4
  * section 3.4 rebuild them after the concepts are found): for the concept at
  * output position i, the output positions of its lower covers (the concepts

@@ -280,6 +280,38 @@ def test_write_range_pages_the_output():
         ctx.close()
 
 
+def test_copy_to_host_through_two_staging_buffers():
+    # the output streamed to host memory in bounded pieces, overlapping the
+    # output kernels of one piece with the copy of the other
+    cells = synth.make_config("ctx2000x64", packed=False)
+    rows = synth.pack_rows(cells)
+    want = oracle.cbo(rows, 64)
+    k = want.n_concepts
+    ctx = fca.Context(rows, 64)
+    try:
+        assert ctx.count() == k
+        hi = torch.full((k, ctx.wm), -1, dtype=torch.int64).pin_memory()
+        he = torch.full((k, ctx.wn), -1, dtype=torch.int64).pin_memory()
+        ctx.copy_to_host(0, k, hi, he, staging_rows=7777)  # ragged last piece
+        assert np.array_equal(hi.numpy().view(np.uint64), want.intents)
+        assert np.array_equal(he.numpy().view(np.uint64), want.extents)
+        # pageable numpy arrays, a middle range, one buffer at a time
+        a = np.zeros((1000, ctx.wm), dtype=np.uint64)
+        ctx.copy_to_host(500, 1000, intents=a, staging_rows=1 << 20)
+        assert np.array_equal(a, want.intents[500:1500])
+        b = np.zeros((10, ctx.wn), dtype=np.uint64)
+        ctx.copy_to_host(k - 10, 10, extents=b, staging_rows=1)
+        assert np.array_equal(b, want.extents[k - 10:])
+        for first, count, staging in [(k - 9, 10, 4), (0, 10, 0)]:
+            with pytest.raises(fca.FcboError) as e:
+                fca.fcbo_copy_to_host(ctx.handle, first, count, a.ctypes.data, 0, staging)
+            assert e.value.code == fca.FCBO_ERR_INVALID_ARGUMENT
+        with pytest.raises(ValueError):
+            ctx.copy_to_host(0, 2000, intents=a)  # fewer rows than asked for
+    finally:
+        ctx.close()
+
+
 def test_memory_limit_fails_part_way_and_leaves_no_stale_result():
     cells = synth.make_config("ctx2000x64", packed=False)
     rows = synth.pack_rows(cells)
