@@ -1,9 +1,9 @@
 """Formal-concept enumeration on MI355X: Python binding of libfcbo.so.
 
 The functions named like the C ABI (``fcbo_context_create``, ``fcbo_enumerate``,
-``fcbo_write_range``, ``fcbo_set_memory_limit``, ``fcbo_level_counts``,
-``fcbo_copy_columns``, ``fcbo_destroy``, ``fcbo_error_string``) only marshal
-arguments; every step of the enumeration
+``fcbo_enumerate_bounded``, ``fcbo_write_range``, ``fcbo_set_memory_limit``,
+``fcbo_level_counts``, ``fcbo_copy_columns``, ``fcbo_destroy``,
+``fcbo_error_string``, ...) only marshal arguments; every step of the enumeration
 runs in the HIP kernels of the library.  :class:`Context` is a convenience
 wrapper that takes device buffers and the stream from PyTorch.
 
@@ -28,12 +28,15 @@ FCBO_ERR_DEVICE = -3
 FCBO_ERR_CAPACITY = -4
 FCBO_ERR_LIMIT = -5
 FCBO_ERR_SCRATCH = -6
+FCBO_ERR_STOPPED = -7
 FCBO_STATIC_SCRATCH_BYTES = 64 << 20
 
 FCBO_ROWS_ON_DEVICE = 1
 FCBO_TINY_BUFFERS = 2
 FCBO_REUSE_RESULT = 1
 FCBO_PROFILE = 2
+FCBO_ONE_SUBTREE_PER_BATCH = 4
+FCBO_SPLIT_ROOT_CHILDREN = 8
 
 KERNEL_CLASSES = ("count", "test_local", "test_medium", "test_big", "scan", "write_local", "write_medium",
                   "write_big", "order", "output")
@@ -41,6 +44,7 @@ KERNEL_CLASSES = ("count", "test_local", "test_medium", "test_big", "scan", "wri
 EXPORTED = (
     "fcbo_context_create",
     "fcbo_enumerate",
+    "fcbo_enumerate_bounded",
     "fcbo_write_range",
     "fcbo_copy_to_host",
     "fcbo_cover_edges",
@@ -78,6 +82,10 @@ class FcboStats(ctypes.Structure):
         ("order_launches", ctypes.c_uint64),
         ("kernel_ms", ctypes.c_double * len(KERNEL_CLASSES)),
         ("kernel_launches", ctypes.c_uint64 * len(KERNEL_CLASSES)),
+        ("batches", ctypes.c_uint64),
+        ("batch_retries", ctypes.c_uint64),
+        ("batch_splits", ctypes.c_uint64),
+        ("peak_device_bytes", ctypes.c_uint64),
     ]
 
     def as_dict(self) -> dict:
@@ -92,6 +100,10 @@ class FcboError(RuntimeError):
         super().__init__("%s failed: %s (%d)" % (what, fcbo_error_string(code), code))
         self.code = code
 
+
+# int sink(void *user, uint64_t first, uint64_t count, const uint64_t *intents, const uint64_t *extents)
+SINK_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
+                           ctypes.c_void_p)
 
 _lib = None
 
@@ -118,6 +130,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         P(FcboStats),
     ]
     lib.fcbo_enumerate.restype = ctypes.c_int
+    lib.fcbo_enumerate_bounded.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_uint32, P(ctypes.c_uint64), P(FcboStats),
+    ]
+    lib.fcbo_enumerate_bounded.restype = ctypes.c_int
     lib.fcbo_write_range.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
                                      ctypes.c_void_p]
     lib.fcbo_write_range.restype = ctypes.c_int
@@ -178,6 +195,36 @@ def fcbo_enumerate(ctx: int, intents_out_ptr: int, extents_out_ptr: int, capacit
     if rc not in (FCBO_OK, FCBO_ERR_CAPACITY):
         raise FcboError(rc, "fcbo_enumerate")
     return rc, k.value, st
+
+
+def fcbo_enumerate_bounded(ctx: int, intents_buf_ptr: int, extents_buf_ptr: int, piece_rows: int, sink=None,
+                           flags: int = 0):
+    """Bounded-memory enumeration.  ``sink(first, count, intents_ptr, extents_ptr)`` is called
+    once per piece with device pointers (0 for a buffer not given) and returns nothing to go
+    on or a true value to stop.  Returns (n_concepts, FcboStats); raises FcboError on failure,
+    or re-raises what the sink raised (the enumeration stops there)."""
+    raised = []
+
+    def trampoline(_user, first, count, ip, ep):
+        try:
+            return 1 if sink(first, count, ip or 0, ep or 0) else 0
+        except BaseException as e:  # handed back to the caller after the C call returns
+            raised.append(e)
+            return 1
+
+    cb = SINK_FN(trampoline) if sink is not None else None
+    k = ctypes.c_uint64(0)
+    st = FcboStats()
+    rc = load_library().fcbo_enumerate_bounded(
+        ctypes.c_void_p(ctx), ctypes.c_void_p(intents_buf_ptr or None), ctypes.c_void_p(extents_buf_ptr or None),
+        piece_rows, ctypes.cast(cb, ctypes.c_void_p) if cb is not None else None, None, flags, ctypes.byref(k),
+        ctypes.byref(st),
+    )
+    if raised:
+        raise raised[0]
+    if rc != FCBO_OK:
+        raise FcboError(rc, "fcbo_enumerate_bounded")
+    return k.value, st
 
 
 def fcbo_write_range(ctx: int, first: int, count: int, intents_out_ptr: int, extents_out_ptr: int) -> None:
@@ -382,7 +429,8 @@ class Context:
         counting and the writing call together."""
         torch = self._torch
         rc, e, ms_count = fcbo_cover_edges(self.handle, 0, 0, 0)
-        assert rc == FCBO_ERR_CAPACITY
+        if rc != FCBO_ERR_CAPACITY:
+            raise FcboError(rc, "fcbo_cover_edges")
         dev = torch.device("cuda", self.device)
         k = fcbo_level_counts(self.handle)[0].sum()
         offsets = torch.empty(int(k) + 1, dtype=torch.int64, device=dev)
@@ -412,6 +460,27 @@ class Context:
             raise ValueError("give an intent or an extent array")
         return fcbo_copy_to_host(self.handle, first, count, ptr(intents, self.wm, "intents"),
                                  ptr(extents, self.wn, "extents"), staging_rows)
+
+    def enumerate_bounded(self, sink=None, piece_rows: int = 1 << 20, intents: bool = True, extents: bool = True,
+                          profile: bool = False, flags: int = 0):
+        """Enumerate in bounded device memory (cap it with set_memory_limit): ``sink(first,
+        intents, extents)`` gets each piece as device tensors of ``count`` rows (views of
+        the piece buffers, valid only during the call; None for an output not asked for)
+        at output positions [first, first + count).  Returns (K, stats dict)."""
+        torch = self._torch
+        dev = torch.device("cuda", self.device)
+        rows = max(1, int(piece_rows))
+        ib = torch.empty((rows, self.wm), dtype=torch.int64, device=dev) if intents else None
+        eb = torch.empty((rows, self.wn), dtype=torch.int64, device=dev) if extents else None
+
+        def piece(first, count, _ip, _ep):
+            return sink(first, ib[:count] if ib is not None else None, eb[:count] if eb is not None else None)
+
+        k, st = fcbo_enumerate_bounded(self.handle, ib.data_ptr() if ib is not None else 0,
+                                       eb.data_ptr() if eb is not None else 0, rows,
+                                       piece if sink is not None else None,
+                                       flags | (FCBO_PROFILE if profile else 0))
+        return k, st.as_dict()
 
     def set_memory_limit(self, nbytes: int) -> None:
         fcbo_set_memory_limit(self.handle, nbytes)

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <mutex>
 #include <numeric>
 #include <new>
@@ -48,6 +49,7 @@ inline uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 struct DeviceMemory {
     uint64_t limit = 0;  // bytes the buffers may hold together; 0 = no cap
     uint64_t held = 0;   // bytes they hold now
+    uint64_t peak = 0;   // most bytes held at once since the last reset of peak
     char *region = nullptr;  // the fixed region, or null
     uint64_t region_size = 0, region_used = 0;
 
@@ -63,6 +65,7 @@ struct DeviceMemory {
         void *q = nullptr;
         CK(hipMalloc(&q, bytes));
         held += bytes;
+        peak = std::max(peak, held);
         return q;
     }
     void put(void *p, uint64_t bytes)
@@ -114,6 +117,7 @@ struct LevelLog {
     uint64_t lo[kMax + 1];    // index of level k's first concept (generation order)
     size_t n = 0;
     void clear() { n = 0; lo[0] = 0; }
+    void truncate(size_t k) { n = std::min(n, k); }
     size_t size() const { return n; }
     void push(uint64_t c, uint64_t t)
     {
@@ -123,6 +127,19 @@ struct LevelLog {
         lo[n + 1] = lo[n] + c;
         ++n;
     }
+};
+
+// Work counts of an enumeration, summed over its levels.
+struct Totals {
+    uint64_t tests = 0, pairs = 0, sum_c = 0;
+    uint64_t local_parents = 0, local_objs = 0, med_parents = 0, med_objs = 0;
+    uint64_t big_parents = 0, big_tests = 0, big_scan = 0, big_nzw = 0, big_cobjs = 0;
+};
+
+// Where the level loop stands: parents [lo, lo + P) of the store, objects
+// used up to obj_hi, and the mid / huge parents expected among them.
+struct LevelCursor {
+    uint64_t lo = 0, P = 0, obj_hi = 0, next_mid = 0, next_huge = 0;
 };
 
 constexpr int kGridCap = 4096;  // blocks for grid-stride wave kernels
@@ -164,6 +181,27 @@ struct BigStore {
         S.bmp_cap = cap_bmp;
         S.cnt_slot = cnt_slot; S.tot_slot = tot_slot; S.pass_slot = pass_slot;
         return S;
+    }
+};
+
+// A run of sibling concepts kept aside by a bounded enumeration, the seeds of
+// its batches: intents, cursors (ascending), extent-list offsets as they were
+// in the store, and the lists, which started at store object obj_base.
+struct SeedSet {
+    uint64_t count = 0, level = 0, obj_base = 0;
+    uint64_t hi = 0, B = 0;  // seeds [0, hi) remain; the next batch takes up to B, ending at hi
+    uint64_t cap_int = 0, cap_cur = 0, cap_loff = 0, cap_obj = 0;
+    uint64_t *ints = nullptr;
+    int32_t *cur = nullptr;
+    uint64_t *loff = nullptr;
+    uint32_t *objs = nullptr;
+    std::vector<uint64_t> h_loff;
+    void free_all(DeviceMemory &dm)
+    {
+        dfree(dm, ints, cap_int);
+        dfree(dm, cur, cap_cur);
+        dfree(dm, loff, cap_loff);
+        dfree(dm, objs, cap_obj);
     }
 };
 
@@ -232,12 +270,15 @@ struct fcbo_context {
     bool have_cover_counts = false;  // ccount / coff / cbig hold the last result's
     uint64_t cover_total = 0;
 
+    // seed sets of a bounded enumeration, the deepest last
+    std::vector<SeedSet> seeds;
+
     // result of the last enumeration
+    bool have_levels = false;  // lev holds the per-level counts of a complete enumeration
     bool have_result = false;
     bool have_perm = false;
-    uint64_t K = 0, tests = 0, pairs = 0, sum_c = 0;
-    uint64_t local_parents = 0, local_objs = 0, med_parents = 0, med_objs = 0;
-    uint64_t big_parents = 0, big_tests = 0, big_scan = 0, big_nzw = 0, big_cobjs = 0, order_launches = 0;
+    uint64_t K = 0, order_launches = 0;
+    Totals tot;
     LevelLog lev;
 
     // profiling
@@ -339,6 +380,7 @@ struct fcbo_context {
         dfree(dmem, rank, cap_rank); dfree(dmem, perm, cap_perm);
         dfree(dmem, ctable, cap_ctable); dfree(dmem, ccount, cap_ccount); dfree(dmem, coff, cap_coff);
         dfree(dmem, cbig, cap_cbig); dfree(dmem, cctr, cap_cctr);
+        release_seeds();
         for (int b = 0; b < 2; ++b) {
             dfree(dmem, hs_int[b], cap_hs_int[b]);
             dfree(dmem, hs_ext[b], cap_hs_ext[b]);
@@ -446,10 +488,20 @@ struct fcbo_context {
         ensure(dmem, lrec, cap_lrec, chunks * kWave * (4 + (uint64_t)wm), 0, stream, 1);
         ensure(dmem, lfill, cap_lfill, chunks, 0, stream, 1);
     }
+    void start_root(LevelCursor &s);
+    void run_levels(LevelCursor &s, uint64_t max_levels);
     void enumerate_levels();
+    void enumerate_bounded(uint64_t *intents_buf, uint64_t *extents_buf, uint64_t piece_rows, fcbo_sink_fn sink,
+                           void *user, uint32_t flags, fcbo_stats &st);
+    void capture_seeds(uint64_t first, uint64_t count, uint64_t obj_lo, uint64_t obj_hi, uint64_t level);
+    void release_seeds();
+    LevelCursor load_seeds(const SeedSet &S, uint64_t a, uint64_t B);
+    void harvest_marks(fcbo_stats &st);
+    void drain();
     void order_concepts();
     void write_output(uint64_t *intents_out, uint64_t *extents_out, uint64_t first, uint64_t count);
-    uint64_t model_bytes() const;
+    uint64_t model_bytes(uint64_t k) const;  // of an enumeration of k concepts with the totals in tot
+    void fill_counts(fcbo_stats &st, uint64_t k) const;
     uint64_t cover_edges(uint64_t *offsets_out, uint32_t *targets_out, uint64_t capacity);
     void copy_to_host(uint64_t first, uint64_t count, uint64_t *host_intents, uint64_t *host_extents,
                       uint64_t staging_rows);
@@ -617,15 +669,15 @@ LevelFns pick_level_fns(int wm)
 
 }  // namespace
 
-void fcbo_context::enumerate_levels()
+// Reset the result and run the root: its intent G' and extent G at store
+// index 0; s is left at the root level.
+void fcbo_context::start_root(LevelCursor &s)
 {
-    const LevelFns fns = pick_level_fns(wm);
     const uint64_t mc = min_cap();
     const bool bm = use_bitmaps();
     // nothing of an earlier result survives a failure part-way through
-    have_result = have_perm = have_cover_counts = false;
+    have_result = have_perm = have_cover_counts = have_levels = false;
     K = 0;
-    // root
     ensure(dmem, intents, cap_int, (uint64_t)wm * 1024, 0, stream, mc);
     ensure(dmem, cursor, cap_cur, 1024, 0, stream, mc);
     ensure(dmem, loff, cap_loff, 1025, 0, stream, mc);
@@ -641,8 +693,7 @@ void fcbo_context::enumerate_levels()
         CK_LAUNCH();
     }
     lev.clear();
-    tests = pairs = sum_c = 0;
-    local_parents = local_objs = med_parents = med_objs = big_parents = big_tests = big_scan = big_nzw = big_cobjs = 0;
+    tot = Totals{};
     const uint64_t rstride = 4 + (uint64_t)wm;
     if (!huge.tasks) {
         if (bm) ensure_huge_tests(start_size(1u << 16));
@@ -652,15 +703,28 @@ void fcbo_context::enumerate_levels()
     if (!mrec) ensure(dmem, mrec, cap_mrec, rstride * start_size(1u << 18), 0, stream, 1);
     if (!wrec) ensure(dmem, wrec, cap_wrec, rstride * start_size(1u << 16), 0, stream, 1);
     if (!lrec) ensure_local_records(tiny ? kWave : start_size(1u << 21));
-    uint64_t lo = 0, P = 1, obj_hi = (uint64_t)n;  // parents [lo, lo+P); objects used so far
-    const uint64_t mid_max = wm <= 8 ? (uint64_t)kMidMax : (uint64_t)kSmallMax;
+    s = LevelCursor{};
+    s.P = 1;
+    s.obj_hi = (uint64_t)n;
     // parents of each class on the level about to run (the root: N objects);
     // later levels learn them from the children counted by the test kernels
-    uint64_t next_mid = ((uint64_t)n > (uint64_t)kSmallMax && (uint64_t)n <= mid_max) ? 1 : 0;
-    uint64_t next_huge = (uint64_t)n > mid_max ? 1 : 0;
+    const uint64_t mid_max = wm <= 8 ? (uint64_t)kMidMax : (uint64_t)kSmallMax;
+    s.next_mid = ((uint64_t)n > (uint64_t)kSmallMax && (uint64_t)n <= mid_max) ? 1 : 0;
+    s.next_huge = (uint64_t)n > mid_max ? 1 : 0;
     ctr = 0;
     clear_words(counters, 2 * CNT_N);
-    while (P > 0) {
+}
+
+// Expand up to max_levels levels from s (parents [s.lo, s.lo + s.P)): test,
+// count, grow the store, write the children; s moves to the children.
+void fcbo_context::run_levels(LevelCursor &s, uint64_t max_levels)
+{
+    const LevelFns fns = pick_level_fns(wm);
+    const uint64_t mc = min_cap();
+    const bool bm = use_bitmaps();
+    const uint64_t rstride = 4 + (uint64_t)wm;
+    uint64_t lo = s.lo, P = s.P, obj_hi = s.obj_hi, next_mid = s.next_mid, next_huge = s.next_huge;
+    for (uint64_t done = 0; P > 0 && done < max_levels; ++done) {
         if (lo + P >= (1ull << 32)) throw HipError{FCBO_ERR_LIMIT};  // concept indices are 32-bit
         // every level adds an attribute to the intent, so there are at most M + 1
         if (lev.size() > (size_t)m + 1) throw HipError{FCBO_ERR_DEVICE};
@@ -739,18 +803,18 @@ void fcbo_context::enumerate_levels()
             next_mid = h_counters[CNT_NEXT_MID];
             next_huge = h_counters[CNT_NEXT_HUGE];
             lev.push(P, h_counters[CNT_TESTS]);
-            tests += h_counters[CNT_TESTS];
-            pairs += h_counters[CNT_PAIRS];
-            sum_c += n_objs;
-            big_parents += h_counters[CNT_HUGE];
-            med_parents += n_mid;
-            local_parents += P - h_counters[CNT_HUGE] - n_mid;
-            local_objs += h_counters[CNT_SMALL_OBJS];
-            med_objs += h_counters[CNT_MID_OBJS];
-            big_tests += h_counters[CNT_THUGE];
-            big_scan += h_counters[CNT_BIG_SCAN];
-            big_nzw += h_counters[CNT_HUGE_NZW];
-            big_cobjs += h_counters[CNT_HUGE_COBJS];
+            tot.tests += h_counters[CNT_TESTS];
+            tot.pairs += h_counters[CNT_PAIRS];
+            tot.sum_c += n_objs;
+            tot.big_parents += h_counters[CNT_HUGE];
+            tot.med_parents += n_mid;
+            tot.local_parents += P - h_counters[CNT_HUGE] - n_mid;
+            tot.local_objs += h_counters[CNT_SMALL_OBJS];
+            tot.med_objs += h_counters[CNT_MID_OBJS];
+            tot.big_tests += h_counters[CNT_THUGE];
+            tot.big_scan += h_counters[CNT_BIG_SCAN];
+            tot.big_nzw += h_counters[CNT_HUGE_NZW];
+            tot.big_cobjs += h_counters[CNT_HUGE_COBJS];
             // room for the children in the store; the writes issued above did
             // nothing if it had to grow
             const uint64_t k_end = lo + P + n_children;
@@ -769,10 +833,289 @@ void fcbo_context::enumerate_levels()
         lo += P;
         P = n_children;
         obj_hi += n_objs;
+        s.lo = lo;
+        s.P = P;
+        s.obj_hi = obj_hi;
+        s.next_mid = next_mid;
+        s.next_huge = next_huge;
     }
-    K = lo;
-    have_result = true;
+}
+
+void fcbo_context::enumerate_levels()
+{
+    LevelCursor s;
+    start_root(s);
+    run_levels(s, ~0ull);
+    K = s.lo;
+    have_result = have_levels = true;
     have_perm = false;
+}
+
+// Add the kernel times recorded since the last harvest to st (after the
+// stream has finished) and recycle their events.
+void fcbo_context::harvest_marks(fcbo_stats &st)
+{
+    float ms = 0;
+    for (auto &mk : marks) {
+        CK(hipEventElapsedTime(&ms, mk.second.first, mk.second.second));
+        st.kernel_ms[mk.first] += ms;
+        st.kernel_launches[mk.first] += 1;
+    }
+    marks.clear();
+    ev_used = 0;
+}
+
+// Wait for everything issued on the context's streams (after a failed batch,
+// whose work may still be running).
+void fcbo_context::drain()
+{
+    for (int i = 0; i < kSide; ++i)
+        if (aux[i]) CK(hipStreamSynchronize(aux[i]));
+    CK(hipStreamSynchronize(stream));
+}
+
+// Keep the store's concepts [first, first + count) (siblings, ascending
+// attribute, lists at store objects [obj_lo, obj_hi)) aside as the seeds of
+// later batches; their concepts sit on the given level of the CbO tree.
+void fcbo_context::capture_seeds(uint64_t first, uint64_t count, uint64_t obj_lo, uint64_t obj_hi, uint64_t level)
+{
+    const uint64_t mc = min_cap();
+    seeds.emplace_back();
+    SeedSet &S = seeds.back();
+    S.count = S.hi = S.B = count;
+    S.level = level;
+    S.obj_base = obj_lo;
+    ensure(dmem, S.ints, S.cap_int, count * wm, 0, stream, mc);
+    ensure(dmem, S.cur, S.cap_cur, count, 0, stream, mc);
+    ensure(dmem, S.loff, S.cap_loff, count + 1, 0, stream, mc);
+    ensure(dmem, S.objs, S.cap_obj, std::max<uint64_t>(1, obj_hi - obj_lo), 0, stream, mc);
+    CK(hipMemcpyAsync(S.ints, intents + first * wm, count * wm * 8, hipMemcpyDeviceToDevice, stream));
+    CK(hipMemcpyAsync(S.cur, cursor + first, count * 4, hipMemcpyDeviceToDevice, stream));
+    CK(hipMemcpyAsync(S.loff, loff + first, (count + 1) * 8, hipMemcpyDeviceToDevice, stream));
+    if (obj_hi > obj_lo)
+        CK(hipMemcpyAsync(S.objs, objs + obj_lo, (obj_hi - obj_lo) * 4, hipMemcpyDeviceToDevice, stream));
+    S.h_loff.resize(count + 1);
+    std::vector<int32_t> h_cur(count);
+    CK(hipMemcpyAsync(S.h_loff.data(), S.loff, (count + 1) * 8, hipMemcpyDeviceToHost, stream));
+    CK(hipMemcpyAsync(h_cur.data(), S.cur, count * 4, hipMemcpyDeviceToHost, stream));
+    CK(hipStreamSynchronize(stream));
+    // a parent's children are stored by ascending attribute and listed in the
+    // output by descending attribute: batches are taken from the end
+    for (uint64_t i = 1; i < count; ++i)
+        if (h_cur[i] <= h_cur[i - 1]) throw HipError{FCBO_ERR_DEVICE};
+    if (S.h_loff[0] != obj_lo || S.h_loff[count] != obj_hi) throw HipError{FCBO_ERR_DEVICE};
+}
+
+void fcbo_context::release_seeds()
+{
+    for (SeedSet &S : seeds) S.free_all(dmem);
+    seeds.clear();
+}
+
+// Seeds [a, a + B) of S become level 1 of the store under a stand-in root at
+// index 0 (its first-child link stays 1; the level loop rewrites the rest).
+LevelCursor fcbo_context::load_seeds(const SeedSet &S, uint64_t a, uint64_t B)
+{
+    const uint64_t mc = min_cap();
+    const uint64_t o0 = S.h_loff[a], o1 = S.h_loff[a + B];
+    ensure(dmem, intents, cap_int, (1 + B) * wm, wm, stream, mc);
+    ensure(dmem, cursor, cap_cur, 1 + B, 1, stream, mc);
+    ensure(dmem, loff, cap_loff, 2 + B, 1, stream, mc);
+    ensure(dmem, objs, cap_o, (uint64_t)n + (o1 - o0) + kObjSlack, (uint64_t)n, stream, mc);
+    ensure(dmem, fchild, cap_fch, 2 + B, 1, stream, mc);
+    CK(hipMemcpyAsync(intents + wm, S.ints + a * wm, B * wm * 8, hipMemcpyDeviceToDevice, stream));
+    CK(hipMemcpyAsync(cursor + 1, S.cur + a, B * 4, hipMemcpyDeviceToDevice, stream));
+    const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(1024, div_up(B + 1, kBlock)));
+    hipLaunchKernelGGL(k_shift_offsets, dim3(g), dim3(kBlock), 0, stream, (const uint64_t *)S.loff + a, B + 1, o0,
+                       (uint64_t)n, loff + 1);
+    CK_LAUNCH();
+    if (o1 > o0)
+        CK(hipMemcpyAsync(objs + n, S.objs + (o0 - S.obj_base), (o1 - o0) * 4, hipMemcpyDeviceToDevice, stream));
+    LevelCursor bs;
+    bs.lo = 1;
+    bs.P = B;
+    bs.obj_hi = (uint64_t)n + (o1 - o0);
+    const uint64_t mid_max = wm <= 8 ? (uint64_t)kMidMax : (uint64_t)kSmallMax;
+    for (uint64_t i = a; i < a + B; ++i) {
+        const uint64_t sz = S.h_loff[i + 1] - S.h_loff[i];
+        bs.next_huge += sz > mid_max;
+        bs.next_mid += sz > (uint64_t)kSmallMax && sz <= mid_max;
+    }
+    lev.truncate(1);
+    ctr = 0;
+    clear_words(counters, 2 * CNT_N);
+    return bs;
+}
+
+void fcbo_context::enumerate_bounded(uint64_t *intents_buf, uint64_t *extents_buf, uint64_t piece_rows,
+                                     fcbo_sink_fn sink, void *user, uint32_t flags, fcbo_stats &st)
+{
+    const bool one_per_batch = (flags & FCBO_ONE_SUBTREE_PER_BATCH) != 0;
+    const bool split_root_children = (flags & FCBO_SPLIT_ROOT_CHILDREN) != 0;
+    const auto t_start = std::chrono::steady_clock::now();
+    const uint64_t mc = min_cap();
+    const bool out = intents_buf || extents_buf;
+    release_seeds();
+    dmem.peak = dmem.held;
+    marks.clear();
+    ev_used = 0;
+    float ms = 0;
+    double loop_ms = 0, order_ms = 0, out_ms = 0;
+    uint64_t pos = 0;  // output positions handed out so far
+    // store positions [p0, p1) of the current order to the sink, piece by piece
+    auto emit = [&](uint64_t p0, uint64_t p1) {
+        if (!out) {
+            pos += p1 - p0;
+            return;
+        }
+        hipEvent_t w0 = ev_get(), w1 = ev_get();
+        for (uint64_t p = p0; p < p1;) {
+            const uint64_t cnt = std::min(piece_rows, p1 - p);
+            CK(hipEventRecord(w0, stream));
+            write_output(intents_buf, extents_buf, p, cnt);
+            CK(hipEventRecord(w1, stream));
+            CK(hipStreamSynchronize(stream));
+            CK(hipEventElapsedTime(&ms, w0, w1));
+            out_ms += ms;
+            if (sink && sink(user, pos, cnt, intents_buf, extents_buf)) throw HipError{FCBO_ERR_STOPPED};
+            pos += cnt;
+            p += cnt;
+        }
+    };
+    // the one concept at store index idx, without an order pass
+    auto emit_concept = [&](uint32_t idx) {
+        if (out) {
+            ensure(dmem, perm, cap_perm, 1, 0, stream, mc);
+            hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, stream, perm, idx);
+            CK_LAUNCH();
+            have_perm = false;
+        }
+        emit(0, 1);
+    };
+    // per-level counts of the whole tree: level l >= 1 of a batch is level
+    // base + l - 1 of the tree
+    std::vector<uint64_t> lev_c, lev_t;
+    auto add_levels = [&](uint64_t base) {
+        for (size_t l = 1; l < lev.size(); ++l) {
+            const size_t at = base + l - 1;
+            if (at >= lev_c.size()) {
+                lev_c.resize(at + 1, 0);
+                lev_t.resize(at + 1, 0);
+            }
+            lev_c[at] += lev.concepts[l];
+            lev_t[at] += lev.tests[l];
+        }
+    };
+
+    // the root, its row, and its children as the first seed set
+    LevelCursor s;
+    {
+        hipEvent_t e0 = ev_get(), e1 = ev_get();
+        CK(hipEventRecord(e0, stream));
+        start_root(s);
+        run_levels(s, 1);
+        CK(hipEventRecord(e1, stream));
+        CK(hipStreamSynchronize(stream));
+        CK(hipEventElapsedTime(&ms, e0, e1));
+        loop_ms += ms;
+        lev_c.assign(1, 1);
+        lev_t.assign(1, lev.tests[0]);
+        emit_concept(0);
+        harvest_marks(st);
+    }
+    uint64_t total = 1, batches = 0, retries = 0, splits = 0, k_max = 0;
+    if (s.P) capture_seeds(1, s.P, (uint64_t)n, s.obj_hi, 1);
+    while (!seeds.empty()) {
+        const size_t si = seeds.size() - 1;
+        if (seeds[si].hi == 0) {
+            seeds[si].free_all(dmem);
+            seeds.pop_back();
+            continue;
+        }
+        const bool force_split = split_root_children && seeds[si].level == 1;
+        const uint64_t B = std::min(one_per_batch || force_split ? 1 : seeds[si].B, seeds[si].hi);
+        const uint64_t a = seeds[si].hi - B;
+        const Totals saved = tot;
+        hipEvent_t b0 = ev_get(), b1 = ev_get(), b2 = ev_get();
+        bool fits = !force_split;
+        if (fits) try {
+            CK(hipEventRecord(b0, stream));
+            LevelCursor bs = load_seeds(seeds[si], a, B);
+            run_levels(bs, ~0ull);
+            K = bs.lo;
+            have_result = true;
+            have_perm = false;
+            CK(hipEventRecord(b1, stream));
+            if (out) order_concepts();
+            CK(hipEventRecord(b2, stream));
+            CK(hipStreamSynchronize(stream));
+        } catch (const HipError &e) {
+            if (e.code != FCBO_ERR_OUT_OF_MEMORY && e.code != FCBO_ERR_LIMIT) throw;
+            drain();
+            harvest_marks(st);
+            tot = saved;
+            have_result = have_perm = false;
+            ++retries;
+            fits = false;
+        }
+        if (!fits) {
+            if (B > 1) {
+                seeds[si].B = (B + 1) / 2;
+                continue;
+            }
+            // A single seed whose subtree does not fit: its own row goes out and
+            // its children become the next seed set (in the output a subtree is
+            // its root, then its children's subtrees by descending attribute).
+            // Should this one level not fit either, the call fails.
+            hipEvent_t x0 = ev_get(), x1 = ev_get();
+            CK(hipEventRecord(x0, stream));
+            LevelCursor bs = load_seeds(seeds[si], a, 1);
+            const uint64_t child_obj_lo = bs.obj_hi;
+            run_levels(bs, 1);
+            CK(hipEventRecord(x1, stream));
+            CK(hipStreamSynchronize(stream));
+            CK(hipEventElapsedTime(&ms, x0, x1));
+            loop_ms += ms;
+            add_levels(seeds[si].level);
+            const uint64_t level = seeds[si].level;
+            seeds[si].hi = a;
+            ++splits;
+            ++total;
+            emit_concept(1);
+            harvest_marks(st);
+            if (bs.P) capture_seeds(2, bs.P, child_obj_lo, bs.obj_hi, level + 1);
+            continue;
+        }
+        CK(hipEventElapsedTime(&ms, b0, b1));
+        loop_ms += ms;
+        CK(hipEventElapsedTime(&ms, b1, b2));
+        order_ms += ms;
+        add_levels(seeds[si].level);
+        emit(1, K);  // the stand-in root at position 0 is not part of the batch
+        harvest_marks(st);
+        total += K - 1;
+        ++batches;
+        seeds[si].hi = a;
+        k_max = std::max(k_max, K);
+        if (2 * K <= k_max) seeds[si].B = 2 * B;
+    }
+    // the level log of the whole enumeration; the store holds only the last batch
+    lev.clear();
+    for (size_t l = 0; l < lev_c.size(); ++l) lev.push(lev_c[l], lev_t[l]);
+    have_result = have_perm = have_cover_counts = false;
+    have_levels = true;
+    K = 0;
+    fill_counts(st, total);
+    st.closure_kernel_ms = loop_ms;
+    st.sort_ms = order_ms;
+    st.output_ms = out_ms;
+    st.output_bytes = out ? total * 8 * ((intents_buf ? (uint64_t)wm : 0) + (extents_buf ? (uint64_t)wn : 0)) : 0;
+    st.batches = batches;
+    st.batch_retries = retries;
+    st.batch_splits = splits;
+    st.peak_device_bytes = dmem.peak;
+    st.enumerate_ms =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
 }
 
 void fcbo_context::order_concepts()
@@ -869,18 +1212,39 @@ void fcbo_context::write_output(uint64_t *intents_out, uint64_t *extents_out, ui
 // Algorithmic bytes of the last enumeration (the formula in fcbo.h, with the
 // row-local threshold of the class split: 4096 objects up to eight intent
 // words, else 64).
-uint64_t fcbo_context::model_bytes() const
+uint64_t fcbo_context::model_bytes(uint64_t k) const
 {
-    if (!have_result) return 0;
+    if (!k) return 0;
     const uint64_t W_M = (uint64_t)wm, W_N = (uint64_t)wn;
-    uint64_t b = K * (8 * W_M + 4 + 16);             // every concept read once as a parent
-    b += (local_objs + med_objs) * (4 + 8 * W_M);   // row-local parents: list entries and rows
-    b += big_parents * 8 * W_N;                      // larger parents: extent bitmap
-    b += big_nzw * 8;                                // their tests: non-zero column words
-    b += big_cobjs * 8 * W_M;                        // their children: rows of C
-    b += (K - 1) * (8 * W_M + 4 + 8) + 4 * sum_c;    // children written
+    uint64_t b = k * (8 * W_M + 4 + 16);             // every concept read once as a parent
+    b += (tot.local_objs + tot.med_objs) * (4 + 8 * W_M);   // row-local parents: list entries and rows
+    b += tot.big_parents * 8 * W_N;                      // larger parents: extent bitmap
+    b += tot.big_nzw * 8;                                // their tests: non-zero column words
+    b += tot.big_cobjs * 8 * W_M;                        // their children: rows of C
+    b += (k - 1) * (8 * W_M + 4 + 8) + 4 * tot.sum_c;    // children written
     b += (uint64_t)n * (8 * W_M + 4);                // the root
     return b;
+}
+
+// The counts of the last enumeration (K, tests, levels, classes, bytes).
+void fcbo_context::fill_counts(fcbo_stats &st, uint64_t k) const
+{
+    st.n_concepts = k;
+    st.model_bytes = model_bytes(k);
+    st.closure_tests = tot.tests;
+    st.item_pairs = tot.pairs;
+    st.n_levels = lev.size();
+    st.sum_child_objects = tot.sum_c;
+    st.local_parents = tot.local_parents;
+    st.local_parent_objects = tot.local_objs;
+    st.medium_parents = tot.med_parents;
+    st.medium_parent_objects = tot.med_objs;
+    st.big_parents = tot.big_parents;
+    st.big_tests = tot.big_tests;
+    st.big_scanned_objects = tot.big_scan;
+    st.big_nonzero_words = tot.big_nzw;
+    st.big_child_objects = tot.big_cobjs;
+    st.order_launches = order_launches;
 }
 
 // The context on the device: rows copied and masked, columns transposed.
@@ -1113,6 +1477,7 @@ const char *fcbo_error_string(int code)
     case FCBO_ERR_CAPACITY: return "output capacity too small";
     case FCBO_ERR_LIMIT: return "2^32 concepts or more (beyond the 32-bit concept indices)";
     case FCBO_ERR_SCRATCH: return "the work does not fit the static scratch of fcbo_enumerate_static";
+    case FCBO_ERR_STOPPED: return "the sink stopped the enumeration";
     default: return "unknown error";
     }
 }
@@ -1174,6 +1539,7 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
         e3 = ctx->ev_get();
         CK(hipEventRecord(e0, ctx->stream));
         const bool reuse = (flags & FCBO_REUSE_RESULT) && ctx->have_result;
+        ctx->dmem.peak = ctx->dmem.held;
         if (!reuse) ctx->enumerate_levels();
         CK(hipEventRecord(e1, ctx->stream));
         if (n_concepts_out) *n_concepts_out = ctx->K;
@@ -1209,22 +1575,9 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
         ctx->have_result = ctx->have_perm = false;
         return FCBO_ERR_OUT_OF_MEMORY;
     }
-    st.n_concepts = ctx->K;
-    st.model_bytes = ctx->model_bytes();
-    st.closure_tests = ctx->tests;
-    st.item_pairs = ctx->pairs;
-    st.n_levels = ctx->lev.size();
-    st.sum_child_objects = ctx->sum_c;
-    st.local_parents = ctx->local_parents;
-    st.local_parent_objects = ctx->local_objs;
-    st.medium_parents = ctx->med_parents;
-    st.medium_parent_objects = ctx->med_objs;
-    st.big_parents = ctx->big_parents;
-    st.big_tests = ctx->big_tests;
-    st.big_scanned_objects = ctx->big_scan;
-    st.big_nonzero_words = ctx->big_nzw;
-    st.big_child_objects = ctx->big_cobjs;
-    st.order_launches = ctx->order_launches;
+    ctx->fill_counts(st, ctx->have_result ? ctx->K : 0);
+    st.batches = 1;
+    st.peak_device_bytes = ctx->dmem.peak;
     if (rc == FCBO_OK)
         st.output_bytes = ctx->K * (uint64_t)ctx->wm * 8 + (extents_out ? ctx->K * (uint64_t)ctx->wn * 8 : 0);
     if (stats_out) *stats_out = st;
@@ -1265,22 +1618,9 @@ int fcbo_enumerate_static(const uint64_t *rows, int64_t n_objects, int64_t n_att
             c.write_output(intents_out, extents_out, 0, c.K);
         }
         CK(hipStreamSynchronize(stream));
-        st.n_concepts = c.K;
-        st.closure_tests = c.tests;
-        st.item_pairs = c.pairs;
-        st.n_levels = c.lev.size();
-        st.model_bytes = c.model_bytes();
-        st.sum_child_objects = c.sum_c;
-        st.local_parents = c.local_parents;
-        st.local_parent_objects = c.local_objs;
-        st.medium_parents = c.med_parents;
-        st.medium_parent_objects = c.med_objs;
-        st.big_parents = c.big_parents;
-        st.big_tests = c.big_tests;
-        st.big_scanned_objects = c.big_scan;
-        st.big_nonzero_words = c.big_nzw;
-        st.big_child_objects = c.big_cobjs;
-        st.order_launches = c.order_launches;
+        c.fill_counts(st, c.have_result ? c.K : 0);
+        st.batches = 1;
+        st.peak_device_bytes = c.dmem.region_used;
         if (rc == FCBO_OK)
             st.output_bytes = c.K * (uint64_t)c.wm * 8 + (extents_out ? c.K * (uint64_t)c.wn * 8 : 0);
     } catch (const HipError &e) {
@@ -1292,6 +1632,42 @@ int fcbo_enumerate_static(const uint64_t *rows, int64_t n_objects, int64_t n_att
     }
     if (stats_out) *stats_out = st;
     return rc;
+}
+
+int fcbo_enumerate_bounded(fcbo_context *ctx, uint64_t *intents_buf, uint64_t *extents_buf, uint64_t piece_rows,
+                           fcbo_sink_fn sink, void *user, uint32_t flags, uint64_t *n_concepts_out,
+                           fcbo_stats *stats_out)
+{
+    if (!ctx || (flags & ~(FCBO_PROFILE | FCBO_ONE_SUBTREE_PER_BATCH | FCBO_SPLIT_ROOT_CHILDREN)) ||
+        ((intents_buf || extents_buf) && piece_rows == 0))
+        return FCBO_ERR_INVALID_ARGUMENT;
+    fcbo_stats st;
+    memset(&st, 0, sizeof(st));
+    int rc = FCBO_OK;
+    try {
+        CK(hipSetDevice(ctx->device));
+        ctx->profile = (flags & FCBO_PROFILE) != 0;
+        ctx->enumerate_bounded(intents_buf, extents_buf, piece_rows, sink, user, flags, st);
+    } catch (const HipError &e) {
+        rc = e.code;
+    } catch (const std::bad_alloc &) {
+        rc = FCBO_ERR_OUT_OF_MEMORY;
+    }
+    if (rc != FCBO_OK) {
+        // nothing half-done stays: no result, no level counts, no work in flight
+        ctx->have_result = ctx->have_perm = ctx->have_cover_counts = ctx->have_levels = false;
+        ctx->K = 0;
+        for (int i = 0; i < fcbo_context::kSide; ++i)
+            if (ctx->aux[i]) (void)hipStreamSynchronize(ctx->aux[i]);
+        (void)hipStreamSynchronize(ctx->stream);
+        ctx->release_seeds();
+        ctx->marks.clear();
+        ctx->ev_used = 0;
+        return rc;
+    }
+    if (n_concepts_out) *n_concepts_out = st.n_concepts;
+    if (stats_out) *stats_out = st;
+    return FCBO_OK;
 }
 
 int fcbo_write_range(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_t *intents_out,
@@ -1392,7 +1768,7 @@ int fcbo_set_memory_limit(fcbo_context *ctx, uint64_t bytes)
 int fcbo_level_counts(const fcbo_context *ctx, uint64_t *concepts_per_level, uint64_t *tests_per_level,
                       uint64_t max_levels, uint64_t *n_levels_out)
 {
-    if (!ctx || !ctx->have_result) return FCBO_ERR_INVALID_ARGUMENT;
+    if (!ctx || !ctx->have_levels) return FCBO_ERR_INVALID_ARGUMENT;
     const uint64_t nl = ctx->lev.size();
     if (n_levels_out) *n_levels_out = nl;
     for (uint64_t i = 0; i < nl && i < max_levels; ++i) {

@@ -340,6 +340,21 @@ __global__ void __launch_bounds__(kBlock) k_fill_u64(uint64_t *p, uint64_t n, ui
         p[i] = v;
 }
 
+// dst[i] = src[i] - sub + add for i < n: extent-list offsets of a run of
+// concepts whose lists move to another place of the object store.
+__global__ void __launch_bounds__(kBlock) k_shift_offsets(const uint64_t *__restrict__ src, uint64_t n, uint64_t sub,
+                                                          uint64_t add, uint64_t *__restrict__ dst)
+{
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+        dst[i] = src[i] - sub + add;
+}
+
+// *p = v (one thread).
+__global__ void k_set_u32(uint32_t *p, uint32_t v)
+{
+    *p = v;
+}
+
 // Clear the bits past the last attribute in every row.
 __global__ void k_mask_rows(uint64_t *rows, int n, int wm, uint64_t tail_m)
 {

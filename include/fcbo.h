@@ -52,7 +52,8 @@ enum {
     FCBO_ERR_DEVICE = -3,           /* any other HIP runtime failure */
     FCBO_ERR_CAPACITY = -4,         /* output buffers hold fewer rows than concepts (or edges) */
     FCBO_ERR_LIMIT = -5,            /* 2^32 concepts or more: beyond the 32-bit concept indices */
-    FCBO_ERR_SCRATCH = -6           /* fcbo_enumerate_static: the work does not fit the static scratch */
+    FCBO_ERR_SCRATCH = -6,          /* fcbo_enumerate_static: the work does not fit the static scratch */
+    FCBO_ERR_STOPPED = -7           /* fcbo_enumerate_bounded: the sink asked to stop */
 };
 
 /* Bytes of the static device scratch of fcbo_enumerate_static (one per GPU). */
@@ -66,6 +67,12 @@ enum {
 /* fcbo_enumerate flags */
 #define FCBO_REUSE_RESULT 1u /* reuse the concepts of the previous call if any */
 #define FCBO_PROFILE 2u      /* time every kernel class with HIP events (fills kernel_ms) */
+
+/* fcbo_enumerate_bounded flags (besides FCBO_PROFILE) */
+#define FCBO_ONE_SUBTREE_PER_BATCH 4u /* test hook: every batch takes a single subtree, so the
+                                         batch path runs on any input */
+#define FCBO_SPLIT_ROOT_CHILDREN 8u   /* test hook: every child of the root is split one level
+                                         down as if its subtree did not fit */
 
 /* Kernel classes reported in fcbo_stats.kernel_ms / kernel_launches. */
 enum {
@@ -138,6 +145,11 @@ typedef struct {
     uint64_t order_launches;    /* kernel launches of the last output ordering */
     double kernel_ms[FCBO_K_NUM_CLASSES];       /* with FCBO_PROFILE only */
     uint64_t kernel_launches[FCBO_K_NUM_CLASSES];
+    uint64_t batches;           /* batches of sibling subtrees enumerated (1 for fcbo_enumerate) */
+    uint64_t batch_retries;     /* batches that hit the memory limit and were run again smaller */
+    uint64_t batch_splits;      /* single subtrees that did not fit and were split one level down */
+    uint64_t peak_device_bytes; /* most device memory the enumeration buffers held at once during
+                                   the call (buffers kept from earlier calls included) */
 } fcbo_stats;
 
 /*
@@ -238,6 +250,60 @@ int fcbo_copy_to_host(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_
  */
 int fcbo_cover_edges(fcbo_context *ctx, uint64_t *offsets_out, uint32_t *targets_out, uint64_t capacity,
                      uint64_t *n_edges_out, double *elapsed_ms);
+
+/*
+ * Receiver of the pieces of a bounded enumeration: rows [0, count) of the
+ * device buffers hold the concepts at output positions [first, first + count)
+ * (intents, and extents unless that buffer is NULL).  Pieces arrive in
+ * ascending order of first and cover every position once.  The context's
+ * stream has finished when the sink is called and the library touches neither
+ * buffer until it returns; the sink may read or copy them on any stream, but
+ * must be done with them when it returns.  Return 0 to go on, anything else to
+ * stop the enumeration.
+ */
+typedef int (*fcbo_sink_fn)(void *user, uint64_t first, uint64_t count, const uint64_t *intents,
+                            const uint64_t *extents);
+
+/*
+ * Enumerate like fcbo_enumerate in bounded device memory, handing the output
+ * to a sink piece by piece (page 1 section 6.1: when the concepts do not fit
+ * the device, move finished ones off it in batches while the search goes on;
+ * section 3.4 bounds the task memory).  In the output order every subtree of
+ * the CbO tree is one run of consecutive positions: a concept, then its
+ * children's subtrees by descending attribute.  So the root's children are
+ * taken in batches, largest attribute first; a batch's subtrees are
+ * enumerated level by level, ordered and written out, and the store is reused
+ * by the next batch.  A batch that hits the memory limit
+ * (fcbo_set_memory_limit) or a full device runs again with half as many
+ * subtrees; a single subtree that does not fit is split one level down (its
+ * root's row goes out, its children become the next run of batches).  After a
+ * batch that used less than half of the largest store so far the next one
+ * takes twice as many subtrees.  Device memory thus stays within the limit as
+ * long as one concept's children (one level) fit; the total concept count may
+ * exceed 2^32, the concepts of one batch may not.
+ *   intents_buf   piece_rows x ceil(M/64) words, device, or NULL
+ *   extents_buf   piece_rows x ceil(N/64) words, device, or NULL
+ *   piece_rows    rows per piece (>= 1 when a buffer is given)
+ *   sink, user    called once per piece; may be NULL.  With both buffers NULL
+ *                 nothing is ordered or written and the sink is not called
+ *                 (counts and statistics only).
+ *   flags         FCBO_PROFILE, FCBO_ONE_SUBTREE_PER_BATCH, FCBO_SPLIT_ROOT_CHILDREN
+ *   n_concepts_out receives K; may be NULL
+ *   stats_out     optional: counts as for fcbo_enumerate, summed over the
+ *                 batches; enumerate_ms = the call's host wall time (sink
+ *                 included), closure_kernel_ms / sort_ms / output_ms = device
+ *                 time of the level loops / order passes / output kernels;
+ *                 batches, batch_retries, batch_splits, peak_device_bytes
+ * Returns FCBO_OK, FCBO_ERR_INVALID_ARGUMENT, FCBO_ERR_OUT_OF_MEMORY (one
+ * concept's children do not fit), FCBO_ERR_STOPPED (the sink returned
+ * non-zero) or FCBO_ERR_DEVICE.  Afterwards the context holds no result
+ * (write_range, copy_to_host and cover_edges return FCBO_ERR_INVALID_ARGUMENT
+ * until the next fcbo_enumerate); fcbo_level_counts reports the whole
+ * enumeration.  After an error it reports nothing either.
+ */
+int fcbo_enumerate_bounded(fcbo_context *ctx, uint64_t *intents_buf, uint64_t *extents_buf, uint64_t piece_rows,
+                           fcbo_sink_fn sink, void *user, uint32_t flags, uint64_t *n_concepts_out,
+                           fcbo_stats *stats_out);
 
 /*
  * Cap the device memory the context's enumeration buffers may hold (bytes;

@@ -100,6 +100,9 @@ def test_null_arguments_are_rejected_without_a_device(lib):
     assert out.value is None
     lib.fcbo_enumerate.restype = ctypes.c_int
     assert lib.fcbo_enumerate(None, None, None, 0, 0, None, None) == fca.FCBO_ERR_INVALID_ARGUMENT
+    lib.fcbo_enumerate_bounded.restype = ctypes.c_int
+    assert lib.fcbo_enumerate_bounded(None, None, None, ctypes.c_uint64(1), None, None, 0, None,
+                                      None) == fca.FCBO_ERR_INVALID_ARGUMENT
     lib.fcbo_write_range.restype = ctypes.c_int
     assert lib.fcbo_write_range(None, ctypes.c_uint64(0), ctypes.c_uint64(0), None, None) == fca.FCBO_ERR_INVALID_ARGUMENT
     lib.fcbo_set_memory_limit.restype = ctypes.c_int
