@@ -23,6 +23,10 @@ Prints one JSON line.  `value` is concepts per second; beside it:
   * `host_stream`: the first rows of the ordered output streamed to pinned
     host memory through two device staging buffers (fcbo_copy_to_host), a
     PCIe-inclusive rate, never the headline value;
+  * `bounded`: the same enumeration in bounded device memory
+    (fcbo_enumerate_bounded under fcbo_set_memory_limit, by default a quarter
+    of what the unbounded step held), the whole output (intents and extent
+    bitmaps) handed to a no-op sink piece by piece;
   * `cpu_baseline`: the store-free CPU oracle over the whole workload on one
     pinned host core, run before the GPU is touched; `cpu_baseline_all_cores`
     the same search split over the host cores.
@@ -350,6 +354,13 @@ def main():
                     "process's cores, at most 16)")
     ap.add_argument("--cpu-bitmap-tests", type=int, default=2_000_000,
                     help="closure-test budget of the bitmap oracle's prefix (0: skip)")
+    ap.add_argument("--bounded-frac", type=float, default=0.25,
+                    help="bounded run: memory limit as a fraction of the unbounded step's peak (0: skip)")
+    ap.add_argument("--bounded-gib", type=float, default=0.0, help="bounded run: memory limit in GiB (overrides "
+                    "--bounded-frac)")
+    ap.add_argument("--bounded-extents", choices=("yes", "no"), default="yes")
+    ap.add_argument("--bounded-piece-rows", type=int, default=1 << 20)
+    ap.add_argument("--bounded-runs", type=int, default=2, help="bounded runs; the last one is reported")
     ap.add_argument("--hbm-probe-gib", type=float, default=4.0)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="run one device-to-device copy of this size first (counter calibration)")
@@ -517,6 +528,36 @@ def main():
             cover = {"error": str(err).splitlines()[0][:160]}
         print("[bench] cover edges: %s" % json.dumps(cover), file=sys.stderr, flush=True)
 
+    # the same enumeration in bounded device memory, every output row handed
+    # to a sink (not part of the step)
+    bounded = None
+    if args.bounded_gib > 0 or args.bounded_frac > 0:
+        ints = exts = None
+        torch.cuda.empty_cache()
+        peak = int(st0["peak_device_bytes"])
+        limit = int(args.bounded_gib * (1 << 30)) if args.bounded_gib > 0 else int(peak * args.bounded_frac)
+        ext_b = args.bounded_extents == "yes"
+        try:
+            ctx.set_memory_limit(limit)
+            for _ in range(max(1, args.bounded_runs)):
+                kb, stb = ctx.enumerate_bounded(lambda first, i, e: None, piece_rows=args.bounded_piece_rows,
+                                                intents=True, extents=ext_b)
+                assert kb == k
+            ms_b = stb["enumerate_ms"]
+            bounded = {"limit_bytes": limit, "unbounded_peak_bytes": peak, "peak_bytes": int(stb["peak_device_bytes"]),
+                       "extents_out": ext_b, "piece_rows": args.bounded_piece_rows,
+                       "output_bytes": int(stb["output_bytes"]), "batches": int(stb["batches"]),
+                       "retries": int(stb["batch_retries"]), "splits": int(stb["batch_splits"]),
+                       "ms": round(ms_b, 3), "concepts_per_s": round(k / (ms_b * 1e-3), 1),
+                       "closure_tests_per_s": round(stb["closure_tests"] / (ms_b * 1e-3), 1),
+                       "device_ms": {"level_loop": round(stb["closure_kernel_ms"], 3),
+                                     "order": round(stb["sort_ms"], 3), "output": round(stb["output_ms"], 3)},
+                       "timing": "host wall time of the last of %d calls, no-op sink" % max(1, args.bounded_runs)}
+        except (fca.FcboError, torch.OutOfMemoryError) as err:
+            bounded = {"limit_bytes": limit, "error": str(err).splitlines()[0][:160]}
+        ctx.set_memory_limit(0)
+        print("[bench] bounded: %s" % json.dumps(bounded), file=sys.stderr, flush=True)
+
     tests = st0["closure_tests"]
     out = {
         "metric": "concepts/sec and closure tests/sec at 1 GPU; % of HBM roofline",
@@ -548,6 +589,7 @@ def main():
         "cpu_baseline_bitmap_oracle": cpu.get("bitmap") if cpu else None,
         "cover_edges": cover,
         "host_stream": stream_host,
+        "bounded": bounded,
     }
     ctx.close()
     del ints, exts  # noqa: F821

@@ -190,6 +190,8 @@ struct BigStore {
 struct SeedSet {
     uint64_t count = 0, level = 0, obj_base = 0;
     uint64_t hi = 0, B = 0;  // seeds [0, hi) remain; the next batch takes up to B, ending at hi
+    uint64_t B_cap = 0;      // no batch larger than this (half of a size that did not fit)
+    std::vector<double> wsum;  // prefix sums of the seeds' weights (see enumerate_bounded)
     uint64_t cap_int = 0, cap_cur = 0, cap_loff = 0, cap_obj = 0;
     uint64_t *ints = nullptr;
     int32_t *cur = nullptr;
@@ -278,6 +280,7 @@ struct fcbo_context {
     bool have_result = false;
     bool have_perm = false;
     uint64_t K = 0, order_launches = 0;
+    uint64_t store_rows_seen = 0;  // concepts the store was being sized for, last seen by the level loop
     Totals tot;
     LevelLog lev;
 
@@ -336,10 +339,14 @@ struct fcbo_context {
     }
 
     uint64_t min_cap() const { return tiny ? 1 : 1024; }
-    // first size of a buffer that normally starts at `normal` elements
-    uint64_t start_size(uint64_t normal) const
+    // first size of a buffer that normally starts at `normal` elements of
+    // elem_bytes bytes; under a memory limit none starts above 1/64 of it
+    uint64_t start_size(uint64_t normal, uint64_t elem_bytes = 8) const
     {
-        return tiny ? 1 : fixed ? std::max<uint64_t>(64, normal / 64) : normal;
+        if (tiny) return 1;
+        if (fixed) return std::max<uint64_t>(64, normal / 64);
+        if (dmem.limit) return std::max<uint64_t>(64, std::min<uint64_t>(normal, dmem.limit / 64 / elem_bytes));
+        return normal;
     }
     void clear_words(uint64_t *p, uint64_t n)
     {
@@ -696,13 +703,13 @@ void fcbo_context::start_root(LevelCursor &s)
     tot = Totals{};
     const uint64_t rstride = 4 + (uint64_t)wm;
     if (!huge.tasks) {
-        if (bm) ensure_huge_tests(start_size(1u << 16));
-        else huge.ensure_tests(dmem, start_size(1u << 20), stream, mc);
+        if (bm) ensure_huge_tests(start_size(1u << 16, 8 * (4 + (uint64_t)wm + (uint64_t)nchunk())));
+        else huge.ensure_tests(dmem, start_size(1u << 20, 32), stream, mc);
     }
-    if (bm && !huge.bmp) ensure(dmem, huge.bmp, huge.cap_bmp, (uint64_t)wn * start_size(64), 0, stream, 1);
-    if (!mrec) ensure(dmem, mrec, cap_mrec, rstride * start_size(1u << 18), 0, stream, 1);
-    if (!wrec) ensure(dmem, wrec, cap_wrec, rstride * start_size(1u << 16), 0, stream, 1);
-    if (!lrec) ensure_local_records(tiny ? kWave : start_size(1u << 21));
+    if (bm && !huge.bmp) ensure(dmem, huge.bmp, huge.cap_bmp, (uint64_t)wn * start_size(64, 8 * (uint64_t)wn), 0, stream, 1);
+    if (!mrec) ensure(dmem, mrec, cap_mrec, rstride * start_size(1u << 18, 8 * rstride), 0, stream, 1);
+    if (!wrec) ensure(dmem, wrec, cap_wrec, rstride * start_size(1u << 16, 8 * rstride), 0, stream, 1);
+    if (!lrec) ensure_local_records(tiny ? kWave : start_size(1u << 21, 8 * rstride));
     s = LevelCursor{};
     s.P = 1;
     s.obj_hi = (uint64_t)n;
@@ -725,6 +732,7 @@ void fcbo_context::run_levels(LevelCursor &s, uint64_t max_levels)
     const uint64_t rstride = 4 + (uint64_t)wm;
     uint64_t lo = s.lo, P = s.P, obj_hi = s.obj_hi, next_mid = s.next_mid, next_huge = s.next_huge;
     for (uint64_t done = 0; P > 0 && done < max_levels; ++done) {
+        store_rows_seen = lo + P;
         if (lo + P >= (1ull << 32)) throw HipError{FCBO_ERR_LIMIT};  // concept indices are 32-bit
         // every level adds an attribute to the intent, so there are at most M + 1
         if (lev.size() > (size_t)m + 1) throw HipError{FCBO_ERR_DEVICE};
@@ -819,6 +827,7 @@ void fcbo_context::run_levels(LevelCursor &s, uint64_t max_levels)
             // nothing if it had to grow
             const uint64_t k_end = lo + P + n_children;
             const uint64_t keep_k = lo + P;
+            store_rows_seen = k_end;
             // first-child offsets (u32) of this level already wrapped if so
             if (k_end >= (1ull << 32)) throw HipError{FCBO_ERR_LIMIT};
             const bool had_room = k_end <= A.child_cap && obj_hi + n_objs <= A.obj_cap;
@@ -882,7 +891,7 @@ void fcbo_context::capture_seeds(uint64_t first, uint64_t count, uint64_t obj_lo
     const uint64_t mc = min_cap();
     seeds.emplace_back();
     SeedSet &S = seeds.back();
-    S.count = S.hi = S.B = count;
+    S.count = S.hi = S.B = S.B_cap = count;
     S.level = level;
     S.obj_base = obj_lo;
     ensure(dmem, S.ints, S.cap_int, count * wm, 0, stream, mc);
@@ -904,6 +913,14 @@ void fcbo_context::capture_seeds(uint64_t first, uint64_t count, uint64_t obj_lo
     for (uint64_t i = 1; i < count; ++i)
         if (h_cur[i] <= h_cur[i - 1]) throw HipError{FCBO_ERR_DEVICE};
     if (S.h_loff[0] != obj_lo || S.h_loff[count] != obj_hi) throw HipError{FCBO_ERR_DEVICE};
+    // A seed's weight, the size of the context its subtree is searched in
+    // (its objects times the attributes above its cursor), stands in for the
+    // subtree's size when batches are sized.
+    S.wsum.assign(count + 1, 0.0);
+    for (uint64_t i = 0; i < count; ++i) {
+        const double objs_i = (double)std::max<uint64_t>(1, S.h_loff[i + 1] - S.h_loff[i]);
+        S.wsum[i + 1] = S.wsum[i] + objs_i * (double)(m - h_cur[i]);
+    }
 }
 
 void fcbo_context::release_seeds()
@@ -1023,7 +1040,23 @@ void fcbo_context::enumerate_bounded(uint64_t *intents_buf, uint64_t *extents_bu
         emit_concept(0);
         harvest_marks(st);
     }
-    uint64_t total = 1, batches = 0, retries = 0, splits = 0, k_max = 0;
+    uint64_t total = 1, batches = 0, retries = 0, splits = 0;
+    // Batch sizing, once a batch has failed: concepts per unit of seed weight,
+    // measured on the last batch that fitted, predicts a batch's concepts, and
+    // a batch aims at 70% of the smallest store size at which one failed.
+    double k_per_w = 0;
+    uint64_t k_fail = ~0ull;
+    auto predict = [&](SeedSet &S) {
+        if (k_per_w <= 0 || k_fail == ~0ull || S.hi == 0) return;
+        const double budget = 0.7 * (double)k_fail;
+        uint64_t lo = 1, hi = std::min(S.hi, S.B_cap);
+        while (lo < hi) {  // the largest batch within the budget
+            const uint64_t mid = (lo + hi + 1) / 2;
+            if ((S.wsum[S.hi] - S.wsum[S.hi - mid]) * k_per_w <= budget) lo = mid;
+            else hi = mid - 1;
+        }
+        S.B = lo;
+    };
     if (s.P) capture_seeds(1, s.P, (uint64_t)n, s.obj_hi, 1);
     while (!seeds.empty()) {
         const size_t si = seeds.size() - 1;
@@ -1059,8 +1092,10 @@ void fcbo_context::enumerate_bounded(uint64_t *intents_buf, uint64_t *extents_bu
             fits = false;
         }
         if (!fits) {
+            k_fail = std::min(k_fail, store_rows_seen);
             if (B > 1) {
-                seeds[si].B = (B + 1) / 2;
+                seeds[si].B = seeds[si].B_cap = (B + 1) / 2;
+                predict(seeds[si]);
                 continue;
             }
             // A single seed whose subtree does not fit: its own row goes out and
@@ -1083,7 +1118,10 @@ void fcbo_context::enumerate_bounded(uint64_t *intents_buf, uint64_t *extents_bu
             ++total;
             emit_concept(1);
             harvest_marks(st);
-            if (bs.P) capture_seeds(2, bs.P, child_obj_lo, bs.obj_hi, level + 1);
+            if (bs.P) {
+                capture_seeds(2, bs.P, child_obj_lo, bs.obj_hi, level + 1);
+                predict(seeds.back());
+            }
             continue;
         }
         CK(hipEventElapsedTime(&ms, b0, b1));
@@ -1096,8 +1134,8 @@ void fcbo_context::enumerate_bounded(uint64_t *intents_buf, uint64_t *extents_bu
         total += K - 1;
         ++batches;
         seeds[si].hi = a;
-        k_max = std::max(k_max, K);
-        if (2 * K <= k_max) seeds[si].B = 2 * B;
+        k_per_w = (double)(K - 1) / std::max(1e-9, seeds[si].wsum[a + B] - seeds[si].wsum[a]);
+        predict(seeds[si]);
     }
     // the level log of the whole enumeration; the store holds only the last batch
     lev.clear();

@@ -276,9 +276,11 @@ typedef int (*fcbo_sink_fn)(void *user, uint64_t first, uint64_t count, const ui
  * by the next batch.  A batch that hits the memory limit
  * (fcbo_set_memory_limit) or a full device runs again with half as many
  * subtrees; a single subtree that does not fit is split one level down (its
- * root's row goes out, its children become the next run of batches).  After a
- * batch that used less than half of the largest store so far the next one
- * takes twice as many subtrees.  Device memory thus stays within the limit as
+ * root's row goes out, its children become the next run of batches).  Once a
+ * batch has failed, batches are sized from the concepts per unit of seed
+ * weight (objects times the attributes above the cursor) of the last batch
+ * that fitted, aiming at 70% of the smallest store size at which one failed,
+ * and never above half a size that failed in the same run.  Device memory thus stays within the limit as
  * long as one concept's children (one level) fit; the total concept count may
  * exceed 2^32, the concepts of one batch may not.
  *   intents_buf   piece_rows x ceil(M/64) words, device, or NULL
