@@ -36,6 +36,7 @@ FCBO_TINY_BUFFERS = 2
 FCBO_REUSE_RESULT = 1
 FCBO_PROFILE = 2
 FCBO_ONE_SUBTREE_PER_BATCH = 4
+FCBO_TASK_POOL = 16
 FCBO_SPLIT_ROOT_CHILDREN = 8
 
 KERNEL_CLASSES = ("count", "test_local", "test_medium", "test_big", "scan", "write_local", "write_medium",
@@ -370,9 +371,9 @@ class Context:
         except Exception:
             pass
 
-    def count(self) -> int:
+    def count(self, pool: bool = False) -> int:
         """Enumerate (keeping the result in the context) and return K."""
-        rc, k, _ = fcbo_enumerate(self.handle, 0, 0, 0, 0)
+        rc, k, _ = fcbo_enumerate(self.handle, 0, 0, 0, FCBO_TASK_POOL if pool else 0)
         assert rc == FCBO_ERR_CAPACITY
         return k
 
@@ -485,8 +486,8 @@ class Context:
     def set_memory_limit(self, nbytes: int) -> None:
         fcbo_set_memory_limit(self.handle, nbytes)
 
-    def enumerate(self, extents: bool = True, profile: bool = False) -> Result:
-        k = self.count()
+    def enumerate(self, extents: bool = True, profile: bool = False, pool: bool = False) -> Result:
+        k = self.count(pool)
         ints, exts = self.alloc_outputs(k, extents)
         flags = FCBO_REUSE_RESULT | (FCBO_PROFILE if profile else 0)
         rc, k2, st = self.enumerate_into(ints, exts, flags)

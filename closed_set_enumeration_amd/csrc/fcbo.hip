@@ -275,6 +275,23 @@ struct fcbo_context {
     // seed sets of a bounded enumeration, the deepest last
     std::vector<SeedSet> seeds;
 
+    // task pool: the subtrees of the concepts with at most 64 objects
+    bool pool_active = false;  // the level loop leaves such parents to the pool
+    bool pool_result = false;  // the last result came from the level loop and the pool
+    uint64_t K_sync = 0, n_pool = 0;  // concepts from the level loop, from the pool
+    uint64_t pool_cap = 0;            // pool slots of the last run
+    LevelLog lev_sync;                // the level loop's levels, walked by the order pass
+    uint64_t cap_pint = 0, cap_prec = 0, cap_desc = 0, cap_towner = 0, cap_toff = 0, cap_tdepth = 0;
+    uint64_t cap_pctr = 0, cap_levlo = 0, cap_pstat = 0;
+    uint64_t *p_int = nullptr;        // pool slots: intents
+    PoolRec *p_rec = nullptr;         // pool slots: records
+    uint32_t *desc = nullptr;         // concepts below each task
+    uint32_t *t_owner = nullptr, *t_off = nullptr;  // per pool concept: task, offset in its subtree
+    uint8_t *t_depth = nullptr;       // per pool concept: levels below the task
+    uint64_t *pool_ctr = nullptr;     // POOL_* counters
+    uint64_t *d_levlo = nullptr;      // the level loop's level starts, for the counts
+    uint64_t *pstat = nullptr;        // per-level and total counts
+
     // result of the last enumeration
     bool have_levels = false;  // lev holds the per-level counts of a complete enumeration
     bool have_result = false;
@@ -388,6 +405,9 @@ struct fcbo_context {
         dfree(dmem, ctable, cap_ctable); dfree(dmem, ccount, cap_ccount); dfree(dmem, coff, cap_coff);
         dfree(dmem, cbig, cap_cbig); dfree(dmem, cctr, cap_cctr);
         release_seeds();
+        dfree(dmem, p_int, cap_pint); dfree(dmem, p_rec, cap_prec); dfree(dmem, desc, cap_desc);
+        dfree(dmem, t_owner, cap_towner); dfree(dmem, t_off, cap_toff); dfree(dmem, t_depth, cap_tdepth);
+        dfree(dmem, pool_ctr, cap_pctr); dfree(dmem, d_levlo, cap_levlo); dfree(dmem, pstat, cap_pstat);
         for (int b = 0; b < 2; ++b) {
             dfree(dmem, hs_int[b], cap_hs_int[b]);
             dfree(dmem, hs_ext[b], cap_hs_ext[b]);
@@ -457,6 +477,7 @@ struct fcbo_context {
         A.counters_next = counters + (uint64_t)(1 - ctr) * CNT_N;
         A.child_cap = std::min(std::min(cap_int / (uint64_t)wm, cap_cur), cap_loff ? cap_loff - 1 : 0);
         A.obj_cap = cap_o > kObjSlack ? cap_o - kObjSlack : 0;  // the output kernel reads past the last list
+        A.pool = pool_active ? 1 : 0;
         return A;
     }
 
@@ -497,7 +518,8 @@ struct fcbo_context {
     }
     void start_root(LevelCursor &s);
     void run_levels(LevelCursor &s, uint64_t max_levels);
-    void enumerate_levels();
+    void enumerate_levels(bool pool = false);
+    void run_pool(uint64_t K0, uint64_t obj0);
     void enumerate_bounded(uint64_t *intents_buf, uint64_t *extents_buf, uint64_t piece_rows, fcbo_sink_fn sink,
                            void *user, uint32_t flags, fcbo_stats &st);
     void capture_seeds(uint64_t first, uint64_t count, uint64_t obj_lo, uint64_t obj_hi, uint64_t level);
@@ -674,6 +696,36 @@ LevelFns pick_level_fns(int wm)
     }
 }
 
+static_assert(POOL_CTR_N <= CNT_N, "the pool's counters are read through the level counters' host buffer");
+
+typedef void (*pool_fn)(fcbo_context *, const PoolArgs &);
+
+template <int WMC>
+void launch_pool(fcbo_context *c, const PoolArgs &PA)
+{
+    // as many workgroups as are resident at once: the tasks are taken from a
+    // counter, so more would only queue behind them
+    int per_cu = 1;
+    CK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pool<WMC>, kWave * kPoolWaves, 0));
+    const unsigned g = (unsigned)std::max<uint64_t>(1, (uint64_t)c->n_cu * std::max(1, per_cu));
+    hipLaunchKernelGGL(k_pool<WMC>, dim3(g), dim3(kWave * kPoolWaves), 0, c->stream, PA);
+    CK_LAUNCH();
+}
+
+pool_fn pick_pool_fn(int wm)
+{
+    switch (wm) {
+    case 1: return launch_pool<1>;
+    case 2: return launch_pool<2>;
+    case 3: return launch_pool<3>;
+    case 4: return launch_pool<4>;
+    case 5: return launch_pool<5>;
+    case 6: return launch_pool<6>;
+    case 7: return launch_pool<7>;
+    default: return launch_pool<8>;
+    }
+}
+
 }  // namespace
 
 // Reset the result and run the root: its intent G' and extent G at store
@@ -683,7 +735,7 @@ void fcbo_context::start_root(LevelCursor &s)
     const uint64_t mc = min_cap();
     const bool bm = use_bitmaps();
     // nothing of an earlier result survives a failure part-way through
-    have_result = have_perm = have_cover_counts = have_levels = false;
+    have_result = have_perm = have_cover_counts = have_levels = pool_result = false;
     K = 0;
     ensure(dmem, intents, cap_int, (uint64_t)wm * 1024, 0, stream, mc);
     ensure(dmem, cursor, cap_cur, 1024, 0, stream, mc);
@@ -850,14 +902,178 @@ void fcbo_context::run_levels(LevelCursor &s, uint64_t max_levels)
     }
 }
 
-void fcbo_context::enumerate_levels()
+void fcbo_context::enumerate_levels(bool pool)
 {
+    if (pool && wm > 8) throw HipError{FCBO_ERR_INVALID_ARGUMENT};  // the pool keeps intents of <= 8 words
     LevelCursor s;
-    start_root(s);
-    run_levels(s, ~0ull);
+    pool_active = pool;
+    pool_result = false;
+    try {
+        start_root(s);
+        run_levels(s, ~0ull);
+    } catch (...) {
+        pool_active = false;
+        throw;
+    }
+    pool_active = false;
     K = s.lo;
+    if (pool) run_pool(s.lo, s.obj_hi);
     have_result = have_levels = true;
     have_perm = false;
+}
+
+// The task pool: every concept of the store [0, K0) with at most 64 objects is
+// a task whose subtree k_pool enumerates; the pool's concepts then join the
+// store after it (lists from obj0 on), and the counts are taken over the whole
+// store.
+void fcbo_context::run_pool(uint64_t K0, uint64_t obj0)
+{
+    const uint64_t mc = min_cap();
+    pool_fn fn = pick_pool_fn(wm);
+    ensure(dmem, desc, cap_desc, K0, 0, stream, mc);
+    ensure(dmem, pool_ctr, cap_pctr, POOL_CTR_N, 0, stream, 1);
+    uint64_t cap = std::max<uint64_t>(pool_cap, tiny ? (uint64_t)kWave : start_size(1u << 22, 8 * (uint64_t)wm + 24));
+    uint64_t slots = 0;
+    for (int attempt = 0;; ++attempt) {
+        if (attempt > 48) throw HipError{FCBO_ERR_DEVICE};
+        ensure(dmem, p_int, cap_pint, cap * wm, 0, stream, mc);
+        ensure(dmem, p_rec, cap_prec, cap, 0, stream, mc);
+        clear_words(pool_ctr, POOL_CTR_N);
+        PoolArgs PA;
+        PA.rows = rows;
+        PA.intents = intents;
+        PA.cursor = cursor;
+        PA.loff = loff;
+        PA.objs = objs;
+        PA.K = K0;
+        PA.m = (int)m;
+        PA.wm = wm;
+        PA.tail_m = tail_m;
+        PA.ctr = pool_ctr;
+        PA.cap = cap;
+        PA.p_int = p_int;
+        PA.p_rec = p_rec;
+        PA.desc = desc;
+        hipEvent_t b = prof_begin();
+        fn(this, PA);
+        prof_end(FCBO_K_TEST_LOCAL, b);
+        CK(hipMemcpyAsync(h_counters, pool_ctr, POOL_CTR_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+        CK(hipStreamSynchronize(stream));
+        if (h_counters[POOL_ERROR]) throw HipError{FCBO_ERR_DEVICE};
+        if (!h_counters[POOL_OVERFLOW]) {
+            slots = h_counters[POOL_SLOTS];
+            break;
+        }
+        cap *= 2;  // the slots ran out: everything again with twice as many
+    }
+    pool_cap = cap;
+    // dense store indices and list offsets of the used slots
+    ensure(dmem, nchild, cap_nch, slots, 0, stream, mc);
+    ensure(dmem, nobj, cap_nob, slots, 0, stream, mc);
+    ensure(dmem, cbase, cap_cb, slots + 1, 0, stream, mc);
+    ensure(dmem, obase, cap_ob, slots + 1, 0, stream, mc);
+    hipEvent_t b = prof_begin();
+    {
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(slots, kBlock)));
+        hipLaunchKernelGGL(k_pool_flags, dim3(g), dim3(kBlock), 0, stream, (const PoolRec *)p_rec, slots, nchild, nobj);
+        CK_LAUNCH();
+    }
+    scan(nchild, nobj, nullptr, slots, slots, cbase, obase, pool_ctr + POOL_TOT_N, pool_ctr + POOL_TOT_OBJ);
+    prof_end(FCBO_K_SCAN, b);
+    CK(hipMemcpyAsync(h_counters, pool_ctr, POOL_CTR_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+    CK(hipStreamSynchronize(stream));
+    const uint64_t np = h_counters[POOL_TOT_N], nob = h_counters[POOL_TOT_OBJ];
+    const uint64_t kt = K0 + np;
+    if (kt >= (1ull << 32)) throw HipError{FCBO_ERR_LIMIT};
+    ensure(dmem, intents, cap_int, kt * wm, K0 * wm, stream, mc);
+    ensure(dmem, cursor, cap_cur, kt, K0, stream, mc);
+    ensure(dmem, loff, cap_loff, kt + 1, K0 + 1, stream, mc);
+    ensure(dmem, objs, cap_o, obj0 + nob + kObjSlack, obj0, stream, mc);
+    ensure(dmem, fchild, cap_fch, kt + 1, K0 + 1, stream, mc);
+    ensure(dmem, t_owner, cap_towner, std::max<uint64_t>(1, np), 0, stream, mc);
+    ensure(dmem, t_off, cap_toff, std::max<uint64_t>(1, np), 0, stream, mc);
+    ensure(dmem, t_depth, cap_tdepth, std::max<uint64_t>(1, np), 0, stream, mc);
+    b = prof_begin();
+    {
+        PoolCommitArgs C;
+        C.rec = p_rec;
+        C.p_int = p_int;
+        C.dense = cbase;
+        C.ooff = obase;
+        C.n = slots;
+        C.K0 = K0;
+        C.obj0 = obj0;
+        C.n_pool = np;
+        C.n_obj = nob;
+        C.wm = wm;
+        C.intents = intents;
+        C.cursor = cursor;
+        C.loff = loff;
+        C.objs = objs;
+        C.t_owner = t_owner;
+        C.t_off = t_off;
+        C.t_depth = t_depth;
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(slots, kBlock)));
+        hipLaunchKernelGGL(k_pool_commit, dim3(g), dim3(kBlock), 0, stream, C);
+        CK_LAUNCH();
+        // the pool's concepts have no children in the store (empty ranges)
+        if (np) {
+            const unsigned gf = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(np, kBlock)));
+            hipLaunchKernelGGL(k_fill_u32, dim3(gf), dim3(kBlock), 0, stream, fchild + K0 + 1, np, (uint32_t)K0);
+            CK_LAUNCH();
+        }
+    }
+    prof_end(FCBO_K_WRITE_LOCAL, b);
+    K_sync = K0;
+    n_pool = np;
+    K = kt;
+    // counts over the whole store; the level loop's levels stay for the order pass
+    lev_sync = lev;
+    const int nlev = (int)lev_sync.size();
+    const int nbins = (int)m + 2;
+    ensure(dmem, d_levlo, cap_levlo, (uint64_t)nlev + 1, 0, stream, 1);
+    ensure(dmem, pstat, cap_pstat, 2 * (uint64_t)nbins + POOLSTAT_N, 0, stream, 1);
+    std::vector<uint64_t> h_lo(lev_sync.lo, lev_sync.lo + nlev + 1);
+    CK(hipMemcpyAsync(d_levlo, h_lo.data(), (nlev + 1) * sizeof(uint64_t), hipMemcpyHostToDevice, stream));
+    clear_words(pstat, 2 * (uint64_t)nbins + POOLSTAT_N);
+    {
+        PoolStatsArgs S;
+        S.intents = intents;
+        S.cursor = cursor;
+        S.loff = loff;
+        S.K = kt;
+        S.K0 = K0;
+        S.m = (int)m;
+        S.wm = wm;
+        S.nlev = nlev;
+        S.nbins = nbins;
+        S.mid_max = kMidMax;
+        S.tail_m = tail_m;
+        S.lev_lo = d_levlo;
+        S.t_owner = t_owner;
+        S.t_depth = t_depth;
+        S.out = pstat;
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(4096, div_up(kt, kBlock)));
+        hipLaunchKernelGGL(k_pool_stats, dim3(g), dim3(kBlock), 2 * (size_t)nbins * sizeof(uint64_t), stream, S);
+        CK_LAUNCH();
+    }
+    std::vector<uint64_t> h_stat(2 * (size_t)nbins + POOLSTAT_N);
+    CK(hipMemcpyAsync(h_stat.data(), pstat, h_stat.size() * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+    CK(hipStreamSynchronize(stream));
+    int last = 0;
+    for (int l = 0; l < nbins; ++l)
+        if (h_stat[l]) last = l;
+    lev.clear();
+    for (int l = 0; l <= last; ++l) lev.push(h_stat[l], h_stat[nbins + l]);
+    const uint64_t *sums = h_stat.data() + 2 * nbins;
+    tot.tests = sums[POOLSTAT_TESTS];
+    tot.pairs = sums[POOLSTAT_PAIRS];
+    tot.sum_c = sums[POOLSTAT_SUMC];
+    tot.local_parents = sums[POOLSTAT_LOCAL];
+    tot.local_objs = sums[POOLSTAT_LOCAL_OBJS];
+    tot.med_parents = sums[POOLSTAT_MID];
+    tot.med_objs = sums[POOLSTAT_MID_OBJS];
+    pool_result = true;
 }
 
 // Add the kernel times recorded since the last harvest to st (after the
@@ -1162,8 +1378,12 @@ void fcbo_context::order_concepts()
     const uint64_t mc = min_cap();
     ensure(dmem, rank, cap_rank, K, 0, stream, mc);
     ensure(dmem, perm, cap_perm, K, 0, stream, mc);
-    const size_t nlev = lev.size();
-    const uint64_t *lev_concepts = lev.concepts, *lev_lo = lev.lo;
+    // with the task pool the levels are the level loop's; the pool's concepts
+    // are placed after them from their tasks' positions
+    const LevelLog &L = pool_result ? lev_sync : lev;
+    const uint32_t *dsc = pool_result ? desc : nullptr;
+    const size_t nlev = L.size();
+    const uint64_t *lev_concepts = L.concepts, *lev_lo = L.lo;
     auto grid = [](uint64_t n) { return (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(n, kBlock))); };
     auto wgrid = [](uint64_t n) {
         return (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(n, kWavesPerBlock)));
@@ -1175,10 +1395,10 @@ void fcbo_context::order_concepts()
     for (size_t l = nlev; l-- > 0;) {  // sizes, deepest level first
         if (wide_level(l))
             hipLaunchKernelGGL(k_subtree_size_wave, dim3(wgrid(lev_concepts[l])), dim3(kBlock), 0, stream,
-                               (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
+                               (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank, dsc);
         else
             hipLaunchKernelGGL(k_subtree_size, dim3(grid(lev_concepts[l])), dim3(kBlock), 0, stream,
-                               (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
+                               (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank, dsc);
         CK_LAUNCH();
         ++order_launches;
     }
@@ -1189,6 +1409,12 @@ void fcbo_context::order_concepts()
         else
             hipLaunchKernelGGL(k_child_position, dim3(grid(lev_concepts[l])), dim3(kBlock), 0, stream,
                                (const uint32_t *)fchild, lev_lo[l], lev_concepts[l], rank);
+        CK_LAUNCH();
+        ++order_launches;
+    }
+    if (pool_result && n_pool) {
+        hipLaunchKernelGGL(k_tail_position, dim3(grid(n_pool)), dim3(kBlock), 0, stream, (const uint32_t *)t_owner,
+                           (const uint32_t *)t_off, n_pool, K_sync, rank);
         CK_LAUNCH();
         ++order_launches;
     }
@@ -1561,7 +1787,8 @@ int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs
 int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_out, uint64_t capacity,
                    uint32_t flags, uint64_t *n_concepts_out, fcbo_stats *stats_out)
 {
-    if (!ctx || (flags & ~(FCBO_REUSE_RESULT | FCBO_PROFILE))) return FCBO_ERR_INVALID_ARGUMENT;
+    if (!ctx || (flags & ~(FCBO_REUSE_RESULT | FCBO_PROFILE | FCBO_TASK_POOL))) return FCBO_ERR_INVALID_ARGUMENT;
+    if ((flags & FCBO_TASK_POOL) && ctx->m > 512) return FCBO_ERR_INVALID_ARGUMENT;
     fcbo_stats st;
     memset(&st, 0, sizeof(st));
     hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr, e3 = nullptr;
@@ -1578,7 +1805,7 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
         CK(hipEventRecord(e0, ctx->stream));
         const bool reuse = (flags & FCBO_REUSE_RESULT) && ctx->have_result;
         ctx->dmem.peak = ctx->dmem.held;
-        if (!reuse) ctx->enumerate_levels();
+        if (!reuse) ctx->enumerate_levels((flags & FCBO_TASK_POOL) != 0);
         CK(hipEventRecord(e1, ctx->stream));
         if (n_concepts_out) *n_concepts_out = ctx->K;
         if (!intents_out || capacity < ctx->K) {

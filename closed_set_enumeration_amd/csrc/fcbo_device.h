@@ -144,6 +144,8 @@ struct LevelArgs {
     int chunk;             // parents per chunk of the local test (at most LocalCfg::kChunk)
     uint64_t child_cap;    // concepts the store can hold (intents, cursors, list offsets)
     uint64_t obj_cap;      // list entries the store can hold
+    int pool;              // parents with at most 64 objects are left to the task pool (no
+                           // tests, no children here)
 };
 
 // ---------------------------------------------------------------------------
@@ -616,7 +618,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads)
             o0 = A.loff[c];
             sz = A.loff[c + 1] - o0;
             y = A.cursor[c];
-            act = sz <= (uint64_t)kSmallMax;
+            act = sz <= (uint64_t)kSmallMax && !A.pool;
             a = act ? (int)sz : 0;
         }
         {
@@ -636,7 +638,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads)
             if (lane < nq)
                 for (int u = 0; u < wm; ++u) nt += (uint32_t)__popcll(~SB[lane * wm + u] & above_mask(y, u));
             const bool is_huge = lane < nq && sz > (uint64_t)A.mid_max;
-            const bool is_mid = lane < nq && !is_huge && !act;
+            const bool is_mid = lane < nq && !is_huge && sz > (uint64_t)kSmallMax;
             // per chunk the sums but the last fit 32 bits (at most 64 parents of
             // at most M tests and mid_max objects each)
             n_tests += wave_sum(nt);
@@ -662,7 +664,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads)
                 const uint64_t wpos = wave_slot(wb, &A.counters[CNT_MIDW]);
                 if (is_wide) A.mid_idx[A.P - 1 - wpos] = (uint32_t)(p0 + lane);
             }
-            if (is_mid || is_huge) {
+            if (lane < nq && !act) {  // mid and huge parents, and those left to the pool
                 A.nchild[p0 + lane] = 0;
                 A.nobj[p0 + lane] = 0;
             }
@@ -2063,13 +2065,16 @@ __global__ void __launch_bounds__(kScanBlocks) k_scan_small(const uint32_t *__re
 // are stored contiguously by ascending attribute, as [fchild[c], fchild[c+1]).
 
 // Subtree sizes of the concepts [lo, lo + P); their children's sizes are final.
+// With the task pool, desc (when given) adds the concepts the pool found below
+// each task.
 __global__ void __launch_bounds__(kBlock) k_subtree_size(const uint32_t *__restrict__ fchild, uint64_t lo,
-                                                          uint64_t P, uint32_t *__restrict__ rank)
+                                                          uint64_t P, uint32_t *__restrict__ rank,
+                                                          const uint32_t *__restrict__ desc)
 {
     for (uint64_t p = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; p < P; p += (uint64_t)gridDim.x * blockDim.x) {
         const uint64_t c = lo + p;
         const uint32_t k0 = fchild[c], k1 = fchild[c + 1];
-        uint32_t s = 1;
+        uint32_t s = 1 + (desc ? desc[c] : 0u);
 #pragma unroll 4
         for (uint32_t k = k0; k < k1; ++k) s += rank[k];
         rank[c] = s;
@@ -2098,7 +2103,8 @@ __global__ void __launch_bounds__(kBlock) k_child_position(const uint32_t *__res
 // lanes; positions come from an exclusive scan of the sizes taken in
 // descending child order, 64 children a step.
 __global__ void __launch_bounds__(kBlock) k_subtree_size_wave(const uint32_t *__restrict__ fchild, uint64_t lo,
-                                                               uint64_t P, uint32_t *__restrict__ rank)
+                                                               uint64_t P, uint32_t *__restrict__ rank,
+                                                               const uint32_t *__restrict__ desc)
 {
     const int lane = lane_id();
     for (uint64_t p = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; p < P;
@@ -2108,7 +2114,7 @@ __global__ void __launch_bounds__(kBlock) k_subtree_size_wave(const uint32_t *__
         uint32_t s = 0;
         for (uint32_t k = k0 + (uint32_t)lane; k < k1; k += kWave) s += rank[k];
         s = wave_sum(s);
-        if (lane == 0) rank[c] = s + 1u;
+        if (lane == 0) rank[c] = s + 1u + (desc ? desc[c] : 0u);
     }
 }
 
@@ -2724,6 +2730,421 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
         if (pass == 1 && tid == 0) C.count[i] = found;
         __syncthreads();
     }
+}
+
+
+// ---------------------------------------------------------------------------
+// task pool (page 1 sections 3.2 and 5.3: workers take tasks from a shared
+// pool as they free up; page 4 section 4.3: a kernel of its own for one class
+// of parents)
+//
+// With the pool the level loop expands only the parents with more than 64
+// objects, and every concept of the store with at most 64 objects is a task
+// whose whole subtree one wavefront enumerates depth-first.  Every concept
+// below a task has its objects among the task's (extents only shrink down the
+// tree), so the wavefront keeps the task's rows in LDS and in registers (lane
+// g: object g of the task's list) and every extent below as a 64-bit mask over
+// them.  Wavefronts take the tasks in turn from an atomic counter until none
+// are left; the pool is fixed before the launch, so no wavefront waits for
+// another.
+//
+// A node's candidates are the task's candidates (above the task's cursor,
+// outside its intent) that lie above the node's cursor and outside its
+// intent; they are tested 64 at a time, one per lane, from the largest
+// attribute down, and the passing ones visited in that order, so concepts come
+// out in the output order of the task's subtree (pre-order, children by
+// descending attribute).  The descent keeps one frame per depth in LDS; a
+// child's extent is a proper subset of its parent's (j is outside the parent's
+// intent, so some object lacks it), so the depth stays within the task's
+// object count.
+//
+// Concepts go to pool slots, reserved 64 at a time per wavefront: the intent,
+// and a record {object mask, task, offset in the task's subtree, cursor, depth
+// below the task}.  Slots a wavefront reserved but did not use keep owner
+// kPoolFree.  If the slots run out, the kernel raises the overflow flag and
+// every wavefront stops; the host grows the slots and runs it again.
+
+constexpr int kPoolWaves = 2;              // wavefronts per block
+constexpr int kPoolDepth = kSmallMax + 1;  // frames: the task and up to 64 levels below
+constexpr uint32_t kPoolFree = 0xFFFFFFFFu;
+// pool counters (word offsets, each in a 128-byte line of its own)
+enum { POOL_TASK = 0, POOL_SLOTS = 16, POOL_OVERFLOW = 32, POOL_ERROR = 48, POOL_TOT_N = 64, POOL_TOT_OBJ = 80,
+       POOL_CTR_N = 96 };
+
+struct PoolRec {
+    uint64_t mask;   // the concept's objects: bit g = object g of the task's list
+    uint32_t owner;  // the task (store index); kPoolFree for a slot not used
+    uint32_t off;    // position in the task's subtree, the task itself excluded
+    int32_t cursor;  // the attribute that generated the concept
+    uint32_t depth;  // levels below the task (1 = a child of the task)
+};
+
+struct PoolArgs {
+    const uint64_t *rows;
+    const uint64_t *intents;
+    const int32_t *cursor;
+    const uint64_t *loff;
+    const uint32_t *objs;
+    uint64_t K;       // store concepts; the tasks are those with at most 64 objects
+    int m, wm;
+    uint64_t tail_m;
+    uint64_t *ctr;    // POOL_* counters
+    uint64_t cap;     // pool slots
+    uint64_t *p_int;  // cap x wm
+    PoolRec *p_rec;   // cap
+    uint32_t *desc;   // K: concepts below each task (0 for the other concepts)
+};
+
+template <int WMC>
+__global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(PoolArgs P)
+{
+    static_assert(WMC <= 8, "the pool keeps intents of at most 8 words");
+    constexpr int kMaxCand = kWave * WMC;
+    __shared__ uint64_t s_rows[kPoolWaves][kSmallMax * WMC];  // the task's rows
+    __shared__ uint64_t s_cm[kPoolWaves][kMaxCand];           // object mask of each task candidate
+    __shared__ uint16_t s_cand[kPoolWaves][kMaxCand];         // the task's candidates, ascending
+    __shared__ uint64_t s_fb[kPoolWaves][kPoolDepth * WMC];   // frame: intent
+    __shared__ uint64_t s_fc[kPoolWaves][kPoolDepth];         // frame: object mask
+    __shared__ uint64_t s_fp[kPoolWaves][kPoolDepth];         // frame: passing candidates of its round not yet visited
+    __shared__ uint16_t s_flo[kPoolWaves][kPoolDepth];        // frame: first candidate above its cursor
+    __shared__ uint16_t s_fhi[kPoolWaves][kPoolDepth];        // frame: candidates [lo, hi) not yet tested
+    __shared__ uint16_t s_fbase[kPoolWaves][kPoolDepth];      // frame: candidate of bit 0 of the round
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wm = words_of<WMC>(P.wm);
+    uint64_t *R = s_rows[wv];
+    uint64_t *CM = s_cm[wv];
+    uint16_t *CAND = s_cand[wv];
+    uint64_t *FB = s_fb[wv];
+    uint64_t *FC = s_fc[wv];
+    uint64_t *FP = s_fp[wv];
+    uint16_t *FLO = s_flo[wv], *FHI = s_fhi[wv], *FBASE = s_fbase[wv];
+    uint64_t slot = 0, slot_end = 0;  // the wavefront's reserved slots not yet used
+    bool stop = false;
+    while (!stop) {
+        uint64_t t = 0;
+        if (lane == 0) t = atomicAdd((unsigned long long *)&P.ctr[POOL_TASK], 1ull);
+        t = lane_value64(t, 0);
+        if (t >= P.K) break;
+        if (__hip_atomic_load(&P.ctr[POOL_OVERFLOW], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+        const uint64_t o0 = P.loff[t];
+        const uint64_t a64 = P.loff[t + 1] - o0;
+        if (a64 > (uint64_t)kSmallMax) {
+            if (lane == 0) P.desc[t] = 0;
+            continue;
+        }
+        const int a = (int)a64;
+        const int y0 = __builtin_amdgcn_readfirstlane(P.cursor[t]);
+        // the task's rows: lane g < a holds object g's row, the others all ones
+        // (neutral for the AND below)
+        uint64_t row[WMC];
+        {
+            const uint64_t g = lane < a ? (uint64_t)P.objs[o0 + lane] : 0ull;
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) {
+                row[u] = ~0ull;
+                if (u < wm && lane < a) {
+                    row[u] = P.rows[g * P.wm + u];
+                    R[lane * WMC + u] = row[u];
+                }
+            }
+        }
+        if (lane < wm) FB[lane] = P.intents[t * P.wm + lane];
+        wave_sync();
+        // the task's candidates and, for each, the objects of the task having it
+        int nc = 0;
+        for (int u = 0; u < wm; ++u) {
+            uint64_t cm = ~uniform64(FB[u]) & above_mask(y0, u);
+            if (u == wm - 1) cm &= P.tail_m;
+            const bool has = ((cm >> lane) & 1ull) != 0;
+            const uint64_t bal = __ballot(has);
+            if (has) CAND[nc + __popcll(bal & below_mask(lane))] = (uint16_t)(64 * u + lane);
+            nc += __popcll(bal);
+        }
+        wave_sync();
+        for (int i = lane; i < nc; i += kWave) {
+            const int j = CAND[i];
+            const int u = j >> 6, b = j & 63;
+            uint64_t msk = 0;
+            for (int g = 0; g < a; ++g) msk |= ((R[g * WMC + u] >> b) & 1ull) << g;
+            CM[i] = msk;
+        }
+        if (lane == 0) {
+            FC[0] = a == 64 ? ~0ull : ((1ull << a) - 1ull);
+            FP[0] = 0;
+            FLO[0] = 0;
+            FHI[0] = (uint16_t)nc;
+        }
+        wave_sync();
+        uint32_t off = 0;  // concepts of the task's subtree written so far
+        int d = 0;
+        while (d >= 0) {
+            const uint64_t pend = uniform64(FP[d]);
+            if (!pend) {
+                const int lo = __builtin_amdgcn_readfirstlane(FLO[d]);
+                const int hi = __builtin_amdgcn_readfirstlane(FHI[d]);
+                if (hi <= lo) {
+                    --d;
+                    continue;
+                }
+                // the next round: the highest untested candidates, one per lane
+                const int base = hi - kWave > lo ? hi - kWave : lo;
+                const int i = base + lane;
+                bool pass = false;
+                if (i < hi) {
+                    const int j = CAND[i];
+                    const int ju = j >> 6;
+                    const uint64_t *Bd = FB + d * WMC;
+                    if (!((Bd[ju] >> (j & 63)) & 1ull)) {
+                        // C = the node's objects having j; D = AND of their rows
+                        // (all attributes when C is empty); canonical: D agrees
+                        // with the node's intent below j
+                        const uint64_t c = FC[d] & CM[i];
+                        uint64_t D[WMC];
+#pragma unroll
+                        for (int u = 0; u < WMC; ++u) D[u] = ~0ull;
+                        for (uint64_t cc = c; cc; cc &= cc - 1ull) {
+                            const int g = __ffsll((unsigned long long)cc) - 1;
+#pragma unroll
+                            for (int u = 0; u < WMC; ++u)
+                                if (u < wm) D[u] &= R[g * WMC + u];
+                        }
+                        bool ok = true;
+#pragma unroll
+                        for (int u = 0; u < WMC; ++u) {
+                            if (u < ju) ok = ok && D[u] == Bd[u];
+                            if (u == ju) ok = ok && ((D[u] ^ Bd[u]) & below_mask(j & 63)) == 0;
+                        }
+                        pass = ok;
+                    }
+                }
+                const uint64_t bal = __ballot(pass);
+                if (lane == 0) {
+                    FP[d] = bal;
+                    FBASE[d] = (uint16_t)base;
+                    FHI[d] = (uint16_t)base;
+                }
+                wave_sync();
+                continue;
+            }
+            // the largest passing candidate not yet visited is the next child
+            const int b = 63 - __clzll((long long)pend);
+            const int i = __builtin_amdgcn_readfirstlane(FBASE[d]) + b;
+            const int j = __builtin_amdgcn_readfirstlane(CAND[i]);
+            const uint64_t c = uniform64(FC[d] & CM[i]);
+            if (d + 1 >= kPoolDepth) {  // cannot happen for a closed intent; never write past the frames
+                if (lane == 0) atomicOr((unsigned long long *)&P.ctr[POOL_ERROR], 1ull);
+                stop = true;
+                break;
+            }
+            // the child's intent: AND of the rows of its objects over the lanes
+            const bool mine = ((c >> lane) & 1ull) != 0;
+            uint64_t word = 0;  // lane u < wm: word u of the intent
+#pragma unroll
+            for (int u = 0; u < WMC; ++u) {
+                if (u < wm) {
+                    uint64_t w = wave_and(mine ? row[u] : ~0ull);
+                    if (u == wm - 1) w &= P.tail_m;
+                    if (lane == u) word = w;
+                }
+            }
+            if (slot == slot_end) {
+                uint64_t s0 = 0;
+                if (lane == 0) s0 = atomicAdd((unsigned long long *)&P.ctr[POOL_SLOTS], (unsigned long long)kWave);
+                s0 = lane_value64(s0, 0);
+                if (s0 + kWave > P.cap) {
+                    if (lane == 0) atomicOr((unsigned long long *)&P.ctr[POOL_OVERFLOW], 1ull);
+                    stop = true;
+                    break;
+                }
+                slot = s0;
+                slot_end = s0 + kWave;
+            }
+            if (lane < wm) P.p_int[slot * P.wm + lane] = word;
+            if (lane == 0) {
+                PoolRec r;
+                r.mask = c;
+                r.owner = (uint32_t)t;
+                r.off = off;
+                r.cursor = j;
+                r.depth = (uint32_t)(d + 1);
+                P.p_rec[slot] = r;
+                FP[d] = pend & ~(1ull << b);
+                FC[d + 1] = c;
+                FP[d + 1] = 0;
+                FLO[d + 1] = (uint16_t)(i + 1);
+                FHI[d + 1] = (uint16_t)nc;
+            }
+            if (lane < wm) FB[(d + 1) * WMC + lane] = word;
+            ++slot;
+            ++off;
+            ++d;
+            wave_sync();
+        }
+        if (stop) break;
+        if (lane == 0) P.desc[t] = off;
+    }
+    // slots reserved but not used stay free
+    for (uint64_t s = slot + (uint64_t)lane; s < slot_end; s += kWave) {
+        P.p_rec[s].owner = kPoolFree;
+        P.p_rec[s].mask = 0;
+    }
+}
+
+// Pool slots [0, n): 1 for a used slot, and its object count, for the scans
+// that place the pool's concepts in the store.
+__global__ void __launch_bounds__(kBlock) k_pool_flags(const PoolRec *__restrict__ rec, uint64_t n,
+                                                       uint32_t *__restrict__ used, uint64_t *__restrict__ nobj)
+{
+    for (uint64_t s = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (uint64_t)gridDim.x * blockDim.x) {
+        const PoolRec r = rec[s];
+        const bool u = r.owner != kPoolFree;
+        used[s] = u ? 1u : 0u;
+        nobj[s] = u ? (uint64_t)__popcll(r.mask) : 0ull;
+    }
+}
+
+struct PoolCommitArgs {
+    const PoolRec *rec;
+    const uint64_t *p_int;
+    const uint64_t *dense;  // exclusive scan of the used flags
+    const uint64_t *ooff;   // exclusive scan of the object counts
+    uint64_t n;             // slots
+    uint64_t K0, obj0;      // the store's concepts and list entries before the pool's
+    uint64_t n_pool, n_obj; // the pool's concepts and list entries
+    int wm;
+    uint64_t *intents;
+    int32_t *cursor;
+    uint64_t *loff;
+    uint32_t *objs;
+    uint32_t *t_owner, *t_off;  // per pool concept (index - K0): task, offset in its subtree
+    uint8_t *t_depth;           // levels below the task
+};
+
+// The used slots, in slot order, become store concepts K0, K0 + 1, ...: the
+// intent, the cursor, and the object list (the task's list entries at the
+// mask's bits, ascending) after the store's last list.
+__global__ void __launch_bounds__(kBlock) k_pool_commit(PoolCommitArgs A)
+{
+    for (uint64_t s = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; s < A.n; s += (uint64_t)gridDim.x * blockDim.x) {
+        const PoolRec r = A.rec[s];
+        if (r.owner == kPoolFree) continue;
+        const uint64_t i = A.dense[s], k = A.K0 + i;
+        for (int u = 0; u < A.wm; ++u) A.intents[k * A.wm + u] = A.p_int[s * A.wm + u];
+        A.cursor[k] = r.cursor;
+        const uint64_t o = A.obj0 + A.ooff[s];
+        A.loff[k] = o;
+        const uint64_t to = A.loff[r.owner];
+        uint64_t q = 0;
+        for (uint64_t m = r.mask; m; m &= m - 1ull) A.objs[o + q++] = A.objs[to + (uint64_t)(__ffsll((unsigned long long)m) - 1)];
+        A.t_owner[i] = r.owner;
+        A.t_off[i] = r.off;
+        A.t_depth[i] = (uint8_t)r.depth;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) A.loff[A.K0 + A.n_pool] = A.obj0 + A.n_obj;
+}
+
+// p[0, n) = v for 32-bit words.
+__global__ void __launch_bounds__(kBlock) k_fill_u32(uint32_t *p, uint64_t n, uint32_t v)
+{
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// Output positions of the pool's concepts: the task's position, plus one, plus
+// the concept's offset in the task's subtree (the subtree is written in output
+// order).  The root's own position is 0 (its rank entry holds its size).
+__global__ void __launch_bounds__(kBlock) k_tail_position(const uint32_t *__restrict__ owner,
+                                                          const uint32_t *__restrict__ off, uint64_t n, uint64_t K0,
+                                                          uint32_t *__restrict__ rank)
+{
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint32_t o = owner[i];
+        rank[K0 + i] = (o == 0 ? 0u : rank[o]) + 1u + off[i];
+    }
+}
+
+// Per-level and total counts of an enumeration whose store holds the level
+// loop's concepts [0, K0) (level l: [lev_lo[l], lev_lo[l + 1])) and the pool's
+// [K0, K): every concept is a parent that tests the attributes above its
+// cursor outside its intent, so the counts follow from the store alone.
+struct PoolStatsArgs {
+    const uint64_t *intents;
+    const int32_t *cursor;
+    const uint64_t *loff;
+    uint64_t K, K0;
+    int m, wm, nlev, nbins, mid_max;
+    uint64_t tail_m;
+    const uint64_t *lev_lo;    // nlev + 1
+    const uint32_t *t_owner;   // pool concepts
+    const uint8_t *t_depth;
+    uint64_t *out;             // [2 * nbins]: concepts, tests per level; then POOLSTAT_* sums
+};
+enum { POOLSTAT_TESTS = 0, POOLSTAT_PAIRS, POOLSTAT_SUMC, POOLSTAT_LOCAL, POOLSTAT_LOCAL_OBJS, POOLSTAT_MID,
+       POOLSTAT_MID_OBJS, POOLSTAT_N };
+
+__device__ __forceinline__ int level_of(const uint64_t *lev_lo, int nlev, uint64_t c)
+{
+    int lo = 0, hi = nlev - 1;  // the last l with lev_lo[l] <= c
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (lev_lo[mid] <= c) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ void __launch_bounds__(kBlock) k_pool_stats(PoolStatsArgs S)
+{
+    extern __shared__ unsigned long long s_bins[];  // 2 * nbins
+    __shared__ uint64_t s_part[POOLSTAT_N][kWavesPerBlock];
+    for (int i = threadIdx.x; i < 2 * S.nbins; i += blockDim.x) s_bins[i] = 0;
+    __syncthreads();
+    uint64_t sum[POOLSTAT_N] = {0, 0, 0, 0, 0, 0, 0};
+    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < S.K; c += (uint64_t)gridDim.x * blockDim.x) {
+        int l;
+        if (c < S.K0) {
+            l = level_of(S.lev_lo, S.nlev, c);
+        } else {
+            const uint64_t i = c - S.K0;
+            l = level_of(S.lev_lo, S.nlev, S.t_owner[i]) + (int)S.t_depth[i];
+        }
+        const int y = S.cursor[c];
+        uint64_t tests = 0;
+        for (int u = 0; u < S.wm; ++u) {
+            uint64_t x = ~S.intents[c * S.wm + u] & above_mask(y, u);
+            if (u == S.wm - 1) x &= S.tail_m;
+            tests += (uint64_t)__popcll(x);
+        }
+        const uint64_t a = S.loff[c + 1] - S.loff[c];
+        if (l >= S.nbins) l = S.nbins - 1;  // cannot happen: a level adds an attribute
+        atomicAdd(&s_bins[l], 1ull);
+        atomicAdd(&s_bins[S.nbins + l], (unsigned long long)tests);
+        sum[POOLSTAT_TESTS] += tests;
+        sum[POOLSTAT_PAIRS] += (uint64_t)(S.m - 1 - y);
+        if (c != 0) sum[POOLSTAT_SUMC] += a;
+        if (a <= (uint64_t)kSmallMax) {
+            sum[POOLSTAT_LOCAL] += 1;
+            sum[POOLSTAT_LOCAL_OBJS] += a;
+        } else if (a <= (uint64_t)S.mid_max) {
+            sum[POOLSTAT_MID] += 1;
+            sum[POOLSTAT_MID_OBJS] += a;
+        }
+    }
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+#pragma unroll
+    for (int k = 0; k < POOLSTAT_N; ++k) {
+        const uint64_t v = wave_sum64(sum[k]);
+        if (lane == 0) s_part[k][w] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < POOLSTAT_N) {
+        uint64_t v = 0;
+        for (int i = 0; i < kWavesPerBlock; ++i) v += s_part[threadIdx.x][i];
+        if (v) atomicAdd((unsigned long long *)&S.out[2 * S.nbins + threadIdx.x], (unsigned long long)v);
+    }
+    for (int i = threadIdx.x; i < 2 * S.nbins; i += blockDim.x)
+        if (s_bins[i]) atomicAdd((unsigned long long *)&S.out[i], s_bins[i]);
 }
 
 }  // namespace fcbo

@@ -67,6 +67,12 @@ enum {
 /* fcbo_enumerate flags */
 #define FCBO_REUSE_RESULT 1u /* reuse the concepts of the previous call if any */
 #define FCBO_PROFILE 2u      /* time every kernel class with HIP events (fills kernel_ms) */
+#define FCBO_TASK_POOL 16u   /* schedule the search as a task pool (M <= 512): the level loop
+                                expands only the parents with more than 64 objects, and the
+                                subtree of every concept with at most 64 objects is one task,
+                                enumerated depth-first by one wavefront; wavefronts take tasks
+                                from a shared counter as they free up (page 1 sections 3.2 and
+                                5.3; page 4 section 4.3) */
 
 /* fcbo_enumerate_bounded flags (besides FCBO_PROFILE) */
 #define FCBO_ONE_SUBTREE_PER_BATCH 4u /* test hook: every batch takes a single subtree, so the
@@ -188,7 +194,8 @@ int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs
  *   intents_out   K x ceil(M/64) words, row i = intent of concept i
  *   extents_out   K x ceil(N/64) words in the same order, or NULL to skip
  *   capacity      rows available in the output buffers
- *   flags         FCBO_REUSE_RESULT, FCBO_PROFILE
+ *   flags         FCBO_REUSE_RESULT, FCBO_PROFILE, FCBO_TASK_POOL (M <= 512, else
+ *                 FCBO_ERR_INVALID_ARGUMENT); the result is the same either way
  *   n_concepts_out receives K (also on FCBO_ERR_CAPACITY); may be NULL
  *   stats_out     optional statistics, or NULL
  * If intents_out is NULL or capacity < K the call returns FCBO_ERR_CAPACITY,
