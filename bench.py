@@ -23,6 +23,10 @@ Prints one JSON line.  `value` is concepts per second; beside it:
   * `host_stream`: the first rows of the ordered output streamed to pinned
     host memory through two device staging buffers (fcbo_copy_to_host), a
     PCIe-inclusive rate, never the headline value;
+  * `task_pool`: the same step with the task-pool schedule (FCBO_TASK_POOL:
+    the level loop expands only parents with more than 16 objects, one
+    wavefront enumerates each smaller concept's subtree depth-first), timed
+    over its own steps into the same buffers;
   * `bounded`: the same enumeration in bounded device memory
     (fcbo_enumerate_bounded under fcbo_set_memory_limit, by default a quarter
     of what the unbounded step held), the whole output (intents and extent
@@ -354,6 +358,7 @@ def main():
                     "process's cores, at most 16)")
     ap.add_argument("--cpu-bitmap-tests", type=int, default=2_000_000,
                     help="closure-test budget of the bitmap oracle's prefix (0: skip)")
+    ap.add_argument("--pool-steps", type=int, default=3, help="timed steps of the task-pool schedule (0: skip)")
     ap.add_argument("--bounded-frac", type=float, default=0.25,
                     help="bounded run: memory limit as a fraction of the unbounded step's peak (0: skip)")
     ap.add_argument("--bounded-gib", type=float, default=0.0, help="bounded run: memory limit in GiB (overrides "
@@ -494,6 +499,44 @@ def main():
     if closure_roof["traffic"]:
         closure_roof["traffic_over_model"] = round(closure_roof["traffic"] / model, 3)
 
+    # the same step with the task-pool schedule (M <= 512)
+    task_pool = None
+    if args.pool_steps > 0 and m <= 512:
+        try:
+            rc, kk, pprof = ctx.enumerate_into(ints, exts, fca.FCBO_TASK_POOL | fca.FCBO_PROFILE)
+            assert rc == fca.FCBO_OK and kk == k
+            rc, kk, _ = ctx.enumerate_into(ints, exts, fca.FCBO_TASK_POOL)
+            pst = []
+            torch.cuda.synchronize()
+            tp0 = time.perf_counter()
+            for i in range(args.pool_steps):
+                rc, kk, sp = ctx.enumerate_into(ints, exts, fca.FCBO_TASK_POOL)
+                assert rc == fca.FCBO_OK and kk == k and sp["closure_tests"] == st0["closure_tests"]
+                pst.append(sp)
+            torch.cuda.synchronize()
+            pms = (time.perf_counter() - tp0) * 1e3 / args.pool_steps
+
+            def pavg(key):
+                return sum(x[key] for x in pst) / len(pst)
+
+            task_pool = {"ms_per_step": round(pms, 4), "concepts_per_s": round(k / (pms * 1e-3), 1),
+                         "closure_tests_per_s": round(st0["closure_tests"] / (pms * 1e-3), 1),
+                         "level_sync_ms_per_step": round(ms_per_step, 4),
+                         "speedup_over_level_sync": round(ms_per_step / pms, 3),
+                         "device_ms": {"enumerate": round(pavg("enumerate_ms"), 4),
+                                       "level_loop_and_pool": round(pavg("closure_kernel_ms"), 4),
+                                       "sort": round(pavg("sort_ms"), 4), "output": round(pavg("output_ms"), 4)},
+                         "kernel_ms": {c: round(v, 4) for c, v in pprof["kernel_ms"].items()},
+                         "kernel_ms_note": "one untimed profiled step; the pool kernel is counted under test_local, "
+                                           "its commit under write_local",
+                         "steps": args.pool_steps}
+        except (fca.FcboError, torch.OutOfMemoryError) as err:
+            task_pool = {"error": str(err).splitlines()[0][:160]}
+        print("[bench] task pool: %s" % json.dumps(task_pool), file=sys.stderr, flush=True)
+        # the timed level-sync result stays the context's result for what follows
+        rc, kk, _ = ctx.enumerate_into(ints, exts, 0)
+        assert rc == fca.FCBO_OK and kk == k
+
     # the ordered output streamed to pinned host memory through two staging
     # buffers (not part of the step; includes the PCIe transfer)
     stream_host = None
@@ -589,6 +632,7 @@ def main():
         "cpu_baseline_bitmap_oracle": cpu.get("bitmap") if cpu else None,
         "cover_edges": cover,
         "host_stream": stream_host,
+        "task_pool": task_pool,
         "bounded": bounded,
     }
     ctx.close()

@@ -143,6 +143,10 @@ struct LevelCursor {
 };
 
 constexpr int kGridCap = 4096;  // blocks for grid-stride wave kernels
+// Task pool: concepts with at most this many objects are tasks (measured
+// against 8, 32 and 64: best on the 2,000 x 64 context, 1.10 against 1.14 to
+// 1.41 ms a step, and within 4% of the best on the 50,000 x 400 one).
+constexpr int kPoolTaskMax = 16;
 // Average children per concept from which the order passes take a wavefront
 // per concept (measured: 8 against 4 and 16 on both full-size workloads).
 constexpr uint64_t kOrderWaveFanout = 8;
@@ -275,7 +279,7 @@ struct fcbo_context {
     // seed sets of a bounded enumeration, the deepest last
     std::vector<SeedSet> seeds;
 
-    // task pool: the subtrees of the concepts with at most 64 objects
+    // task pool: the subtrees of the concepts with at most kPoolTaskMax objects
     bool pool_active = false;  // the level loop leaves such parents to the pool
     bool pool_result = false;  // the last result came from the level loop and the pool
     uint64_t K_sync = 0, n_pool = 0;  // concepts from the level loop, from the pool
@@ -289,6 +293,9 @@ struct fcbo_context {
     uint32_t *t_owner = nullptr, *t_off = nullptr;  // per pool concept: task, offset in its subtree
     uint8_t *t_depth = nullptr;       // per pool concept: levels below the task
     uint64_t *pool_ctr = nullptr;     // POOL_* counters
+    uint64_t *task_ctr = nullptr;     // the pool's claim counters
+    uint32_t *ptasks = nullptr;       // the pool's tasks
+    uint64_t cap_tctr = 0, cap_ptasks = 0;
     uint64_t *d_levlo = nullptr;      // the level loop's level starts, for the counts
     uint64_t *pstat = nullptr;        // per-level and total counts
 
@@ -408,11 +415,12 @@ struct fcbo_context {
         dfree(dmem, p_int, cap_pint); dfree(dmem, p_rec, cap_prec); dfree(dmem, desc, cap_desc);
         dfree(dmem, t_owner, cap_towner); dfree(dmem, t_off, cap_toff); dfree(dmem, t_depth, cap_tdepth);
         dfree(dmem, pool_ctr, cap_pctr); dfree(dmem, d_levlo, cap_levlo); dfree(dmem, pstat, cap_pstat);
+        dfree(dmem, task_ctr, cap_tctr); dfree(dmem, ptasks, cap_ptasks);
         for (int b = 0; b < 2; ++b) {
             dfree(dmem, hs_int[b], cap_hs_int[b]);
             dfree(dmem, hs_ext[b], cap_hs_ext[b]);
         }
-        have_result = have_perm = have_cover_counts = false;
+        have_result = have_perm = have_cover_counts = have_levels = pool_result = false;
     }
 
     void free_all()
@@ -477,7 +485,7 @@ struct fcbo_context {
         A.counters_next = counters + (uint64_t)(1 - ctr) * CNT_N;
         A.child_cap = std::min(std::min(cap_int / (uint64_t)wm, cap_cur), cap_loff ? cap_loff - 1 : 0);
         A.obj_cap = cap_o > kObjSlack ? cap_o - kObjSlack : 0;  // the output kernel reads past the last list
-        A.pool = pool_active ? 1 : 0;
+        A.pool_max = pool_active ? kPoolTaskMax : -1;
         return A;
     }
 
@@ -697,6 +705,7 @@ LevelFns pick_level_fns(int wm)
 }
 
 static_assert(POOL_CTR_N <= CNT_N, "the pool's counters are read through the level counters' host buffer");
+static_assert(kPoolTaskMax <= kSmallMax, "pool tasks keep their objects in one wavefront");
 
 typedef void (*pool_fn)(fcbo_context *, const PoolArgs &);
 
@@ -707,7 +716,8 @@ void launch_pool(fcbo_context *c, const PoolArgs &PA)
     // counter, so more would only queue behind them
     int per_cu = 1;
     CK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pool<WMC>, kWave * kPoolWaves, 0));
-    const unsigned g = (unsigned)std::max<uint64_t>(1, (uint64_t)c->n_cu * std::max(1, per_cu));
+    const uint64_t resident = (uint64_t)c->n_cu * std::max(1, per_cu);
+    const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(resident, div_up(PA.n_tasks, kPoolWaves)));
     hipLaunchKernelGGL(k_pool<WMC>, dim3(g), dim3(kWave * kPoolWaves), 0, c->stream, PA);
     CK_LAUNCH();
 }
@@ -922,7 +932,7 @@ void fcbo_context::enumerate_levels(bool pool)
     have_perm = false;
 }
 
-// The task pool: every concept of the store [0, K0) with at most 64 objects is
+// The task pool: every concept of the store [0, K0) with at most kPoolTaskMax objects is
 // a task whose subtree k_pool enumerates; the pool's concepts then join the
 // store after it (lists from obj0 on), and the counts are taken over the whole
 // store.
@@ -932,6 +942,28 @@ void fcbo_context::run_pool(uint64_t K0, uint64_t obj0)
     pool_fn fn = pick_pool_fn(wm);
     ensure(dmem, desc, cap_desc, K0, 0, stream, mc);
     ensure(dmem, pool_ctr, cap_pctr, POOL_CTR_N, 0, stream, 1);
+    ensure(dmem, task_ctr, cap_tctr, (uint64_t)kPoolStripes * kCntPad, 0, stream, 1);
+    // the task list: the store's concepts with at most kPoolTaskMax objects
+    ensure(dmem, nchild, cap_nch, K0, 0, stream, mc);
+    ensure(dmem, cbase, cap_cb, K0 + 1, 0, stream, mc);
+    clear_words(pool_ctr, POOL_CTR_N);
+    {
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(K0, kBlock)));
+        hipLaunchKernelGGL(k_pool_task_flags, dim3(g), dim3(kBlock), 0, stream, (const uint64_t *)loff, K0,
+                           kPoolTaskMax, nchild, desc);
+        CK_LAUNCH();
+        scan(nchild, nullptr, nullptr, K0, K0, cbase, nullptr, pool_ctr + POOL_NTASKS, nullptr);
+        CK(hipMemcpyAsync(h_counters, pool_ctr, POOL_CTR_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+        CK(hipStreamSynchronize(stream));
+    }
+    const uint64_t n_tasks = h_counters[POOL_NTASKS];
+    ensure(dmem, ptasks, cap_ptasks, std::max<uint64_t>(1, n_tasks), 0, stream, mc);
+    {
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(K0, kBlock)));
+        hipLaunchKernelGGL(k_pool_task_list, dim3(g), dim3(kBlock), 0, stream, (const uint32_t *)nchild,
+                           (const uint64_t *)cbase, K0, ptasks);
+        CK_LAUNCH();
+    }
     uint64_t cap = std::max<uint64_t>(pool_cap, tiny ? (uint64_t)kWave : start_size(1u << 22, 8 * (uint64_t)wm + 24));
     uint64_t slots = 0;
     for (int attempt = 0;; ++attempt) {
@@ -939,6 +971,7 @@ void fcbo_context::run_pool(uint64_t K0, uint64_t obj0)
         ensure(dmem, p_int, cap_pint, cap * wm, 0, stream, mc);
         ensure(dmem, p_rec, cap_prec, cap, 0, stream, mc);
         clear_words(pool_ctr, POOL_CTR_N);
+        clear_words(task_ctr, (uint64_t)kPoolStripes * kCntPad);
         PoolArgs PA;
         PA.rows = rows;
         PA.intents = intents;
@@ -946,6 +979,9 @@ void fcbo_context::run_pool(uint64_t K0, uint64_t obj0)
         PA.loff = loff;
         PA.objs = objs;
         PA.K = K0;
+        PA.tasks = ptasks;
+        PA.n_tasks = n_tasks;
+        PA.task_ctr = task_ctr;
         PA.m = (int)m;
         PA.wm = wm;
         PA.tail_m = tail_m;
@@ -955,7 +991,7 @@ void fcbo_context::run_pool(uint64_t K0, uint64_t obj0)
         PA.p_rec = p_rec;
         PA.desc = desc;
         hipEvent_t b = prof_begin();
-        fn(this, PA);
+        if (n_tasks) fn(this, PA);
         prof_end(FCBO_K_TEST_LOCAL, b);
         CK(hipMemcpyAsync(h_counters, pool_ctr, POOL_CTR_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
         CK(hipStreamSynchronize(stream));

@@ -144,8 +144,8 @@ struct LevelArgs {
     int chunk;             // parents per chunk of the local test (at most LocalCfg::kChunk)
     uint64_t child_cap;    // concepts the store can hold (intents, cursors, list offsets)
     uint64_t obj_cap;      // list entries the store can hold
-    int pool;              // parents with at most 64 objects are left to the task pool (no
-                           // tests, no children here)
+    int pool_max;          // parents with at most this many objects are left to the task
+                           // pool (no tests, no children here); -1 without the pool
 };
 
 // ---------------------------------------------------------------------------
@@ -618,7 +618,7 @@ __global__ void __launch_bounds__(LocalCfg<WMC>::kThreads)
             o0 = A.loff[c];
             sz = A.loff[c + 1] - o0;
             y = A.cursor[c];
-            act = sz <= (uint64_t)kSmallMax && !A.pool;
+            act = sz <= (uint64_t)kSmallMax && (int64_t)sz > (int64_t)A.pool_max;
             a = act ? (int)sz : 0;
         }
         {
@@ -2738,9 +2738,12 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
 // pool as they free up; page 4 section 4.3: a kernel of its own for one class
 // of parents)
 //
-// With the pool the level loop expands only the parents with more than 64
-// objects, and every concept of the store with at most 64 objects is a task
-// whose whole subtree one wavefront enumerates depth-first.  Every concept
+// With the pool the level loop expands only the parents with more than
+// task_max objects (at most 64), and every concept of the store with at most
+// task_max objects is a task whose whole subtree one wavefront enumerates
+// depth-first.  A task of a objects has at most 2^a concepts below it, so a
+// small task_max keeps the tasks short and many, and the wavefronts evenly
+// loaded; the larger concepts stay with the level loop's packed kernels.  Every concept
 // below a task has its objects among the task's (extents only shrink down the
 // tree), so the wavefront keeps the task's rows in LDS and in registers (lane
 // g: object g of the task's list) and every extent below as a 64-bit mask over
@@ -2765,10 +2768,11 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
 // every wavefront stops; the host grows the slots and runs it again.
 
 constexpr int kPoolWaves = 2;              // wavefronts per block
+constexpr int kPoolStripes = 64;           // task claim counters
 constexpr int kPoolDepth = kSmallMax + 1;  // frames: the task and up to 64 levels below
 constexpr uint32_t kPoolFree = 0xFFFFFFFFu;
 // pool counters (word offsets, each in a 128-byte line of its own)
-enum { POOL_TASK = 0, POOL_SLOTS = 16, POOL_OVERFLOW = 32, POOL_ERROR = 48, POOL_TOT_N = 64, POOL_TOT_OBJ = 80,
+enum { POOL_NTASKS = 0, POOL_SLOTS = 16, POOL_OVERFLOW = 32, POOL_ERROR = 48, POOL_TOT_N = 64, POOL_TOT_OBJ = 80,
        POOL_CTR_N = 96 };
 
 struct PoolRec {
@@ -2785,7 +2789,10 @@ struct PoolArgs {
     const int32_t *cursor;
     const uint64_t *loff;
     const uint32_t *objs;
-    uint64_t K;       // store concepts; the tasks are those with at most 64 objects
+    uint64_t K;       // store concepts
+    const uint32_t *tasks;  // the tasks: store concepts with at most kPoolTaskMax objects
+    uint64_t n_tasks;
+    uint64_t *task_ctr;     // kPoolStripes claim counters, kCntPad words apart
     int m, wm;
     uint64_t tail_m;
     uint64_t *ctr;    // POOL_* counters
@@ -2821,19 +2828,25 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(PoolArgs P)
     uint16_t *FLO = s_flo[wv], *FHI = s_fhi[wv], *FBASE = s_fbase[wv];
     uint64_t slot = 0, slot_end = 0;  // the wavefront's reserved slots not yet used
     bool stop = false;
+    // Tasks are claimed one at a time from kPoolStripes counters (task i from
+    // counter i mod kPoolStripes, each on a line of its own: atomics on one
+    // address serialise); a wavefront starts on its own counter and moves to
+    // the next one when that is used up, until every counter is.
+    const int wid = (int)((blockIdx.x * (unsigned)kPoolWaves + (unsigned)wv) % (unsigned)kPoolStripes);
+    int stripes_left = kPoolStripes, stripe = wid;
     while (!stop) {
-        uint64_t t = 0;
-        if (lane == 0) t = atomicAdd((unsigned long long *)&P.ctr[POOL_TASK], 1ull);
-        t = lane_value64(t, 0);
-        if (t >= P.K) break;
-        if (__hip_atomic_load(&P.ctr[POOL_OVERFLOW], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
-        const uint64_t o0 = P.loff[t];
-        const uint64_t a64 = P.loff[t + 1] - o0;
-        if (a64 > (uint64_t)kSmallMax) {
-            if (lane == 0) P.desc[t] = 0;
+        uint64_t k = 0;
+        if (lane == 0) k = atomicAdd((unsigned long long *)&P.task_ctr[stripe * kCntPad], 1ull);
+        const uint64_t ti = lane_value64(k, 0) * kPoolStripes + (uint64_t)stripe;
+        if (ti >= P.n_tasks) {
+            if (--stripes_left == 0) break;
+            stripe = stripe + 1 == kPoolStripes ? 0 : stripe + 1;
             continue;
         }
-        const int a = (int)a64;
+        if (__hip_atomic_load(&P.ctr[POOL_OVERFLOW], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+        const uint64_t t = P.tasks[ti];
+        const uint64_t o0 = P.loff[t];
+        const int a = (int)(P.loff[t + 1] - o0);
         const int y0 = __builtin_amdgcn_readfirstlane(P.cursor[t]);
         // the task's rows: lane g < a holds object g's row, the others all ones
         // (neutral for the AND below)
@@ -3002,6 +3015,28 @@ __global__ void __launch_bounds__(kBlock) k_pool_flags(const PoolRec *__restrict
         used[s] = u ? 1u : 0u;
         nobj[s] = u ? (uint64_t)__popcll(r.mask) : 0ull;
     }
+}
+
+// Store concepts [0, K): 1 for a task (at most task_max objects); every
+// concept's descendant count starts at 0 (the pool sets the tasks').
+__global__ void __launch_bounds__(kBlock) k_pool_task_flags(const uint64_t *__restrict__ loff, uint64_t K,
+                                                            int task_max, uint32_t *__restrict__ flag,
+                                                            uint32_t *__restrict__ desc)
+{
+    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < K; c += (uint64_t)gridDim.x * blockDim.x) {
+        flag[c] = loff[c + 1] - loff[c] <= (uint64_t)task_max ? 1u : 0u;
+        desc[c] = 0;
+    }
+}
+
+// The tasks in store order (shallow levels first, whose subtrees are the
+// larger ones), at the places the scan of the flags gives.
+__global__ void __launch_bounds__(kBlock) k_pool_task_list(const uint32_t *__restrict__ flag,
+                                                           const uint64_t *__restrict__ at, uint64_t K,
+                                                           uint32_t *__restrict__ tasks)
+{
+    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < K; c += (uint64_t)gridDim.x * blockDim.x)
+        if (flag[c]) tasks[at[c]] = (uint32_t)c;
 }
 
 struct PoolCommitArgs {

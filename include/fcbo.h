@@ -68,10 +68,10 @@ enum {
 #define FCBO_REUSE_RESULT 1u /* reuse the concepts of the previous call if any */
 #define FCBO_PROFILE 2u      /* time every kernel class with HIP events (fills kernel_ms) */
 #define FCBO_TASK_POOL 16u   /* schedule the search as a task pool (M <= 512): the level loop
-                                expands only the parents with more than 64 objects, and the
-                                subtree of every concept with at most 64 objects is one task,
-                                enumerated depth-first by one wavefront; wavefronts take tasks
-                                from a shared counter as they free up (page 1 sections 3.2 and
+                                expands only the parents with more than 16 objects, and the
+                                subtree of every concept with at most 16 objects is one task,
+                                enumerated depth-first by one wavefront; wavefronts claim tasks
+                                from shared counters as they free up (page 1 sections 3.2 and
                                 5.3; page 4 section 4.3) */
 
 /* fcbo_enumerate_bounded flags (besides FCBO_PROFILE) */
