@@ -143,10 +143,6 @@ struct LevelCursor {
 };
 
 constexpr int kGridCap = 4096;  // blocks for grid-stride wave kernels
-// Task pool: concepts with at most this many objects are tasks (measured
-// against 8, 32 and 64: best on the 2,000 x 64 context, 1.10 against 1.14 to
-// 1.41 ms a step, and within 4% of the best on the 50,000 x 400 one).
-constexpr int kPoolTaskMax = 16;
 // Average children per concept from which the order passes take a wavefront
 // per concept (measured: 8 against 4 and 16 on both full-size workloads).
 constexpr uint64_t kOrderWaveFanout = 8;
