@@ -499,18 +499,22 @@ def main():
     if closure_roof["traffic"]:
         closure_roof["traffic_over_model"] = round(closure_roof["traffic"] / model, 3)
 
-    # the same step with the task-pool schedule (M <= 512)
+    # the same step with the task-pool schedule (M <= 512), on a context of its
+    # own so that the timed context keeps its result and its memory
     task_pool = None
     if args.pool_steps > 0 and m <= 512:
+        free_before_pool = int(torch.cuda.mem_get_info()[0])
+        pctx = None
         try:
-            rc, kk, pprof = ctx.enumerate_into(ints, exts, fca.FCBO_TASK_POOL | fca.FCBO_PROFILE)
+            pctx = fca.Context(rows, m)
+            rc, kk, pprof = pctx.enumerate_into(ints, exts, fca.FCBO_TASK_POOL | fca.FCBO_PROFILE)
             assert rc == fca.FCBO_OK and kk == k
-            rc, kk, _ = ctx.enumerate_into(ints, exts, fca.FCBO_TASK_POOL)
+            rc, kk, _ = pctx.enumerate_into(ints, exts, fca.FCBO_TASK_POOL)
             pst = []
             torch.cuda.synchronize()
             tp0 = time.perf_counter()
             for i in range(args.pool_steps):
-                rc, kk, sp = ctx.enumerate_into(ints, exts, fca.FCBO_TASK_POOL)
+                rc, kk, sp = pctx.enumerate_into(ints, exts, fca.FCBO_TASK_POOL)
                 assert rc == fca.FCBO_OK and kk == k and sp["closure_tests"] == st0["closure_tests"]
                 pst.append(sp)
             torch.cuda.synchronize()
@@ -529,13 +533,20 @@ def main():
                          "kernel_ms": {c: round(v, 4) for c, v in pprof["kernel_ms"].items()},
                          "kernel_ms_note": "one untimed profiled step; the pool kernel is counted under test_local, "
                                            "its commit under write_local",
+                         "peak_device_bytes": int(pst[-1]["peak_device_bytes"]),
                          "steps": args.pool_steps}
         except (fca.FcboError, torch.OutOfMemoryError) as err:
-            task_pool = {"error": str(err).splitlines()[0][:160]}
+            free, total = torch.cuda.mem_get_info()
+            task_pool = {"error": str(err).splitlines()[0][:160], "device_free_bytes": int(free),
+                         "device_total_bytes": int(total)}
+        finally:
+            if pctx is not None:
+                pctx.close()
+        if task_pool and "error" in task_pool:
+            task_pool["device_free_bytes_before"] = free_before_pool
+            task_pool["device_free_bytes_after_close"] = int(torch.cuda.mem_get_info()[0])
+            task_pool["torch_reserved_bytes"] = int(torch.cuda.memory_reserved())
         print("[bench] task pool: %s" % json.dumps(task_pool), file=sys.stderr, flush=True)
-        # the timed level-sync result stays the context's result for what follows
-        rc, kk, _ = ctx.enumerate_into(ints, exts, 0)
-        assert rc == fca.FCBO_OK and kk == k
 
     # the ordered output streamed to pinned host memory through two staging
     # buffers (not part of the step; includes the PCIe transfer)
@@ -544,11 +555,16 @@ def main():
         nrow = min(args.host_stream_rows, k)
         hi = torch.empty((nrow, wm), dtype=torch.int64).pin_memory()
         he = torch.empty((nrow, wn), dtype=torch.int64).pin_memory() if extents else None
-        ctx.copy_to_host(0, nrow, hi, he, staging_rows=1 << 18)
-        t_h = ctx.copy_to_host(0, nrow, hi, he, staging_rows=1 << 18)
-        nb = nrow * 8 * (wm + (wn if extents else 0))
-        stream_host = {"rows": nrow, "bytes": nb, "ms": round(t_h, 3), "GBps": round(nb / (t_h * 1e-3) / 1e9, 1),
-                       "staging_rows": 1 << 18, "timing": "second call, HIP events; device-to-host over PCIe"}
+        try:
+            ctx.copy_to_host(0, nrow, hi, he, staging_rows=1 << 18)
+            t_h = ctx.copy_to_host(0, nrow, hi, he, staging_rows=1 << 18)
+            nb = nrow * 8 * (wm + (wn if extents else 0))
+            stream_host = {"rows": nrow, "bytes": nb, "ms": round(t_h, 3),
+                           "GBps": round(nb / (t_h * 1e-3) / 1e9, 1), "staging_rows": 1 << 18,
+                           "timing": "second call, HIP events; device-to-host over PCIe"}
+        except fca.FcboError as err:
+            stream_host = {"error": str(err).splitlines()[0][:160],
+                           "device_free_bytes": int(torch.cuda.mem_get_info()[0])}
         del hi, he
         print("[bench] host stream: %s" % json.dumps(stream_host), file=sys.stderr, flush=True)
 

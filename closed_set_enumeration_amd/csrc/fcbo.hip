@@ -40,6 +40,18 @@ inline int map_error(hipError_t e)
 
 #define CK_LAUNCH() CK(hipGetLastError())
 
+// An allocation that fails is reported by the call that made it; its error
+// must not stay behind as the thread's last error, where the next launch check
+// (of this or any other context) would read it as its own failure.
+#define CK_ALLOC(expr)                                             \
+    do {                                                           \
+        hipError_t e_ = (expr);                                    \
+        if (e_ != hipSuccess) {                                    \
+            (void)hipGetLastError();                               \
+            throw HipError{map_error(e_)};                         \
+        }                                                          \
+    } while (0)
+
 inline uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 // Where the enumeration buffers come from: hipMalloc, optionally under a cap
@@ -63,7 +75,7 @@ struct DeviceMemory {
         }
         if (limit && held + bytes > limit) throw HipError{FCBO_ERR_OUT_OF_MEMORY};
         void *q = nullptr;
-        CK(hipMalloc(&q, bytes));
+        CK_ALLOC(hipMalloc(&q, bytes));
         held += bytes;
         peak = std::max(peak, held);
         return q;
@@ -408,10 +420,7 @@ struct fcbo_context {
         dfree(dmem, ctable, cap_ctable); dfree(dmem, ccount, cap_ccount); dfree(dmem, coff, cap_coff);
         dfree(dmem, cbig, cap_cbig); dfree(dmem, cctr, cap_cctr);
         release_seeds();
-        dfree(dmem, p_int, cap_pint); dfree(dmem, p_rec, cap_prec); dfree(dmem, desc, cap_desc);
-        dfree(dmem, t_owner, cap_towner); dfree(dmem, t_off, cap_toff); dfree(dmem, t_depth, cap_tdepth);
-        dfree(dmem, pool_ctr, cap_pctr); dfree(dmem, d_levlo, cap_levlo); dfree(dmem, pstat, cap_pstat);
-        dfree(dmem, task_ctr, cap_tctr); dfree(dmem, ptasks, cap_ptasks);
+        release_pool();
         for (int b = 0; b < 2; ++b) {
             dfree(dmem, hs_int[b], cap_hs_int[b]);
             dfree(dmem, hs_ext[b], cap_hs_ext[b]);
@@ -523,6 +532,24 @@ struct fcbo_context {
     void start_root(LevelCursor &s);
     void run_levels(LevelCursor &s, uint64_t max_levels);
     void enumerate_levels(bool pool = false);
+    // the task pool's buffers (its slots, task list and per-concept arrays)
+    void release_pool()
+    {
+        drain_quiet();
+        dfree(dmem, p_int, cap_pint); dfree(dmem, p_rec, cap_prec); dfree(dmem, desc, cap_desc);
+        dfree(dmem, t_owner, cap_towner); dfree(dmem, t_off, cap_toff); dfree(dmem, t_depth, cap_tdepth);
+        dfree(dmem, pool_ctr, cap_pctr); dfree(dmem, d_levlo, cap_levlo); dfree(dmem, pstat, cap_pstat);
+        dfree(dmem, task_ctr, cap_tctr); dfree(dmem, ptasks, cap_ptasks);
+        pool_cap = 0;
+        pool_result = false;
+    }
+    // wait for the context's streams, ignoring errors (before freeing after a failure)
+    void drain_quiet()
+    {
+        for (int i = 0; i < kSide; ++i)
+            if (aux[i]) (void)hipStreamSynchronize(aux[i]);
+        (void)hipStreamSynchronize(stream);
+    }
     void run_pool(uint64_t K0, uint64_t obj0);
     void enumerate_bounded(uint64_t *intents_buf, uint64_t *extents_buf, uint64_t piece_rows, fcbo_sink_fn sink,
                            void *user, uint32_t flags, fcbo_stats &st);
@@ -923,7 +950,17 @@ void fcbo_context::enumerate_levels(bool pool)
     }
     pool_active = false;
     K = s.lo;
-    if (pool) run_pool(s.lo, s.obj_hi);
+    if (pool) {
+        try {
+            run_pool(s.lo, s.obj_hi);
+        } catch (...) {
+            // a failed pool run keeps none of its memory (its commit grew the
+            // level scratch to the pool's slots)
+            release_pool();
+            free_level_scratch();
+            throw;
+        }
+    }
     have_result = have_levels = true;
     have_perm = false;
 }
@@ -1565,11 +1602,11 @@ void fcbo_context::setup(const uint64_t *rows_in, int64_t n_objects, int64_t n_a
         counters = (uint64_t *)dmem.get(2 * CNT_N * sizeof(uint64_t));
         h_counters = h_counters_own;
     } else {
-        CK(hipMalloc((void **)&rows, row_words * sizeof(uint64_t)));
-        CK(hipMalloc((void **)&cols, col_words * sizeof(uint64_t)));
-        CK(hipMalloc((void **)&scan_part, 2 * kScanBlocks * sizeof(uint64_t)));
-        CK(hipMalloc((void **)&counters, 2 * CNT_N * sizeof(uint64_t)));
-        CK(hipHostMalloc((void **)&h_counters, CNT_N * sizeof(uint64_t), hipHostMallocDefault));
+        CK_ALLOC(hipMalloc((void **)&rows, row_words * sizeof(uint64_t)));
+        CK_ALLOC(hipMalloc((void **)&cols, col_words * sizeof(uint64_t)));
+        CK_ALLOC(hipMalloc((void **)&scan_part, 2 * kScanBlocks * sizeof(uint64_t)));
+        CK_ALLOC(hipMalloc((void **)&counters, 2 * CNT_N * sizeof(uint64_t)));
+        CK_ALLOC(hipHostMalloc((void **)&h_counters, CNT_N * sizeof(uint64_t), hipHostMallocDefault));
     }
     clear_words(rows, row_words);
     const hipMemcpyKind kind = rows_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
@@ -1800,6 +1837,7 @@ int fcbo_context_create(const uint64_t *rows, int64_t n_objects, int64_t n_attrs
     if (!c) return FCBO_ERR_OUT_OF_MEMORY;
     try {
         CK(hipGetDevice(&c->device));
+        (void)hipGetLastError();  // an error left by earlier, unrelated work is not this call's
         c->stream = (hipStream_t)hip_stream;
         c->tiny = (flags & FCBO_TINY_BUFFERS) != 0;
         c->setup(rows, n_objects, n_attrs, row_stride_words, (flags & FCBO_ROWS_ON_DEVICE) != 0);
@@ -1827,6 +1865,7 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
     int rc = FCBO_OK;
     try {
         CK(hipSetDevice(ctx->device));
+        (void)hipGetLastError();  // an error left by earlier, unrelated work is not this call's
         ctx->profile = (flags & FCBO_PROFILE) != 0;
         ctx->ev_used = 0;
         ctx->marks.clear();
@@ -1867,6 +1906,12 @@ int fcbo_enumerate(fcbo_context *ctx, uint64_t *intents_out, uint64_t *extents_o
         }
     } catch (const HipError &e) {
         ctx->have_result = ctx->have_perm = false;
+        if (e.code == FCBO_ERR_OUT_OF_MEMORY) {
+            // give back what the failed run grew beyond the store, so the
+            // next call has the room
+            ctx->release_pool();  // waits for the streams first
+            ctx->free_level_scratch();
+        }
         return e.code;
     } catch (const std::bad_alloc &) {
         ctx->have_result = ctx->have_perm = false;
@@ -1901,6 +1946,7 @@ int fcbo_enumerate_static(const uint64_t *rows, int64_t n_objects, int64_t n_att
     try {
         fcbo_context c;
         CK(hipGetDevice(&c.device));
+        (void)hipGetLastError();  // an error left by earlier, unrelated work is not this call's
         c.stream = stream;
         c.fixed = true;
         c.dmem.region = scratch_on_device(c.device);
@@ -1943,6 +1989,7 @@ int fcbo_enumerate_bounded(fcbo_context *ctx, uint64_t *intents_buf, uint64_t *e
     int rc = FCBO_OK;
     try {
         CK(hipSetDevice(ctx->device));
+        (void)hipGetLastError();  // an error left by earlier, unrelated work is not this call's
         ctx->profile = (flags & FCBO_PROFILE) != 0;
         ctx->enumerate_bounded(intents_buf, extents_buf, piece_rows, sink, user, flags, st);
     } catch (const HipError &e) {
@@ -1974,6 +2021,7 @@ int fcbo_write_range(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_t
         return FCBO_ERR_INVALID_ARGUMENT;
     try {
         CK(hipSetDevice(ctx->device));
+        (void)hipGetLastError();  // an error left by earlier, unrelated work is not this call's
         ctx->profile = false;
         ctx->ev_used = 0;
         ctx->marks.clear();
@@ -1996,6 +2044,7 @@ int fcbo_cover_edges(fcbo_context *ctx, uint64_t *offsets_out, uint32_t *targets
     int rc = FCBO_OK;
     try {
         CK(hipSetDevice(ctx->device));
+        (void)hipGetLastError();  // an error left by earlier, unrelated work is not this call's
         ctx->profile = false;
         ctx->ev_used = 0;
         ctx->marks.clear();
@@ -2027,6 +2076,7 @@ int fcbo_copy_to_host(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_
         return FCBO_ERR_INVALID_ARGUMENT;
     try {
         CK(hipSetDevice(ctx->device));
+        (void)hipGetLastError();  // an error left by earlier, unrelated work is not this call's
         ctx->profile = false;
         ctx->ev_used = 0;
         ctx->marks.clear();

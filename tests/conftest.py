@@ -1,3 +1,4 @@
+import gc
 import os
 import sys
 
@@ -22,3 +23,18 @@ def _flush_case(item):
 def pytest_runtest_setup(item):
     if item.get_closest_marker("gpu") is not None:
         _flush_case(item)
+
+
+def release_device_cache():
+    """Hand the memory torch's caching allocator keeps from earlier tests back to
+    the device.  The library allocates with hipMalloc directly, so the full-size
+    tests, which need most of the device, call this first."""
+    gc.collect()
+    try:
+        import torch
+
+        if torch.cuda.is_available():
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+    except ImportError:
+        pass

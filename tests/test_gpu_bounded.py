@@ -20,6 +20,7 @@ import pytest
 import oracle
 import synth
 from tests import intent_digest as dg
+from tests.conftest import release_device_cache
 from tests.golden_io import read_fixture
 
 torch = pytest.importorskip("torch")
@@ -350,6 +351,7 @@ def _check_root_subtrees(g, hashes, which):
 
 
 def test_full_ctx50000x400_bounded_against_stored_oracle():
+    release_device_cache()
     path = os.path.join(GOLDEN, "ctx50000x400.json")
     if not os.path.exists(path):
         pytest.skip("stored oracle values not generated")
@@ -395,6 +397,7 @@ def test_full_ctx20000x256_bounded_against_store_free_oracle():
     # 1.41e9 concepts whose store alone takes some 150 GB, enumerated with
     # 24 GiB for every enumeration buffer; intents and all 3.5 TB of extents
     # pass through 2^21-row pieces and are hashed on the device.
+    release_device_cache()
     path = os.path.join(GOLDEN, "ctx20000x256.json")
     if not os.path.exists(path):
         pytest.skip("stored oracle values not generated")
@@ -427,3 +430,5 @@ def test_full_ctx20000x256_bounded_against_store_free_oracle():
              % (st["batches"], st["batch_retries"], st["peak_device_bytes"] / 2**30, st["enumerate_ms"] / 1e3))
     finally:
         ctx.close()
+        hs = None
+        release_device_cache()

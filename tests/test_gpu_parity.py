@@ -18,6 +18,7 @@ import pytest
 import oracle
 import synth
 from tests import intent_digest as dg
+from tests.conftest import release_device_cache
 from tests.golden_io import read_fixture
 from tests.intent_digest import digest_torch
 
@@ -347,6 +348,25 @@ def test_memory_limit_fails_part_way_and_leaves_no_stale_result():
         ctx.close()
 
 
+def test_failed_device_allocation_leaves_no_error_behind():
+    # A context whose rows alone need ~1.1 TB: the row allocation fails (a real
+    # hipMalloc failure, not the memory limit) and the call returns
+    # FCBO_ERR_OUT_OF_MEMORY before it reads its input.  The HIP error of that
+    # allocation must not surface in later calls as their own.
+    n, m = (1 << 31) - 1, 4096
+    need = n * (m // 64) * 8
+    _, total = torch.cuda.mem_get_info()
+    assert need > 2 * total
+    with pytest.raises(torch.OutOfMemoryError):  # the device cannot hold it: nothing below can run
+        torch.empty(need // 8, dtype=torch.int64, device="cuda")
+    release_device_cache()
+    small = torch.zeros(64, dtype=torch.int64, device="cuda")
+    with pytest.raises(fca.FcboError) as e:
+        fca.fcbo_context_create(small.data_ptr(), n, m, m // 64, fca.FCBO_ROWS_ON_DEVICE, 0)
+    assert e.value.code == fca.FCBO_ERR_OUT_OF_MEMORY
+    assert_parity(synth.make_config("ctx64x16", packed=False))
+
+
 def test_output_buffers_are_checked_before_any_launch():
     rows = synth.make_config("ctx64x16")
     ctx = fca.Context(rows, 16)
@@ -446,6 +466,7 @@ def test_full_ctx50000x400_against_stored_oracle():
     # counts, SHA-256 of the ordered intents and of the ordered extent hashes
     # (every one of the 4.9 million extent rows hashed on the device), and the
     # positional digests of the store-free oracle.
+    release_device_cache()
     path = os.path.join(GOLDEN, "ctx50000x400.json")
     if not os.path.exists(path):
         pytest.skip("stored oracle values not generated")
@@ -522,6 +543,7 @@ def test_full_ctx20000x256_against_store_free_oracle():
     # lexicographic order and slices compared byte for byte.  Extents (3.5 TB in
     # all) are paged through a bounded buffer with fcbo_write_range and every
     # row hashed on the device: positional extent digest and the root's subtrees.
+    release_device_cache()
     path = os.path.join(GOLDEN, "ctx20000x256.json")
     if not os.path.exists(path):
         pytest.skip("stored oracle values not generated")

@@ -1,6 +1,6 @@
 """GPU parity of the task-pool schedule (FCBO_TASK_POOL).
 
-With the flag the level loop expands only the parents with more than 64
+With the flag the level loop expands only the parents with more than 16
 objects and the subtrees of all other concepts are enumerated depth-first, one
 task per wavefront.  The result must be the one the oracle gives, bit for bit:
 concept count, ordered intents and extents, closure tests, item pairs, the
@@ -18,6 +18,7 @@ import pytest
 import oracle
 import synth
 from tests import intent_digest as dg
+from tests.conftest import release_device_cache
 from tests.golden_io import read_fixture
 
 torch = pytest.importorskip("torch")
@@ -107,11 +108,15 @@ def test_special_contexts():
 
 
 def test_deepest_task_subtree():
-    # the contranominal scale of 64 objects padded with full columns: the root
-    # has 64 objects (a pool task) and the pool's descent reaches depth 16
-    # below it here (2^16 concepts in one task)
-    cells = synth.pad_with_full(synth.contranominal(16), extra_objects=48, extra_attrs=20)
-    res, _ = pool_parity(cells, extents=False)
+    # the contranominal scale of 16 objects padded with full columns: the root
+    # has 16 objects, the largest pool task, and the pool's descent reaches
+    # depth 16 below it (all 2^16 concepts in one task); the same scale under
+    # 48 more objects, where the level loop expands the root and the tasks
+    # start lower
+    res, _ = pool_parity(synth.pad_with_full(synth.contranominal(16), extra_attrs=20), extents=False)
+    assert res.n_concepts == 65536
+    res, _ = pool_parity(synth.pad_with_full(synth.contranominal(16), extra_objects=48, extra_attrs=20),
+                         extents=False)
     assert res.n_concepts == 65536
 
 
@@ -168,7 +173,37 @@ def test_pool_then_level_sync_on_one_context():
         ctx.close()
 
 
+def test_pool_out_of_memory_leaves_a_usable_context():
+    # A pool run that crosses the memory limit fails with FCBO_ERR_OUT_OF_MEMORY,
+    # keeps no result and releases its buffers; the same context then
+    # enumerates correctly with either schedule.
+    cells = synth.make_config("ctx2000x64", packed=False)
+    rows = synth.pack_rows(cells)
+    want = oracle.cbo(rows, 64, keep_extents=False)
+    ctx = fca.Context(rows, 64, flags=fca.FCBO_TINY_BUFFERS)
+    try:
+        ints, _ = ctx.alloc_outputs(want.n_concepts, extents=False)
+        rc, k, st = ctx.enumerate_into(ints, None, fca.FCBO_TASK_POOL)
+        assert rc == fca.FCBO_OK and k == want.n_concepts
+        ctx.set_memory_limit(st["peak_device_bytes"] * 9 // 10)  # releases what the run held
+        with pytest.raises(fca.FcboError) as e:
+            ctx.enumerate_into(ints, None, fca.FCBO_TASK_POOL)
+        assert e.value.code == fca.FCBO_ERR_OUT_OF_MEMORY
+        with pytest.raises(fca.FcboError):
+            ctx.level_counts()
+        ctx.set_memory_limit(0)
+        for flags in (0, fca.FCBO_TASK_POOL):
+            ints.fill_(-1)
+            rc, k, st = ctx.enumerate_into(ints, None, flags)
+            assert rc == fca.FCBO_OK and k == want.n_concepts
+            assert np.array_equal(ints.cpu().numpy().view(np.uint64), want.intents)
+            assert st["closure_tests"] == want.tests
+    finally:
+        ctx.close()
+
+
 def test_full_ctx50000x400_pool_against_stored_oracle():
+    release_device_cache()
     path = os.path.join(GOLDEN, "ctx50000x400.json")
     if not os.path.exists(path):
         pytest.skip("stored oracle values not generated")
