@@ -359,6 +359,8 @@ def main():
     ap.add_argument("--cpu-bitmap-tests", type=int, default=2_000_000,
                     help="closure-test budget of the bitmap oracle's prefix (0: skip)")
     ap.add_argument("--pool-steps", type=int, default=3, help="timed steps of the task-pool schedule (0: skip)")
+    ap.add_argument("--schedule", choices=("level", "pool"), default="level",
+                    help="schedule of the timed steps: level sync, or the task pool (then no separate pool run)")
     ap.add_argument("--bounded-frac", type=float, default=0.25,
                     help="bounded run: memory limit as a fraction of the unbounded step's peak (0: skip)")
     ap.add_argument("--bounded-gib", type=float, default=0.0, help="bounded run: memory limit in GiB (overrides "
@@ -431,7 +433,11 @@ def main():
     probe = hbm_probe(torch, args.hbm_probe_gib) if args.hbm_probe_gib > 0 else None
 
     ctx = fca.Context(rows, m)
-    k = ctx.count()
+    sched = fca.FCBO_TASK_POOL if args.schedule == "pool" else 0
+    if sched and m > 512:
+        print("the task-pool schedule needs at most 512 attributes", file=sys.stderr)
+        sys.exit(2)
+    k = ctx.count(pool=bool(sched))
     if args.extents == "auto":
         free, _ = torch.cuda.mem_get_info()
         extents = k * wn * 8 <= free / 3
@@ -441,11 +447,11 @@ def main():
     print("[bench] %s: K=%d, output buffers %.2f GB" % (args.workload, k, (ints.numel() + (exts.numel() if extents else 0)) * 8 / 1e9),
           file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        rc, kk, st = ctx.enumerate_into(ints, exts, 0)
+        rc, kk, st = ctx.enumerate_into(ints, exts, sched)
         assert rc == fca.FCBO_OK and kk == k
         print("[bench] warmup %d: %.3f ms" % (i, st["enumerate_ms"]), file=sys.stderr, flush=True)
     # per-kernel-class breakdown: one untimed step with an event pair around every kernel class
-    rc, kk, prof = ctx.enumerate_into(ints, exts, fca.FCBO_PROFILE)
+    rc, kk, prof = ctx.enumerate_into(ints, exts, sched | fca.FCBO_PROFILE)
     assert rc == fca.FCBO_OK and kk == k
     print("[bench] profiled step: %.3f ms" % prof["enumerate_ms"], file=sys.stderr, flush=True)
 
@@ -453,7 +459,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        rc, kk, st = ctx.enumerate_into(ints, exts, 0)
+        rc, kk, st = ctx.enumerate_into(ints, exts, sched)
         assert rc == fca.FCBO_OK and kk == k
         per_step.append(st)
     torch.cuda.synchronize()
@@ -502,7 +508,7 @@ def main():
     # the same step with the task-pool schedule (M <= 512), on a context of its
     # own so that the timed context keeps its result and its memory
     task_pool = None
-    if args.pool_steps > 0 and m <= 512:
+    if args.pool_steps > 0 and m <= 512 and not sched:
         free_before_pool = int(torch.cuda.mem_get_info()[0])
         pctx = None
         try:
@@ -632,7 +638,8 @@ def main():
         "dtype": "u64",
         "data": "synthetic",
         "config": {"workload": args.workload, "objects": n, "attributes": m, "extents_out": extents,
-                   "concepts": k, "closure_tests": tests, "levels": st0["n_levels"]},
+                   "concepts": k, "closure_tests": tests, "levels": st0["n_levels"],
+                   "schedule": "task_pool" if sched else "level_sync"},
         "closure_tests_per_s": round(tests / (ms_per_step * 1e-3), 1),
         "device_ms": {"enumerate": round(avg("enumerate_ms"), 4), "level_loop": round(loop_ms, 4),
                       "sort": round(avg("sort_ms"), 4), "output": round(out_ms, 4)},

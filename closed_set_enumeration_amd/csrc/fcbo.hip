@@ -997,7 +997,20 @@ void fcbo_context::run_pool(uint64_t K0, uint64_t obj0)
                            (const uint64_t *)cbase, K0, ptasks);
         CK_LAUNCH();
     }
-    uint64_t cap = std::max<uint64_t>(pool_cap, tiny ? (uint64_t)kWave : start_size(1u << 22, 8 * (uint64_t)wm + 24));
+    // Slots the device can hold beside what it holds now (the slots being
+    // replaced included), leaving room for the commit, which adds about as
+    // many bytes per concept to the store again.
+    const uint64_t slot_bytes = 8 * (uint64_t)wm + sizeof(PoolRec);
+    const uint64_t commit_bytes = 8 * (uint64_t)wm + 4 + 8 + 4 + 9 + 2 * (uint64_t)kPoolTaskMax;
+    auto affordable = [&]() -> uint64_t {
+        size_t free_b = 0, total_b = 0;
+        CK(hipMemGetInfo(&free_b, &total_b));
+        const double room = (double)(free_b + cap_pint * 8 + cap_prec * sizeof(PoolRec)) * 0.85;
+        return (uint64_t)(room / (double)(slot_bytes + commit_bytes));
+    };
+    uint64_t cap = pool_cap;
+    if (!cap) cap = tiny ? (uint64_t)kWave : std::min(std::max<uint64_t>(start_size(1u << 22, slot_bytes), 8 * K0),
+                                                       std::max<uint64_t>(kWave, affordable()));
     uint64_t slots = 0;
     for (int attempt = 0;; ++attempt) {
         if (attempt > 48) throw HipError{FCBO_ERR_DEVICE};
@@ -1033,21 +1046,39 @@ void fcbo_context::run_pool(uint64_t K0, uint64_t obj0)
             slots = h_counters[POOL_SLOTS];
             break;
         }
-        cap *= 2;  // the slots ran out: everything again with twice as many
+        // The slots ran out: everything again, with room for the slots used so
+        // far scaled by the share of the tasks claimed (the tasks go largest
+        // first, so this overestimates), and at least half as many again.
+        const uint64_t reserved = h_counters[POOL_SLOTS];
+        std::vector<uint64_t> claims((size_t)kPoolStripes * kCntPad);
+        CK(hipMemcpyAsync(claims.data(), task_ctr, claims.size() * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+        CK(hipStreamSynchronize(stream));
+        uint64_t started = 0;
+        for (int st = 0; st < kPoolStripes; ++st) {
+            const uint64_t in_stripe = n_tasks > (uint64_t)st ? div_up(n_tasks - st, kPoolStripes) : 0;
+            started += std::min(claims[(size_t)st * kCntPad], in_stripe);
+        }
+        const double share = std::max(1e-3, (double)started / (double)std::max<uint64_t>(1, n_tasks));
+        const uint64_t guess = (uint64_t)((double)reserved / share * 1.1) + kWave;
+        const uint64_t want = std::min(std::max(cap + cap / 2, guess), affordable());
+        if (want <= cap) throw HipError{FCBO_ERR_OUT_OF_MEMORY};
+        cap = want;
     }
     pool_cap = cap;
-    // dense store indices and list offsets of the used slots
-    ensure(dmem, nchild, cap_nch, slots, 0, stream, mc);
-    ensure(dmem, nobj, cap_nob, slots, 0, stream, mc);
-    ensure(dmem, cbase, cap_cb, slots + 1, 0, stream, mc);
-    ensure(dmem, obase, cap_ob, slots + 1, 0, stream, mc);
+    // dense store indices and list offsets of the used slots, per chunk of 64
+    const uint64_t n_chunks = slots / kWave;  // reservations are whole chunks
+    ensure(dmem, nchild, cap_nch, std::max<uint64_t>(1, n_chunks), 0, stream, mc);
+    ensure(dmem, nobj, cap_nob, std::max<uint64_t>(1, n_chunks), 0, stream, mc);
+    ensure(dmem, cbase, cap_cb, n_chunks + 1, 0, stream, mc);
+    ensure(dmem, obase, cap_ob, n_chunks + 1, 0, stream, mc);
     hipEvent_t b = prof_begin();
     {
-        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(slots, kBlock)));
-        hipLaunchKernelGGL(k_pool_flags, dim3(g), dim3(kBlock), 0, stream, (const PoolRec *)p_rec, slots, nchild, nobj);
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(n_chunks, kWavesPerBlock)));
+        hipLaunchKernelGGL(k_pool_chunk_counts, dim3(g), dim3(kBlock), 0, stream, (const PoolRec *)p_rec, n_chunks,
+                           nchild, nobj);
         CK_LAUNCH();
     }
-    scan(nchild, nobj, nullptr, slots, slots, cbase, obase, pool_ctr + POOL_TOT_N, pool_ctr + POOL_TOT_OBJ);
+    scan(nchild, nobj, nullptr, n_chunks, n_chunks, cbase, obase, pool_ctr + POOL_TOT_N, pool_ctr + POOL_TOT_OBJ);
     prof_end(FCBO_K_SCAN, b);
     CK(hipMemcpyAsync(h_counters, pool_ctr, POOL_CTR_N * sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
     CK(hipStreamSynchronize(stream));
@@ -1069,7 +1100,7 @@ void fcbo_context::run_pool(uint64_t K0, uint64_t obj0)
         C.p_int = p_int;
         C.dense = cbase;
         C.ooff = obase;
-        C.n = slots;
+        C.n_chunks = n_chunks;
         C.K0 = K0;
         C.obj0 = obj0;
         C.n_pool = np;
@@ -1082,7 +1113,7 @@ void fcbo_context::run_pool(uint64_t K0, uint64_t obj0)
         C.t_owner = t_owner;
         C.t_off = t_off;
         C.t_depth = t_depth;
-        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(slots, kBlock)));
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(65535, div_up(n_chunks, kWavesPerBlock)));
         hipLaunchKernelGGL(k_pool_commit, dim3(g), dim3(kBlock), 0, stream, C);
         CK_LAUNCH();
         // the pool's concepts have no children in the store (empty ranges)

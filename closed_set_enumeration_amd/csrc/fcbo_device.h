@@ -3012,16 +3012,24 @@ __global__ void __launch_bounds__(kWave * kPoolWaves) k_pool(PoolArgs P)
     }
 }
 
-// Pool slots [0, n): 1 for a used slot, and its object count, for the scans
-// that place the pool's concepts in the store.
-__global__ void __launch_bounds__(kBlock) k_pool_flags(const PoolRec *__restrict__ rec, uint64_t n,
-                                                       uint32_t *__restrict__ used, uint64_t *__restrict__ nobj)
+// Per chunk of 64 pool slots (the unit a wavefront reserves): its used slots
+// and their objects, for the scans that place the pool's concepts in the
+// store.  One wavefront per chunk, a lane per slot.
+__global__ void __launch_bounds__(kBlock) k_pool_chunk_counts(const PoolRec *__restrict__ rec, uint64_t n_chunks,
+                                                              uint32_t *__restrict__ used, uint64_t *__restrict__ nobj)
 {
-    for (uint64_t s = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (uint64_t)gridDim.x * blockDim.x) {
-        const PoolRec r = rec[s];
+    const int lane = lane_id();
+    for (uint64_t c = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; c < n_chunks;
+         c += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const PoolRec r = rec[c * kWave + (uint64_t)lane];
         const bool u = r.owner != kPoolFree;
-        used[s] = u ? 1u : 0u;
-        nobj[s] = u ? (uint64_t)__popcll(r.mask) : 0ull;
+        const uint32_t pc = u ? (uint32_t)__popcll(r.mask) : 0u;
+        const uint64_t bal = __ballot(u);
+        const uint32_t objs = wave_sum(pc);
+        if (lane == 0) {
+            used[c] = (uint32_t)__popcll(bal);
+            nobj[c] = objs;
+        }
     }
 }
 
@@ -3050,9 +3058,9 @@ __global__ void __launch_bounds__(kBlock) k_pool_task_list(const uint32_t *__res
 struct PoolCommitArgs {
     const PoolRec *rec;
     const uint64_t *p_int;
-    const uint64_t *dense;  // exclusive scan of the used flags
-    const uint64_t *ooff;   // exclusive scan of the object counts
-    uint64_t n;             // slots
+    const uint64_t *dense;  // per chunk of 64 slots: exclusive scan of its used slots
+    const uint64_t *ooff;   // per chunk: exclusive scan of its objects
+    uint64_t n_chunks;
     uint64_t K0, obj0;      // the store's concepts and list entries before the pool's
     uint64_t n_pool, n_obj; // the pool's concepts and list entries
     int wm;
@@ -3066,23 +3074,33 @@ struct PoolCommitArgs {
 
 // The used slots, in slot order, become store concepts K0, K0 + 1, ...: the
 // intent, the cursor, and the object list (the task's list entries at the
-// mask's bits, ascending) after the store's last list.
+// mask's bits, ascending) after the store's last list.  One wavefront per
+// chunk of 64 slots, a lane per slot.
 __global__ void __launch_bounds__(kBlock) k_pool_commit(PoolCommitArgs A)
 {
-    for (uint64_t s = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; s < A.n; s += (uint64_t)gridDim.x * blockDim.x) {
+    const int lane = lane_id();
+    for (uint64_t c = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; c < A.n_chunks;
+         c += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t s = c * kWave + (uint64_t)lane;
         const PoolRec r = A.rec[s];
-        if (r.owner == kPoolFree) continue;
-        const uint64_t i = A.dense[s], k = A.K0 + i;
-        for (int u = 0; u < A.wm; ++u) A.intents[k * A.wm + u] = A.p_int[s * A.wm + u];
-        A.cursor[k] = r.cursor;
-        const uint64_t o = A.obj0 + A.ooff[s];
-        A.loff[k] = o;
-        const uint64_t to = A.loff[r.owner];
-        uint64_t q = 0;
-        for (uint64_t m = r.mask; m; m &= m - 1ull) A.objs[o + q++] = A.objs[to + (uint64_t)(__ffsll((unsigned long long)m) - 1)];
-        A.t_owner[i] = r.owner;
-        A.t_off[i] = r.off;
-        A.t_depth[i] = (uint8_t)r.depth;
+        const bool u = r.owner != kPoolFree;
+        const uint32_t pc = u ? (uint32_t)__popcll(r.mask) : 0u;
+        const uint64_t bal = __ballot(u);
+        const uint32_t before = wave_excl_scan(pc);
+        if (u) {
+            const uint64_t i = A.dense[c] + (uint64_t)lanes_below(bal), k = A.K0 + i;
+            for (int w = 0; w < A.wm; ++w) A.intents[k * A.wm + w] = A.p_int[s * A.wm + w];
+            A.cursor[k] = r.cursor;
+            const uint64_t o = A.obj0 + A.ooff[c] + before;
+            A.loff[k] = o;
+            const uint64_t to = A.loff[r.owner];
+            uint64_t q = 0;
+            for (uint64_t m = r.mask; m; m &= m - 1ull)
+                A.objs[o + q++] = A.objs[to + (uint64_t)(__ffsll((unsigned long long)m) - 1)];
+            A.t_owner[i] = r.owner;
+            A.t_off[i] = r.off;
+            A.t_depth[i] = (uint8_t)r.depth;
+        }
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) A.loff[A.K0 + A.n_pool] = A.obj0 + A.n_obj;
 }
