@@ -87,6 +87,7 @@ class FcboStats(ctypes.Structure):
         ("batch_retries", ctypes.c_uint64),
         ("batch_splits", ctypes.c_uint64),
         ("peak_device_bytes", ctypes.c_uint64),
+        ("level_redos", ctypes.c_uint64),
     ]
 
     def as_dict(self) -> dict:

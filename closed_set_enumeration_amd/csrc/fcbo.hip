@@ -143,7 +143,7 @@ struct LevelLog {
 
 // Work counts of an enumeration, summed over its levels.
 struct Totals {
-    uint64_t tests = 0, pairs = 0, sum_c = 0;
+    uint64_t tests = 0, pairs = 0, sum_c = 0, redos = 0;
     uint64_t local_parents = 0, local_objs = 0, med_parents = 0, med_objs = 0;
     uint64_t big_parents = 0, big_tests = 0, big_scan = 0, big_nzw = 0, big_cobjs = 0;
 };
@@ -555,7 +555,7 @@ struct fcbo_context {
                            void *user, uint32_t flags, fcbo_stats &st);
     void capture_seeds(uint64_t first, uint64_t count, uint64_t obj_lo, uint64_t obj_hi, uint64_t level);
     void release_seeds();
-    LevelCursor load_seeds(const SeedSet &S, uint64_t a, uint64_t B);
+    LevelCursor load_seeds(const SeedSet &S, uint64_t a, uint64_t B, bool announce_classes = true);
     void harvest_marks(fcbo_stats &st);
     void drain();
     void order_concepts();
@@ -867,6 +867,7 @@ void fcbo_context::run_levels(LevelCursor &s, uint64_t max_levels)
                 ensure(dmem, pass, cap_pass, std::max<uint64_t>(1, h_counters[CNT_HUGE]) * wm, 0, stream, mc);
                 redo = true;
                 ++redos;
+                ++tot.redos;
                 continue;
             }
             if (h_counters[CNT_OVERFLOW]) {
@@ -889,6 +890,7 @@ void fcbo_context::run_levels(LevelCursor &s, uint64_t max_levels)
                 ensure_local_records(lstripe_max * kRecStripes / 4 * 5);
                 redo = true;
                 ++redos;
+                ++tot.redos;
                 continue;
             }
             n_children = h_counters[CNT_CHILDREN];
@@ -1247,7 +1249,7 @@ void fcbo_context::release_seeds()
 
 // Seeds [a, a + B) of S become level 1 of the store under a stand-in root at
 // index 0 (its first-child link stays 1; the level loop rewrites the rest).
-LevelCursor fcbo_context::load_seeds(const SeedSet &S, uint64_t a, uint64_t B)
+LevelCursor fcbo_context::load_seeds(const SeedSet &S, uint64_t a, uint64_t B, bool announce_classes)
 {
     const uint64_t mc = min_cap();
     const uint64_t o0 = S.h_loff[a], o1 = S.h_loff[a + B];
@@ -1268,8 +1270,10 @@ LevelCursor fcbo_context::load_seeds(const SeedSet &S, uint64_t a, uint64_t B)
     bs.lo = 1;
     bs.P = B;
     bs.obj_hi = (uint64_t)n + (o1 - o0);
+    // the seeds' classes, so the level loop launches the kernels they need
+    // (without them it finds the classes on the level and runs it again)
     const uint64_t mid_max = wm <= 8 ? (uint64_t)kMidMax : (uint64_t)kSmallMax;
-    for (uint64_t i = a; i < a + B; ++i) {
+    for (uint64_t i = a; i < a + B && announce_classes; ++i) {
         const uint64_t sz = S.h_loff[i + 1] - S.h_loff[i];
         bs.next_huge += sz > mid_max;
         bs.next_mid += sz > (uint64_t)kSmallMax && sz <= mid_max;
@@ -1389,7 +1393,7 @@ void fcbo_context::enumerate_bounded(uint64_t *intents_buf, uint64_t *extents_bu
         bool fits = !force_split;
         if (fits) try {
             CK(hipEventRecord(b0, stream));
-            LevelCursor bs = load_seeds(seeds[si], a, B);
+            LevelCursor bs = load_seeds(seeds[si], a, B, !one_per_batch);
             run_levels(bs, ~0ull);
             K = bs.lo;
             have_result = true;
@@ -1609,6 +1613,7 @@ void fcbo_context::fill_counts(fcbo_stats &st, uint64_t k) const
     st.big_nonzero_words = tot.big_nzw;
     st.big_child_objects = tot.big_cobjs;
     st.order_launches = order_launches;
+    st.level_redos = tot.redos;
 }
 
 // The context on the device: rows copied and masked, columns transposed.

@@ -76,7 +76,9 @@ enum {
 
 /* fcbo_enumerate_bounded flags (besides FCBO_PROFILE) */
 #define FCBO_ONE_SUBTREE_PER_BATCH 4u /* test hook: every batch takes a single subtree, so the
-                                         batch path runs on any input */
+                                         batch path runs on any input; its seeds' parent classes
+                                         are not announced to the level loop, which then finds
+                                         them on the level and runs the level again */
 #define FCBO_SPLIT_ROOT_CHILDREN 8u   /* test hook: every child of the root is split one level
                                          down as if its subtree did not fit */
 
@@ -156,6 +158,8 @@ typedef struct {
     uint64_t batch_splits;      /* single subtrees that did not fit and were split one level down */
     uint64_t peak_device_bytes; /* most device memory the enumeration buffers held at once during
                                    the call (buffers kept from earlier calls included) */
+    uint64_t level_redos;       /* levels run again: a record buffer overflowed, or parents of a
+                                   class the level loop was not told about turned up */
 } fcbo_stats;
 
 /*

@@ -92,7 +92,12 @@ def test_hand_derived_examples(name):
 @pytest.mark.parametrize("name", ["ctx64x16", "ctx2000x64", "ctx10000x128"])
 @pytest.mark.parametrize("flags", [0, fca.FCBO_TINY_BUFFERS])
 def test_seeded_contexts(name, flags):
-    assert_parity(synth.make_config(name, packed=False), flags=flags)
+    res = assert_parity(synth.make_config(name, packed=False), flags=flags)
+    if flags & fca.FCBO_TINY_BUFFERS:
+        # buffers start at their minimum: record buffers overflow and levels run again
+        assert res.stats["level_redos"] >= 1
+    else:
+        assert res.stats["level_redos"] == 0
 
 
 # --- edge shapes: word boundaries on both axes, ragged tails ---------------------------
