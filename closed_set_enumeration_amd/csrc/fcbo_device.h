@@ -30,6 +30,13 @@
 // After the last level the output order comes from the CbO tree (subtree sizes
 // bottom-up, positions top-down), k_output_intents and k_output_block write the
 // caller's rows.
+//
+// The task pool (an alternative schedule, section at the end): the level loop
+// expands only the parents with more than kPoolTaskMax objects, and k_pool
+// enumerates the subtree of every smaller concept depth-first, one wavefront
+// per task; k_pool_commit moves its concepts into the store, k_tail_position
+// places them after their tasks, k_pool_stats counts over the whole store.
+// Lattice cover edges (k_cover_*) are computed from a finished store.
 #pragma once
 
 #include <hip/hip_runtime.h>
