@@ -396,13 +396,16 @@ def main():
             print("```")
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
     import synth
 
     n, m, _ = synth.CONFIGS[args.workload]
+    if args.schedule == "pool" and m > 512:
+        print("the task-pool schedule needs at most 512 attributes (%s has %d)" % (args.workload, m), file=sys.stderr)
+        sys.exit(2)
     rows = synth.make_config(args.workload)
     wn, wm = (n + 63) // 64, (m + 63) // 64
 
@@ -434,9 +437,6 @@ def main():
 
     ctx = fca.Context(rows, m)
     sched = fca.FCBO_TASK_POOL if args.schedule == "pool" else 0
-    if sched and m > 512:
-        print("the task-pool schedule needs at most 512 attributes", file=sys.stderr)
-        sys.exit(2)
     k = ctx.count(pool=bool(sched))
     if args.extents == "auto":
         free, _ = torch.cuda.mem_get_info()

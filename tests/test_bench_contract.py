@@ -29,3 +29,40 @@ def test_output_byte_model_counts_reads_and_writes():
     assert bench.kernel_bytes("output", st, wm=2, wn=3, n=130, k=3, extents=False) == intents_only
     got = bench.kernel_bytes("output", st, wm=2, wn=3, n=130, k=3, extents=True)
     assert got == intents_only + 3 * (4 + 16) + (130 + 5) * 4 + 3 * 24
+
+
+def test_traffic_records_are_kept_only_for_the_sources_they_were_taken_on(tmp_path, monkeypatch):
+    # A counter summary holds one record per kernel class with the hash of the
+    # device sources it was measured on; a record whose hash differs from the
+    # sources in the tree is dropped, so a changed kernel reports no traffic.
+    csrc = tmp_path / "closed_set_enumeration_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "fcbo_device.h").write_bytes(b"device header\n")
+    (csrc / "fcbo.hip").write_bytes(b"host source\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    sha = bench.source_sha256()
+    (tmp_path / "profiles" / "w_traffic.md").write_text(
+        "# summary\n"
+        "traffic-record: class=output source_sha256=%s fetch=1 write=2\n"
+        "traffic-record: class=level_loop source_sha256=%s fetch=3 write=4\n"
+        "not a record: class=other\n" % (sha, "0" * 64))
+    got = bench.profile_records("w")
+    assert list(got) == ["output"]
+    assert got["output"]["fetch"] == "1" and got["output"]["write"] == "2"
+    assert bench.profile_records("missing") == {}
+    (csrc / "fcbo.hip").write_bytes(b"host source, edited\n")
+    assert bench.profile_records("w") == {}
+
+
+def test_task_pool_schedule_beyond_512_attributes_is_refused_before_any_device_work(monkeypatch):
+    import synth
+
+    monkeypatch.setitem(synth.CONFIGS, "wide", (10, 513, None))
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "wide", "--schedule", "pool", "--no-cpu"])
+    try:
+        bench.main()
+    except SystemExit as e:
+        assert e.code == 2
+    else:
+        raise AssertionError("bench.main() accepted 513 attributes with the task pool")
