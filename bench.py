@@ -17,7 +17,8 @@ Prints one JSON line.  `value` is concepts per second; beside it:
     scans, child writes, the per-level host wait), the library's algorithmic
     byte count `model_bytes` over its measured time;
   * `hbm_probe`: a device copy and a fill timed in the same process, the
-    achievable bandwidth on this box;
+    achievable bandwidth on this machine, and a fill of the extent buffer itself
+    (the store rate a destination of that size allows);
   * `cover_edges`: the lattice's cover edges of the same result
     (fcbo_cover_edges), timed once after the steps;
   * `host_stream`: the first rows of the ordered output streamed to pinned
@@ -446,6 +447,19 @@ def main():
     ints, exts = ctx.alloc_outputs(k, extents)
     print("[bench] %s: K=%d, output buffers %.2f GB" % (args.workload, k, (ints.numel() + (exts.numel() if extents else 0)) * 8 / 1e9),
           file=sys.stderr, flush=True)
+    if probe and extents:
+        # the store rate this destination allows: a fill of the extent buffer itself
+        # (a 30 GB buffer fills slower than the 4 GiB probe)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        best = None
+        for _ in range(3):
+            e[0].record()
+            exts.zero_()
+            e[1].record()
+            torch.cuda.synchronize()
+            best = e[0].elapsed_time(e[1]) if best is None else min(best, e[0].elapsed_time(e[1]))
+        probe["output_buffer_fill"] = {"bytes": exts.numel() * 8, "ms": round(best, 4),
+                                       "GBps": round(exts.numel() * 8 / (best * 1e-3) / 1e9, 1)}
     for i in range(args.warmup):
         rc, kk, st = ctx.enumerate_into(ints, exts, sched)
         assert rc == fca.FCBO_OK and kk == k
@@ -488,6 +502,8 @@ def main():
             "traffic": (int(rec["fetch_bytes_per_launch"]) + int(rec["write_bytes_per_launch"])) if rec else None,
             "bytes_per_launch": int(out_bytes), "avg_launch_ms": round(out_ms, 4),
             "frac_of_fill_probe": round(achieved / probe["fill_GBps"], 4) if probe else None,
+            "frac_of_output_buffer_fill": (round(achieved / probe["output_buffer_fill"]["GBps"], 4)
+                                           if probe and "output_buffer_fill" in probe else None),
             "timing": "timed steps, HIP events around the output phase"}
 
     # the closure kernels: the level loop against the model byte count
