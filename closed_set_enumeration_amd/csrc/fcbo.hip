@@ -280,9 +280,15 @@ struct fcbo_context {
     uint32_t *ccount = nullptr;   // covers per output position
     uint64_t *coff = nullptr;     // their exclusive scan
     uint32_t *cbig = nullptr;     // positions of the concepts with more than 64 objects
-    uint64_t *cctr = nullptr;     // [0] their number, [1] covers not found
+    uint64_t *cctr = nullptr;     // [0] their number, [1] covers not found, [2] scratch used, [3] scratch short
     bool have_cover_counts = false;  // ccount / coff / cbig hold the last result's
     uint64_t cover_total = 0;
+    // with the counts: the table of concepts by intent is built, and the covers'
+    // positions are kept in cscratch (one run per concept, starting at csstart)
+    bool cover_table_ok = false, cover_kept = false;
+    uint64_t cap_cscratch = 0, cap_csstart = 0;
+    uint32_t *cscratch = nullptr;
+    uint64_t *csstart = nullptr;
 
     // seed sets of a bounded enumeration, the deepest last
     std::vector<SeedSet> seeds;
@@ -419,6 +425,7 @@ struct fcbo_context {
         dfree(dmem, rank, cap_rank); dfree(dmem, perm, cap_perm);
         dfree(dmem, ctable, cap_ctable); dfree(dmem, ccount, cap_ccount); dfree(dmem, coff, cap_coff);
         dfree(dmem, cbig, cap_cbig); dfree(dmem, cctr, cap_cctr);
+        dfree(dmem, cscratch, cap_cscratch); dfree(dmem, csstart, cap_csstart);
         release_seeds();
         release_pool();
         for (int b = 0; b < 2; ++b) {
@@ -770,6 +777,9 @@ void fcbo_context::start_root(LevelCursor &s)
     // nothing of an earlier result survives a failure part-way through
     have_result = have_perm = have_cover_counts = have_levels = pool_result = false;
     K = 0;
+    // the last result's cover runs (their room goes to the enumeration)
+    dfree(dmem, cscratch, cap_cscratch);
+    dfree(dmem, csstart, cap_csstart);
     ensure(dmem, intents, cap_int, (uint64_t)wm * 1024, 0, stream, mc);
     ensure(dmem, cursor, cap_cur, 1024, 0, stream, mc);
     ensure(dmem, loff, cap_loff, 1025, 0, stream, mc);
@@ -1709,48 +1719,103 @@ uint64_t fcbo_context::cover_edges(uint64_t *offsets_out, uint32_t *targets_out,
     CK(hipStreamSynchronize(stream));
     free_level_scratch();  // the cover buffers of 10^9 concepts need that room
     const uint64_t mc = min_cap();
-    if (!have_cover_counts) {
-        ensure(dmem, ccount, cap_ccount, K, 0, stream, mc);
-        ensure(dmem, coff, cap_coff, K + 1, 0, stream, mc);
-        ensure(dmem, cbig, cap_cbig, K, 0, stream, mc);
-        ensure(dmem, cctr, cap_cctr, 2, 0, stream, 2);
-        clear_words(cctr, 2);
-    }
     CoverArgs C;
     memset(&C, 0, sizeof(C));
     C.rows = rows; C.intents = intents; C.cursor = cursor; C.fchild = fchild; C.rank = rank;
     C.loff = loff; C.objs = objs; C.perm = perm;
     C.K = K; C.m = (int)m; C.wm = wm; C.tail_m = tail_m;
     C.small_max = wm <= 8 ? kSmallMax : -1;
-    C.big = cbig; C.ctr = cctr; C.count = ccount; C.offsets = coff; C.targets = targets_out;
     const cover_fn fn = pick_cover_fn(wm);
+    uint64_t slots = 1024;
+    while (slots < 2 * K) slots *= 2;
+    auto build_table = [&]() {
+        ensure(dmem, ctable, cap_ctable, slots, 0, stream, mc);
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(16384, div_up(slots, kBlock)));
+        hipLaunchKernelGGL(k_fill_u64, dim3(g), dim3(kBlock), 0, stream, (uint64_t *)ctable, slots / 2, ~0ull);
+        CK_LAUNCH();
+        C.table = ctable;
+        C.table_mask = slots - 1;
+        fn(C, 0, stream, n_cu);
+        cover_table_ok = true;
+    };
     if (!have_cover_counts) {
-        // counts kept until the next enumeration: a count call and the call
-        // that writes take one counting pass together
+        cover_table_ok = cover_kept = false;
+        ensure(dmem, ccount, cap_ccount, K, 0, stream, mc);
+        ensure(dmem, coff, cap_coff, K + 1, 0, stream, mc);
+        ensure(dmem, cbig, cap_cbig, K, 0, stream, mc);
+        ensure(dmem, cctr, cap_cctr, 4, 0, stream, 4);
+        clear_words(cctr, 4);
+    }
+    C.big = cbig; C.ctr = cctr; C.count = ccount; C.offsets = coff; C.targets = targets_out;
+    if (cover_table_ok) {
+        C.table = ctable;
+        C.table_mask = slots - 1;
+    }
+    if (!have_cover_counts) {
+        // Counts kept until the next enumeration: a count call and the call
+        // that writes take one counting pass together.  When the room is
+        // there, that pass also keeps every cover's position (one run per
+        // concept), so the writing call only moves the runs; the room is
+        // guessed (8 covers a concept on average, plus the wavefronts' part-used
+        // chunks) and the writing call falls back to a second pass over the
+        // concepts if it ran out.
         const unsigned gl = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(4096, div_up(K, kBlock)));
         hipLaunchKernelGGL(k_cover_list_big, dim3(gl), dim3(kBlock), 0, stream, C);
         CK_LAUNCH();
-        fn(C, 1, stream, n_cu);
+        const uint64_t local_waves = std::min<uint64_t>(16384, div_up(K, kWavesPerBlock)) * kWavesPerBlock;
+        // (FCBO_TINY_BUFFERS: two chunks, so the fallback runs on any input)
+        const uint64_t entries = tiny ? 2 * kCoverChunk : 8 * K + kCoverChunk * local_waves + 4096;
+        const uint64_t need = entries * 4 + K * 8 + (cap_ctable >= slots ? 0 : slots * 4);
+        size_t free_b = 0, total_b = 0;
+        CK(hipMemGetInfo(&free_b, &total_b));
+        bool keep = !fixed && need + need / 4 < (uint64_t)free_b && (!dmem.limit || dmem.held + need <= dmem.limit);
+        if (keep) {
+            try {
+                ensure(dmem, cscratch, cap_cscratch, entries, 0, stream, mc);
+                ensure(dmem, csstart, cap_csstart, K, 0, stream, mc);
+                build_table();
+            } catch (const HipError &e) {
+                if (e.code != FCBO_ERR_OUT_OF_MEMORY) throw;
+                dfree(dmem, cscratch, cap_cscratch);
+                dfree(dmem, csstart, cap_csstart);
+                keep = false;
+            }
+        }
+        if (keep) {
+            C.scratch = cscratch;
+            C.scratch_cap = cap_cscratch;
+            C.sstart = csstart;
+        }
+        fn(C, keep ? kCoverKeep : kCoverCount, stream, n_cu);
         scan(ccount, nullptr, nullptr, K, K, coff, nullptr, nullptr, nullptr);
+        uint64_t h[3] = {0, 0, 0};  // covers not found, scratch entries used, scratch short
         CK(hipMemcpyAsync(&cover_total, coff + K, sizeof(uint64_t), hipMemcpyDeviceToHost, stream));
+        CK(hipMemcpyAsync(h, cctr + 1, sizeof(h), hipMemcpyDeviceToHost, stream));
         CK(hipStreamSynchronize(stream));
+        if (h[0]) throw HipError{FCBO_ERR_DEVICE};  // a cover that is not a concept: cannot happen
+        cover_kept = keep && !h[2];
+        if (keep && !cover_kept) {  // the runs are of no use
+            dfree(dmem, cscratch, cap_cscratch);
+            dfree(dmem, csstart, cap_csstart);
+        }
         have_cover_counts = true;
     }
     const uint64_t e = cover_total;
     if (!offsets_out || !targets_out || capacity < e) return e;
-    clear_words(cctr + 1, 1);
-    uint64_t slots = 1024;
-    while (slots < 2 * K) slots *= 2;
-    ensure(dmem, ctable, cap_ctable, slots, 0, stream, mc);
-    {
-        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(16384, div_up(slots, kBlock)));
-        hipLaunchKernelGGL(k_fill_u64, dim3(g), dim3(kBlock), 0, stream, (uint64_t *)ctable, slots / 2, ~0ull);
+    if (cover_kept) {
+        C.scratch = cscratch;
+        C.scratch_cap = cap_cscratch;
+        C.sstart = csstart;
+        const unsigned g = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(16384, div_up(K, kBlock)));
+        hipLaunchKernelGGL(k_cover_copy_runs, dim3(g), dim3(kBlock), 0, stream, C);
         CK_LAUNCH();
+        CK(hipMemcpyAsync(offsets_out, coff, (K + 1) * sizeof(uint64_t), hipMemcpyDeviceToDevice, stream));
+        CK(hipStreamSynchronize(stream));
+        return e;
     }
-    C.table = ctable;
-    C.table_mask = slots - 1;
-    fn(C, 0, stream, n_cu);
-    fn(C, 2, stream, n_cu);
+    clear_words(cctr + 1, 1);
+    if (!cover_table_ok) build_table();
+    fn(C, kCoverWrite, stream, n_cu);
     CK(hipMemcpyAsync(offsets_out, coff, (K + 1) * sizeof(uint64_t), hipMemcpyDeviceToDevice, stream));
     uint64_t missing = 0;
     CK(hipMemcpyAsync(&missing, cctr + 1, sizeof(uint64_t), hipMemcpyDeviceToHost, stream));

@@ -2397,11 +2397,24 @@ struct CoverArgs {
     int64_t small_max;        // concepts with at most this many objects take the wavefront kernel
     uint64_t tail_m;
     uint32_t *big;            // output positions of the other concepts
-    uint64_t *ctr;            // [0]: their number, [1]: covers not found among the intents (stays 0)
-    uint32_t *count;          // pass 1: covers per output position
+    uint64_t *ctr;            // [0]: their number, [1]: covers not found among the intents (stays 0),
+                              // [2]: scratch entries handed out, [3]: set when the scratch ran out
+    uint32_t *count;          // passes 1 and 3: covers per output position
     const uint64_t *offsets;  // pass 2: their exclusive scan
     uint32_t *targets;        // pass 2: output positions of the covers
+    uint32_t *scratch;        // pass 3: every concept's covers' positions, one run per concept
+    uint64_t scratch_cap;     // entries
+    uint64_t *sstart;         // pass 3: start of each concept's run in scratch
 };
+
+// The passes of the cover kernels: 1 counts the covers of every concept; 2
+// (after the scan of the counts) writes their positions to the caller's
+// targets; 3 counts them and keeps their positions in the scratch buffer, one
+// run per concept, which k_cover_copy_runs moves to the targets after the scan.
+constexpr int kCoverCount = 1, kCoverWrite = 2, kCoverKeep = 3;
+// Scratch entries a wavefront of k_cover_local takes at a time (concepts with
+// more covers reserve their run alone).
+constexpr uint32_t kCoverChunk = 128;
 
 // Every concept into the table, keyed by its intent.
 template <int WMC>
@@ -2480,11 +2493,15 @@ __global__ void __launch_bounds__(kBlock) k_cover_local(CoverArgs C, int pass)
     static_assert(WMC <= 8, "the wavefront cover kernel keeps rows of at most 8 words in LDS");
     __shared__ uint64_t s_rows[kWavesPerBlock][kWave * WMC];
     __shared__ uint8_t s_cnt[kWavesPerBlock][64 * WMC];
+    __shared__ uint32_t s_run[kWavesPerBlock][64 * WMC];  // pass 3: the concept's covers' positions
     const int lane = lane_id();
     const int wv = threadIdx.x / kWave;
     const int wm = words_of<WMC>(C.wm);
     uint64_t *R = s_rows[wv];
     uint8_t *CN = s_cnt[wv];
+    uint32_t *RUN = s_run[wv];
+    uint64_t chunk = 0;             // pass 3: the wavefront's scratch chunk
+    uint32_t used = kCoverChunk;    // entries of it taken
     for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + wv; i < C.K; i += (uint64_t)gridDim.x * kWavesPerBlock) {
         const uint64_t c = C.perm[i];
         const uint64_t o0 = C.loff[c], a64 = C.loff[c + 1] - o0;
@@ -2516,7 +2533,8 @@ __global__ void __launch_bounds__(kBlock) k_cover_local(CoverArgs C, int pass)
         if (!any) {
             // every attribute outside B gives the bottom
             ncov = full ? 0u : 1u;
-            if (pass == 2 && ncov && lane == 0) C.targets[C.offsets[i]] = (uint32_t)(C.K - 1);
+            if (pass == kCoverWrite && ncov && lane == 0) C.targets[C.offsets[i]] = (uint32_t)(C.K - 1);
+            if (pass == kCoverKeep && ncov && lane == 0) RUN[0] = (uint32_t)(C.K - 1);
         } else {
             wave_sync();
             // lane b: cm[u] = the objects having attribute 64u + b; counts to LDS
@@ -2569,15 +2587,56 @@ __global__ void __launch_bounds__(kBlock) k_cover_local(CoverArgs C, int pass)
                     }
                 }
                 const uint64_t emit = __ballot(is_cover);
-                if (pass == 2 && is_cover) {
+                if (pass != kCoverCount && is_cover) {
                     const uint32_t pos = cover_position<WMC>(C, c, 64 * u + lane, D);
-                    C.targets[C.offsets[i] + ncov + (uint32_t)__popcll(emit & ~upto_mask(lane))] = pos;
+                    const uint32_t k = ncov + (uint32_t)__popcll(emit & ~upto_mask(lane));
+                    if (pass == kCoverWrite) C.targets[C.offsets[i] + k] = pos;
+                    else RUN[k] = pos;
                 }
                 ncov += (uint32_t)__popcll(emit);
             }
         }
-        if (pass == 1 && lane == 0) C.count[i] = ncov;
+        if (pass != kCoverWrite && lane == 0) C.count[i] = ncov;
+        if (pass == kCoverKeep && ncov) {
+            // the run goes to the wavefront's chunk (a new chunk when it does not
+            // fit; a run longer than a chunk is reserved on its own)
+            uint64_t at = 0;
+            if (ncov > kCoverChunk) {
+                if (lane == 0) at = atomicAdd((unsigned long long *)&C.ctr[2], (unsigned long long)ncov);
+                at = uniform64(at);
+            } else {
+                if (used + ncov > kCoverChunk) {
+                    uint64_t b = 0;
+                    if (lane == 0) b = atomicAdd((unsigned long long *)&C.ctr[2], (unsigned long long)kCoverChunk);
+                    chunk = uniform64(b);
+                    used = 0;
+                }
+                at = chunk + used;
+                used += ncov;
+            }
+            wave_sync();  // RUN written by other lanes above
+            const bool fits = at + ncov <= C.scratch_cap;
+            if (fits)
+                for (uint32_t k = (uint32_t)lane; k < ncov; k += kWave) C.scratch[at + k] = RUN[k];
+            if (lane == 0) {
+                C.sstart[i] = at;
+                if (!fits) C.ctr[3] = 1;
+            }
+        }
         wave_sync();
+    }
+}
+
+// Pass 3's runs to the caller's targets: concept i's run of count[i] positions
+// from scratch[sstart[i]] to targets[offsets[i]], one thread per concept.
+__global__ void __launch_bounds__(kBlock) k_cover_copy_runs(CoverArgs C)
+{
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < C.K; i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint32_t n = C.count[i];
+        if (!n) continue;
+        const uint32_t *src = C.scratch + C.sstart[i];
+        uint32_t *dst = C.targets + C.offsets[i];
+        for (uint32_t k = 0; k < n; ++k) dst[k] = src[k];
     }
 }
 
@@ -2663,7 +2722,15 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
             bool full = true;
             for (int u = 0; u < wm; ++u) full = full && (Bp[u] == (u == wm - 1 ? C.tail_m : ~0ull));
             found = full ? 0u : 1u;
-            if (pass == 2 && found && tid == 0) C.targets[C.offsets[i]] = (uint32_t)(C.K - 1);
+            if (pass == kCoverWrite && found && tid == 0) C.targets[C.offsets[i]] = (uint32_t)(C.K - 1);
+            if (pass == kCoverKeep && tid == 0) {
+                uint64_t at = 0;
+                if (found) at = atomicAdd((unsigned long long *)&C.ctr[2], 1ull);
+                const bool fits = at + found <= C.scratch_cap;
+                if (found && fits) C.scratch[at] = (uint32_t)(C.K - 1);
+                C.sstart[i] = at;
+                if (!fits) C.ctr[3] = 1;
+            }
         } else {
             __syncthreads();
             for (uint32_t s0 = 0; s0 < ncand; s0 += kCoverSlice) {
@@ -2710,7 +2777,7 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
                     }
                     if (ok) {
                         uint32_t pos = 0;
-                        if (pass == 2) {
+                        if (pass != kCoverCount) {
                             uint64_t d[WS];
                             for (int v = 0; v < wm; ++v) d[v] = (v == wm - 1) ? (D[v] & C.tail_m) : D[v];
                             pos = cover_position<WS>(C, c, n, d);
@@ -2728,13 +2795,33 @@ __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pa
             for (int n = hi - 1; n >= lo; --n) nmine += s_pos[n] != 0xFFFFFFFFu ? 1u : 0u;
             uint32_t before;
             found = cover_block_scan(nmine, before, s_sum);
-            if (pass == 2) {
-                uint64_t w = C.offsets[i] + before;
+            uint64_t w = 0;
+            bool fits = true;
+            if (pass == kCoverWrite) {
+                w = C.offsets[i] + before;
+            } else if (pass == kCoverKeep) {
+                // the concept's run: one reservation for the workgroup
+                if (tid == 0) s_sum[0] = 0;
+                __syncthreads();
+                if (tid == 0 && found) {
+                    const uint64_t at = atomicAdd((unsigned long long *)&C.ctr[2], (unsigned long long)found);
+                    s_sum[0] = (uint32_t)at;
+                    s_sum[1] = (uint32_t)(at >> 32);
+                    C.sstart[i] = at;
+                    if (at + found > C.scratch_cap) C.ctr[3] = 1;
+                }
+                __syncthreads();
+                const uint64_t at = found ? ((uint64_t)s_sum[0] | ((uint64_t)s_sum[1] << 32)) : 0ull;
+                fits = at + found <= C.scratch_cap;
+                w = at + before;
+            }
+            if (pass != kCoverCount && fits) {
+                uint32_t *out = pass == kCoverWrite ? C.targets : C.scratch;
                 for (int n = hi - 1; n >= lo; --n)
-                    if (s_pos[n] != 0xFFFFFFFFu) C.targets[w++] = s_pos[n];
+                    if (s_pos[n] != 0xFFFFFFFFu) out[w++] = s_pos[n];
             }
         }
-        if (pass == 1 && tid == 0) C.count[i] = found;
+        if (pass != kCoverWrite && tid == 0) C.count[i] = found;
         __syncthreads();
     }
 }
