@@ -1686,7 +1686,13 @@ void launch_cover(const CoverArgs &C, int pass, hipStream_t s, int n_cu)
         hipLaunchKernelGGL(k_cover_local<WMC>, dim3(g), dim3(kBlock), 0, s, C, pass);
         CK_LAUNCH();
     }
-    hipLaunchKernelGGL(k_cover_big<WMC>, dim3((unsigned)(4 * n_cu)), dim3(kCoverThreads), 0, s, C, pass);
+    // as many workgroups as fit the compute units (the big concepts are few
+    // and their passes wait on memory)
+    const size_t lds = cover_big_lds<WMC>(C.m);
+    int per_cu = 1;
+    CK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_cover_big<WMC>, kCoverThreads, lds));
+    hipLaunchKernelGGL(k_cover_big<WMC>, dim3((unsigned)(std::max(1, per_cu) * n_cu)), dim3(kCoverThreads), lds, s, C,
+                       pass);
     CK_LAUNCH();
 }
 

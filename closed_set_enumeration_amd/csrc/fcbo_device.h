@@ -2482,9 +2482,41 @@ __device__ __forceinline__ uint32_t cover_position(const CoverArgs &C, uint64_t 
     return kCoverEmpty;
 }
 
+// 1 when any of the lane's flags is set
+template <int N>
+__device__ __forceinline__ uint32_t live_any(const bool (&f)[N])
+{
+    uint32_t r = 0;
+#pragma unroll
+    for (int u = 0; u < N; ++u) r |= f[u] ? 1u : 0u;
+    return r;
+}
+
+// 64 x 64 bit transpose across the wavefront: lane l holds row l on entry and
+// column l on return (bit o of the result is bit l of row o).  Six butterfly
+// stages; in the stage of distance j, lanes l and l ^ j exchange the half
+// blocks that cross the diagonal (the recursive block transpose, done with
+// one lane per row).
+__device__ __forceinline__ uint64_t wave_transpose64(uint64_t x)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+        const int j = 32 >> s;
+        // bits whose index has the bit j clear
+        const uint64_t m = s == 0 ? 0x00000000FFFFFFFFull : s == 1 ? 0x0000FFFF0000FFFFull
+                         : s == 2 ? 0x00FF00FF00FF00FFull : s == 3 ? 0x0F0F0F0F0F0F0F0Full
+                         : s == 4 ? 0x3333333333333333ull : 0x5555555555555555ull;
+        const uint64_t p = __shfl_xor(x, j);
+        x = (lane & j) ? ((x & ~m) | ((p >> j) & m)) : ((x & m) | ((p << j) & ~m));
+    }
+    return x;
+}
+
 // Concepts with at most 64 objects, one wavefront each.  The object rows are
-// staged in LDS; lane b builds, for every intent word u, the mask of the
-// objects having attribute 64u + b from broadcast reads of the staged rows.
+// staged in LDS; lane b gets, for every intent word u, the mask of the objects
+// having attribute 64u + b: a transpose of the wavefront's rows (one object a
+// lane), or for a few objects broadcast reads of the staged rows.
 // When no object carries an attribute outside B the one lower cover is the
 // bottom (for every concept but the bottom itself).
 template <int WMC>
@@ -2492,14 +2524,16 @@ __global__ void __launch_bounds__(kBlock) k_cover_local(CoverArgs C, int pass)
 {
     static_assert(WMC <= 8, "the wavefront cover kernel keeps rows of at most 8 words in LDS");
     __shared__ uint64_t s_rows[kWavesPerBlock][kWave * WMC];
-    __shared__ uint8_t s_cnt[kWavesPerBlock][64 * WMC];
-    __shared__ uint32_t s_run[kWavesPerBlock][64 * WMC];  // pass 3: the concept's covers' positions
+    __shared__ uint32_t s_pos[kWavesPerBlock][64 * WMC];  // passes 2, 3: position of the cover emitted by n
+    __shared__ uint64_t s_cmax[kWavesPerBlock][kWave];    // passes 2, 3: a batch of covers' objects
+    __shared__ uint16_t s_emit[kWavesPerBlock][kWave];    // and their emitters
     const int lane = lane_id();
     const int wv = threadIdx.x / kWave;
     const int wm = words_of<WMC>(C.wm);
     uint64_t *R = s_rows[wv];
-    uint8_t *CN = s_cnt[wv];
-    uint32_t *RUN = s_run[wv];
+    uint32_t *POS = s_pos[wv];
+    uint64_t *CMX = s_cmax[wv];
+    uint16_t *EMT = s_emit[wv];
     uint64_t chunk = 0;             // pass 3: the wavefront's scratch chunk
     uint32_t used = kCoverChunk;    // entries of it taken
     for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + wv; i < C.K; i += (uint64_t)gridDim.x * kWavesPerBlock) {
@@ -2521,106 +2555,154 @@ __global__ void __launch_bounds__(kBlock) k_cover_local(CoverArgs C, int pass)
         const bool mine = lane < a;
         const uint64_t g = mine ? C.objs[o0 + lane] : 0;
         uint64_t cand[WMC];  // attributes outside B carried by some object
+        uint64_t row[WMC];   // this lane's object's row (zero past the last object)
         uint64_t any = 0;
 #pragma unroll
         for (int u = 0; u < WMC; ++u) {
-            const uint64_t r = (mine && u < wm) ? C.rows[g * C.wm + u] : 0ull;
-            R[lane * WMC + u] = r;
-            cand[u] = (u < wm) ? (wave_or(r) & ~B[u]) : 0ull;
+            row[u] = (mine && u < wm) ? C.rows[g * C.wm + u] : 0ull;
+            R[lane * WMC + u] = row[u];
+            cand[u] = (u < wm) ? (wave_or(row[u]) & ~B[u]) : 0ull;
             any |= cand[u];
         }
-        uint32_t ncov = 0;
-        if (!any) {
-            // every attribute outside B gives the bottom
-            ncov = full ? 0u : 1u;
-            if (pass == kCoverWrite && ncov && lane == 0) C.targets[C.offsets[i]] = (uint32_t)(C.K - 1);
-            if (pass == kCoverKeep && ncov && lane == 0) RUN[0] = (uint32_t)(C.K - 1);
-        } else {
+        // with no attribute outside B carried, every one gives the bottom, the
+        // one lower cover (none when B is already every attribute)
+        uint32_t ncov = any ? 0u : (full ? 0u : 1u);
+        if (any) {
             wave_sync();
-            // lane b: cm[u] = the objects having attribute 64u + b; counts to LDS
+            // lane b: cm[u] = c_n, the objects having attribute n = 64u + b (the
+            // transpose costs about as much as ten objects' broadcast reads)
             uint64_t cm[WMC];
 #pragma unroll
             for (int u = 0; u < WMC; ++u) cm[u] = 0;
-            for (int o = 0; o < a; ++o) {
+            if (a > 10) {
 #pragma unroll
                 for (int u = 0; u < WMC; ++u)
-                    if (u < wm && cand[u]) cm[u] |= ((R[o * WMC + u] >> lane) & 1ull) << o;
+                    if (u < wm && cand[u]) cm[u] = wave_transpose64(row[u]);
+            } else {
+                for (int o = 0; o < a; ++o) {
+#pragma unroll
+                    for (int u = 0; u < WMC; ++u)
+                        if (u < wm && cand[u]) cm[u] |= ((R[o * WMC + u] >> lane) & 1ull) << o;
+                }
             }
+            // Every extent strictly inside A lies in some c_n (n an attribute of
+            // its intent outside B), and (B + {n})'' = c_n' adds exactly the k
+            // with c_n inside c_k.  So the lower covers are the concepts (c_n,
+            // c_n') of the maximal c_n, each emitted by the smallest n with that
+            // c_n (the first attribute of c_n' outside B).  Taken largest first:
+            // the largest live c_n is maximal (a strict superset would be larger
+            // and would have taken it out); it takes out every live c_k inside
+            // it, equal ones included; and ties go to the smallest attribute,
+            // which for equal sets is the emitter.  The covers' intents and
+            // positions are then found a lane each, 64 covers at a time, so
+            // that their lookups overlap.
+            bool live[WMC];
+            uint32_t cnt[WMC];
 #pragma unroll
-            for (int u = 0; u < WMC; ++u)
-                if (u < wm) CN[u * 64 + lane] = (uint8_t)__popcll(cm[u]);
+            for (int u = 0; u < WMC; ++u) {
+                live[u] = u < wm && ((cand[u] >> lane) & 1ull);
+                cnt[u] = (uint32_t)__popcll(cm[u]);
+                if (pass != kCoverCount && u < wm) POS[u * 64 + lane] = kCoverEmpty;
+            }
             wave_sync();
+            for (;;) {
+                uint32_t key = 0;  // count, then the smaller attribute
 #pragma unroll
-            for (int u = WMC - 1; u >= 0; --u) {
-                if (u >= wm || !cand[u]) continue;
-                bool is_cover = (cand[u] >> lane) & 1ull;
-                uint64_t D[WMC];
-#pragma unroll
-                for (int v = 0; v < WMC; ++v) D[v] = ~0ull;
-                if (is_cover) {
-                    uint64_t mm = cm[u];
-                    while (mm) {
-                        const int o = __ffsll((unsigned long long)mm) - 1;
-                        mm &= mm - 1ull;
-#pragma unroll
-                        for (int v = 0; v < WMC; ++v)
-                            if (v < wm) D[v] &= R[o * WMC + v];
-                    }
-                    D[wm - 1] &= C.tail_m;
-                    // emitted by its first attribute outside B; a cover when every
-                    // attribute outside B has the object count of n = 64u + lane
-                    const int cnt_n = __popcll(cm[u]);
-                    bool first = true;
-#pragma unroll
-                    for (int v = 0; v < WMC; ++v) {
-                        if (v >= wm) continue;
-                        uint64_t x = D[v] & ~B[v];
-                        if (first && x) {
-                            if (v != u || (__ffsll((unsigned long long)x) - 1) != lane) is_cover = false;
-                            first = false;
-                        }
-                        while (x && is_cover) {
-                            const int k = __ffsll((unsigned long long)x) - 1;
-                            x &= x - 1ull;
-                            if ((int)CN[v * 64 + k] != cnt_n) is_cover = false;
-                        }
-                    }
+                for (int u = 0; u < WMC; ++u) {
+                    const uint32_t ku = (cnt[u] << 13) | 4096u | (uint32_t)(4095 - (64 * u + lane));
+                    if (live[u] && ku > key) key = ku;
                 }
-                const uint64_t emit = __ballot(is_cover);
-                if (pass != kCoverCount && is_cover) {
-                    const uint32_t pos = cover_position<WMC>(C, c, 64 * u + lane, D);
-                    const uint32_t k = ncov + (uint32_t)__popcll(emit & ~upto_mask(lane));
-                    if (pass == kCoverWrite) C.targets[C.offsets[i] + k] = pos;
-                    else RUN[k] = pos;
+                key = lane_value(wave_incl_scan_op<uint32_t>(key, 0u, [](uint32_t x, uint32_t y) { return x > y ? x : y; }),
+                                 kWave - 1);
+                if (!key) break;
+                const int n = 4095 - (int)(key & 4095u);
+                uint64_t pick = 0;
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (u == (n >> 6)) pick = cm[u];
+                const uint64_t cmax = lane_value64(pick, n & 63);
+#pragma unroll
+                for (int u = 0; u < WMC; ++u)
+                    if (live[u] && (cm[u] & ~cmax) == 0) live[u] = false;
+                const uint32_t slot = ncov & (kWave - 1);
+                if (pass != kCoverCount && lane == 0) {
+                    CMX[slot] = cmax;
+                    EMT[slot] = (uint16_t)n;
                 }
-                ncov += (uint32_t)__popcll(emit);
+                ++ncov;
+                // a full batch, or the last covers: lane k finds cover k's
+                // intent (the AND of its objects' rows) and position
+                const bool last = __ballot(live_any(live) != 0u) == 0ull;
+                if (pass != kCoverCount && (slot == kWave - 1 || last)) {
+                    wave_sync();
+                    if ((uint32_t)lane <= slot) {
+                        const uint64_t cx = CMX[lane];
+                        const int ne = (int)EMT[lane];
+                        uint64_t D[WMC];
+#pragma unroll
+                        for (int v = 0; v < WMC; ++v) D[v] = ~0ull;
+                        for (uint64_t x = cx; x; x &= x - 1ull) {
+                            const int o = __ffsll((unsigned long long)x) - 1;
+#pragma unroll
+                            for (int v = 0; v < WMC; ++v)
+                                if (v < wm) D[v] &= R[o * WMC + v];
+                        }
+                        D[wm - 1] &= C.tail_m;
+                        POS[ne] = cover_position<WMC>(C, c, ne, D);
+                    }
+                    wave_sync();
+                }
+                if (last) break;
             }
         }
         if (pass != kCoverWrite && lane == 0) C.count[i] = ncov;
-        if (pass == kCoverKeep && ncov) {
-            // the run goes to the wavefront's chunk (a new chunk when it does not
-            // fit; a run longer than a chunk is reserved on its own)
+        if (pass != kCoverCount && ncov) {
+            // the positions by descending emitter (ascending position): to the
+            // targets, or (pass 3) to a run in the wavefront's scratch chunk (a
+            // new chunk when it does not fit; a run longer than a chunk is
+            // reserved on its own)
+            uint32_t *out = C.targets;
             uint64_t at = 0;
-            if (ncov > kCoverChunk) {
-                if (lane == 0) at = atomicAdd((unsigned long long *)&C.ctr[2], (unsigned long long)ncov);
-                at = uniform64(at);
+            bool fits = true;
+            if (pass == kCoverWrite) {
+                at = C.offsets[i];
             } else {
-                if (used + ncov > kCoverChunk) {
-                    uint64_t b = 0;
-                    if (lane == 0) b = atomicAdd((unsigned long long *)&C.ctr[2], (unsigned long long)kCoverChunk);
-                    chunk = uniform64(b);
-                    used = 0;
+                out = C.scratch;
+                if (ncov > kCoverChunk) {
+                    if (lane == 0) at = atomicAdd((unsigned long long *)&C.ctr[2], (unsigned long long)ncov);
+                    at = uniform64(at);
+                } else {
+                    if (used + ncov > kCoverChunk) {
+                        uint64_t b = 0;
+                        if (lane == 0) b = atomicAdd((unsigned long long *)&C.ctr[2], (unsigned long long)kCoverChunk);
+                        chunk = uniform64(b);
+                        used = 0;
+                    }
+                    at = chunk + used;
+                    used += ncov;
                 }
-                at = chunk + used;
-                used += ncov;
+                fits = at + ncov <= C.scratch_cap;
+                if (lane == 0) {
+                    C.sstart[i] = at;
+                    if (!fits) C.ctr[3] = 1;
+                }
             }
-            wave_sync();  // RUN written by other lanes above
-            const bool fits = at + ncov <= C.scratch_cap;
-            if (fits)
-                for (uint32_t k = (uint32_t)lane; k < ncov; k += kWave) C.scratch[at + k] = RUN[k];
-            if (lane == 0) {
-                C.sstart[i] = at;
-                if (!fits) C.ctr[3] = 1;
+            if (fits) {
+                if (!any) {
+                    if (lane == 0) out[at] = (uint32_t)(C.K - 1);
+                } else {
+                    wave_sync();  // POS written by the batches above
+                    uint32_t k0 = 0;
+#pragma unroll
+                    for (int u = WMC - 1; u >= 0; --u) {
+                        if (u >= wm) continue;
+                        const uint32_t p = POS[u * 64 + lane];
+                        const bool e = p != kCoverEmpty;
+                        const uint64_t bal = __ballot(e);
+                        if (e) out[at + k0 + (uint32_t)__popcll(bal & ~upto_mask(lane))] = p;
+                        k0 += (uint32_t)__popcll(bal);
+                    }
+                }
             }
         }
         wave_sync();
@@ -2667,16 +2749,29 @@ __device__ __forceinline__ uint32_t cover_block_scan(uint32_t v, uint32_t &excl,
     return all;
 }
 
+// LDS of k_cover_big for M attributes (dynamic, so that small M leaves room
+// for more workgroups per compute unit): D slice, slice mask, counts,
+// positions, candidates, slots.
+template <int WMC>
+constexpr size_t cover_big_lds(int m)
+{
+    constexpr int WS = WMC <= 8 ? WMC : 64;
+    const size_t mm = ((size_t)m + 7) / 8 * 8;
+    return (size_t)kCoverSlice * WS * 8 + WS * 8 + mm * (4 + 4 + 2 + 2);
+}
+
 template <int WMC>
 __global__ void __launch_bounds__(kCoverThreads) k_cover_big(CoverArgs C, int pass)
 {
     constexpr int WS = WMC <= 8 ? WMC : 64;  // words of a D entry kept in LDS
-    __shared__ uint32_t s_cnt[kCoverMaxM];   // |c_n|
-    __shared__ uint32_t s_pos[kCoverMaxM];   // position of the cover emitted by n, else ~0
-    __shared__ uint16_t s_cand[kCoverMaxM];  // the carried candidates, ascending
-    __shared__ int16_t s_slot[kCoverMaxM];   // slot of n in the current slice, else -1
-    __shared__ uint64_t s_d[kCoverSlice * WS];
-    __shared__ uint64_t s_mask[WS];          // the current slice's attributes
+    extern __shared__ __attribute__((aligned(16))) uint64_t s_big[];
+    const size_t mm = ((size_t)C.m + 7) / 8 * 8;
+    uint64_t *s_d = s_big;                                          // kCoverSlice x WS
+    uint64_t *s_mask = s_d + kCoverSlice * WS;                      // WS: the current slice's attributes
+    uint32_t *s_cnt = (uint32_t *)(s_mask + WS);                    // mm: |c_n|
+    uint32_t *s_pos = s_cnt + mm;                                   // mm: position of the cover emitted by n, else ~0
+    uint16_t *s_cand = (uint16_t *)(s_pos + mm);                    // mm: the carried candidates, ascending
+    int16_t *s_slot = (int16_t *)(s_cand + mm);                     // mm: slot of n in the current slice, else -1
     __shared__ uint32_t s_sum[kCoverThreads / kWave];
     const int tid = threadIdx.x;
     const int wm = words_of<WMC>(C.wm);
