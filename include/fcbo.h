@@ -259,9 +259,10 @@ int fcbo_copy_to_host(fcbo_context *ctx, uint64_t first, uint64_t count, uint64_
  * stores E and writes nothing.  FCBO_ERR_INVALID_ARGUMENT if nothing was
  * enumerated.  Returns after the stream has finished.
  * The first call on a result finds every concept's covers and keeps the
- * counts, and (when device memory allows: about 4 bytes a cover and 8 a
- * concept) the covers' positions too, until the next enumeration; a later call
- * with large enough buffers then only copies them out.
+ * counts, and for 2^20 concepts or more (when device memory allows: about 4
+ * bytes a cover and 8 a concept) the covers' positions too, until the next
+ * enumeration; a later call with large enough buffers then only copies them
+ * out.
  */
 int fcbo_cover_edges(fcbo_context *ctx, uint64_t *offsets_out, uint32_t *targets_out, uint64_t capacity,
                      uint64_t *n_edges_out, double *elapsed_ms);

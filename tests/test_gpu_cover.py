@@ -110,3 +110,15 @@ def test_five_to_eight_word_intents(m):
 def test_wide_attribute_sets(n, m, d):
     # more than 8 intent words: every concept takes the workgroup kernel
     assert_cover_parity(synth.random_context(n * m + 1, n, m, d))
+
+
+@pytest.mark.parametrize("extra", [3, 70])
+def test_a_million_concepts_keep_the_positions(extra):
+    # 2^20 concepts (the contranominal scale of 20, padded across intent
+    # words): from that size on the counting pass keeps every cover's position
+    # and the writing call only copies them; with 70 full objects added every
+    # extent has more than 64 objects and the workgroup kernel does it all.
+    # The Boolean lattice of 20 atoms has 20 * 2^19 cover edges.
+    cells = synth.pad_with_full(synth.contranominal(20), extra_objects=extra, extra_attrs=50)
+    _, tg = assert_cover_parity(cells)
+    assert len(tg) == 20 * 2 ** 19
