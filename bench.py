@@ -377,6 +377,8 @@ def main():
     ap.add_argument("--rocprof-sq", nargs=2, metavar=("SQ_A_CSV", "SQ_B_CSV"))
     ap.add_argument("--enumerations", type=int, default=3, help="enumerations in the profiled process")
     ap.add_argument("--output-launches", type=int, default=2, help="output phases in the profiled process")
+    ap.add_argument("--intents-only", action="store_true",
+                    help="the profiled process wrote intents only (its output record is output_intents)")
     args = ap.parse_args()
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
@@ -388,8 +390,12 @@ def main():
             of, ow, lf, lw = rocprof_traffic(*args.rocprof_traffic, args.enumerations, args.output_launches,
                                              args.copy_probe_gib or 1.0)
             print("```")
-            print("traffic-record: class=output kernel=k_output_intents+k_output_block source_sha256=%s "
-                  "fetch_bytes_per_launch=%d write_bytes_per_launch=%d" % (sha, of, ow))
+            if args.intents_only:
+                print("traffic-record: class=output_intents kernel=k_output_intents source_sha256=%s "
+                      "fetch_bytes_per_launch=%d write_bytes_per_launch=%d" % (sha, of, ow))
+            else:
+                print("traffic-record: class=output kernel=k_output_intents+k_output_block source_sha256=%s "
+                      "fetch_bytes_per_launch=%d write_bytes_per_launch=%d" % (sha, of, ow))
             loop_issue = {k: v for k, v in (issue or {}).items() if k.split("<")[0] in LEVEL_LOOP_KERNELS}
             extra = " valu_issue=%s" % json.dumps(loop_issue, separators=(",", ":")) if loop_issue else ""
             print("traffic-record: class=level_loop source_sha256=%s fetch_bytes_per_step=%d write_bytes_per_step=%d%s"
