@@ -1,5 +1,5 @@
-"""GPU results under the symmetries the concept lattice has (the survey's P4 and
-P5, there checked on the oracle): renaming the objects changes no intent,
+"""GPU results under the symmetries of the concept lattice (the oracle's own
+tests check the same on the CPU): renaming the objects changes no intent,
 renaming the attributes renames the intents, and the transposed context has
 the same lattice with intents and extents exchanged.  These compare device
 results with device results, so they pin the kernels independently of the
