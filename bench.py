@@ -15,7 +15,9 @@ Prints one JSON line.  `value` is concepts per second; beside it:
     events on the library's stream, against the 8 TB/s HBM peak;
   * `closure_roofline`: the level loop (root to last level: closure tests,
     scans, child writes, the per-level host wait), the library's algorithmic
-    byte count `model_bytes` over its measured time;
+    byte count `model_bytes` over its measured time, and (`alu`) its VALU
+    wave-instructions per step from the committed counter pass over the same
+    time, against the chip's issue rate (the bound these kernels meet);
   * `hbm_probe`: a device copy and a fill timed in the same process, the
     achievable bandwidth on this machine, and a fill of the extent buffer itself
     (the store rate a destination of that size allows);
@@ -59,6 +61,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+VALU_ISSUE_PEAK_G = 256 * 4 * 2.4 / 4  # wave64 VALU instructions per ns: 256 CUs x 4 SIMDs at 2.4 GHz, 4 cycles each
 LEVEL_LOOP_KERNELS = ("k_local_test", "k_mid_test", "k_mid_test_wide", "k_huge_tasks", "k_huge_partial",
                       "k_huge_finalize", "k_big_test_list", "k_local_write", "k_mid_write", "k_mid_write_wide",
                       "k_huge_write", "k_big_write_list", "k_scan_up", "k_scan_mid", "k_scan_down", "k_scan_small",
@@ -314,7 +317,8 @@ def rocprof_traffic(fetch_csv, write_csv, enumerations, output_launches, copy_gi
 
 
 def rocprof_sq(a_csv, b_csv, n_cu=256, ghz=2.4):
-    """VALU issue share, wait share and LDS bank conflicts per kernel from the two SQ passes."""
+    """VALU issue share, wait share and LDS bank conflicts per kernel from the two SQ passes;
+    returns the issue shares and the VALU wave-instruction counts by kernel."""
     agg = {}
     for path in (a_csv, b_csv):
         for r in _counter_rows(path):
@@ -327,7 +331,7 @@ def rocprof_sq(a_csv, b_csv, n_cu=256, ghz=2.4):
             d["ns"][key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     print("| kernel | ms | VALU instr | VALU issue | LDS instr | VALU active | waiting | LDS bank conflict cycles |")
     print("|---|---:|---:|---:|---:|---:|---:|---:|")
-    issue = {}
+    issue, valu_by = {}, {}
     for name, d in sorted(agg.items(), key=lambda kv: -sum(v for (p, _), v in kv[1]["ns"].items() if p == a_csv)):
         c = d["c"]
         ms = sum(v for (p, _), v in d["ns"].items() if p == a_csv) / 1e6
@@ -337,10 +341,11 @@ def rocprof_sq(a_csv, b_csv, n_cu=256, ghz=2.4):
         active = c.get("SQ_ACTIVE_INST_VALU", 0.0) / cyc if cyc else 0.0
         wait = c.get("SQ_WAIT_ANY", 0.0) / cyc if cyc else 0.0
         issue[name.split("::")[1]] = round(frac, 3)
+        valu_by[name.split("::")[1]] = valu
         print("| `%s` | %.3f | %.3g | %.2f | %.3g | %.2f | %.2f | %.3g |" % (
             name, ms, valu, frac, c.get("SQ_INSTS_LDS", 0.0), active, wait, c.get("SQ_LDS_BANK_CONFLICT", 0.0)))
     print()
-    return issue
+    return issue, valu_by
 
 
 def main():
@@ -385,7 +390,7 @@ def main():
         return
     if args.rocprof_traffic or args.rocprof_sq:
         sha = source_sha256()
-        issue = rocprof_sq(*args.rocprof_sq) if args.rocprof_sq else None
+        issue, valu_by = rocprof_sq(*args.rocprof_sq) if args.rocprof_sq else (None, None)
         if args.rocprof_traffic:
             of, ow, lf, lw = rocprof_traffic(*args.rocprof_traffic, args.enumerations, args.output_launches,
                                              args.copy_probe_gib or 1.0)
@@ -398,6 +403,9 @@ def main():
                       "fetch_bytes_per_launch=%d write_bytes_per_launch=%d" % (sha, of, ow))
             loop_issue = {k: v for k, v in (issue or {}).items() if k.split("<")[0] in LEVEL_LOOP_KERNELS}
             extra = " valu_issue=%s" % json.dumps(loop_issue, separators=(",", ":")) if loop_issue else ""
+            if valu_by:
+                loop_valu = sum(v for k, v in valu_by.items() if k.split("<")[0] in LEVEL_LOOP_KERNELS)
+                extra += " valu_instr_per_step=%d" % int(loop_valu / args.enumerations)
             print("traffic-record: class=level_loop source_sha256=%s fetch_bytes_per_step=%d write_bytes_per_step=%d%s"
                   % (sha, lf, lw, extra))
             print("```")
@@ -526,6 +534,16 @@ def main():
         "timing": "timed steps, HIP events around the level loop"}
     if closure_roof["traffic"]:
         closure_roof["traffic_over_model"] = round(closure_roof["traffic"] / model, 3)
+    # The level loop's kernels are bound by vector-instruction issue, not HBM: their
+    # VALU wave-instructions per step (counter pass of the same sources) over the
+    # measured level loop, against the chip's issue rate, 256 CUs x 4 SIMDs x 2.4 GHz
+    # / 4 cycles per wave64 instruction = 614.4 G/s (some instructions issue faster,
+    # so this is the common-case peak)
+    if lrec and "valu_instr_per_step" in lrec:
+        vps = int(lrec["valu_instr_per_step"]) / (loop_ms * 1e-3) / 1e9
+        closure_roof["alu"] = {"bound": "alu", "achieved": round(vps, 1), "peak": VALU_ISSUE_PEAK_G,
+                               "unit": "G VALU wave-instructions/s", "frac": round(vps / VALU_ISSUE_PEAK_G, 4),
+                               "valu_instr_per_step": int(lrec["valu_instr_per_step"])}
 
     # the same step with the task-pool schedule (M <= 512), on a context of its
     # own so that the timed context keeps its result and its memory
