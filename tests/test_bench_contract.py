@@ -66,3 +66,39 @@ def test_task_pool_schedule_beyond_512_attributes_is_refused_before_any_device_w
         assert e.code == 2
     else:
         raise AssertionError("bench.main() accepted 513 attributes with the task pool")
+
+
+def _write_counters(path, rows):
+    import csv
+
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                                          "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_sq_summary_issue_share_and_valu_counts(tmp_path, capsys):
+    # One dispatch of 1 ms issuing 6.144e8 VALU wave-instructions: at four
+    # cycles each that is the whole issue capacity of 256 CUs x 4 SIMDs at
+    # 2.4 GHz (share 1.0); a second kernel at a quarter of it over 2 ms.
+    a, b = tmp_path / "a.csv", tmp_path / "b.csv"
+    k1, k2 = "void fcbo::k_local_test<7>(fcbo::LevelArgs)", "fcbo::k_scan_up(...)"
+    _write_counters(a, [
+        {"Dispatch_Id": 1, "Kernel_Name": k1, "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": 6.144e8,
+         "Start_Timestamp": 0, "End_Timestamp": 1_000_000},
+        {"Dispatch_Id": 2, "Kernel_Name": k2, "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": 3.072e8,
+         "Start_Timestamp": 0, "End_Timestamp": 2_000_000},
+    ])
+    _write_counters(b, [
+        {"Dispatch_Id": 1, "Kernel_Name": k1, "Counter_Name": "SQ_WAIT_ANY", "Counter_Value": 5,
+         "Start_Timestamp": 0, "End_Timestamp": 1_000_000},
+    ])
+    issue, valu = bench.rocprof_sq(str(a), str(b))
+    capsys.readouterr()
+    assert abs(issue["k_local_test<7>"] - 1.0) < 1e-9
+    assert abs(issue["k_scan_up"] - 0.25) < 1e-9
+    assert valu == {"k_local_test<7>": 6.144e8, "k_scan_up": 3.072e8}
+    # the issue-rate peak the bench divides by: 614.4 G wave-instructions a second
+    assert abs(bench.VALU_ISSUE_PEAK_G - 614.4) < 1e-9
