@@ -610,3 +610,38 @@ def test_full_ctx20000x256_against_store_free_oracle():
         _check_root_subtrees(g, eh, "extent")
     finally:
         ctx.close()
+
+
+def _planted(seed, n, m, density, blocks):
+    """A random context with `blocks` planted all-ones rectangles (rows and
+    columns drawn at random), so that some parents are large and deep."""
+    cells = synth.random_context(seed, n, m, density)
+    rng = np.random.default_rng(seed + 1)
+    for _ in range(blocks):
+        r = rng.choice(n, max(1, n // 6), replace=False)
+        c = rng.choice(m, max(1, m // 10), replace=False)
+        cells[np.ix_(r, c)] = True
+    return cells
+
+
+SWEEP = [(seed, n, m, d, b)
+         for seed, (n, m, d, b) in enumerate([(70, 40, 0.3, 1), (150, 66, 0.2, 2), (300, 127, 0.08, 3),
+                                               (513, 129, 0.06, 2), (1000, 200, 0.03, 4), (2049, 64, 0.1, 2),
+                                               (4100, 90, 0.04, 3), (700, 300, 0.02, 5), (260, 450, 0.015, 4),
+                                               (90, 700, 0.01, 2), (5000, 33, 0.15, 1), (129, 257, 0.05, 3)],
+                                              start=900)]
+
+
+@pytest.mark.parametrize("seed,n,m,d,b", SWEEP)
+def test_random_shapes_with_planted_blocks(seed, n, m, d, b):
+    # shapes on and off word boundaries, densities from 1% to 30%, planted
+    # blocks that make large parents (mid and huge classes) and long chains
+    assert_parity(_planted(seed, n, m, d, b))
+
+
+@pytest.mark.parametrize("n,m,d", [(200, 4096, 0.004), (300, 2000, 0.006)])
+def test_wide_intents_with_large_parents(n, m, d):
+    # more than eight intent words with parents of more than 64 objects (there
+    # every such parent takes the chunked huge path)
+    cells = _planted(n * 7 + m, n, m, d, 2)
+    assert_parity(cells)
