@@ -122,3 +122,11 @@ def test_a_million_concepts_keep_the_positions(extra):
     cells = synth.pad_with_full(synth.contranominal(20), extra_objects=extra, extra_attrs=50)
     _, tg = assert_cover_parity(cells)
     assert len(tg) == 20 * 2 ** 19
+
+
+from tests.test_gpu_parity import SWEEP, _planted  # noqa: E402
+
+
+@pytest.mark.parametrize("seed,n,m,d,b", SWEEP[:8])
+def test_random_shapes_with_planted_blocks(seed, n, m, d, b):
+    assert_cover_parity(_planted(seed, n, m, d, b))

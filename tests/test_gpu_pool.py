@@ -228,3 +228,11 @@ def test_full_ctx50000x400_pool_against_stored_oracle():
         assert hashlib.sha256(np.ascontiguousarray(eh, dtype="<u8").tobytes()).hexdigest() == g["extent_hashes_sha256"]
     finally:
         ctx.close()
+
+
+from tests.test_gpu_parity import SWEEP, _planted  # noqa: E402
+
+
+@pytest.mark.parametrize("seed,n,m,d,b", [c for c in SWEEP if c[2] <= 512])
+def test_random_shapes_with_planted_blocks(seed, n, m, d, b):
+    pool_parity(_planted(seed, n, m, d, b))
