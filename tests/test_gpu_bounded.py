@@ -436,3 +436,12 @@ def test_full_ctx20000x256_bounded_against_store_free_oracle():
         ctx.close()
         hs = None
         release_device_cache()
+
+
+from tests.test_gpu_parity import SWEEP, _planted  # noqa: E402
+
+
+@pytest.mark.parametrize("seed,n,m,d,b", SWEEP[:6])
+def test_random_shapes_with_planted_blocks_in_batches(seed, n, m, d, b):
+    # every batch one subtree (the hook), pieces of a few hundred rows
+    assert_matches_oracle(_planted(seed, n, m, d, b), piece_rows=333, flags=ONE)
