@@ -19,7 +19,7 @@ Prints one JSON line.  `value` is concepts per second; beside it:
     wave-instructions per step from the committed counter pass over the same
     time, against the chip's issue rate (the bound these kernels meet);
   * `hbm_probe`: a device copy and a fill timed in the same process, the
-    achievable bandwidth on this box, and a fill of the extent buffer itself
+    achievable bandwidth on this machine, and a fill of the extent buffer itself
     (the store rate a destination of that size allows);
   * `cover_edges`: the lattice's cover edges of the same result
     (fcbo_cover_edges), timed once after the steps;

@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 
 def _flush_case(item):
-    # Name the case before any GPU step, so a lost box still tells which one ran.
+    # Name the case before any GPU step, so a run that ends abruptly still tells which one ran.
     print("\n[case] %s" % item.nodeid, flush=True)
 
 
