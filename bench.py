@@ -255,6 +255,50 @@ def rocprof_summary(paths):
         print()
 
 
+def rocprof_gaps(path, top=12):
+    """Print the level loop of the last enumeration in a rocprofv3 kernel_trace CSV
+    (from the last k_root_init to the first ordering kernel): its span, the time at
+    least one kernel runs, the time none does, and the longest gaps between kernels
+    with the kernel and stream on each side."""
+    import csv
+
+    with open(path) as f:
+        rows = list(csv.DictReader(f))
+    ks = sorted(({"n": _short(r["Kernel_Name"]).replace("fcbo::", ""), "s": int(r["Start_Timestamp"]),
+                  "e": int(r["End_Timestamp"]), "q": r.get("Stream_Id", "?")} for r in rows), key=lambda k: k["s"])
+    roots = [i for i, k in enumerate(ks) if k["n"] == "k_root_init"]
+    if not roots:
+        raise SystemExit("no k_root_init dispatch in %s" % path)
+    i0 = roots[-1]
+    i1 = next((i for i in range(i0, len(ks)) if ks[i]["n"].startswith("k_subtree_size")), len(ks))
+    loop = ks[i0:i1]
+    t0, t1 = loop[0]["s"], (ks[i1]["s"] if i1 < len(ks) else max(k["e"] for k in loop))
+    busy, gaps = 0, []
+    cur_s, cur_e, last = loop[0]["s"], loop[0]["e"], loop[0]
+    for k in loop[1:]:
+        if k["s"] > cur_e:
+            busy += cur_e - cur_s
+            gaps.append((cur_e - t0, k["s"] - cur_e, last, k))
+            cur_s, cur_e, last = k["s"], k["e"], k
+        elif k["e"] > cur_e:
+            cur_e, last = k["e"], k
+    busy += cur_e - cur_s
+    if t1 > cur_e:
+        gaps.append((cur_e - t0, t1 - cur_e, last, ks[i1] if i1 < len(ks) else last))
+    span = t1 - t0
+    cross = [g for g in gaps if g[2]["q"] != g[3]["q"]]
+    print("## Level loop of the last enumeration: time with no kernel running\n")
+    print("| span us | some kernel running us | no kernel running us | gaps | gaps across streams | their us |")
+    print("|---:|---:|---:|---:|---:|---:|")
+    print("| %.1f | %.1f | %.1f | %d | %d | %.1f |\n" % (span / 1e3, busy / 1e3, (span - busy) / 1e3, len(gaps),
+                                                         len(cross), sum(g[1] for g in cross) / 1e3))
+    print("| at us | gap us | after (stream) | before (stream) |")
+    print("|---:|---:|---|---|")
+    for at, gap, a, b in sorted(gaps, key=lambda g: -g[1])[:top]:
+        print("| %.1f | %.1f | `%s` (%s) | `%s` (%s) |" % (at / 1e3, gap / 1e3, a["n"], a["q"], b["n"], b["q"]))
+    print()
+
+
 def _counter_rows(path):
     import csv
 
@@ -378,6 +422,8 @@ def main():
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="run one device-to-device copy of this size first (counter calibration)")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="CSV")
+    ap.add_argument("--rocprof-gaps", metavar="KERNEL_TRACE_CSV",
+                    help="idle time between kernels in the last enumeration's level loop")
     ap.add_argument("--rocprof-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--rocprof-sq", nargs=2, metavar=("SQ_A_CSV", "SQ_B_CSV"))
     ap.add_argument("--enumerations", type=int, default=3, help="enumerations in the profiled process")
@@ -387,6 +433,9 @@ def main():
     args = ap.parse_args()
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
+        return
+    if args.rocprof_gaps:
+        rocprof_gaps(args.rocprof_gaps)
         return
     if args.rocprof_traffic or args.rocprof_sq:
         sha = source_sha256()

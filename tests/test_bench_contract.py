@@ -102,3 +102,31 @@ def test_sq_summary_issue_share_and_valu_counts(tmp_path, capsys):
     assert valu == {"k_local_test<7>": 6.144e8, "k_scan_up": 3.072e8}
     # the issue-rate peak the bench divides by: 614.4 G wave-instructions a second
     assert abs(bench.VALU_ISSUE_PEAK_G - 614.4) < 1e-9
+
+
+def test_kernel_trace_gaps_of_the_last_level_loop(tmp_path, capsys):
+    # Two enumerations; only the second one's level loop (from its k_root_init to
+    # its first k_subtree_size) is read.  Its kernels, in us from its start:
+    #   root [0, 100) s0, test [100, 400) s0, mid [420, 500) s1, write [450, 600)
+    #   s0 (overlapping mid), then the ordering kernel at 630.  Some kernel runs
+    #   in [0, 400) and [420, 600): 580 of a 630 us span; the gaps are 20 us
+    #   (s0 test -> s1 mid, across streams) and 30 us (write -> ordering).
+    head = '"Kind","Dispatch_Id","Kernel_Name","Stream_Id","Start_Timestamp","End_Timestamp"\n'
+    us = 1000
+    t = 50_000 * us
+    rows = [("fcbo::k_root_init(x)", 0, 0, 50 * us), ("fcbo::k_subtree_size(x)", 0, 60 * us, 70 * us),
+            ("fcbo::k_root_init(x)", 0, t, t + 100 * us),
+            ("void fcbo::k_local_test<7>(x)", 0, t + 100 * us, t + 400 * us),
+            ("void fcbo::k_mid_test<7>(x)", 1, t + 420 * us, t + 500 * us),
+            ("void fcbo::k_local_write<7>(x)", 0, t + 450 * us, t + 600 * us),
+            ("fcbo::k_subtree_size(x)", 0, t + 630 * us, t + 700 * us)]
+    p = tmp_path / "trace_kernel_trace.csv"
+    p.write_text(head + "".join('"KERNEL_DISPATCH",%d,"%s",%d,%d,%d\n' % (i, n, q, s, e)
+                                for i, (n, q, s, e) in enumerate(rows)))
+    bench.rocprof_gaps(str(p))
+    out = capsys.readouterr().out
+    assert "| 630.0 | 580.0 | 50.0 | 2 | 1 | 20.0 |" in out
+    gaps = [ln for ln in out.splitlines() if ln.startswith("| 600.0 |") or ln.startswith("| 400.0 |")]
+    # longest first: 30 us after the write, then 20 us across streams
+    assert gaps == ["| 600.0 | 30.0 | `k_local_write<7>` (0) | `k_subtree_size` (0) |",
+                    "| 400.0 | 20.0 | `k_local_test<7>` (0) | `k_mid_test<7>` (1) |"]
