@@ -375,7 +375,8 @@ class Context:
     def count(self, pool: bool = False) -> int:
         """Enumerate (keeping the result in the context) and return K."""
         rc, k, _ = fcbo_enumerate(self.handle, 0, 0, 0, FCBO_TASK_POOL if pool else 0)
-        assert rc == FCBO_ERR_CAPACITY
+        if rc != FCBO_ERR_CAPACITY:  # a context has at least one concept, so no call with capacity 0 succeeds
+            raise FcboError(rc, "fcbo_enumerate")
         return k
 
     def alloc_outputs(self, capacity: int, extents: bool = True):
