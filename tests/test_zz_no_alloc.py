@@ -82,3 +82,23 @@ def test_static_entry_capacity_and_scratch_errors():
     big_dev = torch.from_numpy(big.view(np.int64)).cuda()
     rc, kk, _, _, _ = _static_call(big_dev, cells.shape[0], cells.shape[1], 0, extents=False)
     assert rc == fca.FCBO_ERR_SCRATCH
+
+
+from tests.test_gpu_parity import SWEEP, _planted  # noqa: E402
+
+
+@pytest.mark.parametrize("seed,n,m,d,b", SWEEP)
+def test_static_entry_on_random_shapes_with_planted_blocks(seed, n, m, d, b):
+    # shapes on and off word boundaries (up to eleven intent words), planted
+    # blocks that make mid and huge parents: every level kernel and buffer
+    # growth, all of it carved from the static scratch, against the oracle
+    cells = _planted(seed, n, m, d, b)
+    rows = synth.pack_rows(cells)
+    want = oracle.cbo(rows, m)
+    rows_dev = torch.from_numpy(rows.view(np.int64)).cuda()
+    rc, k, st, ints, exts = _static_call(rows_dev, n, m, want.n_concepts)
+    assert rc == fca.FCBO_OK and k == want.n_concepts
+    assert np.array_equal(ints.cpu().numpy().view(np.uint64), want.intents)
+    assert np.array_equal(exts.cpu().numpy().view(np.uint64), want.extents)
+    assert st.closure_tests == want.tests and st.item_pairs == want.pairs
+    assert st.sum_child_objects == want.sum_c
