@@ -639,6 +639,15 @@ def test_random_shapes_with_planted_blocks(seed, n, m, d, b):
     assert_parity(_planted(seed, n, m, d, b))
 
 
+@pytest.mark.parametrize("seed,n,m,d,b", SWEEP)
+def test_random_shapes_with_planted_blocks_from_minimal_buffers(seed, n, m, d, b):
+    # the same shapes with every buffer starting at its minimum: the store,
+    # the record buffers and the huge tests grow level by level, and levels
+    # whose records overflowed are redone
+    res = assert_parity(_planted(seed, n, m, d, b), flags=fca.FCBO_TINY_BUFFERS)
+    assert res.stats["level_redos"] >= 1  # the root (70 objects or more) overflows its one record slot
+
+
 @pytest.mark.parametrize("n,m,d", [(200, 4096, 0.004), (300, 2000, 0.006)])
 def test_wide_intents_with_large_parents(n, m, d):
     # more than eight intent words with parents of more than 64 objects (there
