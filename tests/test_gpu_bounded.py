@@ -445,3 +445,11 @@ from tests.test_gpu_parity import SWEEP, _planted  # noqa: E402
 def test_random_shapes_with_planted_blocks_in_batches(seed, n, m, d, b):
     # every batch one subtree (the hook), pieces of a few hundred rows
     assert_matches_oracle(_planted(seed, n, m, d, b), piece_rows=333, flags=ONE)
+
+
+@pytest.mark.parametrize("seed,n,m,d,b", SWEEP[6:])
+def test_random_shapes_with_planted_blocks_split_below_the_root(seed, n, m, d, b):
+    # every root child split one level down (the hook), so the batches hold
+    # grandchildren of the root; pieces of a thousand rows
+    k, st, want = assert_matches_oracle(_planted(seed, n, m, d, b), piece_rows=1000, flags=SPLIT)
+    assert st["batch_splits"] == int(want.level_concepts[1])
