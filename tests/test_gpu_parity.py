@@ -654,3 +654,37 @@ def test_wide_intents_with_large_parents(n, m, d):
     # every such parent takes the chunked huge path)
     cells = _planted(n * 7 + m, n, m, d, 2)
     assert_parity(cells)
+
+
+@pytest.mark.parametrize("seed,n,m,d,b", [c for c in SWEEP if c[0] in (905, 906, 907, 908, 909, 910)])
+def test_paged_and_streamed_output_on_planted_shapes(seed, n, m, d, b):
+    # row widths from 33 to 79 extent words and 1 to 11 intent words: the
+    # output kernels' tile shapes, fetched in pieces of seeded random sizes
+    # (write_range) and streamed to pinned host memory (copy_to_host)
+    cells = _planted(seed, n, m, d, b)
+    rows = synth.pack_rows(cells)
+    want = oracle.cbo(rows, m)
+    k = want.n_concepts
+    rng = np.random.default_rng(seed)
+    ctx = fca.Context(rows, m)
+    try:
+        assert ctx.count() == k
+        got_i = np.zeros_like(want.intents)
+        got_e = np.zeros_like(want.extents)
+        bi, be = ctx.alloc_outputs(4096, True)
+        first = 0
+        while first < k:
+            cnt = min(int(rng.integers(1, 4097)), k - first)
+            ctx.write_range(first, bi[:cnt], be[:cnt])
+            got_i[first:first + cnt] = bi[:cnt].cpu().numpy().view(np.uint64)
+            got_e[first:first + cnt] = be[:cnt].cpu().numpy().view(np.uint64)
+            first += cnt
+        assert np.array_equal(got_i, want.intents)
+        assert np.array_equal(got_e, want.extents)
+        hi = torch.full((k, ctx.wm), -1, dtype=torch.int64).pin_memory()
+        he = torch.full((k, ctx.wn), -1, dtype=torch.int64).pin_memory()
+        ctx.copy_to_host(0, k, hi, he, staging_rows=int(rng.integers(100, 3000)))
+        assert np.array_equal(hi.numpy().view(np.uint64), want.intents)
+        assert np.array_equal(he.numpy().view(np.uint64), want.extents)
+    finally:
+        ctx.close()
