@@ -527,3 +527,38 @@ def test_cover_edges_invariants_ctx2000x64():
     for e in sample:
         a, b = ib[src[e]], ib[tg[e]]
         assert (b | ~a).all() and (b != a).any()
+
+
+# --- property-based: contexts drawn and shrunk by hypothesis ----------------------------
+
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as hs  # noqa: E402
+
+
+@hs.composite
+def _contexts(draw, max_n=24, max_m=9):
+    """A 0/1 context; hypothesis favours the edge structure random draws rarely
+    give (empty and full rows, repeated rows and columns) and shrinks a failure
+    to a minimal context."""
+    n = draw(hs.integers(1, max_n))
+    m = draw(hs.integers(1, max_m))
+    bits = draw(hs.lists(hs.lists(hs.booleans(), min_size=m, max_size=m), min_size=n, max_size=n))
+    return np.array(bits, dtype=bool)
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow], derandomize=True,
+          database=None)
+@given(_contexts())
+def test_property_concepts_against_both_brute_forces(cells):
+    # every closed set from all attribute subsets and from row meets, in the
+    # output order, with the CbO tree's counts
+    check_against_brute(cells, tree=True, subsets=True)
+
+
+@settings(max_examples=200, deadline=None, suppress_health_check=[HealthCheck.too_slow], derandomize=True,
+          database=None)
+@given(_contexts(max_n=16, max_m=8))
+def test_property_cover_edges_against_the_hasse_diagram(cells):
+    r = run(cells, keep_extents=False)
+    off, tg = oracle.cover_edges(synth.pack_rows(cells), cells.shape[1], r.intents)
+    assert _edges_as_lists(off, tg) == brute.hasse_lower_covers(as_sets(r.intents))
