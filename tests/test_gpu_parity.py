@@ -688,3 +688,48 @@ def test_paged_and_streamed_output_on_planted_shapes(seed, n, m, d, b):
         assert np.array_equal(he.numpy().view(np.uint64), want.extents)
     finally:
         ctx.close()
+
+
+def test_two_contexts_enumerate_at_once_from_two_host_threads():
+    # Contexts share no state (the static scratch of the allocation-free entry
+    # point aside): two of them, each on a stream of its own, enumerating at
+    # the same time from two host threads (ctypes releases the GIL in the
+    # library's calls) give the oracle's results, three rounds over
+    import threading
+
+    cases = []
+    for name in ("ctx2000x64", "ctx10000x128"):
+        n, m, _ = synth.CONFIGS[name]
+        rows = synth.make_config(name)
+        cases.append((name, rows, m, oracle.cbo(rows, m)))
+    for rnd in range(3):
+        results, errors = {}, []
+
+        def work(name, rows, m):
+            try:
+                s = torch.cuda.Stream()
+                with torch.cuda.stream(s):
+                    ctx = fca.Context(rows, m, stream=s)
+                    try:
+                        res = ctx.enumerate(extents=True)
+                        s.synchronize()
+                        results[name] = (res.n_concepts, res.intents.cpu().numpy().view(np.uint64),
+                                         res.extents.cpu().numpy().view(np.uint64), res.stats["closure_tests"])
+                    finally:
+                        ctx.close()
+            except BaseException as e:  # handed to the main thread
+                errors.append((name, e))
+
+        threads = [threading.Thread(target=work, args=(name, rows, m)) for name, rows, m, _ in cases]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join(timeout=120)
+        assert not any(t.is_alive() for t in threads), rnd
+        assert not errors, errors
+        for name, _, _, want in cases:
+            k, ints, exts, tests = results[name]
+            assert k == want.n_concepts, (rnd, name)
+            assert np.array_equal(ints, want.intents), (rnd, name)
+            assert np.array_equal(exts, want.extents), (rnd, name)
+            assert tests == want.tests, (rnd, name)
